@@ -1,0 +1,167 @@
+/*
+ * CPU fp64 oracle for decayed recurrent (Lightning) attention, forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this file's library.  It shares
+ * no code, header, table or helper with the GPU library and must never be
+ * used as a fallback for it.
+ *
+ * What it computes (ejkernel "recurrent" interface page, docstring "The core
+ * update is"): for every sequence n and query head h, a state S of shape
+ * [dk, dv] is carried token by token,
+ *
+ *     S_t = exp(g_gamma[h]) * S_{t-1} + k_t^T v_t          (outer product)
+ *     o_t = scale * (q_t S_t)                              (contract over dk)
+ *
+ * with S_{-1} = initial_state (or zeros) and final_state = S after the last
+ * token.  Readings taken where the pages are silent or garbled:
+ *   - g_gamma is a log-decay: the per-step factor is exp(g_gamma[h]); all-zero
+ *     g_gamma is "no decay" (recurrent page, defaults of the forward rule).
+ *   - decay first, then add token t, then read out: token t reaches o_t with
+ *     weight 1.
+ *   - the printed "o_t = h_t @ q_t" is read as q_t^T S_t (a dv-vector), the
+ *     only orientation whose shapes agree when dk != dv.
+ *   - scale multiplies q (lightning_attn page, softmax_scale argument), so it
+ *     scales o and never the state.
+ *   - GQA: query head h reads kv head h / (H / Hkv) (grouped, contiguous);
+ *     decay and state are per query head.
+ *   - reverse: the same recurrence run from the last position to the first;
+ *     o_t stays at index t; initial_state enters at the last position.
+ *   - packed varlen (cu_seqlens): the state restarts at every boundary and
+ *     each sequence has its own initial/final state.
+ *
+ * All arithmetic is IEEE fp64.  Inputs are the exact values of the bf16 or
+ * fp32 words the GPU receives.  Loops are written in the order of the
+ * recurrence, with no blocking or reordering.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_IN_BF16 0
+#define ORACLE_IN_F32 1
+
+/* Exact value of element i of an input array stored as bf16 words or fp32. */
+static double in_value(const void* base, int dtype, int64_t i) {
+    if (dtype == ORACLE_IN_F32) return (double)((const float*)base)[i];
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Lightning per-head log-decay (ejkernel lightning_attn page, module docstring
+ * "Key innovation" and the wrapper body):
+ *     g_gamma[h] = -(8 / H) * (1 - layer_idx / num_layers) * h,  h = 0..H-1.
+ * The wrapper builds the coefficient as a Python float (fp64) and multiplies
+ * it into a float32 arange; under JAX's weak typing the coefficient is first
+ * rounded to float32, then the product is taken in float32.
+ */
+int oracle_lightning_g_gamma(int num_heads, int layer_idx, int num_layers, float* out) {
+    if (num_heads <= 0 || num_layers <= 0 || out == NULL) return -1;
+    double coef = -(8.0 / (double)num_heads * (1.0 - (double)layer_idx / (double)num_layers));
+    float coef32 = (float)coef;
+    for (int h = 0; h < num_heads; ++h) {
+        volatile float hv = (float)h; /* float32 arange element */
+        out[h] = coef32 * hv;         /* float32 product */
+    }
+    return 0;
+}
+
+int oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
+/*
+ * Forward recurrence (ejkernel "recurrent" page, update equation; lightning_attn
+ * page for the argument meanings).
+ *
+ *   q [B, T, H, dk], k [B, T, Hkv, dk], v [B, T, Hkv, dv]   (in_dtype)
+ *   g_gamma [H] float32, scale (fp64 value of the float32 scale)
+ *   initial_state [N_seq, H, dk, dv] float32, or NULL for zeros
+ *   cu_seqlens [N_seq + 1] int64, or NULL: then N_seq = B and sequence n is
+ *     batch row n; else B must be 1 and sequence n is rows [cu[n], cu[n+1]).
+ *   pair_mask [N_seq * H] or NULL: when given, only (n, h) pairs with a
+ *     non-zero entry are computed (the others are left untouched).
+ *   o [B, T, H, dv] fp64, final_state [N_seq, H, dk, dv] fp64 (outputs)
+ * Returns 0, or -1 on inconsistent arguments.
+ */
+int oracle_recurrent_fwd(int batch, int seqlen, int num_heads, int num_kv_heads,
+                         int dk, int dv, int in_dtype,
+                         const void* q, const void* k, const void* v,
+                         const float* g_gamma, double scale,
+                         const float* initial_state, int reverse,
+                         const int64_t* cu_seqlens, int num_seqs,
+                         const uint8_t* pair_mask,
+                         double* o, double* final_state) {
+    if (batch <= 0 || seqlen < 0 || num_heads <= 0 || num_kv_heads <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (num_heads % num_kv_heads != 0) return -1;
+    if (cu_seqlens != NULL && batch != 1) return -1;
+    const int n_seq = cu_seqlens ? num_seqs : batch;
+    const int group = num_heads / num_kv_heads;
+    const int64_t n_pairs = (int64_t)n_seq * num_heads;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t pair = 0; pair < n_pairs; ++pair) {
+        if (pair_mask && !pair_mask[pair]) continue;
+        const int n = (int)(pair / num_heads);
+        const int h = (int)(pair % num_heads);
+        const int kvh = h / group;
+        int64_t row0, len; /* rows row0 .. row0+len-1 of the flattened [B*T] axis */
+        if (cu_seqlens) {
+            row0 = cu_seqlens[n];
+            len = cu_seqlens[n + 1] - cu_seqlens[n];
+        } else {
+            row0 = (int64_t)n * seqlen;
+            len = seqlen;
+        }
+        const double lam = exp((double)g_gamma[h]);
+
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+        double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* kt = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* vt = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* out_row = (double*)malloc(sizeof(double) * (size_t)dv);
+        const int64_t st_base = ((int64_t)n * num_heads + h) * dk * dv;
+        for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
+            S[i] = initial_state ? (double)initial_state[st_base + i] : 0.0;
+
+        for (int64_t step = 0; step < len; ++step) {
+            const int64_t row = reverse ? row0 + len - 1 - step : row0 + step;
+            const int64_t qo = (row * num_heads + h) * dk;
+            const int64_t ko = (row * num_kv_heads + kvh) * dk;
+            const int64_t vo = (row * num_kv_heads + kvh) * dv;
+            for (int a = 0; a < dk; ++a) qt[a] = in_value(q, in_dtype, qo + a);
+            for (int a = 0; a < dk; ++a) kt[a] = in_value(k, in_dtype, ko + a);
+            for (int c = 0; c < dv; ++c) vt[c] = in_value(v, in_dtype, vo + c);
+            /* S <- lam * S + k_t^T v_t */
+            for (int a = 0; a < dk; ++a)
+                for (int c = 0; c < dv; ++c)
+                    S[(int64_t)a * dv + c] = lam * S[(int64_t)a * dv + c] + kt[a] * vt[c];
+            /* o_t = scale * (q_t S) */
+            for (int c = 0; c < dv; ++c) out_row[c] = 0.0;
+            for (int a = 0; a < dk; ++a)
+                for (int c = 0; c < dv; ++c) out_row[c] += qt[a] * S[(int64_t)a * dv + c];
+            for (int c = 0; c < dv; ++c) o[(row * num_heads + h) * dv + c] = scale * out_row[c];
+        }
+        for (int64_t i = 0; i < (int64_t)dk * dv; ++i) final_state[st_base + i] = S[i];
+        free(qt);
+        free(kt);
+        free(vt);
+        free(out_row);
+        free(S);
+    }
+    return 0;
+}

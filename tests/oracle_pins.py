@@ -1,0 +1,290 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Every function takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with the pin.  ``test_oracle.py`` runs them against the real
+oracle; ``test_oracle_mutants.py`` runs them against deliberately broken copies
+of the oracle source to show that each plausible mistake is caught.
+
+None of the pins re-types the oracle's loop: they use the closed (all-pairs)
+form of the recurrence written with numpy array algebra, textbook causal linear
+attention, structural invariants (chaining, reversal, packing), and closed-form
+values of the pages' all-ones examples.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+
+from decayed_recurrent_attention_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "page_examples.json")
+
+
+def golden() -> dict:
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Independent closed form: o_t = scale * [lam^(t+1) q_t S0 + sum_{s<=t} lam^(t-s) (q_t.k_s) v_s]
+# (forward), mirrored for reverse; final = lam^T S0 + sum_s lam^(T-1-s) k_s^T v_s.
+# ---------------------------------------------------------------------------
+def closed_form(q, k, v, g, scale, S0=None, reverse=False):
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, T, H, dk = q.shape
+    Hkv = k.shape[2]
+    dv = v.shape[3]
+    rep = H // Hkv
+    k = np.repeat(k, rep, axis=2)  # query head h uses kv head h // rep
+    v = np.repeat(v, rep, axis=2)
+    t = np.arange(T)
+    if reverse:
+        steps = t[None, :] - t[:, None]  # s - t, contributes when s >= t
+        to_end = t  # decay applied to the state entering at the end
+        init_pow = T - t  # lam^(T - t) on S0 for output t
+    else:
+        steps = t[:, None] - t[None, :]  # t - s, contributes when s <= t
+        to_end = T - 1 - t
+        init_pow = t + 1
+    o = np.zeros((B, T, H, dv))
+    fs = np.zeros((B, H, dk, dv))
+    for h in range(H):
+        lam = np.exp(np.float64(g[h]))
+        D = np.where(steps >= 0, lam ** np.maximum(steps, 0), 0.0)  # [T(t), T(s)]
+        for b in range(B):
+            Q, K, V = q[b, :, h], k[b, :, h], v[b, :, h]
+            o[b, :, h] = (D * (Q @ K.T)) @ V
+            fs[b, h] = (K * (lam ** to_end)[:, None]).T @ V
+            if S0 is not None:
+                S = np.asarray(S0[b, h], dtype=np.float64)
+                o[b, :, h] += (lam ** init_pow)[:, None] * (Q @ S)
+                fs[b, h] += lam ** T * S
+    return scale * o, fs
+
+
+def _rand_case(seed, B, T, H, Hkv, dk, dv, with_init, zero_head=True):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = rng.standard_normal((B, T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((B, T, Hkv, dk)).astype(np.float32)
+    v = rng.standard_normal((B, T, Hkv, dv)).astype(np.float32)
+    g = -rng.uniform(0.0, 2.5, size=H).astype(np.float32)
+    if zero_head:
+        g[0] = np.float32(-0.0)
+    S0 = rng.standard_normal((B, H, dk, dv)).astype(np.float32) if with_init else None
+    scale = float(np.float32(rng.uniform(0.1, 1.0)))
+    return q, k, v, g, S0, scale
+
+
+def _close(a, b, rtol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    den = max(float(np.max(np.abs(b))), 1e-300)
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= rtol * den, f"{what}: max err {err:.3e} > {rtol:.1e} * {den:.3e}"
+
+
+# -- pin (a): brute-force closed form on tiny random inputs ---------------------
+BRUTE_CASES = [
+    # seed, B, T, H, Hkv, dk, dv, init, reverse
+    (1, 1, 1, 1, 1, 3, 2, False, False),
+    (2, 2, 7, 2, 1, 5, 3, True, False),
+    (3, 1, 33, 4, 2, 4, 6, True, True),
+    (4, 2, 19, 4, 4, 8, 8, False, True),
+    (5, 1, 40, 6, 3, 3, 5, True, False),
+    (6, 1, 64, 2, 2, 8, 4, True, True),
+]
+
+
+def pin_brute_force(orc):
+    for seed, B, T, H, Hkv, dk, dv, init, rev in BRUTE_CASES:
+        q, k, v, g, S0, scale = _rand_case(seed, B, T, H, Hkv, dk, dv, init)
+        o, fs = orc.recurrent_fwd(q, k, v, g, scale, initial_state=S0, reverse=rev)
+        o_ref, fs_ref = closed_form(q, k, v, g, scale, S0, rev)
+        _close(o, o_ref, 1e-11, f"o, case {seed}")
+        _close(fs, fs_ref, 1e-11, f"final_state, case {seed}")
+
+
+def pin_bf16_words(orc):
+    """bf16 words are read as their exact values."""
+    q, k, v, g, S0, scale = _rand_case(11, 1, 20, 2, 1, 8, 4, True)
+    qw, kw, vw = (inputs.bf16_words(x) for x in (q, k, v))
+    o_w, fs_w = orc.recurrent_fwd(qw, kw, vw, g, scale, initial_state=S0)
+    qf, kf, vf = (inputs.bf16_values(x) for x in (qw, kw, vw))
+    o_ref, fs_ref = closed_form(qf, kf, vf, g, scale, S0)
+    _close(o_w, o_ref, 1e-11, "bf16 o")
+    _close(fs_w, fs_ref, 1e-11, "bf16 final_state")
+
+
+# -- pin (b): no decay is textbook causal linear attention ----------------------
+def pin_no_decay(orc):
+    rng = np.random.Generator(np.random.PCG64(21))
+    B, T, H, d = 2, 37, 3, 6
+    q = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    scale = 0.5
+    o, fs = orc.recurrent_fwd(q, k, v, np.zeros(H, np.float32), scale)
+    mask = np.tril(np.ones((T, T)))
+    for b in range(B):
+        for h in range(H):
+            Q, K, V = (x[b, :, h].astype(np.float64) for x in (q, k, v))
+            _close(o[b, :, h], scale * (mask * (Q @ K.T)) @ V, 1e-12, "no-decay o")
+            _close(fs[b, h], K.T @ V, 1e-12, "no-decay final_state")
+
+
+# -- pin (c): chaining final_state -> initial_state ------------------------------
+def pin_chaining(orc):
+    q, k, v, g, S0, scale = _rand_case(31, 2, 50, 4, 2, 6, 5, True)
+    for rev in (False, True):
+        o, fs = orc.recurrent_fwd(q, k, v, g, scale, initial_state=S0, reverse=rev)
+        m = 23
+        first = slice(m, None) if rev else slice(0, m)
+        second = slice(0, m) if rev else slice(m, None)
+        o1, fs1 = orc.recurrent_fwd(q[:, first], k[:, first], v[:, first], g, scale,
+                                    initial_state=S0, reverse=rev)
+        o2, fs2 = orc.recurrent_fwd(q[:, second], k[:, second], v[:, second], g, scale,
+                                    initial_state=fs1.astype(np.float32), reverse=rev)
+        # the hand-over state passes through float32, so allow its rounding
+        _close(o[:, first], o1, 1e-12, "chained o (first part)")
+        _close(o[:, second], o2, 1e-6, "chained o (second part)")
+        _close(fs, fs2, 1e-6, "chained final_state")
+
+
+# -- pin (d): reverse is the forward run on the flipped sequence ----------------
+def pin_reverse_flip(orc):
+    q, k, v, g, S0, scale = _rand_case(41, 2, 29, 4, 4, 5, 7, True)
+    o_r, fs_r = orc.recurrent_fwd(q, k, v, g, scale, initial_state=S0, reverse=True)
+    fl = lambda x: np.ascontiguousarray(x[:, ::-1])
+    o_f, fs_f = orc.recurrent_fwd(fl(q), fl(k), fl(v), g, scale, initial_state=S0)
+    assert np.array_equal(o_r, o_f[:, ::-1]), "reverse != flip(forward(flip))"
+    assert np.array_equal(fs_r, fs_f), "reverse final_state != forward on flipped"
+
+
+# -- pin (e): packed varlen equals per-sequence runs -----------------------------
+def pin_packed(orc):
+    rng = np.random.Generator(np.random.PCG64(51))
+    lens = [5, 0, 17, 1, 30]
+    T = sum(lens)
+    H, Hkv, dk, dv = 4, 2, 6, 3
+    q = rng.standard_normal((T, H, dk)).astype(np.float32)
+    k = rng.standard_normal((T, Hkv, dk)).astype(np.float32)
+    v = rng.standard_normal((T, Hkv, dv)).astype(np.float32)
+    g = -rng.uniform(0, 1.5, H).astype(np.float32)
+    S0 = rng.standard_normal((len(lens), H, dk, dv)).astype(np.float32)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    for rev in (False, True):
+        o, fs = orc.recurrent_fwd(q, k, v, g, 0.7, initial_state=S0, reverse=rev, cu_seqlens=cu)
+        assert o.shape == (T, H, dv) and fs.shape == (len(lens), H, dk, dv)
+        for n, L in enumerate(lens):
+            a, b = cu[n], cu[n + 1]
+            if L == 0:
+                assert np.array_equal(fs[n], S0[n].astype(np.float64)), "empty sequence state"
+                continue
+            o_n, fs_n = orc.recurrent_fwd(q[None, a:b], k[None, a:b], v[None, a:b], g, 0.7,
+                                          initial_state=S0[n:n + 1], reverse=rev)
+            assert np.array_equal(o[a:b], o_n[0]), f"packed o, sequence {n}"
+            assert np.array_equal(fs[n], fs_n[0]), f"packed final_state, sequence {n}"
+
+
+# -- pin (f): the pages' all-ones examples --------------------------------------
+def _geom(lam, n):
+    """sum_{i<n} lam^i, with the lam == 1 limit."""
+    n = np.asarray(n, dtype=np.float64)
+    if lam == 1.0:
+        return n
+    return (1.0 - lam ** n) / (1.0 - lam)
+
+
+def pin_lightning_ones(orc):
+    ex = golden()["lightning_ones"]
+    B, T, H, d = ex["input_shape"]
+    ones = np.ones((B, T, H, d), np.float32)
+    o, fs = orc.lightning_attn(ones, ones, ones, ex["layer_idx"], ex["num_layers"])
+    assert o.shape == (B, T, H, d) and fs.shape == (B, H, d, d)
+    g = orc.lightning_g_gamma(H, ex["layer_idx"], ex["num_layers"])
+    scale = float(np.float32(d ** -0.5))
+    t = np.arange(T)
+    for h in range(H):
+        lam = float(np.exp(np.float64(g[h])))
+        want = scale * d * _geom(lam, t + 1)  # every q.k_s = d, every v entry 1
+        _close(o[:, :, h, :], np.broadcast_to(want[None, :, None], (B, T, d)), 1e-10,
+               f"ones o, head {h}")
+        _close(fs[:, h], np.full((B, d, d), _geom(lam, T)), 1e-10, f"ones state, head {h}")
+    # head 0 has no decay: o_t = 8 (t + 1) exactly, state entries = T
+    assert np.array_equal(o[:, :, 0, :], np.broadcast_to((8.0 * (t + 1))[None, :, None], (B, T, d)))
+    assert np.all(fs[:, 0] == float(T))
+
+
+def pin_recurrent_examples(orc):
+    gd = golden()
+    ex = gd["recurrent_ones"]
+    B, T, H, d = ex["input_shape"]
+    ones = np.ones((B, T, H, d), np.float32)
+    scale = float(np.float32(d ** -0.5))
+    o, fs = orc.recurrent_fwd(ones, ones, ones, np.zeros(H, np.float32), scale)
+    assert list(o.shape) == ex["printed_output_shape"]
+    t = np.arange(T)
+    assert np.array_equal(o, np.broadcast_to((8.0 * (t + 1))[None, :, None, None], o.shape))
+    # per-head decay -0.1 h
+    ex = gd["recurrent_g_gamma"]
+    g = (np.float32(ex["g_gamma_step"]) * np.arange(H, dtype=np.float32)).astype(np.float32)
+    o, fs = orc.recurrent_fwd(ones, ones, ones, g, scale)
+    for h in range(H):
+        lam = float(np.exp(np.float64(g[h])))
+        _close(o[:, :, h], np.broadcast_to((scale * d * _geom(lam, t + 1))[None, :, None],
+                                           (B, T, d)), 1e-10, f"g_gamma example head {h}")
+    # packed: the state restarts at every boundary
+    ex = gd["recurrent_varlen"]
+    Tp, H, d = ex["input_shape"]
+    ones = np.ones((Tp, H, d), np.float32)
+    cu = np.asarray(ex["cu_seqlens"])
+    o, fs = orc.recurrent_fwd(ones, ones, ones, np.zeros(H, np.float32), scale, cu_seqlens=cu)
+    assert list(o.shape) == ex["printed_output_shape"]
+    assert list(fs.shape) == ex["printed_final_state_shape"]
+    local = np.concatenate([np.arange(b - a) for a, b in zip(cu[:-1], cu[1:])])
+    assert np.array_equal(o, np.broadcast_to((8.0 * (local + 1))[:, None, None], o.shape))
+    assert np.all(fs == 50.0)
+
+
+# -- decay schedule of the lightning_attn wrapper --------------------------------
+def pin_g_gamma(orc):
+    # layer 0: coefficient -(8 / H), exact in float32 for these H
+    assert np.array_equal(orc.lightning_g_gamma(8, 0, 12), -np.arange(8, dtype=np.float32))
+    assert np.array_equal(orc.lightning_g_gamma(32, 0, 12),
+                          -0.25 * np.arange(32, dtype=np.float32))
+    # last layer: no decay anywhere
+    assert np.all(orc.lightning_g_gamma(16, 12, 12) == 0.0)
+    # head 0 never decays, and its value is a negative zero when the coefficient is negative
+    g = orc.lightning_g_gamma(8, 5, 12)
+    assert g[0] == 0.0 and np.signbit(g[0])
+    # H = 8, layer 5 of 12: coefficient -(1 - 5/12) = -7/12 rounded to float32,
+    # then float32 products with the head index
+    c = np.float32(-7.0 / 12.0)
+    assert g[1] == c
+    assert g[2] == np.float32(2.0) * c and g[4] == np.float32(4.0) * c
+    # coefficient rounded to float32 first, product in float32 (JAX weak typing):
+    # head 5 is -2.9166665 (0xc03aaaaa); a float64 product would give -2.9166667
+    assert g[5].view(np.uint32) == 0xC03AAAAA and g[7].view(np.uint32) == 0xC082AAAA
+    assert np.all(np.diff(g) < 0), "decay grows with the head index"
+    # decay is strictly weaker for deeper layers
+    assert np.all(orc.lightning_g_gamma(8, 9, 12)[1:] > g[1:])
+
+
+def pin_pairs(orc):
+    """Computing a subset of (sequence, head) pairs gives the same values."""
+    q, k, v, g, S0, scale = _rand_case(61, 2, 21, 4, 2, 4, 4, True)
+    o, fs = orc.recurrent_fwd(q, k, v, g, scale, initial_state=S0)
+    pairs = [(0, 1), (1, 3)]
+    o_p, fs_p = orc.recurrent_fwd(q, k, v, g, scale, initial_state=S0, pairs=pairs)
+    for n, h in pairs:
+        assert np.array_equal(o_p[n, :, h], o[n, :, h]) and np.array_equal(fs_p[n, h], fs[n, h])
+    assert np.isnan(o_p[0, :, 0]).all()
+
+
+ALL_PINS = [pin_brute_force, pin_bf16_words, pin_no_decay, pin_chaining, pin_reverse_flip,
+            pin_packed, pin_lightning_ones, pin_recurrent_examples, pin_g_gamma, pin_pairs]

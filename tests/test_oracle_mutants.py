@@ -1,0 +1,62 @@
+"""The oracle pins catch plausible mistakes.
+
+Each case plants one mistake in a copy of the oracle's C source (on the CPU,
+in a temporary directory), builds it, and checks that at least one pin fails.
+The real oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from oracle.build import SRC, build
+from tests import oracle_pins
+
+MUTANTS = {
+    "decay_after_add": ("lam * S[(int64_t)a * dv + c] + kt[a] * vt[c]",
+                        "lam * (S[(int64_t)a * dv + c] + kt[a] * vt[c])"),
+    "no_decay": ("lam * S[(int64_t)a * dv + c] + kt[a] * vt[c]",
+                 "S[(int64_t)a * dv + c] + kt[a] * vt[c]"),
+    "inverse_decay": ("exp((double)g_gamma[h])", "exp(-(double)g_gamma[h])"),
+    "q_for_k": ("out_row[c] += qt[a] * S", "out_row[c] += kt[a] * S"),
+    "k_for_q": ("lam * S[(int64_t)a * dv + c] + kt[a] * vt[c]",
+                "lam * S[(int64_t)a * dv + c] + qt[a] * vt[c]"),
+    "kv_head_modulo": ("const int kvh = h / group;", "const int kvh = h % num_kv_heads;"),
+    "no_scale": ("= scale * out_row[c]", "= out_row[c]"),
+    "scale_twice": ("= scale * out_row[c]", "= scale * scale * out_row[c]"),
+    "ignore_reverse": ("reverse ? row0 + len - 1 - step : row0 + step", "row0 + step"),
+    "ignore_initial_state": ("initial_state ? (double)initial_state[st_base + i] : 0.0", "0.0"),
+    "varlen_from_row0": ("row0 = cu_seqlens[n];", "row0 = 0;"),
+    "gamma_plus": ("(1.0 - (double)layer_idx / (double)num_layers)",
+                   "(1.0 + (double)layer_idx / (double)num_layers)"),
+    "gamma_head_offset": ("volatile float hv = (float)h;", "volatile float hv = (float)(h + 1);"),
+    "gamma_fp64_product": ("out[h] = coef32 * hv;", "out[h] = (float)(coef * (double)hv);"),
+    "bf16_low_half": ("<< 16;", "<< 0;"),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as f:
+        return f.read()
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, source, name):
+    old, new = MUTANTS[name]
+    assert source.count(old) == 1, f"mutation site for {name} not found exactly once"
+    src = os.path.join(tmp_path, "mutant.c")
+    with open(src, "w") as f:
+        f.write(source.replace(old, new))
+    lib = build(src, os.path.join(tmp_path, "libmutant.so"))
+    orc = oracle.load(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin catches the mutant {name}"
