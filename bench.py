@@ -1,0 +1,186 @@
+#!/usr/bin/env python3
+"""Forward-pass throughput of Lightning attention on one MI355X.
+
+Workload: B=4, H=Hkv=32, dk=dv=128, N=32768 tokens per row, bf16 q/k/v, fp32 o and
+final state, decay schedule of layer 0 of 12, no initial state, forward direction.
+A step is one lattn_fwd call over the whole batch with inputs already in HBM.
+
+Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
+  roofline      achieved HBM GB/s of the forward kernel (algorithmic bytes / mean
+                kernel time from HIP events on the launch stream) against 8 TB/s,
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd tokens/s at B4 H32 d128 bf16 N=32K; % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0
+# Lightning2 forward at B4 H32 d128 bf16 n=32768 from the OpenNLPLab lightning-attention
+# README benchmark table (hardware unstated, time read as milliseconds): 17.661427 ms.
+PAGE_LIGHTNING2_MS = 17.661427
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_b4_h32_d128_n32768.json")
+KERNEL_SRC = os.path.join(ROOT, "decayed_recurrent_attention_amd", "csrc", "lattn_kernels.hip")
+
+
+def algorithmic_bytes(B, T, H, Hkv, dk, dv, in_bytes, with_init=False):
+    """Bytes the forward must move at least once: q, k, v in, o (fp32) out, final state out."""
+    qkv = B * T * (H * dk + Hkv * dk + Hkv * dv) * in_bytes
+    o = B * T * H * dv * 4
+    state = B * H * dk * dv * 4 * (2 if with_init else 1)
+    return qkv + o + state
+
+
+def kernel_sha() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from committed counter runs, if they match this kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_sha") != kernel_sha():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, data, seconds_target: float):
+    """Time the oracle on a bounded set of (batch row, head) pairs of the workload."""
+    import oracle
+
+    orc = oracle.load()
+    threads = orc.set_threads(0)
+    n_pairs = max(1, min(w.batch * w.num_heads, 2 * threads))
+    pairs = [(i % w.batch, (i * 7) % w.num_heads) for i in range(n_pairs)]
+    pairs = list(dict.fromkeys(pairs))
+    g = orc.lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers)
+    t0 = time.perf_counter()
+    orc.recurrent_fwd(data["q"], data["k"], data["v"], g, w.scale, pairs=pairs)
+    dt = time.perf_counter() - t0
+    frac = len(pairs) / (w.batch * w.num_heads)
+    return {
+        "value": w.batch * w.seqlen * frac / dt,
+        "unit": "tokens/s",
+        "cores": min(threads, len(pairs)),
+        "kind": "oracle",
+        "sample": f"{len(pairs)} of {w.batch * w.num_heads} (batch row, head) pairs over all "
+                  f"{w.seqlen} tokens, fp64, {dt:.1f} s wall; tokens/s scaled by the pair fraction",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seqlen", type=int, default=32768)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a 1 GiB device copy (counter calibration for traffic)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the forward pass has no multi-GPU path "
+              "(pass --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from decayed_recurrent_attention_amd import inputs, lattn
+
+    w = inputs.long_d128(seqlen=args.seqlen)
+    B, T, H, Hkv, dk, dv = w.batch, w.seqlen, w.num_heads, w.num_kv_heads, w.dk, w.dv
+    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    data = w.make()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = to_dev(data["q"]), to_dev(data["k"]), to_dev(data["v"])
+    g = torch.from_numpy(lattn.lattn_lightning_g_gamma(H, w.layer_idx, w.num_layers)).to(dev)
+    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+    fs = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+    prob = lattn.LattnProblem(B, T, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        rc = lattn.lattn_fwd(prob, q, k, v, g, w.scale, None, False, None, o, fs,
+                             stream=stream.cuda_stream)
+        if rc != lattn.LATTN_OK:
+            raise lattn.LattnError(rc)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    ms_per_step = 1000.0 * wall / args.steps
+    mean_kernel_ms = sum(kernel_ms) / len(kernel_ms)
+    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel mean "
+          f"{mean_kernel_ms:.4f} ms min {min(kernel_ms):.4f} max {max(kernel_ms):.4f}",
+          file=sys.stderr, flush=True)
+
+    if args.copy_probe:
+        src = torch.empty(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    alg = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2)
+    achieved = alg / (mean_kernel_ms * 1e-3) / 1e9
+    value = B * T / (ms_per_step * 1e-3)
+    page_tok_s = 4 * 32768 / (PAGE_LIGHTNING2_MS * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": (value / page_tok_s) if T == 32768 else None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"lightning_attn_fwd_b{B}_h{H}_d{dk}_n{T}_bf16", "batch": B,
+                   "seq_len": T, "num_heads": H, "num_kv_heads": Hkv, "head_dim_qk": dk,
+                   "head_dim_v": dv, "layer_idx": w.layer_idx, "num_layers": w.num_layers,
+                   "out_dtype": "f32", "reverse": False, "initial_state": False},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
+                     "algorithmic_bytes": alg, "kernel_ms": mean_kernel_ms},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, data, 10.0)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

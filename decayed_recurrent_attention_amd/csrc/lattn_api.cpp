@@ -1,0 +1,177 @@
+// C ABI of liblattn.so: argument validation, kernel selection and launch.
+// Every check that needs no GPU runs before the first HIP call, so argument
+// errors are reported identically on machines without a device.
+#include <atomic>
+#include <initializer_list>
+#include <climits>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "lattn.h"
+#include "lattn_launch.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+// Per device: 0 = not checked yet, 1 = gfx950, -1 = other.
+std::atomic<int> g_device_ok[kMaxDevices];
+
+bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
+
+bool is_varlen(const lattn_problem& p) { return p.num_seqs > 0; }
+
+int num_seqs_of(const lattn_problem& p) { return is_varlen(p) ? p.num_seqs : p.batch; }
+
+// Shape/dtype checks that do not look at pointers.
+int check_problem(const lattn_problem& p) {
+    if (p.batch < 1 || p.seqlen < 0 || p.num_heads < 1 || p.num_kv_heads < 1 || p.head_dim_qk < 1 ||
+        p.head_dim_v < 1 || p.num_seqs < 0)
+        return LATTN_ERR_INVALID_ARG;
+    if (p.num_heads % p.num_kv_heads != 0) return LATTN_ERR_HEADS;
+    if (is_varlen(p) && p.batch != 1) return LATTN_ERR_VARLEN_BATCH;
+    if (p.in_dtype != LATTN_BF16 && p.in_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
+    if (p.out_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
+    if (p.head_dim_v % 16 != 0 || p.head_dim_v > 256) return LATTN_ERR_UNSUPPORTED;
+    bool any = false;
+    for (int nw : {1, 2, 4})
+        any = any || (lattn::have_fwd_kernel(p.in_dtype, p.head_dim_qk, nw) && (p.head_dim_v / 16) % nw == 0);
+    if (!any) return LATTN_ERR_UNSUPPORTED;
+    return LATTN_OK;
+}
+
+// Workgroup width (waves) for a problem: the widest value block (fewer re-reads of
+// Q and K) that still yields at least one workgroup per compute unit; small
+// problems fall back to narrower blocks for more parallel workgroups.
+int choose_nw(const lattn_problem& p) {
+    const int units = p.head_dim_v / 16;
+    auto usable = [&](int nw) { return units % nw == 0 && lattn::have_fwd_kernel(p.in_dtype, p.head_dim_qk, nw); };
+    if (const char* env = std::getenv("LATTN_NW")) {
+        const int want = std::atoi(env);
+        if ((want == 1 || want == 2 || want == 4) && usable(want)) return want;
+    }
+    const int64_t heads = (int64_t)num_seqs_of(p) * p.num_heads;
+    int narrowest = 0;
+    for (int nw : {4, 2, 1}) {
+        if (!usable(nw)) continue;
+        if (heads * (units / nw) >= 256) return nw;
+        narrowest = nw;
+    }
+    return narrowest;
+}
+
+int device_check() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return LATTN_ERR_DEVICE;
+    if (dev < kMaxDevices) {
+        const int known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known != 0) return known > 0 ? LATTN_OK : LATTN_ERR_DEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LATTN_ERR_DEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices) g_device_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? LATTN_OK : LATTN_ERR_DEVICE;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int lattn_abi_version(void) { return 1; }
+
+const char* lattn_status_string(int status) {
+    switch (status) {
+        case LATTN_OK: return "success";
+        case LATTN_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or misaligned buffer)";
+        case LATTN_ERR_VARLEN_BATCH: return "batch size must be 1 when cu_seqlens is given";
+        case LATTN_ERR_HEADS: return "num_heads must be a multiple of num_kv_heads";
+        case LATTN_ERR_UNSUPPORTED: return "unsupported head dimension or dtype";
+        case LATTN_ERR_WORKSPACE: return "workspace missing or too small";
+        case LATTN_ERR_LAUNCH: return "kernel launch failed";
+        case LATTN_ERR_DEVICE: return "no usable gfx950 device";
+        default: return "unknown status";
+    }
+}
+
+size_t lattn_fwd_workspace_size(const lattn_problem* p) {
+    if (p == nullptr || check_problem(*p) != LATTN_OK || !is_varlen(*p)) return 0;
+    if (p->num_seqs > lattn::kMaxOrderedSeqs) return 0;
+    return round_up((size_t)p->num_seqs * sizeof(int32_t), 256);
+}
+
+int lattn_lightning_g_gamma(int num_heads, int layer_idx, int num_layers, float* out_host) {
+    if (num_heads < 1 || num_layers < 1 || layer_idx < 0 || layer_idx > num_layers || out_host == nullptr)
+        return LATTN_ERR_INVALID_ARG;
+    // Coefficient in double (a Python float on the page), rounded to float32; the
+    // product with the float32 head index is a float32 product.
+    const double coef = -(8.0 / (double)num_heads * (1.0 - (double)layer_idx / (double)num_layers));
+    const float coef32 = (float)coef;
+    for (int h = 0; h < num_heads; ++h) {
+        volatile float hv = (float)h;
+        out_host[h] = coef32 * hv;
+    }
+    return LATTN_OK;
+}
+
+int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* v, const float* g_gamma,
+              float scale, const float* initial_state, int reverse, const int32_t* cu_seqlens, void* o,
+              float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    if (p == nullptr) return LATTN_ERR_INVALID_ARG;
+    const int rc = check_problem(*p);
+    if (rc != LATTN_OK) return rc;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen != is_varlen(*p)) return LATTN_ERR_INVALID_ARG;
+    const int64_t tokens = (int64_t)p->batch * p->seqlen;
+    if (tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr))
+        return LATTN_ERR_INVALID_ARG;
+    if (g_gamma == nullptr || final_state == nullptr) return LATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g_gamma, 4) ||
+        !aligned(final_state, 16) || !aligned(initial_state, 16) || !aligned(cu_seqlens, 4) ||
+        !aligned(workspace, 4))
+        return LATTN_ERR_INVALID_ARG;
+    const size_t need = lattn_fwd_workspace_size(p);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LATTN_ERR_WORKSPACE;
+
+    const int nw = choose_nw(*p);
+    lattn::FwdParams fp;
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
+    fp.g_gamma = g_gamma;
+    fp.init = initial_state;
+    fp.cu = cu_seqlens;
+    fp.order = (varlen && need > 0) ? static_cast<const int32_t*>(workspace) : nullptr;
+    fp.o = static_cast<float*>(o);
+    fp.final_state = final_state;
+    fp.batch = p->batch;
+    fp.seqlen = p->seqlen;
+    fp.num_heads = p->num_heads;
+    fp.num_kv_heads = p->num_kv_heads;
+    fp.dk = p->head_dim_qk;
+    fp.dv = p->head_dim_v;
+    fp.num_seqs = num_seqs_of(*p);
+    fp.nvb = p->head_dim_v / (16 * nw);
+    if ((int64_t)fp.num_seqs * p->num_kv_heads > INT_MAX) return LATTN_ERR_INVALID_ARG;
+    fp.num_groups = fp.num_seqs * p->num_kv_heads;
+    fp.group_size = (p->num_heads / p->num_kv_heads) * fp.nvb;
+    fp.scale = scale;
+    const int64_t grid = (int64_t)lattn::kNumXcd * ((fp.num_groups + lattn::kNumXcd - 1) / lattn::kNumXcd) *
+                         fp.group_size;
+    if (grid > INT_MAX) return LATTN_ERR_INVALID_ARG;
+
+    const int dc = device_check();
+    if (dc != LATTN_OK) return dc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fp.order != nullptr) {
+        if (lattn::launch_seq_order(cu_seqlens, fp.num_seqs, p->seqlen, const_cast<int32_t*>(fp.order), s) !=
+            hipSuccess)
+            return LATTN_ERR_LAUNCH;
+    }
+    if (lattn::launch_fwd(fp, p->in_dtype, nw, reverse != 0, s) != hipSuccess) return LATTN_ERR_LAUNCH;
+    return LATTN_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,804 @@
+// Chunked forward kernels for Lightning (decayed recurrent) attention on gfx950.
+//
+// The recurrence (ejkernel "recurrent" interface page, docstring "The core update
+// is"), per sequence and query head with lam = exp(g):
+//     S_t = lam S_{t-1} + k_t^T v_t,      o_t = scale * q_t S_t.
+// Unrolled over a chunk of C tokens with local rows i, j = 0..Lc-1 and S the state
+// entering the chunk, it is exactly
+//     O   = scale * [ ((Q K^T) .* M) V  +  diag(lam^(i+1)) (Q S) ],  M_ij = lam^(i-j) (j <= i)
+//     S'  = lam^Lc S + (diag(lam^(Lc-1-j)) K)^T V.
+// The intra-chunk term and both state products are dense contractions and run on
+// MFMA; only non-negative powers of lam are ever formed, so fast decays underflow
+// to zero instead of overflowing, and lam = 1 (g = 0, no decay) is exact.
+//
+// Work decomposition: one workgroup per (sequence, query head, block of BV = 16*NW
+// value columns).  Value columns are independent (column c of S only sees column c
+// of V), so the state block S[:, BV] lives in MFMA accumulator registers for the
+// whole sequence: wave w owns columns [16w, 16w+16).  Each chunk of Q, K, V is
+// staged through LDS: Q and K row-major for the QK^T and Q S products, K
+// (pre-multiplied by its decay) and V transposed, so the token index is contiguous
+// for the products that contract over tokens.  Global loads of chunk c+1 are in
+// flight while chunk c is computed.
+//
+// Two layout facts of the 16x16 MFMA shapes make accumulators reusable as
+// operands without an LDS round trip: an output tile gives lane l column l%16 and
+// rows 4*(l/16)+{0..3}, while an A (B) operand gives lane l row (column) l%16 and
+// eight k values that only have to be paired the same way in A and B.  Hence
+//   * the state tile pair (2kb, 2kb+1), converted to bf16 hi + lo, is directly the
+//     B operand of Q S for dk block kb, provided the state's dk rows are mapped by
+//     dmap() below so that they line up with Q's natural 8 consecutive dk values;
+//   * a (K Q^T) output tile pair, masked and converted, is directly the A operand
+//     of P V, with V read in the matching token order.
+// The state is kept in fp32 and fed to the Q S product as bf16 hi + lo (two MFMAs)
+// so that its rounding does not reach the output; o and the states are fp32.
+#include "lattn_launch.h"
+
+namespace lattn {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLdsBudget = 160 * 1024;
+
+// One unit of work, decoded from the workgroup id.
+struct Work {
+    int n;          // sequence (batch row, or packed sequence)
+    int h;          // query head
+    int kvh;        // kv head read by h
+    int vb;         // value block
+    int64_t start;  // first token row of the sequence in the flattened [B*T] axis
+    int64_t len;    // tokens in the sequence
+};
+
+// Workgroup id -> work.  Groups are (sequence rank, kv head); the workgroups of one
+// group (its query heads x value blocks, which re-read the same K and V, and per
+// head the same Q) get ids that are equal mod kNumXcd, so they share one L2.
+// Consecutive groups go to consecutive dies; with sequences ranked longest first,
+// each die receives its longest work first.
+__device__ inline bool decode_work(const FwdParams& p, Work& w) {
+    const int id = blockIdx.x;
+    const int x = id % kNumXcd;
+    const int slot = id / kNumXcd;
+    const int g = (slot / p.group_size) * kNumXcd + x;
+    if (g >= p.num_groups) return false;
+    const int j = slot % p.group_size;
+    const int rank = g / p.num_kv_heads;
+    w.kvh = g % p.num_kv_heads;
+    w.n = p.order ? p.order[rank] : rank;
+    w.h = w.kvh * (p.num_heads / p.num_kv_heads) + j / p.nvb;
+    w.vb = j % p.nvb;
+    if (p.cu) {
+        int64_t a = p.cu[w.n];
+        int64_t e = p.cu[w.n + 1];
+        a = min(max(a, (int64_t)0), (int64_t)p.seqlen);
+        e = min(max(e, a), (int64_t)p.seqlen);
+        w.start = a;
+        w.len = e - a;
+    } else {
+        w.start = (int64_t)w.n * p.seqlen;
+        w.len = p.seqlen;
+    }
+    return true;
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline float bf16_half(uint32_t w, int hi) { return hi ? bf16_hi(w) : bf16_lo(w); }
+__device__ inline uint32_t half16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
+
+__device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ inline T lds_load(const void* p) {
+    return *reinterpret_cast<const T*>(p);
+}
+template <typename T>
+__device__ inline void lds_store(void* p, T v) {
+    *reinterpret_cast<T*>(p) = v;
+}
+
+// Index of (K Q^T) tile (a, b), a <= b, among the 10 lower-triangle tiles of a chunk.
+__host__ __device__ constexpr int tidx(int a, int b) { return b * (b + 1) / 2 + a; }
+
+// dk index of row m of state tile mt (bf16 path): tiles 2kb and 2kb+1 interleave in
+// groups of four so that lane group g of the tile pair holds dk 32kb + 8g + 0..7.
+__host__ __device__ constexpr int dmap(int mt, int m) {
+    return 32 * (mt >> 1) + 8 * (m >> 2) + 4 * (mt & 1) + (m & 3);
+}
+
+// Per-lane decay factors that do not depend on the chunk: the causal mask of the
+// ten (K Q^T) tiles and lam^(i+1) for this lane's output rows.
+struct LaneDecay {
+    float mask[10][4];
+    float lamq[4][4];
+};
+
+__device__ inline void make_lane_decay(float g2, int lr, int lg, LaneDecay& d) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+#pragma unroll
+        for (int a = 0; a <= b; ++a) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int j = 16 * a + 4 * lg + ii;
+                const int i = 16 * b + lr;
+                d.mask[tidx(a, b)][ii] = (j <= i) ? exp2f(g2 * (float)(i - j)) : 0.f;
+            }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) d.lamq[b][ii] = exp2f(g2 * (float)(16 * b + 4 * lg + ii + 1));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 inputs: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
+// ---------------------------------------------------------------------------
+template <int DK, int NW>
+struct Bf16Cfg {
+    static constexpr int BV = 16 * NW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int QLD = DK + 8;       // Q/K row stride in LDS (elements); +16 B breaks bank aliasing
+    static constexpr int TLD = kChunk + 8;   // K^T / V^T row stride in LDS (elements)
+    static constexpr int Q_ELEMS = kChunk * QLD;
+    static constexpr int KT_ELEMS = DK * TLD;
+    static constexpr int VT_ELEMS = BV * TLD;
+    static constexpr int STAGE_ELEMS = 2 * Q_ELEMS + KT_ELEMS + VT_ELEMS;
+    static constexpr int STAGES = (2 * STAGE_ELEMS * 2 <= kLdsBudget) ? 2 : 1;
+    static constexpr int KB = DK / 32;       // dk blocks of one MFMA
+    static constexpr int MT = DK / 16;       // state row tiles
+    static constexpr int QITEMS = kChunk * DK / 8;          // 16-byte pieces of a Q chunk
+    static constexpr int KITEMS = (kChunk / 4) * (DK / 8);  // 4-token x 8-dk blocks of K
+    static constexpr int VITEMS = (kChunk / 4) * (BV / 8);  // 4-token x 8-column blocks of V
+    static constexpr int QPER = (QITEMS + NT - 1) / NT;
+    static constexpr int KPER = (KITEMS + NT - 1) / NT;
+    static constexpr int VPER = (VITEMS + NT - 1) / NT;
+    static_assert(DK % 32 == 0 && DK <= 256, "dk must be a multiple of 32 up to 256");
+    static_assert(STAGES * STAGE_ELEMS * 2 <= kLdsBudget, "LDS budget");
+};
+
+template <int KB>
+__device__ inline void split_state(const f32x4* S, bf16x8* hi, bf16x8* lo) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const float s[8] = {S[2 * kb][0],     S[2 * kb][1],     S[2 * kb][2],     S[2 * kb][3],
+                            S[2 * kb + 1][0], S[2 * kb + 1][1], S[2 * kb + 1][2], S[2 * kb + 1][3]};
+        u32x4 h, l;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const uint32_t w = pack_bf16x2(s[2 * e], s[2 * e + 1]);
+            h[e] = w;
+            l[e] = pack_bf16x2(s[2 * e] - bf16_lo(w), s[2 * e + 1] - bf16_hi(w));
+        }
+        hi[kb] = __builtin_bit_cast(bf16x8, h);
+        lo[kb] = __builtin_bit_cast(bf16x8, l);
+    }
+}
+
+template <int DK, int NW, bool REV>
+__global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p) {
+    using Cfg = Bf16Cfg<DK, NW>;
+    constexpr int BV = Cfg::BV, NT = Cfg::NT, QLD = Cfg::QLD, TLD = Cfg::TLD;
+    constexpr int KB = Cfg::KB, MT = Cfg::MT;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::STAGES * Cfg::STAGE_ELEMS];
+
+    Work wk;
+    if (!decode_work(p, wk)) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const float g2 = p.g_gamma[wk.h] * kLog2e;
+    const int64_t L = wk.len;
+    const int nch = (int)((L + kChunk - 1) / kChunk);
+    const int H = p.num_heads, dv = p.dv;
+    const int vcol = wk.vb * BV + 16 * wv + lr;  // this lane's value column
+
+    const uint16_t* qbase = static_cast<const uint16_t*>(p.q) + (int64_t)wk.h * DK;
+    const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + (int64_t)wk.kvh * DK;
+    const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + (int64_t)wk.kvh * dv + wk.vb * BV;
+    const int64_t qstride = (int64_t)H * DK;
+    const int64_t kstride = (int64_t)p.num_kv_heads * DK;
+    const int64_t vstride = (int64_t)p.num_kv_heads * dv;
+    auto tok_row = [&](int64_t pos) -> int64_t { return REV ? wk.start + L - 1 - pos : wk.start + pos; };
+
+    LaneDecay dec;
+    make_lane_decay(g2, lr, lg, dec);
+    const float lamC = exp2f(g2 * (float)kChunk);
+
+    // State block: tile mt holds rows dmap(mt, 4*lg + ii), column vcol.
+    f32x4 S[MT];
+    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            S[mt][ii] = p.init ? p.init[st_off + (int64_t)dmap(mt, 4 * lg + ii) * dv + vcol] : 0.f;
+    bf16x8 Shi[KB], Slo[KB];
+    split_state<KB>(S, Shi, Slo);
+
+    // ---- staging: global -> registers (prefetch) -> LDS ----
+    u32x4 pq[Cfg::QPER];
+    u32x4 pk[Cfg::KPER][4];
+    u32x4 pv[Cfg::VPER][4];
+    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+
+    auto load_chunk = [&](int c) {
+        const int64_t p0 = (int64_t)c * kChunk;
+#pragma unroll
+        for (int s = 0; s < Cfg::QPER; ++s) {
+            const int item = tid + s * NT;
+            pq[s] = zero4;
+            if (item < Cfg::QITEMS) {
+                const int r = item / (DK / 8), c8 = item % (DK / 8);
+                if (p0 + r < L) pq[s] = *reinterpret_cast<const u32x4*>(qbase + tok_row(p0 + r) * qstride + c8 * 8);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::KPER; ++s) {
+            const int item = tid + s * NT;
+            const int tg = item / (DK / 8), c8 = item % (DK / 8);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pk[s][u] = zero4;
+                if (item < Cfg::KITEMS && p0 + 4 * tg + u < L)
+                    pk[s][u] = *reinterpret_cast<const u32x4*>(kbase + tok_row(p0 + 4 * tg + u) * kstride + c8 * 8);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::VPER; ++s) {
+            const int item = tid + s * NT;
+            const int tg = item / (BV / 8), c8 = item % (BV / 8);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pv[s][u] = zero4;
+                if (item < Cfg::VITEMS && p0 + 4 * tg + u < L)
+                    pv[s][u] = *reinterpret_cast<const u32x4*>(vbase + tok_row(p0 + 4 * tg + u) * vstride + c8 * 8);
+            }
+        }
+    };
+
+    auto store_chunk = [&](int c, uint16_t* st) {
+        uint16_t* Qs = st;
+        uint16_t* Ks = st + Cfg::Q_ELEMS;
+        uint16_t* Kt = Ks + Cfg::Q_ELEMS;
+        uint16_t* Vt = Kt + Cfg::KT_ELEMS;
+        const int Lc = (int)min((int64_t)kChunk, L - (int64_t)c * kChunk);
+#pragma unroll
+        for (int s = 0; s < Cfg::QPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::QITEMS) {
+                const int r = item / (DK / 8), c8 = item % (DK / 8);
+                lds_store<u32x4>(Qs + r * QLD + c8 * 8, pq[s]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::KPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::KITEMS) {
+                const int tg = item / (DK / 8), c8 = item % (DK / 8);
+                float wgt[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    lds_store<u32x4>(Ks + (4 * tg + u) * QLD + c8 * 8, pk[s][u]);
+                    const int tok = 4 * tg + u;
+                    wgt[u] = tok < Lc ? exp2f(g2 * (float)(Lc - 1 - tok)) : 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float k0 = bf16_half(pk[s][0][e >> 1], e & 1) * wgt[0];
+                    const float k1 = bf16_half(pk[s][1][e >> 1], e & 1) * wgt[1];
+                    const float k2 = bf16_half(pk[s][2][e >> 1], e & 1) * wgt[2];
+                    const float k3 = bf16_half(pk[s][3][e >> 1], e & 1) * wgt[3];
+                    const u32x2 val = {pack_bf16x2(k0, k1), pack_bf16x2(k2, k3)};
+                    lds_store<u32x2>(Kt + (c8 * 8 + e) * TLD + 4 * tg, val);
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::VPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::VITEMS) {
+                const int tg = item / (BV / 8), c8 = item % (BV / 8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t v0 = half16(pv[s][0][e >> 1], e & 1), v1 = half16(pv[s][1][e >> 1], e & 1);
+                    const uint32_t v2 = half16(pv[s][2][e >> 1], e & 1), v3 = half16(pv[s][3][e >> 1], e & 1);
+                    const u32x2 val = {v0 | (v1 << 16), v2 | (v3 << 16)};
+                    lds_store<u32x2>(Vt + (c8 * 8 + e) * TLD + 4 * tg, val);
+                }
+            }
+        }
+    };
+
+    auto compute_chunk = [&](int c, const uint16_t* st) {
+        const uint16_t* Qs = st;
+        const uint16_t* Ks = st + Cfg::Q_ELEMS;
+        const uint16_t* Kt = Ks + Cfg::Q_ELEMS;
+        const uint16_t* Vt = Kt + Cfg::KT_ELEMS;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 O[4], At[10];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) O[b] = z;
+#pragma unroll
+        for (int t = 0; t < 10; ++t) At[t] = z;
+
+        // A^T = K Q^T (lower-triangle tiles) and Q S, sharing the Q operands.
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            bf16x8 qa[4], ka[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                qa[r] = lds_load<bf16x8>(Qs + (16 * r + lr) * QLD + 32 * kb + 8 * lg);
+                ka[r] = lds_load<bf16x8>(Ks + (16 * r + lr) * QLD + 32 * kb + 8 * lg);
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+#pragma unroll
+                for (int a = 0; a <= b; ++a) At[tidx(a, b)] = mfma_bf16(ka[a], qa[b], At[tidx(a, b)]);
+                O[b] = mfma_bf16(qa[b], Shi[kb], O[b]);
+                O[b] = mfma_bf16(qa[b], Slo[kb], O[b]);
+            }
+        }
+        // Inter-chunk part decays by lam^(i+1).
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) O[b][ii] *= dec.lamq[b][ii];
+
+        // P = (A .* M) as the A operand of P V: for row tile b and token block kb,
+        // elements 0..3 come from tile (2kb, b), 4..7 from tile (2kb+1, b).
+        bf16x8 P[4][2];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+#pragma unroll
+            for (int kb = 0; 2 * kb <= b; ++kb) {
+                const int t0 = tidx(2 * kb, b);
+                u32x4 w;
+                w[0] = pack_bf16x2(At[t0][0] * dec.mask[t0][0], At[t0][1] * dec.mask[t0][1]);
+                w[1] = pack_bf16x2(At[t0][2] * dec.mask[t0][2], At[t0][3] * dec.mask[t0][3]);
+                if (2 * kb + 1 <= b) {
+                    const int t1 = tidx(2 * kb + 1, b);
+                    w[2] = pack_bf16x2(At[t1][0] * dec.mask[t1][0], At[t1][1] * dec.mask[t1][1]);
+                    w[3] = pack_bf16x2(At[t1][2] * dec.mask[t1][2], At[t1][3] * dec.mask[t1][3]);
+                } else {
+                    w[2] = 0u;
+                    w[3] = 0u;
+                }
+                P[b][kb] = __builtin_bit_cast(bf16x8, w);
+            }
+        }
+        // O += P V  (token order matching P: 4 from each half of the 32-token block)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const uint16_t* vr = Vt + (16 * wv + lr) * TLD + 32 * kb + 4 * lg;
+            const u32x2 lo = lds_load<u32x2>(vr);
+            const u32x2 hi = lds_load<u32x2>(vr + 16);
+            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int b = 2 * kb; b < 4; ++b) O[b] = mfma_bf16(P[b][kb], vop, O[b]);
+        }
+        // Store o rows of this chunk.
+        const int64_t p0 = (int64_t)c * kChunk;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int i = 16 * b + 4 * lg + ii;
+                if (p0 + i < L) p.o[(tok_row(p0 + i) * H + wk.h) * dv + vcol] = p.scale * O[b][ii];
+            }
+
+        // S <- lam^Lc S + (decayed K)^T V
+        const int Lc = (int)min((int64_t)kChunk, L - p0);
+        const float lamL = (Lc == kChunk) ? lamC : exp2f(g2 * (float)Lc);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) S[mt] *= lamL;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const bf16x8 vop = lds_load<bf16x8>(Vt + (16 * wv + lr) * TLD + 32 * kb + 8 * lg);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const bf16x8 kop = lds_load<bf16x8>(Kt + dmap(mt, lr) * TLD + 32 * kb + 8 * lg);
+                S[mt] = mfma_bf16(kop, vop, S[mt]);
+            }
+        }
+        split_state<KB>(S, Shi, Slo);
+    };
+
+    if (nch > 0) load_chunk(0);
+    for (int c = 0; c < nch; ++c) {
+        uint16_t* st = smem + (Cfg::STAGES == 2 ? (c & 1) * Cfg::STAGE_ELEMS : 0);
+        if (Cfg::STAGES == 1) __syncthreads();
+        store_chunk(c, st);
+        if (c + 1 < nch) load_chunk(c + 1);
+        __syncthreads();
+        compute_chunk(c, st);
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            p.final_state[st_off + (int64_t)dmap(mt, 4 * lg + ii) * dv + vcol] = S[mt][ii];
+}
+
+// ---------------------------------------------------------------------------
+// fp32 inputs: v_mfma_f32_16x16x4_f32, no rounding of any operand.
+// ---------------------------------------------------------------------------
+template <int DK, int NW>
+struct F32Cfg {
+    static constexpr int BV = 16 * NW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int QLD = DK + 4;       // floats
+    static constexpr int TLD = kChunk + 4;   // floats
+    static constexpr int Q_ELEMS = kChunk * QLD;
+    static constexpr int KT_ELEMS = DK * TLD;
+    static constexpr int VT_ELEMS = BV * TLD;
+    static constexpr int STAGE_ELEMS = 2 * Q_ELEMS + KT_ELEMS + VT_ELEMS;
+    static constexpr int STAGES = (2 * STAGE_ELEMS * 4 <= kLdsBudget) ? 2 : 1;
+    static constexpr int MT = DK / 16;
+    static constexpr int QITEMS = kChunk * DK / 4;          // 16-byte pieces of a Q chunk
+    static constexpr int KITEMS = (kChunk / 4) * (DK / 4);  // 4-token x 4-dk blocks of K
+    static constexpr int VITEMS = (kChunk / 4) * (BV / 4);
+    static constexpr int QPER = (QITEMS + NT - 1) / NT;
+    static constexpr int KPER = (KITEMS + NT - 1) / NT;
+    static constexpr int VPER = (VITEMS + NT - 1) / NT;
+    static_assert(DK % 16 == 0 && DK <= 128, "dk must be a multiple of 16 up to 128");
+    static_assert(STAGES * STAGE_ELEMS * 4 <= kLdsBudget, "LDS budget");
+};
+
+template <int DK, int NW, bool REV>
+__global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) {
+    using Cfg = F32Cfg<DK, NW>;
+    constexpr int BV = Cfg::BV, NT = Cfg::NT, QLD = Cfg::QLD, TLD = Cfg::TLD, MT = Cfg::MT;
+    __shared__ __attribute__((aligned(16))) float smem[Cfg::STAGES * Cfg::STAGE_ELEMS];
+
+    Work wk;
+    if (!decode_work(p, wk)) return;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const float g2 = p.g_gamma[wk.h] * kLog2e;
+    const int64_t L = wk.len;
+    const int nch = (int)((L + kChunk - 1) / kChunk);
+    const int H = p.num_heads, dv = p.dv;
+    const int vcol = wk.vb * BV + 16 * wv + lr;
+
+    const float* qbase = static_cast<const float*>(p.q) + (int64_t)wk.h * DK;
+    const float* kbase = static_cast<const float*>(p.k) + (int64_t)wk.kvh * DK;
+    const float* vbase = static_cast<const float*>(p.v) + (int64_t)wk.kvh * dv + wk.vb * BV;
+    const int64_t qstride = (int64_t)H * DK;
+    const int64_t kstride = (int64_t)p.num_kv_heads * DK;
+    const int64_t vstride = (int64_t)p.num_kv_heads * dv;
+    auto tok_row = [&](int64_t pos) -> int64_t { return REV ? wk.start + L - 1 - pos : wk.start + pos; };
+
+    LaneDecay dec;
+    make_lane_decay(g2, lr, lg, dec);
+    const float lamC = exp2f(g2 * (float)kChunk);
+
+    // State tile mt holds rows 16*mt + 4*lg + ii, column vcol.
+    f32x4 S[MT];
+    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
+
+    f32x4 pq[Cfg::QPER];
+    f32x4 pk[Cfg::KPER][4];
+    f32x4 pv[Cfg::VPER][4];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+    auto load_chunk = [&](int c) {
+        const int64_t p0 = (int64_t)c * kChunk;
+#pragma unroll
+        for (int s = 0; s < Cfg::QPER; ++s) {
+            const int item = tid + s * NT;
+            pq[s] = zero4;
+            if (item < Cfg::QITEMS) {
+                const int r = item / (DK / 4), c4 = item % (DK / 4);
+                if (p0 + r < L) pq[s] = *reinterpret_cast<const f32x4*>(qbase + tok_row(p0 + r) * qstride + c4 * 4);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::KPER; ++s) {
+            const int item = tid + s * NT;
+            const int tg = item / (DK / 4), c4 = item % (DK / 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pk[s][u] = zero4;
+                if (item < Cfg::KITEMS && p0 + 4 * tg + u < L)
+                    pk[s][u] = *reinterpret_cast<const f32x4*>(kbase + tok_row(p0 + 4 * tg + u) * kstride + c4 * 4);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::VPER; ++s) {
+            const int item = tid + s * NT;
+            const int tg = item / (BV / 4), c4 = item % (BV / 4);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                pv[s][u] = zero4;
+                if (item < Cfg::VITEMS && p0 + 4 * tg + u < L)
+                    pv[s][u] = *reinterpret_cast<const f32x4*>(vbase + tok_row(p0 + 4 * tg + u) * vstride + c4 * 4);
+            }
+        }
+    };
+
+    auto store_chunk = [&](int c, float* st) {
+        float* Qs = st;
+        float* Ks = st + Cfg::Q_ELEMS;
+        float* Kt = Ks + Cfg::Q_ELEMS;
+        float* Vt = Kt + Cfg::KT_ELEMS;
+        const int Lc = (int)min((int64_t)kChunk, L - (int64_t)c * kChunk);
+#pragma unroll
+        for (int s = 0; s < Cfg::QPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::QITEMS) {
+                const int r = item / (DK / 4), c4 = item % (DK / 4);
+                lds_store<f32x4>(Qs + r * QLD + c4 * 4, pq[s]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::KPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::KITEMS) {
+                const int tg = item / (DK / 4), c4 = item % (DK / 4);
+                float wgt[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    lds_store<f32x4>(Ks + (4 * tg + u) * QLD + c4 * 4, pk[s][u]);
+                    const int tok = 4 * tg + u;
+                    wgt[u] = tok < Lc ? exp2f(g2 * (float)(Lc - 1 - tok)) : 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f32x4 col = {pk[s][0][e] * wgt[0], pk[s][1][e] * wgt[1], pk[s][2][e] * wgt[2],
+                                       pk[s][3][e] * wgt[3]};
+                    lds_store<f32x4>(Kt + (c4 * 4 + e) * TLD + 4 * tg, col);
+                }
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::VPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::VITEMS) {
+                const int tg = item / (BV / 4), c4 = item % (BV / 4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const f32x4 col = {pv[s][0][e], pv[s][1][e], pv[s][2][e], pv[s][3][e]};
+                    lds_store<f32x4>(Vt + (c4 * 4 + e) * TLD + 4 * tg, col);
+                }
+            }
+        }
+    };
+
+    auto compute_chunk = [&](int c, const float* st) {
+        const float* Qs = st;
+        const float* Ks = st + Cfg::Q_ELEMS;
+        const float* Kt = Ks + Cfg::Q_ELEMS;
+        const float* Vt = Kt + Cfg::KT_ELEMS;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 O[4], At[10];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) O[b] = z;
+#pragma unroll
+        for (int t = 0; t < 10; ++t) At[t] = z;
+        // Step (t, ii) pairs lane group lg with dk = 16t + 4lg + ii in every operand.
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            f32x4 qa[4], ka[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                qa[r] = lds_load<f32x4>(Qs + (16 * r + lr) * QLD + 16 * t + 4 * lg);
+                ka[r] = lds_load<f32x4>(Ks + (16 * r + lr) * QLD + 16 * t + 4 * lg);
+            }
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+#pragma unroll
+                    for (int a = 0; a <= b; ++a) At[tidx(a, b)] = mfma_f32(ka[a][ii], qa[b][ii], At[tidx(a, b)]);
+                    O[b] = mfma_f32(qa[b][ii], S[t][ii], O[b]);
+                }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) O[b][ii] *= dec.lamq[b][ii];
+        // O += (A .* M) V; token step (a, ii) pairs lane group lg with j = 16a + 4lg + ii.
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const f32x4 vop = lds_load<f32x4>(Vt + (16 * wv + lr) * TLD + 16 * a + 4 * lg);
+#pragma unroll
+            for (int b = a; b < 4; ++b)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii)
+                    O[b] = mfma_f32(At[tidx(a, b)][ii] * dec.mask[tidx(a, b)][ii], vop[ii], O[b]);
+        }
+        const int64_t p0 = (int64_t)c * kChunk;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int i = 16 * b + 4 * lg + ii;
+                if (p0 + i < L) p.o[(tok_row(p0 + i) * H + wk.h) * dv + vcol] = p.scale * O[b][ii];
+            }
+        const int Lc = (int)min((int64_t)kChunk, L - p0);
+        const float lamL = (Lc == kChunk) ? lamC : exp2f(g2 * (float)Lc);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) S[mt] *= lamL;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const f32x4 vop = lds_load<f32x4>(Vt + (16 * wv + lr) * TLD + 16 * a + 4 * lg);
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f32x4 kop = lds_load<f32x4>(Kt + (16 * mt + lr) * TLD + 16 * a + 4 * lg);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) S[mt] = mfma_f32(kop[ii], vop[ii], S[mt]);
+            }
+        }
+    };
+
+    if (nch > 0) load_chunk(0);
+    for (int c = 0; c < nch; ++c) {
+        float* st = smem + (Cfg::STAGES == 2 ? (c & 1) * Cfg::STAGE_ELEMS : 0);
+        if (Cfg::STAGES == 1) __syncthreads();
+        store_chunk(c, st);
+        if (c + 1 < nch) load_chunk(c + 1);
+        __syncthreads();
+        compute_chunk(c, st);
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = S[mt][ii];
+}
+
+// ---------------------------------------------------------------------------
+// Longest-first order of packed sequences (ties by index): order[rank] = sequence.
+// Lengths are clamped exactly as decode_work clamps them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* cu, int num_seqs, int seqlen,
+                                                        int32_t* order) {
+    extern __shared__ int32_t lens[];
+    for (int i = threadIdx.x; i < num_seqs; i += blockDim.x) {
+        int64_t a = cu[i], e = cu[i + 1];
+        a = min(max(a, (int64_t)0), (int64_t)seqlen);
+        e = min(max(e, a), (int64_t)seqlen);
+        lens[i] = (int32_t)(e - a);
+    }
+    __syncthreads();
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= num_seqs) return;
+    const int li = lens[i];
+    int rank = 0;
+    for (int j = 0; j < num_seqs; ++j) {
+        const int lj = lens[j];
+        rank += (lj > li) || (lj == li && j < i);
+    }
+    order[rank] = i;
+}
+
+template <int DK, int NW>
+hipError_t launch_bf16(const FwdParams& p, bool rev, hipStream_t s) {
+    const dim3 grid(fwd_grid_size(p)), block(64 * NW);
+    if (rev)
+        hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+template <int DK, int NW>
+hipError_t launch_f32(const FwdParams& p, bool rev, hipStream_t s) {
+    const dim3 grid(fwd_grid_size(p)), block(64 * NW);
+    if (rev)
+        hipLaunchKernelGGL((fwd_f32_kernel<DK, NW, true>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((fwd_f32_kernel<DK, NW, false>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+
+// Compiled variants.  Narrow workgroups (fewer waves) stage more data per thread;
+// with a wide head that exceeds the register file, so wide heads use 4 waves.
+__host__ __device__ constexpr bool bf16_variant(int dk, int nw) {
+    return (dk == 32 || dk == 64) ? (nw == 1 || nw == 2 || nw == 4)
+           : dk == 128            ? (nw == 2 || nw == 4)
+           : (dk == 192 || dk == 256) ? nw == 4
+                                      : false;
+}
+__host__ __device__ constexpr bool f32_variant(int dk, int nw) {
+    return (dk == 16 || dk == 32) ? (nw == 1 || nw == 2 || nw == 4)
+           : dk == 64             ? (nw == 2 || nw == 4)
+           : dk == 128            ? nw == 4
+                                  : false;
+}
+
+template <int DK>
+hipError_t launch_bf16_nw(const FwdParams& p, int nw, bool rev, hipStream_t s) {
+    if constexpr (bf16_variant(DK, 1)) {
+        if (nw == 1) return launch_bf16<DK, 1>(p, rev, s);
+    }
+    if constexpr (bf16_variant(DK, 2)) {
+        if (nw == 2) return launch_bf16<DK, 2>(p, rev, s);
+    }
+    if constexpr (bf16_variant(DK, 4)) {
+        if (nw == 4) return launch_bf16<DK, 4>(p, rev, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int DK>
+hipError_t launch_f32_nw(const FwdParams& p, int nw, bool rev, hipStream_t s) {
+    if constexpr (f32_variant(DK, 1)) {
+        if (nw == 1) return launch_f32<DK, 1>(p, rev, s);
+    }
+    if constexpr (f32_variant(DK, 2)) {
+        if (nw == 2) return launch_f32<DK, 2>(p, rev, s);
+    }
+    if constexpr (f32_variant(DK, 4)) {
+        if (nw == 4) return launch_f32<DK, 4>(p, rev, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// dtype codes follow lattn_dtype: 0 = bf16, 1 = f32.
+bool have_fwd_kernel(int in_dtype, int dk, int nw) {
+    if (in_dtype == 0) return bf16_variant(dk, nw);
+    if (in_dtype == 1) return f32_variant(dk, nw);
+    return false;
+}
+
+int fwd_grid_size(const FwdParams& p) {
+    const int per_xcd = (p.num_groups + kNumXcd - 1) / kNumXcd;
+    return kNumXcd * per_xcd * p.group_size;
+}
+
+hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t s) {
+    if (in_dtype == 0) {
+        switch (p.dk) {
+            case 32: return launch_bf16_nw<32>(p, nw, reverse, s);
+            case 64: return launch_bf16_nw<64>(p, nw, reverse, s);
+            case 128: return launch_bf16_nw<128>(p, nw, reverse, s);
+            case 192: return launch_bf16_nw<192>(p, nw, reverse, s);
+            case 256: return launch_bf16_nw<256>(p, nw, reverse, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    if (in_dtype == 1) {
+        switch (p.dk) {
+            case 16: return launch_f32_nw<16>(p, nw, reverse, s);
+            case 32: return launch_f32_nw<32>(p, nw, reverse, s);
+            case 64: return launch_f32_nw<64>(p, nw, reverse, s);
+            case 128: return launch_f32_nw<128>(p, nw, reverse, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_seq_order(const int32_t* cu, int num_seqs, int seqlen, int32_t* order, hipStream_t s) {
+    const int blocks = (num_seqs + 255) / 256;
+    hipLaunchKernelGGL(seq_order_kernel, dim3(blocks), dim3(256), (size_t)num_seqs * sizeof(int32_t), s, cu,
+                       num_seqs, seqlen, order);
+    return hipGetLastError();
+}
+
+}  // namespace lattn

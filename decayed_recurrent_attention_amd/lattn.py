@@ -1,0 +1,230 @@
+"""Python binding of liblattn.so (the C ABI in include/lattn.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the forward pass runs in the library's kernels.  A
+missing library raises; there is no fallback path.
+
+Functions with the C names (``lattn_fwd``, ``lattn_fwd_workspace_size``,
+``lattn_lightning_g_gamma``, ``lattn_status_string``) map one to one onto the
+ABI.  ``lightning_attn`` and ``recurrent`` mirror the signatures of the
+ejkernel lightning_attn and recurrent interface pages (without the GLA gates).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblattn.so")
+
+LATTN_BF16 = 0
+LATTN_F32 = 1
+
+LATTN_OK = 0
+LATTN_ERR_INVALID_ARG = -1
+LATTN_ERR_VARLEN_BATCH = -2
+LATTN_ERR_HEADS = -3
+LATTN_ERR_UNSUPPORTED = -4
+LATTN_ERR_WORKSPACE = -5
+LATTN_ERR_LAUNCH = -6
+LATTN_ERR_DEVICE = -7
+
+# Every function declared in include/lattn.h.
+EXPORTS = ("lattn_fwd", "lattn_fwd_workspace_size", "lattn_lightning_g_gamma",
+           "lattn_status_string", "lattn_abi_version")
+
+
+class LattnProblem(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "batch", "seqlen", "num_heads", "num_kv_heads", "head_dim_qk", "head_dim_v",
+        "num_seqs", "in_dtype", "out_dtype")]
+
+
+class LattnError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(f"lattn status {status}: {lattn_status_string(status)}")
+        self.status = status
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load liblattn.so once (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError(f"{path} is missing: build it with "
+                                   "`python -m decayed_recurrent_attention_amd.build`")
+            lib = ctypes.CDLL(path)
+            P = ctypes.POINTER(LattnProblem)
+            vp = ctypes.c_void_p
+            lib.lattn_fwd.restype = ctypes.c_int
+            lib.lattn_fwd.argtypes = [P, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int, vp, vp,
+                                      vp, vp, ctypes.c_size_t, vp]
+            lib.lattn_fwd_workspace_size.restype = ctypes.c_size_t
+            lib.lattn_fwd_workspace_size.argtypes = [P]
+            lib.lattn_lightning_g_gamma.restype = ctypes.c_int
+            lib.lattn_lightning_g_gamma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+            lib.lattn_status_string.restype = ctypes.c_char_p
+            lib.lattn_status_string.argtypes = [ctypes.c_int]
+            lib.lattn_abi_version.restype = ctypes.c_int
+            lib.lattn_abi_version.argtypes = []
+            _lib = lib
+    return _lib
+
+
+# -- one-to-one ABI wrappers ------------------------------------------------------
+def lattn_status_string(status: int) -> str:
+    return load_library().lattn_status_string(int(status)).decode()
+
+
+def lattn_abi_version() -> int:
+    return int(load_library().lattn_abi_version())
+
+
+def lattn_fwd_workspace_size(problem: LattnProblem) -> int:
+    return int(load_library().lattn_fwd_workspace_size(ctypes.byref(problem)))
+
+
+def lattn_lightning_g_gamma(num_heads: int, layer_idx: int, num_layers: int) -> np.ndarray:
+    """Lightning per-head log-decay as float32 [num_heads] (host)."""
+    out = np.empty(num_heads, dtype=np.float32)
+    rc = load_library().lattn_lightning_g_gamma(int(num_heads), int(layer_idx), int(num_layers),
+                                                out.ctypes.data)
+    if rc != LATTN_OK:
+        raise LattnError(rc)
+    return out
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr()) or None
+
+
+def lattn_fwd(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_state, reverse: bool,
+              cu_seqlens, o, final_state, workspace=None, stream=None) -> int:
+    """Raw call: tensors (or None) are passed by address; returns the status code."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return int(load_library().lattn_fwd(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g_gamma), float(scale),
+        _ptr(initial_state), int(bool(reverse)), _ptr(cu_seqlens), _ptr(o), _ptr(final_state),
+        _ptr(workspace), ws_bytes, stream))
+
+
+# -- tensor-level forward ---------------------------------------------------------
+_G_CACHE: dict = {}
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return LATTN_BF16
+    if t.dtype == torch.float32:
+        return LATTN_F32
+    raise TypeError(f"q, k, v must be bfloat16 or float32, got {t.dtype}")
+
+
+def recurrent(query, key, value, g_gamma=None, softmax_scale=None, initial_state=None,
+              reverse=False, cu_seqlens=None):
+    """Decayed recurrent attention forward on the GPU.
+
+    Shapes follow the recurrent interface page: q [B, T, H, dk], k [B, T, Hkv, dk],
+    v [B, T, Hkv, dv]; packed input (``cu_seqlens``) may drop the batch axis.
+    Returns (o float32 [.., T, H, dv], final_state float32 [N_seq, H, dk, dv]).
+    """
+    import torch
+
+    squeeze = query.dim() == 3
+    if squeeze:
+        if cu_seqlens is None:
+            raise ValueError("3-D inputs are only accepted with cu_seqlens")
+        query, key, value = query.unsqueeze(0), key.unsqueeze(0), value.unsqueeze(0)
+    if query.dim() != 4 or key.dim() != 4 or value.dim() != 4:
+        raise ValueError("query, key and value must be 4-D (batch, seq, heads, dim)")
+    B, T, H, dk = query.shape
+    Hkv = key.shape[2]
+    dv = value.shape[3]
+    if key.shape != (B, T, Hkv, dk) or value.shape != (B, T, Hkv, dv):
+        raise ValueError(f"inconsistent shapes q{tuple(query.shape)} k{tuple(key.shape)} "
+                         f"v{tuple(value.shape)}")
+    if not (query.dtype == key.dtype == value.dtype):
+        raise TypeError("query, key and value must share one dtype")
+    dev = query.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be GPU tensors")
+    num_seqs = 0
+    cu = None
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError(f"cu_seqlens needs batch size 1 (got {B}); pack the sequences "
+                             "along the token axis")
+        cu = torch.as_tensor(cu_seqlens).to(device=dev, dtype=torch.int32).contiguous()
+        num_seqs = cu.numel() - 1
+        if num_seqs < 1:
+            raise ValueError("cu_seqlens needs at least two entries")
+        if initial_state is not None and initial_state.shape[0] != num_seqs:
+            raise ValueError(f"initial_state holds {initial_state.shape[0]} states but "
+                             f"cu_seqlens describes {num_seqs} sequences")
+    n_seq = num_seqs if cu is not None else B
+    if softmax_scale is None:
+        softmax_scale = float(np.float32(dk ** -0.5))
+    if g_gamma is None:
+        g_gamma = torch.zeros(H, device=dev, dtype=torch.float32)
+    g_gamma = torch.as_tensor(g_gamma).to(device=dev, dtype=torch.float32).contiguous()
+    if g_gamma.shape != (H,):
+        raise ValueError(f"g_gamma must have shape ({H},)")
+    if initial_state is not None:
+        initial_state = initial_state.to(device=dev, dtype=torch.float32).contiguous()
+        if initial_state.shape != (n_seq, H, dk, dv):
+            raise ValueError(f"initial_state must have shape {(n_seq, H, dk, dv)}")
+    q, k, v = query.contiguous(), key.contiguous(), value.contiguous()
+    prob = LattnProblem(B, T, H, Hkv, dk, dv, num_seqs, _dtype_code(q), LATTN_F32)
+    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+    fs = torch.empty((n_seq, H, dk, dv), device=dev, dtype=torch.float32)
+    ws_bytes = lattn_fwd_workspace_size(prob)
+    ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
+    rc = lattn_fwd(prob, q, k, v, g_gamma, softmax_scale, initial_state, reverse, cu, o, fs, ws)
+    if rc != LATTN_OK:
+        raise LattnError(rc)
+    return (o[0] if squeeze else o), fs
+
+
+def lightning_g_gamma_tensor(num_heads: int, layer_idx: int, num_layers: int, device):
+    """Device copy of the lightning decay schedule (cached per device and arguments)."""
+    import torch
+
+    key = (num_heads, layer_idx, num_layers, str(device))
+    g = _G_CACHE.get(key)
+    if g is None:
+        g = torch.from_numpy(lattn_lightning_g_gamma(num_heads, layer_idx, num_layers)).to(device)
+        _G_CACHE[key] = g
+    return g
+
+
+def lightning_attn(query, key, value, layer_idx: int, num_layers: int, softmax_scale=None,
+                   initial_state=None, reverse=False, cu_seqlens=None):
+    """Lightning attention forward (lightning_attn interface page): the layer-dependent
+    decay schedule, default scale dk^-1/2, then the recurrent forward."""
+    if num_layers < 1 or not 0 <= layer_idx <= num_layers:
+        raise ValueError("need num_layers >= 1 and 0 <= layer_idx <= num_layers")
+    if cu_seqlens is not None and query.dim() == 4 and query.shape[0] != 1:
+        raise ValueError(f"cu_seqlens needs batch size 1 (got {query.shape[0]}); pack the "
+                         "sequences along the token axis")
+    if cu_seqlens is not None and initial_state is not None and \
+            initial_state.shape[0] != len(cu_seqlens) - 1:
+        raise ValueError(f"initial_state holds {initial_state.shape[0]} states but cu_seqlens "
+                         f"describes {len(cu_seqlens) - 1} sequences")
+    if softmax_scale is None:
+        softmax_scale = float(np.float32(key.shape[-1] ** -0.5))
+    g = lightning_g_gamma_tensor(query.shape[-2], layer_idx, num_layers, query.device)
+    return recurrent(query, key, value, g_gamma=g, softmax_scale=softmax_scale,
+                     initial_state=initial_state, reverse=reverse, cu_seqlens=cu_seqlens)

@@ -1,0 +1,121 @@
+/*
+ * lattn — Lightning (decayed recurrent) attention forward pass on AMD MI355X (gfx950).
+ *
+ * Public C ABI of liblattn.so.  Plain C types only: device buffers are passed as
+ * untyped pointers, the HIP stream as `void*` (a hipStream_t; NULL = the default
+ * stream).  No function allocates device memory, synchronises, or keeps a pointer
+ * after it returns.  Every function is thread-safe.
+ *
+ * The operation (ejkernel "recurrent" interface page, docstring of recurrent():
+ * "The core update is"; lightning_attn interface page for the argument meanings):
+ * for each sequence n and query head h, with lam = exp(g_gamma[h]),
+ *
+ *     S_t = lam * S_{t-1} + k_t^T v_t        S_{-1} = initial_state[n, h] or 0
+ *     o_t = scale * (q_t S_t)                final_state[n, h] = S after the last token
+ *
+ * where k_t, v_t are the rows of kv head h / (H / Hkv) (grouped-query attention).
+ * With `reverse` the positions are visited from last to first (o_t stays at t).
+ * With `cu_seqlens` the input is packed: sequence n is rows [cu[n], cu[n+1]) of a
+ * batch-1 input and the state restarts at every boundary.
+ */
+#ifndef LATTN_H
+#define LATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. */
+typedef enum {
+    LATTN_BF16 = 0, /* bfloat16 words */
+    LATTN_F32 = 1   /* IEEE float32 */
+} lattn_dtype;
+
+/* Status codes: 0 on success, negative on error.  Nothing is launched on error. */
+enum {
+    LATTN_OK = 0,
+    LATTN_ERR_INVALID_ARG = -1,  /* null pointer, non-positive size, bad alignment */
+    LATTN_ERR_VARLEN_BATCH = -2, /* cu_seqlens given with batch != 1 (lightning_attn page, Raises) */
+    LATTN_ERR_HEADS = -3,        /* num_heads not a multiple of num_kv_heads */
+    LATTN_ERR_UNSUPPORTED = -4,  /* head dims or dtypes without a compiled kernel */
+    LATTN_ERR_WORKSPACE = -5,    /* workspace missing or smaller than lattn_fwd_workspace_size */
+    LATTN_ERR_LAUNCH = -6,       /* the HIP runtime rejected a launch */
+    LATTN_ERR_DEVICE = -7        /* no usable device, or the current device is not gfx950 */
+};
+
+/*
+ * Problem description (shapes of the lightning_attn / recurrent signatures).
+ *   q  [batch, seqlen, num_heads,    head_dim_qk]
+ *   k  [batch, seqlen, num_kv_heads, head_dim_qk]
+ *   v  [batch, seqlen, num_kv_heads, head_dim_v]
+ *   o  [batch, seqlen, num_heads,    head_dim_v]           (out_dtype)
+ *   initial_state / final_state [num_seqs, num_heads, head_dim_qk, head_dim_v] float32
+ * All arrays are dense, row-major, in that axis order.
+ */
+typedef struct {
+    int32_t batch;        /* B >= 1; must be 1 when cu_seqlens is given */
+    int32_t seqlen;       /* T >= 0 tokens per batch row (total packed tokens when varlen) */
+    int32_t num_heads;    /* H >= 1: query heads; o, g_gamma and the states use H */
+    int32_t num_kv_heads; /* Hkv >= 1, H % Hkv == 0; head h reads kv head h / (H / Hkv) */
+    int32_t head_dim_qk;  /* dk */
+    int32_t head_dim_v;   /* dv */
+    int32_t num_seqs;     /* packed sequences: > 0 exactly when cu_seqlens is given, else 0 (then N_seq = B) */
+    int32_t in_dtype;     /* lattn_dtype of q, k, v: LATTN_BF16 or LATTN_F32 */
+    int32_t out_dtype;    /* lattn_dtype of o: LATTN_F32 (the only one supported) */
+} lattn_problem;
+
+/*
+ * Device workspace (bytes) that lattn_fwd needs for problem *p; 0 for fixed-length
+ * input.  Packed input needs room for the longest-first sequence order.
+ * Returns 0 also for an invalid problem (lattn_fwd then reports the error).
+ */
+size_t lattn_fwd_workspace_size(const lattn_problem* p);
+
+/*
+ * Forward pass, enqueued on `stream`; returns without waiting for the GPU.
+ *   q, k, v        device, in_dtype, 16-byte aligned, layout above.
+ *   g_gamma        device float32 [H]: per-head log-decay, finite and <= 0.
+ *   scale          multiplies q (so o), never the state.
+ *   initial_state  device float32 [N_seq, H, dk, dv], or NULL for zeros.
+ *   reverse        0: positions ascending; 1: descending.
+ *   cu_seqlens     device int32 [N_seq + 1], or NULL.  Must start at 0, be
+ *                  non-decreasing and end at seqlen; values outside [0, seqlen]
+ *                  are clamped into it so that no access leaves the buffers.
+ *   o              device float32 output.
+ *   final_state    device float32 output [N_seq, H, dk, dv].
+ *   workspace      device buffer of >= lattn_fwd_workspace_size(p) bytes (may be
+ *                  NULL when that is 0).  Owned by the caller; contents on entry
+ *                  are ignored; must not be shared by calls that overlap in time.
+ * Supported: in_dtype BF16 with dk in {32, 64, 128, 192, 256}; in_dtype F32 with
+ * dk in {16, 32, 64, 128}; dv a multiple of 16 up to 256; out_dtype F32.
+ * Returns LATTN_OK or a negative status; buffers are untouched on error.
+ */
+int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* v,
+              const float* g_gamma, float scale, const float* initial_state, int reverse,
+              const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * Lightning decay schedule (lightning_attn interface page, module docstring "Key
+ * innovation" and wrapper body): out_host[h] = -(8/H) * (1 - layer_idx/num_layers) * h,
+ * coefficient computed in double, rounded to float32, then multiplied by the
+ * float32 head index in float32.  out_host is host memory of num_heads floats.
+ * Returns LATTN_OK, or LATTN_ERR_INVALID_ARG (num_heads < 1, num_layers < 1,
+ * layer_idx outside [0, num_layers], out_host NULL).
+ */
+int lattn_lightning_g_gamma(int num_heads, int layer_idx, int num_layers, float* out_host);
+
+/* Static description of a status code (never NULL). */
+const char* lattn_status_string(int status);
+
+/* ABI version of this header: 1. */
+int lattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LATTN_H */

@@ -1,0 +1,132 @@
+"""C ABI of liblattn.so without a GPU: symbols, host-side functions, argument errors.
+
+Every call here returns before the library touches the HIP runtime, so these
+tests run on machines without a device.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from decayed_recurrent_attention_amd import lattn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(lattn_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lattn.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names == sorted(lattn.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lattn.lattn_abi_version() == 1
+    for code in range(-7, 1):
+        s = lattn.lattn_status_string(code)
+        assert s and s != "unknown status"
+    assert lattn.lattn_status_string(-99) == "unknown status"
+
+
+@pytest.mark.parametrize("H,l,L", [(2, 5, 12), (8, 5, 12), (32, 0, 12), (12, 3, 24), (16, 6, 12),
+                                   (7, 2, 9), (64, 11, 12), (16, 12, 12)])
+def test_g_gamma_matches_oracle_bits(H, l, L):
+    mine = lattn.lattn_lightning_g_gamma(H, l, L)
+    ref = oracle.load().lightning_g_gamma(H, l, L)
+    assert np.array_equal(mine.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("args", [(0, 0, 12), (8, -1, 12), (8, 13, 12), (8, 0, 0)])
+def test_g_gamma_rejects(args):
+    with pytest.raises(lattn.LattnError):
+        lattn.lattn_lightning_g_gamma(*args)
+
+
+def P(**kw):
+    base = dict(batch=2, seqlen=128, num_heads=8, num_kv_heads=8, head_dim_qk=64, head_dim_v=64,
+                num_seqs=0, in_dtype=lattn.LATTN_BF16, out_dtype=lattn.LATTN_F32)
+    base.update(kw)
+    return lattn.LattnProblem(**base)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: validation fails before any device access
+
+
+def call(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, init=None, cu=None, o=FAKE, fs=FAKE, ws=None,
+         ws_bytes=0):
+    L = lattn.load_library()
+    return L.lattn_fwd(ctypes.byref(prob), q, k, v, g, 0.125, init, 0, cu, o, fs, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("prob,status", [
+    (P(batch=0), lattn.LATTN_ERR_INVALID_ARG),
+    (P(seqlen=-1), lattn.LATTN_ERR_INVALID_ARG),
+    (P(num_heads=0), lattn.LATTN_ERR_INVALID_ARG),
+    (P(num_kv_heads=3), lattn.LATTN_ERR_HEADS),
+    (P(num_seqs=3), lattn.LATTN_ERR_VARLEN_BATCH),
+    (P(head_dim_qk=48), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(head_dim_v=24), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(head_dim_v=272), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(in_dtype=7), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(out_dtype=lattn.LATTN_BF16), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(in_dtype=lattn.LATTN_F32, head_dim_qk=192), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(head_dim_qk=128, head_dim_v=16), lattn.LATTN_ERR_UNSUPPORTED),
+])
+def test_problem_errors(prob, status):
+    assert call(prob) == status
+    assert lattn.lattn_fwd_workspace_size(prob) == 0
+
+
+def test_pointer_errors():
+    prob = P()
+    assert call(prob, q=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call(prob, g=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call(prob, fs=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call(prob, q=FAKE + 2) == lattn.LATTN_ERR_INVALID_ARG  # misaligned
+    assert call(prob, init=FAKE + 4) == lattn.LATTN_ERR_INVALID_ARG
+    # cu_seqlens must be given exactly when num_seqs > 0
+    assert call(prob, cu=FAKE) == lattn.LATTN_ERR_INVALID_ARG
+    L = lattn.load_library()
+    assert L.lattn_fwd(None, FAKE, FAKE, FAKE, FAKE, 1.0, None, 0, None, FAKE, FAKE, None, 0,
+                       None) == lattn.LATTN_ERR_INVALID_ARG
+
+
+def test_varlen_workspace():
+    prob = P(batch=1, seqlen=300, num_seqs=5)
+    need = lattn.lattn_fwd_workspace_size(prob)
+    assert need >= 5 * 4 and need % 256 == 0
+    assert lattn.lattn_fwd_workspace_size(P()) == 0  # fixed length needs none
+    assert call(prob, cu=FAKE) == lattn.LATTN_ERR_WORKSPACE
+    assert call(prob, cu=FAKE, ws=FAKE, ws_bytes=need - 1) == lattn.LATTN_ERR_WORKSPACE
+    big = P(batch=1, seqlen=300, num_seqs=20000)  # beyond the ordering limit: no workspace
+    assert lattn.lattn_fwd_workspace_size(big) == 0
+
+
+def test_wrapper_value_errors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(2, 10, 4, 16)
+    with pytest.raises(ValueError, match="batch size 1"):
+        lattn.lightning_attn(q, q, q, 1, 4, cu_seqlens=[0, 4, 10])
+    q1 = torch.zeros(1, 10, 4, 16)
+    with pytest.raises(ValueError, match="initial_state"):
+        lattn.lightning_attn(q1, q1, q1, 1, 4, cu_seqlens=[0, 4, 10],
+                             initial_state=torch.zeros(3, 4, 16, 16))
+    with pytest.raises(ValueError):
+        lattn.lightning_attn(q1, q1, q1, 5, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        lattn.recurrent(q1, q1, q1)

@@ -1,0 +1,194 @@
+"""GPU parity: the HIP path against the fp64 oracle, element by element.
+
+Runs on an MI355X through the C ABI (via the Python binding).  Sizes are chosen so
+that the oracle finishes in seconds while spanning several 64-token chunks and a
+ragged tail; the full-size long-sequence case compares sampled (sequence, head)
+pairs in the same launch configuration that the benchmark times.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from decayed_recurrent_attention_amd import inputs, lattn
+from tests.parity_util import TOL, check, gpu_run, oracle_run, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lattn.load_library()
+
+
+def _compare(w, data, reverse=None, tag=""):
+    o, fs = gpu_run(w, data, reverse)
+    o_ref, fs_ref = oracle_run(w, data, reverse)
+    tol = TOL[w.dtype]
+    name = w.name + tag
+    check(o.cpu().numpy(), o_ref, tol, name + " o")
+    check(fs.cpu().numpy(), fs_ref, tol, name + " final_state")
+
+
+# -- the five workloads ------------------------------------------------------------
+def test_tiny_fp32():
+    w = inputs.tiny_fp32()
+    _compare(w, w.make())
+
+
+def test_tiny_fp32_reverse_with_state():
+    w = inputs.tiny_fp32(seqlen=200)
+    w.init_std = 0.5
+    _compare(w, w.make(), reverse=True, tag=" rev+init")
+
+
+def test_bf16_d64():
+    w = inputs.bf16_d64()
+    _compare(w, w.make())
+
+
+@pytest.mark.parametrize("n", [512, 2048])
+def test_long_d128_full(n):
+    w = inputs.long_d128(seqlen=n)
+    _compare(w, w.make())
+
+
+def test_d192():
+    w = inputs.d192()
+    _compare(w, w.make())
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_varlen_gqa(reverse):
+    w = inputs.varlen_gqa(reverse=reverse)
+    _compare(w, w.make())
+
+
+def test_long_d128_n32768_sampled():
+    """Full-size long sequence (B=4, H=32, d=128, N=32768), sampled pairs."""
+    import torch
+
+    w = inputs.long_d128(seqlen=32768)
+    data = w.make()
+    o, fs = gpu_run(w, data)
+    pairs = [(0, 0), (1, 1), (2, 5), (3, 17), (0, 31), (3, 0), (1, 30), (2, 16)]
+    o_ref, fs_ref = oracle_run(w, data, pairs=pairs)
+    idx_b = torch.tensor([b for b, _ in pairs], device=o.device)
+    idx_h = torch.tensor([h for _, h in pairs], device=o.device)
+    o_s = o[idx_b, :, idx_h, :].cpu().numpy()            # [pairs, T, dv]
+    fs_s = fs[idx_b, idx_h].cpu().numpy()                 # [pairs, dk, dv]
+    o_rs = np.stack([o_ref[b, :, h, :] for b, h in pairs])
+    fs_rs = np.stack([fs_ref[b, h] for b, h in pairs])
+    tol = TOL["bf16"]
+    check(o_s, o_rs, tol, "n32768 sampled o")
+    check(fs_s, fs_rs, tol, "n32768 sampled final_state")
+    # every output is finite
+    assert torch.isfinite(o).all().item() and torch.isfinite(fs).all().item()
+
+
+# -- edge cases ----------------------------------------------------------------------
+@pytest.mark.parametrize("reverse", [False, True])
+def test_ragged_packed_lengths(reverse):
+    lens = [0, 1, 63, 64, 65, 127, 200, 2, 0, 129]
+    w = inputs.Workload("ragged_packed", 1, sum(lens), 8, 2, 64, 64, "bf16", 3, 12,
+                        reverse=reverse, seq_lens=lens, init_std=0.3, seed=3)
+    _compare(w, w.make(), tag=" rev" if reverse else "")
+
+
+def test_ragged_fixed_length_reverse_with_state():
+    w = inputs.Workload("ragged_fixed", 2, 1000, 4, 4, 128, 128, "bf16", 2, 12, reverse=True,
+                        init_std=1.0, seed=4)
+    _compare(w, w.make())
+
+
+@pytest.mark.parametrize("dk,dv,dtype", [(64, 128, "bf16"), (128, 64, "bf16"), (32, 16, "bf16"),
+                                         (256, 64, "bf16"), (64, 32, "f32"), (128, 64, "f32"),
+                                         (32, 48, "f32")])
+def test_unequal_head_dims(dk, dv, dtype):
+    w = inputs.Workload(f"dk{dk}_dv{dv}_{dtype}", 2, 300, 4, 2, dk, dv, dtype, 4, 12,
+                        init_std=0.2, seed=5)
+    _compare(w, w.make())
+
+
+@pytest.mark.parametrize("nw", ["1", "2", "4"])
+def test_workgroup_widths(nw, monkeypatch):
+    monkeypatch.setenv("LATTN_NW", nw)
+    w = inputs.Workload(f"nw{nw}", 2, 333, 4, 4, 64, 64, "bf16", 1, 12, init_std=0.1, seed=6)
+    _compare(w, w.make(), tag=f" nw={nw}")
+
+
+def test_no_decay_long():
+    """Last layer: g = 0 for every head, the state only grows."""
+    w = inputs.Workload("no_decay", 1, 8192, 4, 4, 128, 128, "bf16", 12, 12, seed=7)
+    _compare(w, w.make())
+
+
+def test_explicit_g_gamma_strong_decay():
+    import torch
+
+    w = inputs.Workload("strong_decay", 1, 700, 4, 4, 64, 64, "bf16", 0, 1, init_std=1.0, seed=8)
+    data = w.make()
+    g = np.array([-0.0, -3.0, -30.0, -200.0], dtype=np.float32)
+    o, fs = gpu_run(w, data, g_gamma=torch.from_numpy(g).cuda())
+    o_ref, fs_ref = oracle_run(w, data, g_gamma=g)
+    check(o.cpu().numpy(), o_ref, TOL["bf16"], "strong decay o")
+    check(fs.cpu().numpy(), fs_ref, TOL["bf16"], "strong decay final_state")
+
+
+def test_empty_sequence_batch():
+    import torch
+
+    w = inputs.Workload("empty", 2, 0, 4, 4, 64, 64, "bf16", 1, 12, init_std=1.0, seed=9)
+    data = w.make()
+    o, fs = gpu_run(w, data)
+    assert o.shape == (2, 0, 4, 64)
+    assert torch.equal(fs.cpu(), torch.from_numpy(data["initial_state"]))
+
+
+def test_chained_segments_match_whole():
+    """Splitting a sequence and chaining final_state -> initial_state matches one call."""
+    import torch
+
+    w = inputs.Workload("chain", 2, 1100, 4, 4, 128, 128, "bf16", 5, 12, seed=10)
+    data = w.make()
+    q, k, v = (to_device(data[n], "bf16") for n in ("q", "k", "v"))
+    o, fs = lattn.lightning_attn(q, k, v, 5, 12)
+    m = 517
+    o1, fs1 = lattn.lightning_attn(q[:, :m], k[:, :m], v[:, :m], 5, 12)
+    o2, fs2 = lattn.lightning_attn(q[:, m:], k[:, m:], v[:, m:], 5, 12, initial_state=fs1)
+    o_ref, fs_ref = oracle_run(w, data)
+    check(torch.cat([o1, o2], 1).cpu().numpy(), o_ref, TOL["bf16"], "chained o")
+    check(fs2.cpu().numpy(), fs_ref, TOL["bf16"], "chained final_state")
+    assert (o - torch.cat([o1, o2], 1)).abs().max().item() <= 1e-3 * o.abs().max().item()
+
+
+def test_deterministic():
+    import torch
+
+    w = inputs.varlen_gqa(num_seqs=5, lo=60, hi=700, seed=11)
+    data = w.make()
+    o1, fs1 = gpu_run(w, data)
+    o2, fs2 = gpu_run(w, data)
+    assert torch.equal(o1, o2) and torch.equal(fs1, fs2)
+
+
+def test_varlen_3d_input_matches_4d():
+    import torch
+
+    w = inputs.varlen_gqa(num_seqs=4, lo=10, hi=300, seed=12)
+    data = w.make()
+    o4, fs4 = gpu_run(w, data)
+    q, k, v = (to_device(data[n], "bf16")[0] for n in ("q", "k", "v"))
+    o3, fs3 = lattn.lightning_attn(q, k, v, w.layer_idx, w.num_layers, softmax_scale=w.scale,
+                                   initial_state=to_device(data["initial_state"], "f32"),
+                                   cu_seqlens=data["cu_seqlens"])
+    assert torch.equal(o3, o4[0]) and torch.equal(fs3, fs4)
+
+
+def test_library_is_the_one_loaded():
+    """The HIP library in the package directory is what runs (no fallback)."""
+    lib = lattn.load_library()
+    assert os.path.samefile(lib._name, lattn.LIB_PATH)
