@@ -29,8 +29,9 @@
 //     dmap() below so that they line up with Q's natural 8 consecutive dk values;
 //   * a (K Q^T) output tile pair, masked and converted, is directly the A operand
 //     of P V, with V read in the matching token order.
-// The state is kept in fp32 and fed to the Q S product as bf16 hi + lo (two MFMAs)
-// so that its rounding does not reach the output; o and the states are fp32.
+// The state is kept in fp32 and fed to the Q S product as bf16 hi + lo (two MFMAs),
+// and so is the masked intra-chunk matrix P in P V, so that neither rounding reaches
+// the output; o and the states are fp32.
 #include "lattn_launch.h"
 
 namespace lattn {
@@ -146,28 +147,64 @@ __device__ inline void make_lane_decay(float g2, int lr, int lg, LaneDecay& d) {
 }
 
 // ---------------------------------------------------------------------------
+// Global memory through raw buffer descriptors.  A descriptor covers exactly the
+// valid token rows of one chunk, so out-of-range loads return zero and
+// out-of-range stores are dropped by the hardware: partial chunks and the rows of
+// neighbouring packed sequences need no branches.  Offsets stay 32-bit because
+// every descriptor is rebased at its chunk.
+// ---------------------------------------------------------------------------
+constexpr int kRawBufferDword3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
+
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferDword3);
+}
+__device__ inline u32x4 buf_load_b128(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ inline float buf_load_f32(__amdgpu_buffer_rsrc_t r, int off) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ inline void buf_store_f32(float v, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane s
+// supplies the address of four consecutive 16-bit elements; lane i receives
+// element (i & 3) of the piece addressed by lane 4e + (i >> 2), as its element e.
+// With lane s pointing at row (r0 + (s >> 2)), columns c(s & 3) .. c(s & 3) + 3 of
+// a row-major tile, lane i therefore receives column c(i >> 2) + (i & 3) of rows
+// r0 .. r0 + 3: one column per lane, four consecutive rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline u32x2 lds_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
+__device__ inline bf16x8 cat_bf16(u32x2 a, u32x2 b) {
+    const u32x4 w = {a[0], a[1], b[0], b[1]};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+// ---------------------------------------------------------------------------
 // bf16 inputs: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
 // ---------------------------------------------------------------------------
 template <int DK, int NW>
 struct Bf16Cfg {
     static constexpr int BV = 16 * NW;
     static constexpr int NT = 64 * NW;
-    static constexpr int QLD = DK + 8;       // Q/K row stride in LDS (elements); +16 B breaks bank aliasing
-    static constexpr int TLD = kChunk + 8;   // K^T / V^T row stride in LDS (elements)
+    static constexpr int QLD = DK + 8;  // Q, K, decayed-K row stride in LDS (elements); +16 B against bank aliasing
+    static constexpr int VLD = BV + 16; // V row stride in LDS (elements)
     static constexpr int Q_ELEMS = kChunk * QLD;
-    static constexpr int KT_ELEMS = DK * TLD;
-    static constexpr int VT_ELEMS = BV * TLD;
-    static constexpr int STAGE_ELEMS = 2 * Q_ELEMS + KT_ELEMS + VT_ELEMS;
+    static constexpr int V_ELEMS = kChunk * VLD;
+    static constexpr int STAGE_ELEMS = 3 * Q_ELEMS + V_ELEMS;
     static constexpr int STAGES = (2 * STAGE_ELEMS * 2 <= kLdsBudget) ? 2 : 1;
-    static constexpr int KB = DK / 32;       // dk blocks of one MFMA
-    static constexpr int MT = DK / 16;       // state row tiles
-    static constexpr int QITEMS = kChunk * DK / 8;          // 16-byte pieces of a Q chunk
-    static constexpr int KITEMS = (kChunk / 4) * (DK / 8);  // 4-token x 8-dk blocks of K
-    static constexpr int VITEMS = (kChunk / 4) * (BV / 8);  // 4-token x 8-column blocks of V
-    static constexpr int QPER = (QITEMS + NT - 1) / NT;
-    static constexpr int KPER = (KITEMS + NT - 1) / NT;
-    static constexpr int VPER = (VITEMS + NT - 1) / NT;
+    static constexpr int KB = DK / 32;  // dk blocks of one MFMA
+    static constexpr int MT = DK / 16;  // state row tiles
+    static constexpr int QITEMS = kChunk * DK / 8;  // 16-byte pieces of a Q (or K) chunk
+    static constexpr int VITEMS = kChunk * BV / 8;  // 16-byte pieces of a V chunk block
+    static constexpr int QPER = QITEMS / NT;
+    static constexpr int VPER = VITEMS / NT;
     static_assert(DK % 32 == 0 && DK <= 256, "dk must be a multiple of 32 up to 256");
+    static_assert(QITEMS % NT == 0 && VITEMS % NT == 0, "staging pieces must divide evenly");
     static_assert(STAGES * STAGE_ELEMS * 2 <= kLdsBudget, "LDS budget");
 };
 
@@ -192,7 +229,7 @@ __device__ inline void split_state(const f32x4* S, bf16x8* hi, bf16x8* lo) {
 template <int DK, int NW, bool REV>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p) {
     using Cfg = Bf16Cfg<DK, NW>;
-    constexpr int BV = Cfg::BV, NT = Cfg::NT, QLD = Cfg::QLD, TLD = Cfg::TLD;
+    constexpr int BV = Cfg::BV, NT = Cfg::NT, QLD = Cfg::QLD, VLD = Cfg::VLD;
     constexpr int KB = Cfg::KB, MT = Cfg::MT;
     __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::STAGES * Cfg::STAGE_ELEMS];
 
@@ -200,142 +237,134 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
     if (!decode_work(p, wk)) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, lr = lane & 15, lg = lane >> 4;
-    const float g2 = p.g_gamma[wk.h] * kLog2e;
-    const int64_t L = wk.len;
-    const int nch = (int)((L + kChunk - 1) / kChunk);
-    const int H = p.num_heads, dv = p.dv;
-    const int vcol = wk.vb * BV + 16 * wv + lr;  // this lane's value column
+    const float g2 = p.g_gamma[wk.h] * kLog2e;  // log2 of the per-step decay
+    const int L = (int)wk.len;
+    const int nch = (L + kChunk - 1) / kChunk;
+    const int H = p.num_heads, Hkv = p.num_kv_heads, dv = p.dv;
+    const int col = 16 * wv + lr;  // this lane's value column inside the block
+    const uint32_t qrow_b = (uint32_t)H * DK * 2, krow_b = (uint32_t)Hkv * DK * 2;
+    const uint32_t vrow_b = (uint32_t)Hkv * dv * 2, orow_b = (uint32_t)H * dv * 4;
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q);
+    const uint16_t* kg = static_cast<const uint16_t*>(p.k);
+    const uint16_t* vg = static_cast<const uint16_t*>(p.v);
 
-    const uint16_t* qbase = static_cast<const uint16_t*>(p.q) + (int64_t)wk.h * DK;
-    const uint16_t* kbase = static_cast<const uint16_t*>(p.k) + (int64_t)wk.kvh * DK;
-    const uint16_t* vbase = static_cast<const uint16_t*>(p.v) + (int64_t)wk.kvh * dv + wk.vb * BV;
-    const int64_t qstride = (int64_t)H * DK;
-    const int64_t kstride = (int64_t)p.num_kv_heads * DK;
-    const int64_t vstride = (int64_t)p.num_kv_heads * dv;
-    auto tok_row = [&](int64_t pos) -> int64_t { return REV ? wk.start + L - 1 - pos : wk.start + pos; };
-
-    LaneDecay dec;
-    make_lane_decay(g2, lr, lg, dec);
+    // Decay factors, all with non-negative exponents and with `scale` folded in.
+    // Mask of (K Q^T) tile (a, b): diagonal tiles use dg[ii] = lam^(lr - 4lg - ii)
+    // (0 above the diagonal); tile b - a = d > 0 uses od[d-1][ii] = lam^(16d + lr - 4lg - ii).
+    const float sc = p.scale;
+    float dg[4], od[3][4], lamq[4][4];
+#pragma unroll
+    for (int ii = 0; ii < 4; ++ii) {
+        const int e = lr - 4 * lg - ii;
+        dg[ii] = e >= 0 ? sc * exp2f(g2 * (float)e) : 0.f;
+#pragma unroll
+        for (int d = 1; d <= 3; ++d) od[d - 1][ii] = sc * exp2f(g2 * (float)(16 * d + e));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) lamq[b][ii] = sc * exp2f(g2 * (float)(16 * b + 4 * lg + ii + 1));
+    }
     const float lamC = exp2f(g2 * (float)kChunk);
 
-    // State block: tile mt holds rows dmap(mt, 4*lg + ii), column vcol.
+    // State block: tile mt holds rows dmap(mt, 4*lg + ii) at column `col`.
     f32x4 S[MT];
-    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
+    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv + (int64_t)wk.vb * BV;
+    {
+        const auto ri = make_rsrc(p.init ? p.init + st_off : p.final_state, p.init ? (uint32_t)(DK * dv * 4) : 0u);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            S[mt][ii] = p.init ? p.init[st_off + (int64_t)dmap(mt, 4 * lg + ii) * dv + vcol] : 0.f;
+            for (int ii = 0; ii < 4; ++ii) S[mt][ii] = buf_load_f32(ri, (dmap(mt, 4 * lg + ii) * dv + col) * 4);
+    }
     bf16x8 Shi[KB], Slo[KB];
     split_state<KB>(S, Shi, Slo);
 
-    // ---- staging: global -> registers (prefetch) -> LDS ----
-    u32x4 pq[Cfg::QPER];
-    u32x4 pk[Cfg::KPER][4];
-    u32x4 pv[Cfg::VPER][4];
-    const u32x4 zero4 = {0u, 0u, 0u, 0u};
+    // Staging: thread piece s covers row r = item / (pieces per row) of the chunk.
+    u32x4 pq[Cfg::QPER], pk[Cfg::QPER], pv[Cfg::VPER];
+    float wfull[Cfg::QPER];  // lam^(C-1-r): decay of key row r to the end of a full chunk
+#pragma unroll
+    for (int s = 0; s < Cfg::QPER; ++s) wfull[s] = exp2f(g2 * (float)(kChunk - 1 - (tid + s * NT) / (DK / 8)));
+
+    auto first_row = [&](int p0, int Lc) -> int64_t { return REV ? wk.start + L - p0 - Lc : wk.start + p0; };
 
     auto load_chunk = [&](int c) {
-        const int64_t p0 = (int64_t)c * kChunk;
+        const int p0 = c * kChunk, Lc = min(kChunk, L - p0);
+        const int64_t r0 = first_row(p0, Lc);
+        const auto rq = make_rsrc(qg + (r0 * H + wk.h) * DK, (uint32_t)(Lc - 1) * qrow_b + DK * 2);
+        const auto rk = make_rsrc(kg + (r0 * Hkv + wk.kvh) * DK, (uint32_t)(Lc - 1) * krow_b + DK * 2);
+        const auto rv = make_rsrc(vg + (r0 * Hkv + wk.kvh) * dv + wk.vb * BV, (uint32_t)(Lc - 1) * vrow_b + BV * 2);
 #pragma unroll
         for (int s = 0; s < Cfg::QPER; ++s) {
-            const int item = tid + s * NT;
-            pq[s] = zero4;
-            if (item < Cfg::QITEMS) {
-                const int r = item / (DK / 8), c8 = item % (DK / 8);
-                if (p0 + r < L) pq[s] = *reinterpret_cast<const u32x4*>(qbase + tok_row(p0 + r) * qstride + c8 * 8);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = tid + s * NT;
-            const int tg = item / (DK / 8), c8 = item % (DK / 8);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                pk[s][u] = zero4;
-                if (item < Cfg::KITEMS && p0 + 4 * tg + u < L)
-                    pk[s][u] = *reinterpret_cast<const u32x4*>(kbase + tok_row(p0 + 4 * tg + u) * kstride + c8 * 8);
-            }
+            const int item = tid + s * NT, r = item / (DK / 8), c8 = item % (DK / 8);
+            const int rs = REV ? Lc - 1 - r : r;  // row relative to r0; out of range past the end
+            pq[s] = buf_load_b128(rq, rs * (int)qrow_b + c8 * 16);
+            pk[s] = buf_load_b128(rk, rs * (int)krow_b + c8 * 16);
         }
 #pragma unroll
         for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = tid + s * NT;
-            const int tg = item / (BV / 8), c8 = item % (BV / 8);
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                pv[s][u] = zero4;
-                if (item < Cfg::VITEMS && p0 + 4 * tg + u < L)
-                    pv[s][u] = *reinterpret_cast<const u32x4*>(vbase + tok_row(p0 + 4 * tg + u) * vstride + c8 * 8);
-            }
+            const int item = tid + s * NT, r = item / (BV / 8), c8 = item % (BV / 8);
+            const int rs = REV ? Lc - 1 - r : r;
+            pv[s] = buf_load_b128(rv, rs * (int)vrow_b + c8 * 16);
         }
     };
 
     auto store_chunk = [&](int c, uint16_t* st) {
         uint16_t* Qs = st;
         uint16_t* Ks = st + Cfg::Q_ELEMS;
-        uint16_t* Kt = Ks + Cfg::Q_ELEMS;
-        uint16_t* Vt = Kt + Cfg::KT_ELEMS;
-        const int Lc = (int)min((int64_t)kChunk, L - (int64_t)c * kChunk);
+        uint16_t* Kd = Ks + Cfg::Q_ELEMS;  // keys decayed to the chunk end
+        uint16_t* Vs = Kd + Cfg::Q_ELEMS;
+        const int Lc = min(kChunk, L - c * kChunk);
 #pragma unroll
         for (int s = 0; s < Cfg::QPER; ++s) {
-            const int item = tid + s * NT;
-            if (item < Cfg::QITEMS) {
-                const int r = item / (DK / 8), c8 = item % (DK / 8);
-                lds_store<u32x4>(Qs + r * QLD + c8 * 8, pq[s]);
-            }
-        }
+            const int item = tid + s * NT, r = item / (DK / 8), c8 = item % (DK / 8);
+            lds_store<u32x4>(Qs + r * QLD + c8 * 8, pq[s]);
+            lds_store<u32x4>(Ks + r * QLD + c8 * 8, pk[s]);
+            const float w = Lc == kChunk ? wfull[s] : (r < Lc ? exp2f(g2 * (float)(Lc - 1 - r)) : 0.f);
+            u32x4 d;
 #pragma unroll
-        for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = tid + s * NT;
-            if (item < Cfg::KITEMS) {
-                const int tg = item / (DK / 8), c8 = item % (DK / 8);
-                float wgt[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    lds_store<u32x4>(Ks + (4 * tg + u) * QLD + c8 * 8, pk[s][u]);
-                    const int tok = 4 * tg + u;
-                    wgt[u] = tok < Lc ? exp2f(g2 * (float)(Lc - 1 - tok)) : 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float k0 = bf16_half(pk[s][0][e >> 1], e & 1) * wgt[0];
-                    const float k1 = bf16_half(pk[s][1][e >> 1], e & 1) * wgt[1];
-                    const float k2 = bf16_half(pk[s][2][e >> 1], e & 1) * wgt[2];
-                    const float k3 = bf16_half(pk[s][3][e >> 1], e & 1) * wgt[3];
-                    const u32x2 val = {pack_bf16x2(k0, k1), pack_bf16x2(k2, k3)};
-                    lds_store<u32x2>(Kt + (c8 * 8 + e) * TLD + 4 * tg, val);
-                }
-            }
+            for (int e = 0; e < 4; ++e) d[e] = pack_bf16x2(bf16_lo(pk[s][e]) * w, bf16_hi(pk[s][e]) * w);
+            lds_store<u32x4>(Kd + r * QLD + c8 * 8, d);
         }
 #pragma unroll
         for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = tid + s * NT;
-            if (item < Cfg::VITEMS) {
-                const int tg = item / (BV / 8), c8 = item % (BV / 8);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t v0 = half16(pv[s][0][e >> 1], e & 1), v1 = half16(pv[s][1][e >> 1], e & 1);
-                    const uint32_t v2 = half16(pv[s][2][e >> 1], e & 1), v3 = half16(pv[s][3][e >> 1], e & 1);
-                    const u32x2 val = {v0 | (v1 << 16), v2 | (v3 << 16)};
-                    lds_store<u32x2>(Vt + (c8 * 8 + e) * TLD + 4 * tg, val);
-                }
-            }
+            const int item = tid + s * NT, r = item / (BV / 8), c8 = item % (BV / 8);
+            lds_store<u32x4>(Vs + r * VLD + c8 * 8, pv[s]);
         }
     };
 
     auto compute_chunk = [&](int c, const uint16_t* st) {
         const uint16_t* Qs = st;
         const uint16_t* Ks = st + Cfg::Q_ELEMS;
-        const uint16_t* Kt = Ks + Cfg::Q_ELEMS;
-        const uint16_t* Vt = Kt + Cfg::KT_ELEMS;
+        const uint16_t* Kd = Ks + Cfg::Q_ELEMS;
+        const uint16_t* Vs = Kd + Cfg::Q_ELEMS;
+        const int p0 = c * kChunk, Lc = min(kChunk, L - p0);
+
+        // S <- lam^Lc S + Kd^T V.  Operands by transposing reads of the row-major
+        // tiles: lane group lg takes tokens 32kb + 8lg + 0..7; the A operand row of
+        // lane lr is dk dmap(mt, lr), the B operand column is `col`.
+        const float lamL = (Lc == kChunk) ? lamC : exp2f(g2 * (float)Lc);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) S[mt] *= lamL;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int jr = 32 * kb + 8 * lg + (lr >> 2);  // token row this lane addresses
+            const uint16_t* vp = Vs + jr * VLD + 16 * wv + 4 * (lr & 3);
+            const bf16x8 vop = cat_bf16(lds_tr16(vp), lds_tr16(vp + 4 * VLD));
+            bf16x8 kop[MT];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const uint16_t* kp = Kd + jr * QLD + 32 * (mt >> 1) + 8 * (lr & 3) + 4 * (mt & 1);
+                kop[mt] = cat_bf16(lds_tr16(kp), lds_tr16(kp + 4 * QLD));
+            }
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_bf16(kop[mt], vop, S[mt]);
+        }
+
+        // A^T = K Q^T (lower-triangle tiles) and Q S_prev, sharing the Q operands.
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 O[4], At[10];
 #pragma unroll
         for (int b = 0; b < 4; ++b) O[b] = z;
 #pragma unroll
         for (int t = 0; t < 10; ++t) At[t] = z;
-
-        // A^T = K Q^T (lower-triangle tiles) and Q S, sharing the Q operands.
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             bf16x8 qa[4], ka[4];
@@ -352,87 +381,81 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
                 O[b] = mfma_bf16(qa[b], Slo[kb], O[b]);
             }
         }
-        // Inter-chunk part decays by lam^(i+1).
+        // The inter-chunk part decays by lam^(i+1) (times scale).
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[b][ii] *= dec.lamq[b][ii];
+            for (int ii = 0; ii < 4; ++ii) O[b][ii] *= lamq[b][ii];
 
-        // P = (A .* M) as the A operand of P V: for row tile b and token block kb,
-        // elements 0..3 come from tile (2kb, b), 4..7 from tile (2kb+1, b).
-        bf16x8 P[4][2];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-#pragma unroll
-            for (int kb = 0; 2 * kb <= b; ++kb) {
-                const int t0 = tidx(2 * kb, b);
-                u32x4 w;
-                w[0] = pack_bf16x2(At[t0][0] * dec.mask[t0][0], At[t0][1] * dec.mask[t0][1]);
-                w[1] = pack_bf16x2(At[t0][2] * dec.mask[t0][2], At[t0][3] * dec.mask[t0][3]);
-                if (2 * kb + 1 <= b) {
-                    const int t1 = tidx(2 * kb + 1, b);
-                    w[2] = pack_bf16x2(At[t1][0] * dec.mask[t1][0], At[t1][1] * dec.mask[t1][1]);
-                    w[3] = pack_bf16x2(At[t1][2] * dec.mask[t1][2], At[t1][3] * dec.mask[t1][3]);
-                } else {
-                    w[2] = 0u;
-                    w[3] = 0u;
-                }
-                P[b][kb] = __builtin_bit_cast(bf16x8, w);
-            }
-        }
-        // O += P V  (token order matching P: 4 from each half of the 32-token block)
+        // O += P V with P = scale (A .* M) in bf16 hi + lo.  For row tile b and token block
+        // kb, elements 0..3 come from tile (2kb, b) and 4..7 from tile (2kb+1, b),
+        // i.e. tokens 32kb + 4lg + 0..3 and 32kb + 16 + 4lg + 0..3; V is read in
+        // the same token order.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const uint16_t* vr = Vt + (16 * wv + lr) * TLD + 32 * kb + 4 * lg;
-            const u32x2 lo = lds_load<u32x2>(vr);
-            const u32x2 hi = lds_load<u32x2>(vr + 16);
-            const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, w);
+            const uint16_t* vp = Vs + (32 * kb + 4 * lg + (lr >> 2)) * VLD + 16 * wv + 4 * (lr & 3);
+            const bf16x8 vop = cat_bf16(lds_tr16(vp), lds_tr16(vp + 16 * VLD));
 #pragma unroll
-            for (int b = 2 * kb; b < 4; ++b) O[b] = mfma_bf16(P[b][kb], vop, O[b]);
+            for (int b = 2 * kb; b < 4; ++b) {
+                float pvals[8];
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const int a = 2 * kb + half;
+                    const int t = tidx(a, b);           // in range for a = b + 1 too; unused then
+                    const int d = a < b ? b - a - 1 : 0;  // off-diagonal distance - 1
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const float m = (a == b) ? dg[ii] : od[d][ii];
+                        pvals[4 * half + ii] = (a <= b) ? At[t][ii] * m : 0.f;
+                    }
+                }
+                u32x4 wh, wl;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t w = pack_bf16x2(pvals[2 * e], pvals[2 * e + 1]);
+                    wh[e] = w;
+                    wl[e] = pack_bf16x2(pvals[2 * e] - bf16_lo(w), pvals[2 * e + 1] - bf16_hi(w));
+                }
+                O[b] = mfma_bf16(__builtin_bit_cast(bf16x8, wh), vop, O[b]);
+                O[b] = mfma_bf16(__builtin_bit_cast(bf16x8, wl), vop, O[b]);
+            }
         }
-        // Store o rows of this chunk.
-        const int64_t p0 = (int64_t)c * kChunk;
+
+        // Store the chunk's outputs; rows past the end fall outside the descriptor.
+        const int64_t r0 = first_row(p0, Lc);
+        const auto ro = make_rsrc(p.o + (r0 * H + wk.h) * dv + wk.vb * BV, (uint32_t)(Lc - 1) * orow_b + BV * 4);
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * b + 4 * lg + ii;
-                if (p0 + i < L) p.o[(tok_row(p0 + i) * H + wk.h) * dv + vcol] = p.scale * O[b][ii];
+                const int rs = REV ? Lc - 1 - i : i;
+                buf_store_f32(O[b][ii], ro, rs * (int)orow_b + col * 4);
             }
 
-        // S <- lam^Lc S + (decayed K)^T V
-        const int Lc = (int)min((int64_t)kChunk, L - p0);
-        const float lamL = (Lc == kChunk) ? lamC : exp2f(g2 * (float)Lc);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) S[mt] *= lamL;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const bf16x8 vop = lds_load<bf16x8>(Vt + (16 * wv + lr) * TLD + 32 * kb + 8 * lg);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const bf16x8 kop = lds_load<bf16x8>(Kt + dmap(mt, lr) * TLD + 32 * kb + 8 * lg);
-                S[mt] = mfma_bf16(kop, vop, S[mt]);
-            }
-        }
         split_state<KB>(S, Shi, Slo);
     };
 
-    if (nch > 0) load_chunk(0);
-    for (int c = 0; c < nch; ++c) {
+    auto iteration = [&](int c) {
         uint16_t* st = smem + (Cfg::STAGES == 2 ? (c & 1) * Cfg::STAGE_ELEMS : 0);
         if (Cfg::STAGES == 1) __syncthreads();
         store_chunk(c, st);
         if (c + 1 < nch) load_chunk(c + 1);
         __syncthreads();
         compute_chunk(c, st);
+    };
+    // The first chunk is peeled so that, inside the loop, the wait for the
+    // prefetched loads never has to include the previous chunk's output stores.
+    if (nch > 0) {
+        load_chunk(0);
+        iteration(0);
     }
+    for (int c = 1; c < nch; ++c) iteration(c);
 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            p.final_state[st_off + (int64_t)dmap(mt, 4 * lg + ii) * dv + vcol] = S[mt][ii];
+        for (int ii = 0; ii < 4; ++ii) p.final_state[st_off + (int64_t)dmap(mt, 4 * lg + ii) * dv + col] = S[mt][ii];
 }
 
 // ---------------------------------------------------------------------------
