@@ -17,6 +17,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     # packed fp32 instructions stay off (hipcc's host pass warns it does not know the feature)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in VGPRs: the register budget fits, and it avoids
+    # moving every accumulator between AGPRs and VGPRs for the VALU steps
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
 ]

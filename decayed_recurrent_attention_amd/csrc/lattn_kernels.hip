@@ -115,6 +115,7 @@ __device__ inline void lds_store(void* p, T v) {
 
 // Index of (K Q^T) tile (a, b), a <= b, among the 10 lower-triangle tiles of a chunk.
 __host__ __device__ constexpr int tidx(int a, int b) { return b * (b + 1) / 2 + a; }
+__host__ __device__ constexpr int tile_b(int t) { return t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3; }
 
 // dk index of row m of state tile mt (bf16 path): tiles 2kb and 2kb+1 interleave in
 // groups of four so that lane group g of the tile pair holds dk 32kb + 8g + 0..7.
@@ -191,12 +192,22 @@ template <int DK, int NW>
 struct Bf16Cfg {
     static constexpr int BV = 16 * NW;
     static constexpr int NT = 64 * NW;
-    static constexpr int QLD = DK + 8;  // Q, K, decayed-K row stride in LDS (elements); +16 B against bank aliasing
-    static constexpr int VLD = BV + 16; // V row stride in LDS (elements)
+    // Q and K row stride in LDS (elements).  The 16-byte operand reads of a
+    // half-wave touch 16 rows x 2 pieces; a stride of 8 * (odd * 2) elements puts
+    // those 32 pieces in distinct banks.
+    static constexpr int QLD = DK + 16;
+    // Decayed-K row stride: the transposing reads touch 4 rows x 4 pieces 16 B apart;
+    // a stride of 16 or 48 dwords (mod 64) keeps those 16 pieces in distinct banks.
+    static constexpr int KDLD = DK + (DK == 32 ? 64 : 32);
+    static constexpr int VLD = BV + 16;  // V row stride in LDS (elements)
     static constexpr int Q_ELEMS = kChunk * QLD;
+    static constexpr int KD_ELEMS = kChunk * KDLD;
     static constexpr int V_ELEMS = kChunk * VLD;
-    static constexpr int STAGE_ELEMS = 3 * Q_ELEMS + V_ELEMS;
-    static constexpr int STAGES = (2 * STAGE_ELEMS * 2 <= kLdsBudget) ? 2 : 1;
+    static constexpr int STAGE_ELEMS = 2 * Q_ELEMS + KD_ELEMS + V_ELEMS;
+    // Masked intra-chunk matrix P, exchanged between waves in MFMA A-operand layout:
+    // 6 operand blocks (row tile b, token block kb) x {hi, lo} x 64 lanes x 8 values.
+    static constexpr int P_ELEMS = 6 * 2 * 64 * 8;
+    static constexpr int STAGES = (2 * (2 * STAGE_ELEMS + P_ELEMS) <= kLdsBudget) ? 2 : 1;
     static constexpr int KB = DK / 32;  // dk blocks of one MFMA
     static constexpr int MT = DK / 16;  // state row tiles
     static constexpr int QITEMS = kChunk * DK / 8;  // 16-byte pieces of a Q (or K) chunk
@@ -205,7 +216,17 @@ struct Bf16Cfg {
     static constexpr int VPER = VITEMS / NT;
     static_assert(DK % 32 == 0 && DK <= 256, "dk must be a multiple of 32 up to 256");
     static_assert(QITEMS % NT == 0 && VITEMS % NT == 0, "staging pieces must divide evenly");
-    static_assert(STAGES * STAGE_ELEMS * 2 <= kLdsBudget, "LDS budget");
+    static_assert((STAGES * STAGE_ELEMS + P_ELEMS) * 2 <= kLdsBudget, "LDS budget");
+};
+
+// Operand block of P for row tile b and token block kb (2kb <= b): 0..5.
+__host__ __device__ constexpr int pidx(int b, int kb) { return b < 2 ? b : 2 + 2 * (b - 2) + kb; }
+// Tile coordinates of lower-triangle (K Q^T) tile t = tidx(a, b).
+__host__ __device__ constexpr int tile_a(int t) { return t - tile_b(t) * (tile_b(t) + 1) / 2; }
+
+template <int V>
+struct IntC {
+    static constexpr int value = V;
 };
 
 template <int KB>
@@ -231,13 +252,24 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
     using Cfg = Bf16Cfg<DK, NW>;
     constexpr int BV = Cfg::BV, NT = Cfg::NT, QLD = Cfg::QLD, VLD = Cfg::VLD;
     constexpr int KB = Cfg::KB, MT = Cfg::MT;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::STAGES * Cfg::STAGE_ELEMS];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::STAGES * Cfg::STAGE_ELEMS + Cfg::P_ELEMS];
+    uint16_t* Pbuf = smem + Cfg::STAGES * Cfg::STAGE_ELEMS;
 
     Work wk;
     if (!decode_work(p, wk)) return;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6, lr = lane & 15, lg = lane >> 4;
+    const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const float g2 = p.g_gamma[wk.h] * kLog2e;  // log2 of the per-step decay
+    // Tiles (1, 0) and (3, 2) lie above the diagonal: their halves of P stay zero.
+    if (tid < 64) {
+        const u32x2 z2 = {0u, 0u};
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) {
+            lds_store<u32x2>(Pbuf + ((pidx(0, 0) * 2 + hl) * 64 + tid) * 8 + 4, z2);
+            lds_store<u32x2>(Pbuf + ((pidx(2, 1) * 2 + hl) * 64 + tid) * 8 + 4, z2);
+        }
+    }
     const int L = (int)wk.len;
     const int nch = (L + kChunk - 1) / kChunk;
     const int H = p.num_heads, Hkv = p.num_kv_heads, dv = p.dv;
@@ -310,7 +342,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
         uint16_t* Qs = st;
         uint16_t* Ks = st + Cfg::Q_ELEMS;
         uint16_t* Kd = Ks + Cfg::Q_ELEMS;  // keys decayed to the chunk end
-        uint16_t* Vs = Kd + Cfg::Q_ELEMS;
+        uint16_t* Vs = Kd + Cfg::KD_ELEMS;
         const int Lc = min(kChunk, L - c * kChunk);
 #pragma unroll
         for (int s = 0; s < Cfg::QPER; ++s) {
@@ -321,7 +353,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
             u32x4 d;
 #pragma unroll
             for (int e = 0; e < 4; ++e) d[e] = pack_bf16x2(bf16_lo(pk[s][e]) * w, bf16_hi(pk[s][e]) * w);
-            lds_store<u32x4>(Kd + r * QLD + c8 * 8, d);
+            lds_store<u32x4>(Kd + r * Cfg::KDLD + c8 * 8, d);
         }
 #pragma unroll
         for (int s = 0; s < Cfg::VPER; ++s) {
@@ -334,8 +366,9 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
         const uint16_t* Qs = st;
         const uint16_t* Ks = st + Cfg::Q_ELEMS;
         const uint16_t* Kd = Ks + Cfg::Q_ELEMS;
-        const uint16_t* Vs = Kd + Cfg::Q_ELEMS;
+        const uint16_t* Vs = Kd + Cfg::KD_ELEMS;
         const int p0 = c * kChunk, Lc = min(kChunk, L - p0);
+        constexpr int KDLD = Cfg::KDLD;
 
         // S <- lam^Lc S + Kd^T V.  Operands by transposing reads of the row-major
         // tiles: lane group lg takes tokens 32kb + 8lg + 0..7; the A operand row of
@@ -351,34 +384,73 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
             bf16x8 kop[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const uint16_t* kp = Kd + jr * QLD + 32 * (mt >> 1) + 8 * (lr & 3) + 4 * (mt & 1);
-                kop[mt] = cat_bf16(lds_tr16(kp), lds_tr16(kp + 4 * QLD));
+                const uint16_t* kp = Kd + jr * KDLD + 32 * (mt >> 1) + 8 * (lr & 3) + 4 * (mt & 1);
+                kop[mt] = cat_bf16(lds_tr16(kp), lds_tr16(kp + 4 * KDLD));
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_bf16(kop[mt], vop, S[mt]);
         }
 
-        // A^T = K Q^T (lower-triangle tiles) and Q S_prev, sharing the Q operands.
+        // Q S_prev for all 64 rows of this wave's columns, and this wave's share of
+        // the ten lower-triangle (K Q^T) tiles: tiles t = wv, wv + NW, ... (round
+        // robin).  Each wave masks its tiles and publishes P = scale (A .* M) in
+        // bf16 hi + lo to LDS in A-operand layout; all waves then read all of P.
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 O[4], At[10];
+        f32x4 O[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) O[b] = z;
+        auto qs_and_tiles = [&](auto wconst) {
+            constexpr int W = decltype(wconst)::value;
+            constexpr int NTILE = (10 - W + NW - 1) / NW;
+            f32x4 At[NTILE];
 #pragma unroll
-        for (int t = 0; t < 10; ++t) At[t] = z;
+            for (int s = 0; s < NTILE; ++s) At[s] = z;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            bf16x8 qa[4], ka[4];
+            for (int kb = 0; kb < KB; ++kb) {
+                bf16x8 qa[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                qa[r] = lds_load<bf16x8>(Qs + (16 * r + lr) * QLD + 32 * kb + 8 * lg);
-                ka[r] = lds_load<bf16x8>(Ks + (16 * r + lr) * QLD + 32 * kb + 8 * lg);
+                for (int r = 0; r < 4; ++r) qa[r] = lds_load<bf16x8>(Qs + (16 * r + lr) * QLD + 32 * kb + 8 * lg);
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    O[b] = mfma_bf16(qa[b], Shi[kb], O[b]);
+                    O[b] = mfma_bf16(qa[b], Slo[kb], O[b]);
+                }
+#pragma unroll
+                for (int s = 0; s < NTILE; ++s) {
+                    constexpr int T0 = W;  // first tile of this wave
+                    const int t = T0 + s * NW;
+                    const int a = tile_a(t), b = tile_b(t);
+                    const bf16x8 ka = lds_load<bf16x8>(Ks + (16 * a + lr) * QLD + 32 * kb + 8 * lg);
+                    At[s] = mfma_bf16(ka, qa[b], At[s]);
+                }
             }
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int s = 0; s < NTILE; ++s) {
+                const int t = W + s * NW;
+                const int a = tile_a(t), b = tile_b(t);
+                float pv4[4];
 #pragma unroll
-                for (int a = 0; a <= b; ++a) At[tidx(a, b)] = mfma_bf16(ka[a], qa[b], At[tidx(a, b)]);
-                O[b] = mfma_bf16(qa[b], Shi[kb], O[b]);
-                O[b] = mfma_bf16(qa[b], Slo[kb], O[b]);
+                for (int ii = 0; ii < 4; ++ii) pv4[ii] = At[s][ii] * (a == b ? dg[ii] : od[a < b ? b - a - 1 : 0][ii]);
+                const uint32_t h0 = pack_bf16x2(pv4[0], pv4[1]), h1 = pack_bf16x2(pv4[2], pv4[3]);
+                const uint32_t l0 = pack_bf16x2(pv4[0] - bf16_lo(h0), pv4[1] - bf16_hi(h0));
+                const uint32_t l1 = pack_bf16x2(pv4[2] - bf16_lo(h1), pv4[3] - bf16_hi(h1));
+                uint16_t* dst = Pbuf + (pidx(b, a >> 1) * 2 * 64 + lane) * 8 + 4 * (a & 1);
+                const u32x2 hv = {h0, h1}, lv = {l0, l1};
+                lds_store<u32x2>(dst, hv);
+                lds_store<u32x2>(dst + 64 * 8, lv);
+            }
+        };
+        if constexpr (NW == 1) {
+            qs_and_tiles(IntC<0>{});
+        } else if constexpr (NW == 2) {
+            if (wv == 0) qs_and_tiles(IntC<0>{});
+            else qs_and_tiles(IntC<1>{});
+        } else {
+            switch (wv) {
+                case 0: qs_and_tiles(IntC<0>{}); break;
+                case 1: qs_and_tiles(IntC<1>{}); break;
+                case 2: qs_and_tiles(IntC<2>{}); break;
+                default: qs_and_tiles(IntC<3>{}); break;
             }
         }
         // The inter-chunk part decays by lam^(i+1) (times scale).
@@ -386,38 +458,20 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) O[b][ii] *= lamq[b][ii];
+        __syncthreads();  // P complete
 
-        // O += P V with P = scale (A .* M) in bf16 hi + lo.  For row tile b and token block
-        // kb, elements 0..3 come from tile (2kb, b) and 4..7 from tile (2kb+1, b),
-        // i.e. tokens 32kb + 4lg + 0..3 and 32kb + 16 + 4lg + 0..3; V is read in
-        // the same token order.
+        // O += P V.  For row tile b and token block kb, P elements 0..3 are tokens
+        // 32kb + 4lg + 0..3 and 4..7 are 32kb + 16 + 4lg + 0..3; V is read in the
+        // same token order.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const uint16_t* vp = Vs + (32 * kb + 4 * lg + (lr >> 2)) * VLD + 16 * wv + 4 * (lr & 3);
             const bf16x8 vop = cat_bf16(lds_tr16(vp), lds_tr16(vp + 16 * VLD));
 #pragma unroll
             for (int b = 2 * kb; b < 4; ++b) {
-                float pvals[8];
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    const int a = 2 * kb + half;
-                    const int t = tidx(a, b);           // in range for a = b + 1 too; unused then
-                    const int d = a < b ? b - a - 1 : 0;  // off-diagonal distance - 1
-#pragma unroll
-                    for (int ii = 0; ii < 4; ++ii) {
-                        const float m = (a == b) ? dg[ii] : od[d][ii];
-                        pvals[4 * half + ii] = (a <= b) ? At[t][ii] * m : 0.f;
-                    }
-                }
-                u32x4 wh, wl;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t w = pack_bf16x2(pvals[2 * e], pvals[2 * e + 1]);
-                    wh[e] = w;
-                    wl[e] = pack_bf16x2(pvals[2 * e] - bf16_lo(w), pvals[2 * e + 1] - bf16_hi(w));
-                }
-                O[b] = mfma_bf16(__builtin_bit_cast(bf16x8, wh), vop, O[b]);
-                O[b] = mfma_bf16(__builtin_bit_cast(bf16x8, wl), vop, O[b]);
+                const uint16_t* pp = Pbuf + (pidx(b, kb) * 2 * 64 + lane) * 8;
+                O[b] = mfma_bf16(lds_load<bf16x8>(pp), vop, O[b]);
+                O[b] = mfma_bf16(lds_load<bf16x8>(pp + 64 * 8), vop, O[b]);
             }
         }
 
