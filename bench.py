@@ -56,15 +56,14 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, data, seconds_target: float):
+def cpu_baseline(w, data):
     """Time the oracle on a bounded set of (batch row, head) pairs of the workload."""
     import oracle
 
     orc = oracle.load()
     threads = orc.set_threads(0)
-    n_pairs = max(1, min(w.batch * w.num_heads, 2 * threads))
-    pairs = [(i % w.batch, (i * 7) % w.num_heads) for i in range(n_pairs)]
-    pairs = list(dict.fromkeys(pairs))
+    n_pairs = max(1, min(w.batch * w.num_heads, 4 * threads))
+    pairs = [(b, h) for h in range(w.num_heads) for b in range(w.batch)][:n_pairs]
     g = orc.lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers)
     t0 = time.perf_counter()
     orc.recurrent_fwd(data["q"], data["k"], data["v"], g, w.scale, pairs=pairs)
@@ -178,7 +177,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, data, 10.0)
+        line["cpu_baseline"] = cpu_baseline(w, data)
     print(json.dumps(line), flush=True)
 
 

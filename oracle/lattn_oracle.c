@@ -24,7 +24,9 @@
  *   - scale multiplies q (lightning_attn page, softmax_scale argument), so it
  *     scales o and never the state.
  *   - GQA: query head h reads kv head h / (H / Hkv) (grouped, contiguous);
- *     decay and state are per query head.
+ *     decay and state are per query head.  The pages fix no grouping, so this
+ *     convention is parity unpinned against them: the pins check it only
+ *     against an independent statement of the same convention.
  *   - reverse: the same recurrence run from the last position to the first;
  *     o_t stays at index t; initial_state enters at the last position.
  *   - packed varlen (cu_seqlens): the state restarts at every boundary and
