@@ -186,42 +186,96 @@ __device__ inline bf16x8 cat_bf16(u32x2 a, u32x2 b) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS copies (buffer_load_dwordx4 ... lds).  One instruction moves
+// 16 bytes per lane to LDS address M0 + 16 * lane, so a wave fills one contiguous
+// kilobyte while each lane picks its own source.  The copies are issued from
+// inline assembly: the compiler would otherwise make every later LDS access wait
+// for all of them.  Their completion is awaited explicitly (vmcnt) before the
+// barrier that publishes a stage, and every barrier in the chunk loop waits for
+// LDS operations only.
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+struct RawBuf {
+    i32x4 d;  // raw buffer descriptor (base, stride 0, size in bytes, gfx9 raw format)
+};
+__device__ inline RawBuf raw_buf(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    RawBuf r;
+    r.d = i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kRawBufferDword3};
+    return r;
+}
+__device__ inline uint32_t lds_addr(const void* p) {
+    typedef __attribute__((address_space(3))) const void* lds_ptr;
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)p);
+}
+__device__ inline void copy16_to_lds(uint32_t lds_base, const RawBuf& r, int voffset) {
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :
+                 : "s"(lds_base), "v"(voffset), "s"(r.d)
+                 : "memory", "m0");
+}
+template <int N>
+__device__ inline void wait_vmem() {  // at most N vector-memory operations outstanding
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ inline void lds_barrier() {  // this wave's LDS accesses done, then workgroup barrier
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+// ---------------------------------------------------------------------------
 // bf16 inputs: v_mfma_f32_16x16x32_bf16, fp32 accumulation.
 // ---------------------------------------------------------------------------
+// XOR swizzles of the 16-byte blocks of a row (rows are unpadded), chosen with the
+// measured gfx950 bank behaviour (a half-wave's 16-byte reads conflict-free when
+// their blocks differ mod 32; 8-byte reads when their 8-byte slots differ mod 32):
+// Q/K rows serve 16-byte operand reads conflict-free and the transposing K^T reads
+// at the two-way floor; V rows serve both transposing read patterns conflict-free.
+template <int PP>
+__host__ __device__ constexpr int qk_swz(int r) {
+    if constexpr (PP == 4) return ((r >> 3) & 1) << 1;
+    else if constexpr (PP == 8) return (r & 1) ^ ((r >> 1) & 7);
+    else if constexpr (PP == 16) return ((r & 1) << 2) ^ (r & 15);
+    else if constexpr (PP == 24) return (r >> 1) & 7;
+    else return ((r & 1) << 3) ^ ((r & 15) << 1);
+}
+template <int PVB>
+__host__ __device__ constexpr int v_swz(int r) {
+    if constexpr (PVB == 8) return (r & 7) ^ ((r >> 1) & 7);
+    else if constexpr (PVB == 4) return ((r >> 1) & 3) ^ ((r >> 2) & 3);
+    else return 0;
+}
+
 template <int DK, int NW>
 struct Bf16Cfg {
     static constexpr int BV = 16 * NW;
-    static constexpr int NT = 64 * NW;
-    // Q and K row stride in LDS (elements).  The 16-byte operand reads of a
-    // half-wave touch 16 rows x 2 pieces; a stride of 8 * (odd * 2) elements puts
-    // those 32 pieces in distinct banks.
-    static constexpr int QLD = DK + 16;
-    // Decayed-K row stride: the transposing reads touch 4 rows x 4 pieces 16 B apart;
-    // a stride of 16 or 48 dwords (mod 64) keeps those 16 pieces in distinct banks.
-    static constexpr int KDLD = DK + (DK == 32 ? 64 : 32);
-    static constexpr int VLD = BV + 16;  // V row stride in LDS (elements)
-    static constexpr int Q_ELEMS = kChunk * QLD;
-    static constexpr int KD_ELEMS = kChunk * KDLD;
-    static constexpr int V_ELEMS = kChunk * VLD;
-    static constexpr int STAGE_ELEMS = 2 * Q_ELEMS + KD_ELEMS + V_ELEMS;
+    static constexpr int PP = DK / 8;    // 16-byte blocks per Q / K row
+    static constexpr int PVB = BV / 8;   // 16-byte blocks per V row (this value block)
+    static constexpr int Q_BYTES = kChunk * DK * 2;
+    static constexpr int V_BYTES = kChunk * BV * 2;
+    static constexpr int STAGE_BYTES = 2 * Q_BYTES + V_BYTES;
     // Masked intra-chunk matrix P, exchanged between waves in MFMA A-operand layout:
-    // 6 operand blocks (row tile b, token block kb) x {hi, lo} x 64 lanes x 8 values.
-    static constexpr int P_ELEMS = 6 * 2 * 64 * 8;
-    static constexpr int STAGES = (2 * (2 * STAGE_ELEMS + P_ELEMS) <= kLdsBudget) ? 2 : 1;
-    static constexpr int KB = DK / 32;  // dk blocks of one MFMA
-    static constexpr int MT = DK / 16;  // state row tiles
-    static constexpr int QITEMS = kChunk * DK / 8;  // 16-byte pieces of a Q (or K) chunk
-    static constexpr int VITEMS = kChunk * BV / 8;  // 16-byte pieces of a V chunk block
-    static constexpr int QPER = QITEMS / NT;
-    static constexpr int VPER = VITEMS / NT;
+    // 6 operand blocks (row tile b, token block kb) x {hi, lo} x 64 lanes x 16 bytes.
+    static constexpr int P_BYTES = 6 * 2 * 64 * 16;
+    static constexpr int FIT = (kLdsBudget - P_BYTES) / STAGE_BYTES;
+    static constexpr int STAGES = FIT >= 3 ? 3 : FIT;  // ring of chunk stages
+    static constexpr int DEPTH = STAGES - 1;           // chunks copied ahead of the one computed
+    static constexpr int QCOPIES = PP / NW;            // copy instructions per wave per Q (or K) tile
+    static constexpr int VCOPIES = PVB / NW;           // ... per V tile
+    static constexpr int NCOPY = 2 * QCOPIES + VCOPIES;
+    static constexpr int NSTORE = 16;                  // output stores per wave per chunk
+    static constexpr int KB = DK / 32;                 // dk blocks of one MFMA
+    static constexpr int MT = DK / 16;                 // state row tiles
     static_assert(DK % 32 == 0 && DK <= 256, "dk must be a multiple of 32 up to 256");
-    static_assert(QITEMS % NT == 0 && VITEMS % NT == 0, "staging pieces must divide evenly");
-    static_assert((STAGES * STAGE_ELEMS + P_ELEMS) * 2 <= kLdsBudget, "LDS budget");
+    static_assert(STAGES >= 2, "need at least two stages");
+    static_assert(PP % NW == 0 && PVB % NW == 0, "copies divide evenly between waves");
+    static_assert(STAGES * STAGE_BYTES + P_BYTES <= kLdsBudget, "LDS budget");
 };
 
 // Operand block of P for row tile b and token block kb (2kb <= b): 0..5.
 __host__ __device__ constexpr int pidx(int b, int kb) { return b < 2 ? b : 2 + 2 * (b - 2) + kb; }
-// Tile coordinates of lower-triangle (K Q^T) tile t = tidx(a, b).
+// Column tile a of lower-triangle (K Q^T) tile t = tidx(a, b).
 __host__ __device__ constexpr int tile_a(int t) { return t - tile_b(t) * (tile_b(t) + 1) / 2; }
 
 template <int V>
@@ -250,10 +304,11 @@ __device__ inline void split_state(const f32x4* S, bf16x8* hi, bf16x8* lo) {
 template <int DK, int NW, bool REV>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p) {
     using Cfg = Bf16Cfg<DK, NW>;
-    constexpr int BV = Cfg::BV, NT = Cfg::NT, QLD = Cfg::QLD, VLD = Cfg::VLD;
-    constexpr int KB = Cfg::KB, MT = Cfg::MT;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[Cfg::STAGES * Cfg::STAGE_ELEMS + Cfg::P_ELEMS];
-    uint16_t* Pbuf = smem + Cfg::STAGES * Cfg::STAGE_ELEMS;
+    constexpr int BV = Cfg::BV, PP = Cfg::PP, PVB = Cfg::PVB, KB = Cfg::KB, MT = Cfg::MT;
+    constexpr int NST = Cfg::STAGES, DEPTH = Cfg::DEPTH;
+    constexpr int QROW = DK * 2, VROW = BV * 2;  // LDS row bytes
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * Cfg::STAGE_BYTES + Cfg::P_BYTES];
+    uint8_t* Pbuf = smem + NST * Cfg::STAGE_BYTES;
 
     Work wk;
     if (!decode_work(p, wk)) return;
@@ -261,30 +316,32 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
     const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     const float g2 = p.g_gamma[wk.h] * kLog2e;  // log2 of the per-step decay
-    // Tiles (1, 0) and (3, 2) lie above the diagonal: their halves of P stay zero.
-    if (tid < 64) {
-        const u32x2 z2 = {0u, 0u};
-#pragma unroll
-        for (int hl = 0; hl < 2; ++hl) {
-            lds_store<u32x2>(Pbuf + ((pidx(0, 0) * 2 + hl) * 64 + tid) * 8 + 4, z2);
-            lds_store<u32x2>(Pbuf + ((pidx(2, 1) * 2 + hl) * 64 + tid) * 8 + 4, z2);
-        }
-    }
     const int L = (int)wk.len;
     const int nch = (L + kChunk - 1) / kChunk;
     const int H = p.num_heads, Hkv = p.num_kv_heads, dv = p.dv;
     const int col = 16 * wv + lr;  // this lane's value column inside the block
     const uint32_t qrow_b = (uint32_t)H * DK * 2, krow_b = (uint32_t)Hkv * DK * 2;
     const uint32_t vrow_b = (uint32_t)Hkv * dv * 2, orow_b = (uint32_t)H * dv * 4;
-    const uint16_t* qg = static_cast<const uint16_t*>(p.q);
-    const uint16_t* kg = static_cast<const uint16_t*>(p.k);
-    const uint16_t* vg = static_cast<const uint16_t*>(p.v);
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)wk.h * DK;
+    const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)wk.kvh * DK;
+    const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)wk.kvh * dv + wk.vb * BV;
+    const uint32_t smem_base = lds_addr(smem);
+
+    // Tiles (1, 0) and (3, 2) lie above the diagonal: their halves of P stay zero.
+    if (tid < 64) {
+        const u32x2 z2 = {0u, 0u};
+#pragma unroll
+        for (int hl = 0; hl < 2; ++hl) {
+            lds_store<u32x2>(Pbuf + ((pidx(0, 0) * 2 + hl) * 64 + tid) * 16 + 8, z2);
+            lds_store<u32x2>(Pbuf + ((pidx(2, 1) * 2 + hl) * 64 + tid) * 16 + 8, z2);
+        }
+    }
 
     // Decay factors, all with non-negative exponents and with `scale` folded in.
     // Mask of (K Q^T) tile (a, b): diagonal tiles use dg[ii] = lam^(lr - 4lg - ii)
     // (0 above the diagonal); tile b - a = d > 0 uses od[d-1][ii] = lam^(16d + lr - 4lg - ii).
     const float sc = p.scale;
-    float dg[4], od[3][4], lamq[4][4];
+    float dg[4], od[3][4], lamq[4][4], vw[2][8];
 #pragma unroll
     for (int ii = 0; ii < 4; ++ii) {
         const int e = lr - 4 * lg - ii;
@@ -294,6 +351,11 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
         for (int b = 0; b < 4; ++b) lamq[b][ii] = sc * exp2f(g2 * (float)(16 * b + 4 * lg + ii + 1));
     }
+    // Decay of value token j = 32kb + 8lg + e to the end of a full chunk: lam^(C-1-j).
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vw[kb][e] = exp2f(g2 * (float)(kChunk - 1 - (32 * kb + 8 * lg + e)));
     const float lamC = exp2f(g2 * (float)kChunk);
 
     // State block: tile mt holds rows dmap(mt, 4*lg + ii) at column `col`.
@@ -309,83 +371,94 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
     bf16x8 Shi[KB], Slo[KB];
     split_state<KB>(S, Shi, Slo);
 
-    // Staging: thread piece s covers row r = item / (pieces per row) of the chunk.
-    u32x4 pq[Cfg::QPER], pk[Cfg::QPER], pv[Cfg::VPER];
-    float wfull[Cfg::QPER];  // lam^(C-1-r): decay of key row r to the end of a full chunk
-#pragma unroll
-    for (int s = 0; s < Cfg::QPER; ++s) wfull[s] = exp2f(g2 * (float)(kChunk - 1 - (tid + s * NT) / (DK / 8)));
-
     auto first_row = [&](int p0, int Lc) -> int64_t { return REV ? wk.start + L - p0 - Lc : wk.start + p0; };
+    auto qk_off = [](int row, int blk) { return row * QROW + 16 * (blk ^ qk_swz<PP>(row)); };
+    auto v_off = [](int row, int blk) { return row * VROW + 16 * (blk ^ v_swz<PVB>(row)); };
 
-    auto load_chunk = [&](int c) {
-        const int p0 = c * kChunk, Lc = min(kChunk, L - p0);
-        const int64_t r0 = first_row(p0, Lc);
-        const auto rq = make_rsrc(qg + (r0 * H + wk.h) * DK, (uint32_t)(Lc - 1) * qrow_b + DK * 2);
-        const auto rk = make_rsrc(kg + (r0 * Hkv + wk.kvh) * DK, (uint32_t)(Lc - 1) * krow_b + DK * 2);
-        const auto rv = make_rsrc(vg + (r0 * Hkv + wk.kvh) * dv + wk.vb * BV, (uint32_t)(Lc - 1) * vrow_b + BV * 2);
+    // Copy chunk c into stage c % NST.  Past the last chunk the descriptors are
+    // empty, so the copies only write zeros (keeping the per-chunk operation count
+    // fixed for the waits below) into the stage the previous chunk used.
+    auto issue_chunk = [&](int c) {
+        const uint32_t stage = smem_base + (uint32_t)((c % NST) * Cfg::STAGE_BYTES);
+        const int p0 = c * kChunk;
+        const bool real = c < nch;
+        const int Lc = real ? min(kChunk, L - p0) : 1;
+        const int64_t r0 = real ? first_row(p0, Lc) : 0;
+        const RawBuf rq = raw_buf(qg + r0 * H * DK, real ? (uint32_t)(Lc - 1) * qrow_b + DK * 2 : 0u);
+        const RawBuf rk = raw_buf(kg + r0 * Hkv * DK, real ? (uint32_t)(Lc - 1) * krow_b + DK * 2 : 0u);
+        const RawBuf rv = raw_buf(vg + r0 * Hkv * dv, real ? (uint32_t)(Lc - 1) * vrow_b + BV * 2 : 0u);
 #pragma unroll
-        for (int s = 0; s < Cfg::QPER; ++s) {
-            const int item = tid + s * NT, r = item / (DK / 8), c8 = item % (DK / 8);
-            const int rs = REV ? Lc - 1 - r : r;  // row relative to r0; out of range past the end
-            pq[s] = buf_load_b128(rq, rs * (int)qrow_b + c8 * 16);
-            pk[s] = buf_load_b128(rk, rs * (int)krow_b + c8 * 16);
+        for (int j = 0; j < Cfg::QCOPIES; ++j) {
+            const int kbyte = j * NW + wv;  // this wave's kilobyte of the tile
+            const int B = kbyte * 64 + lane, row = B / PP;
+            const int blk = (B % PP) ^ qk_swz<PP>(row);
+            const int rs = REV ? Lc - 1 - row : row;  // out of range past the end
+            copy16_to_lds(stage + kbyte * 1024, rq, rs * (int)qrow_b + blk * 16);
+            copy16_to_lds(stage + Cfg::Q_BYTES + kbyte * 1024, rk, rs * (int)krow_b + blk * 16);
         }
 #pragma unroll
-        for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = tid + s * NT, r = item / (BV / 8), c8 = item % (BV / 8);
-            const int rs = REV ? Lc - 1 - r : r;
-            pv[s] = buf_load_b128(rv, rs * (int)vrow_b + c8 * 16);
+        for (int j = 0; j < Cfg::VCOPIES; ++j) {
+            const int kbyte = j * NW + wv;
+            const int B = kbyte * 64 + lane, row = B / PVB;
+            const int blk = (B % PVB) ^ v_swz<PVB>(row);
+            const int rs = REV ? Lc - 1 - row : row;
+            copy16_to_lds(stage + 2 * Cfg::Q_BYTES + kbyte * 1024, rv, rs * (int)vrow_b + blk * 16);
+        }
+    };
+    // Wait until this wave's copies of chunk c are in LDS.  Issued after them, in
+    // order: the copies of DEPTH-1 later chunks and the output stores of the
+    // min(c, DEPTH) chunks computed since.
+    constexpr int W0 = (DEPTH - 1) * Cfg::NCOPY;
+    constexpr int WC = W0 + DEPTH * Cfg::NSTORE;
+    auto wait_chunk = [&](int c) {
+        if (c >= DEPTH) {
+            wait_vmem<(WC < 63 ? WC : 63)>();
+        } else if (c == 0) {
+            wait_vmem<(W0 < 63 ? W0 : 63)>();
+        } else {
+            constexpr int W1 = W0 + Cfg::NSTORE;
+            wait_vmem<(W1 < 63 ? W1 : 63)>();
         }
     };
 
-    auto store_chunk = [&](int c, uint16_t* st) {
-        uint16_t* Qs = st;
-        uint16_t* Ks = st + Cfg::Q_ELEMS;
-        uint16_t* Kd = Ks + Cfg::Q_ELEMS;  // keys decayed to the chunk end
-        uint16_t* Vs = Kd + Cfg::KD_ELEMS;
-        const int Lc = min(kChunk, L - c * kChunk);
-#pragma unroll
-        for (int s = 0; s < Cfg::QPER; ++s) {
-            const int item = tid + s * NT, r = item / (DK / 8), c8 = item % (DK / 8);
-            lds_store<u32x4>(Qs + r * QLD + c8 * 8, pq[s]);
-            lds_store<u32x4>(Ks + r * QLD + c8 * 8, pk[s]);
-            const float w = Lc == kChunk ? wfull[s] : (r < Lc ? exp2f(g2 * (float)(Lc - 1 - r)) : 0.f);
-            u32x4 d;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) d[e] = pack_bf16x2(bf16_lo(pk[s][e]) * w, bf16_hi(pk[s][e]) * w);
-            lds_store<u32x4>(Kd + r * Cfg::KDLD + c8 * 8, d);
-        }
-#pragma unroll
-        for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = tid + s * NT, r = item / (BV / 8), c8 = item % (BV / 8);
-            lds_store<u32x4>(Vs + r * VLD + c8 * 8, pv[s]);
-        }
-    };
-
-    auto compute_chunk = [&](int c, const uint16_t* st) {
-        const uint16_t* Qs = st;
-        const uint16_t* Ks = st + Cfg::Q_ELEMS;
-        const uint16_t* Kd = Ks + Cfg::Q_ELEMS;
-        const uint16_t* Vs = Kd + Cfg::KD_ELEMS;
+    auto compute_chunk = [&](int c, const uint8_t* st) {
+        const uint8_t* Qs = st;
+        const uint8_t* Ks = st + Cfg::Q_BYTES;
+        const uint8_t* Vs = st + 2 * Cfg::Q_BYTES;
         const int p0 = c * kChunk, Lc = min(kChunk, L - p0);
-        constexpr int KDLD = Cfg::KDLD;
+        const int vblk = 2 * wv + ((lr & 3) >> 1), vhalf = 8 * (lr & 1);  // this lane's V piece
 
-        // S <- lam^Lc S + Kd^T V.  Operands by transposing reads of the row-major
-        // tiles: lane group lg takes tokens 32kb + 8lg + 0..7; the A operand row of
-        // lane lr is dk dmap(mt, lr), the B operand column is `col`.
-        const float lamL = (Lc == kChunk) ? lamC : exp2f(g2 * (float)Lc);
+        // S <- lam^Lc S + K^T (decayed V).  Operands by transposing reads: lane group
+        // lg takes tokens 32kb + 8lg + 0..7; the A operand row of lane lr is dk
+        // dmap(mt, lr); the B operand (column `col`) is decayed in registers.
+        float lamL = lamC;
+        if (Lc != kChunk) {  // the last chunk of a sequence: decays to its own end
+            lamL = exp2f(g2 * (float)Lc);
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int j = 32 * kb + 8 * lg + e;
+                    vw[kb][e] = j < Lc ? exp2f(g2 * (float)(Lc - 1 - j)) : 0.f;
+                }
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) S[mt] *= lamL;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int jr = 32 * kb + 8 * lg + (lr >> 2);  // token row this lane addresses
-            const uint16_t* vp = Vs + jr * VLD + 16 * wv + 4 * (lr & 3);
-            const bf16x8 vop = cat_bf16(lds_tr16(vp), lds_tr16(vp + 4 * VLD));
+            u32x4 vw4 = __builtin_bit_cast(u32x4, cat_bf16(lds_tr16((const uint16_t*)(Vs + v_off(jr, vblk) + vhalf)),
+                                                         lds_tr16((const uint16_t*)(Vs + v_off(jr + 4, vblk) + vhalf))));
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                vw4[e] = pack_bf16x2(bf16_lo(vw4[e]) * vw[kb][2 * e], bf16_hi(vw4[e]) * vw[kb][2 * e + 1]);
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, vw4);
             bf16x8 kop[MT];
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
-                const uint16_t* kp = Kd + jr * KDLD + 32 * (mt >> 1) + 8 * (lr & 3) + 4 * (mt & 1);
-                kop[mt] = cat_bf16(lds_tr16(kp), lds_tr16(kp + 4 * KDLD));
+                const int kblk = 4 * (mt >> 1) + (lr & 3), khalf = 8 * (mt & 1);
+                kop[mt] = cat_bf16(lds_tr16((const uint16_t*)(Ks + qk_off(jr, kblk) + khalf)),
+                                   lds_tr16((const uint16_t*)(Ks + qk_off(jr + 4, kblk) + khalf)));
             }
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_bf16(kop[mt], vop, S[mt]);
@@ -409,7 +482,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
             for (int kb = 0; kb < KB; ++kb) {
                 bf16x8 qa[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) qa[r] = lds_load<bf16x8>(Qs + (16 * r + lr) * QLD + 32 * kb + 8 * lg);
+                for (int r = 0; r < 4; ++r) qa[r] = lds_load<bf16x8>(Qs + qk_off(16 * r + lr, 4 * kb + lg));
 #pragma unroll
                 for (int b = 0; b < 4; ++b) {
                     O[b] = mfma_bf16(qa[b], Shi[kb], O[b]);
@@ -417,10 +490,9 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
                 }
 #pragma unroll
                 for (int s = 0; s < NTILE; ++s) {
-                    constexpr int T0 = W;  // first tile of this wave
-                    const int t = T0 + s * NW;
+                    const int t = W + s * NW;
                     const int a = tile_a(t), b = tile_b(t);
-                    const bf16x8 ka = lds_load<bf16x8>(Ks + (16 * a + lr) * QLD + 32 * kb + 8 * lg);
+                    const bf16x8 ka = lds_load<bf16x8>(Ks + qk_off(16 * a + lr, 4 * kb + lg));
                     At[s] = mfma_bf16(ka, qa[b], At[s]);
                 }
             }
@@ -434,10 +506,10 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
                 const uint32_t h0 = pack_bf16x2(pv4[0], pv4[1]), h1 = pack_bf16x2(pv4[2], pv4[3]);
                 const uint32_t l0 = pack_bf16x2(pv4[0] - bf16_lo(h0), pv4[1] - bf16_hi(h0));
                 const uint32_t l1 = pack_bf16x2(pv4[2] - bf16_lo(h1), pv4[3] - bf16_hi(h1));
-                uint16_t* dst = Pbuf + (pidx(b, a >> 1) * 2 * 64 + lane) * 8 + 4 * (a & 1);
+                uint8_t* dst = Pbuf + (pidx(b, a >> 1) * 2 * 64 + lane) * 16 + 8 * (a & 1);
                 const u32x2 hv = {h0, h1}, lv = {l0, l1};
                 lds_store<u32x2>(dst, hv);
-                lds_store<u32x2>(dst + 64 * 8, lv);
+                lds_store<u32x2>(dst + 64 * 16, lv);
             }
         };
         if constexpr (NW == 1) {
@@ -458,20 +530,21 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
         for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) O[b][ii] *= lamq[b][ii];
-        __syncthreads();  // P complete
+        lds_barrier();  // P complete
 
         // O += P V.  For row tile b and token block kb, P elements 0..3 are tokens
         // 32kb + 4lg + 0..3 and 4..7 are 32kb + 16 + 4lg + 0..3; V is read in the
         // same token order.
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const uint16_t* vp = Vs + (32 * kb + 4 * lg + (lr >> 2)) * VLD + 16 * wv + 4 * (lr & 3);
-            const bf16x8 vop = cat_bf16(lds_tr16(vp), lds_tr16(vp + 16 * VLD));
+            const int jr = 32 * kb + 4 * lg + (lr >> 2);
+            const bf16x8 vop = cat_bf16(lds_tr16((const uint16_t*)(Vs + v_off(jr, vblk) + vhalf)),
+                                        lds_tr16((const uint16_t*)(Vs + v_off(jr + 16, vblk) + vhalf)));
 #pragma unroll
             for (int b = 2 * kb; b < 4; ++b) {
-                const uint16_t* pp = Pbuf + (pidx(b, kb) * 2 * 64 + lane) * 8;
+                const uint8_t* pp = Pbuf + (pidx(b, kb) * 2 * 64 + lane) * 16;
                 O[b] = mfma_bf16(lds_load<bf16x8>(pp), vop, O[b]);
-                O[b] = mfma_bf16(lds_load<bf16x8>(pp + 64 * 8), vop, O[b]);
+                O[b] = mfma_bf16(lds_load<bf16x8>(pp + 64 * 16), vop, O[b]);
             }
         }
 
@@ -490,21 +563,17 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
         split_state<KB>(S, Shi, Slo);
     };
 
-    auto iteration = [&](int c) {
-        uint16_t* st = smem + (Cfg::STAGES == 2 ? (c & 1) * Cfg::STAGE_ELEMS : 0);
-        if (Cfg::STAGES == 1) __syncthreads();
-        store_chunk(c, st);
-        if (c + 1 < nch) load_chunk(c + 1);
-        __syncthreads();
-        compute_chunk(c, st);
-    };
-    // The first chunk is peeled so that, inside the loop, the wait for the
-    // prefetched loads never has to include the previous chunk's output stores.
     if (nch > 0) {
-        load_chunk(0);
-        iteration(0);
+#pragma unroll
+        for (int c = 0; c < DEPTH; ++c) issue_chunk(c);
+        for (int c = 0; c < nch; ++c) {
+            wait_chunk(c);
+            lds_barrier();  // chunk c is in LDS; every wave is done with chunk c - 1
+            issue_chunk(c + DEPTH);
+            compute_chunk(c, smem + (c % NST) * Cfg::STAGE_BYTES);
+        }
+        wait_vmem<0>();  // no copy may still be writing LDS when the workgroup ends
     }
-    for (int c = 1; c < nch; ++c) iteration(c);
 
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
