@@ -130,3 +130,18 @@ def test_wrapper_value_errors():
         lattn.lightning_attn(q1, q1, q1, 5, 4)
     with pytest.raises(ValueError, match="GPU"):
         lattn.recurrent(q1, q1, q1)
+
+
+def test_graft_entry_build_calls_both_builds(monkeypatch):
+    """build() compiles the HIP library and the oracle (compilers stubbed out here)."""
+    import importlib
+
+    import __graft_entry__ as entry
+
+    calls = []
+    hip_build = importlib.import_module("decayed_recurrent_attention_amd.build")
+    oracle_build = importlib.import_module("oracle.build")
+    monkeypatch.setattr(hip_build, "build", lambda *a, **k: calls.append("hip"))
+    monkeypatch.setattr(oracle_build, "build", lambda *a, **k: calls.append("oracle"))
+    entry.build()
+    assert calls == ["hip", "oracle"]
