@@ -56,27 +56,70 @@ def measured_traffic():
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline(w, data):
-    """Time the oracle on a bounded set of (batch row, head) pairs of the workload."""
+def cpu_baseline(w, data, target_s=15.0):
+    """Time the oracle on the workload's (batch row, head) pairs, about target_s of CPU work.
+
+    The sample grows until it takes about target_s: more (batch row, head) pairs, or the
+    whole workload repeated once every pair is in.  Only the last pass is reported.
+    """
     import oracle
 
     orc = oracle.load()
     threads = orc.set_threads(0)
-    n_pairs = max(1, min(w.batch * w.num_heads, 4 * threads))
-    pairs = [(b, h) for h in range(w.num_heads) for b in range(w.batch)][:n_pairs]
+    all_pairs = [(b, h) for h in range(w.num_heads) for b in range(w.batch)]
     g = orc.lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers)
-    t0 = time.perf_counter()
-    orc.recurrent_fwd(data["q"], data["k"], data["v"], g, w.scale, pairs=pairs)
-    dt = time.perf_counter() - t0
-    frac = len(pairs) / (w.batch * w.num_heads)
+
+    def timed(pairs, reps=1):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            orc.recurrent_fwd(data["q"], data["k"], data["v"], g, w.scale, pairs=pairs)
+        return time.perf_counter() - t0
+
+    # Grow the sample fourfold until it takes a quarter of target_s, then size it to
+    # about target_s: more pairs, or whole-workload repeats once every pair is in.
+    n, reps = min(len(all_pairs), threads), 1
+    timed(all_pairs[:1])  # untimed: first-touch of the output buffers, thread start-up
+    dt = timed(all_pairs[:n])
+    while dt < target_s / 4 and n < len(all_pairs):
+        n = min(len(all_pairs), 4 * n)
+        dt = timed(all_pairs[:n])
+    if dt < target_s:
+        if n < len(all_pairs):
+            n = min(len(all_pairs), int(n * target_s / dt))
+        else:
+            reps = max(1, min(20, round(target_s / dt)))
+        dt = timed(all_pairs[:n], reps)
+    frac = n * reps / len(all_pairs)
+    what = (f"all {len(all_pairs)} (batch row, head) pairs x {reps}" if n == len(all_pairs)
+            else f"{n} of {len(all_pairs)} (batch row, head) pairs")
     return {
         "value": w.batch * w.seqlen * frac / dt,
         "unit": "tokens/s",
-        "cores": min(threads, len(pairs)),
+        "cores": min(threads, n),
         "kind": "oracle",
-        "sample": f"{len(pairs)} of {w.batch * w.num_heads} (batch row, head) pairs over all "
-                  f"{w.seqlen} tokens, fp64, {dt:.1f} s wall; tokens/s scaled by the pair fraction",
+        "sample": f"{what} over all {w.seqlen} tokens, fp64, {dt:.1f} s wall; "
+                  f"tokens/s = whole-workload tokens x {frac:.3g} / wall",
     }
+
+
+def device_bandwidth(torch, dev, gib=2, reps=5):
+    """Best-of-reps GB/s of a device copy (read + write bytes) and a fill (write bytes)."""
+    n = gib * (1 << 30) // 4
+    src = torch.ones(n, device=dev, dtype=torch.float32)
+    dst = torch.empty_like(src)
+    res = {}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * 4 * n), ("fill", lambda: dst.fill_(2.0), 4 * n)):
+        best = float("inf")
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        res[name] = moved / (best * 1e-3) / 1e9
+    del src, dst
+    return f"device copy {gib} GiB: {res['copy']:.0f} GB/s (read + write), fill: {res['fill']:.0f} GB/s"
 
 
 def main():
@@ -88,6 +131,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for traffic)")
+    ap.add_argument("--bandwidth", action="store_true",
+                    help="also time a 2 GiB device copy (read + write) and fill (write) for reference")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the forward pass has no multi-GPU path "
@@ -149,6 +194,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.bandwidth:
+        print("[bench] " + device_bandwidth(torch, dev), file=sys.stderr, flush=True)
 
     alg = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2)
     achieved = alg / (mean_kernel_ms * 1e-3) / 1e9
