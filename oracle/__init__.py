@@ -53,6 +53,13 @@ class Oracle:
             + [ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         )
+        lib.oracle_recurrent_bwd.restype = ctypes.c_int
+        lib.oracle_recurrent_bwd.argtypes = (
+            [ctypes.c_int] * 7
+            + [ctypes.c_void_p] * 4
+            + [ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int]
+            + [ctypes.c_void_p] * 6
+        )
         self._lib = lib
 
     # -- decay schedule ---------------------------------------------------------
@@ -126,6 +133,68 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return (o[0] if squeeze else o), fs
+
+    # -- backward ----------------------------------------------------------------
+    def recurrent_bwd(self, q, k, v, g_gamma, scale, d_o, d_final=None, initial_state=None,
+                      reverse=False, cu_seqlens=None, want_d_init=True):
+        """fp64 gradients of the forward recurrence.
+
+        Returns (dq [.., T, H, dk], dk [.., T, Hkv, dk], dv [.., T, Hkv, dv],
+        d_initial_state [N_seq, H, dk, dv] or None).  ``d_o`` and ``d_final`` are
+        taken as float32 values.  Rows outside every packed sequence are zero.
+        """
+        q = np.ascontiguousarray(q)
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        squeeze = q.ndim == 3
+        if squeeze:
+            q, k, v = q[None], k[None], v[None]
+            d_o = np.asarray(d_o)[None]
+        if not (q.dtype == k.dtype == v.dtype):
+            raise TypeError("q, k, v must share one dtype")
+        dt = _in_dtype(q)
+        B, T, H, dk = q.shape
+        Hkv = k.shape[2]
+        dv = v.shape[3]
+        if k.shape != (B, T, Hkv, dk) or v.shape != (B, T, Hkv, dv):
+            raise ValueError("inconsistent q/k/v shapes")
+        do32 = np.ascontiguousarray(d_o, dtype=np.float32)
+        if do32.shape != (B, T, H, dv):
+            raise ValueError("d_o must have the shape of o")
+        g = np.ascontiguousarray(g_gamma, dtype=np.float32)
+        if cu_seqlens is not None:
+            cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+            n_seq = cu.shape[0] - 1
+            cu_ptr = cu.ctypes.data
+        else:
+            n_seq = B
+            cu_ptr = None
+        st_shape = (n_seq, H, dk, dv)
+        init_ptr = fin_ptr = None
+        if initial_state is not None:
+            init = np.ascontiguousarray(initial_state, dtype=np.float32)
+            if init.shape != st_shape:
+                raise ValueError(f"initial_state must be {st_shape}")
+            init_ptr = init.ctypes.data
+        if d_final is not None:
+            fin = np.ascontiguousarray(d_final, dtype=np.float32)
+            if fin.shape != st_shape:
+                raise ValueError(f"d_final must be {st_shape}")
+            fin_ptr = fin.ctypes.data
+        dq = np.zeros((B, T, H, dk))
+        dk_ = np.zeros((B, T, Hkv, dk))
+        dv_ = np.zeros((B, T, Hkv, dv))
+        d_init = np.zeros(st_shape) if want_d_init else None
+        rc = self._lib.oracle_recurrent_bwd(
+            B, T, H, Hkv, dk, dv, dt, q.ctypes.data, k.ctypes.data, v.ctypes.data,
+            g.ctypes.data, float(scale), init_ptr, int(bool(reverse)), cu_ptr, n_seq,
+            do32.ctypes.data, fin_ptr, dq.ctypes.data, dk_.ctypes.data, dv_.ctypes.data,
+            d_init.ctypes.data if want_d_init else None)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        if squeeze:
+            dq, dk_, dv_ = dq[0], dk_[0], dv_[0]
+        return dq, dk_, dv_, d_init
 
     def lightning_attn(self, q, k, v, layer_idx, num_layers, softmax_scale=None,
                        initial_state=None, reverse=False, cu_seqlens=None):

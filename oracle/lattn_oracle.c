@@ -1,5 +1,6 @@
 /*
- * CPU fp64 oracle for decayed recurrent (Lightning) attention, forward pass.
+ * CPU fp64 oracle for decayed recurrent (Lightning) attention: forward pass and
+ * its gradients (backward).
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * CPU-baseline leg of the benchmark may load this file's library.  It shares
@@ -163,6 +164,139 @@ int oracle_recurrent_fwd(int batch, int seqlen, int num_heads, int num_kv_heads,
         free(kt);
         free(vt);
         free(out_row);
+        free(S);
+    }
+    return 0;
+}
+
+/*
+ * Gradients of the forward recurrence above (the recurrent page's custom-VJP
+ * backward: given dO and d final_state it returns dq, dk, dv and d
+ * initial_state; g_gamma is not differentiated, as in the lightning wrapper).
+ *
+ * Derivation by the chain rule through S_t = lam S_{t-1} + k_t^T v_t and
+ * o_t = scale q_t S_t.  Write D_t for the total gradient that reaches S_t:
+ *
+ *     D_t  = scale q_t^T dO_t + lam D_{t+1}     (D after the last token = d_final / lam,
+ *                                                i.e. the last step adds d_final undecayed)
+ *     dq_t = scale dO_t S_t^T                   (dk-vector)
+ *     dk_t = D_t v_t                            (contract over dv)
+ *     dv_t = k_t D_t                            (contract over dk)
+ *     d_initial_state = lam D_first
+ *
+ * "first" and "last" follow the direction of the forward pass (reverse runs
+ * from the last position to the first).  Under GQA, dk and dv of kv head j
+ * sum the contributions of every query head that reads j.
+ *
+ *   d_o [B, T, H, dv] float32;  d_final [N_seq, H, dk, dv] float32 or NULL (zeros)
+ *   dq [B, T, H, dk], dk_out [B, T, Hkv, dk], dv_out [B, T, Hkv, dv] fp64 (outputs;
+ *     rows outside every sequence are left untouched)
+ *   d_init [N_seq, H, dk, dv] fp64 or NULL (then not computed)
+ * Two sweeps per (sequence, query head): forward for S_t and dq_t, then backward
+ * for D_t, dk_t and dv_t.  Returns 0, or -1 on inconsistent arguments.
+ */
+int oracle_recurrent_bwd(int batch, int seqlen, int num_heads, int num_kv_heads,
+                         int dk, int dv, int in_dtype,
+                         const void* q, const void* k, const void* v,
+                         const float* g_gamma, double scale,
+                         const float* initial_state, int reverse,
+                         const int64_t* cu_seqlens, int num_seqs,
+                         const float* d_o, const float* d_final,
+                         double* dq, double* dk_out, double* dv_out, double* d_init) {
+    if (batch <= 0 || seqlen < 0 || num_heads <= 0 || num_kv_heads <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (num_heads % num_kv_heads != 0) return -1;
+    if (cu_seqlens != NULL && batch != 1) return -1;
+    const int n_seq = cu_seqlens ? num_seqs : batch;
+    const int group = num_heads / num_kv_heads;
+    const int64_t n_groups = (int64_t)n_seq * num_kv_heads;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t gi = 0; gi < n_groups; ++gi) {
+        const int n = (int)(gi / num_kv_heads);
+        const int kvh = (int)(gi % num_kv_heads);
+        int64_t row0, len;
+        if (cu_seqlens) {
+            row0 = cu_seqlens[n];
+            len = cu_seqlens[n + 1] - cu_seqlens[n];
+        } else {
+            row0 = (int64_t)n * seqlen;
+            len = seqlen;
+        }
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+        double* D = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+        double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* kt = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* vt = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* dot = (double*)malloc(sizeof(double) * (size_t)dv);
+
+        /* the group's rows of dk and dv start from zero and collect every head */
+        for (int64_t step = 0; step < len; ++step) {
+            const int64_t row = row0 + step;
+            for (int a = 0; a < dk; ++a) dk_out[(row * num_kv_heads + kvh) * dk + a] = 0.0;
+            for (int c = 0; c < dv; ++c) dv_out[(row * num_kv_heads + kvh) * dv + c] = 0.0;
+        }
+        for (int h = kvh * group; h < (kvh + 1) * group; ++h) {
+            const double lam = exp((double)g_gamma[h]);
+            const int64_t st_base = ((int64_t)n * num_heads + h) * dk * dv;
+
+            /* sweep 1, in the forward direction: S_t, then dq_t = scale dO_t S_t^T */
+            for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
+                S[i] = initial_state ? (double)initial_state[st_base + i] : 0.0;
+            for (int64_t step = 0; step < len; ++step) {
+                const int64_t row = reverse ? row0 + len - 1 - step : row0 + step;
+                const int64_t ko = (row * num_kv_heads + kvh) * dk;
+                const int64_t vo = (row * num_kv_heads + kvh) * dv;
+                for (int a = 0; a < dk; ++a) kt[a] = in_value(k, in_dtype, ko + a);
+                for (int c = 0; c < dv; ++c) vt[c] = in_value(v, in_dtype, vo + c);
+                for (int c = 0; c < dv; ++c) dot[c] = (double)d_o[(row * num_heads + h) * dv + c];
+                for (int a = 0; a < dk; ++a)
+                    for (int c = 0; c < dv; ++c)
+                        S[(int64_t)a * dv + c] = lam * S[(int64_t)a * dv + c] + kt[a] * vt[c];
+                for (int a = 0; a < dk; ++a) {
+                    double acc = 0.0;
+                    for (int c = 0; c < dv; ++c) acc += dot[c] * S[(int64_t)a * dv + c];
+                    dq[(row * num_heads + h) * dk + a] = scale * acc;
+                }
+            }
+
+            /* sweep 2, against the forward direction: D_t, dk_t, dv_t */
+            for (int64_t i = 0; i < (int64_t)dk * dv; ++i) D[i] = d_final ? (double)d_final[st_base + i] : 0.0;
+            for (int64_t step = 0; step < len; ++step) {
+                const int64_t row = reverse ? row0 + step : row0 + len - 1 - step;
+                const int64_t qo = (row * num_heads + h) * dk;
+                const int64_t ko = (row * num_kv_heads + kvh) * dk;
+                const int64_t vo = (row * num_kv_heads + kvh) * dv;
+                for (int a = 0; a < dk; ++a) qt[a] = in_value(q, in_dtype, qo + a);
+                for (int a = 0; a < dk; ++a) kt[a] = in_value(k, in_dtype, ko + a);
+                for (int c = 0; c < dv; ++c) vt[c] = in_value(v, in_dtype, vo + c);
+                for (int c = 0; c < dv; ++c) dot[c] = (double)d_o[(row * num_heads + h) * dv + c];
+                const double carry = step == 0 ? 1.0 : lam; /* d_final enters undecayed */
+                for (int a = 0; a < dk; ++a)
+                    for (int c = 0; c < dv; ++c)
+                        D[(int64_t)a * dv + c] = carry * D[(int64_t)a * dv + c] + scale * qt[a] * dot[c];
+                for (int a = 0; a < dk; ++a) {
+                    double acc = 0.0;
+                    for (int c = 0; c < dv; ++c) acc += D[(int64_t)a * dv + c] * vt[c];
+                    dk_out[ko + a] += acc;
+                }
+                for (int c = 0; c < dv; ++c) {
+                    double acc = 0.0;
+                    for (int a = 0; a < dk; ++a) acc += kt[a] * D[(int64_t)a * dv + c];
+                    dv_out[vo + c] += acc;
+                }
+            }
+            if (d_init) {
+                /* S_first = lam S_init + ..., so the state handed in receives lam D_first */
+                for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
+                    d_init[st_base + i] = (len > 0 ? lam * D[i] : (d_final ? (double)d_final[st_base + i] : 0.0));
+            }
+        }
+        free(dot);
+        free(vt);
+        free(kt);
+        free(qt);
+        free(D);
         free(S);
     }
     return 0;

@@ -83,6 +83,8 @@ def _close(a, b, rtol, what):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    if b.size == 0:
+        return
     den = max(float(np.max(np.abs(b))), 1e-300)
     err = float(np.max(np.abs(a - b))) if a.size else 0.0
     assert err <= rtol * den, f"{what}: max err {err:.3e} > {rtol:.1e} * {den:.3e}"
@@ -286,5 +288,119 @@ def pin_pairs(orc):
     assert np.isnan(o_p[0, :, 0]).all()
 
 
+# ---------------------------------------------------------------------------
+# Backward pins.  The loss  L = <dO, o> + <dF, final_state>  is linear in each of q,
+# k, v and the initial state separately (o and the final state are multilinear in
+# them), so a central difference with any step is the exact partial derivative up
+# to fp64 rounding: the forward oracle (pinned above) then fixes every gradient.
+# ---------------------------------------------------------------------------
+def _bwd_case(seed, B, T, H, Hkv, dk, dv, n_seq=None):
+    q, k, v, g, _, scale = _rand_case(seed, B, T, H, Hkv, dk, dv, False)
+    rng = np.random.Generator(np.random.PCG64(seed + 1000))
+    n = B if n_seq is None else n_seq
+    S0 = rng.standard_normal((n, H, dk, dv)).astype(np.float32)
+    do = rng.standard_normal((B, T, H, dv)).astype(np.float32)
+    dF = rng.standard_normal((n, H, dk, dv)).astype(np.float32)
+    return q, k, v, g, S0, scale, do, dF
+
+
+BWD_FD_CASES = [
+    # seed, B, T, H, Hkv, dk, dv, reverse, cu_seqlens
+    (71, 1, 6, 2, 1, 3, 2, False, None),
+    (72, 2, 5, 2, 2, 2, 3, True, None),
+    (73, 1, 8, 4, 2, 3, 2, False, [0, 3, 3, 8]),
+    (74, 1, 7, 2, 1, 2, 2, True, [0, 5, 7]),
+]
+
+
+def pin_bwd_finite_difference(orc):
+    for seed, B, T, H, Hkv, dk, dv, rev, cu in BWD_FD_CASES:
+        n_seq = None if cu is None else len(cu) - 1
+        q, k, v, g, S0, scale, do, dF = _bwd_case(seed, B, T, H, Hkv, dk, dv, n_seq)
+        cu_a = None if cu is None else np.asarray(cu, dtype=np.int64)
+
+        def loss(x):
+            o, fs = orc.recurrent_fwd(x["q"], x["k"], x["v"], g, scale, initial_state=x["S0"],
+                                      reverse=rev, cu_seqlens=cu_a)
+            return float(np.sum(o * do) + np.sum(fs * dF))
+
+        grads = orc.recurrent_bwd(q, k, v, g, scale, do, dF, S0, reverse=rev, cu_seqlens=cu_a)
+        base = {"q": q, "k": k, "v": v, "S0": S0}
+        for name, grad in zip(("q", "k", "v", "S0"), grads):
+            fd = np.zeros(base[name].shape)
+            for idx in np.ndindex(base[name].shape):
+                up, dn = base[name].copy(), base[name].copy()
+                up[idx] += np.float32(1.0)
+                dn[idx] -= np.float32(1.0)
+                step = np.float64(up[idx]) - np.float64(dn[idx])
+                fd[idx] = (loss({**base, name: up}) - loss({**base, name: dn})) / step
+            _close(grad, fd, 1e-11, f"d{name} by central differences, case {seed}")
+
+
+def closed_form_bwd(q, k, v, g, scale, do, dF, S0, reverse=False):
+    """All-pairs gradients of closed_form's loss <do, o> + <dF, final> (fixed length)."""
+    if reverse:  # the reverse recurrence is the forward one on time-flipped sequences
+        dq, dk, dv, dS = closed_form_bwd(q[:, ::-1], k[:, ::-1], v[:, ::-1], g, scale,
+                                         do[:, ::-1], dF, S0, False)
+        return dq[:, ::-1], dk[:, ::-1], dv[:, ::-1], dS
+    q, k, v, do, dF, S0 = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do, dF, S0))
+    B, T, H, dkd = q.shape
+    Hkv, rep = k.shape[2], H // k.shape[2]
+    t = np.arange(T)
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    dS = np.zeros(S0.shape)
+    for h in range(H):
+        lam = np.exp(np.float64(g[h]))
+        j = h // rep
+        Dm = np.where(t[:, None] >= t[None, :], lam ** np.maximum(t[:, None] - t[None, :], 0), 0.0)
+        for b in range(B):
+            Q, K, V, dO = q[b, :, h], k[b, :, j], v[b, :, j], do[b, :, h]
+            F, S = dF[b, h], S0[b, h]
+            to_end = lam ** (T - 1 - t)
+            dq[b, :, h] = scale * (Dm * (dO @ V.T)) @ K + scale * (lam ** (t + 1))[:, None] * (dO @ S.T)
+            dk[b, :, j] += scale * (Dm * (dO @ V.T)).T @ Q + to_end[:, None] * (V @ F.T)
+            dv[b, :, j] += scale * (Dm * (Q @ K.T)).T @ dO + to_end[:, None] * (K @ F)
+            dS[b, h] = scale * ((lam ** (t + 1))[:, None] * Q).T @ dO + lam ** T * F
+    return dq, dk, dv, dS
+
+
+BWD_CLOSED_CASES = [
+    # seed, B, T, H, Hkv, dk, dv, reverse
+    (81, 1, 1, 1, 1, 3, 2, False),
+    (82, 2, 17, 4, 2, 5, 3, False),
+    (83, 1, 40, 4, 1, 4, 6, True),
+    (84, 2, 64, 2, 2, 8, 8, True),
+]
+
+
+def pin_bwd_closed_form(orc):
+    for seed, B, T, H, Hkv, dk, dv, rev in BWD_CLOSED_CASES:
+        q, k, v, g, S0, scale, do, dF = _bwd_case(seed, B, T, H, Hkv, dk, dv)
+        got = orc.recurrent_bwd(q, k, v, g, scale, do, dF, S0, reverse=rev)
+        ref = closed_form_bwd(q, k, v, g, scale, do, dF, S0, rev)
+        for name, a, b in zip(("dq", "dk", "dv", "d_initial_state"), got, ref):
+            _close(a, b, 1e-11, f"{name}, case {seed}")
+
+
+def pin_bwd_packed(orc):
+    """A packed batch gives each sequence the gradients of running it alone."""
+    lens = [4, 0, 9, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    q, k, v, g, S0, scale, do, dF = _bwd_case(91, 1, T, 4, 2, 3, 4, len(lens))
+    got = orc.recurrent_bwd(q, k, v, g, scale, do, dF, S0, cu_seqlens=cu, reverse=True)
+    for n in range(len(lens)):
+        a, e = cu[n], cu[n + 1]
+        one = orc.recurrent_bwd(q[:, a:e], k[:, a:e], v[:, a:e], g, scale, do[:, a:e], dF[n:n + 1],
+                                S0[n:n + 1], reverse=True)
+        for name, x, y in zip(("dq", "dk", "dv"), got[:3], one[:3]):
+            _close(x[:, a:e], y, 1e-12, f"packed {name}, sequence {n}")
+        _close(got[3][n:n + 1], one[3], 1e-12, f"packed d_initial_state, sequence {n}")
+
+
+BWD_PINS = [pin_bwd_finite_difference, pin_bwd_closed_form, pin_bwd_packed]
+
 ALL_PINS = [pin_brute_force, pin_bf16_words, pin_no_decay, pin_chaining, pin_reverse_flip,
-            pin_packed, pin_lightning_ones, pin_recurrent_examples, pin_g_gamma, pin_pairs]
+            pin_packed, pin_lightning_ones, pin_recurrent_examples, pin_g_gamma, pin_pairs] + BWD_PINS
