@@ -2,6 +2,7 @@
 // Every check that needs no GPU runs before the first HIP call, so argument
 // errors are reported identically on machines without a device.
 #include <atomic>
+#include <cmath>
 #include <initializer_list>
 #include <climits>
 #include <cstdint>
@@ -23,6 +24,14 @@ bool is_varlen(const lattn_problem& p) { return p.num_seqs > 0; }
 
 int num_seqs_of(const lattn_problem& p) { return is_varlen(p) ? p.num_seqs : p.batch; }
 
+// A kernel exists for head dims (dk, dv) of dtype `in_dtype` at some width.
+bool have_dims(int in_dtype, int dk, int dv) {
+    if (dv % 16 != 0 || dv > 256) return false;
+    for (int nw : {1, 2, 4})
+        if (lattn::have_fwd_kernel(in_dtype, dk, nw) && (dv / 16) % nw == 0) return true;
+    return false;
+}
+
 // Shape/dtype checks that do not look at pointers.
 int check_problem(const lattn_problem& p) {
     if (p.batch < 1 || p.seqlen < 0 || p.num_heads < 1 || p.num_kv_heads < 1 || p.head_dim_qk < 1 ||
@@ -32,25 +41,28 @@ int check_problem(const lattn_problem& p) {
     if (is_varlen(p) && p.batch != 1) return LATTN_ERR_VARLEN_BATCH;
     if (p.in_dtype != LATTN_BF16 && p.in_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
     if (p.out_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
-    if (p.head_dim_v % 16 != 0 || p.head_dim_v > 256) return LATTN_ERR_UNSUPPORTED;
-    bool any = false;
-    for (int nw : {1, 2, 4})
-        any = any || (lattn::have_fwd_kernel(p.in_dtype, p.head_dim_qk, nw) && (p.head_dim_v / 16) % nw == 0);
-    if (!any) return LATTN_ERR_UNSUPPORTED;
+    if (!have_dims(p.in_dtype, p.head_dim_qk, p.head_dim_v)) return LATTN_ERR_UNSUPPORTED;
+    return LATTN_OK;
+}
+
+// The backward also runs the kernel with the head dims swapped.
+int check_bwd_problem(const lattn_problem& p) {
+    const int rc = check_problem(p);
+    if (rc != LATTN_OK) return rc;
+    if (!have_dims(p.in_dtype, p.head_dim_v, p.head_dim_qk)) return LATTN_ERR_UNSUPPORTED;
     return LATTN_OK;
 }
 
 // Workgroup width (waves) for a problem: the widest value block (fewer re-reads of
 // Q and K) that still yields at least one workgroup per compute unit; small
 // problems fall back to narrower blocks for more parallel workgroups.
-int choose_nw(const lattn_problem& p) {
-    const int units = p.head_dim_v / 16;
-    auto usable = [&](int nw) { return units % nw == 0 && lattn::have_fwd_kernel(p.in_dtype, p.head_dim_qk, nw); };
+int choose_nw(int in_dtype, int dk, int dv, int64_t heads) {
+    const int units = dv / 16;
+    auto usable = [&](int nw) { return units % nw == 0 && lattn::have_fwd_kernel(in_dtype, dk, nw); };
     if (const char* env = std::getenv("LATTN_NW")) {
         const int want = std::atoi(env);
         if ((want == 1 || want == 2 || want == 4) && usable(want)) return want;
     }
-    const int64_t heads = (int64_t)num_seqs_of(p) * p.num_heads;
     int narrowest = 0;
     for (int nw : {4, 2, 1}) {
         if (!usable(nw)) continue;
@@ -76,11 +88,61 @@ int device_check() {
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Launch parameters for one run of the chunked kernel over problem p with head dims
+// (dk, dv) of its operands (the forward's, or swapped for a gradient sweep).
+// Returns false when the grid would not fit an int.
+bool make_params(const lattn_problem& p, int dk, int dv, int nw, const float* g_gamma, float scale,
+                 const int32_t* cu, const int32_t* order, lattn::FwdParams& fp) {
+    fp = lattn::FwdParams{};
+    fp.g_gamma = g_gamma;
+    fp.cu = cu;
+    fp.order = order;
+    fp.batch = p.batch;
+    fp.seqlen = p.seqlen;
+    fp.num_heads = p.num_heads;
+    fp.num_kv_heads = p.num_kv_heads;
+    fp.dk = dk;
+    fp.dv = dv;
+    fp.num_seqs = num_seqs_of(p);
+    fp.nvb = dv / (16 * nw);
+    if ((int64_t)fp.num_seqs * p.num_kv_heads > INT_MAX) return false;
+    fp.num_groups = fp.num_seqs * p.num_kv_heads;
+    fp.group_size = (p.num_heads / p.num_kv_heads) * fp.nvb;
+    fp.scale = scale;
+    lattn::set_forward_defaults(fp);
+    const int64_t grid = (int64_t)lattn::kNumXcd * ((fp.num_groups + lattn::kNumXcd - 1) / lattn::kNumXcd) *
+                         fp.group_size;
+    return grid <= INT_MAX;
+}
+
+int64_t heads_of(const lattn_problem& p) { return (int64_t)num_seqs_of(p) * p.num_heads; }
+
+// Byte offsets of the backward workspace regions (each 256-byte aligned).
+struct BwdLayout {
+    size_t order = 0, part = 0, total = 0;
+};
+BwdLayout bwd_layout(const lattn_problem& p) {
+    BwdLayout l;
+    size_t off = 0;
+    if (is_varlen(p) && p.num_seqs <= lattn::kMaxOrderedSeqs) {
+        l.order = off;
+        off += round_up((size_t)p.num_seqs * sizeof(int32_t), 256);
+    }
+    const size_t rows = (size_t)p.batch * (size_t)p.seqlen;
+    if (p.num_heads > p.num_kv_heads) {
+        l.part = off;
+        const int d = p.head_dim_qk > p.head_dim_v ? p.head_dim_qk : p.head_dim_v;
+        off += round_up(rows * p.num_heads * d * 4, 256);
+    }
+    l.total = off;
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
 
-int lattn_abi_version(void) { return 1; }
+int lattn_abi_version(void) { return 2; }
 
 const char* lattn_status_string(int status) {
     switch (status) {
@@ -135,32 +197,17 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
     const size_t need = lattn_fwd_workspace_size(p);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LATTN_ERR_WORKSPACE;
 
-    const int nw = choose_nw(*p);
+    const int nw = choose_nw(p->in_dtype, p->head_dim_qk, p->head_dim_v, heads_of(*p));
+    const int32_t* order = (varlen && need > 0) ? static_cast<const int32_t*>(workspace) : nullptr;
     lattn::FwdParams fp;
+    if (!make_params(*p, p->head_dim_qk, p->head_dim_v, nw, g_gamma, scale, cu_seqlens, order, fp))
+        return LATTN_ERR_INVALID_ARG;
     fp.q = q;
     fp.k = k;
     fp.v = v;
-    fp.g_gamma = g_gamma;
     fp.init = initial_state;
-    fp.cu = cu_seqlens;
-    fp.order = (varlen && need > 0) ? static_cast<const int32_t*>(workspace) : nullptr;
     fp.o = static_cast<float*>(o);
     fp.final_state = final_state;
-    fp.batch = p->batch;
-    fp.seqlen = p->seqlen;
-    fp.num_heads = p->num_heads;
-    fp.num_kv_heads = p->num_kv_heads;
-    fp.dk = p->head_dim_qk;
-    fp.dv = p->head_dim_v;
-    fp.num_seqs = num_seqs_of(*p);
-    fp.nvb = p->head_dim_v / (16 * nw);
-    if ((int64_t)fp.num_seqs * p->num_kv_heads > INT_MAX) return LATTN_ERR_INVALID_ARG;
-    fp.num_groups = fp.num_seqs * p->num_kv_heads;
-    fp.group_size = (p->num_heads / p->num_kv_heads) * fp.nvb;
-    fp.scale = scale;
-    const int64_t grid = (int64_t)lattn::kNumXcd * ((fp.num_groups + lattn::kNumXcd - 1) / lattn::kNumXcd) *
-                         fp.group_size;
-    if (grid > INT_MAX) return LATTN_ERR_INVALID_ARG;
 
     const int dc = device_check();
     if (dc != LATTN_OK) return dc;
@@ -171,6 +218,104 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
             return LATTN_ERR_LAUNCH;
     }
     if (lattn::launch_fwd(fp, p->in_dtype, nw, reverse != 0, s) != hipSuccess) return LATTN_ERR_LAUNCH;
+    return LATTN_OK;
+}
+
+size_t lattn_bwd_workspace_size(const lattn_problem* p) {
+    if (p == nullptr || check_bwd_problem(*p) != LATTN_OK) return 0;
+    return bwd_layout(*p).total;
+}
+
+int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* v, const float* g_gamma,
+              float scale, const float* initial_state, int reverse, const int32_t* cu_seqlens, const void* d_o,
+              const float* d_final_state, float* dq, float* dk, float* dv, float* d_initial_state,
+              void* workspace, size_t workspace_bytes, void* stream) {
+    if (p == nullptr) return LATTN_ERR_INVALID_ARG;
+    const int rc = check_bwd_problem(*p);
+    if (rc != LATTN_OK) return rc;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen != is_varlen(*p)) return LATTN_ERR_INVALID_ARG;
+    const int64_t tokens = (int64_t)p->batch * p->seqlen;
+    if (tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || d_o == nullptr || dq == nullptr ||
+                       dk == nullptr || dv == nullptr))
+        return LATTN_ERR_INVALID_ARG;
+    if (g_gamma == nullptr) return LATTN_ERR_INVALID_ARG;
+    // The dk and dv sweeps carry D / scale, so scale must be finite, normal and nonzero.
+    if (!(std::fabs(scale) >= 1.17549435e-38f && std::fabs(scale) <= 3.40282347e+38f)) return LATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(d_o, 16) || !aligned(g_gamma, 4) ||
+        !aligned(initial_state, 16) || !aligned(d_final_state, 16) || !aligned(dq, 16) || !aligned(dk, 16) ||
+        !aligned(dv, 16) || !aligned(d_initial_state, 16) || !aligned(cu_seqlens, 4) || !aligned(workspace, 16))
+        return LATTN_ERR_INVALID_ARG;
+    const BwdLayout lay = bwd_layout(*p);
+    if (lay.total > 0 && (workspace == nullptr || workspace_bytes < lay.total)) return LATTN_ERR_WORKSPACE;
+
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const int32_t* order =
+        (varlen && p->num_seqs <= lattn::kMaxOrderedSeqs) ? reinterpret_cast<const int32_t*>(ws + lay.order) : nullptr;
+    const int dkd = p->head_dim_qk, dvd = p->head_dim_v;
+    const bool grouped = p->num_heads > p->num_kv_heads;
+    const void* dob = d_o;
+    float* part = grouped ? reinterpret_cast<float*>(ws + lay.part) : nullptr;
+    const float inv_scale = 1.0f / scale;
+    const int64_t heads = heads_of(*p);
+
+    // dq: the forward recurrence on (dO, V, K) with the transposed initial state.
+    lattn::FwdParams pq, pk, pv;
+    const int nw_q = choose_nw(p->in_dtype, dvd, dkd, heads);
+    if (!make_params(*p, dvd, dkd, nw_q, g_gamma, scale, cu_seqlens, order, pq)) return LATTN_ERR_INVALID_ARG;
+    pq.q = dob;
+    pq.k = v;
+    pq.v = k;
+    pq.init = initial_state;
+    pq.init_rs = 1;
+    pq.init_cs = dvd;
+    pq.o = dq;
+    pq.final_state = nullptr;
+    // dk: opposite direction on (V, dO, Q); the state is D^T / scale and d_final_state
+    // enters at the first processed position.
+    const int nw_k = nw_q;
+    if (!make_params(*p, dvd, dkd, nw_k, g_gamma, scale, cu_seqlens, order, pk)) return LATTN_ERR_INVALID_ARG;
+    pk.swap_heads = 1;
+    pk.q = v;
+    pk.k = dob;
+    pk.v = q;
+    pk.init = d_final_state;
+    pk.init_rs = 1;
+    pk.init_cs = dvd;
+    pk.init_mul = inv_scale;
+    pk.init_at_end = 1;
+    pk.o = grouped ? part : dk;
+    pk.final_state = nullptr;
+    // dv: opposite direction on (K, Q, dO); the state is D / scale, and its final
+    // value gives d_initial_state = lam * scale * state.
+    const int nw_v = choose_nw(p->in_dtype, dkd, dvd, heads);
+    if (!make_params(*p, dkd, dvd, nw_v, g_gamma, scale, cu_seqlens, order, pv)) return LATTN_ERR_INVALID_ARG;
+    pv.swap_heads = 1;
+    pv.q = k;
+    pv.k = q;
+    pv.v = dob;
+    pv.init = d_final_state;
+    pv.init_mul = inv_scale;
+    pv.init_at_end = 1;
+    pv.o = grouped ? part : dv;
+    pv.final_state = d_initial_state;
+    pv.final_mul = scale;
+    pv.final_lam = 1;
+
+    const int dc = device_check();
+    if (dc != LATTN_OK) return dc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (order != nullptr &&
+        lattn::launch_seq_order(cu_seqlens, p->num_seqs, p->seqlen, const_cast<int32_t*>(order), s) != hipSuccess)
+        return LATTN_ERR_LAUNCH;
+    const bool rev = reverse != 0;
+    if (lattn::launch_fwd(pq, p->in_dtype, nw_q, rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
+    if (lattn::launch_fwd(pk, p->in_dtype, nw_k, !rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
+    if (grouped && lattn::launch_group_sum(part, dk, tokens, p->num_heads, p->num_kv_heads, dkd, s) != hipSuccess)
+        return LATTN_ERR_LAUNCH;
+    if (lattn::launch_fwd(pv, p->in_dtype, nw_v, !rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
+    if (grouped && lattn::launch_group_sum(part, dv, tokens, p->num_heads, p->num_kv_heads, dvd, s) != hipSuccess)
+        return LATTN_ERR_LAUNCH;
     return LATTN_OK;
 }
 

@@ -318,13 +318,16 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
     const float g2 = p.g_gamma[wk.h] * kLog2e;  // log2 of the per-step decay
     const int L = (int)wk.len;
     const int nch = (L + kChunk - 1) / kChunk;
-    const int H = p.num_heads, Hkv = p.num_kv_heads, dv = p.dv;
+    const int H = p.num_heads, dv = p.dv;
     const int col = 16 * wv + lr;  // this lane's value column inside the block
-    const uint32_t qrow_b = (uint32_t)H * DK * 2, krow_b = (uint32_t)Hkv * DK * 2;
-    const uint32_t vrow_b = (uint32_t)Hkv * dv * 2, orow_b = (uint32_t)H * dv * 4;
-    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)wk.h * DK;
-    const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)wk.kvh * DK;
-    const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)wk.kvh * dv + wk.vb * BV;
+    // Operand heads: q at h and k, v at the kv head, or the other way round.
+    const int qh = p.swap_heads ? wk.kvh : wk.h, kh = p.swap_heads ? wk.h : wk.kvh;
+    const int QH = p.swap_heads ? p.num_kv_heads : H, KH = p.swap_heads ? H : p.num_kv_heads;
+    const uint32_t qrow_b = (uint32_t)QH * DK * 2, krow_b = (uint32_t)KH * DK * 2;
+    const uint32_t vrow_b = (uint32_t)KH * dv * 2, orow_b = (uint32_t)H * dv * 4;
+    const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)qh * DK;
+    const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)kh * DK;
+    const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)kh * dv + wk.vb * BV;
     const uint32_t smem_base = lds_addr(smem);
 
     // Tiles (1, 0) and (3, 2) lie above the diagonal: their halves of P stay zero.
@@ -360,13 +363,17 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
 
     // State block: tile mt holds rows dmap(mt, 4*lg + ii) at column `col`.
     f32x4 S[MT];
-    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv + (int64_t)wk.vb * BV;
+    const int64_t st_blk = ((int64_t)wk.n * H + wk.h) * DK * dv;  // this head's state block
+    const int64_t st_off = st_blk + (int64_t)wk.vb * BV;
     {
-        const auto ri = make_rsrc(p.init ? p.init + st_off : p.final_state, p.init ? (uint32_t)(DK * dv * 4) : 0u);
+        // Without an initial state the descriptor is empty and every load returns 0.
+        const auto ri = make_rsrc(p.init ? p.init + st_blk : p.g_gamma, p.init ? (uint32_t)(DK * dv * 4) : 0u);
+        const int rs = (int)p.init_rs, cs = (int)p.init_cs, gcol = wk.vb * BV + col;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) S[mt][ii] = buf_load_f32(ri, (dmap(mt, 4 * lg + ii) * dv + col) * 4);
+            for (int ii = 0; ii < 4; ++ii)
+                S[mt][ii] = p.init_mul * buf_load_f32(ri, (dmap(mt, 4 * lg + ii) * rs + gcol * cs) * 4);
     }
     bf16x8 Shi[KB], Slo[KB];
     split_state<KB>(S, Shi, Slo);
@@ -384,9 +391,9 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
         const bool real = c < nch;
         const int Lc = real ? min(kChunk, L - p0) : 1;
         const int64_t r0 = real ? first_row(p0, Lc) : 0;
-        const RawBuf rq = raw_buf(qg + r0 * H * DK, real ? (uint32_t)(Lc - 1) * qrow_b + DK * 2 : 0u);
-        const RawBuf rk = raw_buf(kg + r0 * Hkv * DK, real ? (uint32_t)(Lc - 1) * krow_b + DK * 2 : 0u);
-        const RawBuf rv = raw_buf(vg + r0 * Hkv * dv, real ? (uint32_t)(Lc - 1) * vrow_b + BV * 2 : 0u);
+        const RawBuf rq = raw_buf(qg + r0 * QH * DK, real ? (uint32_t)(Lc - 1) * qrow_b + DK * 2 : 0u);
+        const RawBuf rk = raw_buf(kg + r0 * KH * DK, real ? (uint32_t)(Lc - 1) * krow_b + DK * 2 : 0u);
+        const RawBuf rv = raw_buf(vg + r0 * KH * dv, real ? (uint32_t)(Lc - 1) * vrow_b + BV * 2 : 0u);
 #pragma unroll
         for (int j = 0; j < Cfg::QCOPIES; ++j) {
             const int kbyte = j * NW + wv;  // this wave's kilobyte of the tile
@@ -431,9 +438,12 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
         // S <- lam^Lc S + K^T (decayed V).  Operands by transposing reads: lane group
         // lg takes tokens 32kb + 8lg + 0..7; the A operand row of lane lr is dk
         // dmap(mt, lr); the B operand (column `col`) is decayed in registers.
-        float lamL = lamC;
+        // A state handed in at the first processed position (gradient sweeps) reaches
+        // the first chunk one decay step less far.
+        const bool at_end = p.init_at_end && c == 0;
+        float lamL = at_end ? exp2f(g2 * (float)(Lc - 1)) : lamC;
         if (Lc != kChunk) {  // the last chunk of a sequence: decays to its own end
-            lamL = exp2f(g2 * (float)Lc);
+            lamL = exp2f(g2 * (float)(at_end ? Lc - 1 : Lc));
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -525,11 +535,19 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
                 default: qs_and_tiles(IntC<3>{}); break;
             }
         }
-        // The inter-chunk part decays by lam^(i+1) (times scale).
+        // The inter-chunk part decays by lam^(i+1) (times scale); lam^i for a state
+        // handed in at the first position.
+        if (at_end) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[b][ii] *= lamq[b][ii];
+                for (int ii = 0; ii < 4; ++ii) O[b][ii] *= sc * exp2f(g2 * (float)(16 * b + 4 * lg + ii));
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) O[b][ii] *= lamq[b][ii];
+        }
         lds_barrier();  // P complete
 
         // O += P V.  For row tile b and token block kb, P elements 0..3 are tokens
@@ -575,10 +593,14 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
         wait_vmem<0>();  // no copy may still be writing LDS when the workgroup ends
     }
 
+    if (p.final_state) {
+        const float fm = (p.final_lam && nch > 0) ? p.final_mul * exp2f(g2) : p.final_mul;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) p.final_state[st_off + (int64_t)dmap(mt, 4 * lg + ii) * dv + col] = S[mt][ii];
+            for (int ii = 0; ii < 4; ++ii)
+                p.final_state[st_off + (int64_t)dmap(mt, 4 * lg + ii) * dv + col] = fm * S[mt][ii];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -622,12 +644,15 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
     const int H = p.num_heads, dv = p.dv;
     const int vcol = wk.vb * BV + 16 * wv + lr;
 
-    const float* qbase = static_cast<const float*>(p.q) + (int64_t)wk.h * DK;
-    const float* kbase = static_cast<const float*>(p.k) + (int64_t)wk.kvh * DK;
-    const float* vbase = static_cast<const float*>(p.v) + (int64_t)wk.kvh * dv + wk.vb * BV;
-    const int64_t qstride = (int64_t)H * DK;
-    const int64_t kstride = (int64_t)p.num_kv_heads * DK;
-    const int64_t vstride = (int64_t)p.num_kv_heads * dv;
+    // Operand heads: q at h and k, v at the kv head, or the other way round.
+    const int qh = p.swap_heads ? wk.kvh : wk.h, kh = p.swap_heads ? wk.h : wk.kvh;
+    const int QH = p.swap_heads ? p.num_kv_heads : H, KH = p.swap_heads ? H : p.num_kv_heads;
+    const float* qbase = static_cast<const float*>(p.q) + (int64_t)qh * DK;
+    const float* kbase = static_cast<const float*>(p.k) + (int64_t)kh * DK;
+    const float* vbase = static_cast<const float*>(p.v) + (int64_t)kh * dv + wk.vb * BV;
+    const int64_t qstride = (int64_t)QH * DK;
+    const int64_t kstride = (int64_t)KH * DK;
+    const int64_t vstride = (int64_t)KH * dv;
     auto tok_row = [&](int64_t pos) -> int64_t { return REV ? wk.start + L - 1 - pos : wk.start + pos; };
 
     LaneDecay dec;
@@ -641,7 +666,9 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-            S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
+            S[mt][ii] = p.init ? p.init_mul * p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * p.init_rs +
+                                                      (int64_t)vcol * p.init_cs]
+                               : 0.f;
 
     f32x4 pq[Cfg::QPER];
     f32x4 pk[Cfg::KPER][4];
@@ -760,10 +787,20 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
                     O[b] = mfma_f32(qa[b][ii], S[t][ii], O[b]);
                 }
         }
+        // A state handed in at the first processed position (gradient sweeps) reaches
+        // the first chunk one decay step less far.
+        const bool at_end = p.init_at_end && c == 0;
+        if (at_end) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+            for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[b][ii] *= dec.lamq[b][ii];
+                for (int ii = 0; ii < 4; ++ii) O[b][ii] *= exp2f(g2 * (float)(16 * b + 4 * lg + ii));
+        } else {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) O[b][ii] *= dec.lamq[b][ii];
+        }
         // O += (A .* M) V; token step (a, ii) pairs lane group lg with j = 16a + 4lg + ii.
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
@@ -783,7 +820,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
                 if (p0 + i < L) p.o[(tok_row(p0 + i) * H + wk.h) * dv + vcol] = p.scale * O[b][ii];
             }
         const int Lc = (int)min((int64_t)kChunk, L - p0);
-        const float lamL = (Lc == kChunk) ? lamC : exp2f(g2 * (float)Lc);
+        const float lamL = at_end ? exp2f(g2 * (float)(Lc - 1)) : (Lc == kChunk) ? lamC : exp2f(g2 * (float)Lc);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) S[mt] *= lamL;
 #pragma unroll
@@ -808,11 +845,32 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
         compute_chunk(c, st);
     }
 
+    if (p.final_state) {
+        const float fm = (p.final_lam && nch > 0) ? p.final_mul * exp2f(g2) : p.final_mul;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = S[mt][ii];
+            for (int ii = 0; ii < 4; ++ii)
+                p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = fm * S[mt][ii];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Gradient sweeps under grouped-query attention: the sum of per-query-head
+// gradients into their kv head, streamed in 16-byte pieces.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void group_sum_kernel(const float* __restrict__ part, float* __restrict__ out,
+                                                        int64_t n4, int G, int d4) {
+    // n4 = rows * Hkv * d4 output pieces; piece i is (row * Hkv + j, x4) and reads
+    // the G query heads j*G .. j*G+G-1 of the same row, which are contiguous.
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+        const int64_t rj = i / d4, x4 = i % d4;
+        const float* src = part + (rj * G * d4 + x4) * 4;
+        f32x4 acc = *reinterpret_cast<const f32x4*>(src);
+        for (int g = 1; g < G; ++g) acc += *reinterpret_cast<const f32x4*>(src + (int64_t)g * d4 * 4);
+        *reinterpret_cast<f32x4*>(out + i * 4) = acc;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -938,6 +996,20 @@ hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hi
         }
     }
     return hipErrorInvalidValue;
+}
+
+namespace {
+int stream_blocks(int64_t n4) {
+    const int64_t b = (n4 + 255) / 256;
+    return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+}  // namespace
+
+hipError_t launch_group_sum(const float* part, float* out, int64_t rows, int H, int Hkv, int d, hipStream_t s) {
+    const int64_t n4 = rows * Hkv * (d / 4);
+    if (n4 == 0) return hipSuccess;
+    hipLaunchKernelGGL(group_sum_kernel, dim3(stream_blocks(n4)), dim3(256), 0, s, part, out, n4, H / Hkv, d / 4);
+    return hipGetLastError();
 }
 
 hipError_t launch_seq_order(const int32_t* cu, int num_seqs, int seqlen, int32_t* order, hipStream_t s) {

@@ -38,7 +38,29 @@ struct FwdParams {
     int num_groups;   // num_seqs * num_kv_heads
     int group_size;   // (num_heads / num_kv_heads) * nvb workgroups per group
     float scale;
+    // Generalisations used by the gradient sweeps; the forward pass sets the
+    // defaults noted on each field.
+    int swap_heads;   // 1: q is read at kv head h / group and k, v at query head h (default 0)
+    int64_t init_rs;  // element stride of a state row (dk index) inside one init block (default dv)
+    int64_t init_cs;  // element stride of a state column (dv index) (default 1)
+    float init_mul;   // init is multiplied by this when loaded (default 1)
+    int init_at_end;  // 1: init already sits at the first processed position, so it
+                      //    reaches that token undecayed (default 0: one decay step)
+    float final_mul;  // final_state = final_mul * S (default 1) ...
+    int final_lam;    // ... times exp(g_gamma[h]) when set and the sequence is not empty
+                      //    (default 0); final_state may be null
 };
+
+// Forward defaults of the fields above.
+inline void set_forward_defaults(FwdParams& p) {
+    p.swap_heads = 0;
+    p.init_rs = p.dv;
+    p.init_cs = 1;
+    p.init_mul = 1.f;
+    p.init_at_end = 0;
+    p.final_mul = 1.f;
+    p.final_lam = 0;
+}
 
 // Workgroups of 64 * nw threads own BV = 16 * nw value columns each.
 bool have_fwd_kernel(int in_dtype, int dk, int nw);
@@ -46,6 +68,10 @@ bool have_fwd_kernel(int in_dtype, int dk, int nw);
 int fwd_grid_size(const FwdParams& p);
 // Enqueue the forward kernel; returns the HIP error of the launch.
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t stream);
+// out[r, j, :] = sum over g < G of part[r, j * G + g, :] for rows r < rows, j < Hkv,
+// with G = H / Hkv and d a multiple of 4.
+hipError_t launch_group_sum(const float* part, float* out, int64_t rows, int H, int Hkv, int d,
+                            hipStream_t stream);
 // Enqueue the longest-first ordering of packed sequences into `order`.
 hipError_t launch_seq_order(const int32_t* cu, int num_seqs, int seqlen, int32_t* order,
                             hipStream_t stream);

@@ -28,6 +28,7 @@ import numpy as np
 BLOCK = 1 << 22
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_INIT, STREAM_LENS = 0, 1, 2, 3, 4
+STREAM_DO, STREAM_DFINAL = 5, 6  # gradients for the backward
 
 
 def _threads() -> int:
@@ -131,6 +132,17 @@ class Workload:
         if self.init_std is not None:
             out["initial_state"] = normal((self.num_seqs, H, self.dk, self.dv), self.seed,
                                           STREAM_INIT, std=self.init_std)
+        return out
+
+    def make_grads(self, final_std: float | None = 1.0) -> dict:
+        """Draw an output gradient d_o (the shape of o, in the input dtype like q, k, v)
+        and, unless ``final_std`` is None, a float32 final-state gradient d_final_state."""
+        B, T, H = self.batch, self.seqlen, self.num_heads
+        bf = self.dtype == "bf16"
+        out = {"d_o": normal((B, T, H, self.dv), self.seed, STREAM_DO, as_bf16=bf), "d_final_state": None}
+        if final_std is not None:
+            out["d_final_state"] = normal((self.num_seqs, H, self.dk, self.dv), self.seed,
+                                          STREAM_DFINAL, std=final_std)
         return out
 
 

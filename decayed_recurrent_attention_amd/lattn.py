@@ -4,10 +4,11 @@ Argument marshalling only: torch tensors supply device memory and the current
 HIP stream; every step of the forward pass runs in the library's kernels.  A
 missing library raises; there is no fallback path.
 
-Functions with the C names (``lattn_fwd``, ``lattn_fwd_workspace_size``,
-``lattn_lightning_g_gamma``, ``lattn_status_string``) map one to one onto the
-ABI.  ``lightning_attn`` and ``recurrent`` mirror the signatures of the
-ejkernel lightning_attn and recurrent interface pages (without the GLA gates).
+Functions with the C names (``lattn_fwd``, ``lattn_bwd`` and their workspace
+queries, ``lattn_lightning_g_gamma``, ``lattn_status_string``) map one to one onto
+the ABI.  ``lightning_attn`` and ``recurrent`` mirror the signatures of the ejkernel
+lightning_attn and recurrent interface pages (without the GLA gates);
+``recurrent_bwd`` and ``lightning_attn_bwd`` return the gradients of those.
 """
 from __future__ import annotations
 
@@ -32,8 +33,8 @@ LATTN_ERR_LAUNCH = -6
 LATTN_ERR_DEVICE = -7
 
 # Every function declared in include/lattn.h.
-EXPORTS = ("lattn_fwd", "lattn_fwd_workspace_size", "lattn_lightning_g_gamma",
-           "lattn_status_string", "lattn_abi_version")
+EXPORTS = ("lattn_fwd", "lattn_fwd_workspace_size", "lattn_bwd", "lattn_bwd_workspace_size",
+           "lattn_lightning_g_gamma", "lattn_status_string", "lattn_abi_version")
 
 
 class LattnProblem(ctypes.Structure):
@@ -68,6 +69,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp, vp, ctypes.c_size_t, vp]
             lib.lattn_fwd_workspace_size.restype = ctypes.c_size_t
             lib.lattn_fwd_workspace_size.argtypes = [P]
+            lib.lattn_bwd.restype = ctypes.c_int
+            lib.lattn_bwd.argtypes = [P, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int, vp, vp, vp,
+                                      vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+            lib.lattn_bwd_workspace_size.restype = ctypes.c_size_t
+            lib.lattn_bwd_workspace_size.argtypes = [P]
             lib.lattn_lightning_g_gamma.restype = ctypes.c_int
             lib.lattn_lightning_g_gamma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
             lib.lattn_status_string.restype = ctypes.c_char_p
@@ -89,6 +95,10 @@ def lattn_abi_version() -> int:
 
 def lattn_fwd_workspace_size(problem: LattnProblem) -> int:
     return int(load_library().lattn_fwd_workspace_size(ctypes.byref(problem)))
+
+
+def lattn_bwd_workspace_size(problem: LattnProblem) -> int:
+    return int(load_library().lattn_bwd_workspace_size(ctypes.byref(problem)))
 
 
 def lattn_lightning_g_gamma(num_heads: int, layer_idx: int, num_layers: int) -> np.ndarray:
@@ -119,7 +129,22 @@ def lattn_fwd(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_sta
         _ptr(workspace), ws_bytes, stream))
 
 
-# -- tensor-level forward ---------------------------------------------------------
+def lattn_bwd(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_state, reverse: bool,
+              cu_seqlens, d_o, d_final_state, dq, dk, dv, d_initial_state, workspace=None,
+              stream=None) -> int:
+    """Raw call: tensors (or None) are passed by address; returns the status code."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return int(load_library().lattn_bwd(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g_gamma), float(scale),
+        _ptr(initial_state), int(bool(reverse)), _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state),
+        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_initial_state), _ptr(workspace), ws_bytes, stream))
+
+
+# -- tensor-level forward and backward ----------------------------------------------
 _G_CACHE: dict = {}
 
 
@@ -133,18 +158,16 @@ def _dtype_code(t) -> int:
     raise TypeError(f"q, k, v must be bfloat16 or float32, got {t.dtype}")
 
 
-def recurrent(query, key, value, g_gamma=None, softmax_scale=None, initial_state=None,
-              reverse=False, cu_seqlens=None):
-    """Decayed recurrent attention forward on the GPU.
+class _Args:
+    """Validated, contiguous arguments shared by the forward and backward calls."""
 
-    Shapes follow the recurrent interface page: q [B, T, H, dk], k [B, T, Hkv, dk],
-    v [B, T, Hkv, dv]; packed input (``cu_seqlens``) may drop the batch axis.
-    Returns (o float32 [.., T, H, dv], final_state float32 [N_seq, H, dk, dv]).
-    """
+
+def _prepare(query, key, value, g_gamma, softmax_scale, initial_state, cu_seqlens) -> _Args:
     import torch
 
-    squeeze = query.dim() == 3
-    if squeeze:
+    a = _Args()
+    a.squeeze = query.dim() == 3
+    if a.squeeze:
         if cu_seqlens is None:
             raise ValueError("3-D inputs are only accepted with cu_seqlens")
         query, key, value = query.unsqueeze(0), key.unsqueeze(0), value.unsqueeze(0)
@@ -174,7 +197,7 @@ def recurrent(query, key, value, g_gamma=None, softmax_scale=None, initial_state
         if initial_state is not None and initial_state.shape[0] != num_seqs:
             raise ValueError(f"initial_state holds {initial_state.shape[0]} states but "
                              f"cu_seqlens describes {num_seqs} sequences")
-    n_seq = num_seqs if cu is not None else B
+    a.n_seq = num_seqs if cu is not None else B
     if softmax_scale is None:
         softmax_scale = float(np.float32(dk ** -0.5))
     if g_gamma is None:
@@ -182,20 +205,76 @@ def recurrent(query, key, value, g_gamma=None, softmax_scale=None, initial_state
     g_gamma = torch.as_tensor(g_gamma).to(device=dev, dtype=torch.float32).contiguous()
     if g_gamma.shape != (H,):
         raise ValueError(f"g_gamma must have shape ({H},)")
+    a.state_shape = (a.n_seq, H, dk, dv)
     if initial_state is not None:
         initial_state = initial_state.to(device=dev, dtype=torch.float32).contiguous()
-        if initial_state.shape != (n_seq, H, dk, dv):
-            raise ValueError(f"initial_state must have shape {(n_seq, H, dk, dv)}")
-    q, k, v = query.contiguous(), key.contiguous(), value.contiguous()
-    prob = LattnProblem(B, T, H, Hkv, dk, dv, num_seqs, _dtype_code(q), LATTN_F32)
-    o = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
-    fs = torch.empty((n_seq, H, dk, dv), device=dev, dtype=torch.float32)
-    ws_bytes = lattn_fwd_workspace_size(prob)
-    ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
-    rc = lattn_fwd(prob, q, k, v, g_gamma, softmax_scale, initial_state, reverse, cu, o, fs, ws)
+        if initial_state.shape != a.state_shape:
+            raise ValueError(f"initial_state must have shape {a.state_shape}")
+    a.q, a.k, a.v = query.contiguous(), key.contiguous(), value.contiguous()
+    a.cu, a.g, a.scale, a.init, a.dev = cu, g_gamma, softmax_scale, initial_state, dev
+    a.B, a.T, a.H, a.Hkv, a.dk, a.dv = B, T, H, Hkv, dk, dv
+    a.prob = LattnProblem(B, T, H, Hkv, dk, dv, num_seqs, _dtype_code(a.q), LATTN_F32)
+    return a
+
+
+def recurrent(query, key, value, g_gamma=None, softmax_scale=None, initial_state=None,
+              reverse=False, cu_seqlens=None):
+    """Decayed recurrent attention forward on the GPU.
+
+    Shapes follow the recurrent interface page: q [B, T, H, dk], k [B, T, Hkv, dk],
+    v [B, T, Hkv, dv]; packed input (``cu_seqlens``) may drop the batch axis.
+    Returns (o float32 [.., T, H, dv], final_state float32 [N_seq, H, dk, dv]).
+    """
+    import torch
+
+    a = _prepare(query, key, value, g_gamma, softmax_scale, initial_state, cu_seqlens)
+    o = torch.empty((a.B, a.T, a.H, a.dv), device=a.dev, dtype=torch.float32)
+    fs = torch.empty(a.state_shape, device=a.dev, dtype=torch.float32)
+    ws_bytes = lattn_fwd_workspace_size(a.prob)
+    ws = torch.empty(ws_bytes, device=a.dev, dtype=torch.uint8) if ws_bytes else None
+    rc = lattn_fwd(a.prob, a.q, a.k, a.v, a.g, a.scale, a.init, reverse, a.cu, o, fs, ws)
     if rc != LATTN_OK:
         raise LattnError(rc)
-    return (o[0] if squeeze else o), fs
+    return (o[0] if a.squeeze else o), fs
+
+
+def recurrent_bwd(query, key, value, d_o, g_gamma=None, softmax_scale=None, initial_state=None,
+                  d_final_state=None, reverse=False, cu_seqlens=None, want_d_initial_state=True):
+    """Gradients of ``recurrent`` on the GPU for output gradient ``d_o`` (the shape of
+    o, in the dtype of the inputs) and ``d_final_state`` (float32 [N_seq, H, dk, dv]
+    or None).
+
+    Returns float32 (dq [.., T, H, dk], dk [.., T, Hkv, dk], dv [.., T, Hkv, dv],
+    d_initial_state [N_seq, H, dk, dv] or None).
+    """
+    import torch
+
+    a = _prepare(query, key, value, g_gamma, softmax_scale, initial_state, cu_seqlens)
+    if a.squeeze:
+        d_o = d_o.unsqueeze(0)
+    if d_o.dtype != a.q.dtype:
+        raise TypeError(f"d_o must have the dtype of the inputs ({a.q.dtype}), got {d_o.dtype}")
+    d_o = d_o.to(device=a.dev).contiguous()
+    if d_o.shape != (a.B, a.T, a.H, a.dv):
+        raise ValueError(f"d_o must have shape {(a.B, a.T, a.H, a.dv)}")
+    if d_final_state is not None:
+        d_final_state = d_final_state.to(device=a.dev, dtype=torch.float32).contiguous()
+        if d_final_state.shape != a.state_shape:
+            raise ValueError(f"d_final_state must have shape {a.state_shape}")
+    f32 = dict(device=a.dev, dtype=torch.float32)
+    dq = torch.empty((a.B, a.T, a.H, a.dk), **f32)
+    dk = torch.empty((a.B, a.T, a.Hkv, a.dk), **f32)
+    dv = torch.empty((a.B, a.T, a.Hkv, a.dv), **f32)
+    d_init = torch.empty(a.state_shape, **f32) if want_d_initial_state else None
+    ws_bytes = lattn_bwd_workspace_size(a.prob)
+    ws = torch.empty(ws_bytes, device=a.dev, dtype=torch.uint8) if ws_bytes else None
+    rc = lattn_bwd(a.prob, a.q, a.k, a.v, a.g, a.scale, a.init, reverse, a.cu, d_o, d_final_state,
+                   dq, dk, dv, d_init, ws)
+    if rc != LATTN_OK:
+        raise LattnError(rc)
+    if a.squeeze:
+        dq, dk, dv = dq[0], dk[0], dv[0]
+    return dq, dk, dv, d_init
 
 
 def lightning_g_gamma_tensor(num_heads: int, layer_idx: int, num_layers: int, device):
@@ -228,3 +307,16 @@ def lightning_attn(query, key, value, layer_idx: int, num_layers: int, softmax_s
     g = lightning_g_gamma_tensor(query.shape[-2], layer_idx, num_layers, query.device)
     return recurrent(query, key, value, g_gamma=g, softmax_scale=softmax_scale,
                      initial_state=initial_state, reverse=reverse, cu_seqlens=cu_seqlens)
+
+
+def lightning_attn_bwd(query, key, value, d_o, layer_idx: int, num_layers: int, softmax_scale=None,
+                       initial_state=None, d_final_state=None, reverse=False, cu_seqlens=None):
+    """Gradients of ``lightning_attn`` (same decay schedule and default scale)."""
+    if num_layers < 1 or not 0 <= layer_idx <= num_layers:
+        raise ValueError("need num_layers >= 1 and 0 <= layer_idx <= num_layers")
+    if softmax_scale is None:
+        softmax_scale = float(np.float32(key.shape[-1] ** -0.5))
+    g = lightning_g_gamma_tensor(query.shape[-2], layer_idx, num_layers, query.device)
+    return recurrent_bwd(query, key, value, d_o, g_gamma=g, softmax_scale=softmax_scale,
+                         initial_state=initial_state, d_final_state=d_final_state, reverse=reverse,
+                         cu_seqlens=cu_seqlens)

@@ -1,5 +1,5 @@
 /*
- * lattn — Lightning (decayed recurrent) attention forward pass on AMD MI355X (gfx950).
+ * lattn — Lightning (decayed recurrent) attention, forward and backward, on AMD MI355X (gfx950).
  *
  * Public C ABI of liblattn.so.  Plain C types only: device buffers are passed as
  * untyped pointers, the HIP stream as `void*` (a hipStream_t; NULL = the default
@@ -99,6 +99,52 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
               size_t workspace_bytes, void* stream);
 
 /*
+ * Device workspace (bytes) that lattn_bwd needs for problem *p: room for the
+ * per-query-head gradients before their sum into kv heads (num_heads >
+ * num_kv_heads) and for the sequence order of packed input; 0 when neither
+ * applies.  Returns 0 also for an invalid problem.
+ */
+size_t lattn_bwd_workspace_size(const lattn_problem* p);
+
+/*
+ * Backward pass, enqueued on `stream` (recurrent interface page, the custom-VJP
+ * backward rule: from dO and d final_state to dq, dk, dv and d initial_state;
+ * g_gamma is not differentiated, as in the lightning_attn wrapper).  With
+ * lam = exp(g_gamma[h]) and D_t the gradient reaching S_t,
+ *
+ *     D_t  = scale q_t^T dO_t + lam D_{t+1}      (d_final_state enters at the last
+ *                                                 position without decay)
+ *     dq_t = scale dO_t S_t^T,   dk_t = D_t v_t,   dv_t = k_t D_t,
+ *     d_initial_state = lam D_first,
+ *
+ * "first"/"last" in the direction of the forward pass; dk and dv of a kv head sum
+ * over its query heads.  Computed as three chunked sweeps: dq in the forward
+ * direction, dk and dv in the opposite one.
+ *   q, k, v, g_gamma, scale, initial_state, reverse, cu_seqlens: as for lattn_fwd
+ *                  (the forward inputs; initial_state may be NULL).  scale must be a
+ *                  finite normal float (the sweeps carry D / scale).
+ *   d_o            device [B, T, H, dv] in in_dtype (like q, k, v), 16-byte aligned:
+ *                  the gradient of o.  A caller holding an fp32 gradient of a bf16
+ *                  problem rounds it first; the sweeps compute on bf16 operands.
+ *   d_final_state  device float32 [N_seq, H, dk, dv] or NULL (zeros).
+ *   dq             device float32 [B, T, H, dk]   (written)
+ *   dk, dv         device float32 [B, T, Hkv, dk], [B, T, Hkv, dv]   (written)
+ *   d_initial_state device float32 [N_seq, H, dk, dv] or NULL (not computed).
+ *   workspace      device buffer of >= lattn_bwd_workspace_size(p) bytes, 16-byte
+ *                  aligned, owned by the caller; must not be shared by calls that
+ *                  overlap in time.
+ * Rows of packed input outside every sequence are unspecified in dq, dk and dv.
+ * Supported: every problem lattn_fwd supports whose transposed head dims
+ * (dk' = dv, dv' = dk) it also supports.  Returns LATTN_OK or a negative status;
+ * nothing is launched on error.
+ */
+int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* v,
+              const float* g_gamma, float scale, const float* initial_state, int reverse,
+              const int32_t* cu_seqlens, const void* d_o, const float* d_final_state, float* dq,
+              float* dk, float* dv, float* d_initial_state, void* workspace, size_t workspace_bytes,
+              void* stream);
+
+/*
  * Lightning decay schedule (lightning_attn interface page, module docstring "Key
  * innovation" and wrapper body): out_host[h] = -(8/H) * (1 - layer_idx/num_layers) * h,
  * coefficient computed in double, rounded to float32, then multiplied by the
@@ -111,7 +157,7 @@ int lattn_lightning_g_gamma(int num_heads, int layer_idx, int num_layers, float*
 /* Static description of a status code (never NULL). */
 const char* lattn_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2 (1 had no backward). */
 int lattn_abi_version(void);
 
 #ifdef __cplusplus

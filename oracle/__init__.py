@@ -140,8 +140,9 @@ class Oracle:
         """fp64 gradients of the forward recurrence.
 
         Returns (dq [.., T, H, dk], dk [.., T, Hkv, dk], dv [.., T, Hkv, dv],
-        d_initial_state [N_seq, H, dk, dv] or None).  ``d_o`` and ``d_final`` are
-        taken as float32 values.  Rows outside every packed sequence are zero.
+        d_initial_state [N_seq, H, dk, dv] or None).  ``d_o`` has the dtype of q, k, v
+        (float32 values or bf16 words); ``d_final`` is taken as float32.  Rows outside
+        every packed sequence are zero.
         """
         q = np.ascontiguousarray(q)
         k = np.ascontiguousarray(k)
@@ -158,8 +159,10 @@ class Oracle:
         dv = v.shape[3]
         if k.shape != (B, T, Hkv, dk) or v.shape != (B, T, Hkv, dv):
             raise ValueError("inconsistent q/k/v shapes")
-        do32 = np.ascontiguousarray(d_o, dtype=np.float32)
-        if do32.shape != (B, T, H, dv):
+        do_ = np.ascontiguousarray(d_o)
+        if do_.dtype != q.dtype:
+            raise TypeError("d_o must have the dtype of q, k, v")
+        if do_.shape != (B, T, H, dv):
             raise ValueError("d_o must have the shape of o")
         g = np.ascontiguousarray(g_gamma, dtype=np.float32)
         if cu_seqlens is not None:
@@ -188,7 +191,7 @@ class Oracle:
         rc = self._lib.oracle_recurrent_bwd(
             B, T, H, Hkv, dk, dv, dt, q.ctypes.data, k.ctypes.data, v.ctypes.data,
             g.ctypes.data, float(scale), init_ptr, int(bool(reverse)), cu_ptr, n_seq,
-            do32.ctypes.data, fin_ptr, dq.ctypes.data, dk_.ctypes.data, dv_.ctypes.data,
+            do_.ctypes.data, fin_ptr, dq.ctypes.data, dk_.ctypes.data, dv_.ctypes.data,
             d_init.ctypes.data if want_d_init else None)
         if rc != 0:
             raise ValueError("oracle rejected the arguments")

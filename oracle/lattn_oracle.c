@@ -188,7 +188,7 @@ int oracle_recurrent_fwd(int batch, int seqlen, int num_heads, int num_kv_heads,
  * from the last position to the first).  Under GQA, dk and dv of kv head j
  * sum the contributions of every query head that reads j.
  *
- *   d_o [B, T, H, dv] float32;  d_final [N_seq, H, dk, dv] float32 or NULL (zeros)
+ *   d_o [B, T, H, dv] in_dtype (like q, k, v);  d_final [N_seq, H, dk, dv] float32 or NULL (zeros)
  *   dq [B, T, H, dk], dk_out [B, T, Hkv, dk], dv_out [B, T, Hkv, dv] fp64 (outputs;
  *     rows outside every sequence are left untouched)
  *   d_init [N_seq, H, dk, dv] fp64 or NULL (then not computed)
@@ -201,7 +201,7 @@ int oracle_recurrent_bwd(int batch, int seqlen, int num_heads, int num_kv_heads,
                          const float* g_gamma, double scale,
                          const float* initial_state, int reverse,
                          const int64_t* cu_seqlens, int num_seqs,
-                         const float* d_o, const float* d_final,
+                         const void* d_o, const float* d_final,
                          double* dq, double* dk_out, double* dv_out, double* d_init) {
     if (batch <= 0 || seqlen < 0 || num_heads <= 0 || num_kv_heads <= 0 || dk <= 0 || dv <= 0)
         return -1;
@@ -249,7 +249,7 @@ int oracle_recurrent_bwd(int batch, int seqlen, int num_heads, int num_kv_heads,
                 const int64_t vo = (row * num_kv_heads + kvh) * dv;
                 for (int a = 0; a < dk; ++a) kt[a] = in_value(k, in_dtype, ko + a);
                 for (int c = 0; c < dv; ++c) vt[c] = in_value(v, in_dtype, vo + c);
-                for (int c = 0; c < dv; ++c) dot[c] = (double)d_o[(row * num_heads + h) * dv + c];
+                for (int c = 0; c < dv; ++c) dot[c] = in_value(d_o, in_dtype, (row * num_heads + h) * dv + c);
                 for (int a = 0; a < dk; ++a)
                     for (int c = 0; c < dv; ++c)
                         S[(int64_t)a * dv + c] = lam * S[(int64_t)a * dv + c] + kt[a] * vt[c];
@@ -270,7 +270,7 @@ int oracle_recurrent_bwd(int batch, int seqlen, int num_heads, int num_kv_heads,
                 for (int a = 0; a < dk; ++a) qt[a] = in_value(q, in_dtype, qo + a);
                 for (int a = 0; a < dk; ++a) kt[a] = in_value(k, in_dtype, ko + a);
                 for (int c = 0; c < dv; ++c) vt[c] = in_value(v, in_dtype, vo + c);
-                for (int c = 0; c < dv; ++c) dot[c] = (double)d_o[(row * num_heads + h) * dv + c];
+                for (int c = 0; c < dv; ++c) dot[c] = in_value(d_o, in_dtype, (row * num_heads + h) * dv + c);
                 const double carry = step == 0 ? 1.0 : lam; /* d_final enters undecayed */
                 for (int a = 0; a < dk; ++a)
                     for (int c = 0; c < dv; ++c)

@@ -47,6 +47,34 @@ def oracle_run(w: inputs.Workload, data: dict, reverse: bool | None = None, pair
                              cu_seqlens=data["cu_seqlens"], pairs=pairs)
 
 
+def gpu_run_bwd(w: inputs.Workload, data: dict, grads: dict, reverse: bool | None = None,
+                g_gamma=None, want_d_init: bool = True):
+    """Run the HIP backward; returns device tensors (dq, dk, dv, d_initial_state)."""
+    import torch
+
+    rev = w.reverse if reverse is None else reverse
+    q, k, v = (to_device(data[n], w.dtype) for n in ("q", "k", "v"))
+    init = to_device(data["initial_state"], "f32")
+    d_o = to_device(grads["d_o"], w.dtype)
+    d_fin = to_device(grads["d_final_state"], "f32")
+    g = g_gamma
+    if g is None:
+        g = torch.from_numpy(lattn.lattn_lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers)).cuda()
+    return lattn.recurrent_bwd(q, k, v, d_o, g_gamma=g, softmax_scale=w.scale, initial_state=init,
+                               d_final_state=d_fin, reverse=rev, cu_seqlens=data["cu_seqlens"],
+                               want_d_initial_state=want_d_init)
+
+
+def oracle_run_bwd(w: inputs.Workload, data: dict, grads: dict, reverse: bool | None = None,
+                   g_gamma=None):
+    rev = w.reverse if reverse is None else reverse
+    orc = oracle.load()
+    g = orc.lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers) if g_gamma is None else g_gamma
+    return orc.recurrent_bwd(data["q"], data["k"], data["v"], g, w.scale, grads["d_o"],
+                             grads["d_final_state"], data["initial_state"], reverse=rev,
+                             cu_seqlens=data["cu_seqlens"])
+
+
 def rel_err(got, ref) -> float:
     """max |got - ref| / RMS(ref) (0 for empty or all-zero references)."""
     got = np.asarray(got, dtype=np.float64)

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lattn.lattn_abi_version() == 1
+    assert lattn.lattn_abi_version() == 2
     for code in range(-7, 1):
         s = lattn.lattn_status_string(code)
         assert s and s != "unknown status"
@@ -115,6 +115,59 @@ def test_varlen_workspace():
     assert call(prob, cu=FAKE, ws=FAKE, ws_bytes=need - 1) == lattn.LATTN_ERR_WORKSPACE
     big = P(batch=1, seqlen=300, num_seqs=20000)  # beyond the ordering limit: no workspace
     assert lattn.lattn_fwd_workspace_size(big) == 0
+
+
+def call_bwd(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, scale=0.125, init=None, cu=None, do=FAKE,
+             dfin=None, dq=FAKE, dk=FAKE, dv=FAKE, dinit=FAKE, ws=FAKE, ws_bytes=None):
+    L = lattn.load_library()
+    if ws_bytes is None:
+        ws_bytes = lattn.lattn_bwd_workspace_size(prob)
+    return L.lattn_bwd(ctypes.byref(prob), q, k, v, g, scale, init, 0, cu, do, dfin, dq, dk, dv, dinit,
+                       ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("prob,status", [
+    (P(batch=0), lattn.LATTN_ERR_INVALID_ARG),
+    (P(num_kv_heads=3), lattn.LATTN_ERR_HEADS),
+    (P(num_seqs=3), lattn.LATTN_ERR_VARLEN_BATCH),
+    (P(head_dim_qk=48), lattn.LATTN_ERR_UNSUPPORTED),
+    # forward-supported, but the swapped dims (dk' = 48) have no kernel
+    (P(head_dim_qk=64, head_dim_v=48), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(in_dtype=lattn.LATTN_F32, head_dim_qk=64, head_dim_v=48), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(out_dtype=lattn.LATTN_BF16), lattn.LATTN_ERR_UNSUPPORTED),
+])
+def test_bwd_problem_errors(prob, status):
+    assert call_bwd(prob, ws_bytes=1 << 30) == status
+    assert lattn.lattn_bwd_workspace_size(prob) == 0
+
+
+def test_bwd_argument_errors():
+    prob = P()
+    assert call_bwd(prob, do=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_bwd(prob, dq=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_bwd(prob, dk=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_bwd(prob, g=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_bwd(prob, do=FAKE + 8) == lattn.LATTN_ERR_INVALID_ARG  # misaligned
+    assert call_bwd(prob, dfin=FAKE + 4) == lattn.LATTN_ERR_INVALID_ARG
+    for bad in (0.0, float("inf"), float("nan"), 1e-45):  # the sweeps divide by scale
+        assert call_bwd(prob, scale=bad) == lattn.LATTN_ERR_INVALID_ARG
+    gqa = P(num_kv_heads=2)
+    assert call_bwd(gqa, ws=None) == lattn.LATTN_ERR_WORKSPACE
+    need = lattn.lattn_bwd_workspace_size(gqa)
+    assert call_bwd(gqa, ws_bytes=need - 1) == lattn.LATTN_ERR_WORKSPACE
+
+
+def test_bwd_workspace_size():
+    rows = 2 * 128
+    # MHA, fixed length: nothing
+    assert lattn.lattn_bwd_workspace_size(P()) == 0
+    assert lattn.lattn_bwd_workspace_size(P(in_dtype=lattn.LATTN_F32)) == 0
+    # GQA: per-query-head gradients of the wider head dim
+    gqa = P(num_kv_heads=2, head_dim_qk=128, head_dim_v=64)
+    assert lattn.lattn_bwd_workspace_size(gqa) == rows * 8 * 128 * 4
+    # packed input adds the sequence order, 256-byte rounded
+    var = P(batch=1, seqlen=300, num_seqs=5, in_dtype=lattn.LATTN_F32)
+    assert lattn.lattn_bwd_workspace_size(var) == 256
 
 
 def test_wrapper_value_errors():
