@@ -8,7 +8,9 @@ A step is one lattn_fwd call over the whole batch with inputs already in HBM.
 Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
   roofline      achieved HBM GB/s of the forward kernel (algorithmic bytes / mean
                 kernel time from HIP events on the launch stream) against 8 TB/s,
-  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload.
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload,
+  backward      the same for lattn_bwd on the same inputs (bf16 d_o), with its own
+                roofline and oracle baseline (skipped with --no-bwd).
 """
 from __future__ import annotations
 
@@ -27,6 +29,7 @@ HBM_PEAK_GBS = 8000.0
 # Lightning2 forward at B4 H32 d128 bf16 n=32768 from the OpenNLPLab lightning-attention
 # README benchmark table (hardware unstated, time read as milliseconds): 17.661427 ms.
 PAGE_LIGHTNING2_MS = 17.661427
+PAGE_LIGHTNING2_BWD_MS = 74.594788  # same table's backward row at n = 32768
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_b4_h32_d128_n32768.json")
 KERNEL_SRC = os.path.join(ROOT, "decayed_recurrent_attention_amd", "csrc", "lattn_kernels.hip")
 
@@ -122,6 +125,84 @@ def device_bandwidth(torch, dev, gib=2, reps=5):
     return f"device copy {gib} GiB: {res['copy']:.0f} GB/s (read + write), fill: {res['fill']:.0f} GB/s"
 
 
+def time_calls(torch, fn, stream, warmup, steps):
+    """Run fn warmup times, then time `steps` calls; returns (wall ms per call, event ms list).
+    The events bracket each call on the launch stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return 1000.0 * wall / steps, [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def bwd_algorithmic_bytes(B, T, H, Hkv, dk, dv, in_bytes):
+    """Bytes the backward must move at least once: q, k, v and dO in (input dtype); dq, dk,
+    dv (fp32) and d_initial_state (fp32) out."""
+    ins = B * T * (H * dk + Hkv * dk + Hkv * dv + H * dv) * in_bytes
+    outs = B * T * (H * dk + Hkv * dk + Hkv * dv) * 4
+    return ins + outs + B * H * dk * dv * 4
+
+
+def cpu_baseline_bwd(w, data, grads, target_s=10.0):
+    """Time the oracle's backward on the first (batch row, head) pairs of the workload
+    (row-major), about target_s of CPU work; heads of one row run as one call."""
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.load()
+    threads = orc.set_threads(0)
+    B, H = w.batch, w.num_heads
+    assert w.num_kv_heads == H, "the sample slices heads, which needs one kv head per head"
+    g = orc.lightning_g_gamma(H, w.layer_idx, w.num_layers)
+    rows = {}
+
+    def sliced(b):
+        if b not in rows:
+            rows[b] = [np.ascontiguousarray(a[b:b + 1]) for a in (data["q"], data["k"], data["v"], grads["d_o"])]
+        return rows[b]
+
+    def timed(n):
+        dt = 0.0
+        for b in range(B):
+            nh = min(H, n - b * H)
+            if nh <= 0:
+                break
+            q, k, v, do = (np.ascontiguousarray(a[:, :, :nh]) for a in sliced(b))
+            t0 = time.perf_counter()
+            orc.recurrent_bwd(q, k, v, g[:nh], w.scale, do, want_d_init=True)
+            dt += time.perf_counter() - t0
+        return dt
+
+    total = B * H
+    n = min(total, threads)
+    timed(1)  # untimed warm-up
+    dt = timed(n)
+    while dt < target_s / 4 and n < total:
+        n = min(total, 4 * n)
+        dt = timed(n)
+    if dt < target_s and n < total:
+        n = min(total, int(n * target_s / dt))
+        dt = timed(n)
+    return {
+        "value": B * w.seqlen * (n / total) / dt,
+        "unit": "tokens/s",
+        "cores": min(threads, n),
+        "kind": "oracle",
+        "sample": f"backward of {n} of {total} (batch row, head) pairs over all {w.seqlen} tokens, "
+                  f"fp64, {dt:.1f} s in the oracle; tokens/s scaled by the pair fraction",
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,6 +210,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seqlen", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for traffic)")
     ap.add_argument("--bandwidth", action="store_true",
@@ -164,27 +246,44 @@ def main():
         if rc != lattn.LATTN_OK:
             raise lattn.LattnError(rc)
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
-        step()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kernel_ms = [e0.elapsed_time(e1) for e0, e1 in ev]
-    ms_per_step = 1000.0 * wall / args.steps
+    print("[bench] forward", file=sys.stderr, flush=True)
+    ms_per_step, kernel_ms = time_calls(torch, step, stream, args.warmup, args.steps)
     mean_kernel_ms = sum(kernel_ms) / len(kernel_ms)
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel mean "
           f"{mean_kernel_ms:.4f} ms min {min(kernel_ms):.4f} max {max(kernel_ms):.4f}",
           file=sys.stderr, flush=True)
+
+    bwd = None
+    if not args.no_bwd:
+        grads = w.make_grads(final_std=None)
+        d_o = to_dev(grads["d_o"])
+        dq = torch.empty((B, T, H, dk), device=dev, dtype=torch.float32)
+        dkk = torch.empty((B, T, Hkv, dk), device=dev, dtype=torch.float32)
+        dvv = torch.empty((B, T, Hkv, dv), device=dev, dtype=torch.float32)
+        dinit = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+        ws_bytes = lattn.lattn_bwd_workspace_size(prob)
+        ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
+
+        def bstep():
+            rc = lattn.lattn_bwd(prob, q, k, v, g, w.scale, None, False, None, d_o, None, dq, dkk, dvv,
+                                 dinit, ws, stream=stream.cuda_stream)
+            if rc != lattn.LATTN_OK:
+                raise lattn.LattnError(rc)
+
+        print("[bench] backward", file=sys.stderr, flush=True)
+        b_wall, b_ms = time_calls(torch, bstep, stream, args.warmup, args.steps)
+        b_mean = sum(b_ms) / len(b_ms)
+        b_alg = bwd_algorithmic_bytes(B, T, H, Hkv, dk, dv, 2)
+        b_ach = b_alg / (b_mean * 1e-3) / 1e9
+        print(f"[bench] backward {args.steps} steps: {b_wall:.4f} ms/step wall, mean {b_mean:.4f} ms",
+              file=sys.stderr, flush=True)
+        bwd = {"ms_per_step": b_wall, "tokens_per_s": B * T / (b_wall * 1e-3),
+               "roofline": {"bound": "hbm", "achieved": b_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": b_ach / HBM_PEAK_GBS, "algorithmic_bytes": b_alg, "call_ms": b_mean},
+               "inputs": "q, k, v, d_o bf16; no initial state, no final-state gradient; "
+                         "d_initial_state computed",
+               "page_lightning2_bwd_ms": PAGE_LIGHTNING2_BWD_MS if T == 32768 else None}
+        del dq, dkk, dvv, d_o
 
     if args.copy_probe:
         src = torch.empty(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
@@ -226,6 +325,11 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(w, data)
+        if bwd is not None:
+            print("[bench] cpu baseline of the backward (oracle)", file=sys.stderr, flush=True)
+            bwd["cpu_baseline"] = cpu_baseline_bwd(w, data, grads)
+    if bwd is not None:
+        line["backward"] = bwd
     print(json.dumps(line), flush=True)
 
 
