@@ -10,7 +10,9 @@ Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
                 kernel time from HIP events on the launch stream) against 8 TB/s,
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload,
   backward      the same for lattn_bwd on the same inputs (bf16 d_o), with its own
-                roofline and oracle baseline (skipped with --no-bwd).
+                roofline and oracle baseline (skipped with --no-bwd),
+  decode        one decoding step (lattn_decode) over --decode-batch sequences of the
+                same head shape, state updated in place.
 """
 from __future__ import annotations
 
@@ -203,6 +205,27 @@ def cpu_baseline_bwd(w, data, grads, target_s=10.0):
     }
 
 
+def cpu_baseline_decode(w, data, target_s=5.0):
+    """Time the oracle on the decoding step (the recurrence at seqlen 1 from the state),
+    repeated until about target_s."""
+    import oracle
+
+    orc = oracle.load()
+    threads = orc.set_threads(0)
+    g = orc.lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers)
+    args = (data["q"], data["k"], data["v"], g, w.scale)
+    orc.recurrent_fwd(*args, initial_state=data["initial_state"])  # untimed warm-up
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < target_s and reps < 1000:
+        orc.recurrent_fwd(*args, initial_state=data["initial_state"])
+        reps += 1
+    dt = time.perf_counter() - t0
+    return {"value": w.batch * reps / dt, "unit": "tokens/s", "cores": min(threads, w.batch * w.num_heads),
+            "kind": "oracle",
+            "sample": f"the whole decoding step ({w.batch} sequences) x {reps}, fp64, {dt:.1f} s wall"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -211,6 +234,8 @@ def main():
     ap.add_argument("--seqlen", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--decode-batch", type=int, default=128,
+                    help="sequences per decoding step in the decode measurement (0 skips it)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for traffic)")
     ap.add_argument("--bandwidth", action="store_true",
@@ -285,6 +310,38 @@ def main():
                "page_lightning2_bwd_ms": PAGE_LIGHTNING2_BWD_MS if T == 32768 else None}
         del dq, dkk, dvv, d_o
 
+    dec = None
+    if args.decode_batch > 0:
+        Bd = args.decode_batch
+        wd = inputs.Workload("decode", Bd, 1, H, Hkv, dk, dv, "bf16", w.layer_idx, w.num_layers,
+                             init_std=0.5, seed=3)
+        dd = wd.make()
+        dq_, dk_, dv_ = (to_dev(dd[n])[:, 0].contiguous() for n in ("q", "k", "v"))
+        state = torch.from_numpy(dd["initial_state"]).to(dev)
+        o_dec = torch.empty((Bd, H, dv), device=dev, dtype=torch.float32)
+        dprob = lattn.LattnProblem(Bd, 1, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
+
+        def dstep():
+            rc = lattn.lattn_decode(dprob, dq_, dk_, dv_, g, w.scale, state, state, o_dec,
+                                    stream=stream.cuda_stream)
+            if rc != lattn.LATTN_OK:
+                raise lattn.LattnError(rc)
+
+        print("[bench] decode", file=sys.stderr, flush=True)
+        d_wall, d_ms = time_calls(torch, dstep, stream, args.warmup, args.steps)
+        d_mean = sum(d_ms) / len(d_ms)
+        d_alg = 2 * Bd * H * dk * dv * 4 + Bd * (H * dk + Hkv * dk + Hkv * dv) * 2 + Bd * H * dv * 4
+        d_ach = d_alg / (d_mean * 1e-3) / 1e9
+        print(f"[bench] decode {args.steps} steps: {d_wall:.4f} ms/step wall, mean {d_mean:.4f} ms",
+              file=sys.stderr, flush=True)
+        dec = {"batch": Bd, "ms_per_step": d_wall, "tokens_per_s": Bd / (d_wall * 1e-3),
+               "roofline": {"bound": "hbm", "achieved": d_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": d_ach / HBM_PEAK_GBS, "algorithmic_bytes": d_alg, "call_ms": d_mean},
+               "inputs": f"{Bd} sequences x H{H} d{dk}: q, k, v bf16, fp32 state updated in place"}
+        if not args.no_cpu_baseline:
+            dec["cpu_baseline"] = cpu_baseline_decode(wd, dd)
+        del state, o_dec
+
     if args.copy_probe:
         src = torch.empty(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
         dst = torch.empty_like(src)
@@ -330,6 +387,8 @@ def main():
             bwd["cpu_baseline"] = cpu_baseline_bwd(w, data, grads)
     if bwd is not None:
         line["backward"] = bwd
+    if dec is not None:
+        line["decode"] = dec
     print(json.dumps(line), flush=True)
 
 

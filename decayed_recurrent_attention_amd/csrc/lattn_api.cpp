@@ -142,7 +142,7 @@ BwdLayout bwd_layout(const lattn_problem& p) {
 
 extern "C" {
 
-int lattn_abi_version(void) { return 2; }
+int lattn_abi_version(void) { return 3; }
 
 const char* lattn_status_string(int status) {
     switch (status) {
@@ -315,6 +315,45 @@ int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* 
         return LATTN_ERR_LAUNCH;
     if (lattn::launch_fwd(pv, p->in_dtype, nw_v, !rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
     if (grouped && lattn::launch_group_sum(part, dv, tokens, p->num_heads, p->num_kv_heads, dvd, s) != hipSuccess)
+        return LATTN_ERR_LAUNCH;
+    return LATTN_OK;
+}
+
+int lattn_decode(const lattn_problem* p, const void* q, const void* k, const void* v, const float* g_gamma,
+                 float scale, const float* state_in, float* state_out, void* o, void* stream) {
+    if (p == nullptr) return LATTN_ERR_INVALID_ARG;
+    if (p->batch < 1 || p->seqlen != 1 || p->num_seqs != 0 || p->num_heads < 1 || p->num_kv_heads < 1 ||
+        p->head_dim_qk < 1 || p->head_dim_v < 1)
+        return LATTN_ERR_INVALID_ARG;
+    if (p->num_heads % p->num_kv_heads != 0) return LATTN_ERR_HEADS;
+    if (p->in_dtype != LATTN_BF16 && p->in_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
+    if (p->out_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
+    if (p->head_dim_qk % 16 != 0 || p->head_dim_qk > 256 || p->head_dim_v % 16 != 0 || p->head_dim_v > 256)
+        return LATTN_ERR_UNSUPPORTED;
+    if (q == nullptr || k == nullptr || v == nullptr || g_gamma == nullptr || state_out == nullptr || o == nullptr)
+        return LATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g_gamma, 4) || !aligned(state_in, 16) ||
+        !aligned(state_out, 16) || !aligned(o, 16))
+        return LATTN_ERR_INVALID_ARG;
+    const int64_t blocks = (int64_t)p->batch * p->num_heads * (p->head_dim_v / lattn::decode_block(p->head_dim_v));
+    if (blocks > INT_MAX) return LATTN_ERR_INVALID_ARG;
+    lattn::DecodeParams dp;
+    dp.q = q;
+    dp.k = k;
+    dp.v = v;
+    dp.g_gamma = g_gamma;
+    dp.state_in = state_in;
+    dp.state_out = state_out;
+    dp.o = static_cast<float*>(o);
+    dp.batch = p->batch;
+    dp.num_heads = p->num_heads;
+    dp.num_kv_heads = p->num_kv_heads;
+    dp.dk = p->head_dim_qk;
+    dp.dv = p->head_dim_v;
+    dp.scale = scale;
+    const int dc = device_check();
+    if (dc != LATTN_OK) return dc;
+    if (lattn::launch_decode(dp, p->in_dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
         return LATTN_ERR_LAUNCH;
     return LATTN_OK;
 }

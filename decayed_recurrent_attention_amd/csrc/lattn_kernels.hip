@@ -874,6 +874,71 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// Decoding step: state <- lam * state + k^T v, o = scale * q state, for one new
+// token per sequence.  The state is streamed once (read, updated, written back),
+// so the kernel is bound by HBM: a workgroup owns the state block of one
+// (sequence, head, BV columns); thread t updates column quad t % (BV/4) of rows
+// t / (BV/4) + i * RG, each row a coalesced run of BV floats, and accumulates its
+// share of q state; the row groups are then summed in LDS.
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ inline float in_elem(const void* base, int64_t i) {
+    if constexpr (BF16) return bf16_lo((uint32_t) static_cast<const uint16_t*>(base)[i]);
+    else return static_cast<const float*>(base)[i];
+}
+
+template <int BV, bool BF16>
+__global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
+    constexpr int TPR = BV / 4;      // threads per state row (one float4 each)
+    constexpr int RG = 256 / TPR;    // rows handled per pass of the workgroup
+    constexpr int MAXR = (256 + RG - 1) / RG;  // passes for the widest head (dk = 256)
+    __shared__ f32x4 red[256];
+    const int tid = threadIdx.x, cq = tid % TPR, rg = tid / TPR;
+    const int H = p.num_heads, dk = p.dk, dv = p.dv;
+    const int nvb = dv / BV;
+    const int64_t nh = blockIdx.x / nvb;  // n * H + h
+    const int vb = blockIdx.x % nvb;
+    const int h = (int)(nh % H);
+    const int64_t n = nh / H;
+    const int kvh = h / (H / p.num_kv_heads);
+    const int c = vb * BV + 4 * cq;
+    const float lam = exp2f(p.g_gamma[h] * kLog2e);
+    const int64_t kvrow = n * p.num_kv_heads + kvh;
+    f32x4 vq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) vq[e] = in_elem<BF16>(p.v, kvrow * dv + c + e);
+
+    const int64_t blk = nh * dk * dv + c;
+    f32x4 s[MAXR];
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {  // all loads first: MAXR independent 16-byte reads in flight
+        const int r = rg + i * RG;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        s[i] = (r < dk && p.state_in) ? *reinterpret_cast<const f32x4*>(p.state_in + blk + (int64_t)r * dv) : z;
+    }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < MAXR; ++i) {
+        const int r = rg + i * RG;
+        if (r < dk) {
+            const float kr = in_elem<BF16>(p.k, kvrow * dk + r);
+            const float qr = in_elem<BF16>(p.q, nh * dk + r);
+            const f32x4 u = lam * s[i] + kr * vq;
+            *reinterpret_cast<f32x4*>(p.state_out + blk + (int64_t)r * dv) = u;
+            acc += qr * u;
+        }
+    }
+    red[tid] = acc;
+    __syncthreads();
+#pragma unroll
+    for (int stride = RG / 2; stride > 0; stride /= 2) {
+        if (rg < stride) red[tid] += red[tid + stride * TPR];
+        __syncthreads();
+    }
+    if (rg == 0) *reinterpret_cast<f32x4*>(p.o + nh * dv + c) = p.scale * red[cq];
+}
+
+// ---------------------------------------------------------------------------
 // Longest-first order of packed sequences (ties by index): order[rank] = sequence.
 // Lengths are clamped exactly as decode_work clamps them.
 // ---------------------------------------------------------------------------
@@ -1010,6 +1075,29 @@ hipError_t launch_group_sum(const float* part, float* out, int64_t rows, int H, 
     if (n4 == 0) return hipSuccess;
     hipLaunchKernelGGL(group_sum_kernel, dim3(stream_blocks(n4)), dim3(256), 0, s, part, out, n4, H / Hkv, d / 4);
     return hipGetLastError();
+}
+
+int decode_block(int dv) { return dv % 64 == 0 ? 64 : dv % 32 == 0 ? 32 : 16; }
+
+namespace {
+template <int BV>
+hipError_t launch_decode_bv(const DecodeParams& p, int in_dtype, hipStream_t s) {
+    const int64_t blocks = (int64_t)p.batch * p.num_heads * (p.dv / BV);
+    if (blocks == 0) return hipSuccess;
+    if (in_dtype == 0)
+        hipLaunchKernelGGL((decode_kernel<BV, true>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<BV, false>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, int in_dtype, hipStream_t s) {
+    switch (decode_block(p.dv)) {
+        case 64: return launch_decode_bv<64>(p, in_dtype, s);
+        case 32: return launch_decode_bv<32>(p, in_dtype, s);
+        default: return launch_decode_bv<16>(p, in_dtype, s);
+    }
 }
 
 hipError_t launch_seq_order(const int32_t* cu, int num_seqs, int seqlen, int32_t* order, hipStream_t s) {

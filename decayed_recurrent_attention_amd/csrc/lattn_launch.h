@@ -72,6 +72,26 @@ hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hi
 // with G = H / Hkv and d a multiple of 4.
 hipError_t launch_group_sum(const float* part, float* out, int64_t rows, int H, int Hkv, int d,
                             hipStream_t stream);
+// One decoding step over a batch of states (one new token per sequence).
+struct DecodeParams {
+    const void* q;         // [B, H, dk]   (in_dtype)
+    const void* k;         // [B, Hkv, dk]
+    const void* v;         // [B, Hkv, dv]
+    const float* g_gamma;  // [H]
+    const float* state_in; // [B, H, dk, dv] or nullptr (zeros); may equal state_out
+    float* state_out;      // [B, H, dk, dv]
+    float* o;              // [B, H, dv]
+    int batch;
+    int num_heads;
+    int num_kv_heads;
+    int dk;                // multiple of 16, at most 256
+    int dv;                // multiple of 16, at most 256
+    float scale;
+};
+// Value-block width (16, 32 or 64 columns) the decode kernel uses for dv.
+int decode_block(int dv);
+hipError_t launch_decode(const DecodeParams& p, int in_dtype, hipStream_t stream);
+
 // Enqueue the longest-first ordering of packed sequences into `order`.
 hipError_t launch_seq_order(const int32_t* cu, int num_seqs, int seqlen, int32_t* order,
                             hipStream_t stream);

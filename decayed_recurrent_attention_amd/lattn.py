@@ -34,7 +34,7 @@ LATTN_ERR_DEVICE = -7
 
 # Every function declared in include/lattn.h.
 EXPORTS = ("lattn_fwd", "lattn_fwd_workspace_size", "lattn_bwd", "lattn_bwd_workspace_size",
-           "lattn_lightning_g_gamma", "lattn_status_string", "lattn_abi_version")
+           "lattn_decode", "lattn_lightning_g_gamma", "lattn_status_string", "lattn_abi_version")
 
 
 class LattnProblem(ctypes.Structure):
@@ -74,6 +74,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
             lib.lattn_bwd_workspace_size.restype = ctypes.c_size_t
             lib.lattn_bwd_workspace_size.argtypes = [P]
+            lib.lattn_decode.restype = ctypes.c_int
+            lib.lattn_decode.argtypes = [P, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
             lib.lattn_lightning_g_gamma.restype = ctypes.c_int
             lib.lattn_lightning_g_gamma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
             lib.lattn_status_string.restype = ctypes.c_char_p
@@ -142,6 +144,18 @@ def lattn_bwd(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_sta
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g_gamma), float(scale),
         _ptr(initial_state), int(bool(reverse)), _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_initial_state), _ptr(workspace), ws_bytes, stream))
+
+
+def lattn_decode(problem: LattnProblem, q, k, v, g_gamma, scale: float, state_in, state_out, o,
+                 stream=None) -> int:
+    """Raw call: tensors (or None) are passed by address; returns the status code."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().lattn_decode(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g_gamma), float(scale), _ptr(state_in),
+        _ptr(state_out), _ptr(o), stream))
 
 
 # -- tensor-level forward and backward ----------------------------------------------
@@ -320,3 +334,47 @@ def lightning_attn_bwd(query, key, value, d_o, layer_idx: int, num_layers: int, 
     return recurrent_bwd(query, key, value, d_o, g_gamma=g, softmax_scale=softmax_scale,
                          initial_state=initial_state, d_final_state=d_final_state, reverse=reverse,
                          cu_seqlens=cu_seqlens)
+
+
+def decode_step(query, key, value, state, g_gamma=None, softmax_scale=None, in_place=True):
+    """One decoding step: q, k, v of one new token per sequence ([B, H|Hkv, d] or
+    [B, 1, H|Hkv, d]) and the float32 state [B, H, dk, dv] (None for zeros).
+
+    Returns (o float32 [B, H, dv] (or [B, 1, H, dv]), new state).  With ``in_place``
+    the new state overwrites ``state``.
+    """
+    import torch
+
+    unsq = query.dim() == 4
+    if unsq:
+        if query.shape[1] != 1:
+            raise ValueError("decode_step takes one token per sequence")
+        query, key, value = query[:, 0], key[:, 0], value[:, 0]
+    if query.dim() != 3 or key.dim() != 3 or value.dim() != 3:
+        raise ValueError("query, key and value must be [batch, heads, dim]")
+    B, H, dk = query.shape
+    Hkv, dv = key.shape[1], value.shape[2]
+    if key.shape != (B, Hkv, dk) or value.shape != (B, Hkv, dv):
+        raise ValueError("inconsistent q/k/v shapes")
+    if not (query.dtype == key.dtype == value.dtype):
+        raise TypeError("query, key and value must share one dtype")
+    dev = query.device
+    if dev.type != "cuda":
+        raise ValueError("inputs must be GPU tensors")
+    if softmax_scale is None:
+        softmax_scale = float(np.float32(dk ** -0.5))
+    if g_gamma is None:
+        g_gamma = torch.zeros(H, device=dev, dtype=torch.float32)
+    g_gamma = torch.as_tensor(g_gamma).to(device=dev, dtype=torch.float32).contiguous()
+    if state is not None:
+        if state.shape != (B, H, dk, dv) or state.dtype != torch.float32 or not state.is_contiguous():
+            raise ValueError(f"state must be a contiguous float32 tensor of shape {(B, H, dk, dv)}")
+    out_state = state if (in_place and state is not None) else torch.empty(
+        (B, H, dk, dv), device=dev, dtype=torch.float32)
+    q, k, v = query.contiguous(), key.contiguous(), value.contiguous()
+    o = torch.empty((B, H, dv), device=dev, dtype=torch.float32)
+    prob = LattnProblem(B, 1, H, Hkv, dk, dv, 0, _dtype_code(q), LATTN_F32)
+    rc = lattn_decode(prob, q, k, v, g_gamma, softmax_scale, state, out_state, o)
+    if rc != LATTN_OK:
+        raise LattnError(rc)
+    return (o.unsqueeze(1) if unsq else o), out_state

@@ -145,6 +145,26 @@ int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* 
               void* stream);
 
 /*
+ * One decoding step for a batch of sequences: the recurrence of lattn_fwd advanced
+ * by one new token per sequence (the GLA interface page notes that the recurrent
+ * form suits autoregressive decoding).  For every batch row n and query head h,
+ *
+ *     state[n, h] <- lam * state[n, h] + k_n^T v_n,    o[n, h] = scale * (q_n state[n, h]),
+ *
+ * i.e. lattn_fwd with seqlen 1, initial_state = state_in and final_state = state_out.
+ *   p              seqlen must be 1 and num_seqs 0; batch = number of sequences; dk and
+ *                  dv multiples of 16 up to 256; in_dtype BF16 or F32; out_dtype F32.
+ *   q, k, v        device [B, 1, H|Hkv, dk|dv] in in_dtype, 16-byte aligned.
+ *   state_in       device float32 [B, H, dk, dv], or NULL for zeros (a first token).
+ *   state_out      device float32 [B, H, dk, dv]; may be state_in (update in place).
+ *   o              device float32 [B, 1, H, dv].
+ * Returns LATTN_OK or a negative status; nothing is launched on error.
+ */
+int lattn_decode(const lattn_problem* p, const void* q, const void* k, const void* v,
+                 const float* g_gamma, float scale, const float* state_in, float* state_out, void* o,
+                 void* stream);
+
+/*
  * Lightning decay schedule (lightning_attn interface page, module docstring "Key
  * innovation" and wrapper body): out_host[h] = -(8/H) * (1 - layer_idx/num_layers) * h,
  * coefficient computed in double, rounded to float32, then multiplied by the
@@ -157,7 +177,7 @@ int lattn_lightning_g_gamma(int num_heads, int layer_idx, int num_layers, float*
 /* Static description of a status code (never NULL). */
 const char* lattn_status_string(int status);
 
-/* ABI version of this header: 2 (1 had no backward). */
+/* ABI version of this header: 3 (1 had no backward, 2 no decoding step). */
 int lattn_abi_version(void);
 
 #ifdef __cplusplus

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lattn.lattn_abi_version() == 2
+    assert lattn.lattn_abi_version() == 3
     for code in range(-7, 1):
         s = lattn.lattn_status_string(code)
         assert s and s != "unknown status"
@@ -168,6 +168,32 @@ def test_bwd_workspace_size():
     # packed input adds the sequence order, 256-byte rounded
     var = P(batch=1, seqlen=300, num_seqs=5, in_dtype=lattn.LATTN_F32)
     assert lattn.lattn_bwd_workspace_size(var) == 256
+
+
+def call_decode(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, s_in=FAKE, s_out=FAKE, o=FAKE):
+    L = lattn.load_library()
+    return L.lattn_decode(ctypes.byref(prob), q, k, v, g, 0.125, s_in, s_out, o, None)
+
+
+@pytest.mark.parametrize("prob,status", [
+    (P(seqlen=2), lattn.LATTN_ERR_INVALID_ARG),  # one token per step
+    (P(seqlen=1, num_seqs=2, batch=1), lattn.LATTN_ERR_INVALID_ARG),  # no packed input
+    (P(seqlen=1, batch=0), lattn.LATTN_ERR_INVALID_ARG),
+    (P(seqlen=1, num_kv_heads=3), lattn.LATTN_ERR_HEADS),
+    (P(seqlen=1, head_dim_qk=40), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(seqlen=1, head_dim_v=272), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(seqlen=1, in_dtype=5), lattn.LATTN_ERR_UNSUPPORTED),
+])
+def test_decode_problem_errors(prob, status):
+    assert call_decode(prob) == status
+
+
+def test_decode_pointer_errors():
+    prob = P(seqlen=1)
+    assert call_decode(prob, q=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_decode(prob, s_out=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_decode(prob, o=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_decode(prob, s_in=FAKE + 8) == lattn.LATTN_ERR_INVALID_ARG
 
 
 def test_wrapper_value_errors():
