@@ -12,7 +12,9 @@ Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
   backward      the same for lattn_bwd on the same inputs (bf16 d_o), with its own
                 roofline and oracle baseline (skipped with --no-bwd),
   decode        one decoding step (lattn_decode) over --decode-batch sequences of the
-                same head shape, state updated in place.
+                same head shape, state updated in place,
+  split         the forward at B1 H8 (same head dims and N), where the rows are split
+                along the sequence, against the same call unsplit.
 """
 from __future__ import annotations
 
@@ -234,6 +236,8 @@ def main():
     ap.add_argument("--seqlen", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-split", action="store_true",
+                    help="skip the intra-sequence split measurement (B1 H8, same head dims and N)")
     ap.add_argument("--decode-batch", type=int, default=128,
                     help="sequences per decoding step in the decode measurement (0 skips it)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -309,6 +313,48 @@ def main():
                          "d_initial_state computed",
                "page_lightning2_bwd_ms": PAGE_LIGHTNING2_BWD_MS if T == 32768 else None}
         del dq, dkk, dvv, d_o
+
+    split = None
+    if not args.no_split:
+        # One batch row and 8 heads: 32 workgroups unsplit, so the forward cuts each row
+        # into segments chained through their states.
+        Hs = 8
+        ws_ = inputs.Workload("split", 1, T, Hs, Hs, dk, dv, "bf16", w.layer_idx, w.num_layers, seed=5)
+        sd = ws_.make()
+        sq, sk, sv = (to_dev(sd[n]) for n in ("q", "k", "v"))
+        gs = torch.from_numpy(lattn.lattn_lightning_g_gamma(Hs, w.layer_idx, w.num_layers)).to(dev)
+        so = torch.empty((1, T, Hs, dv), device=dev, dtype=torch.float32)
+        sfs = torch.empty((1, Hs, dk, dv), device=dev, dtype=torch.float32)
+        sprob = lattn.LattnProblem(1, T, Hs, Hs, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
+        res = {}
+        for mode in ("split", "unsplit"):
+            if mode == "unsplit":
+                os.environ["LATTN_SPLIT"] = "0"
+            nbytes = lattn.lattn_fwd_workspace_size(sprob)
+            sws = torch.empty(nbytes, device=dev, dtype=torch.uint8) if nbytes else None
+
+            def sstep():
+                rc = lattn.lattn_fwd(sprob, sq, sk, sv, gs, ws_.scale, None, False, None, so, sfs, sws,
+                                     stream=stream.cuda_stream)
+                if rc != lattn.LATTN_OK:
+                    raise lattn.LattnError(rc)
+
+            wall_ms, ev_ms = time_calls(torch, sstep, stream, args.warmup, args.steps)
+            res[mode] = (wall_ms, sum(ev_ms) / len(ev_ms), nbytes)
+            os.environ.pop("LATTN_SPLIT", None)
+        s_alg = algorithmic_bytes(1, T, Hs, Hs, dk, dv, 2)
+        s_ach = s_alg / (res["split"][1] * 1e-3) / 1e9
+        print(f"[bench] split B1 H{Hs}: {res['split'][1]:.4f} ms split, {res['unsplit'][1]:.4f} ms unsplit",
+              file=sys.stderr, flush=True)
+        split = {"workload": f"B1 H{Hs} d{dk} N{T} bf16, no initial state",
+                 "ms_per_step": res["split"][0], "tokens_per_s": T / (res["split"][0] * 1e-3),
+                 "unsplit_ms_per_step": res["unsplit"][0],
+                 "speedup": res["unsplit"][1] / res["split"][1],
+                 "workspace_bytes": res["split"][2],
+                 "roofline": {"bound": "hbm", "achieved": s_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": s_ach / HBM_PEAK_GBS, "algorithmic_bytes": s_alg,
+                              "call_ms": res["split"][1]}}
+        del sq, sk, sv, so
 
     dec = None
     if args.decode_batch > 0:
@@ -389,6 +435,8 @@ def main():
         line["backward"] = bwd
     if dec is not None:
         line["decode"] = dec
+    if split is not None:
+        line["split"] = split
     print(json.dumps(line), flush=True)
 
 

@@ -92,7 +92,7 @@ size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // (dk, dv) of its operands (the forward's, or swapped for a gradient sweep).
 // Returns false when the grid would not fit an int.
 bool make_params(const lattn_problem& p, int dk, int dv, int nw, const float* g_gamma, float scale,
-                 const int32_t* cu, const int32_t* order, lattn::FwdParams& fp) {
+                 const int32_t* cu, const int32_t* order, lattn::FwdParams& fp, int num_seqs = -1) {
     fp = lattn::FwdParams{};
     fp.g_gamma = g_gamma;
     fp.cu = cu;
@@ -103,7 +103,7 @@ bool make_params(const lattn_problem& p, int dk, int dv, int nw, const float* g_
     fp.num_kv_heads = p.num_kv_heads;
     fp.dk = dk;
     fp.dv = dv;
-    fp.num_seqs = num_seqs_of(p);
+    fp.num_seqs = num_seqs < 0 ? num_seqs_of(p) : num_seqs;
     fp.nvb = dv / (16 * nw);
     if ((int64_t)fp.num_seqs * p.num_kv_heads > INT_MAX) return false;
     fp.num_groups = fp.num_seqs * p.num_kv_heads;
@@ -116,6 +116,59 @@ bool make_params(const lattn_problem& p, int dk, int dv, int nw, const float* g_
 }
 
 int64_t heads_of(const lattn_problem& p) { return (int64_t)num_seqs_of(p) * p.num_heads; }
+
+// Intra-sequence split of a fixed-length bf16 forward: each batch row is cut into P
+// segments of seg_len tokens (a multiple of the chunk) that run as independent
+// sequences, so that few (row, head) pairs still fill the GPU.  A state-only pass
+// gives every segment's own state contribution, a scan chains them into the state
+// entering each segment, and the main pass runs every segment from that state.
+struct Split {
+    int P = 0;
+    int seg_len = 0;
+};
+
+Split choose_split(const lattn_problem& p, int nw) {
+    Split sp;
+    if (is_varlen(p) || p.in_dtype != LATTN_BF16 || p.seqlen < 2 * lattn::kChunk) return sp;
+    if ((int64_t)p.batch * p.num_heads > 65535) return sp;  // the scan's grid rows
+    const int64_t wgs = (int64_t)p.batch * p.num_heads * (p.head_dim_v / (16 * nw));
+    int want;
+    if (const char* env = std::getenv("LATTN_SPLIT")) {  // forced segment count (tests)
+        want = std::atoi(env);
+        if (want < 2) return sp;
+    } else {
+        if (wgs >= 128) return sp;  // at least half the compute units busy already
+        want = (int)((256 + wgs - 1) / wgs);
+        const int cap = p.seqlen / (16 * lattn::kChunk);  // segments of at least 16 chunks
+        if (want > cap) want = cap;
+        if (want < 2) return sp;
+    }
+    const int chunks = (p.seqlen + lattn::kChunk - 1) / lattn::kChunk;
+    if (want > chunks) want = chunks;
+    sp.seg_len = ((chunks + want - 1) / want) * lattn::kChunk;
+    sp.P = (p.seqlen + sp.seg_len - 1) / sp.seg_len;
+    if (sp.P < 2) sp = Split{};
+    return sp;
+}
+
+// Width and split of a forward launch: a split run uses the widest workgroups (most
+// waves per compute unit) and makes up the count with segments.
+int widest_nw(int in_dtype, int dk, int dv) {
+    for (int nw : {4, 2, 1})
+        if ((dv / 16) % nw == 0 && lattn::have_fwd_kernel(in_dtype, dk, nw)) return nw;
+    return 0;
+}
+
+Split plan_forward(const lattn_problem& p, int& nw) {
+    const int wide = widest_nw(p.in_dtype, p.head_dim_qk, p.head_dim_v);
+    const Split sp = is_varlen(p) ? Split{} : choose_split(p, wide);
+    nw = sp.P > 0 ? wide : choose_nw(p.in_dtype, p.head_dim_qk, p.head_dim_v, heads_of(p));
+    return sp;
+}
+
+size_t split_state_bytes(const lattn_problem& p, const Split& sp) {
+    return round_up((size_t)p.batch * sp.P * p.num_heads * p.head_dim_qk * p.head_dim_v * sizeof(float), 256);
+}
 
 // Byte offsets of the backward workspace regions (each 256-byte aligned).
 struct BwdLayout {
@@ -159,7 +212,12 @@ const char* lattn_status_string(int status) {
 }
 
 size_t lattn_fwd_workspace_size(const lattn_problem* p) {
-    if (p == nullptr || check_problem(*p) != LATTN_OK || !is_varlen(*p)) return 0;
+    if (p == nullptr || check_problem(*p) != LATTN_OK) return 0;
+    if (!is_varlen(*p)) {
+        int nw = 0;
+        const Split sp = plan_forward(*p, nw);
+        return sp.P > 0 ? 2 * split_state_bytes(*p, sp) : 0;
+    }
     if (p->num_seqs > lattn::kMaxOrderedSeqs) return 0;
     return round_up((size_t)p->num_seqs * sizeof(int32_t), 256);
 }
@@ -192,12 +250,43 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
     if (g_gamma == nullptr || final_state == nullptr) return LATTN_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(g_gamma, 4) ||
         !aligned(final_state, 16) || !aligned(initial_state, 16) || !aligned(cu_seqlens, 4) ||
-        !aligned(workspace, 4))
+        !aligned(workspace, 16))
         return LATTN_ERR_INVALID_ARG;
     const size_t need = lattn_fwd_workspace_size(p);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LATTN_ERR_WORKSPACE;
 
-    const int nw = choose_nw(p->in_dtype, p->head_dim_qk, p->head_dim_v, heads_of(*p));
+    int nw = 0;
+    const Split sp = plan_forward(*p, nw);
+    if (sp.P > 0) {
+        // state-only pass over the segments -> dS; scan -> state entering each segment
+        // and final_state; main pass over the segments from those states.
+        float* dS = static_cast<float*>(workspace);
+        float* s_in = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + split_state_bytes(*p, sp));
+        const int nseg = p->batch * sp.P;
+        lattn::FwdParams f1, f3;
+        if (!make_params(*p, p->head_dim_qk, p->head_dim_v, nw, g_gamma, scale, nullptr, nullptr, f1, nseg))
+            return LATTN_ERR_INVALID_ARG;
+        f1.seg_count = sp.P;
+        f1.seg_len = sp.seg_len;
+        f1.k = k;
+        f1.v = v;
+        f1.q = q;
+        f1.final_state = dS;
+        f3 = f1;
+        f3.init = s_in;
+        f3.o = static_cast<float*>(o);
+        f3.final_state = nullptr;
+        const int dc = device_check();
+        if (dc != LATTN_OK) return dc;
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        if (lattn::launch_fwd(f1, p->in_dtype, nw, reverse != 0, s, true) != hipSuccess) return LATTN_ERR_LAUNCH;
+        if (lattn::launch_seg_scan(dS, initial_state, s_in, final_state, g_gamma, p->batch, p->num_heads, sp.P,
+                                   sp.seg_len, p->seqlen, (int64_t)p->head_dim_qk * p->head_dim_v, reverse != 0,
+                                   s) != hipSuccess)
+            return LATTN_ERR_LAUNCH;
+        if (lattn::launch_fwd(f3, p->in_dtype, nw, reverse != 0, s) != hipSuccess) return LATTN_ERR_LAUNCH;
+        return LATTN_OK;
+    }
     const int32_t* order = (varlen && need > 0) ? static_cast<const int32_t*>(workspace) : nullptr;
     lattn::FwdParams fp;
     if (!make_params(*p, p->head_dim_qk, p->head_dim_v, nw, g_gamma, scale, cu_seqlens, order, fp))

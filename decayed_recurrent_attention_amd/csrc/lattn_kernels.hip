@@ -74,7 +74,13 @@ __device__ inline bool decode_work(const FwdParams& p, Work& w) {
     w.n = p.order ? p.order[rank] : rank;
     w.h = w.kvh * (p.num_heads / p.num_kv_heads) + j / p.nvb;
     w.vb = j % p.nvb;
-    if (p.cu) {
+    if (p.seg_count > 0) {  // sequence n = segment n % seg_count of batch row n / seg_count
+        const int b = w.n / p.seg_count, sg = w.n % p.seg_count;
+        const int64_t a = (int64_t)sg * p.seg_len;
+        const int64_t e = min(a + p.seg_len, (int64_t)p.seqlen);
+        w.start = (int64_t)b * p.seqlen + a;
+        w.len = e > a ? e - a : 0;
+    } else if (p.cu) {
         int64_t a = p.cu[w.n];
         int64_t e = p.cu[w.n + 1];
         a = min(max(a, (int64_t)0), (int64_t)p.seqlen);
@@ -301,7 +307,9 @@ __device__ inline void split_state(const f32x4* S, bf16x8* hi, bf16x8* lo) {
     }
 }
 
-template <int DK, int NW, bool REV>
+// SONLY: only the state recurrence (no Q, no output): the final state of every
+// sequence from K and V alone.
+template <int DK, int NW, bool REV, bool SONLY>
 __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p) {
     using Cfg = Bf16Cfg<DK, NW>;
     constexpr int BV = Cfg::BV, PP = Cfg::PP, PVB = Cfg::PVB, KB = Cfg::KB, MT = Cfg::MT;
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
             const int B = kbyte * 64 + lane, row = B / PP;
             const int blk = (B % PP) ^ qk_swz<PP>(row);
             const int rs = REV ? Lc - 1 - row : row;  // out of range past the end
-            copy16_to_lds(stage + kbyte * 1024, rq, rs * (int)qrow_b + blk * 16);
+            if constexpr (!SONLY) copy16_to_lds(stage + kbyte * 1024, rq, rs * (int)qrow_b + blk * 16);
             copy16_to_lds(stage + Cfg::Q_BYTES + kbyte * 1024, rk, rs * (int)krow_b + blk * 16);
         }
 #pragma unroll
@@ -415,15 +423,17 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
     // Wait until this wave's copies of chunk c are in LDS.  Issued after them, in
     // order: the copies of DEPTH-1 later chunks and the output stores of the
     // min(c, DEPTH) chunks computed since.
-    constexpr int W0 = (DEPTH - 1) * Cfg::NCOPY;
-    constexpr int WC = W0 + DEPTH * Cfg::NSTORE;
+    constexpr int NCOPY = SONLY ? Cfg::QCOPIES + Cfg::VCOPIES : Cfg::NCOPY;
+    constexpr int NSTORE = SONLY ? 0 : Cfg::NSTORE;
+    constexpr int W0 = (DEPTH - 1) * NCOPY;
+    constexpr int WC = W0 + DEPTH * NSTORE;
     auto wait_chunk = [&](int c) {
         if (c >= DEPTH) {
             wait_vmem<(WC < 63 ? WC : 63)>();
         } else if (c == 0) {
             wait_vmem<(W0 < 63 ? W0 : 63)>();
         } else {
-            constexpr int W1 = W0 + Cfg::NSTORE;
+            constexpr int W1 = W0 + NSTORE;
             wait_vmem<(W1 < 63 ? W1 : 63)>();
         }
     };
@@ -473,6 +483,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_bf16(kop[mt], vop, S[mt]);
         }
+        if constexpr (SONLY) return;
 
         // Q S_prev for all 64 rows of this wave's columns, and this wave's share of
         // the ten lower-triangle (K Q^T) tiles: tiles t = wv, wv + NW, ... (round
@@ -939,6 +950,36 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
+// Intra-sequence split: chain the segments' own state contributions dS (from a
+// state-only pass) into the state entering each segment and the final state.
+// Per (row b, head h) and 4 state elements, in processing order:
+//     S_in[seg] = S;   S = lam^len(seg) * S + dS[seg];   final = S.
+// dS and S_in are [B * P, H, dk, dv] with segment index b * P + seg.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ dS, const float* __restrict__ init,
+                                                       float* __restrict__ s_in, float* __restrict__ final_state,
+                                                       const float* __restrict__ g_gamma, int H, int P, int seg_len,
+                                                       int seqlen, int elems4, int rev) {
+    const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e4 >= elems4) return;
+    const int64_t bh = blockIdx.y;  // b * H + h
+    const int h = (int)(bh % H);
+    const int64_t b = bh / H;
+    const float g2 = g_gamma[h] * kLog2e;
+    const int64_t elems = (int64_t)elems4 * 4;
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    if (init) S = *reinterpret_cast<const f32x4*>(init + bh * elems + 4 * e4);
+    for (int j = 0; j < P; ++j) {
+        const int sg = rev ? P - 1 - j : j;
+        const int len = min(seg_len, seqlen - sg * seg_len);
+        const int64_t at = ((b * P + sg) * H + h) * elems + 4 * e4;
+        *reinterpret_cast<f32x4*>(s_in + at) = S;
+        S = exp2f(g2 * (float)len) * S + *reinterpret_cast<const f32x4*>(dS + at);
+    }
+    if (final_state) *reinterpret_cast<f32x4*>(final_state + bh * elems + 4 * e4) = S;
+}
+
+// ---------------------------------------------------------------------------
 // Longest-first order of packed sequences (ties by index): order[rank] = sequence.
 // Lengths are clamped exactly as decode_work clamps them.
 // ---------------------------------------------------------------------------
@@ -964,12 +1005,19 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* cu, int n
 }
 
 template <int DK, int NW>
-hipError_t launch_bf16(const FwdParams& p, bool rev, hipStream_t s) {
+hipError_t launch_bf16(const FwdParams& p, bool rev, bool sonly, hipStream_t s) {
     const dim3 grid(fwd_grid_size(p)), block(64 * NW);
-    if (rev)
-        hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true>), grid, block, 0, s, p);
-    else
-        hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false>), grid, block, 0, s, p);
+    if (sonly) {
+        if (rev)
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false, true>), grid, block, 0, s, p);
+    } else {
+        if (rev)
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, false>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false, false>), grid, block, 0, s, p);
+    }
     return hipGetLastError();
 }
 
@@ -999,15 +1047,15 @@ __host__ __device__ constexpr bool f32_variant(int dk, int nw) {
 }
 
 template <int DK>
-hipError_t launch_bf16_nw(const FwdParams& p, int nw, bool rev, hipStream_t s) {
+hipError_t launch_bf16_nw(const FwdParams& p, int nw, bool rev, bool sonly, hipStream_t s) {
     if constexpr (bf16_variant(DK, 1)) {
-        if (nw == 1) return launch_bf16<DK, 1>(p, rev, s);
+        if (nw == 1) return launch_bf16<DK, 1>(p, rev, sonly, s);
     }
     if constexpr (bf16_variant(DK, 2)) {
-        if (nw == 2) return launch_bf16<DK, 2>(p, rev, s);
+        if (nw == 2) return launch_bf16<DK, 2>(p, rev, sonly, s);
     }
     if constexpr (bf16_variant(DK, 4)) {
-        if (nw == 4) return launch_bf16<DK, 4>(p, rev, s);
+        if (nw == 4) return launch_bf16<DK, 4>(p, rev, sonly, s);
     }
     return hipErrorInvalidValue;
 }
@@ -1040,17 +1088,18 @@ int fwd_grid_size(const FwdParams& p) {
     return kNumXcd * per_xcd * p.group_size;
 }
 
-hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t s) {
+hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t s, bool state_only) {
     if (in_dtype == 0) {
         switch (p.dk) {
-            case 32: return launch_bf16_nw<32>(p, nw, reverse, s);
-            case 64: return launch_bf16_nw<64>(p, nw, reverse, s);
-            case 128: return launch_bf16_nw<128>(p, nw, reverse, s);
-            case 192: return launch_bf16_nw<192>(p, nw, reverse, s);
-            case 256: return launch_bf16_nw<256>(p, nw, reverse, s);
+            case 32: return launch_bf16_nw<32>(p, nw, reverse, state_only, s);
+            case 64: return launch_bf16_nw<64>(p, nw, reverse, state_only, s);
+            case 128: return launch_bf16_nw<128>(p, nw, reverse, state_only, s);
+            case 192: return launch_bf16_nw<192>(p, nw, reverse, state_only, s);
+            case 256: return launch_bf16_nw<256>(p, nw, reverse, state_only, s);
             default: return hipErrorInvalidValue;
         }
     }
+    if (state_only) return hipErrorInvalidValue;  // the split runs bf16 problems only
     if (in_dtype == 1) {
         switch (p.dk) {
             case 16: return launch_f32_nw<16>(p, nw, reverse, s);
@@ -1098,6 +1147,15 @@ hipError_t launch_decode(const DecodeParams& p, int in_dtype, hipStream_t s) {
         case 32: return launch_decode_bv<32>(p, in_dtype, s);
         default: return launch_decode_bv<16>(p, in_dtype, s);
     }
+}
+
+hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, float* final_state, const float* g_gamma,
+                           int B, int H, int P, int seg_len, int seqlen, int64_t elems, bool rev, hipStream_t s) {
+    const int elems4 = (int)(elems / 4);
+    const dim3 grid((elems4 + 255) / 256, (unsigned)(B * H));
+    hipLaunchKernelGGL(seg_scan_kernel, grid, dim3(256), 0, s, dS, init, s_in, final_state, g_gamma, H, P, seg_len,
+                       seqlen, elems4, rev ? 1 : 0);
+    return hipGetLastError();
 }
 
 hipError_t launch_seq_order(const int32_t* cu, int num_seqs, int seqlen, int32_t* order, hipStream_t s) {

@@ -49,6 +49,8 @@ struct FwdParams {
     float final_mul;  // final_state = final_mul * S (default 1) ...
     int final_lam;    // ... times exp(g_gamma[h]) when set and the sequence is not empty
                       //    (default 0); final_state may be null
+    int seg_count;    // > 0: sequence n is segment n % seg_count of batch row n / seg_count,
+    int seg_len;      //    positions [s * seg_len, min((s + 1) * seg_len, seqlen)) (default 0)
 };
 
 // Forward defaults of the fields above.
@@ -60,14 +62,22 @@ inline void set_forward_defaults(FwdParams& p) {
     p.init_at_end = 0;
     p.final_mul = 1.f;
     p.final_lam = 0;
+    p.seg_count = 0;
+    p.seg_len = 0;
 }
 
 // Workgroups of 64 * nw threads own BV = 16 * nw value columns each.
 bool have_fwd_kernel(int in_dtype, int dk, int nw);
 // Grid size for the decode used by the forward kernels.
 int fwd_grid_size(const FwdParams& p);
-// Enqueue the forward kernel; returns the HIP error of the launch.
-hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t stream);
+// Enqueue the forward kernel; returns the HIP error of the launch.  state_only (bf16
+// only) runs just the state recurrence: final_state from K and V, no Q, no output.
+hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t stream,
+                      bool state_only = false);
+// Chain per-segment state contributions (intra-sequence split); see seg_scan_kernel.
+hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, float* final_state,
+                           const float* g_gamma, int B, int H, int P, int seg_len, int seqlen,
+                           int64_t elems, bool rev, hipStream_t stream);
 // out[r, j, :] = sum over g < G of part[r, j * G + g, :] for rows r < rows, j < Hkv,
 // with G = H / Hkv and d a multiple of 4.
 hipError_t launch_group_sum(const float* part, float* out, int64_t rows, int H, int Hkv, int d,

@@ -68,9 +68,13 @@ typedef struct {
 } lattn_problem;
 
 /*
- * Device workspace (bytes) that lattn_fwd needs for problem *p; 0 for fixed-length
- * input.  Packed input needs room for the longest-first sequence order.
- * Returns 0 also for an invalid problem (lattn_fwd then reports the error).
+ * Device workspace (bytes) that lattn_fwd needs for problem *p.  Packed input needs
+ * room for the longest-first sequence order.  Fixed-length bf16 input with too few
+ * (batch row, head) pairs to fill the GPU is split along the sequence (each row cut
+ * into segments that run in parallel, chained through their states) and needs two
+ * float32 states per segment: 2 * B * P * H * dk * dv * 4 bytes for P segments.
+ * Otherwise 0.  The environment variable LATTN_SPLIT=N forces N segments (N < 2:
+ * never split).  Returns 0 also for an invalid problem (lattn_fwd then reports it).
  */
 size_t lattn_fwd_workspace_size(const lattn_problem* p);
 
@@ -86,9 +90,10 @@ size_t lattn_fwd_workspace_size(const lattn_problem* p);
  *                  are clamped into it so that no access leaves the buffers.
  *   o              device float32 output.
  *   final_state    device float32 output [N_seq, H, dk, dv].
- *   workspace      device buffer of >= lattn_fwd_workspace_size(p) bytes (may be
- *                  NULL when that is 0).  Owned by the caller; contents on entry
- *                  are ignored; must not be shared by calls that overlap in time.
+ *   workspace      device buffer of >= lattn_fwd_workspace_size(p) bytes, 16-byte
+ *                  aligned (may be NULL when that is 0).  Owned by the caller;
+ *                  contents on entry are ignored; must not be shared by calls that
+ *                  overlap in time.
  * Supported: in_dtype BF16 with dk in {32, 64, 128, 192, 256}; in_dtype F32 with
  * dk in {16, 32, 64, 128}; dv a multiple of 16 up to 256; out_dtype F32.
  * Returns LATTN_OK or a negative status; buffers are untouched on error.

@@ -196,6 +196,27 @@ def test_decode_pointer_errors():
     assert call_decode(prob, s_in=FAKE + 8) == lattn.LATTN_ERR_INVALID_ARG
 
 
+def test_split_workspace(monkeypatch):
+    """Few (row, head) pairs of a long fixed-length bf16 input: split along the sequence."""
+    monkeypatch.delenv("LATTN_SPLIT", raising=False)
+    prob = P(batch=1, seqlen=32768, num_heads=8, num_kv_heads=8, head_dim_qk=128, head_dim_v=128)
+    # widest workgroups: 8 heads x 2 value blocks = 16 -> 16 segments of 2048 tokens
+    assert lattn.lattn_fwd_workspace_size(prob) == 2 * 16 * 8 * 128 * 128 * 4
+    assert call(prob) == lattn.LATTN_ERR_WORKSPACE
+    # enough pairs, short sequences, fp32 and packed input never split
+    assert lattn.lattn_fwd_workspace_size(P(batch=4, seqlen=32768, num_heads=32, head_dim_qk=128,
+                                            head_dim_v=128)) == 0
+    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=1500, num_heads=2)) == 0
+    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=32768, num_heads=2,
+                                            in_dtype=lattn.LATTN_F32)) == 0
+    monkeypatch.setenv("LATTN_SPLIT", "3")
+    small = P(batch=2, seqlen=1000, num_heads=4, num_kv_heads=4)
+    # 16 chunks in 3 segments of 6 chunks (384 tokens)
+    assert lattn.lattn_fwd_workspace_size(small) == 2 * 2 * 3 * 4 * 64 * 64 * 4
+    monkeypatch.setenv("LATTN_SPLIT", "0")
+    assert lattn.lattn_fwd_workspace_size(prob) == 0
+
+
 def test_wrapper_value_errors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(2, 10, 4, 16)

@@ -188,6 +188,44 @@ def test_varlen_3d_input_matches_4d():
     assert torch.equal(o3, o4[0]) and torch.equal(fs3, fs4)
 
 
+# -- intra-sequence split (fixed-length bf16 input with few (row, head) pairs) -------------
+@pytest.mark.parametrize("reverse", [False, True])
+def test_split_forced_segments(reverse, monkeypatch):
+    monkeypatch.setenv("LATTN_SPLIT", "3")  # 16 chunks -> 3 segments of 6, 6 and 4 chunks
+    w = inputs.Workload("split3", 2, 1000, 4, 4, 64, 64, "bf16", 3, 12, reverse=reverse,
+                        init_std=0.5, seed=41)
+    _compare(w, w.make(), tag=" rev" if reverse else "")
+
+
+def test_split_forced_gqa_unequal_dims(monkeypatch):
+    monkeypatch.setenv("LATTN_SPLIT", "5")
+    w = inputs.Workload("split5_gqa", 1, 777, 8, 2, 128, 64, "bf16", 6, 12, init_std=0.3, seed=43)
+    _compare(w, w.make())
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_split_automatic_long_sequence(reverse, monkeypatch):
+    monkeypatch.delenv("LATTN_SPLIT", raising=False)
+    w = inputs.Workload("split_auto", 1, 16384, 4, 4, 128, 128, "bf16", 1, 12, reverse=reverse,
+                        init_std=0.2, seed=42)
+    prob = lattn.LattnProblem(1, 16384, 4, 4, 128, 128, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
+    assert lattn.lattn_fwd_workspace_size(prob) > 0, "expected the split path"
+    _compare(w, w.make(), tag=" rev" if reverse else "")
+
+
+def test_split_matches_unsplit(monkeypatch):
+    """Split and unsplit runs agree to rounding (different summation order)."""
+    w = inputs.Workload("split_vs", 2, 3000, 2, 2, 128, 128, "bf16", 2, 12, init_std=0.5, seed=44)
+    data = w.make()
+    monkeypatch.setenv("LATTN_SPLIT", "0")
+    o0, f0 = gpu_run(w, data)
+    monkeypatch.setenv("LATTN_SPLIT", "4")
+    o1, f1 = gpu_run(w, data)
+    scale_o = float(o0.abs().max())
+    assert float((o0 - o1).abs().max()) <= 1e-4 * scale_o
+    assert float((f0 - f1).abs().max()) <= 1e-4 * float(f0.abs().max())
+
+
 def test_library_is_the_one_loaded():
     """The HIP library in the package directory is what runs (no fallback)."""
     lib = lattn.load_library()
