@@ -53,6 +53,13 @@ class Oracle:
             + [ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
                ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         )
+        lib.oracle_recurrent_gated_fwd.restype = ctypes.c_int
+        lib.oracle_recurrent_gated_fwd.argtypes = (
+            [ctypes.c_int] * 7
+            + [ctypes.c_void_p] * 7
+            + [ctypes.c_double, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+               ctypes.c_void_p, ctypes.c_void_p]
+        )
         lib.oracle_recurrent_bwd.restype = ctypes.c_int
         lib.oracle_recurrent_bwd.argtypes = (
             [ctypes.c_int] * 7
@@ -130,6 +137,56 @@ class Oracle:
             B, T, H, Hkv, dk, dv, dt, q.ctypes.data, k.ctypes.data, v.ctypes.data,
             g.ctypes.data, float(scale), init_ptr, int(bool(reverse)), cu_ptr, n_seq, mask_ptr,
             o.ctypes.data, fs.ctypes.data)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return (o[0] if squeeze else o), fs
+
+    # -- gated forward -----------------------------------------------------------
+    def recurrent_gated_fwd(self, q, k, v, g=None, gk=None, gv=None, g_gamma=None, scale=1.0,
+                            initial_state=None, reverse=False, cu_seqlens=None):
+        """fp64 forward with log-decay gates: g, gk [.., T, H, dk] per key channel, gv
+        [.., T, H, dv] per value channel (each in the dtype of q, k, v, or None), g_gamma [H]
+        float32 or None.  Returns (o, final_state) like recurrent_fwd."""
+        q = np.ascontiguousarray(q)
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        squeeze = q.ndim == 3
+        gates = [None if x is None else np.ascontiguousarray(x) for x in (g, gk, gv)]
+        if squeeze:
+            q, k, v = q[None], k[None], v[None]
+            gates = [None if x is None else x[None] for x in gates]
+        if not (q.dtype == k.dtype == v.dtype):
+            raise TypeError("q, k, v must share one dtype")
+        dt = _in_dtype(q)
+        B, T, H, dk = q.shape
+        Hkv = k.shape[2]
+        dv = v.shape[3]
+        if k.shape != (B, T, Hkv, dk) or v.shape != (B, T, Hkv, dv):
+            raise ValueError("inconsistent q/k/v shapes")
+        for x, d in zip(gates, (dk, dk, dv)):
+            if x is not None and (x.dtype != q.dtype or x.shape != (B, T, H, d)):
+                raise ValueError("gates need the dtype of q and shape [B, T, H, dk | dv]")
+        gg = None if g_gamma is None else np.ascontiguousarray(g_gamma, dtype=np.float32)
+        if cu_seqlens is not None:
+            cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+            n_seq = cu.shape[0] - 1
+            cu_ptr = cu.ctypes.data
+        else:
+            n_seq = B
+            cu_ptr = None
+        init_ptr = None
+        if initial_state is not None:
+            init = np.ascontiguousarray(initial_state, dtype=np.float32)
+            if init.shape != (n_seq, H, dk, dv):
+                raise ValueError(f"initial_state must be {(n_seq, H, dk, dv)}")
+            init_ptr = init.ctypes.data
+        o = np.zeros((B, T, H, dv))
+        fs = np.zeros((n_seq, H, dk, dv))
+        ptr = lambda x: None if x is None else x.ctypes.data
+        rc = self._lib.oracle_recurrent_gated_fwd(
+            B, T, H, Hkv, dk, dv, dt, q.ctypes.data, k.ctypes.data, v.ctypes.data,
+            *(ptr(x) for x in gates), ptr(gg), float(scale), init_ptr, int(bool(reverse)), cu_ptr,
+            n_seq, o.ctypes.data, fs.ctypes.data)
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return (o[0] if squeeze else o), fs

@@ -301,3 +301,97 @@ int oracle_recurrent_bwd(int batch, int seqlen, int num_heads, int num_kv_heads,
     }
     return 0;
 }
+
+/*
+ * Gated forward recurrence (recurrent page: the g, gk and gv gate arguments of
+ * recurrent(), "GLA-style gating"; recurrent_gla page: the GLA wrapper passes g).
+ * The pages give only the shapes of the gates and the update with a decay_t
+ * factor; the reading taken here is that every gate is a log-decay like g_gamma,
+ * acting on the state axis its last dimension names:
+ *
+ *     S_t[a][c] = exp(g_gamma[h] + g_t[a] + gk_t[a] + gv_t[c]) * S_{t-1}[a][c] + k_t[a] v_t[c]
+ *     o_t       = scale * (q_t S_t)
+ *
+ * g and gk are [B, T, H, dk] (per query head and key channel), gv is [B, T, H, dv]
+ * (per value channel); each may be NULL (zero).  They are stored in in_dtype, like
+ * q, k and v; g_gamma [H] float32 may be NULL.  Everything else (GQA, reverse,
+ * packed sequences, initial and final states) is as in oracle_recurrent_fwd.
+ */
+int oracle_recurrent_gated_fwd(int batch, int seqlen, int num_heads, int num_kv_heads,
+                               int dk, int dv, int in_dtype,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* gk, const void* gv,
+                               const float* g_gamma, double scale,
+                               const float* initial_state, int reverse,
+                               const int64_t* cu_seqlens, int num_seqs,
+                               double* o, double* final_state) {
+    if (batch <= 0 || seqlen < 0 || num_heads <= 0 || num_kv_heads <= 0 || dk <= 0 || dv <= 0)
+        return -1;
+    if (num_heads % num_kv_heads != 0) return -1;
+    if (cu_seqlens != NULL && batch != 1) return -1;
+    const int n_seq = cu_seqlens ? num_seqs : batch;
+    const int group = num_heads / num_kv_heads;
+    const int64_t n_pairs = (int64_t)n_seq * num_heads;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t pair = 0; pair < n_pairs; ++pair) {
+        const int n = (int)(pair / num_heads);
+        const int h = (int)(pair % num_heads);
+        const int kvh = h / group;
+        int64_t row0, len;
+        if (cu_seqlens) {
+            row0 = cu_seqlens[n];
+            len = cu_seqlens[n + 1] - cu_seqlens[n];
+        } else {
+            row0 = (int64_t)n * seqlen;
+            len = seqlen;
+        }
+        const double base = g_gamma ? (double)g_gamma[h] : 0.0;
+        double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)dv);
+        double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* kt = (double*)malloc(sizeof(double) * (size_t)dk);
+        double* la = (double*)malloc(sizeof(double) * (size_t)dk); /* log-decay per key channel */
+        double* vt = (double*)malloc(sizeof(double) * (size_t)dv);
+        double* lb = (double*)malloc(sizeof(double) * (size_t)dv); /* log-decay per value channel */
+        double* out_row = (double*)malloc(sizeof(double) * (size_t)dv);
+        const int64_t st_base = ((int64_t)n * num_heads + h) * dk * dv;
+        for (int64_t i = 0; i < (int64_t)dk * dv; ++i)
+            S[i] = initial_state ? (double)initial_state[st_base + i] : 0.0;
+
+        for (int64_t step = 0; step < len; ++step) {
+            const int64_t row = reverse ? row0 + len - 1 - step : row0 + step;
+            const int64_t qo = (row * num_heads + h) * dk;
+            const int64_t ko = (row * num_kv_heads + kvh) * dk;
+            const int64_t vo = (row * num_kv_heads + kvh) * dv;
+            const int64_t go = (row * num_heads + h) * dk;
+            const int64_t gvo = (row * num_heads + h) * dv;
+            for (int a = 0; a < dk; ++a) {
+                qt[a] = in_value(q, in_dtype, qo + a);
+                kt[a] = in_value(k, in_dtype, ko + a);
+                la[a] = base + (g ? in_value(g, in_dtype, go + a) : 0.0) + (gk ? in_value(gk, in_dtype, go + a) : 0.0);
+            }
+            for (int c = 0; c < dv; ++c) {
+                vt[c] = in_value(v, in_dtype, vo + c);
+                lb[c] = gv ? in_value(gv, in_dtype, gvo + c) : 0.0;
+            }
+            /* S <- exp(la + lb) .* S + k_t^T v_t */
+            for (int a = 0; a < dk; ++a)
+                for (int c = 0; c < dv; ++c)
+                    S[(int64_t)a * dv + c] = exp(la[a] + lb[c]) * S[(int64_t)a * dv + c] + kt[a] * vt[c];
+            /* o_t = scale * (q_t S) */
+            for (int c = 0; c < dv; ++c) out_row[c] = 0.0;
+            for (int a = 0; a < dk; ++a)
+                for (int c = 0; c < dv; ++c) out_row[c] += qt[a] * S[(int64_t)a * dv + c];
+            for (int c = 0; c < dv; ++c) o[(row * num_heads + h) * dv + c] = scale * out_row[c];
+        }
+        for (int64_t i = 0; i < (int64_t)dk * dv; ++i) final_state[st_base + i] = S[i];
+        free(out_row);
+        free(lb);
+        free(vt);
+        free(la);
+        free(kt);
+        free(qt);
+        free(S);
+    }
+    return 0;
+}

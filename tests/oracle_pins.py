@@ -402,5 +402,116 @@ def pin_bwd_packed(orc):
 
 BWD_PINS = [pin_bwd_finite_difference, pin_bwd_closed_form, pin_bwd_packed]
 
+
+# ---------------------------------------------------------------------------
+# Gated (GLA) forward pins: an all-pairs closed form built from cumulative sums of
+# the log-decays (a different formulation from the oracle's step-by-step products),
+# reduction to the pinned Lightning forward, and packing.
+# ---------------------------------------------------------------------------
+def _gates(seed, B, T, H, dk, dv, which):
+    rng = np.random.Generator(np.random.PCG64(seed + 2000))
+    out = {}
+    for name, d in (("g", dk), ("gk", dk), ("gv", dv)):
+        out[name] = (-rng.uniform(0.0, 1.5, size=(B, T, H, d))).astype(np.float32) if name in which else None
+    return out
+
+
+def closed_form_gated(q, k, v, gates, g_gamma, scale, S0=None, reverse=False):
+    """o_t = scale sum_{s<=t} sum_a q_t[a] k_s[a] v_s[c] exp(A_t[a]-A_s[a]+Bv_t[c]-Bv_s[c]) plus
+    scale sum_a q_t[a] exp(A_t[a]+Bv_t[c]) S0[a][c], with A, Bv cumulative log-decays."""
+    if reverse:
+        fl = lambda x: None if x is None else x[:, ::-1]
+        o, fs = closed_form_gated(fl(q), fl(k), fl(v), {n: fl(x) for n, x in gates.items()},
+                                  g_gamma, scale, S0, False)
+        return o[:, ::-1], fs
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, T, H, dk = q.shape
+    Hkv, dv = k.shape[2], v.shape[3]
+    rep = H // Hkv
+    k, v = np.repeat(k, rep, axis=2), np.repeat(v, rep, axis=2)
+    la = np.zeros((B, T, H, dk))
+    lb = np.zeros((B, T, H, dv))
+    for name in ("g", "gk"):
+        if gates.get(name) is not None:
+            la += gates[name].astype(np.float64)
+    if gates.get("gv") is not None:
+        lb += gates["gv"].astype(np.float64)
+    if g_gamma is not None:
+        la += np.asarray(g_gamma, dtype=np.float64)[None, None, :, None]
+    A, Bv = np.cumsum(la, axis=1), np.cumsum(lb, axis=1)
+    causal = np.tril(np.ones((T, T)))
+    o = np.zeros((B, T, H, dv))
+    fs = np.zeros((B, H, dk, dv))
+    for b in range(B):
+        for h in range(H):
+            Q, K, V = q[b, :, h], k[b, :, h], v[b, :, h]
+            Ea = np.exp(A[b, :, h][:, None, :] - A[b, :, h][None, :, :])    # [t, s, a]
+            Eb = np.exp(Bv[b, :, h][:, None, :] - Bv[b, :, h][None, :, :])  # [t, s, c]
+            W = np.einsum("ta,sa,tsa->ts", Q, K, Ea) * causal              # [t, s]
+            o[b, :, h] = np.einsum("ts,sc,tsc->tc", W, V, Eb)
+            Fa = np.exp(A[b, -1, h][None, :] - A[b, :, h])                  # [s, a]
+            Fb = np.exp(Bv[b, -1, h][None, :] - Bv[b, :, h])                # [s, c]
+            fs[b, h] = np.einsum("sa,sc,sa,sc->ac", K, V, Fa, Fb)
+            if S0 is not None:
+                S = np.asarray(S0[b, h], dtype=np.float64)
+                o[b, :, h] += np.einsum("ta,ac,ta,tc->tc", Q, S, np.exp(A[b, :, h]), np.exp(Bv[b, :, h]))
+                fs[b, h] += np.exp(A[b, -1, h])[:, None] * S * np.exp(Bv[b, -1, h])[None, :]
+    return scale * o, fs
+
+
+GATED_CASES = [
+    # seed, B, T, H, Hkv, dk, dv, gates, g_gamma, init, reverse
+    (101, 1, 1, 1, 1, 3, 2, ("g",), False, False, False),
+    (102, 2, 9, 2, 1, 4, 3, ("g", "gk"), True, True, False),
+    (103, 1, 13, 4, 2, 3, 5, ("gv",), False, True, True),
+    (104, 2, 11, 2, 2, 5, 4, ("g", "gk", "gv"), True, True, True),
+    (105, 1, 17, 3, 1, 2, 6, ("gk", "gv"), False, False, False),
+]
+
+
+def pin_gated_closed_form(orc):
+    for seed, B, T, H, Hkv, dk, dv, which, use_gg, init, rev in GATED_CASES:
+        q, k, v, gg, S0, scale = _rand_case(seed, B, T, H, Hkv, dk, dv, init)
+        gates = _gates(seed, B, T, H, dk, dv, which)
+        o, fs = orc.recurrent_gated_fwd(q, k, v, **gates, g_gamma=gg if use_gg else None, scale=scale,
+                                        initial_state=S0, reverse=rev)
+        o_ref, fs_ref = closed_form_gated(q, k, v, gates, gg if use_gg else None, scale, S0, rev)
+        _close(o, o_ref, 1e-11, f"gated o, case {seed}")
+        _close(fs, fs_ref, 1e-11, f"gated final_state, case {seed}")
+
+
+def pin_gated_reduces_to_lightning(orc):
+    """A gate that is constant per head is the per-head decay of the pinned forward."""
+    q, k, v, g, S0, scale = _rand_case(111, 2, 21, 4, 2, 4, 3, True)
+    B, T, H = q.shape[:3]
+    for name, d in (("g", 4), ("gk", 4), ("gv", 3)):
+        gate = np.broadcast_to(g[None, None, :, None], (B, T, H, d)).astype(np.float32)
+        o, fs = orc.recurrent_gated_fwd(q, k, v, **{name: gate}, scale=scale, initial_state=S0)
+        o_ref, fs_ref = orc.recurrent_fwd(q, k, v, g, scale, initial_state=S0)
+        _close(o, o_ref, 1e-12, f"{name} constant per head: o")
+        _close(fs, fs_ref, 1e-12, f"{name} constant per head: final_state")
+
+
+def pin_gated_packed(orc):
+    lens = [5, 0, 12, 1]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T = int(cu[-1])
+    q, k, v, gg, _, scale = _rand_case(121, 1, T, 4, 2, 3, 4, False)
+    rng = np.random.Generator(np.random.PCG64(122))
+    S0 = rng.standard_normal((len(lens), 4, 3, 4)).astype(np.float32)
+    gates = _gates(121, 1, T, 4, 3, 4, ("g", "gv"))
+    o, fs = orc.recurrent_gated_fwd(q, k, v, **gates, g_gamma=gg, scale=scale, initial_state=S0,
+                                    cu_seqlens=cu, reverse=True)
+    for n in range(len(lens)):
+        a, e = cu[n], cu[n + 1]
+        one = orc.recurrent_gated_fwd(q[:, a:e], k[:, a:e], v[:, a:e],
+                                      **{m: x[:, a:e] for m, x in gates.items() if x is not None},
+                                      g_gamma=gg, scale=scale, initial_state=S0[n:n + 1], reverse=True)
+        assert np.array_equal(o[:, a:e], one[0]) and np.array_equal(fs[n:n + 1], one[1]), f"sequence {n}"
+
+
+GATED_PINS = [pin_gated_closed_form, pin_gated_reduces_to_lightning, pin_gated_packed]
+
 ALL_PINS = [pin_brute_force, pin_bf16_words, pin_no_decay, pin_chaining, pin_reverse_flip,
-            pin_packed, pin_lightning_ones, pin_recurrent_examples, pin_g_gamma, pin_pairs] + BWD_PINS
+            pin_packed, pin_lightning_ones, pin_recurrent_examples, pin_g_gamma, pin_pairs] + BWD_PINS \
+    + GATED_PINS

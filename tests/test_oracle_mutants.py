@@ -45,6 +45,15 @@ MUTANTS = {
     "bwd_sweep2_forward_order": ("const int64_t row = reverse ? row0 + step : row0 + len - 1 - step;",
                                  "const int64_t row = reverse ? row0 + len - 1 - step : row0 + step;"),
     "bwd_gqa_overwrites": ("dk_out[ko + a] += acc;", "dk_out[ko + a] = acc;"),
+    # gated forward
+    "gated_gv_on_key_axis": ("lb[c] = gv ? in_value(gv, in_dtype, gvo + c) : 0.0;",
+                             "lb[c] = gv ? in_value(gv, in_dtype, go + c) : 0.0;"),
+    "gated_gk_ignored": ("+ (gk ? in_value(gk, in_dtype, go + a) : 0.0);", ";"),
+    "gated_value_decay_dropped": ("exp(la[a] + lb[c]) * S", "exp(la[a]) * S"),
+    "gated_decay_after_add": ("exp(la[a] + lb[c]) * S[(int64_t)a * dv + c] + kt[a] * vt[c];",
+                              "exp(la[a] + lb[c]) * (S[(int64_t)a * dv + c] + kt[a] * vt[c]);"),
+    "gated_g_gamma_ignored": ("const double base = g_gamma ? (double)g_gamma[h] : 0.0;",
+                              "const double base = 0.0;"),
     "bwd_dq_state_before_update": ("S[(int64_t)a * dv + c] = lam * S[(int64_t)a * dv + c] + kt[a] * vt[c];\n"
                                    "                for (int a = 0; a < dk; ++a) {",
                                    "(void)0;\n                for (int a = 0; a < dk; ++a) {"),
