@@ -14,7 +14,9 @@ Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
   decode        one decoding step (lattn_decode) over --decode-batch sequences of the
                 same head shape, state updated in place,
   split         the forward at B1 H8 (same head dims and N), where the rows are split
-                along the sequence, against the same call unsplit.
+                along the sequence, against the same call unsplit,
+  gated         the gated (GLA) forward on the same inputs plus a per-key-channel gate g,
+                against the fp32 matrix peak (it computes in fp32) and HBM.
 """
 from __future__ import annotations
 
@@ -30,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd tokens/s at B4 H32 d128 bf16 N=32K; % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0
+FP32_MFMA_PEAK_TFS = 157.3  # dense fp32 matrix peak of MI355X
 # Lightning2 forward at B4 H32 d128 bf16 n=32768 from the OpenNLPLab lightning-attention
 # README benchmark table (hardware unstated, time read as milliseconds): 17.661427 ms.
 PAGE_LIGHTNING2_MS = 17.661427
@@ -236,6 +239,8 @@ def main():
     ap.add_argument("--seqlen", type=int, default=32768)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-gated", action="store_true",
+                    help="skip the gated (GLA, per-token log-decay gate g) forward measurement")
     ap.add_argument("--no-split", action="store_true",
                     help="skip the intra-sequence split measurement (B1 H8, same head dims and N)")
     ap.add_argument("--decode-batch", type=int, default=128,
@@ -313,6 +318,36 @@ def main():
                          "d_initial_state computed",
                "page_lightning2_bwd_ms": PAGE_LIGHTNING2_BWD_MS if T == 32768 else None}
         del dq, dkk, dvv, d_o
+
+    gated = None
+    if not args.no_gated:
+        gates = w.make_gates(("g",), 0.1)
+        gdev = to_dev(gates["g"])
+        go = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+        gfs = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+
+        def gstep():
+            rc = lattn.lattn_fwd_gated(prob, q, k, v, gdev, None, None, None, w.scale, None, False, None, go,
+                                       gfs, stream=stream.cuda_stream)
+            if rc != lattn.LATTN_OK:
+                raise lattn.LattnError(rc)
+
+        print("[bench] gated forward", file=sys.stderr, flush=True)
+        g_wall, g_ms = time_calls(torch, gstep, stream, args.warmup, args.steps)
+        g_mean = sum(g_ms) / len(g_ms)
+        g_bytes = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2) + B * T * H * dk * 2
+        # the recurrence: decay (1), rank-1 update (2) and readout (2) flops per state element per token
+        g_flops = 5 * B * T * H * dk * dv
+        g_tf = g_flops / (g_mean * 1e-3) / 1e12
+        print(f"[bench] gated {args.steps} steps: {g_wall:.4f} ms/step wall, mean {g_mean:.4f} ms",
+              file=sys.stderr, flush=True)
+        gated = {"workload": f"GLA gate g ~ U[-0.1, 0) per key channel, B{B} H{H} d{dk} N{T} bf16, fp32 compute",
+                 "ms_per_step": g_wall, "tokens_per_s": B * T / (g_wall * 1e-3),
+                 "roofline": {"bound": "mfma", "achieved": g_tf, "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                              "frac": g_tf / FP32_MFMA_PEAK_TFS, "algorithmic_flops": g_flops, "call_ms": g_mean},
+                 "hbm": {"achieved": g_bytes / (g_mean * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": g_bytes / (g_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, "algorithmic_bytes": g_bytes}}
+        del gdev, go, gfs
 
     split = None
     if not args.no_split:
@@ -437,6 +472,8 @@ def main():
         line["decode"] = dec
     if split is not None:
         line["split"] = split
+    if gated is not None:
+        line["gated"] = gated
     print(json.dumps(line), flush=True)
 
 

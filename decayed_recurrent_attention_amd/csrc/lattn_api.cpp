@@ -45,6 +45,23 @@ int check_problem(const lattn_problem& p) {
     return LATTN_OK;
 }
 
+// The gated recurrence: fp32 chunks of 16 tokens, dk 32, 64 or 128, value blocks of
+// 64 columns when dv allows, else 16.
+int gated_nw(int dv) { return dv % 64 == 0 ? 4 : 1; }
+
+int check_gated_problem(const lattn_problem& p) {
+    if (p.batch < 1 || p.seqlen < 0 || p.num_heads < 1 || p.num_kv_heads < 1 || p.head_dim_qk < 1 ||
+        p.head_dim_v < 1 || p.num_seqs < 0)
+        return LATTN_ERR_INVALID_ARG;
+    if (p.num_heads % p.num_kv_heads != 0) return LATTN_ERR_HEADS;
+    if (is_varlen(p) && p.batch != 1) return LATTN_ERR_VARLEN_BATCH;
+    if (p.in_dtype != LATTN_BF16 && p.in_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
+    if (p.out_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
+    if (p.head_dim_v % 16 != 0 || p.head_dim_v > 256) return LATTN_ERR_UNSUPPORTED;
+    if (!lattn::have_gated_kernel(p.head_dim_qk, gated_nw(p.head_dim_v))) return LATTN_ERR_UNSUPPORTED;
+    return LATTN_OK;
+}
+
 // The backward also runs the kernel with the head dims swapped.
 int check_bwd_problem(const lattn_problem& p) {
     const int rc = check_problem(p);
@@ -195,7 +212,7 @@ BwdLayout bwd_layout(const lattn_problem& p) {
 
 extern "C" {
 
-int lattn_abi_version(void) { return 3; }
+int lattn_abi_version(void) { return 4; }
 
 const char* lattn_status_string(int status) {
     switch (status) {
@@ -444,6 +461,55 @@ int lattn_decode(const lattn_problem* p, const void* q, const void* k, const voi
     if (dc != LATTN_OK) return dc;
     if (lattn::launch_decode(dp, p->in_dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
         return LATTN_ERR_LAUNCH;
+    return LATTN_OK;
+}
+
+size_t lattn_fwd_gated_workspace_size(const lattn_problem* p) {
+    if (p == nullptr || check_gated_problem(*p) != LATTN_OK || !is_varlen(*p)) return 0;
+    if (p->num_seqs > lattn::kMaxOrderedSeqs) return 0;
+    return round_up((size_t)p->num_seqs * sizeof(int32_t), 256);
+}
+
+int lattn_fwd_gated(const lattn_problem* p, const void* q, const void* k, const void* v, const void* g,
+                    const void* gk, const void* gv, const float* g_gamma, float scale, const float* initial_state,
+                    int reverse, const int32_t* cu_seqlens, void* o, float* final_state, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+    if (p == nullptr) return LATTN_ERR_INVALID_ARG;
+    const int rc = check_gated_problem(*p);
+    if (rc != LATTN_OK) return rc;
+    const bool varlen = cu_seqlens != nullptr;
+    if (varlen != is_varlen(*p)) return LATTN_ERR_INVALID_ARG;
+    const int64_t tokens = (int64_t)p->batch * p->seqlen;
+    if (tokens > 0 && (q == nullptr || k == nullptr || v == nullptr || o == nullptr)) return LATTN_ERR_INVALID_ARG;
+    if (final_state == nullptr) return LATTN_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(g, 16) || !aligned(gk, 16) ||
+        !aligned(gv, 16) || !aligned(o, 16) || !aligned(g_gamma, 4) || !aligned(final_state, 16) ||
+        !aligned(initial_state, 16) || !aligned(cu_seqlens, 4) || !aligned(workspace, 16))
+        return LATTN_ERR_INVALID_ARG;
+    const size_t need = lattn_fwd_gated_workspace_size(p);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LATTN_ERR_WORKSPACE;
+    const int nw = gated_nw(p->head_dim_v);
+    const int32_t* order = (varlen && need > 0) ? static_cast<const int32_t*>(workspace) : nullptr;
+    lattn::FwdParams fp;
+    if (!make_params(*p, p->head_dim_qk, p->head_dim_v, nw, g_gamma, scale, cu_seqlens, order, fp))
+        return LATTN_ERR_INVALID_ARG;
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
+    fp.g = g;
+    fp.gk = gk;
+    fp.gv = gv;
+    fp.init = initial_state;
+    fp.o = static_cast<float*>(o);
+    fp.final_state = final_state;
+    fp.reverse_gated = reverse != 0;
+    const int dc = device_check();
+    if (dc != LATTN_OK) return dc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (order != nullptr &&
+        lattn::launch_seq_order(cu_seqlens, fp.num_seqs, p->seqlen, const_cast<int32_t*>(order), s) != hipSuccess)
+        return LATTN_ERR_LAUNCH;
+    if (lattn::launch_gated(fp, p->in_dtype, nw, s) != hipSuccess) return LATTN_ERR_LAUNCH;
     return LATTN_OK;
 }
 

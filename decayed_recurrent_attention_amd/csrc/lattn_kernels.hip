@@ -867,6 +867,307 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
 }
 
 // ---------------------------------------------------------------------------
+// Gated recurrence (GLA gates): log-decays per key channel, g_gamma[h] + g_t + gk_t,
+// and per value channel, gv_t, each token.  Chunks of 16 tokens in fp32
+// (v_mfma_f32_16x16x4_f32).  With A_t and B_t the log-decays summed from the chunk
+// start through token t, every exponent below is <= 0, so nothing overflows:
+//   o_t  = scale [ ((q_t .* e^{A_t}) S) .* e^{B_t} + sum_{u<=t} W_tu (v_u .* e^{B_t - B_u}) ]
+//   W_tu = sum_i q_t[i] k_u[i] e^{A_t[i] - A_u[i]}                        (u <= t)
+//   S'   = (e^{A_15} e^{B_15}^T) .* S + (k .* e^{A_15 - A_u})^T (v .* e^{B_15 - B_u})
+// W has a per-channel exponent inside its sum.  When the chunk's decay spans stay
+// below 2^kGSpan, W and the intra term run on MFMA after rescaling about the mid
+// token m (q .* 2^{A_t - A_m} against k .* 2^{A_m - A_u}, v .* 2^{B_m - B_u}, then the
+// rows times 2^{B_t - B_m}): every factor stays below 2^kGSpan, so nothing overflows.
+// Otherwise W is built exactly on the VALU, one entry per thread.  Q S and the state
+// update always run on MFMA.  Wave w owns value columns 16w .. 16w+15 of the block;
+// its state tiles hold rows 16mt + 4lg + ii at column lr (accumulator layout, as in
+// the fp32 kernel).
+// ---------------------------------------------------------------------------
+constexpr int kGChunk = 16;
+constexpr int kGMid = 7;          // reference token of the fast path
+constexpr float kGSpan = 64.f;    // largest |summed log2-decay| of a chunk on the fast path
+
+template <int DK, int NW>
+struct GatedCfg {
+    static constexpr int BV = 16 * NW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int KS = DK + 4;  // row stride (floats) of the dk-wide arrays
+    static constexpr int VS = BV + 4;  // row stride of the BV-wide arrays
+    static constexpr int MT = DK / 16;
+    // dk-wide: q, k, A (cumulative log2-decay), qh = q .* e^A, kt = k .* e^{A_15 - A};
+    // BV-wide: v, B (cumulative log2-decay), vt = v .* e^{B_15 - B}; W is 16 x 17.
+    static constexpr int OFF_Q = 0;
+    static constexpr int OFF_K = OFF_Q + kGChunk * KS;
+    static constexpr int OFF_A = OFF_K + kGChunk * KS;
+    static constexpr int OFF_QH = OFF_A + kGChunk * KS;
+    static constexpr int OFF_KT = OFF_QH + kGChunk * KS;
+    static constexpr int OFF_V = OFF_KT + kGChunk * KS;
+    static constexpr int OFF_B = OFF_V + kGChunk * VS;
+    static constexpr int OFF_VT = OFF_B + kGChunk * VS;
+    static constexpr int OFF_W = OFF_VT + kGChunk * VS;
+    // fast path: q .* 2^{A - A_m}, k .* 2^{A_m - A}, v .* 2^{B_m - B} about the mid token m
+    static constexpr int OFF_QM = OFF_W + kGChunk * 17;
+    static constexpr int OFF_KM = OFF_QM + kGChunk * KS;
+    static constexpr int OFF_VM = OFF_KM + kGChunk * KS;
+    static constexpr int FLOATS = OFF_VM + kGChunk * VS;
+    static constexpr int KITEMS = kGChunk * DK / 4, VITEMS = kGChunk * BV / 4;  // 4-element pieces
+    static constexpr int KPER = (KITEMS + NT - 1) / NT, VPER = (VITEMS + NT - 1) / NT;
+    static_assert(DK % 16 == 0 && DK <= 128, "dk must be a multiple of 16 up to 128");
+    static_assert(FLOATS * 4 <= kLdsBudget, "LDS budget");
+};
+
+// Four consecutive input elements as floats (bf16 words or fp32).
+template <bool BF16>
+__device__ inline f32x4 load4(const void* base, int64_t i) {
+    if constexpr (BF16) {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i);
+        return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+    } else {
+        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
+    }
+}
+
+template <int DK, int NW, bool BF16>
+__global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
+    using Cfg = GatedCfg<DK, NW>;
+    constexpr int BV = Cfg::BV, NT = Cfg::NT, KS = Cfg::KS, VS = Cfg::VS, MT = Cfg::MT;
+    __shared__ __attribute__((aligned(16))) float sm[Cfg::FLOATS];
+    float* Qs = sm + Cfg::OFF_Q;
+    float* Ks = sm + Cfg::OFF_K;
+    float* As = sm + Cfg::OFF_A;
+    float* QHs = sm + Cfg::OFF_QH;
+    float* KTs = sm + Cfg::OFF_KT;
+    float* Vs = sm + Cfg::OFF_V;
+    float* Bs = sm + Cfg::OFF_B;
+    float* VTs = sm + Cfg::OFF_VT;
+    float* Ws = sm + Cfg::OFF_W;
+    float* QMs = sm + Cfg::OFF_QM;
+    float* KMs = sm + Cfg::OFF_KM;
+    float* VMs = sm + Cfg::OFF_VM;
+    __shared__ int wide_span;  // this chunk takes the exact VALU path
+
+    Work wk;
+    if (!decode_work(p, wk)) return;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = p.num_heads, dv = p.dv;
+    const int64_t L = wk.len;
+    const int nch = (int)((L + kGChunk - 1) / kGChunk);
+    const bool rev = p.reverse_gated != 0;
+    const bool has_gv = p.gv != nullptr;
+    const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
+    const int j = 16 * wv + lr;        // this lane's column inside the block
+    const int vcol = wk.vb * BV + j;   // ... of v and o
+    auto tok_row = [&](int64_t pos) -> int64_t { return rev ? wk.start + L - 1 - pos : wk.start + pos; };
+    const int64_t qrow = (int64_t)H * DK, krow = (int64_t)p.num_kv_heads * DK;
+    const int64_t vrow = (int64_t)p.num_kv_heads * dv, gvrow = (int64_t)H * dv;
+    const int64_t qoff = (int64_t)wk.h * DK, koff = (int64_t)wk.kvh * DK;
+    const int64_t voff = (int64_t)wk.kvh * dv + wk.vb * BV, gvoff = (int64_t)wk.h * dv + wk.vb * BV;
+
+    f32x4 S[MT];
+    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
+
+    // Staging registers: one chunk of q, k, key log2-decay, v and value log2-decay.
+    // Rows past the end read as zero and decay nothing.
+    f32x4 rq[Cfg::KPER], rk[Cfg::KPER], ra[Cfg::KPER], rv[Cfg::VPER], rb[Cfg::VPER];
+    auto load_chunk = [&](int c) {
+        const int64_t p0 = (int64_t)c * kGChunk;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < Cfg::KPER; ++s) {
+            const int item = tid + s * NT;
+            const int t = item / (DK / 4), c4 = item % (DK / 4);
+            rq[s] = z;
+            rk[s] = z;
+            ra[s] = z;
+            if (item < Cfg::KITEMS && p0 + t < L) {
+                const int64_t row = tok_row(p0 + t);
+                rq[s] = load4<BF16>(p.q, row * qrow + qoff + 4 * c4);
+                rk[s] = load4<BF16>(p.k, row * krow + koff + 4 * c4);
+                f32x4 la = {gg2, gg2, gg2, gg2};
+                if (p.g) la += kLog2e * load4<BF16>(p.g, row * qrow + qoff + 4 * c4);
+                if (p.gk) la += kLog2e * load4<BF16>(p.gk, row * qrow + qoff + 4 * c4);
+                ra[s] = la;
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::VPER; ++s) {
+            const int item = tid + s * NT;
+            const int t = item / (BV / 4), c4 = item % (BV / 4);
+            rv[s] = z;
+            rb[s] = z;
+            if (item < Cfg::VITEMS && p0 + t < L) {
+                const int64_t row = tok_row(p0 + t);
+                rv[s] = load4<BF16>(p.v, row * vrow + voff + 4 * c4);
+                if (has_gv) rb[s] = kLog2e * load4<BF16>(p.gv, row * gvrow + gvoff + 4 * c4);
+            }
+        }
+    };
+    auto store_chunk = [&]() {
+#pragma unroll
+        for (int s = 0; s < Cfg::KPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::KITEMS) {
+                const int t = item / (DK / 4), c4 = item % (DK / 4);
+                lds_store<f32x4>(Qs + t * KS + 4 * c4, rq[s]);
+                lds_store<f32x4>(Ks + t * KS + 4 * c4, rk[s]);
+                lds_store<f32x4>(As + t * KS + 4 * c4, ra[s]);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::VPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::VITEMS) {
+                const int t = item / (BV / 4), c4 = item % (BV / 4);
+                lds_store<f32x4>(Vs + t * VS + 4 * c4, rv[s]);
+                lds_store<f32x4>(Bs + t * VS + 4 * c4, rb[s]);
+            }
+        }
+    };
+
+    if (nch > 0) load_chunk(0);
+    for (int c = 0; c < nch; ++c) {
+        __syncthreads();  // the previous chunk is done with LDS
+        store_chunk();
+        if (tid == 0) wide_span = 0;
+        if (c + 1 < nch) load_chunk(c + 1);
+        __syncthreads();
+        // Cumulative log2-decays through each token, one channel per thread; flag
+        // the chunk when a channel's total decay leaves the fast path's range.
+        for (int ch = tid; ch < DK + BV; ch += NT) {
+            float* col = ch < DK ? As + ch : Bs + (ch - DK);
+            const int stride = ch < DK ? KS : VS;
+            float acc = 0.f;
+#pragma unroll
+            for (int t = 0; t < kGChunk; ++t) {
+                acc += col[t * stride];
+                col[t * stride] = acc;
+            }
+            if (!(fabsf(acc) <= kGSpan)) wide_span = 1;
+        }
+        __syncthreads();
+        const bool fast = wide_span == 0;
+        // Decayed operands: for Q S and the state update, and for the intra term.
+        for (int e = tid; e < kGChunk * DK; e += NT) {
+            const int t = e / DK, i = e % DK;
+            const float at = As[t * KS + i], aend = As[(kGChunk - 1) * KS + i], amid = As[kGMid * KS + i];
+            const float qv = Qs[t * KS + i], kv = Ks[t * KS + i];
+            QHs[t * KS + i] = qv * exp2f(at);
+            KTs[t * KS + i] = kv * exp2f(aend - at);
+            if (fast) {
+                QMs[t * KS + i] = qv * exp2f(at - amid);
+                KMs[t * KS + i] = kv * exp2f(amid - at);
+            }
+        }
+        for (int e = tid; e < kGChunk * BV; e += NT) {
+            const int t = e / BV, jj = e % BV;
+            const float vv = Vs[t * VS + jj];
+            const float bt = Bs[t * VS + jj];
+            VTs[t * VS + jj] = has_gv ? vv * exp2f(Bs[(kGChunk - 1) * VS + jj] - bt) : vv;
+            if (fast) VMs[t * VS + jj] = has_gv ? vv * exp2f(Bs[kGMid * VS + jj] - bt) : vv;
+        }
+        if (!fast) {  // exact W, one entry per thread
+            for (int e = tid; e < kGChunk * kGChunk; e += NT) {
+                const int t = e >> 4, u = e & 15;
+                float w = 0.f;
+                if (u <= t) {
+                    const float* qt = Qs + t * KS;
+                    const float* ku = Ks + u * KS;
+                    const float* at = As + t * KS;
+                    const float* au = As + u * KS;
+#pragma unroll 4
+                    for (int i = 0; i < DK; i += 4) {
+                        const f32x4 q4 = lds_load<f32x4>(qt + i), k4 = lds_load<f32x4>(ku + i);
+                        const f32x4 a4 = lds_load<f32x4>(at + i), b4 = lds_load<f32x4>(au + i);
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) w += q4[x] * k4[x] * exp2f(a4[x] - b4[x]);
+                    }
+                }
+                Ws[t * 17 + u] = w;
+            }
+        }
+        __syncthreads();
+
+        // Inter-chunk part: (q .* 2^A) S on four independent accumulators.
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 Oq[4] = {z, z, z, z};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) Oq[ii] = mfma_f32(QHs[lr * KS + 16 * mt + 4 * lg + ii], S[mt][ii], Oq[ii]);
+        f32x4 O = (Oq[0] + Oq[1]) + (Oq[2] + Oq[3]);
+        if (has_gv) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) O[ii] *= exp2f(Bs[(4 * lg + ii) * VS + j]);
+        }
+        if (fast) {
+            // W^T = (k .* 2^{A_m - A}) (q .* 2^{A - A_m})^T: lane holds W[t = lr][u = 4lg + ii].
+            f32x4 Wa[4] = {z, z, z, z};
+#pragma unroll
+            for (int sq = 0; sq < DK / 4; ++sq)
+                Wa[sq & 3] = mfma_f32(KMs[lr * KS + 4 * sq + lg], QMs[lr * KS + 4 * sq + lg], Wa[sq & 3]);
+            f32x4 W = (Wa[0] + Wa[1]) + (Wa[2] + Wa[3]);
+            f32x4 Oi = z;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int u = 4 * lg + ii;
+                const float wtu = u <= lr ? W[ii] : 0.f;  // causal: u <= t
+                Oi = mfma_f32(wtu, VMs[u * VS + j], Oi);
+            }
+            if (has_gv) {
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) Oi[ii] *= exp2f(Bs[(4 * lg + ii) * VS + j] - Bs[kGMid * VS + j]);
+            }
+            O += Oi;
+        } else if (has_gv) {
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int t = 4 * lg + ii;
+                const float bt = Bs[t * VS + j];
+                float acc = 0.f;
+                for (int u = 0; u <= t; ++u) acc += Ws[t * 17 + u] * Vs[u * VS + j] * exp2f(bt - Bs[u * VS + j]);
+                O[ii] += acc;
+            }
+        } else {
+#pragma unroll
+            for (int sq = 0; sq < 4; ++sq) O = mfma_f32(Ws[lr * 17 + 4 * sq + lg], Vs[(4 * sq + lg) * VS + j], O);
+        }
+        const int64_t p0 = (int64_t)c * kGChunk;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int t = 4 * lg + ii;
+            if (p0 + t < L) p.o[(tok_row(p0 + t) * H + wk.h) * dv + vcol] = p.scale * O[ii];
+        }
+
+        // State update.
+        const float bend = has_gv ? Bs[(kGChunk - 1) * VS + j] : 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= exp2f(As[(kGChunk - 1) * KS + 16 * mt + 4 * lg + ii] + bend);
+#pragma unroll
+        for (int sq = 0; sq < 4; ++sq) {
+            const float vt = VTs[(4 * sq + lg) * VS + j];
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_f32(KTs[(4 * sq + lg) * KS + 16 * mt + lr], vt, S[mt]);
+        }
+    }
+
+    if (p.final_state) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = S[mt][ii];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Gradient sweeps under grouped-query attention: the sum of per-query-head
 // gradients into their kv head, streamed in 16-byte pieces.
 // ---------------------------------------------------------------------------
@@ -1156,6 +1457,36 @@ hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, floa
     hipLaunchKernelGGL(seg_scan_kernel, grid, dim3(256), 0, s, dS, init, s_in, final_state, g_gamma, H, P, seg_len,
                        seqlen, elems4, rev ? 1 : 0);
     return hipGetLastError();
+}
+
+namespace {
+template <int DK, int NW>
+hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
+    const dim3 grid(fwd_grid_size(p)), block(64 * NW);
+    if (bf16)
+        hipLaunchKernelGGL((gated_kernel<DK, NW, true>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((gated_kernel<DK, NW, false>), grid, block, 0, s, p);
+    return hipGetLastError();
+}
+template <int DK>
+hipError_t launch_gated_dk(const FwdParams& p, int nw, bool bf16, hipStream_t s) {
+    if (nw == 4) return launch_gated_t<DK, 4>(p, bf16, s);
+    if (nw == 1) return launch_gated_t<DK, 1>(p, bf16, s);
+    return hipErrorInvalidValue;
+}
+}  // namespace
+
+bool have_gated_kernel(int dk, int nw) { return (dk == 32 || dk == 64 || dk == 128) && (nw == 1 || nw == 4); }
+
+hipError_t launch_gated(const FwdParams& p, int in_dtype, int nw, hipStream_t s) {
+    const bool bf16 = in_dtype == 0;
+    switch (p.dk) {
+        case 32: return launch_gated_dk<32>(p, nw, bf16, s);
+        case 64: return launch_gated_dk<64>(p, nw, bf16, s);
+        case 128: return launch_gated_dk<128>(p, nw, bf16, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_seq_order(const int32_t* cu, int num_seqs, int seqlen, int32_t* order, hipStream_t s) {

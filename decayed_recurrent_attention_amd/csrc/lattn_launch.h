@@ -51,6 +51,12 @@ struct FwdParams {
                       //    (default 0); final_state may be null
     int seg_count;    // > 0: sequence n is segment n % seg_count of batch row n / seg_count,
     int seg_len;      //    positions [s * seg_len, min((s + 1) * seg_len, seqlen)) (default 0)
+    // Gated recurrence only (gated_kernel): log-decay gates in the input dtype, each
+    // [B, T, H, dk] (g, gk) or [B, T, H, dv] (gv), or null; the direction.
+    const void* g;
+    const void* gk;
+    const void* gv;
+    int reverse_gated;
 };
 
 // Forward defaults of the fields above.
@@ -64,6 +70,8 @@ inline void set_forward_defaults(FwdParams& p) {
     p.final_lam = 0;
     p.seg_count = 0;
     p.seg_len = 0;
+    p.g = p.gk = p.gv = nullptr;
+    p.reverse_gated = 0;
 }
 
 // Workgroups of 64 * nw threads own BV = 16 * nw value columns each.
@@ -74,6 +82,9 @@ int fwd_grid_size(const FwdParams& p);
 // only) runs just the state recurrence: final_state from K and V, no Q, no output.
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t stream,
                       bool state_only = false);
+// Gated recurrence (GLA gates), 64 * nw threads for BV = 16 * nw value columns.
+bool have_gated_kernel(int dk, int nw);
+hipError_t launch_gated(const FwdParams& p, int in_dtype, int nw, hipStream_t stream);
 // Chain per-segment state contributions (intra-sequence split); see seg_scan_kernel.
 hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, float* final_state,
                            const float* g_gamma, int B, int H, int P, int seg_len, int seqlen,

@@ -29,6 +29,7 @@ BLOCK = 1 << 22
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_INIT, STREAM_LENS = 0, 1, 2, 3, 4
 STREAM_DO, STREAM_DFINAL = 5, 6  # gradients for the backward
+STREAM_G, STREAM_GK, STREAM_GV = 7, 8, 9  # log-decay gates of the gated recurrence
 
 
 def _threads() -> int:
@@ -132,6 +133,20 @@ class Workload:
         if self.init_std is not None:
             out["initial_state"] = normal((self.num_seqs, H, self.dk, self.dv), self.seed,
                                           STREAM_INIT, std=self.init_std)
+        return out
+
+    def make_gates(self, which=("g",), gmax: float = 0.5) -> dict:
+        """Draw log-decay gates, uniform in [-gmax, 0), in the input dtype: g and gk are
+        [B, T, H, dk], gv is [B, T, H, dv]; gates not named are None."""
+        B, T, H = self.batch, self.seqlen, self.num_heads
+        out = {}
+        for name, d, stream in (("g", self.dk, STREAM_G), ("gk", self.dk, STREAM_GK), ("gv", self.dv, STREAM_GV)):
+            if name not in which:
+                out[name] = None
+                continue
+            rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([self.seed, stream, 0])))
+            x = (-gmax * rng.random((B, T, H, d), dtype=np.float32)).astype(np.float32)
+            out[name] = bf16_words(x) if self.dtype == "bf16" else x
         return out
 
     def make_grads(self, final_std: float | None = 1.0) -> dict:

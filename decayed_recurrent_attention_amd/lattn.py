@@ -33,8 +33,9 @@ LATTN_ERR_LAUNCH = -6
 LATTN_ERR_DEVICE = -7
 
 # Every function declared in include/lattn.h.
-EXPORTS = ("lattn_fwd", "lattn_fwd_workspace_size", "lattn_bwd", "lattn_bwd_workspace_size",
-           "lattn_decode", "lattn_lightning_g_gamma", "lattn_status_string", "lattn_abi_version")
+EXPORTS = ("lattn_fwd", "lattn_fwd_workspace_size", "lattn_fwd_gated", "lattn_fwd_gated_workspace_size",
+           "lattn_bwd", "lattn_bwd_workspace_size", "lattn_decode", "lattn_lightning_g_gamma",
+           "lattn_status_string", "lattn_abi_version")
 
 
 class LattnProblem(ctypes.Structure):
@@ -74,6 +75,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                       vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
             lib.lattn_bwd_workspace_size.restype = ctypes.c_size_t
             lib.lattn_bwd_workspace_size.argtypes = [P]
+            lib.lattn_fwd_gated.restype = ctypes.c_int
+            lib.lattn_fwd_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int, vp,
+                                            vp, vp, vp, ctypes.c_size_t, vp]
+            lib.lattn_fwd_gated_workspace_size.restype = ctypes.c_size_t
+            lib.lattn_fwd_gated_workspace_size.argtypes = [P]
             lib.lattn_decode.restype = ctypes.c_int
             lib.lattn_decode.argtypes = [P, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
             lib.lattn_lightning_g_gamma.restype = ctypes.c_int
@@ -144,6 +150,24 @@ def lattn_bwd(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_sta
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g_gamma), float(scale),
         _ptr(initial_state), int(bool(reverse)), _ptr(cu_seqlens), _ptr(d_o), _ptr(d_final_state),
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_initial_state), _ptr(workspace), ws_bytes, stream))
+
+
+def lattn_fwd_gated_workspace_size(problem: LattnProblem) -> int:
+    return int(load_library().lattn_fwd_gated_workspace_size(ctypes.byref(problem)))
+
+
+def lattn_fwd_gated(problem: LattnProblem, q, k, v, g, gk, gv, g_gamma, scale: float, initial_state,
+                    reverse: bool, cu_seqlens, o, final_state, workspace=None, stream=None) -> int:
+    """Raw call: tensors (or None) are passed by address; returns the status code."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return int(load_library().lattn_fwd_gated(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(gv), _ptr(g_gamma),
+        float(scale), _ptr(initial_state), int(bool(reverse)), _ptr(cu_seqlens), _ptr(o),
+        _ptr(final_state), _ptr(workspace), ws_bytes, stream))
 
 
 def lattn_decode(problem: LattnProblem, q, k, v, g_gamma, scale: float, state_in, state_out, o,
@@ -231,16 +255,23 @@ def _prepare(query, key, value, g_gamma, softmax_scale, initial_state, cu_seqlen
     return a
 
 
-def recurrent(query, key, value, g_gamma=None, softmax_scale=None, initial_state=None,
-              reverse=False, cu_seqlens=None):
-    """Decayed recurrent attention forward on the GPU.
+def recurrent(query, key, value, g=None, g_gamma=None, gk=None, gv=None, softmax_scale=None,
+              initial_state=None, reverse=False, cu_seqlens=None):
+    """Decayed recurrent attention forward on the GPU (the recurrent interface page's
+    argument order).
 
-    Shapes follow the recurrent interface page: q [B, T, H, dk], k [B, T, Hkv, dk],
-    v [B, T, Hkv, dv]; packed input (``cu_seqlens``) may drop the batch axis.
+    Shapes follow that page: q [B, T, H, dk], k [B, T, Hkv, dk], v [B, T, Hkv, dv];
+    packed input (``cu_seqlens``) may drop the batch axis.  g, gk ([.., T, H, dk]) and gv
+    ([.., T, H, dv]) are optional per-token log-decay gates in the dtype of q; with any
+    of them the gated kernel runs, else the Lightning kernel with g_gamma [H].
     Returns (o float32 [.., T, H, dv], final_state float32 [N_seq, H, dk, dv]).
     """
     import torch
 
+    if g is not None or gk is not None or gv is not None:
+        return recurrent_gated(query, key, value, g=g, gk=gk, gv=gv, g_gamma=g_gamma,
+                               softmax_scale=softmax_scale, initial_state=initial_state,
+                               reverse=reverse, cu_seqlens=cu_seqlens)
     a = _prepare(query, key, value, g_gamma, softmax_scale, initial_state, cu_seqlens)
     o = torch.empty((a.B, a.T, a.H, a.dv), device=a.dev, dtype=torch.float32)
     fs = torch.empty(a.state_shape, device=a.dev, dtype=torch.float32)
@@ -250,6 +281,52 @@ def recurrent(query, key, value, g_gamma=None, softmax_scale=None, initial_state
     if rc != LATTN_OK:
         raise LattnError(rc)
     return (o[0] if a.squeeze else o), fs
+
+
+def recurrent_gated(query, key, value, g=None, gk=None, gv=None, g_gamma=None, softmax_scale=None,
+                    initial_state=None, reverse=False, cu_seqlens=None):
+    """Forward with per-token log-decay gates (gated kernel; see lattn_fwd_gated)."""
+    import torch
+
+    a = _prepare(query, key, value, g_gamma, softmax_scale, initial_state, cu_seqlens)
+    gates = []
+    for name, x, d in (("g", g, a.dk), ("gk", gk, a.dk), ("gv", gv, a.dv)):
+        if x is not None:
+            if a.squeeze:
+                x = x.unsqueeze(0)
+            if x.dtype != a.q.dtype:
+                raise TypeError(f"{name} must have the dtype of the inputs ({a.q.dtype}), got {x.dtype}")
+            x = x.to(device=a.dev).contiguous()
+            if x.shape != (a.B, a.T, a.H, d):
+                raise ValueError(f"{name} must have shape {(a.B, a.T, a.H, d)}")
+        gates.append(x)
+    o = torch.empty((a.B, a.T, a.H, a.dv), device=a.dev, dtype=torch.float32)
+    fs = torch.empty(a.state_shape, device=a.dev, dtype=torch.float32)
+    ws_bytes = lattn_fwd_gated_workspace_size(a.prob)
+    ws = torch.empty(ws_bytes, device=a.dev, dtype=torch.uint8) if ws_bytes else None
+    g_gamma_t = None if g_gamma is None else a.g
+    rc = lattn_fwd_gated(a.prob, a.q, a.k, a.v, *gates, g_gamma_t, a.scale, a.init, reverse, a.cu, o, fs, ws)
+    if rc != LATTN_OK:
+        raise LattnError(rc)
+    return (o[0] if a.squeeze else o), fs
+
+
+def recurrent_gla(query, key, value, g=None, g_gamma=None, softmax_scale=None, initial_state=None,
+                  reverse=False, cu_seqlens=None):
+    """Gated linear attention (recurrent_gla page): the recurrence with the per-key-channel
+    gate g and the per-head decay g_gamma; the default scale is dk^-1/2."""
+    if cu_seqlens is not None and query.dim() == 4 and query.shape[0] != 1:
+        raise ValueError(f"cu_seqlens needs batch size 1 (got {query.shape[0]}); pack the "
+                         "sequences along the token axis")
+    if cu_seqlens is not None and initial_state is not None and \
+            initial_state.shape[0] != len(cu_seqlens) - 1:
+        raise ValueError(f"initial_state holds {initial_state.shape[0]} states but cu_seqlens "
+                         f"describes {len(cu_seqlens) - 1} sequences")
+    if g is None:
+        return recurrent(query, key, value, g_gamma=g_gamma, softmax_scale=softmax_scale,
+                         initial_state=initial_state, reverse=reverse, cu_seqlens=cu_seqlens)
+    return recurrent_gated(query, key, value, g=g, g_gamma=g_gamma, softmax_scale=softmax_scale,
+                           initial_state=initial_state, reverse=reverse, cu_seqlens=cu_seqlens)
 
 
 def recurrent_bwd(query, key, value, d_o, g_gamma=None, softmax_scale=None, initial_state=None,

@@ -150,6 +150,29 @@ int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* 
               void* stream);
 
 /*
+ * Forward pass with per-token log-decay gates (recurrent interface page: the g, gk
+ * and gv arguments, "GLA-style gating"; the recurrent_gla page passes g).  Every gate
+ * is a log-decay on the state axis its last dimension names:
+ *
+ *     S_t[a][c] = exp(g_gamma[h] + g_t[a] + gk_t[a] + gv_t[c]) * S_{t-1}[a][c] + k_t[a] v_t[c]
+ *     o_t       = scale * (q_t S_t)
+ *
+ *   g, gk          device [B, T, H, dk] in in_dtype (per query head and key channel), or NULL.
+ *   gv             device [B, T, H, dv] in in_dtype (per value channel), or NULL.
+ *   g_gamma        device float32 [H] or NULL (zeros).  All gates must be finite and <= 0.
+ *   the rest       as for lattn_fwd (GQA, reverse, packed input, states).
+ * Computed in fp32 throughout (chunks of 16 tokens).  Supported: in_dtype BF16 or F32,
+ * dk in {32, 64, 128}, dv a multiple of 16 up to 256, out_dtype F32.  Workspace:
+ * lattn_fwd_gated_workspace_size (the sequence order of packed input, else 0).
+ * Returns LATTN_OK or a negative status; nothing is launched on error.
+ */
+size_t lattn_fwd_gated_workspace_size(const lattn_problem* p);
+int lattn_fwd_gated(const lattn_problem* p, const void* q, const void* k, const void* v, const void* g,
+                    const void* gk, const void* gv, const float* g_gamma, float scale,
+                    const float* initial_state, int reverse, const int32_t* cu_seqlens, void* o,
+                    float* final_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decoding step for a batch of sequences: the recurrence of lattn_fwd advanced
  * by one new token per sequence (the GLA interface page notes that the recurrent
  * form suits autoregressive decoding).  For every batch row n and query head h,
@@ -182,7 +205,7 @@ int lattn_lightning_g_gamma(int num_heads, int layer_idx, int num_layers, float*
 /* Static description of a status code (never NULL). */
 const char* lattn_status_string(int status);
 
-/* ABI version of this header: 3 (1 had no backward, 2 no decoding step). */
+/* ABI version of this header: 4 (1 had no backward, 2 no decoding step, 3 no gates). */
 int lattn_abi_version(void);
 
 #ifdef __cplusplus

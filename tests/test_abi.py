@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lattn.lattn_abi_version() == 3
+    assert lattn.lattn_abi_version() == 4
     for code in range(-7, 1):
         s = lattn.lattn_status_string(code)
         assert s and s != "unknown status"
@@ -215,6 +215,38 @@ def test_split_workspace(monkeypatch):
     assert lattn.lattn_fwd_workspace_size(small) == 2 * 2 * 3 * 4 * 64 * 64 * 4
     monkeypatch.setenv("LATTN_SPLIT", "0")
     assert lattn.lattn_fwd_workspace_size(prob) == 0
+
+
+def call_gated(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, gv=None, gg=None, o=FAKE, fs=FAKE,
+               cu=None, ws=None, ws_bytes=0):
+    L = lattn.load_library()
+    return L.lattn_fwd_gated(ctypes.byref(prob), q, k, v, g, gk, gv, gg, 0.125, None, 0, cu, o, fs, ws,
+                             ws_bytes, None)
+
+
+@pytest.mark.parametrize("prob,status", [
+    (P(batch=0), lattn.LATTN_ERR_INVALID_ARG),
+    (P(num_kv_heads=3), lattn.LATTN_ERR_HEADS),
+    (P(num_seqs=2), lattn.LATTN_ERR_VARLEN_BATCH),
+    (P(head_dim_qk=16), lattn.LATTN_ERR_UNSUPPORTED),   # gated dk: 32, 64, 128
+    (P(head_dim_qk=256), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(head_dim_v=24), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(out_dtype=lattn.LATTN_BF16), lattn.LATTN_ERR_UNSUPPORTED),
+])
+def test_gated_problem_errors(prob, status):
+    assert call_gated(prob) == status
+    assert lattn.lattn_fwd_gated_workspace_size(prob) == 0
+
+
+def test_gated_pointer_errors():
+    prob = P()
+    assert call_gated(prob, q=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_gated(prob, fs=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call_gated(prob, gv=FAKE + 8) == lattn.LATTN_ERR_INVALID_ARG
+    var = P(batch=1, seqlen=300, num_seqs=5)
+    need = lattn.lattn_fwd_gated_workspace_size(var)
+    assert need == 256
+    assert call_gated(var, cu=FAKE) == lattn.LATTN_ERR_WORKSPACE
 
 
 def test_wrapper_value_errors():

@@ -1,0 +1,126 @@
+"""GPU parity of the gated recurrence (lattn_fwd_gated: g, gk, gv log-decay gates)
+against the fp64 oracle.  Tolerance as for the forward: max |gpu - oracle| <= tol *
+RMS(oracle) per tensor, 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (the kernel
+computes in fp32, so the bf16 cases sit far inside their bar)."""
+import numpy as np
+import pytest
+
+from decayed_recurrent_attention_amd import inputs, lattn
+from tests.parity_util import TOL, check, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    lattn.load_library()
+
+
+def _run(w, data, gates, use_gg=True, reverse=None):
+    import torch
+
+    rev = w.reverse if reverse is None else reverse
+    gg = lattn.lattn_lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers) if use_gg else None
+    dev = {n: to_device(data[n], w.dtype) for n in ("q", "k", "v")}
+    gd = {n: to_device(x, w.dtype) for n, x in gates.items() if x is not None}
+    o, fs = lattn.recurrent_gated(dev["q"], dev["k"], dev["v"], **gd,
+                                  g_gamma=None if gg is None else torch.from_numpy(gg).cuda(),
+                                  softmax_scale=w.scale, initial_state=to_device(data["initial_state"], "f32"),
+                                  reverse=rev, cu_seqlens=data["cu_seqlens"])
+    import oracle
+
+    o_ref, fs_ref = oracle.load().recurrent_gated_fwd(
+        data["q"], data["k"], data["v"], **gates, g_gamma=gg, scale=w.scale,
+        initial_state=data["initial_state"], reverse=rev, cu_seqlens=data["cu_seqlens"])
+    return o, fs, o_ref, fs_ref
+
+
+def _compare(w, which, gmax=0.5, use_gg=True, reverse=None, tag=""):
+    data = w.make()
+    gates = w.make_gates(which, gmax)
+    o, fs, o_ref, fs_ref = _run(w, data, gates, use_gg, reverse)
+    tol = TOL[w.dtype]
+    check(o.cpu().numpy(), o_ref, tol, f"{w.name}{tag} gated o")
+    check(fs.cpu().numpy(), fs_ref, tol, f"{w.name}{tag} gated final_state")
+
+
+@pytest.mark.parametrize("which", [("g",), ("gk", "gv"), ("g", "gk", "gv")])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_gated_fp32(which, reverse):
+    w = inputs.Workload("gated_f32", 2, 150, 4, 2, 32, 32, "f32", 5, 12, init_std=0.5, seed=51)
+    _compare(w, which, reverse=reverse, tag=f" {'+'.join(which)}{' rev' if reverse else ''}")
+
+
+def test_gla_bf16_d64_gqa():
+    w = inputs.Workload("gla_d64", 2, 1000, 8, 4, 64, 64, "bf16", 3, 12, init_std=0.3, seed=52)
+    _compare(w, ("g",), use_gg=False)
+
+
+def test_gated_bf16_d128_value_gates():
+    w = inputs.Workload("gated_d128", 2, 2100, 4, 4, 128, 128, "bf16", 0, 12, init_std=0.2, seed=53)
+    _compare(w, ("g", "gv"), gmax=0.2)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_gated_packed_ragged(reverse):
+    lens = [0, 1, 15, 16, 17, 100, 0, 33]
+    w = inputs.Workload("gated_packed", 1, sum(lens), 4, 2, 64, 48, "bf16", 2, 12, seq_lens=lens,
+                        reverse=reverse, init_std=0.4, seed=54)
+    _compare(w, ("g", "gk", "gv"), tag=" rev" if reverse else "")
+
+
+def test_gated_narrow_value_block():
+    """dv not a multiple of 64: one-wave workgroups of 16 columns."""
+    w = inputs.Workload("gated_dv80", 2, 300, 2, 2, 128, 80, "bf16", 4, 12, init_std=0.3, seed=55)
+    _compare(w, ("g", "gv"))
+
+
+def test_gated_strong_gates():
+    """Per-token decays down to e^-6: cumulative exponents reach about -96 per chunk."""
+    w = inputs.Workload("gated_strong", 1, 500, 4, 4, 64, 64, "bf16", 1, 12, init_std=1.0, seed=56)
+    _compare(w, ("g", "gv"), gmax=6.0)
+
+
+def test_gated_constant_gate_equals_lightning():
+    """gk constant per head equals g_gamma: the gated and Lightning kernels agree."""
+    import torch
+
+    w = inputs.Workload("gated_const", 2, 700, 4, 4, 64, 64, "bf16", 6, 12, init_std=0.3, seed=57)
+    data = w.make()
+    g = np.array([-0.0, -0.5, -1.25, -3.0], dtype=np.float32)
+    gk = np.broadcast_to(g[None, None, :, None], (w.batch, w.seqlen, w.num_heads, w.dk)).astype(np.float32)
+    gk_w = inputs.bf16_words(gk)  # these values are exact in bf16
+    q, k, v = (to_device(data[n], "bf16") for n in ("q", "k", "v"))
+    init = to_device(data["initial_state"], "f32")
+    o1, f1 = lattn.recurrent_gated(q, k, v, gk=to_device(gk_w, "bf16"), softmax_scale=w.scale, initial_state=init)
+    o2, f2 = lattn.recurrent(q, k, v, g_gamma=torch.from_numpy(g).cuda(), softmax_scale=w.scale,
+                             initial_state=init)
+    import oracle
+
+    o_ref, f_ref = oracle.load().recurrent_fwd(data["q"], data["k"], data["v"], g, w.scale,
+                                               initial_state=data["initial_state"])
+    check(o1.cpu().numpy(), o_ref, TOL["bf16"], "constant gate o (gated kernel)")
+    check(f1.cpu().numpy(), f_ref, TOL["bf16"], "constant gate final_state (gated kernel)")
+    check(o2.cpu().numpy(), o_ref, TOL["bf16"], "constant gate o (Lightning kernel)")
+
+
+def test_gla_long_d128_sampled():
+    """The benchmark's gated workload (B4 H32 d128 N32768 bf16, g gates), sampled pairs."""
+    w = inputs.long_d128(seqlen=32768)
+    data = w.make()
+    gates = w.make_gates(("g",), 0.1)
+    dev = {n: to_device(data[n], "bf16") for n in ("q", "k", "v")}
+    o, fs = lattn.recurrent_gla(dev["q"], dev["k"], dev["v"], g=to_device(gates["g"], "bf16"),
+                                softmax_scale=w.scale)
+    import oracle
+
+    orc = oracle.load()
+    for b, h in [(0, 0), (2, 13), (3, 31)]:
+        sl = lambda a: np.ascontiguousarray(a[b:b + 1, :, h:h + 1])
+        o_ref, fs_ref = orc.recurrent_gated_fwd(sl(data["q"]), sl(data["k"]), sl(data["v"]), g=sl(gates["g"]),
+                                                scale=w.scale)
+        check(o[b:b + 1, :, h:h + 1].cpu().numpy(), o_ref, TOL["bf16"], f"gla n32768 ({b}, {h}) o")
+        check(fs[b:b + 1, h:h + 1].cpu().numpy(), fs_ref, TOL["bf16"], f"gla n32768 ({b}, {h}) final_state")
