@@ -464,10 +464,13 @@ int lattn_decode(const lattn_problem* p, const void* q, const void* k, const voi
     return LATTN_OK;
 }
 
-size_t lattn_fwd_gated_workspace_size(const lattn_problem* p) {
-    if (p == nullptr || check_gated_problem(*p) != LATTN_OK || !is_varlen(*p)) return 0;
-    if (p->num_seqs > lattn::kMaxOrderedSeqs) return 0;
-    return round_up((size_t)p->num_seqs * sizeof(int32_t), 256);
+size_t lattn_fwd_gated_workspace_size(const lattn_problem* p, int gates) {
+    if (p == nullptr || check_gated_problem(*p) != LATTN_OK) return 0;
+    size_t bytes = 0;
+    if (is_varlen(*p) && p->num_seqs <= lattn::kMaxOrderedSeqs) bytes += round_up((size_t)p->num_seqs * 4, 256);
+    if ((gates & LATTN_GATE_G) && (gates & LATTN_GATE_GK))  // the two key gates are summed first
+        bytes += round_up((size_t)p->batch * p->seqlen * p->num_heads * p->head_dim_qk * 4, 256);
+    return bytes;
 }
 
 int lattn_fwd_gated(const lattn_problem* p, const void* q, const void* k, const void* v, const void* g,
@@ -486,18 +489,23 @@ int lattn_fwd_gated(const lattn_problem* p, const void* q, const void* k, const 
         !aligned(gv, 16) || !aligned(o, 16) || !aligned(g_gamma, 4) || !aligned(final_state, 16) ||
         !aligned(initial_state, 16) || !aligned(cu_seqlens, 4) || !aligned(workspace, 16))
         return LATTN_ERR_INVALID_ARG;
-    const size_t need = lattn_fwd_gated_workspace_size(p);
+    const int gates = (g ? LATTN_GATE_G : 0) | (gk ? LATTN_GATE_GK : 0) | (gv ? LATTN_GATE_GV : 0);
+    const size_t need = lattn_fwd_gated_workspace_size(p, gates);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return LATTN_ERR_WORKSPACE;
     const int nw = gated_nw(p->head_dim_v);
-    const int32_t* order = (varlen && need > 0) ? static_cast<const int32_t*>(workspace) : nullptr;
+    const bool ordered = varlen && p->num_seqs <= lattn::kMaxOrderedSeqs;
+    const int32_t* order = ordered ? static_cast<const int32_t*>(workspace) : nullptr;
+    float* gsum = (g && gk) ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) +
+                                                       (ordered ? round_up((size_t)p->num_seqs * 4, 256) : 0))
+                            : nullptr;
     lattn::FwdParams fp;
     if (!make_params(*p, p->head_dim_qk, p->head_dim_v, nw, g_gamma, scale, cu_seqlens, order, fp))
         return LATTN_ERR_INVALID_ARG;
     fp.q = q;
     fp.k = k;
     fp.v = v;
-    fp.g = g;
-    fp.gk = gk;
+    fp.g = gsum ? static_cast<const void*>(gsum) : (g ? g : gk);
+    fp.gk_is_f32 = gsum != nullptr;
     fp.gv = gv;
     fp.init = initial_state;
     fp.o = static_cast<float*>(o);
@@ -508,6 +516,9 @@ int lattn_fwd_gated(const lattn_problem* p, const void* q, const void* k, const 
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (order != nullptr &&
         lattn::launch_seq_order(cu_seqlens, fp.num_seqs, p->seqlen, const_cast<int32_t*>(order), s) != hipSuccess)
+        return LATTN_ERR_LAUNCH;
+    if (gsum != nullptr &&
+        lattn::launch_gate_sum(g, gk, gsum, tokens * p->num_heads * p->head_dim_qk, p->in_dtype, s) != hipSuccess)
         return LATTN_ERR_LAUNCH;
     if (lattn::launch_gated(fp, p->in_dtype, nw, s) != hipSuccess) return LATTN_ERR_LAUNCH;
     return LATTN_OK;

@@ -884,8 +884,12 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
 // the fp32 kernel).
 // ---------------------------------------------------------------------------
 constexpr int kGChunk = 16;
-constexpr int kGMid = 7;          // reference token of the fast path
-constexpr float kGSpan = 64.f;    // largest |summed log2-decay| of a chunk on the fast path
+constexpr int kGMid = 7;        // reference token of the fast path
+constexpr float kGSpan = 64.f;  // largest |summed log2-decay| of a chunk on the fast path
+
+// Hardware 2^x (v_exp_f32).  Results below the smallest normal float flush to zero,
+// which only drops terms weighted below 2^-126 against a unit-weight term.
+__device__ inline float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int DK, int NW>
 struct GatedCfg {
@@ -894,57 +898,86 @@ struct GatedCfg {
     static constexpr int KS = DK + 4;  // row stride (floats) of the dk-wide arrays
     static constexpr int VS = BV + 4;  // row stride of the BV-wide arrays
     static constexpr int MT = DK / 16;
-    // dk-wide: q, k, A (cumulative log2-decay), qh = q .* e^A, kt = k .* e^{A_15 - A};
-    // BV-wide: v, B (cumulative log2-decay), vt = v .* e^{B_15 - B}; W is 16 x 17.
+    static constexpr int TS = kGChunk + 4;  // row stride of the token-minor arrays
+    // Staged chunk (from registers): q, k, la = key log2-decay per token; v, lb =
+    // value log2-decay per token (the prep phase turns la, lb into their sums A, B
+    // from the chunk start, in place).  Derived for the matrix phase: qh = q .* 2^A,
+    // qm = q .* 2^{A - A_m}, km = k .* 2^{A_m - A} (token-major); kt = k .* 2^{A_15 - A},
+    // vt = v .* 2^{B_15 - B}, vm = v .* 2^{B_m - B} (token-minor: one 16-byte read gives
+    // an MFMA lane its four tokens); bt = 2^B, bm = 2^{B - B_m}; ea = 2^{A_15},
+    // eb = 2^{B_15}; W and oi for the exact path.
     static constexpr int OFF_Q = 0;
     static constexpr int OFF_K = OFF_Q + kGChunk * KS;
     static constexpr int OFF_A = OFF_K + kGChunk * KS;
     static constexpr int OFF_QH = OFF_A + kGChunk * KS;
     static constexpr int OFF_KT = OFF_QH + kGChunk * KS;
-    static constexpr int OFF_V = OFF_KT + kGChunk * KS;
+    static constexpr int OFF_QM = OFF_KT + DK * TS;
+    static constexpr int OFF_KM = OFF_QM + kGChunk * KS;
+    static constexpr int OFF_V = OFF_KM + kGChunk * KS;
     static constexpr int OFF_B = OFF_V + kGChunk * VS;
     static constexpr int OFF_VT = OFF_B + kGChunk * VS;
-    static constexpr int OFF_W = OFF_VT + kGChunk * VS;
-    // fast path: q .* 2^{A - A_m}, k .* 2^{A_m - A}, v .* 2^{B_m - B} about the mid token m
-    static constexpr int OFF_QM = OFF_W + kGChunk * 17;
-    static constexpr int OFF_KM = OFF_QM + kGChunk * KS;
-    static constexpr int OFF_VM = OFF_KM + kGChunk * KS;
-    static constexpr int FLOATS = OFF_VM + kGChunk * VS;
-    static constexpr int KITEMS = kGChunk * DK / 4, VITEMS = kGChunk * BV / 4;  // 4-element pieces
+    static constexpr int OFF_VM = OFF_VT + BV * TS;
+    static constexpr int OFF_BT = OFF_VM + BV * TS;
+    static constexpr int OFF_BM = OFF_BT + kGChunk * VS;
+    static constexpr int OFF_OI = OFF_BM + kGChunk * VS;
+    static constexpr int OFF_W = OFF_OI + kGChunk * VS;
+    static constexpr int OFF_EA = OFF_W + kGChunk * 17;
+    static constexpr int OFF_EB = OFF_EA + DK;
+    static constexpr int FLOATS = OFF_EB + BV;
+    // Staging: 4-element pieces of a chunk, spread over all threads.
+    static constexpr int KITEMS = kGChunk * DK / 4, VITEMS = kGChunk * BV / 4;
     static constexpr int KPER = (KITEMS + NT - 1) / NT, VPER = (VITEMS + NT - 1) / NT;
     static_assert(DK % 16 == 0 && DK <= 128, "dk must be a multiple of 16 up to 128");
     static_assert(FLOATS * 4 <= kLdsBudget, "LDS budget");
 };
 
-// Four consecutive input elements as floats (bf16 words or fp32).
-template <bool BF16>
-__device__ inline f32x4 load4(const void* base, int64_t i) {
-    if constexpr (BF16) {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i);
-        return f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+// Four consecutive elements as raw words (bf16: words x, y hold them; fp32: all four).
+template <bool F32>
+__device__ inline u32x4 load4_raw(const void* base, int64_t i) {
+    if constexpr (F32) {
+        return *reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + i);
     } else {
-        return *reinterpret_cast<const f32x4*>(static_cast<const float*>(base) + i);
+        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i);
+        u32x4 r;
+        r[0] = w[0];
+        r[1] = w[1];
+        return r;
     }
 }
+__device__ inline f32x4 raw_to_f32(u32x4 w, bool f32) {
+    return f32 ? __builtin_bit_cast(f32x4, w) : f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
+}
 
-template <int DK, int NW, bool BF16>
+// One chunk per loop trip, two barriers: (1) the staged chunk is in LDS and the
+// previous matrix phase is done; each thread then owns state channels (columns)
+// and derives, from the decays summed over the chunk in registers, the decayed
+// operands; (2) they are in LDS; the next chunk is staged from registers (its loads
+// were issued a loop trip earlier; raw words are converted only here, so no load is
+// waited for where it is issued) while the waves run the matrix phase.  The
+// barriers wait for LDS operations only, so the prefetch loads stay in flight.
+template <int DK, int NW, bool BF16, bool GF32>
 __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
     using Cfg = GatedCfg<DK, NW>;
-    constexpr int BV = Cfg::BV, NT = Cfg::NT, KS = Cfg::KS, VS = Cfg::VS, MT = Cfg::MT;
+    constexpr int BV = Cfg::BV, NT = Cfg::NT, KS = Cfg::KS, VS = Cfg::VS, MT = Cfg::MT, TS = Cfg::TS;
     __shared__ __attribute__((aligned(16))) float sm[Cfg::FLOATS];
+    __shared__ int wide_span[2];  // per chunk parity: take the exact VALU path
     float* Qs = sm + Cfg::OFF_Q;
     float* Ks = sm + Cfg::OFF_K;
     float* As = sm + Cfg::OFF_A;
     float* QHs = sm + Cfg::OFF_QH;
     float* KTs = sm + Cfg::OFF_KT;
+    float* QMs = sm + Cfg::OFF_QM;
+    float* KMs = sm + Cfg::OFF_KM;
     float* Vs = sm + Cfg::OFF_V;
     float* Bs = sm + Cfg::OFF_B;
     float* VTs = sm + Cfg::OFF_VT;
-    float* Ws = sm + Cfg::OFF_W;
-    float* QMs = sm + Cfg::OFF_QM;
-    float* KMs = sm + Cfg::OFF_KM;
     float* VMs = sm + Cfg::OFF_VM;
-    __shared__ int wide_span;  // this chunk takes the exact VALU path
+    float* BTs = sm + Cfg::OFF_BT;
+    float* BMs = sm + Cfg::OFF_BM;
+    float* OIs = sm + Cfg::OFF_OI;
+    float* Ws = sm + Cfg::OFF_W;
+    float* EAs = sm + Cfg::OFF_EA;
+    float* EBs = sm + Cfg::OFF_EB;
 
     Work wk;
     if (!decode_work(p, wk)) return;
@@ -954,15 +987,21 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
     const int64_t L = wk.len;
     const int nch = (int)((L + kGChunk - 1) / kGChunk);
     const bool rev = p.reverse_gated != 0;
-    const bool has_gv = p.gv != nullptr;
+    const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
+    constexpr bool g_f32 = !BF16 || GF32;  // dtype of the key gate
     const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
-    const int j = 16 * wv + lr;        // this lane's column inside the block
-    const int vcol = wk.vb * BV + j;   // ... of v and o
+    const int j = 16 * wv + lr;       // this lane's column inside the block
+    const int vcol = wk.vb * BV + j;  // ... of v and o
     auto tok_row = [&](int64_t pos) -> int64_t { return rev ? wk.start + L - 1 - pos : wk.start + pos; };
     const int64_t qrow = (int64_t)H * DK, krow = (int64_t)p.num_kv_heads * DK;
     const int64_t vrow = (int64_t)p.num_kv_heads * dv, gvrow = (int64_t)H * dv;
     const int64_t qoff = (int64_t)wk.h * DK, koff = (int64_t)wk.kvh * DK;
     const int64_t voff = (int64_t)wk.kvh * dv + wk.vb * BV, gvoff = (int64_t)wk.h * dv + wk.vb * BV;
+    // Absent gates read an element of an array with the same layout (q for the key
+    // gate, v itself for the value gate) and are written as zero.
+    const void* gbase = has_g ? p.g : p.q;
+    const void* gvbase = has_gv ? p.gv : p.v;
+    const int64_t gvrow_r = has_gv ? gvrow : vrow, gvoff_r = has_gv ? gvoff : voff;
 
     f32x4 S[MT];
     const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
@@ -971,52 +1010,53 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
             S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
+    // The state is in registers before the loop: inside it, the only loads in flight
+    // are the staging prefetches, which the matrix phase then never waits for.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-    // Staging registers: one chunk of q, k, key log2-decay, v and value log2-decay.
-    // Rows past the end read as zero and decay nothing.
-    f32x4 rq[Cfg::KPER], rk[Cfg::KPER], ra[Cfg::KPER], rv[Cfg::VPER], rb[Cfg::VPER];
+    // Staging registers: raw words of this thread's pieces of q, k, the key gate, v
+    // and the value gate; rows past the end read a valid row and are written as zero.
+    u32x4 rq[Cfg::KPER], rk[Cfg::KPER], ra[Cfg::KPER], rv[Cfg::VPER], rb[Cfg::VPER];
+    uint32_t kok = 0, vok = 0;  // bit s: piece s lies inside the sequence
     auto load_chunk = [&](int c) {
         const int64_t p0 = (int64_t)c * kGChunk;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        kok = vok = 0;
 #pragma unroll
         for (int s = 0; s < Cfg::KPER; ++s) {
             const int item = tid + s * NT;
             const int t = item / (DK / 4), c4 = item % (DK / 4);
-            rq[s] = z;
-            rk[s] = z;
-            ra[s] = z;
-            if (item < Cfg::KITEMS && p0 + t < L) {
-                const int64_t row = tok_row(p0 + t);
-                rq[s] = load4<BF16>(p.q, row * qrow + qoff + 4 * c4);
-                rk[s] = load4<BF16>(p.k, row * krow + koff + 4 * c4);
-                f32x4 la = {gg2, gg2, gg2, gg2};
-                if (p.g) la += kLog2e * load4<BF16>(p.g, row * qrow + qoff + 4 * c4);
-                if (p.gk) la += kLog2e * load4<BF16>(p.gk, row * qrow + qoff + 4 * c4);
-                ra[s] = la;
-            }
+            const bool ok = item < Cfg::KITEMS && p0 + t < L;
+            kok |= (ok ? 1u : 0u) << s;
+            const int64_t row = tok_row(ok ? p0 + t : p0);
+            rq[s] = load4_raw<!BF16>(p.q, row * qrow + qoff + 4 * c4);
+            rk[s] = load4_raw<!BF16>(p.k, row * krow + koff + 4 * c4);
+            ra[s] = load4_raw<g_f32>(gbase, row * qrow + qoff + 4 * c4);
         }
 #pragma unroll
         for (int s = 0; s < Cfg::VPER; ++s) {
             const int item = tid + s * NT;
             const int t = item / (BV / 4), c4 = item % (BV / 4);
-            rv[s] = z;
-            rb[s] = z;
-            if (item < Cfg::VITEMS && p0 + t < L) {
-                const int64_t row = tok_row(p0 + t);
-                rv[s] = load4<BF16>(p.v, row * vrow + voff + 4 * c4);
-                if (has_gv) rb[s] = kLog2e * load4<BF16>(p.gv, row * gvrow + gvoff + 4 * c4);
-            }
+            const bool ok = item < Cfg::VITEMS && p0 + t < L;
+            vok |= (ok ? 1u : 0u) << s;
+            const int64_t row = tok_row(ok ? p0 + t : p0);
+            rv[s] = load4_raw<!BF16>(p.v, row * vrow + voff + 4 * c4);
+            rb[s] = load4_raw<!BF16>(gvbase, row * gvrow_r + gvoff_r + 4 * c4);
         }
     };
+    // Write the staged pieces to LDS as floats: la = log2-decay of the key channels
+    // (g_gamma plus the gate), lb of the value channels; zero past the end.
     auto store_chunk = [&]() {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < Cfg::KPER; ++s) {
             const int item = tid + s * NT;
             if (item < Cfg::KITEMS) {
                 const int t = item / (DK / 4), c4 = item % (DK / 4);
-                lds_store<f32x4>(Qs + t * KS + 4 * c4, rq[s]);
-                lds_store<f32x4>(Ks + t * KS + 4 * c4, rk[s]);
-                lds_store<f32x4>(As + t * KS + 4 * c4, ra[s]);
+                const bool ok = (kok >> s) & 1u;
+                const f32x4 a = has_g ? kLog2e * raw_to_f32(ra[s], g_f32) : z;
+                lds_store<f32x4>(Qs + t * KS + 4 * c4, ok ? raw_to_f32(rq[s], !BF16) : z);
+                lds_store<f32x4>(Ks + t * KS + 4 * c4, ok ? raw_to_f32(rk[s], !BF16) : z);
+                lds_store<f32x4>(As + t * KS + 4 * c4, ok ? a + gg2 : z);
             }
         }
 #pragma unroll
@@ -1024,54 +1064,73 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
             const int item = tid + s * NT;
             if (item < Cfg::VITEMS) {
                 const int t = item / (BV / 4), c4 = item % (BV / 4);
-                lds_store<f32x4>(Vs + t * VS + 4 * c4, rv[s]);
-                lds_store<f32x4>(Bs + t * VS + 4 * c4, rb[s]);
+                const bool ok = (vok >> s) & 1u;
+                const f32x4 b = has_gv ? kLog2e * raw_to_f32(rb[s], !BF16) : z;
+                lds_store<f32x4>(Vs + t * VS + 4 * c4, ok ? raw_to_f32(rv[s], !BF16) : z);
+                lds_store<f32x4>(Bs + t * VS + 4 * c4, ok ? b : z);
             }
         }
     };
 
-    if (nch > 0) load_chunk(0);
-    for (int c = 0; c < nch; ++c) {
-        __syncthreads();  // the previous chunk is done with LDS
+    if (tid == 0) wide_span[0] = wide_span[1] = 0;
+    if (nch > 0) {
+        load_chunk(0);
         store_chunk();
-        if (tid == 0) wide_span = 0;
-        if (c + 1 < nch) load_chunk(c + 1);
-        __syncthreads();
-        // Cumulative log2-decays through each token, one channel per thread; flag
-        // the chunk when a channel's total decay leaves the fast path's range.
+    }
+    if (nch > 1) load_chunk(1);
+    for (int c = 0; c < nch; ++c) {
+        lds_barrier();  // (1) chunk c staged; the previous matrix phase is done
+        if (tid == 0) wide_span[(c + 1) & 1] = 0;  // the next chunk's flag, set in its prep
+        // Prep: a thread owns a key channel (or a value channel) for all 16 tokens:
+        // it sums the decays in registers and writes the decayed operands.
         for (int ch = tid; ch < DK + BV; ch += NT) {
-            float* col = ch < DK ? As + ch : Bs + (ch - DK);
-            const int stride = ch < DK ? KS : VS;
-            float acc = 0.f;
+            if (ch < DK) {
+                const int i = ch;
+                float A[kGChunk];
+                float acc = 0.f;
 #pragma unroll
-            for (int t = 0; t < kGChunk; ++t) {
-                acc += col[t * stride];
-                col[t * stride] = acc;
+                for (int t = 0; t < kGChunk; ++t) {
+                    acc += As[t * KS + i];
+                    A[t] = acc;
+                }
+                if (!(fabsf(acc) <= kGSpan)) wide_span[c & 1] = 1;
+                const float aend = A[kGChunk - 1], amid = A[kGMid];
+                EAs[i] = hw_exp2(aend);
+#pragma unroll
+                for (int t = 0; t < kGChunk; ++t) {
+                    const float qv = Qs[t * KS + i], kv = Ks[t * KS + i];
+                    As[t * KS + i] = A[t];
+                    QHs[t * KS + i] = qv * hw_exp2(A[t]);
+                    KTs[i * TS + t] = kv * hw_exp2(aend - A[t]);
+                    QMs[t * KS + i] = qv * hw_exp2(A[t] - amid);
+                    KMs[t * KS + i] = kv * hw_exp2(amid - A[t]);
+                }
+            } else {
+                const int jj = ch - DK;
+                float Bc[kGChunk];
+                float acc = 0.f;
+#pragma unroll
+                for (int t = 0; t < kGChunk; ++t) {
+                    acc += Bs[t * VS + jj];
+                    Bc[t] = acc;
+                }
+                if (!(fabsf(acc) <= kGSpan)) wide_span[c & 1] = 1;
+                const float bend = Bc[kGChunk - 1], bmid = Bc[kGMid];
+                EBs[jj] = hw_exp2(bend);
+#pragma unroll
+                for (int t = 0; t < kGChunk; ++t) {
+                    const float vv = Vs[t * VS + jj];
+                    Bs[t * VS + jj] = Bc[t];
+                    VTs[jj * TS + t] = vv * hw_exp2(bend - Bc[t]);
+                    VMs[jj * TS + t] = vv * hw_exp2(bmid - Bc[t]);
+                    BTs[t * VS + jj] = hw_exp2(Bc[t]);
+                    BMs[t * VS + jj] = hw_exp2(Bc[t] - bmid);
+                }
             }
-            if (!(fabsf(acc) <= kGSpan)) wide_span = 1;
         }
-        __syncthreads();
-        const bool fast = wide_span == 0;
-        // Decayed operands: for Q S and the state update, and for the intra term.
-        for (int e = tid; e < kGChunk * DK; e += NT) {
-            const int t = e / DK, i = e % DK;
-            const float at = As[t * KS + i], aend = As[(kGChunk - 1) * KS + i], amid = As[kGMid * KS + i];
-            const float qv = Qs[t * KS + i], kv = Ks[t * KS + i];
-            QHs[t * KS + i] = qv * exp2f(at);
-            KTs[t * KS + i] = kv * exp2f(aend - at);
-            if (fast) {
-                QMs[t * KS + i] = qv * exp2f(at - amid);
-                KMs[t * KS + i] = kv * exp2f(amid - at);
-            }
-        }
-        for (int e = tid; e < kGChunk * BV; e += NT) {
-            const int t = e / BV, jj = e % BV;
-            const float vv = Vs[t * VS + jj];
-            const float bt = Bs[t * VS + jj];
-            VTs[t * VS + jj] = has_gv ? vv * exp2f(Bs[(kGChunk - 1) * VS + jj] - bt) : vv;
-            if (fast) VMs[t * VS + jj] = has_gv ? vv * exp2f(Bs[kGMid * VS + jj] - bt) : vv;
-        }
-        if (!fast) {  // exact W, one entry per thread
+        lds_barrier();  // (2) derived operands are in LDS
+        const bool fast = wide_span[c & 1] == 0;
+        if (!fast) {  // exact intra term on the VALU (uniform branch): W, then W (v .* 2^{B_t - B_u})
             for (int e = tid; e < kGChunk * kGChunk; e += NT) {
                 const int t = e >> 4, u = e & 15;
                 float w = 0.f;
@@ -1085,57 +1144,68 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
                         const f32x4 q4 = lds_load<f32x4>(qt + i), k4 = lds_load<f32x4>(ku + i);
                         const f32x4 a4 = lds_load<f32x4>(at + i), b4 = lds_load<f32x4>(au + i);
 #pragma unroll
-                        for (int x = 0; x < 4; ++x) w += q4[x] * k4[x] * exp2f(a4[x] - b4[x]);
+                        for (int x = 0; x < 4; ++x) w += q4[x] * k4[x] * hw_exp2(a4[x] - b4[x]);
                     }
                 }
                 Ws[t * 17 + u] = w;
             }
+            lds_barrier();
+            for (int e = tid; e < kGChunk * BV; e += NT) {
+                const int t = e / BV, jj = e % BV;
+                const float bt = Bs[t * VS + jj];
+                float acc = 0.f;
+                for (int u = 0; u <= t; ++u) acc += Ws[t * 17 + u] * Vs[u * VS + jj] * hw_exp2(bt - Bs[u * VS + jj]);
+                OIs[t * VS + jj] = acc;
+            }
+            lds_barrier();
         }
-        __syncthreads();
+        if (c + 1 < nch) {
+            store_chunk();  // chunk c + 1; q, k, v and the decay arrays are read only before (2)
+            if (c + 2 < nch) load_chunk(c + 2);
+        }
 
         // Inter-chunk part: (q .* 2^A) S on four independent accumulators.
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 Oq[4] = {z, z, z, z};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 qh = lds_load<f32x4>(QHs + lr * KS + 16 * mt + 4 * lg);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) Oq[ii] = mfma_f32(QHs[lr * KS + 16 * mt + 4 * lg + ii], S[mt][ii], Oq[ii]);
+            for (int ii = 0; ii < 4; ++ii) Oq[ii] = mfma_f32(qh[ii], S[mt][ii], Oq[ii]);
+        }
         f32x4 O = (Oq[0] + Oq[1]) + (Oq[2] + Oq[3]);
         if (has_gv) {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[ii] *= exp2f(Bs[(4 * lg + ii) * VS + j]);
+            for (int ii = 0; ii < 4; ++ii) O[ii] *= BTs[(4 * lg + ii) * VS + j];
         }
         if (fast) {
             // W^T = (k .* 2^{A_m - A}) (q .* 2^{A - A_m})^T: lane holds W[t = lr][u = 4lg + ii].
+            // The contraction runs over dk = (DK/4) lg + sq, so each lane reads runs of
+            // its own row.
             f32x4 Wa[4] = {z, z, z, z};
 #pragma unroll
-            for (int sq = 0; sq < DK / 4; ++sq)
-                Wa[sq & 3] = mfma_f32(KMs[lr * KS + 4 * sq + lg], QMs[lr * KS + 4 * sq + lg], Wa[sq & 3]);
-            f32x4 W = (Wa[0] + Wa[1]) + (Wa[2] + Wa[3]);
+            for (int s4 = 0; s4 < DK / 16; ++s4) {
+                const f32x4 km = lds_load<f32x4>(KMs + lr * KS + (DK / 4) * lg + 4 * s4);
+                const f32x4 qm = lds_load<f32x4>(QMs + lr * KS + (DK / 4) * lg + 4 * s4);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) Wa[x] = mfma_f32(km[x], qm[x], Wa[x]);
+            }
+            const f32x4 W = (Wa[0] + Wa[1]) + (Wa[2] + Wa[3]);
+            const f32x4 vm = lds_load<f32x4>(VMs + j * TS + 4 * lg);
             f32x4 Oi = z;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int u = 4 * lg + ii;
-                const float wtu = u <= lr ? W[ii] : 0.f;  // causal: u <= t
-                Oi = mfma_f32(wtu, VMs[u * VS + j], Oi);
+                Oi = mfma_f32(u <= lr ? W[ii] : 0.f, vm[ii], Oi);  // causal: u <= t
             }
             if (has_gv) {
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) Oi[ii] *= exp2f(Bs[(4 * lg + ii) * VS + j] - Bs[kGMid * VS + j]);
+                for (int ii = 0; ii < 4; ++ii) Oi[ii] *= BMs[(4 * lg + ii) * VS + j];
             }
             O += Oi;
-        } else if (has_gv) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int t = 4 * lg + ii;
-                const float bt = Bs[t * VS + j];
-                float acc = 0.f;
-                for (int u = 0; u <= t; ++u) acc += Ws[t * 17 + u] * Vs[u * VS + j] * exp2f(bt - Bs[u * VS + j]);
-                O[ii] += acc;
-            }
         } else {
 #pragma unroll
-            for (int sq = 0; sq < 4; ++sq) O = mfma_f32(Ws[lr * 17 + 4 * sq + lg], Vs[(4 * sq + lg) * VS + j], O);
+            for (int ii = 0; ii < 4; ++ii) O[ii] += OIs[(4 * lg + ii) * VS + j];
         }
         const int64_t p0 = (int64_t)c * kGChunk;
 #pragma unroll
@@ -1144,18 +1214,23 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
             if (p0 + t < L) p.o[(tok_row(p0 + t) * H + wk.h) * dv + vcol] = p.scale * O[ii];
         }
 
-        // State update.
-        const float bend = has_gv ? Bs[(kGChunk - 1) * VS + j] : 0.f;
+        // State update: S <- (2^{A_15} 2^{B_15}^T) .* S + kt^T vt.
+        const float eb = has_gv ? EBs[j] : 1.f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 ea = lds_load<f32x4>(EAs + 16 * mt + 4 * lg);
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= exp2f(As[(kGChunk - 1) * KS + 16 * mt + 4 * lg + ii] + bend);
-#pragma unroll
-        for (int sq = 0; sq < 4; ++sq) {
-            const float vt = VTs[(4 * sq + lg) * VS + j];
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_f32(KTs[(4 * sq + lg) * KS + 16 * mt + lr], vt, S[mt]);
+            for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= ea[ii] * eb;
         }
+        // Contraction over the 16 tokens u = 4lg + sq: kt and vt are token-minor.
+        const f32x4 vt = lds_load<f32x4>(VTs + j * TS + 4 * lg);
+        f32x4 kt[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) kt[mt] = lds_load<f32x4>(KTs + (16 * mt + lr) * TS + 4 * lg);
+#pragma unroll
+        for (int sq = 0; sq < 4; ++sq)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_f32(kt[mt][sq], vt[sq], S[mt]);
     }
 
     if (p.final_state) {
@@ -1165,6 +1240,21 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
             for (int ii = 0; ii < 4; ++ii)
                 p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = S[mt][ii];
     }
+}
+
+// Four consecutive input elements as floats (bf16 words or fp32).
+template <bool BF16>
+__device__ inline f32x4 load4(const void* base, int64_t i) {
+    return raw_to_f32(load4_raw<!BF16>(base, i), !BF16);
+}
+
+// Sum of the two key gates into one fp32 gate (the gated kernel reads one).
+template <bool BF16>
+__global__ __launch_bounds__(256) void gate_sum_kernel(const void* __restrict__ g, const void* __restrict__ gk,
+                                                       float* __restrict__ out, int64_t n4) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        *reinterpret_cast<f32x4*>(out + 4 * i) = load4<BF16>(g, 4 * i) + load4<BF16>(gk, 4 * i);
 }
 
 // ---------------------------------------------------------------------------
@@ -1463,10 +1553,12 @@ namespace {
 template <int DK, int NW>
 hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
     const dim3 grid(fwd_grid_size(p)), block(64 * NW);
-    if (bf16)
-        hipLaunchKernelGGL((gated_kernel<DK, NW, true>), grid, block, 0, s, p);
+    if (bf16 && p.gk_is_f32)
+        hipLaunchKernelGGL((gated_kernel<DK, NW, true, true>), grid, block, 0, s, p);
+    else if (bf16)
+        hipLaunchKernelGGL((gated_kernel<DK, NW, true, false>), grid, block, 0, s, p);
     else
-        hipLaunchKernelGGL((gated_kernel<DK, NW, false>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gated_kernel<DK, NW, false, true>), grid, block, 0, s, p);
     return hipGetLastError();
 }
 template <int DK>
@@ -1476,6 +1568,16 @@ hipError_t launch_gated_dk(const FwdParams& p, int nw, bool bf16, hipStream_t s)
     return hipErrorInvalidValue;
 }
 }  // namespace
+
+hipError_t launch_gate_sum(const void* g, const void* gk, float* out, int64_t n, int in_dtype, hipStream_t s) {
+    const int64_t n4 = n / 4;
+    if (n4 == 0) return hipSuccess;
+    if (in_dtype == 0)
+        hipLaunchKernelGGL((gate_sum_kernel<true>), dim3(stream_blocks(n4)), dim3(256), 0, s, g, gk, out, n4);
+    else
+        hipLaunchKernelGGL((gate_sum_kernel<false>), dim3(stream_blocks(n4)), dim3(256), 0, s, g, gk, out, n4);
+    return hipGetLastError();
+}
 
 bool have_gated_kernel(int dk, int nw) { return (dk == 32 || dk == 64 || dk == 128) && (nw == 1 || nw == 4); }
 

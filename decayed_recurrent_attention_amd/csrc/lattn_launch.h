@@ -51,11 +51,12 @@ struct FwdParams {
                       //    (default 0); final_state may be null
     int seg_count;    // > 0: sequence n is segment n % seg_count of batch row n / seg_count,
     int seg_len;      //    positions [s * seg_len, min((s + 1) * seg_len, seqlen)) (default 0)
-    // Gated recurrence only (gated_kernel): log-decay gates in the input dtype, each
-    // [B, T, H, dk] (g, gk) or [B, T, H, dv] (gv), or null; the direction.
+    // Gated recurrence only (gated_kernel): the key log-decay gate g [B, T, H, dk] and
+    // the value gate gv [B, T, H, dv], in the input dtype (g in fp32 when gk_is_f32:
+    // the sum of two key gates), or null; the direction.
     const void* g;
-    const void* gk;
     const void* gv;
+    int gk_is_f32;
     int reverse_gated;
 };
 
@@ -70,7 +71,8 @@ inline void set_forward_defaults(FwdParams& p) {
     p.final_lam = 0;
     p.seg_count = 0;
     p.seg_len = 0;
-    p.g = p.gk = p.gv = nullptr;
+    p.g = p.gv = nullptr;
+    p.gk_is_f32 = 0;
     p.reverse_gated = 0;
 }
 
@@ -84,6 +86,8 @@ hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hi
                       bool state_only = false);
 // Gated recurrence (GLA gates), 64 * nw threads for BV = 16 * nw value columns.
 bool have_gated_kernel(int dk, int nw);
+// out = g + gk in fp32 (n elements, a multiple of 4; inputs in in_dtype).
+hipError_t launch_gate_sum(const void* g, const void* gk, float* out, int64_t n, int in_dtype, hipStream_t stream);
 hipError_t launch_gated(const FwdParams& p, int in_dtype, int nw, hipStream_t stream);
 // Chain per-segment state contributions (intra-sequence split); see seg_scan_kernel.
 hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, float* final_state,

@@ -79,7 +79,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.lattn_fwd_gated.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int, vp,
                                             vp, vp, vp, ctypes.c_size_t, vp]
             lib.lattn_fwd_gated_workspace_size.restype = ctypes.c_size_t
-            lib.lattn_fwd_gated_workspace_size.argtypes = [P]
+            lib.lattn_fwd_gated_workspace_size.argtypes = [P, ctypes.c_int]
             lib.lattn_decode.restype = ctypes.c_int
             lib.lattn_decode.argtypes = [P, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp]
             lib.lattn_lightning_g_gamma.restype = ctypes.c_int
@@ -152,8 +152,11 @@ def lattn_bwd(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_sta
         _ptr(dq), _ptr(dk), _ptr(dv), _ptr(d_initial_state), _ptr(workspace), ws_bytes, stream))
 
 
-def lattn_fwd_gated_workspace_size(problem: LattnProblem) -> int:
-    return int(load_library().lattn_fwd_gated_workspace_size(ctypes.byref(problem)))
+LATTN_GATE_G, LATTN_GATE_GK, LATTN_GATE_GV = 1, 2, 4
+
+
+def lattn_fwd_gated_workspace_size(problem: LattnProblem, gates: int) -> int:
+    return int(load_library().lattn_fwd_gated_workspace_size(ctypes.byref(problem), int(gates)))
 
 
 def lattn_fwd_gated(problem: LattnProblem, q, k, v, g, gk, gv, g_gamma, scale: float, initial_state,
@@ -302,7 +305,8 @@ def recurrent_gated(query, key, value, g=None, gk=None, gv=None, g_gamma=None, s
         gates.append(x)
     o = torch.empty((a.B, a.T, a.H, a.dv), device=a.dev, dtype=torch.float32)
     fs = torch.empty(a.state_shape, device=a.dev, dtype=torch.float32)
-    ws_bytes = lattn_fwd_gated_workspace_size(a.prob)
+    mask = sum(bit for bit, x in zip((LATTN_GATE_G, LATTN_GATE_GK, LATTN_GATE_GV), gates) if x is not None)
+    ws_bytes = lattn_fwd_gated_workspace_size(a.prob, mask)
     ws = torch.empty(ws_bytes, device=a.dev, dtype=torch.uint8) if ws_bytes else None
     g_gamma_t = None if g_gamma is None else a.g
     rc = lattn_fwd_gated(a.prob, a.q, a.k, a.v, *gates, g_gamma_t, a.scale, a.init, reverse, a.cu, o, fs, ws)

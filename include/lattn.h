@@ -163,10 +163,13 @@ int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* 
  *   the rest       as for lattn_fwd (GQA, reverse, packed input, states).
  * Computed in fp32 throughout (chunks of 16 tokens).  Supported: in_dtype BF16 or F32,
  * dk in {32, 64, 128}, dv a multiple of 16 up to 256, out_dtype F32.  Workspace:
- * lattn_fwd_gated_workspace_size (the sequence order of packed input, else 0).
+ * lattn_fwd_gated_workspace_size(p, gates) with gates the LATTN_GATE_* bits of the
+ * gates that will be passed: the sequence order of packed input, and an fp32
+ * [B, T, H, dk] sum when both g and gk are given; else 0.
  * Returns LATTN_OK or a negative status; nothing is launched on error.
  */
-size_t lattn_fwd_gated_workspace_size(const lattn_problem* p);
+enum { LATTN_GATE_G = 1, LATTN_GATE_GK = 2, LATTN_GATE_GV = 4 };
+size_t lattn_fwd_gated_workspace_size(const lattn_problem* p, int gates);
 int lattn_fwd_gated(const lattn_problem* p, const void* q, const void* k, const void* v, const void* g,
                     const void* gk, const void* gv, const float* g_gamma, float scale,
                     const float* initial_state, int reverse, const int32_t* cu_seqlens, void* o,

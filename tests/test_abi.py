@@ -235,7 +235,7 @@ def call_gated(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, gv=None, gg=Non
 ])
 def test_gated_problem_errors(prob, status):
     assert call_gated(prob) == status
-    assert lattn.lattn_fwd_gated_workspace_size(prob) == 0
+    assert lattn.lattn_fwd_gated_workspace_size(prob, 7) == 0
 
 
 def test_gated_pointer_errors():
@@ -244,9 +244,13 @@ def test_gated_pointer_errors():
     assert call_gated(prob, fs=None) == lattn.LATTN_ERR_INVALID_ARG
     assert call_gated(prob, gv=FAKE + 8) == lattn.LATTN_ERR_INVALID_ARG
     var = P(batch=1, seqlen=300, num_seqs=5)
-    need = lattn.lattn_fwd_gated_workspace_size(var)
-    assert need == 256
+    assert lattn.lattn_fwd_gated_workspace_size(var, lattn.LATTN_GATE_G) == 256
     assert call_gated(var, cu=FAKE) == lattn.LATTN_ERR_WORKSPACE
+    # both key gates: an fp32 [B, T, H, dk] sum
+    both = lattn.LATTN_GATE_G | lattn.LATTN_GATE_GK
+    assert lattn.lattn_fwd_gated_workspace_size(prob, both) == 2 * 128 * 8 * 64 * 4
+    assert lattn.lattn_fwd_gated_workspace_size(prob, lattn.LATTN_GATE_GK | lattn.LATTN_GATE_GV) == 0
+    assert call_gated(prob, gk=FAKE) == lattn.LATTN_ERR_WORKSPACE
 
 
 def test_wrapper_value_errors():
