@@ -1,6 +1,7 @@
 // C ABI of liblattn.so: argument validation, kernel selection and launch.
 // Every check that needs no GPU runs before the first HIP call, so argument
 // errors are reported identically on machines without a device.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <initializer_list>
@@ -59,6 +60,9 @@ int check_gated_problem(const lattn_problem& p) {
     if (p.out_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
     if (p.head_dim_v % 16 != 0 || p.head_dim_v > 256) return LATTN_ERR_UNSUPPORTED;
     if (!lattn::have_gated_kernel(p.head_dim_qk, gated_nw(p.head_dim_v))) return LATTN_ERR_UNSUPPORTED;
+    // the kernel addresses 16 token rows of any array with 32-bit byte offsets
+    if ((int64_t)p.num_heads * std::max(p.head_dim_qk, p.head_dim_v) >= (int64_t(1) << 25))
+        return LATTN_ERR_UNSUPPORTED;
     return LATTN_OK;
 }
 

@@ -1242,6 +1242,565 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Gated recurrence, bf16 inputs: the chunk algebra of gated_kernel with every
+// product on bf16 MFMA.  A decayed fp32 operand X is split X = hi + lo, hi its bf16
+// truncation and lo the bf16 rounding of the exact remainder; a product takes
+// hi*hi + hi*lo + lo*hi with fp32 accumulation (about 2^-14 relative error per
+// term).  Raw bf16 v needs no split.  Where a contraction runs over the 16 tokens,
+// hi and lo share one 16x16x32 MFMA: its k index covers the tokens twice, with the
+// hi and then the lo parts of one operand against the other operand repeated.
+// With e_t = 2^{A_t} per key channel, the fast path (every channel's summed decay
+// over the chunk within 2^-kGSpan) takes one exponential pair per element:
+//   o_t  = scale 2^{B_t} .* [ (q_t .* e_t) S + sum_{u<=t} W_tu (v_u .* 2^{-B_u}) ]
+//   W_tu = (q_t .* e_t) . (k_u ./ e_u)
+//   S'   = 2^{A_15} .* [ 2^{B_15}^T .* S + (k ./ e)^T (v .* 2^{B_15 - B_u}) ]
+// so k ./ e serves both W and the state update; masked pairs u > t and the bracket
+// stay below 2^kGSpan times their operands.  A key channel pair with a wider span
+// stores k .* 2^{A_15 - A_u} instead and moves its factor 2^{A_15} in front of S
+// (per-row factors pre and post); a chunk holding one takes the exact VALU path of
+// gated_kernel for W and the intra term.
+// Prep: one item (channel pair, quarter of the chunk) per lane, the four quarters
+// of a pair in one lane quad; each quarter sums its four decays and the quad
+// exchanges the partial sums (DPP), so every lane has its tokens' A_t and A_15.
+// ---------------------------------------------------------------------------
+template <int DK, int NW>
+struct GatedBCfg {
+    static constexpr int BV = 16 * NW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int MT = DK / 16;
+    static constexpr int KB = DK / 32;  // 32-deep blocks of the dk contraction
+    // Dwords per row.  Staged raw chunk (token-major): q, k and a bf16 key gate;
+    // an fp32 key gate; v and the value gate.  Padded so that the prep reads of a
+    // half-wave (8 pairs x 4 quarters) hit distinct banks.
+    static constexpr int SQ = DK / 2 + 2;
+    static constexpr int SG32 = DK + 4;
+    static constexpr int SV = BV / 2 + 2;
+    // Decayed operands read along dk (token-major): bf16 hi half, lo half, 8 dwords
+    // of pad (16-byte blocks per row = 2 mod 32: conflict-free operand reads).
+    static constexpr int OPR = DK + 8;
+    // Token-minor rows (a row per channel): four 16-byte blocks of four tokens,
+    // [hi x4 | lo x4] in bf16 or four fp32, then two blocks of pad.
+    static constexpr int TMR = 24;
+    // fp32 summed decays for the exact path (token-major).
+    static constexpr int AR = DK + 4, BR = BV + 4;
+    static constexpr int OFF_SQ = 0;
+    static constexpr int OFF_SK = OFF_SQ + kGChunk * SQ;
+    static constexpr int OFF_SG = OFF_SK + kGChunk * SQ;  // bf16 or fp32 key gate
+    static constexpr int OFF_SV = OFF_SG + kGChunk * SG32;
+    static constexpr int OFF_SGV = OFF_SV + kGChunk * SV;
+    static constexpr int OFF_QH = OFF_SGV + kGChunk * SV;
+    static constexpr int OFF_KP = OFF_QH + kGChunk * OPR;
+    static constexpr int OFF_KT = OFF_KP + kGChunk * OPR;
+    static constexpr int OFF_VP = OFF_KT + DK * TMR;
+    static constexpr int OFF_VT = OFF_VP + BV * TMR;
+    static constexpr int OFF_BT = OFF_VT + BV * TMR;
+    static constexpr int OFF_A = OFF_BT + BV * TMR;
+    static constexpr int OFF_B = OFF_A + kGChunk * AR;
+    static constexpr int OFF_OI = OFF_B + kGChunk * BR;
+    static constexpr int OFF_W = OFF_OI + kGChunk * BR;
+    static constexpr int OFF_PRE = OFF_W + kGChunk * 17;
+    static constexpr int OFF_POST = OFF_PRE + DK;
+    static constexpr int OFF_EB = OFF_POST + DK;
+    static constexpr int DWORDS = OFF_EB + BV;
+    // Staging: 4-element pieces of a chunk, spread over all threads.
+    static constexpr int KITEMS = kGChunk * DK / 4, VITEMS = kGChunk * BV / 4;
+    static constexpr int KPER = (KITEMS + NT - 1) / NT, VPER = (VITEMS + NT - 1) / NT;
+    // Prep items: channel pairs x quarters.
+    static constexpr int KPREP = 2 * DK, VPREP = 2 * BV;
+    static_assert(DK % 32 == 0 && DK <= 128, "dk must be 32, 64 or 128");
+    static_assert(OFF_PRE % 4 == 0 && OFF_POST % 4 == 0 && OFF_QH % 4 == 0 && OFF_KT % 4 == 0 && OFF_A % 4 == 0,
+                  "16-byte alignment");
+    static_assert(DWORDS * 4 <= kLdsBudget, "LDS budget");
+};
+
+// Four consecutive elements as raw words at a byte offset from a workgroup-uniform
+// base (the offset fits 32 bits, so the load takes the scalar-base form).
+template <bool F32>
+__device__ inline u32x4 load4_at(const void* base, uint32_t byte_off) {
+    const char* b = static_cast<const char*>(base) + byte_off;
+    if constexpr (F32) {
+        return *reinterpret_cast<const u32x4*>(b);
+    } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(b);
+        return u32x4{w[0], w[1], 0u, 0u};
+    }
+}
+
+__device__ inline f32x4 mfma_bf16_w(u32x4 a, u32x4 b, f32x4 c) {
+    return mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c);
+}
+// hi * lo term of a 16-token contraction as a 16x16x32 MFMA with the upper half of
+// k zeroed.  (A 16x16x16 MFMA accumulating onto a 16x16x32 result read part of the
+// accumulator stale in testing: no wait states were placed between the two
+// opcodes.  Same-opcode chains are fine.)
+__device__ inline f32x4 mfma_bf16_half(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+    return mfma_bf16_w(u32x4{a0, a1, 0u, 0u}, u32x4{b0, b1, 0u, 0u}, c);
+}
+// bf16 truncations of a and b in one word (a in the low half).
+__device__ inline uint32_t hi_pack(float a, float b) {
+    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+__device__ inline float lo_part(float x) { return x - __uint_as_float(__float_as_uint(x) & 0xffff0000u); }
+// bf16 roundings of what the truncations of a and b leave (exact in fp32).
+__device__ inline uint32_t lo_pack(float a, float b) { return pack_bf16x2(lo_part(a), lo_part(b)); }
+// Lane k of this lane's quad.
+template <int K>
+__device__ inline float quad_get(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), K * 0x55, 0xF, 0xF, false));
+}
+// Dword of a token-major operand row that holds channels 2pp, 2pp+1.  Channel
+// 32s + 16h + 4g + r sits at position 32s + 8g + 4h + r, so that the eight
+// positions an MFMA lane group reads for block s are the channels whose state rows
+// that lane group holds in tiles 2s and 2s+1 (accumulator layout).
+__host__ __device__ constexpr int gpos_dword(int pp) {
+    return 16 * (pp >> 4) + 4 * ((pp >> 1) & 3) + 2 * ((pp >> 3) & 1) + (pp & 1);
+}
+// Inclusive sums of a quarter's log2-decays (la, per token and channel) over the
+// chunk: the lane quad holds the four quarters of a channel pair.  a = A_t of this
+// quarter's tokens, tot = A_15.
+__device__ inline void quarter_sums(const float (&la)[4][2], int tq, float (&a)[4][2], float (&tot)[2]) {
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        float cs[4];
+        float acc = 0.f;
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) {
+            acc += la[tau][x];
+            cs[tau] = acc;
+        }
+        const float s0 = quad_get<0>(acc), s1 = quad_get<1>(acc), s2 = quad_get<2>(acc), s3 = quad_get<3>(acc);
+        const float s01 = s0 + s1, s012 = s01 + s2;
+        // sum of the earlier quarters, in the order that gives s012 for tq = 3
+        const float pre = ((tq > 0 ? s0 : 0.f) + (tq > 1 ? s1 : 0.f)) + (tq > 2 ? s2 : 0.f);
+#pragma unroll
+        for (int tau = 0; tau < 4; ++tau) a[tau][x] = pre + cs[tau];
+        tot[x] = s012 + s3;
+    }
+}
+
+template <int DK, int NW, bool GF32>
+__global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams p) {
+    using Cfg = GatedBCfg<DK, NW>;
+    constexpr int BV = Cfg::BV, NT = Cfg::NT, MT = Cfg::MT, KB = Cfg::KB;
+    constexpr int SQ = Cfg::SQ, SV = Cfg::SV, OPR = Cfg::OPR, TMR = Cfg::TMR, AR = Cfg::AR, BR = Cfg::BR;
+    constexpr int SGR = GF32 ? Cfg::SG32 : SQ;  // row stride of the staged key gate
+    __shared__ __attribute__((aligned(16))) uint32_t sm[Cfg::DWORDS];
+    __shared__ int wide_span[2];  // per chunk parity: take the exact VALU path
+    uint32_t* SQw = sm + Cfg::OFF_SQ;
+    uint32_t* SKw = sm + Cfg::OFF_SK;
+    uint32_t* SGw = sm + Cfg::OFF_SG;
+    uint32_t* SVw = sm + Cfg::OFF_SV;
+    uint32_t* SGVw = sm + Cfg::OFF_SGV;
+    uint32_t* QHw = sm + Cfg::OFF_QH;
+    uint32_t* KPw = sm + Cfg::OFF_KP;
+    uint32_t* KTw = sm + Cfg::OFF_KT;
+    uint32_t* VPw = sm + Cfg::OFF_VP;
+    uint32_t* VTw = sm + Cfg::OFF_VT;
+    float* BTf = reinterpret_cast<float*>(sm + Cfg::OFF_BT);
+    float* Af = reinterpret_cast<float*>(sm + Cfg::OFF_A);
+    float* Bf = reinterpret_cast<float*>(sm + Cfg::OFF_B);
+    float* OIf = reinterpret_cast<float*>(sm + Cfg::OFF_OI);
+    float* Wf = reinterpret_cast<float*>(sm + Cfg::OFF_W);
+    float* PREf = reinterpret_cast<float*>(sm + Cfg::OFF_PRE);
+    float* POSTf = reinterpret_cast<float*>(sm + Cfg::OFF_POST);
+    float* EBf = reinterpret_cast<float*>(sm + Cfg::OFF_EB);
+
+    Work wk;
+    if (!decode_work(p, wk)) return;
+    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = p.num_heads, dv = p.dv;
+    const int64_t L = wk.len;
+    const int nch = (int)((L + kGChunk - 1) / kGChunk);
+    const bool rev = p.reverse_gated != 0;
+    const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
+    const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
+    const int j = 16 * wv + lr;       // this lane's column inside the block
+    const int vcol = wk.vb * BV + j;  // ... of v and o
+    const int64_t qrow = (int64_t)H * DK, krow = (int64_t)p.num_kv_heads * DK;
+    const int64_t vrow = (int64_t)p.num_kv_heads * dv, gvrow = (int64_t)H * dv;
+    const int64_t qoff = (int64_t)wk.h * DK, koff = (int64_t)wk.kvh * DK;
+    const int64_t voff = (int64_t)wk.kvh * dv + wk.vb * BV, gvoff = (int64_t)wk.h * dv + wk.vb * BV;
+    // Absent gates read an element of an array with the same layout (q for the key
+    // gate, v itself for the value gate) and are never used.
+    const void* gbase = has_g ? p.g : p.q;
+    const void* gvbase = has_gv ? p.gv : p.v;
+    const int64_t gvrow_r = has_gv ? gvrow : vrow, gvoff_r = has_gv ? gvoff : voff;
+    // Chunk c holds the rows [low, low + nv) of the flattened token axis (in either
+    // direction); token t of the chunk is row low + lrow(t).  Offsets inside a chunk
+    // stay 32-bit (the host bounds 16 rows of every array below 2^31 bytes).
+    auto chunk_nv = [&](int c) -> int { return (int)min((int64_t)kGChunk, L - (int64_t)c * kGChunk); };
+    auto chunk_low = [&](int c, int nv) -> int64_t {
+        const int64_t p0 = (int64_t)c * kGChunk;
+        return rev ? wk.start + L - p0 - nv : wk.start + p0;
+    };
+    auto lrow = [&](int t, int nv) -> uint32_t { return (uint32_t)(rev ? nv - 1 - t : t); };
+
+    f32x4 S[MT];
+    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
+    // The state is in registers before the loop: inside it, the only loads in flight
+    // are the staging prefetches, which the matrix phase then never waits for.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+
+    // Staging registers: raw words of this thread's pieces (bf16: words 0 and 1).
+    u32x4 rq[Cfg::KPER], rk[Cfg::KPER], ra[Cfg::KPER], rv[Cfg::VPER], rb[Cfg::VPER];
+    uint32_t kok = 0, vok = 0;  // bit s: piece s lies inside the sequence
+    auto load_chunk = [&](int c) {
+        const int nv = chunk_nv(c);
+        const int64_t low = chunk_low(c, nv);
+        const uint16_t* qb = static_cast<const uint16_t*>(p.q) + (low * qrow + qoff);
+        const uint16_t* kb = static_cast<const uint16_t*>(p.k) + (low * krow + koff);
+        const uint16_t* vb = static_cast<const uint16_t*>(p.v) + (low * vrow + voff);
+        const uint16_t* gvb = static_cast<const uint16_t*>(gvbase) + (low * gvrow_r + gvoff_r);
+        kok = vok = 0;
+#pragma unroll
+        for (int s = 0; s < Cfg::KPER; ++s) {
+            const int item = tid + s * NT;
+            const int t = item / (DK / 4), c4 = item % (DK / 4);
+            const bool ok = item < Cfg::KITEMS && t < nv;
+            kok |= (ok ? 1u : 0u) << s;
+            const uint32_t rr = ok ? lrow(t, nv) : 0u;  // rows past the end read row 0
+            rq[s] = load4_at<false>(qb, 2 * (rr * (uint32_t)qrow + 4 * c4));
+            rk[s] = load4_at<false>(kb, 2 * (rr * (uint32_t)krow + 4 * c4));
+            if constexpr (GF32)
+                ra[s] = load4_at<true>(static_cast<const float*>(gbase) + (low * qrow + qoff),
+                                       4 * (rr * (uint32_t)qrow + 4 * c4));
+            else
+                ra[s] = load4_at<false>(static_cast<const uint16_t*>(gbase) + (low * qrow + qoff),
+                                        2 * (rr * (uint32_t)qrow + 4 * c4));
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::VPER; ++s) {
+            const int item = tid + s * NT;
+            const int t = item / (BV / 4), c4 = item % (BV / 4);
+            const bool ok = item < Cfg::VITEMS && t < nv;
+            vok |= (ok ? 1u : 0u) << s;
+            const uint32_t rr = ok ? lrow(t, nv) : 0u;
+            rv[s] = load4_at<false>(vb, 2 * (rr * (uint32_t)vrow + 4 * c4));
+            rb[s] = load4_at<false>(gvb, 2 * (rr * (uint32_t)gvrow_r + 4 * c4));
+        }
+    };
+    // Raw words to LDS (zero past the end); nothing is converted here.
+    auto store_chunk = [&]() {
+        const u32x2 z2 = {0u, 0u};
+        const u32x4 z4 = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int s = 0; s < Cfg::KPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::KITEMS) {
+                const int t = item / (DK / 4), c4 = item % (DK / 4);
+                const bool ok = (kok >> s) & 1u;
+                lds_store<u32x2>(SQw + t * SQ + 2 * c4, ok ? u32x2{rq[s][0], rq[s][1]} : z2);
+                lds_store<u32x2>(SKw + t * SQ + 2 * c4, ok ? u32x2{rk[s][0], rk[s][1]} : z2);
+                const bool gok = ok && has_g;  // an absent key gate is staged as zeros
+                if constexpr (GF32) lds_store<u32x4>(SGw + t * SGR + 4 * c4, gok ? ra[s] : z4);
+                else lds_store<u32x2>(SGw + t * SGR + 2 * c4, gok ? u32x2{ra[s][0], ra[s][1]} : z2);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < Cfg::VPER; ++s) {
+            const int item = tid + s * NT;
+            if (item < Cfg::VITEMS) {
+                const int t = item / (BV / 4), c4 = item % (BV / 4);
+                const bool ok = (vok >> s) & 1u;
+                lds_store<u32x2>(SVw + t * SV + 2 * c4, ok ? u32x2{rv[s][0], rv[s][1]} : z2);
+                lds_store<u32x2>(SGVw + t * SV + 2 * c4, ok ? u32x2{rb[s][0], rb[s][1]} : z2);
+            }
+        }
+    };
+
+    if (tid == 0) wide_span[0] = wide_span[1] = 0;
+    if (nch > 0) {
+        load_chunk(0);
+        store_chunk();
+    }
+    if (nch > 1) load_chunk(1);
+    for (int c = 0; c < nch; ++c) {
+        lds_barrier();  // (1) chunk c staged; the previous matrix phase is done
+        if (tid == 0) wide_span[(c + 1) & 1] = 0;  // the next chunk's flag, set in its prep
+        const int nv = chunk_nv(c);
+        // Key prep: channels 2pp, 2pp+1, tokens 4tq .. 4tq+3.
+#pragma unroll
+        for (int r = 0; r < (Cfg::KPREP + NT - 1) / NT; ++r) {
+            const int it = tid + r * NT;
+            if (Cfg::KPREP % NT != 0 && it >= Cfg::KPREP) break;
+            const int pp = it >> 2, tq = it & 3;
+            float la[4][2];
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                const int t = 4 * tq + tau;
+                float g0, g1;
+                if constexpr (GF32) {
+                    const f32x2 g = lds_load<f32x2>(SGw + t * SGR + 2 * pp);
+                    g0 = g[0];
+                    g1 = g[1];
+                } else {
+                    const uint32_t w = SGw[t * SGR + pp];
+                    g0 = bf16_lo(w);
+                    g1 = bf16_hi(w);
+                }
+                const bool tv = t < nv;
+                la[tau][0] = tv ? kLog2e * g0 + gg2 : 0.f;
+                la[tau][1] = tv ? kLog2e * g1 + gg2 : 0.f;
+            }
+            float a[4][2], tot[2];
+            quarter_sums(la, tq, a, tot);
+            const bool wl = !(tot[0] >= -kGSpan) || !(tot[1] >= -kGSpan);
+            if (wl) wide_span[c & 1] = 1;
+            if (tq == 3) {
+                const f32x2 e15 = {hw_exp2(tot[0]), hw_exp2(tot[1])}, one = {1.f, 1.f};
+                lds_store<f32x2>(PREf + 2 * pp, wl ? e15 : one);
+                lds_store<f32x2>(POSTf + 2 * pp, wl ? one : e15);
+            }
+            // kp = k ./ e (narrow pair) or k .* 2^{A_15 - A} (wide pair)
+            const float off[2] = {wl ? tot[0] : 0.f, wl ? tot[1] : 0.f};
+            float qh[4][2], kp[4][2], kl[4][2];
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                const int t = 4 * tq + tau;
+                lds_store<f32x2>(Af + t * AR + 2 * pp, f32x2{a[tau][0], a[tau][1]});
+                const uint32_t qw = SQw[t * SQ + pp], kw = SKw[t * SQ + pp];
+                const float qv[2] = {bf16_lo(qw), bf16_hi(qw)}, kv[2] = {bf16_lo(kw), bf16_hi(kw)};
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    qh[tau][x] = qv[x] * hw_exp2(a[tau][x]);
+                    kp[tau][x] = kv[x] * hw_exp2(off[x] - a[tau][x]);
+                    kl[tau][x] = lo_part(kp[tau][x]);
+                }
+            }
+            const int pd = gpos_dword(pp);
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+                uint32_t* qr = QHw + (4 * tq + tau) * OPR + pd;
+                uint32_t* kr = KPw + (4 * tq + tau) * OPR + pd;
+                qr[0] = hi_pack(qh[tau][0], qh[tau][1]);
+                qr[DK / 2] = lo_pack(qh[tau][0], qh[tau][1]);
+                kr[0] = hi_pack(kp[tau][0], kp[tau][1]);
+                kr[DK / 2] = pack_bf16x2(kl[tau][0], kl[tau][1]);
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+                lds_store<u32x4>(KTw + (2 * pp + x) * TMR + 4 * tq,
+                                 u32x4{hi_pack(kp[0][x], kp[1][x]), hi_pack(kp[2][x], kp[3][x]),
+                                       pack_bf16x2(kl[0][x], kl[1][x]), pack_bf16x2(kl[2][x], kl[3][x])});
+        }
+        // Value prep: columns 2qq, 2qq+1 of the block, tokens 4tq .. 4tq+3; the last
+        // threads take these items (the key prep fills the first ones when the
+        // item counts do not divide evenly).
+#pragma unroll
+        for (int r = 0; r < (Cfg::VPREP + NT - 1) / NT; ++r) {
+            const int it = (NT - 1 - tid) + r * NT;
+            if (Cfg::VPREP % NT != 0 && it >= Cfg::VPREP) break;
+            const int qq = it >> 2, tq = 3 - (it & 3);
+            if (has_gv) {
+                float la[4][2];
+#pragma unroll
+                for (int tau = 0; tau < 4; ++tau) {
+                    const int t = 4 * tq + tau;
+                    const uint32_t w = SGVw[t * SV + qq];
+                    const bool tv = t < nv;
+                    la[tau][0] = tv ? kLog2e * bf16_lo(w) : 0.f;
+                    la[tau][1] = tv ? kLog2e * bf16_hi(w) : 0.f;
+                }
+                float b[4][2], tot[2];
+                quarter_sums(la, tq, b, tot);
+                const bool wl = !(tot[0] >= -kGSpan) || !(tot[1] >= -kGSpan);
+                if (wl) wide_span[c & 1] = 1;
+                const float e15[2] = {hw_exp2(tot[0]), hw_exp2(tot[1])};
+                if (tq == 3) lds_store<f32x2>(EBf + 2 * qq, f32x2{e15[0], e15[1]});
+                float bt[4][2], vp[4][2], vt[4][2];
+#pragma unroll
+                for (int tau = 0; tau < 4; ++tau) {
+                    const int t = 4 * tq + tau;
+                    lds_store<f32x2>(Bf + t * BR + 2 * qq, f32x2{b[tau][0], b[tau][1]});
+                    const uint32_t vw = SVw[t * SV + qq];
+                    const float vv[2] = {bf16_lo(vw), bf16_hi(vw)};
+#pragma unroll
+                    for (int x = 0; x < 2; ++x) {
+                        // wide: v .* 2^{-B} is not needed (and may overflow)
+                        const float e = hw_exp2(b[tau][x]), y = hw_exp2(wl ? tot[x] - b[tau][x] : -b[tau][x]);
+                        bt[tau][x] = e;
+                        vp[tau][x] = wl ? 0.f : vv[x] * y;
+                        vt[tau][x] = wl ? vv[x] * y : vp[tau][x] * e15[x];
+                    }
+                }
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    const int row = (2 * qq + x) * TMR + 4 * tq;
+                    lds_store<f32x4>(BTf + row, f32x4{bt[0][x], bt[1][x], bt[2][x], bt[3][x]});
+                    lds_store<u32x4>(VPw + row, u32x4{hi_pack(vp[0][x], vp[1][x]), hi_pack(vp[2][x], vp[3][x]),
+                                                      lo_pack(vp[0][x], vp[1][x]), lo_pack(vp[2][x], vp[3][x])});
+                    lds_store<u32x4>(VTw + row, u32x4{hi_pack(vt[0][x], vt[1][x]), hi_pack(vt[2][x], vt[3][x]),
+                                                      lo_pack(vt[0][x], vt[1][x]), lo_pack(vt[2][x], vt[3][x])});
+                }
+            } else {  // v is exact in bf16: copy it token-minor, hi only
+                uint32_t w[4];
+#pragma unroll
+                for (int tau = 0; tau < 4; ++tau) w[tau] = SVw[(4 * tq + tau) * SV + qq];
+                lds_store<u32x2>(VTw + (2 * qq) * TMR + 4 * tq, u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                                                                     __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)});
+                lds_store<u32x2>(VTw + (2 * qq + 1) * TMR + 4 * tq,
+                                 u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
+                                       __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)});
+            }
+        }
+        lds_barrier();  // (2) derived operands are in LDS
+        const bool fast = wide_span[c & 1] == 0;
+        if (!fast) {  // exact intra term on the VALU (uniform branch): W, then W (v .* 2^{B_t - B_u})
+            for (int e = tid; e < kGChunk * kGChunk; e += NT) {
+                const int t = e >> 4, u = e & 15;
+                float w = 0.f;
+                if (u <= t) {
+                    const uint32_t* qt = SQw + t * SQ;
+                    const uint32_t* ku = SKw + u * SQ;
+                    const float* at = Af + t * AR;
+                    const float* au = Af + u * AR;
+#pragma unroll 4
+                    for (int i = 0; i < DK; i += 4) {
+                        const u32x2 q2 = lds_load<u32x2>(qt + i / 2), k2 = lds_load<u32x2>(ku + i / 2);
+                        const f32x4 a4 = lds_load<f32x4>(at + i), b4 = lds_load<f32x4>(au + i);
+                        const float q4[4] = {bf16_lo(q2[0]), bf16_hi(q2[0]), bf16_lo(q2[1]), bf16_hi(q2[1])};
+                        const float k4[4] = {bf16_lo(k2[0]), bf16_hi(k2[0]), bf16_lo(k2[1]), bf16_hi(k2[1])};
+#pragma unroll
+                        for (int x = 0; x < 4; ++x) w += q4[x] * k4[x] * hw_exp2(a4[x] - b4[x]);
+                    }
+                }
+                Wf[t * 17 + u] = w;
+            }
+            lds_barrier();
+            for (int e = tid; e < kGChunk * BV; e += NT) {
+                const int t = e / BV, jj = e % BV;
+                const float bt = has_gv ? Bf[t * BR + jj] : 0.f;
+                float acc = 0.f;
+                for (int u = 0; u <= t; ++u) {
+                    const float vu = bf16_half(SVw[u * SV + (jj >> 1)], jj & 1);
+                    const float d = has_gv ? hw_exp2(bt - Bf[u * BR + jj]) : 1.f;
+                    acc += Wf[t * 17 + u] * vu * d;
+                }
+                OIf[t * BR + jj] = acc;
+            }
+            lds_barrier();
+        }
+        if (c + 1 < nch) {
+            store_chunk();  // chunk c + 1; the staged arrays are read only before here
+            if (c + 2 < nch) load_chunk(c + 2);
+        }
+
+        // Inter-chunk part (q .* 2^A) S: the state tile pair (2s, 2s+1), split into
+        // bf16 hi + lo, is the B operand of dk block s.  Fast path: W^T = (k ./ e)
+        // (q .* e)^T in the same loop (q .* e is its B operand too); lane holds
+        // W[t = lr][u = 4lg + ii].
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 O;
+        if (fast) {
+            f32x4 Oa = z, Ob = z, Oc = z, Wa = z, Wb = z, Wc = z;
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                const uint32_t* qr = QHw + lr * OPR + 16 * s + 4 * lg;
+                const uint32_t* kr = KPw + lr * OPR + 16 * s + 4 * lg;
+                const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
+                const u32x4 kh = lds_load<u32x4>(kr), kl = lds_load<u32x4>(kr + DK / 2);
+                const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
+                const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
+                                  hi_pack(s1[2], s1[3])};
+                const u32x4 sl = {lo_pack(s0[0], s0[1]), lo_pack(s0[2], s0[3]), lo_pack(s1[0], s1[1]),
+                                  lo_pack(s1[2], s1[3])};
+                Oa = mfma_bf16_w(qh, sh, Oa);
+                Wa = mfma_bf16_w(kh, qh, Wa);
+                Ob = mfma_bf16_w(qh, sl, Ob);
+                Wb = mfma_bf16_w(kh, ql, Wb);
+                Oc = mfma_bf16_w(ql, sh, Oc);
+                Wc = mfma_bf16_w(kl, qh, Wc);
+            }
+            O = (Oa + Ob) + Oc;
+            f32x4 W = (Wa + Wb) + Wc;
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                if (4 * lg + ii > lr) W[ii] = 0.f;  // causal: u <= t
+            // Intra term W (v .* 2^{-B}): k = 8lg + e covers the tokens 4lg + (e & 3)
+            // with W's hi (e < 4) and lo (e >= 4) parts, against v's hi part twice.
+            const u32x4 vpx = lds_load<u32x4>((has_gv ? VPw : VTw) + j * TMR + 4 * lg);
+            const u32x4 wa = {hi_pack(W[0], W[1]), hi_pack(W[2], W[3]), lo_pack(W[0], W[1]), lo_pack(W[2], W[3])};
+            f32x4 Oi = mfma_bf16_w(wa, u32x4{vpx[0], vpx[1], vpx[0], vpx[1]}, z);
+            if (has_gv) Oi = mfma_bf16_half(wa[0], wa[1], vpx[2], vpx[3], Oi);
+            O += Oi;
+            if (has_gv) O *= lds_load<f32x4>(BTf + j * TMR + 4 * lg);
+        } else {
+            f32x4 Oa = z, Ob = z, Oc = z;
+#pragma unroll
+            for (int s = 0; s < KB; ++s) {
+                const uint32_t* qr = QHw + lr * OPR + 16 * s + 4 * lg;
+                const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
+                const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
+                const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
+                                  hi_pack(s1[2], s1[3])};
+                const u32x4 sl = {lo_pack(s0[0], s0[1]), lo_pack(s0[2], s0[3]), lo_pack(s1[0], s1[1]),
+                                  lo_pack(s1[2], s1[3])};
+                Oa = mfma_bf16_w(qh, sh, Oa);
+                Ob = mfma_bf16_w(qh, sl, Ob);
+                Oc = mfma_bf16_w(ql, sh, Oc);
+            }
+            O = (Oa + Ob) + Oc;
+            if (has_gv) O *= lds_load<f32x4>(BTf + j * TMR + 4 * lg);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) O[ii] += OIf[(4 * lg + ii) * BR + j];
+        }
+        {
+            const int64_t orow = (int64_t)H * dv;
+            char* ob = reinterpret_cast<char*>(p.o + (chunk_low(c, nv) * orow + (int64_t)wk.h * dv + wk.vb * BV));
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int t = 4 * lg + ii;
+                if (t < nv) *reinterpret_cast<float*>(ob + 4 * (lrow(t, nv) * (uint32_t)orow + j)) = p.scale * O[ii];
+            }
+        }
+
+        // State update: S <- post .* (pre .* 2^{B_15}^T .* S + kp^T vt), contracting
+        // over the 16 tokens with kp's hi and lo parts in one k range (token-minor
+        // operands: lane group lg reads tokens 4lg .. 4lg+3).
+        const float eb = has_gv ? EBf[j] : 1.f;
+        if (!fast) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) {
+                const f32x4 pre = lds_load<f32x4>(PREf + 16 * mt + 4 * lg);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= pre[ii] * eb;
+            }
+        } else if (has_gv) {
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) S[mt] *= eb;
+        }
+        const u32x4 vtx = lds_load<u32x4>(VTw + j * TMR + 4 * lg);
+        const u32x4 vt2 = {vtx[0], vtx[1], vtx[0], vtx[1]};
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const u32x4 ktx = lds_load<u32x4>(KTw + (16 * mt + lr) * TMR + 4 * lg);
+            S[mt] = mfma_bf16_w(ktx, vt2, S[mt]);
+            if (has_gv) S[mt] = mfma_bf16_half(ktx[0], ktx[1], vtx[2], vtx[3], S[mt]);
+        }
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            const f32x4 post = lds_load<f32x4>(POSTf + 16 * mt + 4 * lg);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= post[ii];
+        }
+    }
+
+    if (p.final_state) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = S[mt][ii];
+    }
+}
+
 // Four consecutive input elements as floats (bf16 words or fp32).
 template <bool BF16>
 __device__ inline f32x4 load4(const void* base, int64_t i) {
@@ -1554,9 +2113,9 @@ template <int DK, int NW>
 hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
     const dim3 grid(fwd_grid_size(p)), block(64 * NW);
     if (bf16 && p.gk_is_f32)
-        hipLaunchKernelGGL((gated_kernel<DK, NW, true, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true>), grid, block, 0, s, p);
     else if (bf16)
-        hipLaunchKernelGGL((gated_kernel<DK, NW, true, false>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, false>), grid, block, 0, s, p);
     else
         hipLaunchKernelGGL((gated_kernel<DK, NW, false, true>), grid, block, 0, s, p);
     return hipGetLastError();

@@ -161,8 +161,11 @@ int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* 
  *   gv             device [B, T, H, dv] in in_dtype (per value channel), or NULL.
  *   g_gamma        device float32 [H] or NULL (zeros).  All gates must be finite and <= 0.
  *   the rest       as for lattn_fwd (GQA, reverse, packed input, states).
- * Computed in fp32 throughout (chunks of 16 tokens).  Supported: in_dtype BF16 or F32,
- * dk in {32, 64, 128}, dv a multiple of 16 up to 256, out_dtype F32.  Workspace:
+ * Chunks of 16 tokens; fp32 inputs are computed in fp32 (fp32 MFMA), bf16 inputs on
+ * bf16 MFMA with every decayed operand split into bf16 hi + lo parts (fp32
+ * accumulation; about 1e-4 relative to the output RMS).  Supported: in_dtype BF16 or
+ * F32, dk in {32, 64, 128}, dv a multiple of 16 up to 256, out_dtype F32, and
+ * H * max(dk, dv) < 2^25.  Workspace:
  * lattn_fwd_gated_workspace_size(p, gates) with gates the LATTN_GATE_* bits of the
  * gates that will be passed: the sequence order of packed input, and an fp32
  * [B, T, H, dk] sum when both g and gk are given; else 0.
