@@ -1260,14 +1260,22 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
 // stores k .* 2^{A_15 - A_u} instead and moves its factor 2^{A_15} in front of S
 // (per-row factors pre and post); a chunk holding one takes the exact VALU path of
 // gated_kernel for W and the intra term.
-// Prep: one item (channel pair, quarter of the chunk) per lane, the four quarters
-// of a pair in one lane quad; each quarter sums its four decays and the quad
+//
+// Roles: a workgroup of 2 NW waves.  Waves 0 .. NW-1 (matrix waves) own 16 value
+// columns each and the state in accumulator registers; waves NW .. 2NW-1 (producer
+// waves) stage the chunks from global memory and derive the decayed operands.  With
+// one wave of each role per SIMD, the prep of chunk c+1 runs while the matrix waves
+// compute chunk c.  LDS holds two staged raw chunks and two sets of decayed
+// operands; one barrier per chunk hands both over.
+// Prep: one item (channel pair, quarter of the chunk) per producer lane, the four
+// quarters of a pair in one lane quad; each quarter sums its four decays and the quad
 // exchanges the partial sums (DPP), so every lane has its tokens' A_t and A_15.
 // ---------------------------------------------------------------------------
 template <int DK, int NW>
 struct GatedBCfg {
     static constexpr int BV = 16 * NW;
-    static constexpr int NT = 64 * NW;
+    static constexpr int PT = 64 * NW;  // producer threads
+    static constexpr int NT = 2 * PT;   // all threads
     static constexpr int MT = DK / 16;
     static constexpr int KB = DK / 32;  // 32-deep blocks of the dk contraction
     // Dwords per row.  Staged raw chunk (token-major): q, k and a bf16 key gate;
@@ -1280,36 +1288,44 @@ struct GatedBCfg {
     // of pad (16-byte blocks per row = 2 mod 32: conflict-free operand reads).
     static constexpr int OPR = DK + 8;
     // Token-minor rows (a row per channel): four 16-byte blocks of four tokens,
-    // [hi x4 | lo x4] in bf16 or four fp32, then two blocks of pad.
+    // [hi x4 | lo x4] in bf16 or four fp32.  Key rows carry two blocks of pad; value
+    // rows swizzle their blocks instead (vblk).
     static constexpr int TMR = 24;
+    static constexpr int VMR = 16;
     // fp32 summed decays for the exact path (token-major).
     static constexpr int AR = DK + 4, BR = BV + 4;
-    static constexpr int OFF_SQ = 0;
-    static constexpr int OFF_SK = OFF_SQ + kGChunk * SQ;
-    static constexpr int OFF_SG = OFF_SK + kGChunk * SQ;  // bf16 or fp32 key gate
-    static constexpr int OFF_SV = OFF_SG + kGChunk * SG32;
-    static constexpr int OFF_SGV = OFF_SV + kGChunk * SV;
-    static constexpr int OFF_QH = OFF_SGV + kGChunk * SV;
-    static constexpr int OFF_KP = OFF_QH + kGChunk * OPR;
-    static constexpr int OFF_KT = OFF_KP + kGChunk * OPR;
-    static constexpr int OFF_VP = OFF_KT + DK * TMR;
-    static constexpr int OFF_VT = OFF_VP + BV * TMR;
-    static constexpr int OFF_BT = OFF_VT + BV * TMR;
-    static constexpr int OFF_A = OFF_BT + BV * TMR;
+    // One staged raw chunk.
+    static constexpr int ST_Q = 0;
+    static constexpr int ST_K = ST_Q + kGChunk * SQ;
+    static constexpr int ST_G = ST_K + kGChunk * SQ;  // bf16 or fp32 key gate
+    static constexpr int ST_V = ST_G + kGChunk * SG32;
+    static constexpr int ST_GV = ST_V + kGChunk * SV;
+    static constexpr int ST_SIZE = ST_GV + kGChunk * SV;
+    // One set of decayed operands.
+    static constexpr int D_QH = 0;
+    static constexpr int D_KP = D_QH + kGChunk * OPR;
+    static constexpr int D_KT = D_KP + kGChunk * OPR;
+    static constexpr int D_VP = D_KT + DK * TMR;
+    static constexpr int D_VT = D_VP + BV * VMR;
+    static constexpr int D_BT = D_VT + BV * VMR;
+    static constexpr int D_PRE = D_BT + BV * VMR;
+    static constexpr int D_POST = D_PRE + DK;
+    static constexpr int D_EB = D_POST + DK;
+    static constexpr int D_SIZE = D_EB + BV;
+    static constexpr int OFF_ST = 0;
+    static constexpr int OFF_D = OFF_ST + 2 * ST_SIZE;
+    static constexpr int OFF_A = OFF_D + 2 * D_SIZE;
     static constexpr int OFF_B = OFF_A + kGChunk * AR;
     static constexpr int OFF_OI = OFF_B + kGChunk * BR;
     static constexpr int OFF_W = OFF_OI + kGChunk * BR;
-    static constexpr int OFF_PRE = OFF_W + kGChunk * 17;
-    static constexpr int OFF_POST = OFF_PRE + DK;
-    static constexpr int OFF_EB = OFF_POST + DK;
-    static constexpr int DWORDS = OFF_EB + BV;
-    // Staging: 4-element pieces of a chunk, spread over all threads.
+    static constexpr int DWORDS = OFF_W + kGChunk * 17;
+    // Staging: 4-element pieces of a chunk, spread over the producer threads.
     static constexpr int KITEMS = kGChunk * DK / 4, VITEMS = kGChunk * BV / 4;
-    static constexpr int KPER = (KITEMS + NT - 1) / NT, VPER = (VITEMS + NT - 1) / NT;
+    static constexpr int KPER = (KITEMS + PT - 1) / PT, VPER = (VITEMS + PT - 1) / PT;
     // Prep items: channel pairs x quarters.
     static constexpr int KPREP = 2 * DK, VPREP = 2 * BV;
     static_assert(DK % 32 == 0 && DK <= 128, "dk must be 32, 64 or 128");
-    static_assert(OFF_PRE % 4 == 0 && OFF_POST % 4 == 0 && OFF_QH % 4 == 0 && OFF_KT % 4 == 0 && OFF_A % 4 == 0,
+    static_assert(ST_SIZE % 4 == 0 && D_SIZE % 4 == 0 && OFF_A % 4 == 0 && OFF_OI % 4 == 0 && D_PRE % 4 == 0,
                   "16-byte alignment");
     static_assert(DWORDS * 4 <= kLdsBudget, "LDS budget");
 };
@@ -1356,6 +1372,10 @@ __device__ inline float quad_get(float x) {
 __host__ __device__ constexpr int gpos_dword(int pp) {
     return 16 * (pp >> 4) + 4 * ((pp >> 1) & 3) + 2 * ((pp >> 3) & 1) + (pp & 1);
 }
+// Dword offset of block b (tokens 4b .. 4b+3) of value row r: the blocks of rows
+// 8 .. 15 mod 16 are swapped in pairs, so the 32 lanes of a half-wave reading
+// (row, block lg) hit distinct banks.
+__host__ __device__ constexpr int vblk(int r, int b) { return 16 * r + 4 * (b ^ ((r >> 2) & 2)); }
 // Inclusive sums of a quarter's log2-decays (la, per token and channel) over the
 // chunk: the lane quad holds the four quarters of a channel pair.  a = A_t of this
 // quarter's tokens, tot = A_15.
@@ -1380,53 +1400,38 @@ __device__ inline void quarter_sums(const float (&la)[4][2], int tq, float (&a)[
 }
 
 template <int DK, int NW, bool GF32>
-__global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams p) {
     using Cfg = GatedBCfg<DK, NW>;
-    constexpr int BV = Cfg::BV, NT = Cfg::NT, MT = Cfg::MT, KB = Cfg::KB;
+    constexpr int BV = Cfg::BV, NT = Cfg::NT, PT = Cfg::PT, MT = Cfg::MT, KB = Cfg::KB;
     constexpr int SQ = Cfg::SQ, SV = Cfg::SV, OPR = Cfg::OPR, TMR = Cfg::TMR, AR = Cfg::AR, BR = Cfg::BR;
     constexpr int SGR = GF32 ? Cfg::SG32 : SQ;  // row stride of the staged key gate
     __shared__ __attribute__((aligned(16))) uint32_t sm[Cfg::DWORDS];
-    __shared__ int wide_span[2];  // per chunk parity: take the exact VALU path
-    uint32_t* SQw = sm + Cfg::OFF_SQ;
-    uint32_t* SKw = sm + Cfg::OFF_SK;
-    uint32_t* SGw = sm + Cfg::OFF_SG;
-    uint32_t* SVw = sm + Cfg::OFF_SV;
-    uint32_t* SGVw = sm + Cfg::OFF_SGV;
-    uint32_t* QHw = sm + Cfg::OFF_QH;
-    uint32_t* KPw = sm + Cfg::OFF_KP;
-    uint32_t* KTw = sm + Cfg::OFF_KT;
-    uint32_t* VPw = sm + Cfg::OFF_VP;
-    uint32_t* VTw = sm + Cfg::OFF_VT;
-    float* BTf = reinterpret_cast<float*>(sm + Cfg::OFF_BT);
+    __shared__ int wide_flag[3];  // per chunk mod 3: take the exact VALU path
     float* Af = reinterpret_cast<float*>(sm + Cfg::OFF_A);
     float* Bf = reinterpret_cast<float*>(sm + Cfg::OFF_B);
     float* OIf = reinterpret_cast<float*>(sm + Cfg::OFF_OI);
     float* Wf = reinterpret_cast<float*>(sm + Cfg::OFF_W);
-    float* PREf = reinterpret_cast<float*>(sm + Cfg::OFF_PRE);
-    float* POSTf = reinterpret_cast<float*>(sm + Cfg::OFF_POST);
-    float* EBf = reinterpret_cast<float*>(sm + Cfg::OFF_EB);
+    auto staged = [&](int c) -> uint32_t* { return sm + Cfg::OFF_ST + (c & 1) * Cfg::ST_SIZE; };
+    auto derived = [&](int c) -> uint32_t* { return sm + Cfg::OFF_D + (c & 1) * Cfg::D_SIZE; };
 
     Work wk;
     if (!decode_work(p, wk)) return;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool producer = wv >= NW;
+    const int ptid = tid - PT;  // producer thread index
     const int H = p.num_heads, dv = p.dv;
     const int64_t L = wk.len;
     const int nch = (int)((L + kGChunk - 1) / kGChunk);
     const bool rev = p.reverse_gated != 0;
     const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
     const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
-    const int j = 16 * wv + lr;       // this lane's column inside the block
+    const int j = 16 * wv + lr;       // matrix waves: this lane's column inside the block
     const int vcol = wk.vb * BV + j;  // ... of v and o
     const int64_t qrow = (int64_t)H * DK, krow = (int64_t)p.num_kv_heads * DK;
     const int64_t vrow = (int64_t)p.num_kv_heads * dv, gvrow = (int64_t)H * dv;
     const int64_t qoff = (int64_t)wk.h * DK, koff = (int64_t)wk.kvh * DK;
     const int64_t voff = (int64_t)wk.kvh * dv + wk.vb * BV, gvoff = (int64_t)wk.h * dv + wk.vb * BV;
-    // Absent gates read an element of an array with the same layout (q for the key
-    // gate, v itself for the value gate) and are never used.
-    const void* gbase = has_g ? p.g : p.q;
-    const void* gvbase = has_gv ? p.gv : p.v;
-    const int64_t gvrow_r = has_gv ? gvrow : vrow, gvoff_r = has_gv ? gvoff : voff;
     // Chunk c holds the rows [low, low + nv) of the flattened token axis (in either
     // direction); token t of the chunk is row low + lrow(t).  Offsets inside a chunk
     // stay 32-bit (the host bounds 16 rows of every array below 2^31 bytes).
@@ -1439,16 +1444,17 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
 
     f32x4 S[MT];
     const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
+    if (!producer) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
-    // The state is in registers before the loop: inside it, the only loads in flight
-    // are the staging prefetches, which the matrix phase then never waits for.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            for (int ii = 0; ii < 4; ++ii)
+                S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
+    }
 
-    // Staging registers: raw words of this thread's pieces (bf16: words 0 and 1).
+    // Producer staging registers: raw words of this thread's pieces (bf16: words 0
+    // and 1), loaded one chunk ahead of their store to LDS.  Absent gates are not
+    // loaded and are staged as zeros.
     u32x4 rq[Cfg::KPER], rk[Cfg::KPER], ra[Cfg::KPER], rv[Cfg::VPER], rb[Cfg::VPER];
     uint32_t kok = 0, vok = 0;  // bit s: piece s lies inside the sequence
     auto load_chunk = [&](int c) {
@@ -1457,79 +1463,80 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
         const uint16_t* qb = static_cast<const uint16_t*>(p.q) + (low * qrow + qoff);
         const uint16_t* kb = static_cast<const uint16_t*>(p.k) + (low * krow + koff);
         const uint16_t* vb = static_cast<const uint16_t*>(p.v) + (low * vrow + voff);
-        const uint16_t* gvb = static_cast<const uint16_t*>(gvbase) + (low * gvrow_r + gvoff_r);
         kok = vok = 0;
 #pragma unroll
         for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = tid + s * NT;
+            const int item = ptid + s * PT;
             const int t = item / (DK / 4), c4 = item % (DK / 4);
             const bool ok = item < Cfg::KITEMS && t < nv;
             kok |= (ok ? 1u : 0u) << s;
             const uint32_t rr = ok ? lrow(t, nv) : 0u;  // rows past the end read row 0
             rq[s] = load4_at<false>(qb, 2 * (rr * (uint32_t)qrow + 4 * c4));
             rk[s] = load4_at<false>(kb, 2 * (rr * (uint32_t)krow + 4 * c4));
-            if constexpr (GF32)
-                ra[s] = load4_at<true>(static_cast<const float*>(gbase) + (low * qrow + qoff),
-                                       4 * (rr * (uint32_t)qrow + 4 * c4));
-            else
-                ra[s] = load4_at<false>(static_cast<const uint16_t*>(gbase) + (low * qrow + qoff),
-                                        2 * (rr * (uint32_t)qrow + 4 * c4));
+            if (has_g) {
+                if constexpr (GF32)
+                    ra[s] = load4_at<true>(static_cast<const float*>(p.g) + (low * qrow + qoff),
+                                           4 * (rr * (uint32_t)qrow + 4 * c4));
+                else
+                    ra[s] = load4_at<false>(static_cast<const uint16_t*>(p.g) + (low * qrow + qoff),
+                                            2 * (rr * (uint32_t)qrow + 4 * c4));
+            }
         }
 #pragma unroll
         for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = tid + s * NT;
+            const int item = ptid + s * PT;
             const int t = item / (BV / 4), c4 = item % (BV / 4);
             const bool ok = item < Cfg::VITEMS && t < nv;
             vok |= (ok ? 1u : 0u) << s;
             const uint32_t rr = ok ? lrow(t, nv) : 0u;
             rv[s] = load4_at<false>(vb, 2 * (rr * (uint32_t)vrow + 4 * c4));
-            rb[s] = load4_at<false>(gvb, 2 * (rr * (uint32_t)gvrow_r + 4 * c4));
+            if (has_gv)
+                rb[s] = load4_at<false>(static_cast<const uint16_t*>(p.gv) + (low * gvrow + gvoff),
+                                        2 * (rr * (uint32_t)gvrow + 4 * c4));
         }
     };
     // Raw words to LDS (zero past the end); nothing is converted here.
-    auto store_chunk = [&]() {
+    auto store_chunk = [&](int c) {
+        uint32_t* st = staged(c);
         const u32x2 z2 = {0u, 0u};
         const u32x4 z4 = {0u, 0u, 0u, 0u};
 #pragma unroll
         for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = tid + s * NT;
+            const int item = ptid + s * PT;
             if (item < Cfg::KITEMS) {
                 const int t = item / (DK / 4), c4 = item % (DK / 4);
                 const bool ok = (kok >> s) & 1u;
-                lds_store<u32x2>(SQw + t * SQ + 2 * c4, ok ? u32x2{rq[s][0], rq[s][1]} : z2);
-                lds_store<u32x2>(SKw + t * SQ + 2 * c4, ok ? u32x2{rk[s][0], rk[s][1]} : z2);
-                const bool gok = ok && has_g;  // an absent key gate is staged as zeros
-                if constexpr (GF32) lds_store<u32x4>(SGw + t * SGR + 4 * c4, gok ? ra[s] : z4);
-                else lds_store<u32x2>(SGw + t * SGR + 2 * c4, gok ? u32x2{ra[s][0], ra[s][1]} : z2);
+                lds_store<u32x2>(st + Cfg::ST_Q + t * SQ + 2 * c4, ok ? u32x2{rq[s][0], rq[s][1]} : z2);
+                lds_store<u32x2>(st + Cfg::ST_K + t * SQ + 2 * c4, ok ? u32x2{rk[s][0], rk[s][1]} : z2);
+                const bool gok = ok && has_g;
+                if constexpr (GF32) lds_store<u32x4>(st + Cfg::ST_G + t * SGR + 4 * c4, gok ? ra[s] : z4);
+                else lds_store<u32x2>(st + Cfg::ST_G + t * SGR + 2 * c4, gok ? u32x2{ra[s][0], ra[s][1]} : z2);
             }
         }
 #pragma unroll
         for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = tid + s * NT;
+            const int item = ptid + s * PT;
             if (item < Cfg::VITEMS) {
                 const int t = item / (BV / 4), c4 = item % (BV / 4);
                 const bool ok = (vok >> s) & 1u;
-                lds_store<u32x2>(SVw + t * SV + 2 * c4, ok ? u32x2{rv[s][0], rv[s][1]} : z2);
-                lds_store<u32x2>(SGVw + t * SV + 2 * c4, ok ? u32x2{rb[s][0], rb[s][1]} : z2);
+                lds_store<u32x2>(st + Cfg::ST_V + t * SV + 2 * c4, ok ? u32x2{rv[s][0], rv[s][1]} : z2);
+                if (has_gv) lds_store<u32x2>(st + Cfg::ST_GV + t * SV + 2 * c4, ok ? u32x2{rb[s][0], rb[s][1]} : z2);
             }
         }
     };
 
-    if (tid == 0) wide_span[0] = wide_span[1] = 0;
-    if (nch > 0) {
-        load_chunk(0);
-        store_chunk();
-    }
-    if (nch > 1) load_chunk(1);
-    for (int c = 0; c < nch; ++c) {
-        lds_barrier();  // (1) chunk c staged; the previous matrix phase is done
-        if (tid == 0) wide_span[(c + 1) & 1] = 0;  // the next chunk's flag, set in its prep
+    // Prep of chunk c (producer waves): staged(c) -> derived(c), the summed decays
+    // (exact path) and the chunk's flag.
+    auto prep_chunk = [&](int c) {
+        const uint32_t* st = staged(c);
+        uint32_t* d = derived(c);
         const int nv = chunk_nv(c);
-        // Key prep: channels 2pp, 2pp+1, tokens 4tq .. 4tq+3.
+        int* flag = &wide_flag[c % 3];
+        // Key channels 2pp, 2pp+1, tokens 4tq .. 4tq+3.
 #pragma unroll
-        for (int r = 0; r < (Cfg::KPREP + NT - 1) / NT; ++r) {
-            const int it = tid + r * NT;
-            if (Cfg::KPREP % NT != 0 && it >= Cfg::KPREP) break;
+        for (int r = 0; r < (Cfg::KPREP + PT - 1) / PT; ++r) {
+            const int it = ptid + r * PT;
+            if (Cfg::KPREP % PT != 0 && it >= Cfg::KPREP) break;
             const int pp = it >> 2, tq = it & 3;
             float la[4][2];
 #pragma unroll
@@ -1537,11 +1544,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
                 const int t = 4 * tq + tau;
                 float g0, g1;
                 if constexpr (GF32) {
-                    const f32x2 g = lds_load<f32x2>(SGw + t * SGR + 2 * pp);
+                    const f32x2 g = lds_load<f32x2>(st + Cfg::ST_G + t * SGR + 2 * pp);
                     g0 = g[0];
                     g1 = g[1];
                 } else {
-                    const uint32_t w = SGw[t * SGR + pp];
+                    const uint32_t w = st[Cfg::ST_G + t * SGR + pp];
                     g0 = bf16_lo(w);
                     g1 = bf16_hi(w);
                 }
@@ -1552,11 +1559,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
             float a[4][2], tot[2];
             quarter_sums(la, tq, a, tot);
             const bool wl = !(tot[0] >= -kGSpan) || !(tot[1] >= -kGSpan);
-            if (wl) wide_span[c & 1] = 1;
+            if (wl) *flag = 1;
             if (tq == 3) {
                 const f32x2 e15 = {hw_exp2(tot[0]), hw_exp2(tot[1])}, one = {1.f, 1.f};
-                lds_store<f32x2>(PREf + 2 * pp, wl ? e15 : one);
-                lds_store<f32x2>(POSTf + 2 * pp, wl ? one : e15);
+                lds_store<f32x2>(d + Cfg::D_PRE + 2 * pp, wl ? e15 : one);
+                lds_store<f32x2>(d + Cfg::D_POST + 2 * pp, wl ? one : e15);
             }
             // kp = k ./ e (narrow pair) or k .* 2^{A_15 - A} (wide pair)
             const float off[2] = {wl ? tot[0] : 0.f, wl ? tot[1] : 0.f};
@@ -1565,7 +1572,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
             for (int tau = 0; tau < 4; ++tau) {
                 const int t = 4 * tq + tau;
                 lds_store<f32x2>(Af + t * AR + 2 * pp, f32x2{a[tau][0], a[tau][1]});
-                const uint32_t qw = SQw[t * SQ + pp], kw = SKw[t * SQ + pp];
+                const uint32_t qw = st[Cfg::ST_Q + t * SQ + pp], kw = st[Cfg::ST_K + t * SQ + pp];
                 const float qv[2] = {bf16_lo(qw), bf16_hi(qw)}, kv[2] = {bf16_lo(kw), bf16_hi(kw)};
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
@@ -1577,8 +1584,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
             const int pd = gpos_dword(pp);
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
-                uint32_t* qr = QHw + (4 * tq + tau) * OPR + pd;
-                uint32_t* kr = KPw + (4 * tq + tau) * OPR + pd;
+                uint32_t* qr = d + Cfg::D_QH + (4 * tq + tau) * OPR + pd;
+                uint32_t* kr = d + Cfg::D_KP + (4 * tq + tau) * OPR + pd;
                 qr[0] = hi_pack(qh[tau][0], qh[tau][1]);
                 qr[DK / 2] = lo_pack(qh[tau][0], qh[tau][1]);
                 kr[0] = hi_pack(kp[tau][0], kp[tau][1]);
@@ -1586,24 +1593,24 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
             }
 #pragma unroll
             for (int x = 0; x < 2; ++x)
-                lds_store<u32x4>(KTw + (2 * pp + x) * TMR + 4 * tq,
+                lds_store<u32x4>(d + Cfg::D_KT + (2 * pp + x) * TMR + 4 * tq,
                                  u32x4{hi_pack(kp[0][x], kp[1][x]), hi_pack(kp[2][x], kp[3][x]),
                                        pack_bf16x2(kl[0][x], kl[1][x]), pack_bf16x2(kl[2][x], kl[3][x])});
         }
-        // Value prep: columns 2qq, 2qq+1 of the block, tokens 4tq .. 4tq+3; the last
-        // threads take these items (the key prep fills the first ones when the
-        // item counts do not divide evenly).
+        // Value columns 2qq, 2qq+1 of the block, tokens 4tq .. 4tq+3; the last
+        // producer threads take these items (the key prep fills the first ones when
+        // the item counts do not divide evenly).
 #pragma unroll
-        for (int r = 0; r < (Cfg::VPREP + NT - 1) / NT; ++r) {
-            const int it = (NT - 1 - tid) + r * NT;
-            if (Cfg::VPREP % NT != 0 && it >= Cfg::VPREP) break;
+        for (int r = 0; r < (Cfg::VPREP + PT - 1) / PT; ++r) {
+            const int it = (PT - 1 - ptid) + r * PT;
+            if (Cfg::VPREP % PT != 0 && it >= Cfg::VPREP) break;
             const int qq = it >> 2, tq = 3 - (it & 3);
             if (has_gv) {
                 float la[4][2];
 #pragma unroll
                 for (int tau = 0; tau < 4; ++tau) {
                     const int t = 4 * tq + tau;
-                    const uint32_t w = SGVw[t * SV + qq];
+                    const uint32_t w = st[Cfg::ST_GV + t * SV + qq];
                     const bool tv = t < nv;
                     la[tau][0] = tv ? kLog2e * bf16_lo(w) : 0.f;
                     la[tau][1] = tv ? kLog2e * bf16_hi(w) : 0.f;
@@ -1611,15 +1618,15 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
                 float b[4][2], tot[2];
                 quarter_sums(la, tq, b, tot);
                 const bool wl = !(tot[0] >= -kGSpan) || !(tot[1] >= -kGSpan);
-                if (wl) wide_span[c & 1] = 1;
+                if (wl) *flag = 1;
                 const float e15[2] = {hw_exp2(tot[0]), hw_exp2(tot[1])};
-                if (tq == 3) lds_store<f32x2>(EBf + 2 * qq, f32x2{e15[0], e15[1]});
+                if (tq == 3) lds_store<f32x2>(d + Cfg::D_EB + 2 * qq, f32x2{e15[0], e15[1]});
                 float bt[4][2], vp[4][2], vt[4][2];
 #pragma unroll
                 for (int tau = 0; tau < 4; ++tau) {
                     const int t = 4 * tq + tau;
                     lds_store<f32x2>(Bf + t * BR + 2 * qq, f32x2{b[tau][0], b[tau][1]});
-                    const uint32_t vw = SVw[t * SV + qq];
+                    const uint32_t vw = st[Cfg::ST_V + t * SV + qq];
                     const float vv[2] = {bf16_lo(vw), bf16_hi(vw)};
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
@@ -1632,72 +1639,80 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
                 }
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
-                    const int row = (2 * qq + x) * TMR + 4 * tq;
-                    lds_store<f32x4>(BTf + row, f32x4{bt[0][x], bt[1][x], bt[2][x], bt[3][x]});
-                    lds_store<u32x4>(VPw + row, u32x4{hi_pack(vp[0][x], vp[1][x]), hi_pack(vp[2][x], vp[3][x]),
-                                                      lo_pack(vp[0][x], vp[1][x]), lo_pack(vp[2][x], vp[3][x])});
-                    lds_store<u32x4>(VTw + row, u32x4{hi_pack(vt[0][x], vt[1][x]), hi_pack(vt[2][x], vt[3][x]),
-                                                      lo_pack(vt[0][x], vt[1][x]), lo_pack(vt[2][x], vt[3][x])});
+                    const int row = vblk(2 * qq + x, tq);
+                    lds_store<f32x4>(reinterpret_cast<float*>(d + Cfg::D_BT) + row,
+                                     f32x4{bt[0][x], bt[1][x], bt[2][x], bt[3][x]});
+                    lds_store<u32x4>(d + Cfg::D_VP + row, u32x4{hi_pack(vp[0][x], vp[1][x]), hi_pack(vp[2][x], vp[3][x]),
+                                                               lo_pack(vp[0][x], vp[1][x]), lo_pack(vp[2][x], vp[3][x])});
+                    lds_store<u32x4>(d + Cfg::D_VT + row, u32x4{hi_pack(vt[0][x], vt[1][x]), hi_pack(vt[2][x], vt[3][x]),
+                                                               lo_pack(vt[0][x], vt[1][x]), lo_pack(vt[2][x], vt[3][x])});
                 }
             } else {  // v is exact in bf16: copy it token-minor, hi only
                 uint32_t w[4];
 #pragma unroll
-                for (int tau = 0; tau < 4; ++tau) w[tau] = SVw[(4 * tq + tau) * SV + qq];
-                lds_store<u32x2>(VTw + (2 * qq) * TMR + 4 * tq, u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
-                                                                     __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)});
-                lds_store<u32x2>(VTw + (2 * qq + 1) * TMR + 4 * tq,
+                for (int tau = 0; tau < 4; ++tau) w[tau] = st[Cfg::ST_V + (4 * tq + tau) * SV + qq];
+                lds_store<u32x2>(d + Cfg::D_VT + vblk(2 * qq, tq), u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                                                                       __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)});
+                lds_store<u32x2>(d + Cfg::D_VT + vblk(2 * qq + 1, tq),
                                  u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
                                        __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)});
             }
         }
-        lds_barrier();  // (2) derived operands are in LDS
-        const bool fast = wide_span[c & 1] == 0;
-        if (!fast) {  // exact intra term on the VALU (uniform branch): W, then W (v .* 2^{B_t - B_u})
-            for (int e = tid; e < kGChunk * kGChunk; e += NT) {
-                const int t = e >> 4, u = e & 15;
-                float w = 0.f;
-                if (u <= t) {
-                    const uint32_t* qt = SQw + t * SQ;
-                    const uint32_t* ku = SKw + u * SQ;
-                    const float* at = Af + t * AR;
-                    const float* au = Af + u * AR;
-#pragma unroll 4
-                    for (int i = 0; i < DK; i += 4) {
-                        const u32x2 q2 = lds_load<u32x2>(qt + i / 2), k2 = lds_load<u32x2>(ku + i / 2);
-                        const f32x4 a4 = lds_load<f32x4>(at + i), b4 = lds_load<f32x4>(au + i);
-                        const float q4[4] = {bf16_lo(q2[0]), bf16_hi(q2[0]), bf16_lo(q2[1]), bf16_hi(q2[1])};
-                        const float k4[4] = {bf16_lo(k2[0]), bf16_hi(k2[0]), bf16_lo(k2[1]), bf16_hi(k2[1])};
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) w += q4[x] * k4[x] * hw_exp2(a4[x] - b4[x]);
-                    }
-                }
-                Wf[t * 17 + u] = w;
-            }
-            lds_barrier();
-            for (int e = tid; e < kGChunk * BV; e += NT) {
-                const int t = e / BV, jj = e % BV;
-                const float bt = has_gv ? Bf[t * BR + jj] : 0.f;
-                float acc = 0.f;
-                for (int u = 0; u <= t; ++u) {
-                    const float vu = bf16_half(SVw[u * SV + (jj >> 1)], jj & 1);
-                    const float d = has_gv ? hw_exp2(bt - Bf[u * BR + jj]) : 1.f;
-                    acc += Wf[t * 17 + u] * vu * d;
-                }
-                OIf[t * BR + jj] = acc;
-            }
-            lds_barrier();
-        }
-        if (c + 1 < nch) {
-            store_chunk();  // chunk c + 1; the staged arrays are read only before here
-            if (c + 2 < nch) load_chunk(c + 2);
-        }
+    };
 
+    // Exact intra term of a wide chunk (all threads, between barriers): W, then
+    // OI = W (v .* 2^{B_t - B_u}), from the raw staged chunk and the summed decays.
+    auto exact_chunk = [&](int c) {
+        const uint32_t* st = staged(c);
+        for (int e = tid; e < kGChunk * kGChunk; e += NT) {
+            const int t = e >> 4, u = e & 15;
+            float w = 0.f;
+            if (u <= t) {
+                const uint32_t* qt = st + Cfg::ST_Q + t * SQ;
+                const uint32_t* ku = st + Cfg::ST_K + u * SQ;
+                const float* at = Af + t * AR;
+                const float* au = Af + u * AR;
+#pragma unroll 4
+                for (int i = 0; i < DK; i += 4) {
+                    const u32x2 q2 = lds_load<u32x2>(qt + i / 2), k2 = lds_load<u32x2>(ku + i / 2);
+                    const f32x4 a4 = lds_load<f32x4>(at + i), b4 = lds_load<f32x4>(au + i);
+                    const float q4[4] = {bf16_lo(q2[0]), bf16_hi(q2[0]), bf16_lo(q2[1]), bf16_hi(q2[1])};
+                    const float k4[4] = {bf16_lo(k2[0]), bf16_hi(k2[0]), bf16_lo(k2[1]), bf16_hi(k2[1])};
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) w += q4[x] * k4[x] * hw_exp2(a4[x] - b4[x]);
+                }
+            }
+            Wf[t * 17 + u] = w;
+        }
+        lds_barrier();
+        for (int e = tid; e < kGChunk * BV; e += NT) {
+            const int t = e / BV, jj = e % BV;
+            const float bt = has_gv ? Bf[t * BR + jj] : 0.f;
+            float acc = 0.f;
+            for (int u = 0; u <= t; ++u) {
+                const float vu = bf16_half(st[Cfg::ST_V + u * SV + (jj >> 1)], jj & 1);
+                const float dd = has_gv ? hw_exp2(bt - Bf[u * BR + jj]) : 1.f;
+                acc += Wf[t * 17 + u] * vu * dd;
+            }
+            OIf[t * BR + jj] = acc;
+        }
+        lds_barrier();
+    };
+
+    // Matrix phase of chunk c (matrix waves).
+    auto matrix_chunk = [&](int c, bool fast) {
+        const uint32_t* d = derived(c);
+        const uint32_t* QHw = d + Cfg::D_QH;
+        const uint32_t* KPw = d + Cfg::D_KP;
+        const float* BTf = reinterpret_cast<const float*>(d + Cfg::D_BT);
+        const int nv = chunk_nv(c);
         // Inter-chunk part (q .* 2^A) S: the state tile pair (2s, 2s+1), split into
         // bf16 hi + lo, is the B operand of dk block s.  Fast path: W^T = (k ./ e)
         // (q .* e)^T in the same loop (q .* e is its B operand too); lane holds
         // W[t = lr][u = 4lg + ii].
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 O;
+        const int vrow_j = vblk(j, lg);
         if (fast) {
             f32x4 Oa = z, Ob = z, Oc = z, Wa = z, Wb = z, Wc = z;
 #pragma unroll
@@ -1725,12 +1740,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
                 if (4 * lg + ii > lr) W[ii] = 0.f;  // causal: u <= t
             // Intra term W (v .* 2^{-B}): k = 8lg + e covers the tokens 4lg + (e & 3)
             // with W's hi (e < 4) and lo (e >= 4) parts, against v's hi part twice.
-            const u32x4 vpx = lds_load<u32x4>((has_gv ? VPw : VTw) + j * TMR + 4 * lg);
+            const u32x4 vpx = lds_load<u32x4>(d + (has_gv ? Cfg::D_VP : Cfg::D_VT) + vrow_j);
             const u32x4 wa = {hi_pack(W[0], W[1]), hi_pack(W[2], W[3]), lo_pack(W[0], W[1]), lo_pack(W[2], W[3])};
             f32x4 Oi = mfma_bf16_w(wa, u32x4{vpx[0], vpx[1], vpx[0], vpx[1]}, z);
             if (has_gv) Oi = mfma_bf16_half(wa[0], wa[1], vpx[2], vpx[3], Oi);
             O += Oi;
-            if (has_gv) O *= lds_load<f32x4>(BTf + j * TMR + 4 * lg);
+            if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
         } else {
             f32x4 Oa = z, Ob = z, Oc = z;
 #pragma unroll
@@ -1747,7 +1762,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
                 Oc = mfma_bf16_w(ql, sh, Oc);
             }
             O = (Oa + Ob) + Oc;
-            if (has_gv) O *= lds_load<f32x4>(BTf + j * TMR + 4 * lg);
+            if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) O[ii] += OIf[(4 * lg + ii) * BR + j];
         }
@@ -1764,7 +1779,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
         // State update: S <- post .* (pre .* 2^{B_15}^T .* S + kp^T vt), contracting
         // over the 16 tokens with kp's hi and lo parts in one k range (token-minor
         // operands: lane group lg reads tokens 4lg .. 4lg+3).
-        const float eb = has_gv ? EBf[j] : 1.f;
+        const float* PREf = reinterpret_cast<const float*>(d + Cfg::D_PRE);
+        const float* POSTf = reinterpret_cast<const float*>(d + Cfg::D_POST);
+        const float eb = has_gv ? reinterpret_cast<const float*>(d + Cfg::D_EB)[j] : 1.f;
         if (!fast) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) {
@@ -1776,11 +1793,11 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) S[mt] *= eb;
         }
-        const u32x4 vtx = lds_load<u32x4>(VTw + j * TMR + 4 * lg);
+        const u32x4 vtx = lds_load<u32x4>(d + Cfg::D_VT + vrow_j);
         const u32x4 vt2 = {vtx[0], vtx[1], vtx[0], vtx[1]};
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            const u32x4 ktx = lds_load<u32x4>(KTw + (16 * mt + lr) * TMR + 4 * lg);
+            const u32x4 ktx = lds_load<u32x4>(d + Cfg::D_KT + (16 * mt + lr) * TMR + 4 * lg);
             S[mt] = mfma_bf16_w(ktx, vt2, S[mt]);
             if (has_gv) S[mt] = mfma_bf16_half(ktx[0], ktx[1], vtx[2], vtx[3], S[mt]);
         }
@@ -1790,9 +1807,48 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_bf16_kernel(const FwdParams 
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= post[ii];
         }
+    };
+
+    // Pipeline: before the barrier that opens step c, the producers have staged
+    // chunk c+1 and derived chunk c.  During step c the matrix waves compute chunk c
+    // while the producers derive chunk c+1, stage chunk c+2 (into the buffer chunk c
+    // used) and load chunk c+3.  A wide chunk first takes the exact path with all
+    // waves, before its staged buffer is reused.  Chunk flags cycle through three
+    // slots: slot (c+2) mod 3 is cleared during step c, after every read of chunk
+    // c-1's flag and before chunk c+2's prep.
+    if (producer) {
+        if (ptid == 0) wide_flag[0] = wide_flag[1] = wide_flag[2] = 0;
+        if (nch > 0) {
+            load_chunk(0);
+            store_chunk(0);
+        }
+        if (nch > 1) load_chunk(1);
+    }
+    lds_barrier();
+    if (producer && nch > 0) {
+        prep_chunk(0);
+        if (nch > 1) {
+            store_chunk(1);
+            if (nch > 2) load_chunk(2);
+        }
+    }
+    for (int c = 0; c < nch; ++c) {
+        lds_barrier();  // chunk c derived, chunk c+1 staged, chunk c's flag final
+        const bool fast = wide_flag[c % 3] == 0;
+        if (!fast) exact_chunk(c);
+        if (!producer) {
+            matrix_chunk(c, fast);
+        } else if (c + 1 < nch) {
+            if (ptid == 0) wide_flag[(c + 2) % 3] = 0;
+            prep_chunk(c + 1);
+            if (c + 2 < nch) {
+                store_chunk(c + 2);
+                if (c + 3 < nch) load_chunk(c + 3);
+            }
+        }
     }
 
-    if (p.final_state) {
+    if (!producer && p.final_state) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -2111,13 +2167,15 @@ hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, floa
 namespace {
 template <int DK, int NW>
 hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
-    const dim3 grid(fwd_grid_size(p)), block(64 * NW);
+    const dim3 grid(fwd_grid_size(p));
+    // bf16: NW matrix waves plus NW producer waves; fp32: NW waves
+    const dim3 block_bf16(GatedBCfg<DK, NW>::NT), block_f32(64 * NW);
     if (bf16 && p.gk_is_f32)
-        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true>), grid, block_bf16, 0, s, p);
     else if (bf16)
-        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, false>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, false>), grid, block_bf16, 0, s, p);
     else
-        hipLaunchKernelGGL((gated_kernel<DK, NW, false, true>), grid, block, 0, s, p);
+        hipLaunchKernelGGL((gated_kernel<DK, NW, false, true>), grid, block_f32, 0, s, p);
     return hipGetLastError();
 }
 template <int DK>
