@@ -32,6 +32,8 @@
 // The state is kept in fp32 and fed to the Q S product as bf16 hi + lo (two MFMAs),
 // and so is the masked intra-chunk matrix P in P V, so that neither rounding reaches
 // the output; o and the states are fp32.
+#include <type_traits>
+
 #include "lattn_launch.h"
 
 namespace lattn {
@@ -1330,17 +1332,11 @@ struct GatedBCfg {
     static_assert(DWORDS * 4 <= kLdsBudget, "LDS budget");
 };
 
-// Four consecutive elements as raw words at a byte offset from a workgroup-uniform
-// base (the offset fits 32 bits, so the load takes the scalar-base form).
-template <bool F32>
-__device__ inline u32x4 load4_at(const void* base, uint32_t byte_off) {
-    const char* b = static_cast<const char*>(base) + byte_off;
-    if constexpr (F32) {
-        return *reinterpret_cast<const u32x4*>(b);
-    } else {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(b);
-        return u32x4{w[0], w[1], 0u, 0u};
-    }
+// A vector of raw words at a byte offset from a workgroup-uniform base (the offset
+// fits 32 bits, so the load takes the scalar-base form).
+template <typename T>
+__device__ inline T load_at(const void* base, uint32_t byte_off) {
+    return *reinterpret_cast<const T*>(static_cast<const char*>(base) + byte_off);
 }
 
 __device__ inline f32x4 mfma_bf16_w(u32x4 a, u32x4 b, f32x4 c) {
@@ -1411,8 +1407,8 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
     float* Bf = reinterpret_cast<float*>(sm + Cfg::OFF_B);
     float* OIf = reinterpret_cast<float*>(sm + Cfg::OFF_OI);
     float* Wf = reinterpret_cast<float*>(sm + Cfg::OFF_W);
-    auto staged = [&](int c) -> uint32_t* { return sm + Cfg::OFF_ST + (c & 1) * Cfg::ST_SIZE; };
-    auto derived = [&](int c) -> uint32_t* { return sm + Cfg::OFF_D + (c & 1) * Cfg::D_SIZE; };
+    auto staged = [&](int c) __attribute__((always_inline)) -> uint32_t* { return sm + Cfg::OFF_ST + (c & 1) * Cfg::ST_SIZE; };
+    auto derived = [&](int c) __attribute__((always_inline)) -> uint32_t* { return sm + Cfg::OFF_D + (c & 1) * Cfg::D_SIZE; };
 
     Work wk;
     if (!decode_work(p, wk)) return;
@@ -1435,12 +1431,12 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
     // Chunk c holds the rows [low, low + nv) of the flattened token axis (in either
     // direction); token t of the chunk is row low + lrow(t).  Offsets inside a chunk
     // stay 32-bit (the host bounds 16 rows of every array below 2^31 bytes).
-    auto chunk_nv = [&](int c) -> int { return (int)min((int64_t)kGChunk, L - (int64_t)c * kGChunk); };
-    auto chunk_low = [&](int c, int nv) -> int64_t {
+    auto chunk_nv = [&](int c) __attribute__((always_inline)) -> int { return (int)min((int64_t)kGChunk, L - (int64_t)c * kGChunk); };
+    auto chunk_low = [&](int c, int nv) __attribute__((always_inline)) -> int64_t {
         const int64_t p0 = (int64_t)c * kGChunk;
         return rev ? wk.start + L - p0 - nv : wk.start + p0;
     };
-    auto lrow = [&](int t, int nv) -> uint32_t { return (uint32_t)(rev ? nv - 1 - t : t); };
+    auto lrow = [&](int t, int nv) __attribute__((always_inline)) -> uint32_t { return (uint32_t)(rev ? nv - 1 - t : t); };
 
     f32x4 S[MT];
     const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
@@ -1453,16 +1449,36 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
     }
 
     // Producer staging registers: raw words of this thread's pieces (bf16: words 0
-    // and 1), loaded one chunk ahead of their store to LDS.  Absent gates are not
-    // loaded and are staged as zeros.
-    u32x4 rq[Cfg::KPER], rk[Cfg::KPER], ra[Cfg::KPER], rv[Cfg::VPER], rb[Cfg::VPER];
-    uint32_t kok = 0, vok = 0;  // bit s: piece s lies inside the sequence
-    auto load_chunk = [&](int c) {
+    // and 1).  Two sets: chunk m goes through set m & 1, loaded two chunks ahead of
+    // its store to LDS.  Absent gates are staged as zeros.
+    using GateW = typename std::conditional<GF32, u32x4, u32x2>::type;  // four gate values
+    struct StageRegs {
+        u32x2 q[Cfg::KPER], k[Cfg::KPER], v[Cfg::VPER], b[Cfg::VPER];
+        GateW a[Cfg::KPER];
+        uint32_t kok, vok;  // bit s: piece s lies inside the sequence
+    };
+    StageRegs R0, R1;
+    auto load_chunk = [&](int c, StageRegs& r) __attribute__((always_inline)) {
+        u32x2(&rq)[Cfg::KPER] = r.q;
+        u32x2(&rk)[Cfg::KPER] = r.k;
+        GateW(&ra)[Cfg::KPER] = r.a;
+        u32x2(&rv)[Cfg::VPER] = r.v;
+        u32x2(&rb)[Cfg::VPER] = r.b;
+        uint32_t& kok = r.kok;
+        uint32_t& vok = r.vok;
         const int nv = chunk_nv(c);
         const int64_t low = chunk_low(c, nv);
         const uint16_t* qb = static_cast<const uint16_t*>(p.q) + (low * qrow + qoff);
         const uint16_t* kb = static_cast<const uint16_t*>(p.k) + (low * krow + koff);
         const uint16_t* vb = static_cast<const uint16_t*>(p.v) + (low * vrow + voff);
+        // An absent gate re-reads q (v) at the same offsets: the same number of loads
+        // every chunk keeps the waits on the earlier register set exact.
+        constexpr uint32_t gsz = GF32 ? 4 : 2;
+        const char* gb = has_g ? static_cast<const char*>(p.g) + (low * qrow + qoff) * gsz
+                               : reinterpret_cast<const char*>(qb);
+        const char* gvb = has_gv ? reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.gv) + (low * gvrow + gvoff))
+                                 : reinterpret_cast<const char*>(vb);
+        const uint32_t gvstride = (uint32_t)(has_gv ? gvrow : vrow);
         kok = vok = 0;
 #pragma unroll
         for (int s = 0; s < Cfg::KPER; ++s) {
@@ -1471,16 +1487,9 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
             const bool ok = item < Cfg::KITEMS && t < nv;
             kok |= (ok ? 1u : 0u) << s;
             const uint32_t rr = ok ? lrow(t, nv) : 0u;  // rows past the end read row 0
-            rq[s] = load4_at<false>(qb, 2 * (rr * (uint32_t)qrow + 4 * c4));
-            rk[s] = load4_at<false>(kb, 2 * (rr * (uint32_t)krow + 4 * c4));
-            if (has_g) {
-                if constexpr (GF32)
-                    ra[s] = load4_at<true>(static_cast<const float*>(p.g) + (low * qrow + qoff),
-                                           4 * (rr * (uint32_t)qrow + 4 * c4));
-                else
-                    ra[s] = load4_at<false>(static_cast<const uint16_t*>(p.g) + (low * qrow + qoff),
-                                            2 * (rr * (uint32_t)qrow + 4 * c4));
-            }
+            rq[s] = load_at<u32x2>(qb, 2 * (rr * (uint32_t)qrow + 4 * c4));
+            rk[s] = load_at<u32x2>(kb, 2 * (rr * (uint32_t)krow + 4 * c4));
+            ra[s] = load_at<GateW>(gb, gsz * (rr * (uint32_t)qrow + 4 * c4));
         }
 #pragma unroll
         for (int s = 0; s < Cfg::VPER; ++s) {
@@ -1489,14 +1498,18 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
             const bool ok = item < Cfg::VITEMS && t < nv;
             vok |= (ok ? 1u : 0u) << s;
             const uint32_t rr = ok ? lrow(t, nv) : 0u;
-            rv[s] = load4_at<false>(vb, 2 * (rr * (uint32_t)vrow + 4 * c4));
-            if (has_gv)
-                rb[s] = load4_at<false>(static_cast<const uint16_t*>(p.gv) + (low * gvrow + gvoff),
-                                        2 * (rr * (uint32_t)gvrow + 4 * c4));
+            rv[s] = load_at<u32x2>(vb, 2 * (rr * (uint32_t)vrow + 4 * c4));
+            rb[s] = load_at<u32x2>(gvb, 2 * (rr * gvstride + 4 * c4));
         }
     };
     // Raw words to LDS (zero past the end); nothing is converted here.
-    auto store_chunk = [&](int c) {
+    auto store_chunk = [&](int c, const StageRegs& r) __attribute__((always_inline)) {
+        const u32x2(&rq)[Cfg::KPER] = r.q;
+        const u32x2(&rk)[Cfg::KPER] = r.k;
+        const GateW(&ra)[Cfg::KPER] = r.a;
+        const u32x2(&rv)[Cfg::VPER] = r.v;
+        const u32x2(&rb)[Cfg::VPER] = r.b;
+        const uint32_t kok = r.kok, vok = r.vok;
         uint32_t* st = staged(c);
         const u32x2 z2 = {0u, 0u};
         const u32x4 z4 = {0u, 0u, 0u, 0u};
@@ -1506,11 +1519,11 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
             if (item < Cfg::KITEMS) {
                 const int t = item / (DK / 4), c4 = item % (DK / 4);
                 const bool ok = (kok >> s) & 1u;
-                lds_store<u32x2>(st + Cfg::ST_Q + t * SQ + 2 * c4, ok ? u32x2{rq[s][0], rq[s][1]} : z2);
-                lds_store<u32x2>(st + Cfg::ST_K + t * SQ + 2 * c4, ok ? u32x2{rk[s][0], rk[s][1]} : z2);
+                lds_store<u32x2>(st + Cfg::ST_Q + t * SQ + 2 * c4, ok ? rq[s] : z2);
+                lds_store<u32x2>(st + Cfg::ST_K + t * SQ + 2 * c4, ok ? rk[s] : z2);
                 const bool gok = ok && has_g;
                 if constexpr (GF32) lds_store<u32x4>(st + Cfg::ST_G + t * SGR + 4 * c4, gok ? ra[s] : z4);
-                else lds_store<u32x2>(st + Cfg::ST_G + t * SGR + 2 * c4, gok ? u32x2{ra[s][0], ra[s][1]} : z2);
+                else lds_store<u32x2>(st + Cfg::ST_G + t * SGR + 2 * c4, gok ? ra[s] : z2);
             }
         }
 #pragma unroll
@@ -1519,15 +1532,15 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
             if (item < Cfg::VITEMS) {
                 const int t = item / (BV / 4), c4 = item % (BV / 4);
                 const bool ok = (vok >> s) & 1u;
-                lds_store<u32x2>(st + Cfg::ST_V + t * SV + 2 * c4, ok ? u32x2{rv[s][0], rv[s][1]} : z2);
-                if (has_gv) lds_store<u32x2>(st + Cfg::ST_GV + t * SV + 2 * c4, ok ? u32x2{rb[s][0], rb[s][1]} : z2);
+                lds_store<u32x2>(st + Cfg::ST_V + t * SV + 2 * c4, ok ? rv[s] : z2);
+                if (has_gv) lds_store<u32x2>(st + Cfg::ST_GV + t * SV + 2 * c4, ok ? rb[s] : z2);
             }
         }
     };
 
     // Prep of chunk c (producer waves): staged(c) -> derived(c), the summed decays
     // (exact path) and the chunk's flag.
-    auto prep_chunk = [&](int c) {
+    auto prep_chunk = [&](int c) __attribute__((always_inline)) {
         const uint32_t* st = staged(c);
         uint32_t* d = derived(c);
         const int nv = chunk_nv(c);
@@ -1662,7 +1675,7 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
 
     // Exact intra term of a wide chunk (all threads, between barriers): W, then
     // OI = W (v .* 2^{B_t - B_u}), from the raw staged chunk and the summed decays.
-    auto exact_chunk = [&](int c) {
+    auto exact_chunk = [&](int c) __attribute__((always_inline)) {
         const uint32_t* st = staged(c);
         for (int e = tid; e < kGChunk * kGChunk; e += NT) {
             const int t = e >> 4, u = e & 15;
@@ -1700,7 +1713,7 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
     };
 
     // Matrix phase of chunk c (matrix waves).
-    auto matrix_chunk = [&](int c, bool fast) {
+    auto matrix_chunk = [&](int c, bool fast) __attribute__((always_inline)) {
         const uint32_t* d = derived(c);
         const uint32_t* QHw = d + Cfg::D_QH;
         const uint32_t* KPw = d + Cfg::D_KP;
@@ -1812,39 +1825,54 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
     // Pipeline: before the barrier that opens step c, the producers have staged
     // chunk c+1 and derived chunk c.  During step c the matrix waves compute chunk c
     // while the producers derive chunk c+1, stage chunk c+2 (into the buffer chunk c
-    // used) and load chunk c+3.  A wide chunk first takes the exact path with all
-    // waves, before its staged buffer is reused.  Chunk flags cycle through three
-    // slots: slot (c+2) mod 3 is cleared during step c, after every read of chunk
-    // c-1's flag and before chunk c+2's prep.
+    // used) and load chunk c+4 (chunks c+3 and c+4 are in flight).  A wide chunk
+    // first takes the exact path with all waves, before its staged buffer is
+    // reused.  Chunk flags cycle through three slots: slot (c+2) mod 3 is cleared
+    // during step c, after every read of chunk c-1's flag and before chunk c+2's
+    // prep.  The two roles run separate loops with the same barriers in the same
+    // order; the producers' steps run in pairs so that each register set has a
+    // fixed name.
     if (producer) {
         if (ptid == 0) wide_flag[0] = wide_flag[1] = wide_flag[2] = 0;
+        // Every step stores and loads one chunk (past the end: the last chunk again,
+        // into a buffer no prep reads), so the loads in flight are always the two
+        // register sets in order and the waits before each store are exact.
+        auto clampc = [&](int m) __attribute__((always_inline)) -> int { return min(m, nch - 1); };
         if (nch > 0) {
-            load_chunk(0);
-            store_chunk(0);
+            load_chunk(0, R0);
+            load_chunk(clampc(1), R1);
+            store_chunk(0, R0);
+            load_chunk(clampc(2), R0);
         }
-        if (nch > 1) load_chunk(1);
-    }
-    lds_barrier();
-    if (producer && nch > 0) {
-        prep_chunk(0);
-        if (nch > 1) {
-            store_chunk(1);
-            if (nch > 2) load_chunk(2);
-        }
-    }
-    for (int c = 0; c < nch; ++c) {
-        lds_barrier();  // chunk c derived, chunk c+1 staged, chunk c's flag final
-        const bool fast = wide_flag[c % 3] == 0;
-        if (!fast) exact_chunk(c);
-        if (!producer) {
-            matrix_chunk(c, fast);
-        } else if (c + 1 < nch) {
-            if (ptid == 0) wide_flag[(c + 2) % 3] = 0;
-            prep_chunk(c + 1);
-            if (c + 2 < nch) {
-                store_chunk(c + 2);
-                if (c + 3 < nch) load_chunk(c + 3);
+        lds_barrier();
+        if (nch > 0) {
+            prep_chunk(0);
+            store_chunk(1, R1);
+            load_chunk(clampc(3), R1);
+            auto step = [&](int c, StageRegs& r) __attribute__((always_inline)) {  // r: chunks c+2, c+4
+                if (c < nch) {
+                    lds_barrier();  // chunk c derived, chunk c+1 staged, chunk c's flag final
+                    if (wide_flag[c % 3] != 0) exact_chunk(c);
+                }
+                if (c + 1 < nch) {
+                    if (ptid == 0) wide_flag[(c + 2) % 3] = 0;
+                    prep_chunk(c + 1);
+                }
+                store_chunk(c + 2, r);
+                load_chunk(clampc(c + 4), r);
+            };
+            for (int c = 0; c < nch; c += 2) {
+                step(c, R0);
+                step(c + 1, R1);
             }
+        }
+    } else {
+        lds_barrier();
+        for (int c = 0; c < nch; ++c) {
+            lds_barrier();
+            const bool fast = wide_flag[c % 3] == 0;
+            if (!fast) exact_chunk(c);
+            matrix_chunk(c, fast);
         }
     }
 
