@@ -40,7 +40,9 @@ BF16_MFMA_PEAK_TFS = 2500.0  # dense bf16 matrix peak of MI355X
 PAGE_LIGHTNING2_MS = 17.661427
 PAGE_LIGHTNING2_BWD_MS = 74.594788  # same table's backward row at n = 32768
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_b4_h32_d128_n32768.json")
-KERNEL_SRC = os.path.join(ROOT, "decayed_recurrent_attention_amd", "csrc", "lattn_kernels.hip")
+# the forward kernel's translation unit: its source and the two headers it includes
+KERNEL_SRCS = [os.path.join(ROOT, "decayed_recurrent_attention_amd", "csrc", n)
+               for n in ("lattn_kernels.hip", "lattn_device.h", "lattn_launch.h")]
 
 
 def algorithmic_bytes(B, T, H, Hkv, dk, dv, in_bytes, with_init=False):
@@ -52,8 +54,11 @@ def algorithmic_bytes(B, T, H, Hkv, dk, dv, in_bytes, with_init=False):
 
 
 def kernel_sha() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic():

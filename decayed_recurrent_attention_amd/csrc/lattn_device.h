@@ -1,0 +1,103 @@
+// Device helpers shared by the kernel sources (not installed; not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lattn_launch.h"
+
+namespace lattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLdsBudget = 160 * 1024;
+
+// One unit of work, decoded from the workgroup id.
+struct Work {
+    int n;          // sequence (batch row, or packed sequence)
+    int h;          // query head
+    int kvh;        // kv head read by h
+    int vb;         // value block
+    int64_t start;  // first token row of the sequence in the flattened [B*T] axis
+    int64_t len;    // tokens in the sequence
+};
+
+// Workgroup id -> work.  Groups are (sequence rank, kv head); the workgroups of one
+// group (its query heads x value blocks, which re-read the same K and V, and per
+// head the same Q) get ids that are equal mod kNumXcd, so they share one L2.
+// Consecutive groups go to consecutive dies; with sequences ranked longest first,
+// each die receives its longest work first.
+__device__ inline bool decode_work(const FwdParams& p, Work& w) {
+    const int id = blockIdx.x;
+    const int x = id % kNumXcd;
+    const int slot = id / kNumXcd;
+    const int g = (slot / p.group_size) * kNumXcd + x;
+    if (g >= p.num_groups) return false;
+    const int j = slot % p.group_size;
+    const int rank = g / p.num_kv_heads;
+    w.kvh = g % p.num_kv_heads;
+    w.n = p.order ? p.order[rank] : rank;
+    w.h = w.kvh * (p.num_heads / p.num_kv_heads) + j / p.nvb;
+    w.vb = j % p.nvb;
+    if (p.seg_count > 0) {  // sequence n = segment n % seg_count of batch row n / seg_count
+        const int b = w.n / p.seg_count, sg = w.n % p.seg_count;
+        const int64_t a = (int64_t)sg * p.seg_len;
+        const int64_t e = min(a + p.seg_len, (int64_t)p.seqlen);
+        w.start = (int64_t)b * p.seqlen + a;
+        w.len = e > a ? e - a : 0;
+    } else if (p.cu) {
+        int64_t a = p.cu[w.n];
+        int64_t e = p.cu[w.n + 1];
+        a = min(max(a, (int64_t)0), (int64_t)p.seqlen);
+        e = min(max(e, a), (int64_t)p.seqlen);
+        w.start = a;
+        w.len = e - a;
+    } else {
+        w.start = (int64_t)w.n * p.seqlen;
+        w.len = p.seqlen;
+    }
+    return true;
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ inline float bf16_half(uint32_t w, int hi) { return hi ? bf16_hi(w) : bf16_lo(w); }
+__device__ inline uint32_t half16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
+
+__device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <typename T>
+__device__ inline T lds_load(const void* p) {
+    return *reinterpret_cast<const T*>(p);
+}
+template <typename T>
+__device__ inline void lds_store(void* p, T v) {
+    *reinterpret_cast<T*>(p) = v;
+}
+
+__device__ inline void lds_barrier() {  // this wave's LDS accesses done, then workgroup barrier
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+// Workgroups for a grid-stride streaming kernel over n4 16-byte pieces.
+inline int stream_blocks(int64_t n4) {
+    const int64_t b = (n4 + 255) / 256;
+    return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
+}
+
+}  // namespace lattn

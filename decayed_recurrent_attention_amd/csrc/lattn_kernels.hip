@@ -32,94 +32,10 @@
 // The state is kept in fp32 and fed to the Q S product as bf16 hi + lo (two MFMAs),
 // and so is the masked intra-chunk matrix P in P V, so that neither rounding reaches
 // the output; o and the states are fp32.
-#include <type_traits>
-
-#include "lattn_launch.h"
+#include "lattn_device.h"
 
 namespace lattn {
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLdsBudget = 160 * 1024;
-
-// One unit of work, decoded from the workgroup id.
-struct Work {
-    int n;          // sequence (batch row, or packed sequence)
-    int h;          // query head
-    int kvh;        // kv head read by h
-    int vb;         // value block
-    int64_t start;  // first token row of the sequence in the flattened [B*T] axis
-    int64_t len;    // tokens in the sequence
-};
-
-// Workgroup id -> work.  Groups are (sequence rank, kv head); the workgroups of one
-// group (its query heads x value blocks, which re-read the same K and V, and per
-// head the same Q) get ids that are equal mod kNumXcd, so they share one L2.
-// Consecutive groups go to consecutive dies; with sequences ranked longest first,
-// each die receives its longest work first.
-__device__ inline bool decode_work(const FwdParams& p, Work& w) {
-    const int id = blockIdx.x;
-    const int x = id % kNumXcd;
-    const int slot = id / kNumXcd;
-    const int g = (slot / p.group_size) * kNumXcd + x;
-    if (g >= p.num_groups) return false;
-    const int j = slot % p.group_size;
-    const int rank = g / p.num_kv_heads;
-    w.kvh = g % p.num_kv_heads;
-    w.n = p.order ? p.order[rank] : rank;
-    w.h = w.kvh * (p.num_heads / p.num_kv_heads) + j / p.nvb;
-    w.vb = j % p.nvb;
-    if (p.seg_count > 0) {  // sequence n = segment n % seg_count of batch row n / seg_count
-        const int b = w.n / p.seg_count, sg = w.n % p.seg_count;
-        const int64_t a = (int64_t)sg * p.seg_len;
-        const int64_t e = min(a + p.seg_len, (int64_t)p.seqlen);
-        w.start = (int64_t)b * p.seqlen + a;
-        w.len = e > a ? e - a : 0;
-    } else if (p.cu) {
-        int64_t a = p.cu[w.n];
-        int64_t e = p.cu[w.n + 1];
-        a = min(max(a, (int64_t)0), (int64_t)p.seqlen);
-        e = min(max(e, a), (int64_t)p.seqlen);
-        w.start = a;
-        w.len = e - a;
-    } else {
-        w.start = (int64_t)w.n * p.seqlen;
-        w.len = p.seqlen;
-    }
-    return true;
-}
-
-__device__ inline uint32_t pack_bf16x2(float a, float b) {
-    const f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-__device__ inline float bf16_half(uint32_t w, int hi) { return hi ? bf16_hi(w) : bf16_lo(w); }
-__device__ inline uint32_t half16(uint32_t w, int hi) { return hi ? (w >> 16) : (w & 0xffffu); }
-
-__device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ inline f32x4 mfma_f32(float a, float b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
-template <typename T>
-__device__ inline T lds_load(const void* p) {
-    return *reinterpret_cast<const T*>(p);
-}
-template <typename T>
-__device__ inline void lds_store(void* p, T v) {
-    *reinterpret_cast<T*>(p) = v;
-}
 
 // Index of (K Q^T) tile (a, b), a <= b, among the 10 lower-triangle tiles of a chunk.
 __host__ __device__ constexpr int tidx(int a, int b) { return b * (b + 1) / 2 + a; }
@@ -227,9 +143,6 @@ template <int N>
 __device__ inline void wait_vmem() {  // at most N vector-memory operations outstanding
     static_assert(N >= 0 && N <= 63, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-__device__ inline void lds_barrier() {  // this wave's LDS accesses done, then workgroup barrier
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
 // ---------------------------------------------------------------------------
@@ -869,1038 +782,6 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
 }
 
 // ---------------------------------------------------------------------------
-// Gated recurrence (GLA gates): log-decays per key channel, g_gamma[h] + g_t + gk_t,
-// and per value channel, gv_t, each token.  Chunks of 16 tokens in fp32
-// (v_mfma_f32_16x16x4_f32).  With A_t and B_t the log-decays summed from the chunk
-// start through token t, every exponent below is <= 0, so nothing overflows:
-//   o_t  = scale [ ((q_t .* e^{A_t}) S) .* e^{B_t} + sum_{u<=t} W_tu (v_u .* e^{B_t - B_u}) ]
-//   W_tu = sum_i q_t[i] k_u[i] e^{A_t[i] - A_u[i]}                        (u <= t)
-//   S'   = (e^{A_15} e^{B_15}^T) .* S + (k .* e^{A_15 - A_u})^T (v .* e^{B_15 - B_u})
-// W has a per-channel exponent inside its sum.  When the chunk's decay spans stay
-// below 2^kGSpan, W and the intra term run on MFMA after rescaling about the mid
-// token m (q .* 2^{A_t - A_m} against k .* 2^{A_m - A_u}, v .* 2^{B_m - B_u}, then the
-// rows times 2^{B_t - B_m}): every factor stays below 2^kGSpan, so nothing overflows.
-// Otherwise W is built exactly on the VALU, one entry per thread.  Q S and the state
-// update always run on MFMA.  Wave w owns value columns 16w .. 16w+15 of the block;
-// its state tiles hold rows 16mt + 4lg + ii at column lr (accumulator layout, as in
-// the fp32 kernel).
-// ---------------------------------------------------------------------------
-constexpr int kGChunk = 16;
-constexpr int kGMid = 7;        // reference token of the fast path
-constexpr float kGSpan = 64.f;  // largest |summed log2-decay| of a chunk on the fast path
-
-// Hardware 2^x (v_exp_f32).  Results below the smallest normal float flush to zero,
-// which only drops terms weighted below 2^-126 against a unit-weight term.
-__device__ inline float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-template <int DK, int NW>
-struct GatedCfg {
-    static constexpr int BV = 16 * NW;
-    static constexpr int NT = 64 * NW;
-    static constexpr int KS = DK + 4;  // row stride (floats) of the dk-wide arrays
-    static constexpr int VS = BV + 4;  // row stride of the BV-wide arrays
-    static constexpr int MT = DK / 16;
-    static constexpr int TS = kGChunk + 4;  // row stride of the token-minor arrays
-    // Staged chunk (from registers): q, k, la = key log2-decay per token; v, lb =
-    // value log2-decay per token (the prep phase turns la, lb into their sums A, B
-    // from the chunk start, in place).  Derived for the matrix phase: qh = q .* 2^A,
-    // qm = q .* 2^{A - A_m}, km = k .* 2^{A_m - A} (token-major); kt = k .* 2^{A_15 - A},
-    // vt = v .* 2^{B_15 - B}, vm = v .* 2^{B_m - B} (token-minor: one 16-byte read gives
-    // an MFMA lane its four tokens); bt = 2^B, bm = 2^{B - B_m}; ea = 2^{A_15},
-    // eb = 2^{B_15}; W and oi for the exact path.
-    static constexpr int OFF_Q = 0;
-    static constexpr int OFF_K = OFF_Q + kGChunk * KS;
-    static constexpr int OFF_A = OFF_K + kGChunk * KS;
-    static constexpr int OFF_QH = OFF_A + kGChunk * KS;
-    static constexpr int OFF_KT = OFF_QH + kGChunk * KS;
-    static constexpr int OFF_QM = OFF_KT + DK * TS;
-    static constexpr int OFF_KM = OFF_QM + kGChunk * KS;
-    static constexpr int OFF_V = OFF_KM + kGChunk * KS;
-    static constexpr int OFF_B = OFF_V + kGChunk * VS;
-    static constexpr int OFF_VT = OFF_B + kGChunk * VS;
-    static constexpr int OFF_VM = OFF_VT + BV * TS;
-    static constexpr int OFF_BT = OFF_VM + BV * TS;
-    static constexpr int OFF_BM = OFF_BT + kGChunk * VS;
-    static constexpr int OFF_OI = OFF_BM + kGChunk * VS;
-    static constexpr int OFF_W = OFF_OI + kGChunk * VS;
-    static constexpr int OFF_EA = OFF_W + kGChunk * 17;
-    static constexpr int OFF_EB = OFF_EA + DK;
-    static constexpr int FLOATS = OFF_EB + BV;
-    // Staging: 4-element pieces of a chunk, spread over all threads.
-    static constexpr int KITEMS = kGChunk * DK / 4, VITEMS = kGChunk * BV / 4;
-    static constexpr int KPER = (KITEMS + NT - 1) / NT, VPER = (VITEMS + NT - 1) / NT;
-    static_assert(DK % 16 == 0 && DK <= 128, "dk must be a multiple of 16 up to 128");
-    static_assert(FLOATS * 4 <= kLdsBudget, "LDS budget");
-};
-
-// Four consecutive elements as raw words (bf16: words x, y hold them; fp32: all four).
-template <bool F32>
-__device__ inline u32x4 load4_raw(const void* base, int64_t i) {
-    if constexpr (F32) {
-        return *reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + i);
-    } else {
-        const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(base) + i);
-        u32x4 r;
-        r[0] = w[0];
-        r[1] = w[1];
-        return r;
-    }
-}
-__device__ inline f32x4 raw_to_f32(u32x4 w, bool f32) {
-    return f32 ? __builtin_bit_cast(f32x4, w) : f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
-}
-
-// One chunk per loop trip, two barriers: (1) the staged chunk is in LDS and the
-// previous matrix phase is done; each thread then owns state channels (columns)
-// and derives, from the decays summed over the chunk in registers, the decayed
-// operands; (2) they are in LDS; the next chunk is staged from registers (its loads
-// were issued a loop trip earlier; raw words are converted only here, so no load is
-// waited for where it is issued) while the waves run the matrix phase.  The
-// barriers wait for LDS operations only, so the prefetch loads stay in flight.
-template <int DK, int NW, bool BF16, bool GF32>
-__global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
-    using Cfg = GatedCfg<DK, NW>;
-    constexpr int BV = Cfg::BV, NT = Cfg::NT, KS = Cfg::KS, VS = Cfg::VS, MT = Cfg::MT, TS = Cfg::TS;
-    __shared__ __attribute__((aligned(16))) float sm[Cfg::FLOATS];
-    __shared__ int wide_span[2];  // per chunk parity: take the exact VALU path
-    float* Qs = sm + Cfg::OFF_Q;
-    float* Ks = sm + Cfg::OFF_K;
-    float* As = sm + Cfg::OFF_A;
-    float* QHs = sm + Cfg::OFF_QH;
-    float* KTs = sm + Cfg::OFF_KT;
-    float* QMs = sm + Cfg::OFF_QM;
-    float* KMs = sm + Cfg::OFF_KM;
-    float* Vs = sm + Cfg::OFF_V;
-    float* Bs = sm + Cfg::OFF_B;
-    float* VTs = sm + Cfg::OFF_VT;
-    float* VMs = sm + Cfg::OFF_VM;
-    float* BTs = sm + Cfg::OFF_BT;
-    float* BMs = sm + Cfg::OFF_BM;
-    float* OIs = sm + Cfg::OFF_OI;
-    float* Ws = sm + Cfg::OFF_W;
-    float* EAs = sm + Cfg::OFF_EA;
-    float* EBs = sm + Cfg::OFF_EB;
-
-    Work wk;
-    if (!decode_work(p, wk)) return;
-    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int H = p.num_heads, dv = p.dv;
-    const int64_t L = wk.len;
-    const int nch = (int)((L + kGChunk - 1) / kGChunk);
-    const bool rev = p.reverse_gated != 0;
-    const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
-    constexpr bool g_f32 = !BF16 || GF32;  // dtype of the key gate
-    const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
-    const int j = 16 * wv + lr;       // this lane's column inside the block
-    const int vcol = wk.vb * BV + j;  // ... of v and o
-    auto tok_row = [&](int64_t pos) -> int64_t { return rev ? wk.start + L - 1 - pos : wk.start + pos; };
-    const int64_t qrow = (int64_t)H * DK, krow = (int64_t)p.num_kv_heads * DK;
-    const int64_t vrow = (int64_t)p.num_kv_heads * dv, gvrow = (int64_t)H * dv;
-    const int64_t qoff = (int64_t)wk.h * DK, koff = (int64_t)wk.kvh * DK;
-    const int64_t voff = (int64_t)wk.kvh * dv + wk.vb * BV, gvoff = (int64_t)wk.h * dv + wk.vb * BV;
-    // Absent gates read an element of an array with the same layout (q for the key
-    // gate, v itself for the value gate) and are written as zero.
-    const void* gbase = has_g ? p.g : p.q;
-    const void* gvbase = has_gv ? p.gv : p.v;
-    const int64_t gvrow_r = has_gv ? gvrow : vrow, gvoff_r = has_gv ? gvoff : voff;
-
-    f32x4 S[MT];
-    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
-    // The state is in registers before the loop: inside it, the only loads in flight
-    // are the staging prefetches, which the matrix phase then never waits for.
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-
-    // Staging registers: raw words of this thread's pieces of q, k, the key gate, v
-    // and the value gate; rows past the end read a valid row and are written as zero.
-    u32x4 rq[Cfg::KPER], rk[Cfg::KPER], ra[Cfg::KPER], rv[Cfg::VPER], rb[Cfg::VPER];
-    uint32_t kok = 0, vok = 0;  // bit s: piece s lies inside the sequence
-    auto load_chunk = [&](int c) {
-        const int64_t p0 = (int64_t)c * kGChunk;
-        kok = vok = 0;
-#pragma unroll
-        for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = tid + s * NT;
-            const int t = item / (DK / 4), c4 = item % (DK / 4);
-            const bool ok = item < Cfg::KITEMS && p0 + t < L;
-            kok |= (ok ? 1u : 0u) << s;
-            const int64_t row = tok_row(ok ? p0 + t : p0);
-            rq[s] = load4_raw<!BF16>(p.q, row * qrow + qoff + 4 * c4);
-            rk[s] = load4_raw<!BF16>(p.k, row * krow + koff + 4 * c4);
-            ra[s] = load4_raw<g_f32>(gbase, row * qrow + qoff + 4 * c4);
-        }
-#pragma unroll
-        for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = tid + s * NT;
-            const int t = item / (BV / 4), c4 = item % (BV / 4);
-            const bool ok = item < Cfg::VITEMS && p0 + t < L;
-            vok |= (ok ? 1u : 0u) << s;
-            const int64_t row = tok_row(ok ? p0 + t : p0);
-            rv[s] = load4_raw<!BF16>(p.v, row * vrow + voff + 4 * c4);
-            rb[s] = load4_raw<!BF16>(gvbase, row * gvrow_r + gvoff_r + 4 * c4);
-        }
-    };
-    // Write the staged pieces to LDS as floats: la = log2-decay of the key channels
-    // (g_gamma plus the gate), lb of the value channels; zero past the end.
-    auto store_chunk = [&]() {
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = tid + s * NT;
-            if (item < Cfg::KITEMS) {
-                const int t = item / (DK / 4), c4 = item % (DK / 4);
-                const bool ok = (kok >> s) & 1u;
-                const f32x4 a = has_g ? kLog2e * raw_to_f32(ra[s], g_f32) : z;
-                lds_store<f32x4>(Qs + t * KS + 4 * c4, ok ? raw_to_f32(rq[s], !BF16) : z);
-                lds_store<f32x4>(Ks + t * KS + 4 * c4, ok ? raw_to_f32(rk[s], !BF16) : z);
-                lds_store<f32x4>(As + t * KS + 4 * c4, ok ? a + gg2 : z);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = tid + s * NT;
-            if (item < Cfg::VITEMS) {
-                const int t = item / (BV / 4), c4 = item % (BV / 4);
-                const bool ok = (vok >> s) & 1u;
-                const f32x4 b = has_gv ? kLog2e * raw_to_f32(rb[s], !BF16) : z;
-                lds_store<f32x4>(Vs + t * VS + 4 * c4, ok ? raw_to_f32(rv[s], !BF16) : z);
-                lds_store<f32x4>(Bs + t * VS + 4 * c4, ok ? b : z);
-            }
-        }
-    };
-
-    if (tid == 0) wide_span[0] = wide_span[1] = 0;
-    if (nch > 0) {
-        load_chunk(0);
-        store_chunk();
-    }
-    if (nch > 1) load_chunk(1);
-    for (int c = 0; c < nch; ++c) {
-        lds_barrier();  // (1) chunk c staged; the previous matrix phase is done
-        if (tid == 0) wide_span[(c + 1) & 1] = 0;  // the next chunk's flag, set in its prep
-        // Prep: a thread owns a key channel (or a value channel) for all 16 tokens:
-        // it sums the decays in registers and writes the decayed operands.
-        for (int ch = tid; ch < DK + BV; ch += NT) {
-            if (ch < DK) {
-                const int i = ch;
-                float A[kGChunk];
-                float acc = 0.f;
-#pragma unroll
-                for (int t = 0; t < kGChunk; ++t) {
-                    acc += As[t * KS + i];
-                    A[t] = acc;
-                }
-                if (!(fabsf(acc) <= kGSpan)) wide_span[c & 1] = 1;
-                const float aend = A[kGChunk - 1], amid = A[kGMid];
-                EAs[i] = hw_exp2(aend);
-#pragma unroll
-                for (int t = 0; t < kGChunk; ++t) {
-                    const float qv = Qs[t * KS + i], kv = Ks[t * KS + i];
-                    As[t * KS + i] = A[t];
-                    QHs[t * KS + i] = qv * hw_exp2(A[t]);
-                    KTs[i * TS + t] = kv * hw_exp2(aend - A[t]);
-                    QMs[t * KS + i] = qv * hw_exp2(A[t] - amid);
-                    KMs[t * KS + i] = kv * hw_exp2(amid - A[t]);
-                }
-            } else {
-                const int jj = ch - DK;
-                float Bc[kGChunk];
-                float acc = 0.f;
-#pragma unroll
-                for (int t = 0; t < kGChunk; ++t) {
-                    acc += Bs[t * VS + jj];
-                    Bc[t] = acc;
-                }
-                if (!(fabsf(acc) <= kGSpan)) wide_span[c & 1] = 1;
-                const float bend = Bc[kGChunk - 1], bmid = Bc[kGMid];
-                EBs[jj] = hw_exp2(bend);
-#pragma unroll
-                for (int t = 0; t < kGChunk; ++t) {
-                    const float vv = Vs[t * VS + jj];
-                    Bs[t * VS + jj] = Bc[t];
-                    VTs[jj * TS + t] = vv * hw_exp2(bend - Bc[t]);
-                    VMs[jj * TS + t] = vv * hw_exp2(bmid - Bc[t]);
-                    BTs[t * VS + jj] = hw_exp2(Bc[t]);
-                    BMs[t * VS + jj] = hw_exp2(Bc[t] - bmid);
-                }
-            }
-        }
-        lds_barrier();  // (2) derived operands are in LDS
-        const bool fast = wide_span[c & 1] == 0;
-        if (!fast) {  // exact intra term on the VALU (uniform branch): W, then W (v .* 2^{B_t - B_u})
-            for (int e = tid; e < kGChunk * kGChunk; e += NT) {
-                const int t = e >> 4, u = e & 15;
-                float w = 0.f;
-                if (u <= t) {
-                    const float* qt = Qs + t * KS;
-                    const float* ku = Ks + u * KS;
-                    const float* at = As + t * KS;
-                    const float* au = As + u * KS;
-#pragma unroll 4
-                    for (int i = 0; i < DK; i += 4) {
-                        const f32x4 q4 = lds_load<f32x4>(qt + i), k4 = lds_load<f32x4>(ku + i);
-                        const f32x4 a4 = lds_load<f32x4>(at + i), b4 = lds_load<f32x4>(au + i);
-#pragma unroll
-                        for (int x = 0; x < 4; ++x) w += q4[x] * k4[x] * hw_exp2(a4[x] - b4[x]);
-                    }
-                }
-                Ws[t * 17 + u] = w;
-            }
-            lds_barrier();
-            for (int e = tid; e < kGChunk * BV; e += NT) {
-                const int t = e / BV, jj = e % BV;
-                const float bt = Bs[t * VS + jj];
-                float acc = 0.f;
-                for (int u = 0; u <= t; ++u) acc += Ws[t * 17 + u] * Vs[u * VS + jj] * hw_exp2(bt - Bs[u * VS + jj]);
-                OIs[t * VS + jj] = acc;
-            }
-            lds_barrier();
-        }
-        if (c + 1 < nch) {
-            store_chunk();  // chunk c + 1; q, k, v and the decay arrays are read only before (2)
-            if (c + 2 < nch) load_chunk(c + 2);
-        }
-
-        // Inter-chunk part: (q .* 2^A) S on four independent accumulators.
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 Oq[4] = {z, z, z, z};
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 qh = lds_load<f32x4>(QHs + lr * KS + 16 * mt + 4 * lg);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) Oq[ii] = mfma_f32(qh[ii], S[mt][ii], Oq[ii]);
-        }
-        f32x4 O = (Oq[0] + Oq[1]) + (Oq[2] + Oq[3]);
-        if (has_gv) {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[ii] *= BTs[(4 * lg + ii) * VS + j];
-        }
-        if (fast) {
-            // W^T = (k .* 2^{A_m - A}) (q .* 2^{A - A_m})^T: lane holds W[t = lr][u = 4lg + ii].
-            // The contraction runs over dk = (DK/4) lg + sq, so each lane reads runs of
-            // its own row.
-            f32x4 Wa[4] = {z, z, z, z};
-#pragma unroll
-            for (int s4 = 0; s4 < DK / 16; ++s4) {
-                const f32x4 km = lds_load<f32x4>(KMs + lr * KS + (DK / 4) * lg + 4 * s4);
-                const f32x4 qm = lds_load<f32x4>(QMs + lr * KS + (DK / 4) * lg + 4 * s4);
-#pragma unroll
-                for (int x = 0; x < 4; ++x) Wa[x] = mfma_f32(km[x], qm[x], Wa[x]);
-            }
-            const f32x4 W = (Wa[0] + Wa[1]) + (Wa[2] + Wa[3]);
-            const f32x4 vm = lds_load<f32x4>(VMs + j * TS + 4 * lg);
-            f32x4 Oi = z;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int u = 4 * lg + ii;
-                Oi = mfma_f32(u <= lr ? W[ii] : 0.f, vm[ii], Oi);  // causal: u <= t
-            }
-            if (has_gv) {
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) Oi[ii] *= BMs[(4 * lg + ii) * VS + j];
-            }
-            O += Oi;
-        } else {
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[ii] += OIs[(4 * lg + ii) * VS + j];
-        }
-        const int64_t p0 = (int64_t)c * kGChunk;
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int t = 4 * lg + ii;
-            if (p0 + t < L) p.o[(tok_row(p0 + t) * H + wk.h) * dv + vcol] = p.scale * O[ii];
-        }
-
-        // State update: S <- (2^{A_15} 2^{B_15}^T) .* S + kt^T vt.
-        const float eb = has_gv ? EBs[j] : 1.f;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 ea = lds_load<f32x4>(EAs + 16 * mt + 4 * lg);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= ea[ii] * eb;
-        }
-        // Contraction over the 16 tokens u = 4lg + sq: kt and vt are token-minor.
-        const f32x4 vt = lds_load<f32x4>(VTs + j * TS + 4 * lg);
-        f32x4 kt[MT];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) kt[mt] = lds_load<f32x4>(KTs + (16 * mt + lr) * TS + 4 * lg);
-#pragma unroll
-        for (int sq = 0; sq < 4; ++sq)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_f32(kt[mt][sq], vt[sq], S[mt]);
-    }
-
-    if (p.final_state) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = S[mt][ii];
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Gated recurrence, bf16 inputs: the chunk algebra of gated_kernel with every
-// product on bf16 MFMA.  A decayed fp32 operand X is split X = hi + lo, hi its bf16
-// truncation and lo the bf16 rounding of the exact remainder; a product takes
-// hi*hi + hi*lo + lo*hi with fp32 accumulation (about 2^-14 relative error per
-// term).  Raw bf16 v needs no split.  Where a contraction runs over the 16 tokens,
-// hi and lo share one 16x16x32 MFMA: its k index covers the tokens twice, with the
-// hi and then the lo parts of one operand against the other operand repeated.
-// With e_t = 2^{A_t} per key channel, the fast path (every channel's summed decay
-// over the chunk within 2^-kGSpan) takes one exponential pair per element:
-//   o_t  = scale 2^{B_t} .* [ (q_t .* e_t) S + sum_{u<=t} W_tu (v_u .* 2^{-B_u}) ]
-//   W_tu = (q_t .* e_t) . (k_u ./ e_u)
-//   S'   = 2^{A_15} .* [ 2^{B_15}^T .* S + (k ./ e)^T (v .* 2^{B_15 - B_u}) ]
-// so k ./ e serves both W and the state update; masked pairs u > t and the bracket
-// stay below 2^kGSpan times their operands.  A key channel pair with a wider span
-// stores k .* 2^{A_15 - A_u} instead and moves its factor 2^{A_15} in front of S
-// (per-row factors pre and post); a chunk holding one takes the exact VALU path of
-// gated_kernel for W and the intra term.
-//
-// Roles: a workgroup of 2 NW waves.  Waves 0 .. NW-1 (matrix waves) own 16 value
-// columns each and the state in accumulator registers; waves NW .. 2NW-1 (producer
-// waves) stage the chunks from global memory and derive the decayed operands.  With
-// one wave of each role per SIMD, the prep of chunk c+1 runs while the matrix waves
-// compute chunk c.  LDS holds two staged raw chunks and two sets of decayed
-// operands; one barrier per chunk hands both over.
-// Prep: one item (channel pair, quarter of the chunk) per producer lane, the four
-// quarters of a pair in one lane quad; each quarter sums its four decays and the quad
-// exchanges the partial sums (DPP), so every lane has its tokens' A_t and A_15.
-// ---------------------------------------------------------------------------
-template <int DK, int NW>
-struct GatedBCfg {
-    static constexpr int BV = 16 * NW;
-    static constexpr int PT = 64 * NW;  // producer threads
-    static constexpr int NT = 2 * PT;   // all threads
-    static constexpr int MT = DK / 16;
-    static constexpr int KB = DK / 32;  // 32-deep blocks of the dk contraction
-    // Dwords per row.  Staged raw chunk (token-major): q, k and a bf16 key gate;
-    // an fp32 key gate; v and the value gate.  Padded so that the prep reads of a
-    // half-wave (8 pairs x 4 quarters) hit distinct banks.
-    static constexpr int SQ = DK / 2 + 2;
-    static constexpr int SG32 = DK + 4;
-    static constexpr int SV = BV / 2 + 2;
-    // Decayed operands read along dk (token-major): bf16 hi half, lo half, 8 dwords
-    // of pad (16-byte blocks per row = 2 mod 32: conflict-free operand reads).
-    static constexpr int OPR = DK + 8;
-    // Token-minor rows (a row per channel): four 16-byte blocks of four tokens,
-    // [hi x4 | lo x4] in bf16 or four fp32.  Key rows carry two blocks of pad; value
-    // rows swizzle their blocks instead (vblk).
-    static constexpr int TMR = 24;
-    static constexpr int VMR = 16;
-    // fp32 summed decays for the exact path (token-major).
-    static constexpr int AR = DK + 4, BR = BV + 4;
-    // One staged raw chunk.
-    static constexpr int ST_Q = 0;
-    static constexpr int ST_K = ST_Q + kGChunk * SQ;
-    static constexpr int ST_G = ST_K + kGChunk * SQ;  // bf16 or fp32 key gate
-    static constexpr int ST_V = ST_G + kGChunk * SG32;
-    static constexpr int ST_GV = ST_V + kGChunk * SV;
-    static constexpr int ST_SIZE = ST_GV + kGChunk * SV;
-    // One set of decayed operands.
-    static constexpr int D_QH = 0;
-    static constexpr int D_KP = D_QH + kGChunk * OPR;
-    static constexpr int D_KT = D_KP + kGChunk * OPR;
-    static constexpr int D_VP = D_KT + DK * TMR;
-    static constexpr int D_VT = D_VP + BV * VMR;
-    static constexpr int D_BT = D_VT + BV * VMR;
-    static constexpr int D_PRE = D_BT + BV * VMR;
-    static constexpr int D_POST = D_PRE + DK;
-    static constexpr int D_EB = D_POST + DK;
-    static constexpr int D_SIZE = D_EB + BV;
-    static constexpr int OFF_ST = 0;
-    static constexpr int OFF_D = OFF_ST + 2 * ST_SIZE;
-    static constexpr int OFF_A = OFF_D + 2 * D_SIZE;
-    static constexpr int OFF_B = OFF_A + kGChunk * AR;
-    static constexpr int OFF_OI = OFF_B + kGChunk * BR;
-    static constexpr int OFF_W = OFF_OI + kGChunk * BR;
-    static constexpr int DWORDS = OFF_W + kGChunk * 17;
-    // Staging: 4-element pieces of a chunk, spread over the producer threads.
-    static constexpr int KITEMS = kGChunk * DK / 4, VITEMS = kGChunk * BV / 4;
-    static constexpr int KPER = (KITEMS + PT - 1) / PT, VPER = (VITEMS + PT - 1) / PT;
-    // Prep items: channel pairs x quarters.
-    static constexpr int KPREP = 2 * DK, VPREP = 2 * BV;
-    static_assert(DK % 32 == 0 && DK <= 128, "dk must be 32, 64 or 128");
-    static_assert(ST_SIZE % 4 == 0 && D_SIZE % 4 == 0 && OFF_A % 4 == 0 && OFF_OI % 4 == 0 && D_PRE % 4 == 0,
-                  "16-byte alignment");
-    static_assert(DWORDS * 4 <= kLdsBudget, "LDS budget");
-};
-
-// A vector of raw words at a byte offset from a workgroup-uniform base (the offset
-// fits 32 bits, so the load takes the scalar-base form).
-template <typename T>
-__device__ inline T load_at(const void* base, uint32_t byte_off) {
-    return *reinterpret_cast<const T*>(static_cast<const char*>(base) + byte_off);
-}
-
-__device__ inline f32x4 mfma_bf16_w(u32x4 a, u32x4 b, f32x4 c) {
-    return mfma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c);
-}
-// hi * lo term of a 16-token contraction as a 16x16x32 MFMA with the upper half of
-// k zeroed.  (A 16x16x16 MFMA accumulating onto a 16x16x32 result read part of the
-// accumulator stale in testing: no wait states were placed between the two
-// opcodes.  Same-opcode chains are fine.)
-__device__ inline f32x4 mfma_bf16_half(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
-    return mfma_bf16_w(u32x4{a0, a1, 0u, 0u}, u32x4{b0, b1, 0u, 0u}, c);
-}
-// bf16 truncations of a and b in one word (a in the low half).
-__device__ inline uint32_t hi_pack(float a, float b) {
-    return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
-__device__ inline float lo_part(float x) { return x - __uint_as_float(__float_as_uint(x) & 0xffff0000u); }
-// bf16 roundings of what the truncations of a and b leave (exact in fp32).
-__device__ inline uint32_t lo_pack(float a, float b) { return pack_bf16x2(lo_part(a), lo_part(b)); }
-// Lane k of this lane's quad.
-template <int K>
-__device__ inline float quad_get(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), K * 0x55, 0xF, 0xF, false));
-}
-// Dword of a token-major operand row that holds channels 2pp, 2pp+1.  Channel
-// 32s + 16h + 4g + r sits at position 32s + 8g + 4h + r, so that the eight
-// positions an MFMA lane group reads for block s are the channels whose state rows
-// that lane group holds in tiles 2s and 2s+1 (accumulator layout).
-__host__ __device__ constexpr int gpos_dword(int pp) {
-    return 16 * (pp >> 4) + 4 * ((pp >> 1) & 3) + 2 * ((pp >> 3) & 1) + (pp & 1);
-}
-// Dword offset of block b (tokens 4b .. 4b+3) of value row r: the blocks of rows
-// 8 .. 15 mod 16 are swapped in pairs, so the 32 lanes of a half-wave reading
-// (row, block lg) hit distinct banks.
-__host__ __device__ constexpr int vblk(int r, int b) { return 16 * r + 4 * (b ^ ((r >> 2) & 2)); }
-// Inclusive sums of a quarter's log2-decays (la, per token and channel) over the
-// chunk: the lane quad holds the four quarters of a channel pair.  a = A_t of this
-// quarter's tokens, tot = A_15.
-__device__ inline void quarter_sums(const float (&la)[4][2], int tq, float (&a)[4][2], float (&tot)[2]) {
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-        float cs[4];
-        float acc = 0.f;
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
-            acc += la[tau][x];
-            cs[tau] = acc;
-        }
-        const float s0 = quad_get<0>(acc), s1 = quad_get<1>(acc), s2 = quad_get<2>(acc), s3 = quad_get<3>(acc);
-        const float s01 = s0 + s1, s012 = s01 + s2;
-        // sum of the earlier quarters, in the order that gives s012 for tq = 3
-        const float pre = ((tq > 0 ? s0 : 0.f) + (tq > 1 ? s1 : 0.f)) + (tq > 2 ? s2 : 0.f);
-#pragma unroll
-        for (int tau = 0; tau < 4; ++tau) a[tau][x] = pre + cs[tau];
-        tot[x] = s012 + s3;
-    }
-}
-
-template <int DK, int NW, bool GF32>
-__global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams p) {
-    using Cfg = GatedBCfg<DK, NW>;
-    constexpr int BV = Cfg::BV, NT = Cfg::NT, PT = Cfg::PT, MT = Cfg::MT, KB = Cfg::KB;
-    constexpr int SQ = Cfg::SQ, SV = Cfg::SV, OPR = Cfg::OPR, TMR = Cfg::TMR, AR = Cfg::AR, BR = Cfg::BR;
-    constexpr int SGR = GF32 ? Cfg::SG32 : SQ;  // row stride of the staged key gate
-    __shared__ __attribute__((aligned(16))) uint32_t sm[Cfg::DWORDS];
-    __shared__ int wide_flag[3];  // per chunk mod 3: take the exact VALU path
-    float* Af = reinterpret_cast<float*>(sm + Cfg::OFF_A);
-    float* Bf = reinterpret_cast<float*>(sm + Cfg::OFF_B);
-    float* OIf = reinterpret_cast<float*>(sm + Cfg::OFF_OI);
-    float* Wf = reinterpret_cast<float*>(sm + Cfg::OFF_W);
-    auto staged = [&](int c) __attribute__((always_inline)) -> uint32_t* { return sm + Cfg::OFF_ST + (c & 1) * Cfg::ST_SIZE; };
-    auto derived = [&](int c) __attribute__((always_inline)) -> uint32_t* { return sm + Cfg::OFF_D + (c & 1) * Cfg::D_SIZE; };
-
-    Work wk;
-    if (!decode_work(p, wk)) return;
-    const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool producer = wv >= NW;
-    const int ptid = tid - PT;  // producer thread index
-    const int H = p.num_heads, dv = p.dv;
-    const int64_t L = wk.len;
-    const int nch = (int)((L + kGChunk - 1) / kGChunk);
-    const bool rev = p.reverse_gated != 0;
-    const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
-    const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
-    const int j = 16 * wv + lr;       // matrix waves: this lane's column inside the block
-    const int vcol = wk.vb * BV + j;  // ... of v and o
-    const int64_t qrow = (int64_t)H * DK, krow = (int64_t)p.num_kv_heads * DK;
-    const int64_t vrow = (int64_t)p.num_kv_heads * dv, gvrow = (int64_t)H * dv;
-    const int64_t qoff = (int64_t)wk.h * DK, koff = (int64_t)wk.kvh * DK;
-    const int64_t voff = (int64_t)wk.kvh * dv + wk.vb * BV, gvoff = (int64_t)wk.h * dv + wk.vb * BV;
-    // Chunk c holds the rows [low, low + nv) of the flattened token axis (in either
-    // direction); token t of the chunk is row low + lrow(t).  Offsets inside a chunk
-    // stay 32-bit (the host bounds 16 rows of every array below 2^31 bytes).
-    auto chunk_nv = [&](int c) __attribute__((always_inline)) -> int { return (int)min((int64_t)kGChunk, L - (int64_t)c * kGChunk); };
-    auto chunk_low = [&](int c, int nv) __attribute__((always_inline)) -> int64_t {
-        const int64_t p0 = (int64_t)c * kGChunk;
-        return rev ? wk.start + L - p0 - nv : wk.start + p0;
-    };
-    auto lrow = [&](int t, int nv) __attribute__((always_inline)) -> uint32_t { return (uint32_t)(rev ? nv - 1 - t : t); };
-
-    f32x4 S[MT];
-    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
-    if (!producer) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
-    }
-
-    // Producer staging registers: raw words of this thread's pieces (bf16: words 0
-    // and 1).  Two sets: chunk m goes through set m & 1, loaded two chunks ahead of
-    // its store to LDS.  Absent gates are staged as zeros.
-    using GateW = typename std::conditional<GF32, u32x4, u32x2>::type;  // four gate values
-    struct StageRegs {
-        u32x2 q[Cfg::KPER], k[Cfg::KPER], v[Cfg::VPER], b[Cfg::VPER];
-        GateW a[Cfg::KPER];
-        uint32_t kok, vok;  // bit s: piece s lies inside the sequence
-    };
-    StageRegs R0, R1;
-    auto load_chunk = [&](int c, StageRegs& r) __attribute__((always_inline)) {
-        u32x2(&rq)[Cfg::KPER] = r.q;
-        u32x2(&rk)[Cfg::KPER] = r.k;
-        GateW(&ra)[Cfg::KPER] = r.a;
-        u32x2(&rv)[Cfg::VPER] = r.v;
-        u32x2(&rb)[Cfg::VPER] = r.b;
-        uint32_t& kok = r.kok;
-        uint32_t& vok = r.vok;
-        const int nv = chunk_nv(c);
-        const int64_t low = chunk_low(c, nv);
-        const uint16_t* qb = static_cast<const uint16_t*>(p.q) + (low * qrow + qoff);
-        const uint16_t* kb = static_cast<const uint16_t*>(p.k) + (low * krow + koff);
-        const uint16_t* vb = static_cast<const uint16_t*>(p.v) + (low * vrow + voff);
-        // An absent gate re-reads q (v) at the same offsets: the same number of loads
-        // every chunk keeps the waits on the earlier register set exact.
-        constexpr uint32_t gsz = GF32 ? 4 : 2;
-        const char* gb = has_g ? static_cast<const char*>(p.g) + (low * qrow + qoff) * gsz
-                               : reinterpret_cast<const char*>(qb);
-        const char* gvb = has_gv ? reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.gv) + (low * gvrow + gvoff))
-                                 : reinterpret_cast<const char*>(vb);
-        const uint32_t gvstride = (uint32_t)(has_gv ? gvrow : vrow);
-        kok = vok = 0;
-#pragma unroll
-        for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = ptid + s * PT;
-            const int t = item / (DK / 4), c4 = item % (DK / 4);
-            const bool ok = item < Cfg::KITEMS && t < nv;
-            kok |= (ok ? 1u : 0u) << s;
-            const uint32_t rr = ok ? lrow(t, nv) : 0u;  // rows past the end read row 0
-            rq[s] = load_at<u32x2>(qb, 2 * (rr * (uint32_t)qrow + 4 * c4));
-            rk[s] = load_at<u32x2>(kb, 2 * (rr * (uint32_t)krow + 4 * c4));
-            ra[s] = load_at<GateW>(gb, gsz * (rr * (uint32_t)qrow + 4 * c4));
-        }
-#pragma unroll
-        for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = ptid + s * PT;
-            const int t = item / (BV / 4), c4 = item % (BV / 4);
-            const bool ok = item < Cfg::VITEMS && t < nv;
-            vok |= (ok ? 1u : 0u) << s;
-            const uint32_t rr = ok ? lrow(t, nv) : 0u;
-            rv[s] = load_at<u32x2>(vb, 2 * (rr * (uint32_t)vrow + 4 * c4));
-            rb[s] = load_at<u32x2>(gvb, 2 * (rr * gvstride + 4 * c4));
-        }
-    };
-    // Raw words to LDS (zero past the end); nothing is converted here.
-    auto store_chunk = [&](int c, const StageRegs& r) __attribute__((always_inline)) {
-        const u32x2(&rq)[Cfg::KPER] = r.q;
-        const u32x2(&rk)[Cfg::KPER] = r.k;
-        const GateW(&ra)[Cfg::KPER] = r.a;
-        const u32x2(&rv)[Cfg::VPER] = r.v;
-        const u32x2(&rb)[Cfg::VPER] = r.b;
-        const uint32_t kok = r.kok, vok = r.vok;
-        uint32_t* st = staged(c);
-        const u32x2 z2 = {0u, 0u};
-        const u32x4 z4 = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = ptid + s * PT;
-            if (item < Cfg::KITEMS) {
-                const int t = item / (DK / 4), c4 = item % (DK / 4);
-                const bool ok = (kok >> s) & 1u;
-                lds_store<u32x2>(st + Cfg::ST_Q + t * SQ + 2 * c4, ok ? rq[s] : z2);
-                lds_store<u32x2>(st + Cfg::ST_K + t * SQ + 2 * c4, ok ? rk[s] : z2);
-                const bool gok = ok && has_g;
-                if constexpr (GF32) lds_store<u32x4>(st + Cfg::ST_G + t * SGR + 4 * c4, gok ? ra[s] : z4);
-                else lds_store<u32x2>(st + Cfg::ST_G + t * SGR + 2 * c4, gok ? ra[s] : z2);
-            }
-        }
-#pragma unroll
-        for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = ptid + s * PT;
-            if (item < Cfg::VITEMS) {
-                const int t = item / (BV / 4), c4 = item % (BV / 4);
-                const bool ok = (vok >> s) & 1u;
-                lds_store<u32x2>(st + Cfg::ST_V + t * SV + 2 * c4, ok ? rv[s] : z2);
-                if (has_gv) lds_store<u32x2>(st + Cfg::ST_GV + t * SV + 2 * c4, ok ? rb[s] : z2);
-            }
-        }
-    };
-
-    // Prep of chunk c (producer waves): staged(c) -> derived(c), the summed decays
-    // (exact path) and the chunk's flag.
-    auto prep_chunk = [&](int c) __attribute__((always_inline)) {
-        const uint32_t* st = staged(c);
-        uint32_t* d = derived(c);
-        const int nv = chunk_nv(c);
-        int* flag = &wide_flag[c % 3];
-        // Key channels 2pp, 2pp+1, tokens 4tq .. 4tq+3.
-#pragma unroll
-        for (int r = 0; r < (Cfg::KPREP + PT - 1) / PT; ++r) {
-            const int it = ptid + r * PT;
-            if (Cfg::KPREP % PT != 0 && it >= Cfg::KPREP) break;
-            const int pp = it >> 2, tq = it & 3;
-            float la[4][2];
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau) {
-                const int t = 4 * tq + tau;
-                float g0, g1;
-                if constexpr (GF32) {
-                    const f32x2 g = lds_load<f32x2>(st + Cfg::ST_G + t * SGR + 2 * pp);
-                    g0 = g[0];
-                    g1 = g[1];
-                } else {
-                    const uint32_t w = st[Cfg::ST_G + t * SGR + pp];
-                    g0 = bf16_lo(w);
-                    g1 = bf16_hi(w);
-                }
-                const bool tv = t < nv;
-                la[tau][0] = tv ? kLog2e * g0 + gg2 : 0.f;
-                la[tau][1] = tv ? kLog2e * g1 + gg2 : 0.f;
-            }
-            float a[4][2], tot[2];
-            quarter_sums(la, tq, a, tot);
-            const bool wl = !(tot[0] >= -kGSpan) || !(tot[1] >= -kGSpan);
-            if (wl) *flag = 1;
-            if (tq == 3) {
-                const f32x2 e15 = {hw_exp2(tot[0]), hw_exp2(tot[1])}, one = {1.f, 1.f};
-                lds_store<f32x2>(d + Cfg::D_PRE + 2 * pp, wl ? e15 : one);
-                lds_store<f32x2>(d + Cfg::D_POST + 2 * pp, wl ? one : e15);
-            }
-            // kp = k ./ e (narrow pair) or k .* 2^{A_15 - A} (wide pair)
-            const float off[2] = {wl ? tot[0] : 0.f, wl ? tot[1] : 0.f};
-            float qh[4][2], kp[4][2], kl[4][2];
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau) {
-                const int t = 4 * tq + tau;
-                lds_store<f32x2>(Af + t * AR + 2 * pp, f32x2{a[tau][0], a[tau][1]});
-                const uint32_t qw = st[Cfg::ST_Q + t * SQ + pp], kw = st[Cfg::ST_K + t * SQ + pp];
-                const float qv[2] = {bf16_lo(qw), bf16_hi(qw)}, kv[2] = {bf16_lo(kw), bf16_hi(kw)};
-#pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    qh[tau][x] = qv[x] * hw_exp2(a[tau][x]);
-                    kp[tau][x] = kv[x] * hw_exp2(off[x] - a[tau][x]);
-                    kl[tau][x] = lo_part(kp[tau][x]);
-                }
-            }
-            const int pd = gpos_dword(pp);
-#pragma unroll
-            for (int tau = 0; tau < 4; ++tau) {
-                uint32_t* qr = d + Cfg::D_QH + (4 * tq + tau) * OPR + pd;
-                uint32_t* kr = d + Cfg::D_KP + (4 * tq + tau) * OPR + pd;
-                qr[0] = hi_pack(qh[tau][0], qh[tau][1]);
-                qr[DK / 2] = lo_pack(qh[tau][0], qh[tau][1]);
-                kr[0] = hi_pack(kp[tau][0], kp[tau][1]);
-                kr[DK / 2] = pack_bf16x2(kl[tau][0], kl[tau][1]);
-            }
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-                lds_store<u32x4>(d + Cfg::D_KT + (2 * pp + x) * TMR + 4 * tq,
-                                 u32x4{hi_pack(kp[0][x], kp[1][x]), hi_pack(kp[2][x], kp[3][x]),
-                                       pack_bf16x2(kl[0][x], kl[1][x]), pack_bf16x2(kl[2][x], kl[3][x])});
-        }
-        // Value columns 2qq, 2qq+1 of the block, tokens 4tq .. 4tq+3; the last
-        // producer threads take these items (the key prep fills the first ones when
-        // the item counts do not divide evenly).
-#pragma unroll
-        for (int r = 0; r < (Cfg::VPREP + PT - 1) / PT; ++r) {
-            const int it = (PT - 1 - ptid) + r * PT;
-            if (Cfg::VPREP % PT != 0 && it >= Cfg::VPREP) break;
-            const int qq = it >> 2, tq = 3 - (it & 3);
-            if (has_gv) {
-                float la[4][2];
-#pragma unroll
-                for (int tau = 0; tau < 4; ++tau) {
-                    const int t = 4 * tq + tau;
-                    const uint32_t w = st[Cfg::ST_GV + t * SV + qq];
-                    const bool tv = t < nv;
-                    la[tau][0] = tv ? kLog2e * bf16_lo(w) : 0.f;
-                    la[tau][1] = tv ? kLog2e * bf16_hi(w) : 0.f;
-                }
-                float b[4][2], tot[2];
-                quarter_sums(la, tq, b, tot);
-                const bool wl = !(tot[0] >= -kGSpan) || !(tot[1] >= -kGSpan);
-                if (wl) *flag = 1;
-                const float e15[2] = {hw_exp2(tot[0]), hw_exp2(tot[1])};
-                if (tq == 3) lds_store<f32x2>(d + Cfg::D_EB + 2 * qq, f32x2{e15[0], e15[1]});
-                float bt[4][2], vp[4][2], vt[4][2];
-#pragma unroll
-                for (int tau = 0; tau < 4; ++tau) {
-                    const int t = 4 * tq + tau;
-                    lds_store<f32x2>(Bf + t * BR + 2 * qq, f32x2{b[tau][0], b[tau][1]});
-                    const uint32_t vw = st[Cfg::ST_V + t * SV + qq];
-                    const float vv[2] = {bf16_lo(vw), bf16_hi(vw)};
-#pragma unroll
-                    for (int x = 0; x < 2; ++x) {
-                        // wide: v .* 2^{-B} is not needed (and may overflow)
-                        const float e = hw_exp2(b[tau][x]), y = hw_exp2(wl ? tot[x] - b[tau][x] : -b[tau][x]);
-                        bt[tau][x] = e;
-                        vp[tau][x] = wl ? 0.f : vv[x] * y;
-                        vt[tau][x] = wl ? vv[x] * y : vp[tau][x] * e15[x];
-                    }
-                }
-#pragma unroll
-                for (int x = 0; x < 2; ++x) {
-                    const int row = vblk(2 * qq + x, tq);
-                    lds_store<f32x4>(reinterpret_cast<float*>(d + Cfg::D_BT) + row,
-                                     f32x4{bt[0][x], bt[1][x], bt[2][x], bt[3][x]});
-                    lds_store<u32x4>(d + Cfg::D_VP + row, u32x4{hi_pack(vp[0][x], vp[1][x]), hi_pack(vp[2][x], vp[3][x]),
-                                                               lo_pack(vp[0][x], vp[1][x]), lo_pack(vp[2][x], vp[3][x])});
-                    lds_store<u32x4>(d + Cfg::D_VT + row, u32x4{hi_pack(vt[0][x], vt[1][x]), hi_pack(vt[2][x], vt[3][x]),
-                                                               lo_pack(vt[0][x], vt[1][x]), lo_pack(vt[2][x], vt[3][x])});
-                }
-            } else {  // v is exact in bf16: copy it token-minor, hi only
-                uint32_t w[4];
-#pragma unroll
-                for (int tau = 0; tau < 4; ++tau) w[tau] = st[Cfg::ST_V + (4 * tq + tau) * SV + qq];
-                lds_store<u32x2>(d + Cfg::D_VT + vblk(2 * qq, tq), u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
-                                                                       __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)});
-                lds_store<u32x2>(d + Cfg::D_VT + vblk(2 * qq + 1, tq),
-                                 u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
-                                       __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)});
-            }
-        }
-    };
-
-    // Exact intra term of a wide chunk (all threads, between barriers): W, then
-    // OI = W (v .* 2^{B_t - B_u}), from the raw staged chunk and the summed decays.
-    auto exact_chunk = [&](int c) __attribute__((always_inline)) {
-        const uint32_t* st = staged(c);
-        for (int e = tid; e < kGChunk * kGChunk; e += NT) {
-            const int t = e >> 4, u = e & 15;
-            float w = 0.f;
-            if (u <= t) {
-                const uint32_t* qt = st + Cfg::ST_Q + t * SQ;
-                const uint32_t* ku = st + Cfg::ST_K + u * SQ;
-                const float* at = Af + t * AR;
-                const float* au = Af + u * AR;
-#pragma unroll 4
-                for (int i = 0; i < DK; i += 4) {
-                    const u32x2 q2 = lds_load<u32x2>(qt + i / 2), k2 = lds_load<u32x2>(ku + i / 2);
-                    const f32x4 a4 = lds_load<f32x4>(at + i), b4 = lds_load<f32x4>(au + i);
-                    const float q4[4] = {bf16_lo(q2[0]), bf16_hi(q2[0]), bf16_lo(q2[1]), bf16_hi(q2[1])};
-                    const float k4[4] = {bf16_lo(k2[0]), bf16_hi(k2[0]), bf16_lo(k2[1]), bf16_hi(k2[1])};
-#pragma unroll
-                    for (int x = 0; x < 4; ++x) w += q4[x] * k4[x] * hw_exp2(a4[x] - b4[x]);
-                }
-            }
-            Wf[t * 17 + u] = w;
-        }
-        lds_barrier();
-        for (int e = tid; e < kGChunk * BV; e += NT) {
-            const int t = e / BV, jj = e % BV;
-            const float bt = has_gv ? Bf[t * BR + jj] : 0.f;
-            float acc = 0.f;
-            for (int u = 0; u <= t; ++u) {
-                const float vu = bf16_half(st[Cfg::ST_V + u * SV + (jj >> 1)], jj & 1);
-                const float dd = has_gv ? hw_exp2(bt - Bf[u * BR + jj]) : 1.f;
-                acc += Wf[t * 17 + u] * vu * dd;
-            }
-            OIf[t * BR + jj] = acc;
-        }
-        lds_barrier();
-    };
-
-    // Matrix phase of chunk c (matrix waves).
-    auto matrix_chunk = [&](int c, bool fast) __attribute__((always_inline)) {
-        const uint32_t* d = derived(c);
-        const uint32_t* QHw = d + Cfg::D_QH;
-        const uint32_t* KPw = d + Cfg::D_KP;
-        const float* BTf = reinterpret_cast<const float*>(d + Cfg::D_BT);
-        const int nv = chunk_nv(c);
-        // Inter-chunk part (q .* 2^A) S: the state tile pair (2s, 2s+1), split into
-        // bf16 hi + lo, is the B operand of dk block s.  Fast path: W^T = (k ./ e)
-        // (q .* e)^T in the same loop (q .* e is its B operand too); lane holds
-        // W[t = lr][u = 4lg + ii].
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 O;
-        const int vrow_j = vblk(j, lg);
-        if (fast) {
-            f32x4 Oa = z, Ob = z, Oc = z, Wa = z, Wb = z, Wc = z;
-#pragma unroll
-            for (int s = 0; s < KB; ++s) {
-                const uint32_t* qr = QHw + lr * OPR + 16 * s + 4 * lg;
-                const uint32_t* kr = KPw + lr * OPR + 16 * s + 4 * lg;
-                const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
-                const u32x4 kh = lds_load<u32x4>(kr), kl = lds_load<u32x4>(kr + DK / 2);
-                const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
-                const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
-                                  hi_pack(s1[2], s1[3])};
-                const u32x4 sl = {lo_pack(s0[0], s0[1]), lo_pack(s0[2], s0[3]), lo_pack(s1[0], s1[1]),
-                                  lo_pack(s1[2], s1[3])};
-                Oa = mfma_bf16_w(qh, sh, Oa);
-                Wa = mfma_bf16_w(kh, qh, Wa);
-                Ob = mfma_bf16_w(qh, sl, Ob);
-                Wb = mfma_bf16_w(kh, ql, Wb);
-                Oc = mfma_bf16_w(ql, sh, Oc);
-                Wc = mfma_bf16_w(kl, qh, Wc);
-            }
-            O = (Oa + Ob) + Oc;
-            f32x4 W = (Wa + Wb) + Wc;
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                if (4 * lg + ii > lr) W[ii] = 0.f;  // causal: u <= t
-            // Intra term W (v .* 2^{-B}): k = 8lg + e covers the tokens 4lg + (e & 3)
-            // with W's hi (e < 4) and lo (e >= 4) parts, against v's hi part twice.
-            const u32x4 vpx = lds_load<u32x4>(d + (has_gv ? Cfg::D_VP : Cfg::D_VT) + vrow_j);
-            const u32x4 wa = {hi_pack(W[0], W[1]), hi_pack(W[2], W[3]), lo_pack(W[0], W[1]), lo_pack(W[2], W[3])};
-            f32x4 Oi = mfma_bf16_w(wa, u32x4{vpx[0], vpx[1], vpx[0], vpx[1]}, z);
-            if (has_gv) Oi = mfma_bf16_half(wa[0], wa[1], vpx[2], vpx[3], Oi);
-            O += Oi;
-            if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
-        } else {
-            f32x4 Oa = z, Ob = z, Oc = z;
-#pragma unroll
-            for (int s = 0; s < KB; ++s) {
-                const uint32_t* qr = QHw + lr * OPR + 16 * s + 4 * lg;
-                const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
-                const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
-                const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
-                                  hi_pack(s1[2], s1[3])};
-                const u32x4 sl = {lo_pack(s0[0], s0[1]), lo_pack(s0[2], s0[3]), lo_pack(s1[0], s1[1]),
-                                  lo_pack(s1[2], s1[3])};
-                Oa = mfma_bf16_w(qh, sh, Oa);
-                Ob = mfma_bf16_w(qh, sl, Ob);
-                Oc = mfma_bf16_w(ql, sh, Oc);
-            }
-            O = (Oa + Ob) + Oc;
-            if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[ii] += OIf[(4 * lg + ii) * BR + j];
-        }
-        {
-            const int64_t orow = (int64_t)H * dv;
-            char* ob = reinterpret_cast<char*>(p.o + (chunk_low(c, nv) * orow + (int64_t)wk.h * dv + wk.vb * BV));
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int t = 4 * lg + ii;
-                if (t < nv) *reinterpret_cast<float*>(ob + 4 * (lrow(t, nv) * (uint32_t)orow + j)) = p.scale * O[ii];
-            }
-        }
-
-        // State update: S <- post .* (pre .* 2^{B_15}^T .* S + kp^T vt), contracting
-        // over the 16 tokens with kp's hi and lo parts in one k range (token-minor
-        // operands: lane group lg reads tokens 4lg .. 4lg+3).
-        const float* PREf = reinterpret_cast<const float*>(d + Cfg::D_PRE);
-        const float* POSTf = reinterpret_cast<const float*>(d + Cfg::D_POST);
-        const float eb = has_gv ? reinterpret_cast<const float*>(d + Cfg::D_EB)[j] : 1.f;
-        if (!fast) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const f32x4 pre = lds_load<f32x4>(PREf + 16 * mt + 4 * lg);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= pre[ii] * eb;
-            }
-        } else if (has_gv) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) S[mt] *= eb;
-        }
-        const u32x4 vtx = lds_load<u32x4>(d + Cfg::D_VT + vrow_j);
-        const u32x4 vt2 = {vtx[0], vtx[1], vtx[0], vtx[1]};
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const u32x4 ktx = lds_load<u32x4>(d + Cfg::D_KT + (16 * mt + lr) * TMR + 4 * lg);
-            S[mt] = mfma_bf16_w(ktx, vt2, S[mt]);
-            if (has_gv) S[mt] = mfma_bf16_half(ktx[0], ktx[1], vtx[2], vtx[3], S[mt]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 post = lds_load<f32x4>(POSTf + 16 * mt + 4 * lg);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= post[ii];
-        }
-    };
-
-    // Pipeline: before the barrier that opens step c, the producers have staged
-    // chunk c+1 and derived chunk c.  During step c the matrix waves compute chunk c
-    // while the producers derive chunk c+1, stage chunk c+2 (into the buffer chunk c
-    // used) and load chunk c+4 (chunks c+3 and c+4 are in flight).  A wide chunk
-    // first takes the exact path with all waves, before its staged buffer is
-    // reused.  Chunk flags cycle through three slots: slot (c+2) mod 3 is cleared
-    // during step c, after every read of chunk c-1's flag and before chunk c+2's
-    // prep.  The two roles run separate loops with the same barriers in the same
-    // order; the producers' steps run in pairs so that each register set has a
-    // fixed name.
-    if (producer) {
-        if (ptid == 0) wide_flag[0] = wide_flag[1] = wide_flag[2] = 0;
-        // Every step stores and loads one chunk (past the end: the last chunk again,
-        // into a buffer no prep reads), so the loads in flight are always the two
-        // register sets in order and the waits before each store are exact.
-        auto clampc = [&](int m) __attribute__((always_inline)) -> int { return min(m, nch - 1); };
-        if (nch > 0) {
-            load_chunk(0, R0);
-            load_chunk(clampc(1), R1);
-            store_chunk(0, R0);
-            load_chunk(clampc(2), R0);
-        }
-        lds_barrier();
-        if (nch > 0) {
-            prep_chunk(0);
-            store_chunk(1, R1);
-            load_chunk(clampc(3), R1);
-            auto step = [&](int c, StageRegs& r) __attribute__((always_inline)) {  // r: chunks c+2, c+4
-                if (c < nch) {
-                    lds_barrier();  // chunk c derived, chunk c+1 staged, chunk c's flag final
-                    if (wide_flag[c % 3] != 0) exact_chunk(c);
-                }
-                if (c + 1 < nch) {
-                    if (ptid == 0) wide_flag[(c + 2) % 3] = 0;
-                    prep_chunk(c + 1);
-                }
-                store_chunk(c + 2, r);
-                load_chunk(clampc(c + 4), r);
-            };
-            for (int c = 0; c < nch; c += 2) {
-                step(c, R0);
-                step(c + 1, R1);
-            }
-        }
-    } else {
-        lds_barrier();
-        for (int c = 0; c < nch; ++c) {
-            lds_barrier();
-            const bool fast = wide_flag[c % 3] == 0;
-            if (!fast) exact_chunk(c);
-            matrix_chunk(c, fast);
-        }
-    }
-
-    if (!producer && p.final_state) {
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = S[mt][ii];
-    }
-}
-
-// Four consecutive input elements as floats (bf16 words or fp32).
-template <bool BF16>
-__device__ inline f32x4 load4(const void* base, int64_t i) {
-    return raw_to_f32(load4_raw<!BF16>(base, i), !BF16);
-}
-
-// Sum of the two key gates into one fp32 gate (the gated kernel reads one).
-template <bool BF16>
-__global__ __launch_bounds__(256) void gate_sum_kernel(const void* __restrict__ g, const void* __restrict__ gk,
-                                                       float* __restrict__ out, int64_t n4) {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
-        *reinterpret_cast<f32x4*>(out + 4 * i) = load4<BF16>(g, 4 * i) + load4<BF16>(gk, 4 * i);
-}
-
-// ---------------------------------------------------------------------------
 // Gradient sweeps under grouped-query attention: the sum of per-query-head
 // gradients into their kv head, streamed in 16-byte pieces.
 // ---------------------------------------------------------------------------
@@ -2146,13 +1027,6 @@ hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hi
     return hipErrorInvalidValue;
 }
 
-namespace {
-int stream_blocks(int64_t n4) {
-    const int64_t b = (n4 + 255) / 256;
-    return (int)(b < 4096 ? (b > 0 ? b : 1) : 4096);
-}
-}  // namespace
-
 hipError_t launch_group_sum(const float* part, float* out, int64_t rows, int H, int Hkv, int d, hipStream_t s) {
     const int64_t n4 = rows * Hkv * (d / 4);
     if (n4 == 0) return hipSuccess;
@@ -2190,50 +1064,6 @@ hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, floa
     hipLaunchKernelGGL(seg_scan_kernel, grid, dim3(256), 0, s, dS, init, s_in, final_state, g_gamma, H, P, seg_len,
                        seqlen, elems4, rev ? 1 : 0);
     return hipGetLastError();
-}
-
-namespace {
-template <int DK, int NW>
-hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
-    const dim3 grid(fwd_grid_size(p));
-    // bf16: NW matrix waves plus NW producer waves; fp32: NW waves
-    const dim3 block_bf16(GatedBCfg<DK, NW>::NT), block_f32(64 * NW);
-    if (bf16 && p.gk_is_f32)
-        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true>), grid, block_bf16, 0, s, p);
-    else if (bf16)
-        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, false>), grid, block_bf16, 0, s, p);
-    else
-        hipLaunchKernelGGL((gated_kernel<DK, NW, false, true>), grid, block_f32, 0, s, p);
-    return hipGetLastError();
-}
-template <int DK>
-hipError_t launch_gated_dk(const FwdParams& p, int nw, bool bf16, hipStream_t s) {
-    if (nw == 4) return launch_gated_t<DK, 4>(p, bf16, s);
-    if (nw == 1) return launch_gated_t<DK, 1>(p, bf16, s);
-    return hipErrorInvalidValue;
-}
-}  // namespace
-
-hipError_t launch_gate_sum(const void* g, const void* gk, float* out, int64_t n, int in_dtype, hipStream_t s) {
-    const int64_t n4 = n / 4;
-    if (n4 == 0) return hipSuccess;
-    if (in_dtype == 0)
-        hipLaunchKernelGGL((gate_sum_kernel<true>), dim3(stream_blocks(n4)), dim3(256), 0, s, g, gk, out, n4);
-    else
-        hipLaunchKernelGGL((gate_sum_kernel<false>), dim3(stream_blocks(n4)), dim3(256), 0, s, g, gk, out, n4);
-    return hipGetLastError();
-}
-
-bool have_gated_kernel(int dk, int nw) { return (dk == 32 || dk == 64 || dk == 128) && (nw == 1 || nw == 4); }
-
-hipError_t launch_gated(const FwdParams& p, int in_dtype, int nw, hipStream_t s) {
-    const bool bf16 = in_dtype == 0;
-    switch (p.dk) {
-        case 32: return launch_gated_dk<32>(p, nw, bf16, s);
-        case 64: return launch_gated_dk<64>(p, nw, bf16, s);
-        case 128: return launch_gated_dk<128>(p, nw, bf16, s);
-        default: return hipErrorInvalidValue;
-    }
 }
 
 hipError_t launch_seq_order(const int32_t* cu, int num_seqs, int seqlen, int32_t* order, hipStream_t s) {
