@@ -124,3 +124,53 @@ def test_gla_long_d128_sampled():
                                                 scale=w.scale)
         check(o[b:b + 1, :, h:h + 1].cpu().numpy(), o_ref, TOL["bf16"], f"gla n32768 ({b}, {h}) o")
         check(fs[b:b + 1, h:h + 1].cpu().numpy(), fs_ref, TOL["bf16"], f"gla n32768 ({b}, {h}) final_state")
+
+
+def test_gated_bf16_g_plus_gk_d128_reverse():
+    """g and gk both given (summed into one fp32 key gate first), fixed length, reverse,
+    GQA, initial state and g_gamma."""
+    w = inputs.Workload("gated_ggk", 2, 777, 4, 2, 128, 128, "bf16", 3, 12, reverse=True, init_std=0.3, seed=58)
+    _compare(w, ("g", "gk"), gmax=0.3)
+
+
+@pytest.mark.parametrize("shape", [(32, 64), (32, 32), (128, 256), (64, 48)])
+def test_gated_bf16_head_dims(shape):
+    """dk 32 / 64 / 128 with one- and four-wave value blocks (dv 32, 48, 64, 256)."""
+    dk, dv = shape
+    w = inputs.Workload(f"gated_dk{dk}_dv{dv}", 2, 321, 4, 4, dk, dv, "bf16", 2, 12, init_std=0.3, seed=59 + dk + dv)
+    _compare(w, ("g", "gv"), gmax=0.4, tag=f" dk{dk} dv{dv}")
+
+
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 31, 32, 33, 48, 64])
+def test_gated_bf16_short(T):
+    """One to four chunks: the producers' prologue, the last-chunk repeats past the end and
+    the pairing of steps for odd and even chunk counts."""
+    w = inputs.Workload(f"gated_short{T}", 3, T, 4, 4, 64, 64, "bf16", 2, 12, init_std=0.5, seed=61 + T)
+    _compare(w, ("g", "gv"), gmax=0.5, tag=f" T{T}")
+
+
+def _banded_gates(w, strong_k, strong_v, gmax=0.2, gstrong=8.0):
+    """g and gv ~ U[-gmax, 0), with U[-gstrong, 0) on the token ranges strong_k (key gate)
+    and strong_v (value gate); bf16 words."""
+    rng = np.random.default_rng(w.seed + 1000)
+    B, T, H = w.batch, w.seqlen, w.num_heads
+    g = (-gmax * rng.random((B, T, H, w.dk))).astype(np.float32)
+    gv = (-gmax * rng.random((B, T, H, w.dv))).astype(np.float32)
+    a, b = strong_k
+    g[:, a:b] = (-gstrong * rng.random((B, b - a, H, w.dk))).astype(np.float32)
+    a, b = strong_v
+    gv[:, a:b] = (-gstrong * rng.random((B, b - a, H, w.dv))).astype(np.float32)
+    return {"g": inputs.bf16_words(g), "gk": None, "gv": inputs.bf16_words(gv)}
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_gated_bf16_mixed_exact_and_fast_chunks(reverse):
+    """Strong decays on some token ranges only, so chunks switch between the exact and the
+    fast path (the chunk flags cycle through their slots), on the key side and the value side."""
+    w = inputs.Workload("gated_mixed", 2, 400, 4, 4, 128, 128, "bf16", 4, 12, init_std=0.3, seed=70)
+    data = w.make()
+    gates = _banded_gates(w, (40, 72), (200, 216))
+    o, fs, o_ref, fs_ref = _run(w, data, gates, use_gg=False, reverse=reverse)
+    tag = " rev" if reverse else ""
+    check(o.cpu().numpy(), o_ref, TOL["bf16"], f"gated_mixed{tag} o")
+    check(fs.cpu().numpy(), fs_ref, TOL["bf16"], f"gated_mixed{tag} final_state")
