@@ -92,15 +92,15 @@ __device__ inline f32x4 raw_to_f32(u32x4 w, bool f32) {
     return f32 ? __builtin_bit_cast(f32x4, w) : f32x4{bf16_lo(w[0]), bf16_hi(w[0]), bf16_lo(w[1]), bf16_hi(w[1])};
 }
 
-// One chunk per loop trip, two barriers: (1) the staged chunk is in LDS and the
+// fp32 inputs.  One chunk per loop trip, two barriers: (1) the staged chunk is in LDS and the
 // previous matrix phase is done; each thread then owns state channels (columns)
 // and derives, from the decays summed over the chunk in registers, the decayed
 // operands; (2) they are in LDS; the next chunk is staged from registers (its loads
 // were issued a loop trip earlier; raw words are converted only here, so no load is
 // waited for where it is issued) while the waves run the matrix phase.  The
 // barriers wait for LDS operations only, so the prefetch loads stay in flight.
-template <int DK, int NW, bool BF16, bool GF32>
-__global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
+template <int DK, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void gated_f32_kernel(const FwdParams p) {
     using Cfg = GatedCfg<DK, NW>;
     constexpr int BV = Cfg::BV, NT = Cfg::NT, KS = Cfg::KS, VS = Cfg::VS, MT = Cfg::MT, TS = Cfg::TS;
     __shared__ __attribute__((aligned(16))) float sm[Cfg::FLOATS];
@@ -132,7 +132,6 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
     const int nch = (int)((L + kGChunk - 1) / kGChunk);
     const bool rev = p.reverse_gated != 0;
     const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
-    constexpr bool g_f32 = !BF16 || GF32;  // dtype of the key gate
     const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
     const int j = 16 * wv + lr;       // this lane's column inside the block
     const int vcol = wk.vb * BV + j;  // ... of v and o
@@ -172,9 +171,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
             const bool ok = item < Cfg::KITEMS && p0 + t < L;
             kok |= (ok ? 1u : 0u) << s;
             const int64_t row = tok_row(ok ? p0 + t : p0);
-            rq[s] = load4_raw<!BF16>(p.q, row * qrow + qoff + 4 * c4);
-            rk[s] = load4_raw<!BF16>(p.k, row * krow + koff + 4 * c4);
-            ra[s] = load4_raw<g_f32>(gbase, row * qrow + qoff + 4 * c4);
+            rq[s] = load4_raw<true>(p.q, row * qrow + qoff + 4 * c4);
+            rk[s] = load4_raw<true>(p.k, row * krow + koff + 4 * c4);
+            ra[s] = load4_raw<true>(gbase, row * qrow + qoff + 4 * c4);
         }
 #pragma unroll
         for (int s = 0; s < Cfg::VPER; ++s) {
@@ -183,8 +182,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
             const bool ok = item < Cfg::VITEMS && p0 + t < L;
             vok |= (ok ? 1u : 0u) << s;
             const int64_t row = tok_row(ok ? p0 + t : p0);
-            rv[s] = load4_raw<!BF16>(p.v, row * vrow + voff + 4 * c4);
-            rb[s] = load4_raw<!BF16>(gvbase, row * gvrow_r + gvoff_r + 4 * c4);
+            rv[s] = load4_raw<true>(p.v, row * vrow + voff + 4 * c4);
+            rb[s] = load4_raw<true>(gvbase, row * gvrow_r + gvoff_r + 4 * c4);
         }
     };
     // Write the staged pieces to LDS as floats: la = log2-decay of the key channels
@@ -197,9 +196,9 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
             if (item < Cfg::KITEMS) {
                 const int t = item / (DK / 4), c4 = item % (DK / 4);
                 const bool ok = (kok >> s) & 1u;
-                const f32x4 a = has_g ? kLog2e * raw_to_f32(ra[s], g_f32) : z;
-                lds_store<f32x4>(Qs + t * KS + 4 * c4, ok ? raw_to_f32(rq[s], !BF16) : z);
-                lds_store<f32x4>(Ks + t * KS + 4 * c4, ok ? raw_to_f32(rk[s], !BF16) : z);
+                const f32x4 a = has_g ? kLog2e * raw_to_f32(ra[s], true) : z;
+                lds_store<f32x4>(Qs + t * KS + 4 * c4, ok ? raw_to_f32(rq[s], true) : z);
+                lds_store<f32x4>(Ks + t * KS + 4 * c4, ok ? raw_to_f32(rk[s], true) : z);
                 lds_store<f32x4>(As + t * KS + 4 * c4, ok ? a + gg2 : z);
             }
         }
@@ -209,8 +208,8 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
             if (item < Cfg::VITEMS) {
                 const int t = item / (BV / 4), c4 = item % (BV / 4);
                 const bool ok = (vok >> s) & 1u;
-                const f32x4 b = has_gv ? kLog2e * raw_to_f32(rb[s], !BF16) : z;
-                lds_store<f32x4>(Vs + t * VS + 4 * c4, ok ? raw_to_f32(rv[s], !BF16) : z);
+                const f32x4 b = has_gv ? kLog2e * raw_to_f32(rb[s], true) : z;
+                lds_store<f32x4>(Vs + t * VS + 4 * c4, ok ? raw_to_f32(rv[s], true) : z);
                 lds_store<f32x4>(Bs + t * VS + 4 * c4, ok ? b : z);
             }
         }
@@ -387,7 +386,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Gated recurrence, bf16 inputs: the chunk algebra of gated_kernel with every
+// Gated recurrence, bf16 inputs: the chunk algebra of gated_f32_kernel with every
 // product on bf16 MFMA.  A decayed fp32 operand X is split X = hi + lo, hi its bf16
 // truncation and lo the bf16 rounding of the exact remainder; a product takes
 // hi*hi + hi*lo + lo*hi with fp32 accumulation (about 2^-14 relative error per
@@ -403,7 +402,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_kernel(const FwdParams p) {
 // stay below 2^kGSpan times their operands.  A key channel pair with a wider span
 // stores k .* 2^{A_15 - A_u} instead and moves its factor 2^{A_15} in front of S
 // (per-row factors pre and post); a chunk holding one takes the exact VALU path of
-// gated_kernel for W and the intra term.
+// gated_f32_kernel for W and the intra term.
 //
 // Roles: a workgroup of 2 NW waves.  Waves 0 .. NW-1 (matrix waves) own 16 value
 // columns each and the state in accumulator registers; waves NW .. 2NW-1 (producer
@@ -1055,7 +1054,7 @@ hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
     else if (bf16)
         hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, false>), grid, block_bf16, 0, s, p);
     else
-        hipLaunchKernelGGL((gated_kernel<DK, NW, false, true>), grid, block_f32, 0, s, p);
+        hipLaunchKernelGGL((gated_f32_kernel<DK, NW>), grid, block_f32, 0, s, p);
     return hipGetLastError();
 }
 template <int DK>

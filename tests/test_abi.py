@@ -232,6 +232,8 @@ def call_gated(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, gv=None, gg=Non
     (P(head_dim_qk=256), lattn.LATTN_ERR_UNSUPPORTED),
     (P(head_dim_v=24), lattn.LATTN_ERR_UNSUPPORTED),
     (P(out_dtype=lattn.LATTN_BF16), lattn.LATTN_ERR_UNSUPPORTED),
+    # 16 token rows of every array must stay below 2^31 bytes (32-bit offsets in the kernel)
+    (P(num_heads=1 << 18, num_kv_heads=1 << 18, head_dim_qk=128, head_dim_v=128), lattn.LATTN_ERR_UNSUPPORTED),
 ])
 def test_gated_problem_errors(prob, status):
     assert call_gated(prob) == status
