@@ -420,6 +420,16 @@ int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* 
         return LATTN_ERR_LAUNCH;
     const bool rev = reverse != 0;
     if (lattn::launch_fwd(pq, p->in_dtype, nw_q, rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
+    // The dk and dv sweeps read the same Q and dO: with equal head dims (one kernel
+    // shape) they run as one launch whose workgroups pair up per die, so the second
+    // read of a tile mostly hits L2.  LATTN_BWD_PAIR=0 keeps two launches.
+    const char* pair_env = std::getenv("LATTN_BWD_PAIR");
+    const bool pair = p->in_dtype == LATTN_BF16 && !grouped && dkd == dvd && nw_k == nw_v &&
+                      !(pair_env && std::atoi(pair_env) == 0);
+    if (pair) {
+        if (lattn::launch_fwd_pair(pk, pv, nw_k, !rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
+        return LATTN_OK;
+    }
     if (lattn::launch_fwd(pk, p->in_dtype, nw_k, !rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
     if (grouped && lattn::launch_group_sum(part, dk, tokens, p->num_heads, p->num_kv_heads, dkd, s) != hipSuccess)
         return LATTN_ERR_LAUNCH;

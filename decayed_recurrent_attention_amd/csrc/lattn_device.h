@@ -28,13 +28,12 @@ struct Work {
     int64_t len;    // tokens in the sequence
 };
 
-// Workgroup id -> work.  Groups are (sequence rank, kv head); the workgroups of one
+// Work id (normally the workgroup id) -> work.  Groups are (sequence rank, kv head); the workgroups of one
 // group (its query heads x value blocks, which re-read the same K and V, and per
 // head the same Q) get ids that are equal mod kNumXcd, so they share one L2.
 // Consecutive groups go to consecutive dies; with sequences ranked longest first,
 // each die receives its longest work first.
-__device__ inline bool decode_work(const FwdParams& p, Work& w) {
-    const int id = blockIdx.x;
+__device__ inline bool decode_work(const FwdParams& p, int id, Work& w) {
     const int x = id % kNumXcd;
     const int slot = id / kNumXcd;
     const int g = (slot / p.group_size) * kNumXcd + x;

@@ -124,7 +124,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_f32_kernel(const FwdParams p
     float* EBs = sm + Cfg::OFF_EB;
 
     Work wk;
-    if (!decode_work(p, wk)) return;
+    if (!decode_work(p, blockIdx.x, wk)) return;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = p.num_heads, dv = p.dv;
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
     auto derived = [&](int c) __attribute__((always_inline)) -> uint32_t* { return sm + Cfg::OFF_D + (c & 1) * Cfg::D_SIZE; };
 
     Work wk;
-    if (!decode_work(p, wk)) return;
+    if (!decode_work(p, blockIdx.x, wk)) return;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool producer = wv >= NW;

@@ -224,8 +224,9 @@ __device__ inline void split_state(const f32x4* S, bf16x8* hi, bf16x8* lo) {
 
 // SONLY: only the state recurrence (no Q, no output): the final state of every
 // sequence from K and V alone.
+// work_id: the workgroup's unit of work (its id for a single problem).
 template <int DK, int NW, bool REV, bool SONLY>
-__global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p) {
+__device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdParams& p, int work_id) {
     using Cfg = Bf16Cfg<DK, NW>;
     constexpr int BV = Cfg::BV, PP = Cfg::PP, PVB = Cfg::PVB, KB = Cfg::KB, MT = Cfg::MT;
     constexpr int NST = Cfg::STAGES, DEPTH = Cfg::DEPTH;
@@ -234,7 +235,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
     uint8_t* Pbuf = smem + NST * Cfg::STAGE_BYTES;
 
     Work wk;
-    if (!decode_work(p, wk)) return;
+    if (!decode_work(p, work_id, wk)) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
@@ -529,6 +530,20 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p)
     }
 }
 
+template <int DK, int NW, bool REV, bool SONLY>
+__global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p) {
+    fwd_bf16_body<DK, NW, REV, SONLY>(p, blockIdx.x);
+}
+
+// Two problems of the same shape in one launch (a.p[0], a.p[1]: the dk and dv sweeps
+// of the backward).  Workgroup ids alternate between them in runs of kNumXcd, so the
+// two workgroups with the same work id share a die and run together.
+template <int DK, int NW, bool REV>
+__global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_pair_kernel(const FwdArgs a) {
+    const int bid = blockIdx.x;
+    fwd_bf16_body<DK, NW, REV, false>(a.p[(bid / kNumXcd) & 1], (bid / (2 * kNumXcd)) * kNumXcd + bid % kNumXcd);
+}
+
 // ---------------------------------------------------------------------------
 // fp32 inputs: v_mfma_f32_16x16x4_f32, no rounding of any operand.
 // ---------------------------------------------------------------------------
@@ -561,7 +576,7 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
     __shared__ __attribute__((aligned(16))) float smem[Cfg::STAGES * Cfg::STAGE_ELEMS];
 
     Work wk;
-    if (!decode_work(p, wk)) return;
+    if (!decode_work(p, blockIdx.x, wk)) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, lr = lane & 15, lg = lane >> 4;
     const float g2 = p.g_gamma[wk.h] * kLog2e;
@@ -920,8 +935,20 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* cu, int n
 }
 
 template <int DK, int NW>
-hipError_t launch_bf16(const FwdParams& p, bool rev, bool sonly, hipStream_t s) {
-    const dim3 grid(fwd_grid_size(p)), block(64 * NW);
+hipError_t launch_bf16(const FwdParams& p, const FwdParams* p2, bool rev, bool sonly, hipStream_t s) {
+    const dim3 block(64 * NW);
+    if (p2) {
+        FwdArgs a;
+        a.p[0] = p;
+        a.p[1] = *p2;
+        const dim3 grid(2 * fwd_grid_size(p));
+        if (rev)
+            hipLaunchKernelGGL((fwd_bf16_pair_kernel<DK, NW, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((fwd_bf16_pair_kernel<DK, NW, false>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    const dim3 grid(fwd_grid_size(p));
     if (sonly) {
         if (rev)
             hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, true>), grid, block, 0, s, p);
@@ -962,17 +989,28 @@ __host__ __device__ constexpr bool f32_variant(int dk, int nw) {
 }
 
 template <int DK>
-hipError_t launch_bf16_nw(const FwdParams& p, int nw, bool rev, bool sonly, hipStream_t s) {
+hipError_t launch_bf16_nw(const FwdParams& p, const FwdParams* p2, int nw, bool rev, bool sonly, hipStream_t s) {
     if constexpr (bf16_variant(DK, 1)) {
-        if (nw == 1) return launch_bf16<DK, 1>(p, rev, sonly, s);
+        if (nw == 1) return launch_bf16<DK, 1>(p, p2, rev, sonly, s);
     }
     if constexpr (bf16_variant(DK, 2)) {
-        if (nw == 2) return launch_bf16<DK, 2>(p, rev, sonly, s);
+        if (nw == 2) return launch_bf16<DK, 2>(p, p2, rev, sonly, s);
     }
     if constexpr (bf16_variant(DK, 4)) {
-        if (nw == 4) return launch_bf16<DK, 4>(p, rev, sonly, s);
+        if (nw == 4) return launch_bf16<DK, 4>(p, p2, rev, sonly, s);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_bf16_dk(const FwdParams& p, const FwdParams* p2, int nw, bool rev, bool sonly, hipStream_t s) {
+    switch (p.dk) {
+        case 32: return launch_bf16_nw<32>(p, p2, nw, rev, sonly, s);
+        case 64: return launch_bf16_nw<64>(p, p2, nw, rev, sonly, s);
+        case 128: return launch_bf16_nw<128>(p, p2, nw, rev, sonly, s);
+        case 192: return launch_bf16_nw<192>(p, p2, nw, rev, sonly, s);
+        case 256: return launch_bf16_nw<256>(p, p2, nw, rev, sonly, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 template <int DK>
@@ -1004,16 +1042,7 @@ int fwd_grid_size(const FwdParams& p) {
 }
 
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t s, bool state_only) {
-    if (in_dtype == 0) {
-        switch (p.dk) {
-            case 32: return launch_bf16_nw<32>(p, nw, reverse, state_only, s);
-            case 64: return launch_bf16_nw<64>(p, nw, reverse, state_only, s);
-            case 128: return launch_bf16_nw<128>(p, nw, reverse, state_only, s);
-            case 192: return launch_bf16_nw<192>(p, nw, reverse, state_only, s);
-            case 256: return launch_bf16_nw<256>(p, nw, reverse, state_only, s);
-            default: return hipErrorInvalidValue;
-        }
-    }
+    if (in_dtype == 0) return launch_bf16_dk(p, nullptr, nw, reverse, state_only, s);
     if (state_only) return hipErrorInvalidValue;  // the split runs bf16 problems only
     if (in_dtype == 1) {
         switch (p.dk) {
@@ -1025,6 +1054,13 @@ hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hi
         }
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_pair(const FwdParams& a, const FwdParams& b, int nw, bool reverse, hipStream_t s) {
+    if (a.dk != b.dk || a.dv != b.dv || a.nvb != b.nvb || a.group_size != b.group_size ||
+        a.num_groups != b.num_groups)
+        return hipErrorInvalidValue;
+    return launch_bf16_dk(a, &b, nw, reverse, false, s);
 }
 
 hipError_t launch_group_sum(const float* part, float* out, int64_t rows, int H, int Hkv, int d, hipStream_t s) {

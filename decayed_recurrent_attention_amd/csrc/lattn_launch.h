@@ -60,6 +60,12 @@ struct FwdParams {
     int reverse_gated;
 };
 
+// Kernel arguments of the forward kernels: one problem, or two of the same shape
+// run by one launch (launch_fwd_pair).
+struct FwdArgs {
+    FwdParams p[2];
+};
+
 // Forward defaults of the fields above.
 inline void set_forward_defaults(FwdParams& p) {
     p.swap_heads = 0;
@@ -84,6 +90,10 @@ int fwd_grid_size(const FwdParams& p);
 // only) runs just the state recurrence: final_state from K and V, no Q, no output.
 hipError_t launch_fwd(const FwdParams& p, int in_dtype, int nw, bool reverse, hipStream_t stream,
                       bool state_only = false);
+// Two bf16 problems of the same shape (dims, work decode) in one launch; the work
+// of a and b with the same id shares a die and runs together (the backward's dk and
+// dv sweeps read the same Q and dO).
+hipError_t launch_fwd_pair(const FwdParams& a, const FwdParams& b, int nw, bool reverse, hipStream_t stream);
 // Gated recurrence (GLA gates), 64 * nw threads for BV = 16 * nw value columns.
 bool have_gated_kernel(int dk, int nw);
 // out = g + gk in fp32 (n elements, a multiple of 4; inputs in in_dtype).

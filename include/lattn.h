@@ -124,7 +124,9 @@ size_t lattn_bwd_workspace_size(const lattn_problem* p);
  *
  * "first"/"last" in the direction of the forward pass; dk and dv of a kv head sum
  * over its query heads.  Computed as three chunked sweeps: dq in the forward
- * direction, dk and dv in the opposite one.
+ * direction, dk and dv in the opposite one (bf16 with dk = dv and no grouped heads:
+ * the dk and dv sweeps share one launch; the environment variable LATTN_BWD_PAIR=0
+ * keeps them apart).
  *   q, k, v, g_gamma, scale, initial_state, reverse, cu_seqlens: as for lattn_fwd
  *                  (the forward inputs; initial_state may be NULL).  scale must be a
  *                  finite normal float (the sweeps carry D / scale).
