@@ -135,3 +135,22 @@ def test_bwd_deterministic():
     b = gpu_run_bwd(w, data, grads)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_bwd_paired_sweeps_equal_separate(reverse, monkeypatch):
+    """bf16 with dk = dv and no grouped heads runs the dk and dv sweeps as one launch;
+    every workgroup does the same arithmetic either way, so the gradients are
+    bit-identical to two launches (LATTN_BWD_PAIR=0), and both meet the oracle."""
+    import torch
+
+    w = inputs.Workload("bwd_pair", 2, 700, 4, 4, 64, 64, "bf16", 2, 12, reverse=reverse, init_std=0.3, seed=27)
+    data, grads = w.make(), w.make_grads()
+    a = gpu_run_bwd(w, data, grads)
+    monkeypatch.setenv("LATTN_BWD_PAIR", "0")
+    b = gpu_run_bwd(w, data, grads)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    ref = oracle_run_bwd(w, data, grads)
+    for got, exp, name in zip(a, ref, ("dq", "dk", "dv", "d_initial_state")):
+        check(got.cpu().numpy(), exp, TOL["bf16"], f"bwd_pair{' rev' if reverse else ''} {name}")
