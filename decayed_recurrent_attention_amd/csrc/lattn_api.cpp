@@ -46,8 +46,8 @@ int check_problem(const lattn_problem& p) {
     return LATTN_OK;
 }
 
-// The gated recurrence: fp32 chunks of 16 tokens, dk 32, 64 or 128, value blocks of
-// 64 columns when dv allows, else 16.
+// The gated recurrence: chunks of 16 tokens, dk 32, 64 or 128, value blocks of 64
+// columns when dv allows, else 16.
 int gated_nw(int dv) { return dv % 64 == 0 ? 4 : 1; }
 
 int check_gated_problem(const lattn_problem& p) {

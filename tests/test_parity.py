@@ -113,6 +113,15 @@ def test_unequal_head_dims(dk, dv, dtype):
     _compare(w, w.make())
 
 
+@pytest.mark.parametrize("dk,dv,dtype", [(256, 256, "bf16"), (192, 256, "bf16"), (128, 256, "f32")])
+def test_largest_head_dims(dk, dv, dtype):
+    """The largest supported head dims per dtype (dv up to 256), both directions of the
+    work, GQA, ragged length."""
+    w = inputs.Workload(f"max_dk{dk}_dv{dv}_{dtype}", 2, 333, 4, 2, dk, dv, dtype, 3, 12,
+                        init_std=0.2, seed=8)
+    _compare(w, w.make())
+
+
 @pytest.mark.parametrize("nw", ["1", "2", "4"])
 def test_workgroup_widths(nw, monkeypatch):
     monkeypatch.setenv("LATTN_NW", nw)
