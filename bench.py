@@ -17,7 +17,11 @@ Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
                 along the sequence, against the same call unsplit,
   gated         the gated (GLA) forward on the same inputs plus a per-key-channel gate g,
                 against HBM (its binding roofline at bf16 MFMA rates), with the bf16
-                matrix figure beside it.
+                matrix figure beside it,
+  sweep         the forward at N = 512 .. 16384 (same B, H, head dims), each N rotating
+                over enough input sets that about 1 GB is touched between repeats, with
+                the Lightning-2 forward time the pages print for that N beside it
+                (skipped with --no-sweep).
 """
 from __future__ import annotations
 
@@ -38,6 +42,10 @@ BF16_MFMA_PEAK_TFS = 2500.0  # dense bf16 matrix peak of MI355X
 # Lightning2 forward at B4 H32 d128 bf16 n=32768 from the OpenNLPLab lightning-attention
 # README benchmark table (hardware unstated, time read as milliseconds): 17.661427 ms.
 PAGE_LIGHTNING2_MS = 17.661427
+# the same README table (Lightning2 column, read as ms) at B4 H32 d128, by n
+PAGE_LIGHTNING2_SWEEP_MS = {512: 0.351540, 1024: 0.585876, 2048: 1.134238, 4096: 2.240815, 8192: 4.414397,
+                            16384: 8.832678, 32768: 17.661427}
+SWEEP_N = (512, 1024, 2048, 4096, 8192, 16384)
 PAGE_LIGHTNING2_BWD_MS = 74.594788  # same table's backward row at n = 32768
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_b4_h32_d128_n32768.json")
 # the forward kernel's translation unit: its source and the two headers it includes
@@ -253,6 +261,8 @@ def main():
                     help="skip the intra-sequence split measurement (B1 H8, same head dims and N)")
     ap.add_argument("--decode-batch", type=int, default=128,
                     help="sequences per decoding step in the decode measurement (0 skips it)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the forward sweep over N = 512 .. 16384 (same B, H, head dims)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a 1 GiB device copy (counter calibration for traffic)")
     ap.add_argument("--bandwidth", action="store_true",
@@ -294,6 +304,50 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel mean "
           f"{mean_kernel_ms:.4f} ms min {min(kernel_ms):.4f} max {max(kernel_ms):.4f}",
           file=sys.stderr, flush=True)
+
+    sweep = None
+    if not args.no_sweep:
+        # The forward at smaller N on device-drawn inputs of the same shape.  Below 1 GB per
+        # call, calls rotate over enough buffer sets (about 1 GB in all) that the working
+        # set cannot stay in the 256 MB Infinity Cache.
+        print("[bench] sweep over N", file=sys.stderr, flush=True)
+        sweep = []
+        for n in SWEEP_N:
+            nbytes = algorithmic_bytes(B, n, H, Hkv, dk, dv, 2)
+            nsets = max(1, min(16, -(-(1 << 30) // nbytes)))
+            sets = []
+            for _ in range(nsets):
+                qs = torch.randn((B, n, H, dk), device=dev, dtype=torch.bfloat16)
+                ks = torch.randn((B, n, Hkv, dk), device=dev, dtype=torch.bfloat16)
+                vs = torch.randn((B, n, Hkv, dv), device=dev, dtype=torch.bfloat16)
+                os_ = torch.empty((B, n, H, dv), device=dev, dtype=torch.float32)
+                fss = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+                sets.append((qs, ks, vs, os_, fss))
+            sprob = lattn.LattnProblem(B, n, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
+            it = [0]
+
+            def sweep_step():
+                qs, ks, vs, os_, fss = sets[it[0] % nsets]
+                it[0] += 1
+                rc = lattn.lattn_fwd(sprob, qs, ks, vs, g, w.scale, None, False, None, os_, fss,
+                                     stream=stream.cuda_stream)
+                if rc != lattn.LATTN_OK:
+                    raise lattn.LattnError(rc)
+
+            n_wall, n_ms = time_calls(torch, sweep_step, stream, args.warmup, args.steps)
+            n_mean = sum(n_ms) / len(n_ms)
+            gbs = nbytes / (n_mean * 1e-3) / 1e9
+            sweep.append({"seq_len": n, "ms_per_step": n_wall, "kernel_ms": n_mean,
+                          "tokens_per_s": B * n / (n_wall * 1e-3), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                          "buffer_sets": nsets, "page_lightning2_ms": PAGE_LIGHTNING2_SWEEP_MS[n]})
+            print(f"[bench] sweep N={n}: {n_wall:.4f} ms/step wall, kernel mean {n_mean:.4f} ms, "
+                  f"{gbs:.0f} GB/s ({nsets} buffer sets)", file=sys.stderr, flush=True)
+            del sets
+        full_gbs = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2) / (mean_kernel_ms * 1e-3) / 1e9
+        sweep.append({"seq_len": T, "ms_per_step": ms_per_step, "kernel_ms": mean_kernel_ms,
+                      "tokens_per_s": B * T / (ms_per_step * 1e-3), "hbm_gbs": full_gbs,
+                      "hbm_frac": full_gbs / HBM_PEAK_GBS, "buffer_sets": 1,
+                      "page_lightning2_ms": PAGE_LIGHTNING2_SWEEP_MS.get(T)})
 
     bwd = None
     if not args.no_bwd:
@@ -486,6 +540,8 @@ def main():
         line["split"] = split
     if gated is not None:
         line["gated"] = gated
+    if sweep is not None:
+        line["sweep"] = sweep
     print(json.dumps(line), flush=True)
 
 
