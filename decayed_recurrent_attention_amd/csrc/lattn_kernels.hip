@@ -189,7 +189,7 @@ struct Bf16Cfg {
     static constexpr int KB = DK / 32;                 // dk blocks of one MFMA
     static constexpr int MT = DK / 16;                 // state row tiles
     static_assert(DK % 32 == 0 && DK <= 256, "dk must be a multiple of 32 up to 256");
-    static_assert(STAGES >= 2, "need at least two stages");
+    static_assert(STAGES >= 2 && STAGES <= 3, "the chunk loop is unrolled over two or three stages");
     static_assert(PP % NW == 0 && PVB % NW == 0, "copies divide evenly between waves");
     static_assert(STAGES * STAGE_BYTES + P_BYTES <= kLdsBudget, "LDS budget");
 };
@@ -231,6 +231,8 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     constexpr int BV = Cfg::BV, PP = Cfg::PP, PVB = Cfg::PVB, KB = Cfg::KB, MT = Cfg::MT;
     constexpr int NST = Cfg::STAGES, DEPTH = Cfg::DEPTH;
     constexpr int QROW = DK * 2, VROW = BV * 2;  // LDS row bytes
+    // LDS: the Q tiles of every stage, then the K tiles, then the V tiles, then P.
+    constexpr int KREG = NST * Cfg::Q_BYTES, VREG = 2 * NST * Cfg::Q_BYTES;
     __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * Cfg::STAGE_BYTES + Cfg::P_BYTES];
     uint8_t* Pbuf = smem + NST * Cfg::STAGE_BYTES;
 
@@ -302,15 +304,17 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     bf16x8 Shi[KB], Slo[KB];
     split_state<KB>(S, Shi, Slo);
 
-    auto first_row = [&](int p0, int Lc) -> int64_t { return REV ? wk.start + L - p0 - Lc : wk.start + p0; };
-    auto qk_off = [](int row, int blk) { return row * QROW + 16 * (blk ^ qk_swz<PP>(row)); };
-    auto v_off = [](int row, int blk) { return row * VROW + 16 * (blk ^ v_swz<PVB>(row)); };
+    auto first_row = [&](int p0, int Lc) __attribute__((always_inline)) -> int64_t { return REV ? wk.start + L - p0 - Lc : wk.start + p0; };
+    auto qk_off = [](int row, int blk) __attribute__((always_inline)) { return row * QROW + 16 * (blk ^ qk_swz<PP>(row)); };
+    auto v_off = [](int row, int blk) __attribute__((always_inline)) { return row * VROW + 16 * (blk ^ v_swz<PVB>(row)); };
 
     // Copy chunk c into stage c % NST.  Past the last chunk the descriptors are
     // empty, so the copies only write zeros (keeping the per-chunk operation count
     // fixed for the waits below) into the stage the previous chunk used.
-    auto issue_chunk = [&](int c) {
-        const uint32_t stage = smem_base + (uint32_t)((c % NST) * Cfg::STAGE_BYTES);
+    auto issue_chunk = [&](int c) __attribute__((always_inline)) {
+        const uint32_t sidx = (uint32_t)(c % NST);
+        const uint32_t qst = smem_base + sidx * Cfg::Q_BYTES, kst = smem_base + KREG + sidx * Cfg::Q_BYTES;
+        const uint32_t vst = smem_base + VREG + sidx * Cfg::V_BYTES;
         const int p0 = c * kChunk;
         const bool real = c < nch;
         const int Lc = real ? min(kChunk, L - p0) : 1;
@@ -324,8 +328,8 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
             const int B = kbyte * 64 + lane, row = B / PP;
             const int blk = (B % PP) ^ qk_swz<PP>(row);
             const int rs = REV ? Lc - 1 - row : row;  // out of range past the end
-            if constexpr (!SONLY) copy16_to_lds(stage + kbyte * 1024, rq, rs * (int)qrow_b + blk * 16);
-            copy16_to_lds(stage + Cfg::Q_BYTES + kbyte * 1024, rk, rs * (int)krow_b + blk * 16);
+            if constexpr (!SONLY) copy16_to_lds(qst + kbyte * 1024, rq, rs * (int)qrow_b + blk * 16);
+            copy16_to_lds(kst + kbyte * 1024, rk, rs * (int)krow_b + blk * 16);
         }
 #pragma unroll
         for (int j = 0; j < Cfg::VCOPIES; ++j) {
@@ -333,7 +337,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
             const int B = kbyte * 64 + lane, row = B / PVB;
             const int blk = (B % PVB) ^ v_swz<PVB>(row);
             const int rs = REV ? Lc - 1 - row : row;
-            copy16_to_lds(stage + 2 * Cfg::Q_BYTES + kbyte * 1024, rv, rs * (int)vrow_b + blk * 16);
+            copy16_to_lds(vst + kbyte * 1024, rv, rs * (int)vrow_b + blk * 16);
         }
     };
     // Wait until this wave's copies of chunk c are in LDS.  Issued after them, in
@@ -343,7 +347,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     constexpr int NSTORE = SONLY ? 0 : Cfg::NSTORE;
     constexpr int W0 = (DEPTH - 1) * NCOPY;
     constexpr int WC = W0 + DEPTH * NSTORE;
-    auto wait_chunk = [&](int c) {
+    auto wait_chunk = [&](int c) __attribute__((always_inline)) {
         if (c >= DEPTH) {
             wait_vmem<(WC < 63 ? WC : 63)>();
         } else if (c == 0) {
@@ -354,10 +358,8 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         }
     };
 
-    auto compute_chunk = [&](int c, const uint8_t* st) {
-        const uint8_t* Qs = st;
-        const uint8_t* Ks = st + Cfg::Q_BYTES;
-        const uint8_t* Vs = st + 2 * Cfg::Q_BYTES;
+    auto compute_chunk = [&](int c, const uint8_t* Qs, const uint8_t* Ks, const uint8_t* Vs)
+                             __attribute__((always_inline)) {
         const int p0 = c * kChunk, Lc = min(kChunk, L - p0);
         const int vblk = 2 * wv + ((lr & 3) >> 1), vhalf = 8 * (lr & 1);  // this lane's V piece
 
@@ -409,7 +411,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         f32x4 O[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) O[b] = z;
-        auto qs_and_tiles = [&](auto wconst) {
+        auto qs_and_tiles = [&](auto wconst) __attribute__((always_inline)) {
             constexpr int W = decltype(wconst)::value;
             constexpr int NTILE = (10 - W + NW - 1) / NW;
             f32x4 At[NTILE];
@@ -511,11 +513,21 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     if (nch > 0) {
 #pragma unroll
         for (int c = 0; c < DEPTH; ++c) issue_chunk(c);
-        for (int c = 0; c < nch; ++c) {
+        // Unrolled over the ring, so that each stage's LDS addresses are a per-lane
+        // base plus a constant offset.
+        auto step = [&](int c, auto sconst) __attribute__((always_inline)) {
+            constexpr int ST = decltype(sconst)::value;
             wait_chunk(c);
             lds_barrier();  // chunk c is in LDS; every wave is done with chunk c - 1
             issue_chunk(c + DEPTH);
-            compute_chunk(c, smem + (c % NST) * Cfg::STAGE_BYTES);
+            compute_chunk(c, smem + ST * Cfg::Q_BYTES, smem + KREG + ST * Cfg::Q_BYTES, smem + VREG + ST * Cfg::V_BYTES);
+        };
+        for (int c = 0; c < nch; c += NST) {
+            step(c, IntC<0>{});
+            if (c + 1 < nch) step(c + 1, IntC<1>{});
+            if constexpr (NST > 2) {
+                if (c + 2 < nch) step(c + 2, IntC<2>{});
+            }
         }
         wait_vmem<0>();  // no copy may still be writing LDS when the workgroup ends
     }
