@@ -14,11 +14,12 @@
 // Work decomposition: one workgroup per (sequence, query head, block of BV = 16*NW
 // value columns).  Value columns are independent (column c of S only sees column c
 // of V), so the state block S[:, BV] lives in MFMA accumulator registers for the
-// whole sequence: wave w owns columns [16w, 16w+16).  Each chunk of Q, K, V is
-// staged through LDS: Q and K row-major for the QK^T and Q S products, K
-// (pre-multiplied by its decay) and V transposed, so the token index is contiguous
-// for the products that contract over tokens.  Global loads of chunk c+1 are in
-// flight while chunk c is computed.
+// whole sequence: column block w (16 columns) belongs to one wave, or, with the dk
+// split, to two waves that each hold half of its dk rows and exchange partial Q S
+// sums through LDS (eight waves per workgroup, two per SIMD).  Each chunk of Q, K, V
+// goes from HBM straight into LDS, row-major; the products that contract over tokens
+// read K and V with transposing LDS reads.  The copies of the next DEPTH chunks are
+// in flight while a chunk is computed.
 //
 // Two layout facts of the 16x16 MFMA shapes make accumulators reusable as
 // operands without an LDS round trip: an output tile gives lane l column l%16 and
@@ -168,9 +169,13 @@ __host__ __device__ constexpr int v_swz(int r) {
     else return 0;
 }
 
-template <int DK, int NW>
+// Parts of a chunk's copy (issue_chunk).
+constexpr int kCopyQ = 1, kCopyK = 2, kCopyV = 4;
+
+template <int DK, int NW, int DS = 1>
 struct Bf16Cfg {
     static constexpr int BV = 16 * NW;
+    static constexpr int NWD = NW * DS;  // waves: DS of them share each 16-column block
     static constexpr int PP = DK / 8;    // 16-byte blocks per Q / K row
     static constexpr int PVB = BV / 8;   // 16-byte blocks per V row (this value block)
     static constexpr int Q_BYTES = kChunk * DK * 2;
@@ -179,19 +184,22 @@ struct Bf16Cfg {
     // Masked intra-chunk matrix P, exchanged between waves in MFMA A-operand layout:
     // 6 operand blocks (row tile b, token block kb) x {hi, lo} x 64 lanes x 16 bytes.
     static constexpr int P_BYTES = 6 * 2 * 64 * 16;
-    static constexpr int FIT = (kLdsBudget - P_BYTES) / STAGE_BYTES;
+    // With the dk split, each wave hands two row tiles of its partial Q S to its partner.
+    static constexpr int X_BYTES = DS > 1 ? NWD * 2 * 64 * 16 : 0;
+    static constexpr int FIT = (kLdsBudget - P_BYTES - X_BYTES) / STAGE_BYTES;
     static constexpr int STAGES = FIT >= 3 ? 3 : FIT;  // ring of chunk stages
     static constexpr int DEPTH = STAGES - 1;           // chunks copied ahead of the one computed
-    static constexpr int QCOPIES = PP / NW;            // copy instructions per wave per Q (or K) tile
-    static constexpr int VCOPIES = PVB / NW;           // ... per V tile
+    static constexpr int QCOPIES = PP / NWD;           // copy instructions per wave per Q (or K) tile
+    static constexpr int VCOPIES = PVB / NWD;          // ... per V tile
     static constexpr int NCOPY = 2 * QCOPIES + VCOPIES;
-    static constexpr int NSTORE = 16;                  // output stores per wave per chunk
+    static constexpr int NSTORE = 16 / DS;             // output stores per wave per chunk
     static constexpr int KB = DK / 32;                 // dk blocks of one MFMA
     static constexpr int MT = DK / 16;                 // state row tiles
     static_assert(DK % 32 == 0 && DK <= 256, "dk must be a multiple of 32 up to 256");
     static_assert(STAGES >= 2 && STAGES <= 3, "the chunk loop is unrolled over two or three stages");
-    static_assert(PP % NW == 0 && PVB % NW == 0, "copies divide evenly between waves");
-    static_assert(STAGES * STAGE_BYTES + P_BYTES <= kLdsBudget, "LDS budget");
+    static_assert(PP % NWD == 0 && PVB % NWD == 0, "copies divide evenly between waves");
+    static_assert(DS == 1 || (DS == 2 && KB % 2 == 0), "the dk split halves whole dk blocks");
+    static_assert(STAGES * STAGE_BYTES + P_BYTES + X_BYTES <= kLdsBudget, "LDS budget");
 };
 
 // Operand block of P for row tile b and token block kb (2kb <= b): 0..5.
@@ -225,27 +233,32 @@ __device__ inline void split_state(const f32x4* S, bf16x8* hi, bf16x8* lo) {
 // SONLY: only the state recurrence (no Q, no output): the final state of every
 // sequence from K and V alone.
 // work_id: the workgroup's unit of work (its id for a single problem).
-template <int DK, int NW, bool REV, bool SONLY>
+template <int DK, int NW, bool REV, bool SONLY, int DS = 1>
 __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdParams& p, int work_id) {
-    using Cfg = Bf16Cfg<DK, NW>;
+    using Cfg = Bf16Cfg<DK, NW, DS>;
     constexpr int BV = Cfg::BV, PP = Cfg::PP, PVB = Cfg::PVB, KB = Cfg::KB, MT = Cfg::MT;
+    constexpr int NWD = Cfg::NWD, MTL = MT / DS, KBL = KB / DS;  // waves; state tiles, dk blocks per wave
     constexpr int NST = Cfg::STAGES, DEPTH = Cfg::DEPTH;
     constexpr int QROW = DK * 2, VROW = BV * 2;  // LDS row bytes
     // LDS: the Q tiles of every stage, then the K tiles, then the V tiles, then P.
     constexpr int KREG = NST * Cfg::Q_BYTES, VREG = 2 * NST * Cfg::Q_BYTES;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * Cfg::STAGE_BYTES + Cfg::P_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * Cfg::STAGE_BYTES + Cfg::P_BYTES + Cfg::X_BYTES];
     uint8_t* Pbuf = smem + NST * Cfg::STAGE_BYTES;
+    uint8_t* Xbuf = Pbuf + Cfg::P_BYTES;
 
     Work wk;
     if (!decode_work(p, work_id, wk)) return;
     const int tid = threadIdx.x;
     const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
+    // Column block and dk half of this wave (the state rows of wave (wc, wd) are the
+    // global tiles wd*MTL .. wd*MTL + MTL - 1).
+    const int wc = DS == 1 ? wv : wv >> 1, wd = DS == 1 ? 0 : wv & 1;
     const float g2 = p.g_gamma[wk.h] * kLog2e;  // log2 of the per-step decay
     const int L = (int)wk.len;
     const int nch = (L + kChunk - 1) / kChunk;
     const int H = p.num_heads, dv = p.dv;
-    const int col = 16 * wv + lr;  // this lane's value column inside the block
+    const int col = 16 * wc + lr;  // this lane's value column inside the block
     // Operand heads: q at h and k, v at the kv head, or the other way round.
     const int qh = p.swap_heads ? wk.kvh : wk.h, kh = p.swap_heads ? wk.h : wk.kvh;
     const int QH = p.swap_heads ? p.num_kv_heads : H, KH = p.swap_heads ? H : p.num_kv_heads;
@@ -288,7 +301,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     const float lamC = exp2f(g2 * (float)kChunk);
 
     // State block: tile mt holds rows dmap(mt, 4*lg + ii) at column `col`.
-    f32x4 S[MT];
+    f32x4 S[MTL];
     const int64_t st_blk = ((int64_t)wk.n * H + wk.h) * DK * dv;  // this head's state block
     const int64_t st_off = st_blk + (int64_t)wk.vb * BV;
     {
@@ -296,22 +309,25 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         const auto ri = make_rsrc(p.init ? p.init + st_blk : p.g_gamma, p.init ? (uint32_t)(DK * dv * 4) : 0u);
         const int rs = (int)p.init_rs, cs = (int)p.init_cs, gcol = wk.vb * BV + col;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MTL; ++mt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
-                S[mt][ii] = p.init_mul * buf_load_f32(ri, (dmap(mt, 4 * lg + ii) * rs + gcol * cs) * 4);
+                S[mt][ii] = p.init_mul * buf_load_f32(ri, (dmap(wd * MTL + mt, 4 * lg + ii) * rs + gcol * cs) * 4);
     }
-    bf16x8 Shi[KB], Slo[KB];
-    split_state<KB>(S, Shi, Slo);
+    bf16x8 Shi[KBL], Slo[KBL];
+    split_state<KBL>(S, Shi, Slo);
 
     auto first_row = [&](int p0, int Lc) __attribute__((always_inline)) -> int64_t { return REV ? wk.start + L - p0 - Lc : wk.start + p0; };
     auto qk_off = [](int row, int blk) __attribute__((always_inline)) { return row * QROW + 16 * (blk ^ qk_swz<PP>(row)); };
     auto v_off = [](int row, int blk) __attribute__((always_inline)) { return row * VROW + 16 * (blk ^ v_swz<PVB>(row)); };
 
-    // Copy chunk c into stage c % NST.  Past the last chunk the descriptors are
-    // empty, so the copies only write zeros (keeping the per-chunk operation count
-    // fixed for the waits below) into the stage the previous chunk used.
-    auto issue_chunk = [&](int c) __attribute__((always_inline)) {
+    // Copy the parts (Q, K, V) of chunk c into stage c % NST.  Past the last chunk the
+    // descriptors are empty, so the copies only write zeros (keeping the per-chunk
+    // operation count fixed for the waits below) into the stage the previous chunk
+    // used.  While chunk c is computed, the copies of chunk c + DEPTH go out in three
+    // parts (K at the start, V after the state update, Q after the Q S and tile
+    // products), which spreads each workgroup's requests over the chunk.
+    auto issue_chunk = [&](int c, int parts) __attribute__((always_inline)) {
         const uint32_t sidx = (uint32_t)(c % NST);
         const uint32_t qst = smem_base + sidx * Cfg::Q_BYTES, kst = smem_base + KREG + sidx * Cfg::Q_BYTES;
         const uint32_t vst = smem_base + VREG + sidx * Cfg::V_BYTES;
@@ -324,20 +340,20 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         const RawBuf rv = raw_buf(vg + r0 * KH * dv, real ? (uint32_t)(Lc - 1) * vrow_b + BV * 2 : 0u);
 #pragma unroll
         for (int j = 0; j < Cfg::QCOPIES; ++j) {
-            const int kbyte = j * NW + wv;  // this wave's kilobyte of the tile
+            const int kbyte = j * NWD + wv;  // this wave's kilobyte of the tile
             const int B = kbyte * 64 + lane, row = B / PP;
             const int blk = (B % PP) ^ qk_swz<PP>(row);
             const int rs = REV ? Lc - 1 - row : row;  // out of range past the end
-            if constexpr (!SONLY) copy16_to_lds(qst + kbyte * 1024, rq, rs * (int)qrow_b + blk * 16);
-            copy16_to_lds(kst + kbyte * 1024, rk, rs * (int)krow_b + blk * 16);
+            if (!SONLY && (parts & kCopyQ)) copy16_to_lds(qst + kbyte * 1024, rq, rs * (int)qrow_b + blk * 16);
+            if (parts & kCopyK) copy16_to_lds(kst + kbyte * 1024, rk, rs * (int)krow_b + blk * 16);
         }
 #pragma unroll
         for (int j = 0; j < Cfg::VCOPIES; ++j) {
-            const int kbyte = j * NW + wv;
+            const int kbyte = j * NWD + wv;
             const int B = kbyte * 64 + lane, row = B / PVB;
             const int blk = (B % PVB) ^ v_swz<PVB>(row);
             const int rs = REV ? Lc - 1 - row : row;
-            copy16_to_lds(vst + kbyte * 1024, rv, rs * (int)vrow_b + blk * 16);
+            if (parts & kCopyV) copy16_to_lds(vst + kbyte * 1024, rv, rs * (int)vrow_b + blk * 16);
         }
     };
     // Wait until this wave's copies of chunk c are in LDS.  Issued after them, in
@@ -360,8 +376,9 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
 
     auto compute_chunk = [&](int c, const uint8_t* Qs, const uint8_t* Ks, const uint8_t* Vs)
                              __attribute__((always_inline)) {
+        const int cn = c + DEPTH;  // the chunk whose copies go out during this one
         const int p0 = c * kChunk, Lc = min(kChunk, L - p0);
-        const int vblk = 2 * wv + ((lr & 3) >> 1), vhalf = 8 * (lr & 1);  // this lane's V piece
+        const int vblk = 2 * wc + ((lr & 3) >> 1), vhalf = 8 * (lr & 1);  // this lane's V piece
 
         // S <- lam^Lc S + K^T (decayed V).  Operands by transposing reads: lane group
         // lg takes tokens 32kb + 8lg + 0..7; the A operand row of lane lr is dk
@@ -381,7 +398,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
                 }
         }
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) S[mt] *= lamL;
+        for (int mt = 0; mt < MTL; ++mt) S[mt] *= lamL;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int jr = 32 * kb + 8 * lg + (lr >> 2);  // token row this lane addresses
@@ -391,21 +408,23 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
             for (int e = 0; e < 4; ++e)
                 vw4[e] = pack_bf16x2(bf16_lo(vw4[e]) * vw[kb][2 * e], bf16_hi(vw4[e]) * vw[kb][2 * e + 1]);
             const bf16x8 vop = __builtin_bit_cast(bf16x8, vw4);
-            bf16x8 kop[MT];
+            bf16x8 kop[MTL];
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const int kblk = 4 * (mt >> 1) + (lr & 3), khalf = 8 * (mt & 1);
+            for (int mt = 0; mt < MTL; ++mt) {
+                const int mg = wd * MTL + mt;  // global state tile
+                const int kblk = 4 * (mg >> 1) + (lr & 3), khalf = 8 * (mg & 1);
                 kop[mt] = cat_bf16(lds_tr16((const uint16_t*)(Ks + qk_off(jr, kblk) + khalf)),
                                    lds_tr16((const uint16_t*)(Ks + qk_off(jr + 4, kblk) + khalf)));
             }
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) S[mt] = mfma_bf16(kop[mt], vop, S[mt]);
+            for (int mt = 0; mt < MTL; ++mt) S[mt] = mfma_bf16(kop[mt], vop, S[mt]);
         }
+        issue_chunk(cn, kCopyV);
         if constexpr (SONLY) return;
 
-        // Q S_prev for all 64 rows of this wave's columns, and this wave's share of
-        // the ten lower-triangle (K Q^T) tiles: tiles t = wv, wv + NW, ... (round
-        // robin).  Each wave masks its tiles and publishes P = scale (A .* M) in
+        // Q S_prev for all 64 rows of this wave's columns (over its dk rows), and this
+        // wave's share of the ten lower-triangle (K Q^T) tiles: tiles t = wv, wv + NWD,
+        // ... (round robin).  Each wave masks its tiles and publishes P = scale (A .* M) in
         // bf16 hi + lo to LDS in A-operand layout; all waves then read all of P.
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 O[4];
@@ -413,23 +432,28 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         for (int b = 0; b < 4; ++b) O[b] = z;
         auto qs_and_tiles = [&](auto wconst) __attribute__((always_inline)) {
             constexpr int W = decltype(wconst)::value;
-            constexpr int NTILE = (10 - W + NW - 1) / NW;
+            constexpr int WD = DS == 1 ? 0 : (W & 1);  // dk half of wave W
+            constexpr int NTILE = (10 - W + NWD - 1) / NWD;
             f32x4 At[NTILE];
 #pragma unroll
             for (int s = 0; s < NTILE; ++s) At[s] = z;
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
+                const bool own = kb / KBL == WD;  // a dk block of this wave's state rows
                 bf16x8 qa[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) qa[r] = lds_load<bf16x8>(Qs + qk_off(16 * r + lr, 4 * kb + lg));
+                if (own) {
+                    const int kl = own ? kb - WD * KBL : 0;
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    O[b] = mfma_bf16(qa[b], Shi[kb], O[b]);
-                    O[b] = mfma_bf16(qa[b], Slo[kb], O[b]);
+                    for (int b = 0; b < 4; ++b) {
+                        O[b] = mfma_bf16(qa[b], Shi[kl], O[b]);
+                        O[b] = mfma_bf16(qa[b], Slo[kl], O[b]);
+                    }
                 }
 #pragma unroll
                 for (int s = 0; s < NTILE; ++s) {
-                    const int t = W + s * NW;
+                    const int t = W + s * NWD;
                     const int a = tile_a(t), b = tile_b(t);
                     const bf16x8 ka = lds_load<bf16x8>(Ks + qk_off(16 * a + lr, 4 * kb + lg));
                     At[s] = mfma_bf16(ka, qa[b], At[s]);
@@ -437,7 +461,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
             }
 #pragma unroll
             for (int s = 0; s < NTILE; ++s) {
-                const int t = W + s * NW;
+                const int t = W + s * NWD;
                 const int a = tile_a(t), b = tile_b(t);
                 float pv4[4];
 #pragma unroll
@@ -451,19 +475,32 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
                 lds_store<u32x2>(dst + 64 * 16, lv);
             }
         };
-        if constexpr (NW == 1) {
+        if constexpr (NWD == 1) {
             qs_and_tiles(IntC<0>{});
-        } else if constexpr (NW == 2) {
+        } else if constexpr (NWD == 2) {
             if (wv == 0) qs_and_tiles(IntC<0>{});
             else qs_and_tiles(IntC<1>{});
-        } else {
+        } else if constexpr (NWD == 4) {
             switch (wv) {
                 case 0: qs_and_tiles(IntC<0>{}); break;
                 case 1: qs_and_tiles(IntC<1>{}); break;
                 case 2: qs_and_tiles(IntC<2>{}); break;
                 default: qs_and_tiles(IntC<3>{}); break;
             }
+        } else {
+            static_assert(NWD == 8, "2, 4 or 8 waves");
+            switch (wv) {
+                case 0: qs_and_tiles(IntC<0>{}); break;
+                case 1: qs_and_tiles(IntC<1>{}); break;
+                case 2: qs_and_tiles(IntC<2>{}); break;
+                case 3: qs_and_tiles(IntC<3>{}); break;
+                case 4: qs_and_tiles(IntC<4>{}); break;
+                case 5: qs_and_tiles(IntC<5>{}); break;
+                case 6: qs_and_tiles(IntC<6>{}); break;
+                default: qs_and_tiles(IntC<7>{}); break;
+            }
         }
+        issue_chunk(cn, kCopyQ);
         // The inter-chunk part decays by lam^(i+1) (times scale); lam^i for a state
         // handed in at the first position.
         if (at_end) {
@@ -477,7 +514,24 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
 #pragma unroll
                 for (int ii = 0; ii < 4; ++ii) O[b][ii] *= lamq[b][ii];
         }
-        lds_barrier();  // P complete
+        // With the dk split, the two waves of a column block each hold Q S over half of
+        // dk for all 64 rows; each finishes row tiles {0, 3} (wd 0) or {1, 2} (wd 1) and
+        // hands the partner its partial sums for the other two.
+        auto own_rows = [&](int b) __attribute__((always_inline)) { return DS == 1 || ((b == 0 || b == 3) ? 0 : 1) == wd; };
+        auto xslot = [&](int w, int b) __attribute__((always_inline)) {
+            return Xbuf + ((w * 2 + (b < 2 ? 0 : 1)) * 64 + lane) * 16;
+        };
+        if constexpr (DS > 1) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (!own_rows(b)) lds_store<f32x4>(xslot(wv, b), O[b]);
+        }
+        lds_barrier();  // P complete (and the partial sums handed over)
+        if constexpr (DS > 1) {
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+                if (own_rows(b)) O[b] += lds_load<f32x4>(xslot(wv ^ 1, b));
+        }
 
         // O += P V.  For row tile b and token block kb, P elements 0..3 are tokens
         // 32kb + 4lg + 0..3 and 4..7 are 32kb + 16 + 4lg + 0..3; V is read in the
@@ -489,6 +543,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
                                         lds_tr16((const uint16_t*)(Vs + v_off(jr + 16, vblk) + vhalf)));
 #pragma unroll
             for (int b = 2 * kb; b < 4; ++b) {
+                if (!own_rows(b)) continue;
                 const uint8_t* pp = Pbuf + (pidx(b, kb) * 2 * 64 + lane) * 16;
                 O[b] = mfma_bf16(lds_load<bf16x8>(pp), vop, O[b]);
                 O[b] = mfma_bf16(lds_load<bf16x8>(pp + 64 * 16), vop, O[b]);
@@ -499,27 +554,29 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         const int64_t r0 = first_row(p0, Lc);
         const auto ro = make_rsrc(p.o + (r0 * H + wk.h) * dv + wk.vb * BV, (uint32_t)(Lc - 1) * orow_b + BV * 4);
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < 4; ++b) {
+            if (!own_rows(b)) continue;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int i = 16 * b + 4 * lg + ii;
                 const int rs = REV ? Lc - 1 - i : i;
                 buf_store_f32(O[b][ii], ro, rs * (int)orow_b + col * 4);
             }
+        }
 
-        split_state<KB>(S, Shi, Slo);
+        split_state<KBL>(S, Shi, Slo);
     };
 
     if (nch > 0) {
 #pragma unroll
-        for (int c = 0; c < DEPTH; ++c) issue_chunk(c);
+        for (int c = 0; c < DEPTH; ++c) issue_chunk(c, kCopyQ | kCopyK | kCopyV);
         // Unrolled over the ring, so that each stage's LDS addresses are a per-lane
         // base plus a constant offset.
         auto step = [&](int c, auto sconst) __attribute__((always_inline)) {
             constexpr int ST = decltype(sconst)::value;
             wait_chunk(c);
             lds_barrier();  // chunk c is in LDS; every wave is done with chunk c - 1
-            issue_chunk(c + DEPTH);
+            issue_chunk(c + DEPTH, kCopyK);
             compute_chunk(c, smem + ST * Cfg::Q_BYTES, smem + KREG + ST * Cfg::Q_BYTES, smem + VREG + ST * Cfg::V_BYTES);
         };
         for (int c = 0; c < nch; c += NST) {
@@ -535,25 +592,25 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     if (p.final_state) {
         const float fm = (p.final_lam && nch > 0) ? p.final_mul * exp2f(g2) : p.final_mul;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MTL; ++mt)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
-                p.final_state[st_off + (int64_t)dmap(mt, 4 * lg + ii) * dv + col] = fm * S[mt][ii];
+                p.final_state[st_off + (int64_t)dmap(wd * MTL + mt, 4 * lg + ii) * dv + col] = fm * S[mt][ii];
     }
 }
 
-template <int DK, int NW, bool REV, bool SONLY>
-__global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_kernel(const FwdParams p) {
-    fwd_bf16_body<DK, NW, REV, SONLY>(p, blockIdx.x);
+template <int DK, int NW, bool REV, bool SONLY, int DS = 1>
+__global__ __launch_bounds__(64 * NW * DS, 1) void fwd_bf16_kernel(const FwdParams p) {
+    fwd_bf16_body<DK, NW, REV, SONLY, DS>(p, blockIdx.x);
 }
 
 // Two problems of the same shape in one launch (a.p[0], a.p[1]: the dk and dv sweeps
 // of the backward).  Workgroup ids alternate between them in runs of kNumXcd, so the
 // two workgroups with the same work id share a die and run together.
-template <int DK, int NW, bool REV>
-__global__ __launch_bounds__(64 * NW, 1) void fwd_bf16_pair_kernel(const FwdArgs a) {
+template <int DK, int NW, bool REV, int DS = 1>
+__global__ __launch_bounds__(64 * NW * DS, 1) void fwd_bf16_pair_kernel(const FwdArgs a) {
     const int bid = blockIdx.x;
-    fwd_bf16_body<DK, NW, REV, false>(a.p[(bid / kNumXcd) & 1], (bid / (2 * kNumXcd)) * kNumXcd + bid % kNumXcd);
+    fwd_bf16_body<DK, NW, REV, false, DS>(a.p[(bid / kNumXcd) & 1], (bid / (2 * kNumXcd)) * kNumXcd + bid % kNumXcd);
 }
 
 // ---------------------------------------------------------------------------
@@ -946,31 +1003,41 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* cu, int n
     order[rank] = i;
 }
 
+// The dk split (two waves per 16-column block, eight waves per workgroup) for four
+// column blocks at dk 64 and 128; at dk 192 its registers would spill, and dk 256
+// leaves no LDS for the partial sums.  The state-only pass keeps one wave per block.
+template <int DK, int NW>
+constexpr int bf16_dk_split() {
+    return (NW == 4 && (DK == 64 || DK == 128)) ? 2 : 1;
+}
+
 template <int DK, int NW>
 hipError_t launch_bf16(const FwdParams& p, const FwdParams* p2, bool rev, bool sonly, hipStream_t s) {
-    const dim3 block(64 * NW);
+    constexpr int DS = bf16_dk_split<DK, NW>();
+    const dim3 block(64 * NW * DS);
     if (p2) {
         FwdArgs a;
         a.p[0] = p;
         a.p[1] = *p2;
         const dim3 grid(2 * fwd_grid_size(p));
         if (rev)
-            hipLaunchKernelGGL((fwd_bf16_pair_kernel<DK, NW, true>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((fwd_bf16_pair_kernel<DK, NW, true, DS>), grid, block, 0, s, a);
         else
-            hipLaunchKernelGGL((fwd_bf16_pair_kernel<DK, NW, false>), grid, block, 0, s, a);
+            hipLaunchKernelGGL((fwd_bf16_pair_kernel<DK, NW, false, DS>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     const dim3 grid(fwd_grid_size(p));
     if (sonly) {
+        const dim3 block1(64 * NW);
         if (rev)
-            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, true>), grid, block1, 0, s, p);
         else
-            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false, true>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false, true>), grid, block1, 0, s, p);
     } else {
         if (rev)
-            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, false, DS>), grid, block, 0, s, p);
         else
-            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false, false>), grid, block, 0, s, p);
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false, false, DS>), grid, block, 0, s, p);
     }
     return hipGetLastError();
 }
