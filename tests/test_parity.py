@@ -129,6 +129,16 @@ def test_workgroup_widths(nw, monkeypatch):
     _compare(w, w.make(), tag=f" nw={nw}")
 
 
+@pytest.mark.parametrize("dk,reverse", [(128, False), (128, True), (64, True)])
+def test_dk_split_small(dk, reverse, monkeypatch):
+    """Four column blocks force the eight-wave kernel (two waves per column block, each
+    with half of the dk rows) on a small ragged GQA problem with an initial state."""
+    monkeypatch.setenv("LATTN_NW", "4")
+    w = inputs.Workload(f"dksplit{dk}", 2, 333, 4, 2, dk, 64, "bf16", 2, 12, reverse=reverse,
+                        init_std=0.5, seed=31)
+    _compare(w, w.make(), tag=" nw=4")
+
+
 def test_no_decay_long():
     """Last layer: g = 0 for every head, the state only grows."""
     w = inputs.Workload("no_decay", 1, 8192, 4, 4, 128, 128, "bf16", 12, 12, seed=7)

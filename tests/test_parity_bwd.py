@@ -59,6 +59,18 @@ def test_bwd_long_d128(n):
     _compare(w)
 
 
+@pytest.mark.parametrize("dk", [64, 128])
+def test_bwd_dk_split(dk, monkeypatch):
+    """Four column blocks force the eight-wave sweeps (the dq sweep and the paired dk and
+    dv sweeps) on a small problem, both directions, with an initial state."""
+    monkeypatch.setenv("LATTN_NW", "4")
+    w = inputs.Workload(f"bwd_dksplit{dk}", 2, 300, 4, 4, dk, dk, "bf16", 2, 12, init_std=0.4,
+                        seed=32)
+    data = w.make()
+    _compare(w, data, tag=" nw=4")
+    _compare(w, data, reverse=True, tag=" nw=4 rev")
+
+
 def test_bwd_d192():
     w = inputs.d192(seqlen=700)
     _compare(w)
