@@ -417,8 +417,12 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_f32_kernel(const FwdParams p
 template <int DK, int NW>
 struct GatedBCfg {
     static constexpr int BV = 16 * NW;
-    static constexpr int PT = 64 * NW;  // producer threads
-    static constexpr int NT = 2 * PT;   // all threads
+    // Matrix waves first, then two producer waves per matrix wave: the producers'
+    // staging and prep are latency-bound, and twice the waves hide more of it.
+    static constexpr int MTH = 64 * NW;      // matrix threads
+    static constexpr int PW = 2;             // producer waves per matrix wave
+    static constexpr int PT = 64 * NW * PW;  // producer threads
+    static constexpr int NT = MTH + PT;      // all threads
     static constexpr int MT = DK / 16;
     static constexpr int KB = DK / 32;  // 32-deep blocks of the dk contraction
     // Dwords per row.  Staged raw chunk (token-major): q, k and a bf16 key gate;
@@ -537,7 +541,7 @@ __device__ inline void quarter_sums(const float (&la)[4][2], int tq, float (&a)[
 }
 
 template <int DK, int NW, bool GF32>
-__global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams p) {
+__global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(const FwdParams p) {
     using Cfg = GatedBCfg<DK, NW>;
     constexpr int BV = Cfg::BV, NT = Cfg::NT, PT = Cfg::PT, MT = Cfg::MT, KB = Cfg::KB;
     constexpr int SQ = Cfg::SQ, SV = Cfg::SV, OPR = Cfg::OPR, TMR = Cfg::TMR, AR = Cfg::AR, BR = Cfg::BR;
@@ -556,7 +560,7 @@ __global__ __launch_bounds__(128 * NW, 1) void gated_bf16_kernel(const FwdParams
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool producer = wv >= NW;
-    const int ptid = tid - PT;  // producer thread index
+    const int ptid = tid - Cfg::MTH;  // producer thread index
     const int H = p.num_heads, dv = p.dv;
     const int64_t L = wk.len;
     const int nch = (int)((L + kGChunk - 1) / kGChunk);
@@ -1047,7 +1051,7 @@ namespace {
 template <int DK, int NW>
 hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
     const dim3 grid(fwd_grid_size(p));
-    // bf16: NW matrix waves plus NW producer waves; fp32: NW waves
+    // bf16: NW matrix waves plus 2 NW producer waves; fp32: NW waves
     const dim3 block_bf16(GatedBCfg<DK, NW>::NT), block_f32(64 * NW);
     if (bf16 && p.gk_is_f32)
         hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true>), grid, block_bf16, 0, s, p);
