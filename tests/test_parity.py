@@ -139,6 +139,17 @@ def test_dk_split_small(dk, reverse, monkeypatch):
     _compare(w, w.make(), tag=" nw=4")
 
 
+@pytest.mark.parametrize("reverse", [False, True])
+def test_dk_split_ragged_packed(reverse, monkeypatch):
+    """The eight-wave kernel on packed sequences of 0, 1, 63, 64, 65, ... tokens (empty
+    sequences, single tokens, partial chunks) with GQA and an initial state."""
+    monkeypatch.setenv("LATTN_NW", "4")
+    lens = [0, 1, 63, 64, 65, 127, 200, 2, 0, 129]
+    w = inputs.Workload("dksplit_ragged", 1, sum(lens), 8, 2, 128, 64, "bf16", 3, 12,
+                        reverse=reverse, seq_lens=lens, init_std=0.3, seed=33)
+    _compare(w, w.make(), tag=" nw=4" + (" rev" if reverse else ""))
+
+
 def test_no_decay_long():
     """Last layer: g = 0 for every head, the state only grows."""
     w = inputs.Workload("no_decay", 1, 8192, 4, 4, 128, 128, "bf16", 12, 12, seed=7)

@@ -71,6 +71,16 @@ def test_bwd_dk_split(dk, monkeypatch):
     _compare(w, data, reverse=True, tag=" nw=4 rev")
 
 
+def test_bwd_dk_split_ragged_packed(monkeypatch):
+    """The eight-wave sweeps on packed sequences with empty ones and partial chunks."""
+    monkeypatch.setenv("LATTN_NW", "4")
+    lens = [0, 1, 63, 64, 65, 130, 0, 7]
+    w = inputs.Workload("bwd_dksplit_ragged", 1, sum(lens), 4, 4, 128, 64, "bf16", 3, 12,
+                        seq_lens=lens, init_std=0.3, seed=34)
+    _compare(w, tag=" nw=4")
+    _compare(w, reverse=True, tag=" nw=4 rev")
+
+
 def test_bwd_d192():
     w = inputs.d192(seqlen=700)
     _compare(w)
