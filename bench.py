@@ -18,6 +18,7 @@ Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
   gated         the gated (GLA) forward on the same inputs plus a per-key-channel gate g,
                 against HBM (its binding roofline at bf16 MFMA rates), with the bf16
                 matrix figure beside it,
+  bf16_out      the same forward with o in bf16 (skipped with --no-bf16-out),
   sweep         the forward at N = 512 .. 16384 (same B, H, head dims), each N rotating
                 over enough input sets that about 1 GB is touched between repeats, with
                 the Lightning-2 forward time the pages print for that N beside it
@@ -53,10 +54,11 @@ KERNEL_SRCS = [os.path.join(ROOT, "decayed_recurrent_attention_amd", "csrc", n)
                for n in ("lattn_kernels.hip", "lattn_device.h", "lattn_launch.h")]
 
 
-def algorithmic_bytes(B, T, H, Hkv, dk, dv, in_bytes, with_init=False):
-    """Bytes the forward must move at least once: q, k, v in, o (fp32) out, final state out."""
+def algorithmic_bytes(B, T, H, Hkv, dk, dv, in_bytes, with_init=False, o_bytes=4):
+    """Bytes the forward must move at least once: q, k, v in, o (fp32, or bf16 with
+    o_bytes=2) out, final state out."""
     qkv = B * T * (H * dk + Hkv * dk + Hkv * dv) * in_bytes
-    o = B * T * H * dv * 4
+    o = B * T * H * dv * o_bytes
     state = B * H * dk * dv * 4 * (2 if with_init else 1)
     return qkv + o + state
 
@@ -261,6 +263,8 @@ def main():
                     help="skip the intra-sequence split measurement (B1 H8, same head dims and N)")
     ap.add_argument("--decode-batch", type=int, default=128,
                     help="sequences per decoding step in the decode measurement (0 skips it)")
+    ap.add_argument("--no-bf16-out", action="store_true",
+                    help="skip the forward with a bf16 o (same inputs)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the forward sweep over N = 512 .. 16384 (same B, H, head dims)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -304,6 +308,34 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel mean "
           f"{mean_kernel_ms:.4f} ms min {min(kernel_ms):.4f} max {max(kernel_ms):.4f}",
           file=sys.stderr, flush=True)
+
+    bf16_out = None
+    if not args.no_bf16_out:
+        # The same forward with o in bf16 (each element the round-to-nearest-even of the
+        # fp32 result): 20 % fewer bytes per call.
+        print("[bench] forward with a bf16 o", file=sys.stderr, flush=True)
+        ob = torch.empty((B, T, H, dv), device=dev, dtype=torch.bfloat16)
+        prob_b = lattn.LattnProblem(B, T, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_BF16)
+
+        def step_b():
+            rc = lattn.lattn_fwd(prob_b, q, k, v, g, w.scale, None, False, None, ob, fs,
+                                 stream=stream.cuda_stream)
+            if rc != lattn.LATTN_OK:
+                raise lattn.LattnError(rc)
+
+        b_wall, b_ms = time_calls(torch, step_b, stream, args.warmup, args.steps)
+        b_mean = sum(b_ms) / len(b_ms)
+        b_alg = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2, o_bytes=2)
+        b_gbs = b_alg / (b_mean * 1e-3) / 1e9
+        bf16_out = {"ms_per_step": b_wall, "tokens_per_s": B * T / (b_wall * 1e-3),
+                    "roofline": {"bound": "hbm", "achieved": b_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": b_gbs / HBM_PEAK_GBS, "algorithmic_bytes": b_alg,
+                                 "call_ms": b_mean},
+                    "inputs": "the forward's; o bf16 (round to nearest even of the fp32 result), "
+                              "fp32 final state"}
+        print(f"[bench] bf16 o {args.steps} steps: {b_wall:.4f} ms/step wall, mean {b_mean:.4f} ms, "
+              f"{b_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del ob
 
     sweep = None
     if not args.no_sweep:
@@ -540,6 +572,8 @@ def main():
         line["split"] = split
     if gated is not None:
         line["gated"] = gated
+    if bf16_out is not None:
+        line["bf16_out"] = bf16_out
     if sweep is not None:
         line["sweep"] = sweep
     print(json.dumps(line), flush=True)

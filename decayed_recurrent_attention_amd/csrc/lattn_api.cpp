@@ -33,15 +33,17 @@ bool have_dims(int in_dtype, int dk, int dv) {
     return false;
 }
 
-// Shape/dtype checks that do not look at pointers.
-int check_problem(const lattn_problem& p) {
+// Shape/dtype checks that do not look at pointers.  A bf16 o is accepted where the
+// caller allows it (the forward) and only for bf16 input.
+int check_problem(const lattn_problem& p, bool bf16_out_ok = false) {
     if (p.batch < 1 || p.seqlen < 0 || p.num_heads < 1 || p.num_kv_heads < 1 || p.head_dim_qk < 1 ||
         p.head_dim_v < 1 || p.num_seqs < 0)
         return LATTN_ERR_INVALID_ARG;
     if (p.num_heads % p.num_kv_heads != 0) return LATTN_ERR_HEADS;
     if (is_varlen(p) && p.batch != 1) return LATTN_ERR_VARLEN_BATCH;
     if (p.in_dtype != LATTN_BF16 && p.in_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
-    if (p.out_dtype != LATTN_F32) return LATTN_ERR_UNSUPPORTED;
+    const bool bf16_out = bf16_out_ok && p.in_dtype == LATTN_BF16 && p.out_dtype == LATTN_BF16;
+    if (p.out_dtype != LATTN_F32 && !bf16_out) return LATTN_ERR_UNSUPPORTED;
     if (!have_dims(p.in_dtype, p.head_dim_qk, p.head_dim_v)) return LATTN_ERR_UNSUPPORTED;
     return LATTN_OK;
 }
@@ -233,7 +235,7 @@ const char* lattn_status_string(int status) {
 }
 
 size_t lattn_fwd_workspace_size(const lattn_problem* p) {
-    if (p == nullptr || check_problem(*p) != LATTN_OK) return 0;
+    if (p == nullptr || check_problem(*p, true) != LATTN_OK) return 0;
     if (!is_varlen(*p)) {
         int nw = 0;
         const Split sp = plan_forward(*p, nw);
@@ -261,8 +263,9 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
               float scale, const float* initial_state, int reverse, const int32_t* cu_seqlens, void* o,
               float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
     if (p == nullptr) return LATTN_ERR_INVALID_ARG;
-    const int rc = check_problem(*p);
+    const int rc = check_problem(*p, true);
     if (rc != LATTN_OK) return rc;
+    const int o_bf16 = p->out_dtype == LATTN_BF16 ? 1 : 0;
     const bool varlen = cu_seqlens != nullptr;
     if (varlen != is_varlen(*p)) return LATTN_ERR_INVALID_ARG;
     const int64_t tokens = (int64_t)p->batch * p->seqlen;
@@ -296,6 +299,7 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
         f3 = f1;
         f3.init = s_in;
         f3.o = static_cast<float*>(o);
+        f3.o_bf16 = o_bf16;
         f3.final_state = nullptr;
         const int dc = device_check();
         if (dc != LATTN_OK) return dc;
@@ -317,6 +321,7 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
     fp.v = v;
     fp.init = initial_state;
     fp.o = static_cast<float*>(o);
+    fp.o_bf16 = o_bf16;
     fp.final_state = final_state;
 
     const int dc = device_check();

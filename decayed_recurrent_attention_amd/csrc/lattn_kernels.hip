@@ -97,6 +97,17 @@ constexpr int kStreamStore = 2 | 16;
 __device__ inline void buf_store_f32(float v, __amdgpu_buffer_rsrc_t r, int off) {
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, kStreamStore);
 }
+// Two bf16 (round to nearest even), a at the lower address.  Default cache policy: a
+// wave writes only 32 bytes of a bf16 row (16 columns), and the four waves' pieces of a
+// 128-byte line must merge in L2 (with the streaming hint the bf16 forward ran 1.50 ms
+// against 1.09).
+__device__ inline void buf_store_bf16x2(float a, float b, __amdgpu_buffer_rsrc_t r, int off) {
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(a, b), r, off, 0, 0);
+}
+// The value of lane l ^ 1 (the neighbouring column of an MFMA output tile).
+__device__ inline float lane_pair_swap(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+}
 
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane s
 // supplies the address of four consecutive 16-bit elements; lane i receives
@@ -237,7 +248,8 @@ __device__ inline void split_state(const f32x4* S, bf16x8* hi, bf16x8* lo) {
 // SONLY: only the state recurrence (no Q, no output): the final state of every
 // sequence from K and V alone.
 // work_id: the workgroup's unit of work (its id for a single problem).
-template <int DK, int NW, bool REV, bool SONLY, int DS = 1>
+// OB16: o in bf16 (round to nearest even of the fp32 result) instead of fp32.
+template <int DK, int NW, bool REV, bool SONLY, int DS = 1, bool OB16 = false>
 __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdParams& p, int work_id) {
     using Cfg = Bf16Cfg<DK, NW, DS>;
     constexpr int BV = Cfg::BV, PP = Cfg::PP, PVB = Cfg::PVB, KB = Cfg::KB, MT = Cfg::MT;
@@ -267,7 +279,8 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     const int qh = p.swap_heads ? wk.kvh : wk.h, kh = p.swap_heads ? wk.h : wk.kvh;
     const int QH = p.swap_heads ? p.num_kv_heads : H, KH = p.swap_heads ? H : p.num_kv_heads;
     const uint32_t qrow_b = (uint32_t)QH * DK * 2, krow_b = (uint32_t)KH * DK * 2;
-    const uint32_t vrow_b = (uint32_t)KH * dv * 2, orow_b = (uint32_t)H * dv * 4;
+    constexpr uint32_t ob = OB16 ? 2u : 4u;  // bytes per o element
+    const uint32_t vrow_b = (uint32_t)KH * dv * 2, orow_b = (uint32_t)H * dv * ob;
     const uint16_t* qg = static_cast<const uint16_t*>(p.q) + (int64_t)qh * DK;
     const uint16_t* kg = static_cast<const uint16_t*>(p.k) + (int64_t)kh * DK;
     const uint16_t* vg = static_cast<const uint16_t*>(p.v) + (int64_t)kh * dv + wk.vb * BV;
@@ -364,7 +377,8 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     // order: the copies of DEPTH-1 later chunks and the output stores of the
     // min(c, DEPTH) chunks computed since.
     constexpr int NCOPY = SONLY ? Cfg::QCOPIES + Cfg::VCOPIES : Cfg::NCOPY;
-    constexpr int NSTORE = SONLY ? 0 : Cfg::NSTORE;
+    // bf16 o: two adjacent columns per dword, so half as many stores
+    constexpr int NSTORE = SONLY ? 0 : (OB16 ? Cfg::NSTORE / 2 : Cfg::NSTORE);
     constexpr int W0 = (DEPTH - 1) * NCOPY;
     constexpr int WC = W0 + DEPTH * NSTORE;
     auto wait_chunk = [&](int c) __attribute__((always_inline)) {
@@ -556,15 +570,30 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
 
         // Store the chunk's outputs; rows past the end fall outside the descriptor.
         const int64_t r0 = first_row(p0, Lc);
-        const auto ro = make_rsrc(p.o + (r0 * H + wk.h) * dv + wk.vb * BV, (uint32_t)(Lc - 1) * orow_b + BV * 4);
+        const auto ro = make_rsrc(reinterpret_cast<char*>(p.o) + ((r0 * H + wk.h) * dv + wk.vb * BV) * ob,
+                                  (uint32_t)(Lc - 1) * orow_b + BV * ob);
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             if (!own_rows(b)) continue;
+            if constexpr (OB16) {
+                // Lanes lr and lr ^ 1 hold neighbouring columns: the even lane writes
+                // both columns of rows ii = 0, 1, the odd lane those of rows 2, 3.
+                const bool odd = (lr & 1) != 0;
+                const float t0 = lane_pair_swap(O[b][0]), t1 = lane_pair_swap(O[b][1]);
+                const float t2 = lane_pair_swap(O[b][2]), t3 = lane_pair_swap(O[b][3]);
+                const float a0 = odd ? t2 : O[b][0], a1 = odd ? O[b][2] : t0;
+                const float b0 = odd ? t3 : O[b][1], b1 = odd ? O[b][3] : t1;
+                const int i0 = 16 * b + 4 * lg + (odd ? 2 : 0), cpair = (col & ~1) * 2;
+                const int r0s = REV ? Lc - 1 - i0 : i0, r1s = REV ? Lc - 2 - i0 : i0 + 1;
+                buf_store_bf16x2(a0, a1, ro, r0s * (int)orow_b + cpair);
+                buf_store_bf16x2(b0, b1, ro, r1s * (int)orow_b + cpair);
+            } else {
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int i = 16 * b + 4 * lg + ii;
-                const int rs = REV ? Lc - 1 - i : i;
-                buf_store_f32(O[b][ii], ro, rs * (int)orow_b + col * 4);
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int i = 16 * b + 4 * lg + ii;
+                    const int rs = REV ? Lc - 1 - i : i;
+                    buf_store_f32(O[b][ii], ro, rs * (int)orow_b + col * 4);
+                }
             }
         }
 
@@ -603,9 +632,9 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     }
 }
 
-template <int DK, int NW, bool REV, bool SONLY, int DS = 1>
+template <int DK, int NW, bool REV, bool SONLY, int DS = 1, bool OB16 = false>
 __global__ __launch_bounds__(64 * NW * DS, 1) void fwd_bf16_kernel(const FwdParams p) {
-    fwd_bf16_body<DK, NW, REV, SONLY, DS>(p, blockIdx.x);
+    fwd_bf16_body<DK, NW, REV, SONLY, DS, OB16>(p, blockIdx.x);
 }
 
 // Two problems of the same shape in one launch (a.p[0], a.p[1]: the dk and dv sweeps
@@ -1037,6 +1066,11 @@ hipError_t launch_bf16(const FwdParams& p, const FwdParams* p2, bool rev, bool s
             hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, true>), grid, block1, 0, s, p);
         else
             hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false, true>), grid, block1, 0, s, p);
+    } else if (p.o_bf16) {
+        if (rev)
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, false, DS, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, false, false, DS, true>), grid, block, 0, s, p);
     } else {
         if (rev)
             hipLaunchKernelGGL((fwd_bf16_kernel<DK, NW, true, false, DS>), grid, block, 0, s, p);

@@ -51,6 +51,8 @@ struct FwdParams {
                       //    (default 0); final_state may be null
     int seg_count;    // > 0: sequence n is segment n % seg_count of batch row n / seg_count,
     int seg_len;      //    positions [s * seg_len, min((s + 1) * seg_len, seqlen)) (default 0)
+    int o_bf16;       // 1: o holds bf16, each the round-to-nearest-even of the fp32 result
+                      //    (bf16-input chunked kernel only; default 0: fp32)
     // Gated recurrence only (gated kernels): the key log-decay gate g [B, T, H, dk] and
     // the value gate gv [B, T, H, dv], in the input dtype (g in fp32 when gk_is_f32:
     // the sum of two key gates), or null; the direction.

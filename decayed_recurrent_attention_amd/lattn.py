@@ -259,7 +259,7 @@ def _prepare(query, key, value, g_gamma, softmax_scale, initial_state, cu_seqlen
 
 
 def recurrent(query, key, value, g=None, g_gamma=None, gk=None, gv=None, softmax_scale=None,
-              initial_state=None, reverse=False, cu_seqlens=None):
+              initial_state=None, reverse=False, cu_seqlens=None, out_dtype=None):
     """Decayed recurrent attention forward on the GPU (the recurrent interface page's
     argument order).
 
@@ -267,16 +267,28 @@ def recurrent(query, key, value, g=None, g_gamma=None, gk=None, gv=None, softmax
     packed input (``cu_seqlens``) may drop the batch axis.  g, gk ([.., T, H, dk]) and gv
     ([.., T, H, dv]) are optional per-token log-decay gates in the dtype of q; with any
     of them the gated kernel runs, else the Lightning kernel with g_gamma [H].
-    Returns (o float32 [.., T, H, dv], final_state float32 [N_seq, H, dk, dv]).
+    Returns (o [.., T, H, dv], final_state float32 [N_seq, H, dk, dv]); o is float32, or
+    bf16 with ``out_dtype=torch.bfloat16`` for bf16 input without gates (each element the
+    round-to-nearest-even of the float32 result).
     """
     import torch
 
+    bf16_out = out_dtype is not None and out_dtype == torch.bfloat16
+    if out_dtype is not None and out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
     if g is not None or gk is not None or gv is not None:
+        if bf16_out:
+            raise ValueError("the gated recurrence returns o in float32 only")
         return recurrent_gated(query, key, value, g=g, gk=gk, gv=gv, g_gamma=g_gamma,
                                softmax_scale=softmax_scale, initial_state=initial_state,
                                reverse=reverse, cu_seqlens=cu_seqlens)
     a = _prepare(query, key, value, g_gamma, softmax_scale, initial_state, cu_seqlens)
-    o = torch.empty((a.B, a.T, a.H, a.dv), device=a.dev, dtype=torch.float32)
+    if bf16_out:
+        if a.q.dtype != torch.bfloat16:
+            raise ValueError("a bf16 o needs bf16 inputs")
+        a.prob.out_dtype = LATTN_BF16
+    o = torch.empty((a.B, a.T, a.H, a.dv), device=a.dev,
+                    dtype=torch.bfloat16 if bf16_out else torch.float32)
     fs = torch.empty(a.state_shape, device=a.dev, dtype=torch.float32)
     ws_bytes = lattn_fwd_workspace_size(a.prob)
     ws = torch.empty(ws_bytes, device=a.dev, dtype=torch.uint8) if ws_bytes else None
@@ -385,7 +397,7 @@ def lightning_g_gamma_tensor(num_heads: int, layer_idx: int, num_layers: int, de
 
 
 def lightning_attn(query, key, value, layer_idx: int, num_layers: int, softmax_scale=None,
-                   initial_state=None, reverse=False, cu_seqlens=None):
+                   initial_state=None, reverse=False, cu_seqlens=None, out_dtype=None):
     """Lightning attention forward (lightning_attn interface page): the layer-dependent
     decay schedule, default scale dk^-1/2, then the recurrent forward."""
     if num_layers < 1 or not 0 <= layer_idx <= num_layers:
@@ -401,7 +413,8 @@ def lightning_attn(query, key, value, layer_idx: int, num_layers: int, softmax_s
         softmax_scale = float(np.float32(key.shape[-1] ** -0.5))
     g = lightning_g_gamma_tensor(query.shape[-2], layer_idx, num_layers, query.device)
     return recurrent(query, key, value, g_gamma=g, softmax_scale=softmax_scale,
-                     initial_state=initial_state, reverse=reverse, cu_seqlens=cu_seqlens)
+                     initial_state=initial_state, reverse=reverse, cu_seqlens=cu_seqlens,
+                     out_dtype=out_dtype)
 
 
 def lightning_attn_bwd(query, key, value, d_o, layer_idx: int, num_layers: int, softmax_scale=None,

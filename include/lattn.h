@@ -64,7 +64,8 @@ typedef struct {
     int32_t head_dim_v;   /* dv */
     int32_t num_seqs;     /* packed sequences: > 0 exactly when cu_seqlens is given, else 0 (then N_seq = B) */
     int32_t in_dtype;     /* lattn_dtype of q, k, v: LATTN_BF16 or LATTN_F32 */
-    int32_t out_dtype;    /* lattn_dtype of o: LATTN_F32 (the only one supported) */
+    int32_t out_dtype;    /* lattn_dtype of o: LATTN_F32, or LATTN_BF16 for lattn_fwd
+                             with bf16 input (every other call takes LATTN_F32) */
 } lattn_problem;
 
 /*
@@ -88,14 +89,17 @@ size_t lattn_fwd_workspace_size(const lattn_problem* p);
  *   cu_seqlens     device int32 [N_seq + 1], or NULL.  Must start at 0, be
  *                  non-decreasing and end at seqlen; values outside [0, seqlen]
  *                  are clamped into it so that no access leaves the buffers.
- *   o              device float32 output.
+ *   o              device output in out_dtype: float32, or (bf16 input only) bf16,
+ *                  each element the round-to-nearest-even of the float32 result.
  *   final_state    device float32 output [N_seq, H, dk, dv].
  *   workspace      device buffer of >= lattn_fwd_workspace_size(p) bytes, 16-byte
  *                  aligned (may be NULL when that is 0).  Owned by the caller;
  *                  contents on entry are ignored; must not be shared by calls that
  *                  overlap in time.
  * Supported: in_dtype BF16 with dk in {32, 64, 128, 192, 256}; in_dtype F32 with
- * dk in {16, 32, 64, 128}; dv a multiple of 16 up to 256; out_dtype F32.
+ * dk in {16, 32, 64, 128}; dv a multiple of 16 up to 256; out_dtype F32, or BF16
+ * with in_dtype BF16 (o in the input dtype, half the output bytes; the state stays
+ * float32).
  * Returns LATTN_OK or a negative status; buffers are untouched on error.
  */
 int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* v,

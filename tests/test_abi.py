@@ -83,7 +83,8 @@ def call(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, init=None, cu=None, o=FAKE, fs
     (P(head_dim_v=24), lattn.LATTN_ERR_UNSUPPORTED),
     (P(head_dim_v=272), lattn.LATTN_ERR_UNSUPPORTED),
     (P(in_dtype=7), lattn.LATTN_ERR_UNSUPPORTED),
-    (P(out_dtype=lattn.LATTN_BF16), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(in_dtype=lattn.LATTN_F32, out_dtype=lattn.LATTN_BF16), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(out_dtype=7), lattn.LATTN_ERR_UNSUPPORTED),
     (P(in_dtype=lattn.LATTN_F32, head_dim_qk=192), lattn.LATTN_ERR_UNSUPPORTED),
     (P(head_dim_qk=128, head_dim_v=16), lattn.LATTN_ERR_UNSUPPORTED),
 ])
@@ -104,6 +105,18 @@ def test_pointer_errors():
     L = lattn.load_library()
     assert L.lattn_fwd(None, FAKE, FAKE, FAKE, FAKE, 1.0, None, 0, None, FAKE, FAKE, None, 0,
                        None) == lattn.LATTN_ERR_INVALID_ARG
+
+
+def test_bf16_output_accepted():
+    """bf16 input may ask for a bf16 o: validation passes the dtypes and stops at the
+    first bad pointer; the workspace is the same as for a float32 o."""
+    prob = P(out_dtype=lattn.LATTN_BF16)
+    assert call(prob, q=None) == lattn.LATTN_ERR_INVALID_ARG
+    assert call(prob, o=FAKE + 2) == lattn.LATTN_ERR_INVALID_ARG  # misaligned o
+    packed = P(batch=1, seqlen=300, num_seqs=5, out_dtype=lattn.LATTN_BF16)
+    assert lattn.lattn_fwd_workspace_size(packed) == lattn.lattn_fwd_workspace_size(
+        P(batch=1, seqlen=300, num_seqs=5))
+    assert call(packed, cu=FAKE) == lattn.LATTN_ERR_WORKSPACE
 
 
 def test_varlen_workspace():
@@ -183,6 +196,7 @@ def call_decode(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, s_in=FAKE, s_out=FAKE, 
     (P(seqlen=1, head_dim_qk=40), lattn.LATTN_ERR_UNSUPPORTED),
     (P(seqlen=1, head_dim_v=272), lattn.LATTN_ERR_UNSUPPORTED),
     (P(seqlen=1, in_dtype=5), lattn.LATTN_ERR_UNSUPPORTED),
+    (P(seqlen=1, out_dtype=lattn.LATTN_BF16), lattn.LATTN_ERR_UNSUPPORTED),  # decode: float32 o
 ])
 def test_decode_problem_errors(prob, status):
     assert call_decode(prob) == status
@@ -203,6 +217,11 @@ def test_split_workspace(monkeypatch):
     # widest workgroups: 8 heads x 2 value blocks = 16 -> 16 segments of 2048 tokens
     assert lattn.lattn_fwd_workspace_size(prob) == 2 * 16 * 8 * 128 * 128 * 4
     assert call(prob) == lattn.LATTN_ERR_WORKSPACE
+    # a bf16 o splits the same way (the split states are float32)
+    prob_b = P(batch=1, seqlen=32768, num_heads=8, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+               out_dtype=lattn.LATTN_BF16)
+    assert lattn.lattn_fwd_workspace_size(prob_b) == 2 * 16 * 8 * 128 * 128 * 4
+    assert call(prob_b) == lattn.LATTN_ERR_WORKSPACE
     # enough pairs, short sequences, fp32 and packed input never split
     assert lattn.lattn_fwd_workspace_size(P(batch=4, seqlen=32768, num_heads=32, head_dim_qk=128,
                                             head_dim_v=128)) == 0
