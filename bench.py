@@ -19,6 +19,8 @@ Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
                 against HBM (its binding roofline at bf16 MFMA rates), with the bf16
                 matrix figure beside it,
   bf16_out      the same forward with o in bf16 (skipped with --no-bf16-out),
+  configs       the other parity workloads (tiny fp32, B2 H8 d64, B2 H12 d192, packed GQA
+                in both directions), forward only (skipped with --no-configs),
   sweep         the forward at N = 512 .. 16384 (same B, H, head dims), each N rotating
                 over enough input sets that about 1 GB is touched between repeats, with
                 the Lightning-2 forward time the pages print for that N beside it
@@ -265,6 +267,8 @@ def main():
                     help="sequences per decoding step in the decode measurement (0 skips it)")
     ap.add_argument("--no-bf16-out", action="store_true",
                     help="skip the forward with a bf16 o (same inputs)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip timing the other parity workloads (tiny fp32, d64, d192, packed GQA)")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the forward sweep over N = 512 .. 16384 (same B, H, head dims)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -380,6 +384,53 @@ def main():
                       "tokens_per_s": B * T / (ms_per_step * 1e-3), "hbm_gbs": full_gbs,
                       "hbm_frac": full_gbs / HBM_PEAK_GBS, "buffer_sets": 1,
                       "page_lightning2_ms": PAGE_LIGHTNING2_SWEEP_MS.get(T)})
+
+    configs = None
+    if not args.no_configs:
+        # The other workloads of the parity suite, forward only, same timing: ms per call
+        # (HIP events), tokens/s and the HBM fraction on each one's algorithmic bytes.
+        print("[bench] other workloads", file=sys.stderr, flush=True)
+        configs = []
+        for cw in (inputs.tiny_fp32(), inputs.bf16_d64(), inputs.d192(), inputs.varlen_gqa(False),
+                   inputs.varlen_gqa(True)):
+            cd = cw.make()
+            f32in = cw.dtype == "f32"
+            dev_in = (lambda a: torch.from_numpy(a).to(dev)) if f32in else to_dev
+            cq, ck, cv = (dev_in(cd[n]) for n in ("q", "k", "v"))
+            cinit = None if cd["initial_state"] is None else torch.from_numpy(cd["initial_state"]).to(dev)
+            cu = None if cd["cu_seqlens"] is None else torch.from_numpy(cd["cu_seqlens"]).to(dev, torch.int32)
+            cg = torch.from_numpy(lattn.lattn_lightning_g_gamma(cw.num_heads, cw.layer_idx, cw.num_layers)).to(dev)
+            nseq = cw.num_seqs
+            co = torch.empty((cw.batch, cw.seqlen, cw.num_heads, cw.dv), device=dev, dtype=torch.float32)
+            cfs = torch.empty((nseq, cw.num_heads, cw.dk, cw.dv), device=dev, dtype=torch.float32)
+            cprob = lattn.LattnProblem(cw.batch, cw.seqlen, cw.num_heads, cw.num_kv_heads, cw.dk, cw.dv,
+                                       nseq if cu is not None else 0,
+                                       lattn.LATTN_F32 if f32in else lattn.LATTN_BF16, lattn.LATTN_F32)
+            cws_n = lattn.lattn_fwd_workspace_size(cprob)
+            cws = torch.empty(cws_n, device=dev, dtype=torch.uint8) if cws_n else None
+
+            def cstep():
+                rc = lattn.lattn_fwd(cprob, cq, ck, cv, cg, cw.scale, cinit, cw.reverse, cu, co, cfs, cws,
+                                     stream=stream.cuda_stream)
+                if rc != lattn.LATTN_OK:
+                    raise lattn.LattnError(rc)
+
+            c_wall, c_ms = time_calls(torch, cstep, stream, args.warmup, args.steps)
+            c_mean = sum(c_ms) / len(c_ms)
+            ntok = cw.batch * cw.seqlen
+            c_alg = (ntok * (cw.num_heads * cw.dk + cw.num_kv_heads * (cw.dk + cw.dv)) * (4 if f32in else 2)
+                     + ntok * cw.num_heads * cw.dv * 4
+                     + nseq * cw.num_heads * cw.dk * cw.dv * 4 * (2 if cinit is not None else 1))
+            c_gbs = c_alg / (c_mean * 1e-3) / 1e9
+            configs.append({"workload": cw.name, "batch": cw.batch, "tokens": ntok, "num_seqs": nseq,
+                            "num_heads": cw.num_heads, "num_kv_heads": cw.num_kv_heads, "head_dim_qk": cw.dk,
+                            "head_dim_v": cw.dv, "dtype": cw.dtype, "reverse": bool(cw.reverse),
+                            "initial_state": cinit is not None, "ms_per_step": c_wall, "kernel_ms": c_mean,
+                            "tokens_per_s": ntok / (c_wall * 1e-3), "algorithmic_bytes": c_alg,
+                            "hbm_gbs": c_gbs, "hbm_frac": c_gbs / HBM_PEAK_GBS})
+            print(f"[bench] {cw.name}: {c_wall:.4f} ms/step wall, kernel mean {c_mean:.4f} ms, "
+                  f"{c_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+            del cq, ck, cv, co, cfs, cws
 
     bwd = None
     if not args.no_bwd:
@@ -576,6 +627,8 @@ def main():
         line["bf16_out"] = bf16_out
     if sweep is not None:
         line["sweep"] = sweep
+    if configs is not None:
+        line["configs"] = configs
     print(json.dumps(line), flush=True)
 
 
