@@ -162,7 +162,13 @@ Split choose_split(const lattn_problem& p, int nw) {
     } else {
         if (wgs >= 128) return sp;  // at least half the compute units busy already
         want = (int)((256 + wgs - 1) / wgs);
-        const int cap = p.seqlen / (16 * lattn::kChunk);  // segments of at least 16 chunks
+        // Segments of at least 4 chunks up to dk 128 and at least 16 chunks above: a
+        // segment pays for a state-only pass and a scan, which cost more at dk 192 and
+        // 256.  Measured (one box): B2 H8 d64 N2048 runs 23 us in 8 segments against
+        // 41 us in 2 and 57 us unsplit; B2 H12 d192 N2048 runs 75 us in 2 segments and
+        // 84 us in 4.
+        const int min_chunks = p.head_dim_qk <= 128 ? 4 : 16;
+        const int cap = p.seqlen / (min_chunks * lattn::kChunk);
         if (want > cap) want = cap;
         if (want < 2) return sp;
     }

@@ -225,8 +225,14 @@ def test_split_workspace(monkeypatch):
     # enough pairs, short sequences, fp32 and packed input never split
     assert lattn.lattn_fwd_workspace_size(P(batch=4, seqlen=32768, num_heads=32, head_dim_qk=128,
                                             head_dim_v=128)) == 0
-    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=1500, num_heads=2)) == 0
-    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=32768, num_heads=2,
+    # too short for two segments: fewer than 8 chunks at dk <= 128, 32 above
+    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=500, num_heads=2, num_kv_heads=2)) == 0
+    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=2000, num_heads=2, num_kv_heads=2,
+                                            head_dim_qk=192, head_dim_v=64)) == 0
+    # short segments (4 chunks) at dk 64: B1 H2 N1500 -> 5 segments of 320 tokens
+    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=1500, num_heads=2, num_kv_heads=2)) == \
+        2 * 5 * 2 * 64 * 64 * 4
+    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=32768, num_heads=2, num_kv_heads=2,
                                             in_dtype=lattn.LATTN_F32)) == 0
     monkeypatch.setenv("LATTN_SPLIT", "3")
     small = P(batch=2, seqlen=1000, num_heads=4, num_kv_heads=4)
