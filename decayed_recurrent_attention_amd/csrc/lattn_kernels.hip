@@ -443,7 +443,8 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         // Q S_prev for all 64 rows of this wave's columns (over its dk rows), and this
         // wave's share of the ten lower-triangle (K Q^T) tiles: tiles t = wv, wv + NWD,
         // ... (round robin).  Each wave masks its tiles and publishes P = scale (A .* M) in
-        // bf16 hi + lo to LDS in A-operand layout; all waves then read all of P.
+        // bf16 hi + lo to LDS in A-operand layout; after a barrier each wave reads the
+        // blocks of P for the row tiles it finishes.
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         f32x4 O[4];
 #pragma unroll
