@@ -683,8 +683,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
         }
     };
 
-    // Prep of chunk c (producer waves): staged(c) -> derived(c), the summed decays
-    // (exact path) and the chunk's flag.
+    // Prep of chunk c (producer waves): staged(c) -> derived(c) and the chunk's flag.
     auto prep_chunk = [&](int c) __attribute__((always_inline)) {
         const uint32_t* st = staged(c);
         uint32_t* d = derived(c);
@@ -729,7 +728,6 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
                 const int t = 4 * tq + tau;
-                lds_store<f32x2>(Af + t * AR + 2 * pp, f32x2{a[tau][0], a[tau][1]});
                 const uint32_t qw = st[Cfg::ST_Q + t * SQ + pp], kw = st[Cfg::ST_K + t * SQ + pp];
                 const float qv[2] = {bf16_lo(qw), bf16_hi(qw)}, kv[2] = {bf16_lo(kw), bf16_hi(kw)};
 #pragma unroll
@@ -783,7 +781,6 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
 #pragma unroll
                 for (int tau = 0; tau < 4; ++tau) {
                     const int t = 4 * tq + tau;
-                    lds_store<f32x2>(Bf + t * BR + 2 * qq, f32x2{b[tau][0], b[tau][1]});
                     const uint32_t vw = st[Cfg::ST_V + t * SV + qq];
                     const float vv[2] = {bf16_lo(vw), bf16_hi(vw)};
 #pragma unroll
@@ -818,10 +815,32 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
         }
     };
 
-    // Exact intra term of a wide chunk (all threads, between barriers): W, then
-    // OI = W (v .* 2^{B_t - B_u}), from the raw staged chunk and the summed decays.
+    // Exact intra term of a wide chunk (all threads, between barriers): the summed
+    // decays A and B of every channel from the staged gates (the prep keeps its own
+    // only in registers, since few chunks come this way), then W, then
+    // OI = W (v .* 2^{B_t - B_u}).
     auto exact_chunk = [&](int c) __attribute__((always_inline)) {
         const uint32_t* st = staged(c);
+        const int nv = chunk_nv(c);
+        for (int i = tid; i < DK + (has_gv ? BV : 0); i += NT) {
+            float acc = 0.f;
+            if (i < DK) {
+                for (int t = 0; t < kGChunk; ++t) {
+                    float gi;
+                    if constexpr (GF32) gi = reinterpret_cast<const float*>(st + Cfg::ST_G + t * SGR)[i];
+                    else gi = bf16_half(st[Cfg::ST_G + t * SGR + (i >> 1)], i & 1);
+                    acc += t < nv ? kLog2e * gi + gg2 : 0.f;
+                    Af[t * AR + i] = acc;
+                }
+            } else {
+                const int j = i - DK;
+                for (int t = 0; t < kGChunk; ++t) {
+                    acc += t < nv ? kLog2e * bf16_half(st[Cfg::ST_GV + t * SV + (j >> 1)], j & 1) : 0.f;
+                    Bf[t * BR + j] = acc;
+                }
+            }
+        }
+        lds_barrier();
         for (int e = tid; e < kGChunk * kGChunk; e += NT) {
             const int t = e >> 4, u = e & 15;
             float w = 0.f;
