@@ -25,9 +25,7 @@ FLAGS = [
 ]
 
 
-def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
-    """Compile every source into ``out`` (always recompiles)."""
-    cmd = [HIPCC] + FLAGS + list(extra or []) + SOURCES + ["-o", out + ".tmp"]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,6 +34,22 @@ def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if errs.strip() and verbose:
         print(errs, file=sys.stderr)
+
+
+def build(out: str = LIB, extra: list[str] | None = None, verbose: bool = False) -> str:
+    """Compile every source into ``out`` (always recompiles; one hipcc per source, in
+    parallel, then one link)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    objdir = os.path.join(os.path.dirname(out), "_build")
+    os.makedirs(objdir, exist_ok=True)
+    stem = os.path.basename(out)
+    objs = [os.path.join(objdir, f"{stem}.{os.path.basename(src)}.o") for src in SOURCES]
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    cmds = [[HIPCC] + compile_flags + list(extra or []) + ["-c", src, "-o", obj] for src, obj in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(len(cmds)) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", out + ".tmp"], verbose)
     os.replace(out + ".tmp", out)
     return out
 

@@ -7,7 +7,6 @@
 #include <initializer_list>
 #include <climits>
 #include <cstdint>
-#include <cstdlib>
 #include <cstring>
 
 #include "lattn.h"
@@ -18,6 +17,11 @@ namespace {
 constexpr int kMaxDevices = 64;
 // Per device: 0 = not checked yet, 1 = gfx950, -1 = other.
 std::atomic<int> g_device_ok[kMaxDevices];
+
+// Forced kernel choices (lattn_set_knob); LATTN_KNOB_AUTO = the choice from the shape.
+constexpr int kNumKnobs = 3;
+std::atomic<int> g_knob[kNumKnobs] = {LATTN_KNOB_AUTO, LATTN_KNOB_AUTO, LATTN_KNOB_AUTO};
+int knob(int which) { return g_knob[which].load(std::memory_order_relaxed); }
 
 bool aligned(const void* ptr, uintptr_t a) { return (reinterpret_cast<uintptr_t>(ptr) & (a - 1)) == 0; }
 
@@ -45,6 +49,11 @@ int check_problem(const lattn_problem& p, bool bf16_out_ok = false) {
     const bool bf16_out = bf16_out_ok && p.in_dtype == LATTN_BF16 && p.out_dtype == LATTN_BF16;
     if (p.out_dtype != LATTN_F32 && !bf16_out) return LATTN_ERR_UNSUPPORTED;
     if (!have_dims(p.in_dtype, p.head_dim_qk, p.head_dim_v)) return LATTN_ERR_UNSUPPORTED;
+    // The chunked kernels address the 64 token rows of a chunk with 32-bit signed byte
+    // offsets from the chunk's first row: the widest row (an fp32 row of o, q, dq or dk
+    // over all query heads) times 64 must stay below 2^31.
+    if ((int64_t)p.num_heads * std::max(p.head_dim_qk, p.head_dim_v) * 4 * lattn::kChunk > INT32_MAX)
+        return LATTN_ERR_UNSUPPORTED;
     return LATTN_OK;
 }
 
@@ -82,8 +91,7 @@ int check_bwd_problem(const lattn_problem& p) {
 int choose_nw(int in_dtype, int dk, int dv, int64_t heads) {
     const int units = dv / 16;
     auto usable = [&](int nw) { return units % nw == 0 && lattn::have_fwd_kernel(in_dtype, dk, nw); };
-    if (const char* env = std::getenv("LATTN_NW")) {
-        const int want = std::atoi(env);
+    if (const int want = knob(LATTN_KNOB_WAVES); want != LATTN_KNOB_AUTO) {
         if ((want == 1 || want == 2 || want == 4) && usable(want)) return want;
     }
     int narrowest = 0;
@@ -156,8 +164,8 @@ Split choose_split(const lattn_problem& p, int nw) {
     if ((int64_t)p.batch * p.num_heads > 65535) return sp;  // the scan's grid rows
     const int64_t wgs = (int64_t)p.batch * p.num_heads * (p.head_dim_v / (16 * nw));
     int want;
-    if (const char* env = std::getenv("LATTN_SPLIT")) {  // forced segment count (tests)
-        want = std::atoi(env);
+    if (const int forced = knob(LATTN_KNOB_SPLIT); forced != LATTN_KNOB_AUTO) {  // forced segment count
+        want = forced;
         if (want < 2) return sp;
     } else {
         if (wgs >= 128) return sp;  // at least half the compute units busy already
@@ -224,7 +232,15 @@ BwdLayout bwd_layout(const lattn_problem& p) {
 
 extern "C" {
 
-int lattn_abi_version(void) { return 4; }
+int lattn_abi_version(void) { return 5; }
+
+int lattn_set_knob(int which, int value, int* previous) {
+    if (which < 0 || which >= kNumKnobs) return LATTN_ERR_INVALID_ARG;
+    if (value != LATTN_KNOB_AUTO && value < 0) return LATTN_ERR_INVALID_ARG;
+    const int old = g_knob[which].exchange(value, std::memory_order_relaxed);
+    if (previous != nullptr) *previous = old;
+    return LATTN_OK;
+}
 
 const char* lattn_status_string(int status) {
     switch (status) {
@@ -433,10 +449,9 @@ int lattn_bwd(const lattn_problem* p, const void* q, const void* k, const void* 
     if (lattn::launch_fwd(pq, p->in_dtype, nw_q, rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
     // The dk and dv sweeps read the same Q and dO: with equal head dims (one kernel
     // shape) they run as one launch whose workgroups pair up per die, so the second
-    // read of a tile mostly hits L2.  LATTN_BWD_PAIR=0 keeps two launches.
-    const char* pair_env = std::getenv("LATTN_BWD_PAIR");
+    // read of a tile mostly hits L2.  Knob LATTN_KNOB_BWD_PAIR = 0 keeps two launches.
     const bool pair = p->in_dtype == LATTN_BF16 && !grouped && dkd == dvd && nw_k == nw_v &&
-                      !(pair_env && std::atoi(pair_env) == 0);
+                      knob(LATTN_KNOB_BWD_PAIR) != 0;
     if (pair) {
         if (lattn::launch_fwd_pair(pk, pv, nw_k, !rev, s) != hipSuccess) return LATTN_ERR_LAUNCH;
         return LATTN_OK;

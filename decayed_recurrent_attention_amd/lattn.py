@@ -12,6 +12,7 @@ lightning_attn and recurrent interface pages (without the GLA gates);
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import threading
@@ -35,7 +36,13 @@ LATTN_ERR_DEVICE = -7
 # Every function declared in include/lattn.h.
 EXPORTS = ("lattn_fwd", "lattn_fwd_workspace_size", "lattn_fwd_gated", "lattn_fwd_gated_workspace_size",
            "lattn_bwd", "lattn_bwd_workspace_size", "lattn_decode", "lattn_lightning_g_gamma",
-           "lattn_status_string", "lattn_abi_version")
+           "lattn_status_string", "lattn_set_knob", "lattn_abi_version")
+
+# Knobs of lattn_set_knob (forced kernel choices for tests and measurements).
+LATTN_KNOB_AUTO = -1
+LATTN_KNOB_WAVES = 0
+LATTN_KNOB_SPLIT = 1
+LATTN_KNOB_BWD_PAIR = 2
 
 
 class LattnProblem(ctypes.Structure):
@@ -86,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.lattn_lightning_g_gamma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
             lib.lattn_status_string.restype = ctypes.c_char_p
             lib.lattn_status_string.argtypes = [ctypes.c_int]
+            lib.lattn_set_knob.restype = ctypes.c_int
+            lib.lattn_set_knob.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
             lib.lattn_abi_version.restype = ctypes.c_int
             lib.lattn_abi_version.argtypes = []
             _lib = lib
@@ -99,6 +108,26 @@ def lattn_status_string(status: int) -> str:
 
 def lattn_abi_version() -> int:
     return int(load_library().lattn_abi_version())
+
+
+def lattn_set_knob(which: int, value: int) -> int:
+    """Force a kernel choice (LATTN_KNOB_AUTO restores the automatic one); returns the
+    knob's previous value."""
+    prev = ctypes.c_int(0)
+    rc = load_library().lattn_set_knob(int(which), int(value), ctypes.byref(prev))
+    if rc != LATTN_OK:
+        raise LattnError(rc)
+    return prev.value
+
+
+@contextlib.contextmanager
+def knob(which: int, value: int):
+    """Context manager: the knob holds `value` inside the block, its old value after."""
+    prev = lattn_set_knob(which, value)
+    try:
+        yield
+    finally:
+        lattn_set_knob(which, prev)
 
 
 def lattn_fwd_workspace_size(problem: LattnProblem) -> int:

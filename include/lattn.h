@@ -74,8 +74,8 @@ typedef struct {
  * (batch row, head) pairs to fill the GPU is split along the sequence (each row cut
  * into segments that run in parallel, chained through their states) and needs two
  * float32 states per segment: 2 * B * P * H * dk * dv * 4 bytes for P segments.
- * Otherwise 0.  The environment variable LATTN_SPLIT=N forces N segments (N < 2:
- * never split).  Returns 0 also for an invalid problem (lattn_fwd then reports it).
+ * Otherwise 0.  The knob LATTN_KNOB_SPLIT (lattn_set_knob) changes the segment count.
+ * Returns 0 also for an invalid problem (lattn_fwd then reports it).
  */
 size_t lattn_fwd_workspace_size(const lattn_problem* p);
 
@@ -99,7 +99,8 @@ size_t lattn_fwd_workspace_size(const lattn_problem* p);
  * Supported: in_dtype BF16 with dk in {32, 64, 128, 192, 256}; in_dtype F32 with
  * dk in {16, 32, 64, 128}; dv a multiple of 16 up to 256; out_dtype F32, or BF16
  * with in_dtype BF16 (o in the input dtype, half the output bytes; the state stays
- * float32).
+ * float32); num_heads * max(dk, dv) * 256 < 2^31 (the kernels address the 64 rows
+ * of a chunk with 32-bit byte offsets); else LATTN_ERR_UNSUPPORTED.
  * Returns LATTN_OK or a negative status; buffers are untouched on error.
  */
 int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* v,
@@ -129,8 +130,8 @@ size_t lattn_bwd_workspace_size(const lattn_problem* p);
  * "first"/"last" in the direction of the forward pass; dk and dv of a kv head sum
  * over its query heads.  Computed as three chunked sweeps: dq in the forward
  * direction, dk and dv in the opposite one (bf16 with dk = dv and no grouped heads:
- * the dk and dv sweeps share one launch; the environment variable LATTN_BWD_PAIR=0
- * keeps them apart).
+ * the dk and dv sweeps share one launch; the knob LATTN_KNOB_BWD_PAIR = 0 keeps them
+ * apart).
  *   q, k, v, g_gamma, scale, initial_state, reverse, cu_seqlens: as for lattn_fwd
  *                  (the forward inputs; initial_state may be NULL).  scale must be a
  *                  finite normal float (the sweeps carry D / scale).
@@ -217,7 +218,32 @@ int lattn_lightning_g_gamma(int num_heads, int layer_idx, int num_layers, float*
 /* Static description of a status code (never NULL). */
 const char* lattn_status_string(int status);
 
-/* ABI version of this header: 4 (1 had no backward, 2 no decoding step, 3 no gates). */
+/*
+ * Testing and measurement hook: force a kernel choice that the library otherwise
+ * makes from the problem's shape.  The setting is process-wide (every thread and
+ * device) and stays until changed; the results of every choice meet the same
+ * tolerance, only the summation order and the speed differ.  It exists so that
+ * tests can reach every kernel variant on small problems and so that the speed of
+ * one variant can be measured against another; production code leaves every knob at
+ * LATTN_KNOB_AUTO.  Set a knob only while no call that reads it is being made, and
+ * query workspace sizes after setting it (the split changes them).
+ *   which     one of the LATTN_KNOB_* values below
+ *   value     LATTN_KNOB_AUTO, or the forced value (>= 0) described there
+ *   previous  host int receiving the knob's previous value, or NULL
+ * Returns LATTN_OK, or LATTN_ERR_INVALID_ARG for an unknown knob or a negative value
+ * other than LATTN_KNOB_AUTO.  Forced values that the problem cannot use (a width
+ * that does not divide dv, say) fall back to the automatic choice.
+ */
+enum {
+    LATTN_KNOB_AUTO = -1,
+    LATTN_KNOB_WAVES = 0,    /* waves per value block of lattn_fwd / lattn_bwd: 1, 2 or 4 */
+    LATTN_KNOB_SPLIT = 1,    /* lattn_fwd: segments per sequence; 0 or 1 = never split */
+    LATTN_KNOB_BWD_PAIR = 2  /* lattn_bwd: 0 = the dk and dv sweeps as two launches */
+};
+int lattn_set_knob(int which, int value, int* previous);
+
+/* ABI version of this header: 5 (1 had no backward, 2 no decoding step, 3 no gates,
+   4 no knobs). */
 int lattn_abi_version(void);
 
 #ifdef __cplusplus

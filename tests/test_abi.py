@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lattn.lattn_abi_version() == 4
+    assert lattn.lattn_abi_version() == 5
     for code in range(-7, 1):
         s = lattn.lattn_status_string(code)
         assert s and s != "unknown status"
@@ -210,9 +210,8 @@ def test_decode_pointer_errors():
     assert call_decode(prob, s_in=FAKE + 8) == lattn.LATTN_ERR_INVALID_ARG
 
 
-def test_split_workspace(monkeypatch):
+def test_split_workspace():
     """Few (row, head) pairs of a long fixed-length bf16 input: split along the sequence."""
-    monkeypatch.delenv("LATTN_SPLIT", raising=False)
     prob = P(batch=1, seqlen=32768, num_heads=8, num_kv_heads=8, head_dim_qk=128, head_dim_v=128)
     # widest workgroups: 8 heads x 2 value blocks = 16 -> 16 segments of 2048 tokens
     assert lattn.lattn_fwd_workspace_size(prob) == 2 * 16 * 8 * 128 * 128 * 4
@@ -234,12 +233,55 @@ def test_split_workspace(monkeypatch):
         2 * 5 * 2 * 64 * 64 * 4
     assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=32768, num_heads=2, num_kv_heads=2,
                                             in_dtype=lattn.LATTN_F32)) == 0
-    monkeypatch.setenv("LATTN_SPLIT", "3")
     small = P(batch=2, seqlen=1000, num_heads=4, num_kv_heads=4)
-    # 16 chunks in 3 segments of 6 chunks (384 tokens)
-    assert lattn.lattn_fwd_workspace_size(small) == 2 * 2 * 3 * 4 * 64 * 64 * 4
-    monkeypatch.setenv("LATTN_SPLIT", "0")
-    assert lattn.lattn_fwd_workspace_size(prob) == 0
+    with lattn.knob(lattn.LATTN_KNOB_SPLIT, 3):
+        # 16 chunks in 3 segments of 6 chunks (384 tokens)
+        assert lattn.lattn_fwd_workspace_size(small) == 2 * 2 * 3 * 4 * 64 * 64 * 4
+    with lattn.knob(lattn.LATTN_KNOB_SPLIT, 0):
+        assert lattn.lattn_fwd_workspace_size(prob) == 0
+    assert lattn.lattn_fwd_workspace_size(prob) == 2 * 16 * 8 * 128 * 128 * 4  # restored
+
+
+def test_knobs():
+    """Knobs are set and restored explicitly; nothing is read from the environment."""
+    L = lattn.load_library()
+    prev = ctypes.c_int(7)
+    assert L.lattn_set_knob(lattn.LATTN_KNOB_WAVES, 2, ctypes.byref(prev)) == lattn.LATTN_OK
+    assert prev.value == lattn.LATTN_KNOB_AUTO
+    assert L.lattn_set_knob(lattn.LATTN_KNOB_WAVES, lattn.LATTN_KNOB_AUTO, ctypes.byref(prev)) == lattn.LATTN_OK
+    assert prev.value == 2
+    assert L.lattn_set_knob(3, 0, None) == lattn.LATTN_ERR_INVALID_ARG
+    assert L.lattn_set_knob(-1, 0, None) == lattn.LATTN_ERR_INVALID_ARG
+    assert L.lattn_set_knob(lattn.LATTN_KNOB_SPLIT, -5, None) == lattn.LATTN_ERR_INVALID_ARG
+    prob = P(batch=1, seqlen=32768, num_heads=8, num_kv_heads=8, head_dim_qk=128, head_dim_v=128)
+    before = lattn.lattn_fwd_workspace_size(prob)
+    os.environ["LATTN_SPLIT"] = "0"  # the old test variable has no effect
+    try:
+        assert lattn.lattn_fwd_workspace_size(prob) == before > 0
+    finally:
+        del os.environ["LATTN_SPLIT"]
+    with open(os.path.join(ROOT, "decayed_recurrent_attention_amd", "csrc", "lattn_api.cpp")) as f:
+        assert "getenv" not in f.read()
+
+
+@pytest.mark.parametrize("H,dk,dv,ok", [
+    (8192, 256, 256, True),        # 8192 * 256 * 4 * 64 = 2^29
+    (32768, 256, 256, False),      # 2^31: the chunk's row offsets no longer fit 32 bits
+    (65536, 128, 128, False),
+    (32767, 256, 256, True),
+    (32768, 256, 16, False),       # the wider of dk, dv decides
+    (32768, 16 * 2, 256, False),
+])
+def test_row_offset_limit(H, dk, dv, ok):
+    """lattn_fwd and lattn_bwd reject problems whose 64-row chunk byte offsets would
+    overflow 32 bits, before touching the device."""
+    prob = P(batch=1, seqlen=64, num_heads=H, num_kv_heads=H, head_dim_qk=dk, head_dim_v=dv)
+    if not ok:
+        assert call(prob) == lattn.LATTN_ERR_UNSUPPORTED
+        assert lattn.lattn_fwd_workspace_size(prob) == 0
+        assert call_bwd(prob) == lattn.LATTN_ERR_UNSUPPORTED
+    else:
+        assert call(prob, q=None) == lattn.LATTN_ERR_INVALID_ARG  # validation passes the shape
 
 
 def call_gated(prob, *, q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, gv=None, gg=None, o=FAKE, fs=FAKE,

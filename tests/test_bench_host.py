@@ -66,3 +66,25 @@ def test_more_than_one_gpu_refused():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_ms_stats():
+    st = bench.ms_stats([3.0, 1.0, 2.0, 10.0])
+    assert st == {"mean": 4.0, "median": 2.5, "min": 1.0, "max": 10.0, "calls": 4}
+    assert bench.ms_stats([2.0, 1.0, 5.0])["median"] == 2.0
+
+
+def test_roofline_pair_bound():
+    # the headline at 1.0 ms: 5.38 GB -> 5.38 TB/s (0.67 of HBM); 2.2 TFLOP -> 0.09 of bf16 MFMA
+    flops = bench.fwd_algorithmic_flops(B * T, H, D, D)
+    assert flops == 4 * B * T * H * D * D
+    bound, hbm, mfma = bench.roofline_pair(bench.algorithmic_bytes(B, T, H, H, D, D, 2), flops, 1.0)
+    assert bound == "hbm"
+    assert hbm["frac"] == pytest.approx(5_377_097_728 / 1e-3 / 1e9 / 8000.0)
+    assert mfma["frac"] == pytest.approx(flops / 1e-3 / 1e12 / 2500.0)
+    # a compute-heavy kernel names the matrix roofline
+    assert bench.roofline_pair(1e6, 1e13, 1.0)[0] == "mfma"
+
+
+def test_cpu_model_string():
+    assert isinstance(bench.cpu_model(), str) and bench.cpu_model()

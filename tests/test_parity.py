@@ -2,8 +2,10 @@
 
 Runs on an MI355X through the C ABI (via the Python binding).  Sizes are chosen so
 that the oracle finishes in seconds while spanning several 64-token chunks and a
-ragged tail; the full-size long-sequence case compares sampled (sequence, head)
-pairs in the same launch configuration that the benchmark times.
+ragged tail.  The long-sequence workload is compared whole at every N of its sweep,
+N = 32768 included, in the launch configuration that the benchmark times (the oracle
+runs one batch row at a time there).  Every comparison applies the bar to the whole
+tensor and to every (sequence, head) slice against its own RMS.
 """
 import os
 
@@ -11,7 +13,7 @@ import numpy as np
 import pytest
 
 from decayed_recurrent_attention_amd import inputs, lattn
-from tests.parity_util import TOL, check, gpu_run, oracle_run, to_device
+from tests.parity_util import TOL, Accum, check, check_fwd, gpu_run, oracle_run, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -27,10 +29,8 @@ def _gpu():
 def _compare(w, data, reverse=None, tag=""):
     o, fs = gpu_run(w, data, reverse)
     o_ref, fs_ref = oracle_run(w, data, reverse)
-    tol = TOL[w.dtype]
-    name = w.name + tag
-    check(o.cpu().numpy(), o_ref, tol, name + " o")
-    check(fs.cpu().numpy(), fs_ref, tol, name + " final_state")
+    check_fwd(o.cpu().numpy(), fs.cpu().numpy(), o_ref, fs_ref, TOL[w.dtype], w.name + tag,
+              cu=data["cu_seqlens"])
 
 
 # -- the five workloads ------------------------------------------------------------
@@ -50,7 +50,7 @@ def test_bf16_d64():
     _compare(w, w.make())
 
 
-@pytest.mark.parametrize("n", [512, 2048])
+@pytest.mark.parametrize("n", [512, 1024, 2048, 4096])
 def test_long_d128_full(n):
     w = inputs.long_d128(seqlen=n)
     _compare(w, w.make())
@@ -67,26 +67,29 @@ def test_varlen_gqa(reverse):
     _compare(w, w.make())
 
 
-def test_long_d128_n32768_sampled():
-    """Full-size long sequence (B=4, H=32, d=128, N=32768), sampled pairs."""
+@pytest.mark.parametrize("n", [8192, 16384, 32768])
+def test_long_d128_whole_tensor_rowwise(n):
+    """The long-sequence workload (B=4, H=32, d=128) at N = 8192, 16384 and 32768, run as
+    the benchmark runs it (one call over the whole batch); every output is compared with
+    the oracle, which runs one batch row at a time to bound host memory."""
     import torch
 
-    w = inputs.long_d128(seqlen=32768)
+    w = inputs.long_d128(seqlen=n)
     data = w.make()
     o, fs = gpu_run(w, data)
-    pairs = [(0, 0), (1, 1), (2, 5), (3, 17), (0, 31), (3, 0), (1, 30), (2, 16)]
-    o_ref, fs_ref = oracle_run(w, data, pairs=pairs)
-    idx_b = torch.tensor([b for b, _ in pairs], device=o.device)
-    idx_h = torch.tensor([h for _, h in pairs], device=o.device)
-    o_s = o[idx_b, :, idx_h, :].cpu().numpy()            # [pairs, T, dv]
-    fs_s = fs[idx_b, idx_h].cpu().numpy()                 # [pairs, dk, dv]
-    o_rs = np.stack([o_ref[b, :, h, :] for b, h in pairs])
-    fs_rs = np.stack([fs_ref[b, h] for b, h in pairs])
-    tol = TOL["bf16"]
-    check(o_s, o_rs, tol, "n32768 sampled o")
-    check(fs_s, fs_rs, tol, "n32768 sampled final_state")
-    # every output is finite
+    torch.cuda.synchronize()
     assert torch.isfinite(o).all().item() and torch.isfinite(fs).all().item()
+    orc = __import__("oracle").load()
+    g = orc.lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers)
+    acc_o, acc_s = Accum(f"{w.name} o"), Accum(f"{w.name} final_state")
+    for b in range(w.batch):
+        row = lambda a: np.ascontiguousarray(a[b:b + 1])
+        o_ref, fs_ref = orc.recurrent_fwd(row(data["q"]), row(data["k"]), row(data["v"]), g, w.scale)
+        acc_o.add_tokens(o[b:b + 1].cpu().numpy(), o_ref, row0=b)
+        acc_s.add_states(fs[b:b + 1].cpu().numpy(), fs_ref, n0=b)
+        del o_ref, fs_ref
+    acc_o.finish(TOL["bf16"])
+    acc_s.finish(TOL["bf16"])
 
 
 # -- edge cases ----------------------------------------------------------------------
@@ -123,27 +126,27 @@ def test_largest_head_dims(dk, dv, dtype):
 
 
 @pytest.mark.parametrize("nw", ["1", "2", "4"])
-def test_workgroup_widths(nw, monkeypatch):
-    monkeypatch.setenv("LATTN_NW", nw)
+def test_workgroup_widths(nw, knobs):
+    knobs(lattn.LATTN_KNOB_WAVES, int(nw))
     w = inputs.Workload(f"nw{nw}", 2, 333, 4, 4, 64, 64, "bf16", 1, 12, init_std=0.1, seed=6)
     _compare(w, w.make(), tag=f" nw={nw}")
 
 
 @pytest.mark.parametrize("dk,reverse", [(128, False), (128, True), (64, True)])
-def test_dk_split_small(dk, reverse, monkeypatch):
+def test_dk_split_small(dk, reverse, knobs):
     """Four column blocks force the eight-wave kernel (two waves per column block, each
     with half of the dk rows) on a small ragged GQA problem with an initial state."""
-    monkeypatch.setenv("LATTN_NW", "4")
+    knobs(lattn.LATTN_KNOB_WAVES, 4)
     w = inputs.Workload(f"dksplit{dk}", 2, 333, 4, 2, dk, 64, "bf16", 2, 12, reverse=reverse,
                         init_std=0.5, seed=31)
     _compare(w, w.make(), tag=" nw=4")
 
 
 @pytest.mark.parametrize("reverse", [False, True])
-def test_dk_split_ragged_packed(reverse, monkeypatch):
+def test_dk_split_ragged_packed(reverse, knobs):
     """The eight-wave kernel on packed sequences of 0, 1, 63, 64, 65, ... tokens (empty
     sequences, single tokens, partial chunks) with GQA and an initial state."""
-    monkeypatch.setenv("LATTN_NW", "4")
+    knobs(lattn.LATTN_KNOB_WAVES, 4)
     lens = [0, 1, 63, 64, 65, 127, 200, 2, 0, 129]
     w = inputs.Workload("dksplit_ragged", 1, sum(lens), 8, 2, 128, 64, "bf16", 3, 12,
                         reverse=reverse, seq_lens=lens, init_std=0.3, seed=33)
@@ -164,8 +167,7 @@ def test_explicit_g_gamma_strong_decay():
     g = np.array([-0.0, -3.0, -30.0, -200.0], dtype=np.float32)
     o, fs = gpu_run(w, data, g_gamma=torch.from_numpy(g).cuda())
     o_ref, fs_ref = oracle_run(w, data, g_gamma=g)
-    check(o.cpu().numpy(), o_ref, TOL["bf16"], "strong decay o")
-    check(fs.cpu().numpy(), fs_ref, TOL["bf16"], "strong decay final_state")
+    check_fwd(o.cpu().numpy(), fs.cpu().numpy(), o_ref, fs_ref, TOL["bf16"], "strong decay")
 
 
 def test_empty_sequence_batch():
@@ -190,8 +192,8 @@ def test_chained_segments_match_whole():
     o1, fs1 = lattn.lightning_attn(q[:, :m], k[:, :m], v[:, :m], 5, 12)
     o2, fs2 = lattn.lightning_attn(q[:, m:], k[:, m:], v[:, m:], 5, 12, initial_state=fs1)
     o_ref, fs_ref = oracle_run(w, data)
-    check(torch.cat([o1, o2], 1).cpu().numpy(), o_ref, TOL["bf16"], "chained o")
-    check(fs2.cpu().numpy(), fs_ref, TOL["bf16"], "chained final_state")
+    check_fwd(torch.cat([o1, o2], 1).cpu().numpy(), fs2.cpu().numpy(), o_ref, fs_ref, TOL["bf16"],
+              "chained")
     assert (o - torch.cat([o1, o2], 1)).abs().max().item() <= 1e-3 * o.abs().max().item()
 
 
@@ -220,22 +222,21 @@ def test_varlen_3d_input_matches_4d():
 
 # -- intra-sequence split (fixed-length bf16 input with few (row, head) pairs) -------------
 @pytest.mark.parametrize("reverse", [False, True])
-def test_split_forced_segments(reverse, monkeypatch):
-    monkeypatch.setenv("LATTN_SPLIT", "3")  # 16 chunks -> 3 segments of 6, 6 and 4 chunks
+def test_split_forced_segments(reverse, knobs):
+    knobs(lattn.LATTN_KNOB_SPLIT, 3)  # 16 chunks -> 3 segments of 6, 6 and 4 chunks
     w = inputs.Workload("split3", 2, 1000, 4, 4, 64, 64, "bf16", 3, 12, reverse=reverse,
                         init_std=0.5, seed=41)
     _compare(w, w.make(), tag=" rev" if reverse else "")
 
 
-def test_split_forced_gqa_unequal_dims(monkeypatch):
-    monkeypatch.setenv("LATTN_SPLIT", "5")
+def test_split_forced_gqa_unequal_dims(knobs):
+    knobs(lattn.LATTN_KNOB_SPLIT, 5)
     w = inputs.Workload("split5_gqa", 1, 777, 8, 2, 128, 64, "bf16", 6, 12, init_std=0.3, seed=43)
     _compare(w, w.make())
 
 
 @pytest.mark.parametrize("reverse", [False, True])
-def test_split_automatic_long_sequence(reverse, monkeypatch):
-    monkeypatch.delenv("LATTN_SPLIT", raising=False)
+def test_split_automatic_long_sequence(reverse, knobs):
     w = inputs.Workload("split_auto", 1, 16384, 4, 4, 128, 128, "bf16", 1, 12, reverse=reverse,
                         init_std=0.2, seed=42)
     prob = lattn.LattnProblem(1, 16384, 4, 4, 128, 128, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
@@ -243,13 +244,13 @@ def test_split_automatic_long_sequence(reverse, monkeypatch):
     _compare(w, w.make(), tag=" rev" if reverse else "")
 
 
-def test_split_matches_unsplit(monkeypatch):
+def test_split_matches_unsplit(knobs):
     """Split and unsplit runs agree to rounding (different summation order)."""
     w = inputs.Workload("split_vs", 2, 3000, 2, 2, 128, 128, "bf16", 2, 12, init_std=0.5, seed=44)
     data = w.make()
-    monkeypatch.setenv("LATTN_SPLIT", "0")
+    knobs(lattn.LATTN_KNOB_SPLIT, 0)
     o0, f0 = gpu_run(w, data)
-    monkeypatch.setenv("LATTN_SPLIT", "4")
+    knobs(lattn.LATTN_KNOB_SPLIT, 4)
     o1, f1 = gpu_run(w, data)
     scale_o = float(o0.abs().max())
     assert float((o0 - o1).abs().max()) <= 1e-4 * scale_o

@@ -1,19 +1,22 @@
 """GPU parity of the backward pass: the HIP gradients against the fp64 oracle.
 
 Each case compares dq, dk, dv and d_initial_state element by element with the
-stated tolerance (max |gpu - oracle| <= tol * RMS(oracle), per tensor): 1e-4 for
-fp32 inputs, 2e-2 for bf16 inputs.  Sizes span several 64-token chunks and a ragged
-tail; the full-size long-sequence case compares sampled (batch row, head) pairs.
+stated tolerance (max |gpu - oracle| <= tol * RMS(oracle)): 1e-4 for fp32 inputs,
+2e-2 for bf16 inputs, over each whole tensor and over each (sequence, head) slice of
+it against the slice's own RMS.  Sizes span several 64-token chunks and a ragged tail;
+the full-size long-sequence case compares every gradient, with the oracle run one
+batch row at a time.
 """
 import numpy as np
 import pytest
 
 from decayed_recurrent_attention_amd import inputs, lattn
-from tests.parity_util import TOL, check, gpu_run_bwd, oracle_run_bwd
+from tests.parity_util import TOL, Accum, check, gpu_run_bwd, oracle_run_bwd
 
 pytestmark = pytest.mark.gpu
 
 NAMES = ("dq", "dk", "dv", "d_initial_state")
+KINDS = ("tokens", "tokens", "tokens", "states")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -35,8 +38,8 @@ def _compare(w, data=None, grads=None, reverse=None, g_gamma=None, tag=""):
     got = gpu_run_bwd(w, data, grads, reverse, g_gamma=g_dev)
     ref = oracle_run_bwd(w, data, grads, reverse, g_gamma=g_gamma)
     tol = TOL[w.dtype]
-    for name, a, b in zip(NAMES, got, ref):
-        check(a.cpu().numpy(), b, tol, f"{w.name}{tag} {name}")
+    for name, kind, a, b in zip(NAMES, KINDS, got, ref):
+        check(a.cpu().numpy(), b, tol, f"{w.name}{tag} {name}", kind, data["cu_seqlens"])
 
 
 def test_bwd_tiny_fp32_both_directions():
@@ -60,10 +63,10 @@ def test_bwd_long_d128(n):
 
 
 @pytest.mark.parametrize("dk", [64, 128])
-def test_bwd_dk_split(dk, monkeypatch):
+def test_bwd_dk_split(dk, knobs):
     """Four column blocks force the eight-wave sweeps (the dq sweep and the paired dk and
     dv sweeps) on a small problem, both directions, with an initial state."""
-    monkeypatch.setenv("LATTN_NW", "4")
+    knobs(lattn.LATTN_KNOB_WAVES, 4)
     w = inputs.Workload(f"bwd_dksplit{dk}", 2, 300, 4, 4, dk, dk, "bf16", 2, 12, init_std=0.4,
                         seed=32)
     data = w.make()
@@ -71,9 +74,9 @@ def test_bwd_dk_split(dk, monkeypatch):
     _compare(w, data, reverse=True, tag=" nw=4 rev")
 
 
-def test_bwd_dk_split_ragged_packed(monkeypatch):
+def test_bwd_dk_split_ragged_packed(knobs):
     """The eight-wave sweeps on packed sequences with empty ones and partial chunks."""
-    monkeypatch.setenv("LATTN_NW", "4")
+    knobs(lattn.LATTN_KNOB_WAVES, 4)
     lens = [0, 1, 63, 64, 65, 130, 0, 7]
     w = inputs.Workload("bwd_dksplit_ragged", 1, sum(lens), 4, 4, 128, 64, "bf16", 3, 12,
                         seq_lens=lens, init_std=0.3, seed=34)
@@ -123,29 +126,33 @@ def test_bwd_without_state_gradients():
     assert d_init is None
     ref = oracle_run_bwd(w, data, grads)
     for name, a, b in zip(NAMES[:3], (dq, dk, dv), ref[:3]):
-        check(a.cpu().numpy(), b, TOL["bf16"], f"bwd_plain {name}")
+        check(a.cpu().numpy(), b, TOL["bf16"], f"bwd_plain {name}", "tokens")
 
 
-def test_bwd_long_d128_n32768_sampled():
-    """Full-size long sequence (B=4, H=32, d=128, N=32768), sampled (batch row, head) pairs
-    computed one by one by the oracle on slices of the inputs."""
+def test_bwd_long_d128_n32768_whole():
+    """Full-size long sequence (B=4, H=32, d=128, N=32768), every gradient compared with the
+    oracle, which runs one batch row at a time to bound host memory."""
+    import oracle
+
     w = inputs.long_d128(seqlen=32768)
     data = w.make()
     grads = w.make_grads()
-    dq, dk, dv, d_init = (t.cpu().numpy() for t in gpu_run_bwd(w, data, grads))
-    import oracle
-
+    got = gpu_run_bwd(w, data, grads)
     orc = oracle.load()
     g = orc.lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers)
-    pairs = [(0, 0), (1, 5), (2, 17), (3, 31)]
-    for b, h in pairs:
-        sl = lambda a: np.ascontiguousarray(a[b:b + 1, :, h:h + 1])
-        ref = orc.recurrent_bwd(sl(data["q"]), sl(data["k"]), sl(data["v"]), g[h:h + 1], w.scale,
-                                sl(grads["d_o"]), np.ascontiguousarray(grads["d_final_state"][b:b + 1, h:h + 1]))
-        got = (dq[b:b + 1, :, h:h + 1], dk[b:b + 1, :, h:h + 1], dv[b:b + 1, :, h:h + 1],
-               d_init[b:b + 1, h:h + 1])
-        for name, x, y in zip(NAMES, got, ref):
-            check(x, y, TOL["bf16"], f"n32768 pair ({b}, {h}) {name}")
+    accs = [Accum(f"n32768 {name}") for name in NAMES]
+    for b in range(w.batch):
+        row = lambda a: np.ascontiguousarray(a[b:b + 1])
+        ref = orc.recurrent_bwd(row(data["q"]), row(data["k"]), row(data["v"]), g, w.scale, row(grads["d_o"]),
+                                row(grads["d_final_state"]))
+        for acc, kind, x, y in zip(accs, KINDS, got, ref):
+            if kind == "tokens":
+                acc.add_tokens(x[b:b + 1].cpu().numpy(), y, row0=b)
+            else:
+                acc.add_states(x[b:b + 1].cpu().numpy(), y, n0=b)
+        del ref
+    for acc in accs:
+        acc.finish(TOL["bf16"])
 
 
 def test_bwd_deterministic():
@@ -160,19 +167,19 @@ def test_bwd_deterministic():
 
 
 @pytest.mark.parametrize("reverse", [False, True])
-def test_bwd_paired_sweeps_equal_separate(reverse, monkeypatch):
+def test_bwd_paired_sweeps_equal_separate(reverse, knobs):
     """bf16 with dk = dv and no grouped heads runs the dk and dv sweeps as one launch;
     every workgroup does the same arithmetic either way, so the gradients are
-    bit-identical to two launches (LATTN_BWD_PAIR=0), and both meet the oracle."""
+    bit-identical to two launches (knob LATTN_KNOB_BWD_PAIR = 0), and both meet the oracle."""
     import torch
 
     w = inputs.Workload("bwd_pair", 2, 700, 4, 4, 64, 64, "bf16", 2, 12, reverse=reverse, init_std=0.3, seed=27)
     data, grads = w.make(), w.make_grads()
     a = gpu_run_bwd(w, data, grads)
-    monkeypatch.setenv("LATTN_BWD_PAIR", "0")
+    knobs(lattn.LATTN_KNOB_BWD_PAIR, 0)
     b = gpu_run_bwd(w, data, grads)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
     ref = oracle_run_bwd(w, data, grads)
-    for got, exp, name in zip(a, ref, ("dq", "dk", "dv", "d_initial_state")):
-        check(got.cpu().numpy(), exp, TOL["bf16"], f"bwd_pair{' rev' if reverse else ''} {name}")
+    for got, exp, name, kind in zip(a, ref, NAMES, KINDS):
+        check(got.cpu().numpy(), exp, TOL["bf16"], f"bwd_pair{' rev' if reverse else ''} {name}", kind)
