@@ -5,10 +5,20 @@ Workload: B=4, H=Hkv=32, dk=dv=128, N=32768 tokens per row, bf16 q/k/v, fp32 o a
 final state, decay schedule of layer 0 of 12, no initial state, forward direction.
 A step is one lattn_fwd call over the whole batch with inputs already in HBM.
 
+Order: host-side inputs (numpy) first, then the secondary GPU legs back to back, then
+the headline (exactly --warmup untimed and --steps timed calls), then the CPU oracle
+baselines.  Timing the headline after seconds of GPU work keeps it clear of the clock
+ramp that the first calls after an idle period show.  Every leg reports the mean,
+median, minimum and maximum of its per-call HIP-event times.
+
 Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
   roofline      achieved HBM GB/s of the forward kernel (algorithmic bytes / mean
-                kernel time from HIP events on the launch stream) against 8 TB/s,
-  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload,
+                kernel time from HIP events on the launch stream) against 8 TB/s, the
+                same against the dense bf16 MFMA peak on the recurrence's flops, and
+                `bound` = the roofline with the larger fraction,
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload
+                (with the CPU model and thread count); the sweep entries carry one
+                oracle run each over the whole workload at their N,
   backward      the same for lattn_bwd on the same inputs (bf16 d_o), with its own
                 roofline and oracle baseline (skipped with --no-bwd),
   decode        one decoding step (lattn_decode) over --decode-batch sequences of the
@@ -151,11 +161,17 @@ def device_bandwidth(torch, dev, gib=2, reps=5):
     return f"device copy {gib} GiB: {res['copy']:.0f} GB/s (read + write), fill: {res['fill']:.0f} GB/s"
 
 
-def time_calls(torch, fn, stream, warmup, steps):
-    """Run fn warmup times, then time `steps` calls; returns (wall ms per call, event ms list).
+def time_calls(torch, fn, stream, warmup, steps, settle_s=0.0):
+    """Run fn warmup times (and, with settle_s > 0, on until that many seconds of calls
+    have passed), then time `steps` calls; returns (wall ms per call, event ms list).
     The events bracket each call on the launch stream."""
-    for _ in range(warmup):
+    t_end = time.perf_counter() + settle_s
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         fn()
+        n += 1
+        if n % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -168,6 +184,47 @@ def time_calls(torch, fn, stream, warmup, steps):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return 1000.0 * wall / steps, [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def ms_stats(ms):
+    """Mean, median, minimum and maximum of per-call event times (ms)."""
+    srt = sorted(ms)
+    mid = len(srt) // 2
+    med = srt[mid] if len(srt) % 2 else 0.5 * (srt[mid - 1] + srt[mid])
+    return {"mean": sum(ms) / len(ms), "median": med, "min": srt[0], "max": srt[-1], "calls": len(ms)}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (or platform's guess)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+
+    return platform.processor() or "unknown"
+
+
+def roofline_pair(alg_bytes, alg_flops, kernel_ms, flop_peak_tfs=None):
+    """HBM and MFMA roofline figures for one kernel; `bound` names the larger fraction."""
+    flop_peak_tfs = BF16_MFMA_PEAK_TFS if flop_peak_tfs is None else flop_peak_tfs
+    gbs = alg_bytes / (kernel_ms * 1e-3) / 1e9
+    tfs = alg_flops / (kernel_ms * 1e-3) / 1e12
+    hbm = {"achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+           "algorithmic_bytes": alg_bytes}
+    mfma = {"achieved": tfs, "peak": flop_peak_tfs, "unit": "TFLOP/s", "frac": tfs / flop_peak_tfs,
+            "algorithmic_flops": alg_flops}
+    bound = "hbm" if hbm["frac"] >= mfma["frac"] else "mfma"
+    return bound, hbm, mfma
+
+
+def fwd_algorithmic_flops(tokens, H, dk, dv):
+    """The recurrence's flops: a rank-1 state update (2 dk dv) and the readout q S (2 dk dv)
+    per query head and token."""
+    return 4 * tokens * H * dk * dv
 
 
 def bwd_algorithmic_bytes(B, T, H, Hkv, dk, dv, in_bytes):
@@ -257,6 +314,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=50,
                     help="untimed steps first: the clocks take some 20-50 forward calls to settle")
     ap.add_argument("--seqlen", type=int, default=32768)
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed calls before each secondary leg (besides --warmup)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward measurement")
     ap.add_argument("--no-gated", action="store_true",
@@ -286,10 +345,16 @@ def main():
 
     from decayed_recurrent_attention_amd import inputs, lattn
 
+    def log(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    # -- host-side inputs first (numpy), so that the GPU legs below run back to back --------
     w = inputs.long_d128(seqlen=args.seqlen)
     B, T, H, Hkv, dk, dv = w.batch, w.seqlen, w.num_heads, w.num_kv_heads, w.dk, w.dv
-    print(f"[bench] generating {w.name}", file=sys.stderr, flush=True)
+    log(f"generating {w.name}")
     data = w.make()
+    grads = None if args.no_bwd else w.make_grads(final_std=None)
+    gates = None if args.no_gated else w.make_gates(("g",), 0.1)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     to_dev = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
@@ -299,6 +364,7 @@ def main():
     fs = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
     prob = lattn.LattnProblem(B, T, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
     stream = torch.cuda.current_stream(dev)
+    settle = args.settle
 
     def step():
         rc = lattn.lattn_fwd(prob, q, k, v, g, w.scale, None, False, None, o, fs,
@@ -306,18 +372,12 @@ def main():
         if rc != lattn.LATTN_OK:
             raise lattn.LattnError(rc)
 
-    print("[bench] forward", file=sys.stderr, flush=True)
-    ms_per_step, kernel_ms = time_calls(torch, step, stream, args.warmup, args.steps)
-    mean_kernel_ms = sum(kernel_ms) / len(kernel_ms)
-    print(f"[bench] {args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel mean "
-          f"{mean_kernel_ms:.4f} ms min {min(kernel_ms):.4f} max {max(kernel_ms):.4f}",
-          file=sys.stderr, flush=True)
-
+    # -- secondary GPU legs; the headline is timed after them, at settled clocks -------------
     bf16_out = None
     if not args.no_bf16_out:
         # The same forward with o in bf16 (each element the round-to-nearest-even of the
         # fp32 result): 20 % fewer bytes per call.
-        print("[bench] forward with a bf16 o", file=sys.stderr, flush=True)
+        log("forward with a bf16 o")
         ob = torch.empty((B, T, H, dv), device=dev, dtype=torch.bfloat16)
         prob_b = lattn.LattnProblem(B, T, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_BF16)
 
@@ -327,69 +387,155 @@ def main():
             if rc != lattn.LATTN_OK:
                 raise lattn.LattnError(rc)
 
-        b_wall, b_ms = time_calls(torch, step_b, stream, args.warmup, args.steps)
-        b_mean = sum(b_ms) / len(b_ms)
+        b_wall, b_ms = time_calls(torch, step_b, stream, args.warmup, args.steps, settle)
+        st = ms_stats(b_ms)
         b_alg = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2, o_bytes=2)
-        b_gbs = b_alg / (b_mean * 1e-3) / 1e9
-        bf16_out = {"ms_per_step": b_wall, "tokens_per_s": B * T / (b_wall * 1e-3),
+        b_gbs = b_alg / (st["mean"] * 1e-3) / 1e9
+        bf16_out = {"ms_per_step": b_wall, "tokens_per_s": B * T / (b_wall * 1e-3), "kernel_ms": st,
                     "roofline": {"bound": "hbm", "achieved": b_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": b_gbs / HBM_PEAK_GBS, "algorithmic_bytes": b_alg,
-                                 "call_ms": b_mean},
+                                 "call_ms": st["mean"]},
                     "inputs": "the forward's; o bf16 (round to nearest even of the fp32 result), "
                               "fp32 final state"}
-        print(f"[bench] bf16 o {args.steps} steps: {b_wall:.4f} ms/step wall, mean {b_mean:.4f} ms, "
-              f"{b_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        log(f"bf16 o {args.steps} steps: {b_wall:.4f} ms/step wall, mean {st['mean']:.4f} ms, "
+            f"median {st['median']:.4f} ms, {b_gbs:.0f} GB/s")
         del ob
 
-    sweep = None
-    if not args.no_sweep:
-        # The forward at smaller N on device-drawn inputs of the same shape.  Below 1 GB per
-        # call, calls rotate over enough buffer sets (about 1 GB in all) that the working
-        # set cannot stay in the 256 MB Infinity Cache.
-        print("[bench] sweep over N", file=sys.stderr, flush=True)
-        sweep = []
-        for n in SWEEP_N:
-            nbytes = algorithmic_bytes(B, n, H, Hkv, dk, dv, 2)
-            nsets = max(1, min(16, -(-(1 << 30) // nbytes)))
-            sets = []
-            for _ in range(nsets):
-                qs = torch.randn((B, n, H, dk), device=dev, dtype=torch.bfloat16)
-                ks = torch.randn((B, n, Hkv, dk), device=dev, dtype=torch.bfloat16)
-                vs = torch.randn((B, n, Hkv, dv), device=dev, dtype=torch.bfloat16)
-                os_ = torch.empty((B, n, H, dv), device=dev, dtype=torch.float32)
-                fss = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
-                sets.append((qs, ks, vs, os_, fss))
-            sprob = lattn.LattnProblem(B, n, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
-            it = [0]
+    bwd = None
+    if not args.no_bwd:
+        d_o = to_dev(grads["d_o"])
+        dq = torch.empty((B, T, H, dk), device=dev, dtype=torch.float32)
+        dkk = torch.empty((B, T, Hkv, dk), device=dev, dtype=torch.float32)
+        dvv = torch.empty((B, T, Hkv, dv), device=dev, dtype=torch.float32)
+        dinit = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+        ws_bytes = lattn.lattn_bwd_workspace_size(prob)
+        ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
 
-            def sweep_step():
-                qs, ks, vs, os_, fss = sets[it[0] % nsets]
-                it[0] += 1
-                rc = lattn.lattn_fwd(sprob, qs, ks, vs, g, w.scale, None, False, None, os_, fss,
-                                     stream=stream.cuda_stream)
-                if rc != lattn.LATTN_OK:
-                    raise lattn.LattnError(rc)
+        def bstep():
+            rc = lattn.lattn_bwd(prob, q, k, v, g, w.scale, None, False, None, d_o, None, dq, dkk, dvv,
+                                 dinit, ws, stream=stream.cuda_stream)
+            if rc != lattn.LATTN_OK:
+                raise lattn.LattnError(rc)
 
-            n_wall, n_ms = time_calls(torch, sweep_step, stream, args.warmup, args.steps)
-            n_mean = sum(n_ms) / len(n_ms)
-            gbs = nbytes / (n_mean * 1e-3) / 1e9
-            sweep.append({"seq_len": n, "ms_per_step": n_wall, "kernel_ms": n_mean,
-                          "tokens_per_s": B * n / (n_wall * 1e-3), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
-                          "buffer_sets": nsets, "page_lightning2_ms": PAGE_LIGHTNING2_SWEEP_MS[n]})
-            print(f"[bench] sweep N={n}: {n_wall:.4f} ms/step wall, kernel mean {n_mean:.4f} ms, "
-                  f"{gbs:.0f} GB/s ({nsets} buffer sets)", file=sys.stderr, flush=True)
-            del sets
-        full_gbs = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2) / (mean_kernel_ms * 1e-3) / 1e9
-        sweep.append({"seq_len": T, "ms_per_step": ms_per_step, "kernel_ms": mean_kernel_ms,
-                      "tokens_per_s": B * T / (ms_per_step * 1e-3), "hbm_gbs": full_gbs,
-                      "hbm_frac": full_gbs / HBM_PEAK_GBS, "buffer_sets": 1,
-                      "page_lightning2_ms": PAGE_LIGHTNING2_SWEEP_MS.get(T)})
+        log("backward")
+        b_wall, b_ms = time_calls(torch, bstep, stream, args.warmup, args.steps, settle)
+        st = ms_stats(b_ms)
+        b_alg = bwd_algorithmic_bytes(B, T, H, Hkv, dk, dv, 2)
+        bound, hbm, mfma = roofline_pair(b_alg, 2 * fwd_algorithmic_flops(B * T, H, dk, dv) + 2 * B * T * H * dk * dv,
+                                         st["mean"])
+        log(f"backward {args.steps} steps: {b_wall:.4f} ms/step wall, mean {st['mean']:.4f} ms, "
+            f"median {st['median']:.4f} ms")
+        bwd = {"ms_per_step": b_wall, "tokens_per_s": B * T / (b_wall * 1e-3), "kernel_ms": st,
+               "roofline": dict(bound=bound, **hbm, call_ms=st["mean"]), "mfma": mfma,
+               "inputs": "q, k, v, d_o bf16; no initial state, no final-state gradient; "
+                         "d_initial_state computed",
+               "page_lightning2_bwd_ms": PAGE_LIGHTNING2_BWD_MS if T == 32768 else None}
+        del dq, dkk, dvv, d_o
+
+    gated = None
+    if not args.no_gated:
+        gdev = to_dev(gates["g"])
+        go = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
+        gfs = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+
+        def gstep():
+            rc = lattn.lattn_fwd_gated(prob, q, k, v, gdev, None, None, None, w.scale, None, False, None, go,
+                                       gfs, stream=stream.cuda_stream)
+            if rc != lattn.LATTN_OK:
+                raise lattn.LattnError(rc)
+
+        log("gated forward")
+        g_wall, g_ms = time_calls(torch, gstep, stream, args.warmup, args.steps, settle)
+        st = ms_stats(g_ms)
+        g_bytes = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2) + B * T * H * dk * 2
+        # the recurrence: decay (1), rank-1 update (2) and readout (2) flops per state element per token
+        g_flops = 5 * B * T * H * dk * dv
+        log(f"gated {args.steps} steps: {g_wall:.4f} ms/step wall, mean {st['mean']:.4f} ms, "
+            f"median {st['median']:.4f} ms")
+        # bf16 inputs run on bf16 MFMA (hi/lo operand splits): at bf16 rates the
+        # algorithm's bytes bind (6.45 GB at 8 TB/s vs 0.34 TFLOP at 2.5 PFLOP/s)
+        bound, hbm, mfma = roofline_pair(g_bytes, g_flops, st["mean"])
+        gated = {"workload": f"GLA gate g ~ U[-0.1, 0) per key channel, B{B} H{H} d{dk} N{T} bf16, "
+                             "bf16 MFMA with hi/lo splits, fp32 accumulation",
+                 "ms_per_step": g_wall, "tokens_per_s": B * T / (g_wall * 1e-3), "kernel_ms": st,
+                 "roofline": dict(bound=bound, **hbm, call_ms=st["mean"]), "mfma": mfma}
+        del gdev, go, gfs
+
+    split = None
+    if not args.no_split:
+        # One batch row and 8 heads: 32 workgroups unsplit, so the forward cuts each row
+        # into segments chained through their states.
+        Hs = 8
+        ws_ = inputs.Workload("split", 1, T, Hs, Hs, dk, dv, "bf16", w.layer_idx, w.num_layers, seed=5)
+        sd = ws_.make()
+        sq, sk, sv = (to_dev(sd[n]) for n in ("q", "k", "v"))
+        gs = torch.from_numpy(lattn.lattn_lightning_g_gamma(Hs, w.layer_idx, w.num_layers)).to(dev)
+        so = torch.empty((1, T, Hs, dv), device=dev, dtype=torch.float32)
+        sfs = torch.empty((1, Hs, dk, dv), device=dev, dtype=torch.float32)
+        sprob = lattn.LattnProblem(1, T, Hs, Hs, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
+        res = {}
+        for mode in ("split", "unsplit"):
+            with lattn.knob(lattn.LATTN_KNOB_SPLIT, 0 if mode == "unsplit" else lattn.LATTN_KNOB_AUTO):
+                nbytes = lattn.lattn_fwd_workspace_size(sprob)
+                sws = torch.empty(nbytes, device=dev, dtype=torch.uint8) if nbytes else None
+
+                def sstep():
+                    rc = lattn.lattn_fwd(sprob, sq, sk, sv, gs, ws_.scale, None, False, None, so, sfs, sws,
+                                         stream=stream.cuda_stream)
+                    if rc != lattn.LATTN_OK:
+                        raise lattn.LattnError(rc)
+
+                wall_ms, ev_ms = time_calls(torch, sstep, stream, args.warmup, args.steps, settle)
+            res[mode] = (wall_ms, ms_stats(ev_ms), nbytes)
+        s_alg = algorithmic_bytes(1, T, Hs, Hs, dk, dv, 2)
+        s_mean = res["split"][1]["mean"]
+        s_ach = s_alg / (s_mean * 1e-3) / 1e9
+        log(f"split B1 H{Hs}: {s_mean:.4f} ms split, {res['unsplit'][1]['mean']:.4f} ms unsplit")
+        split = {"workload": f"B1 H{Hs} d{dk} N{T} bf16, no initial state",
+                 "ms_per_step": res["split"][0], "tokens_per_s": T / (res["split"][0] * 1e-3),
+                 "kernel_ms": res["split"][1],
+                 "unsplit_ms_per_step": res["unsplit"][0], "unsplit_kernel_ms": res["unsplit"][1],
+                 "speedup": res["unsplit"][1]["mean"] / s_mean,
+                 "workspace_bytes": res["split"][2],
+                 "roofline": {"bound": "hbm", "achieved": s_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": s_ach / HBM_PEAK_GBS, "algorithmic_bytes": s_alg, "call_ms": s_mean}}
+        del sq, sk, sv, so
+
+    dec = None
+    if args.decode_batch > 0:
+        Bd = args.decode_batch
+        wd = inputs.Workload("decode", Bd, 1, H, Hkv, dk, dv, "bf16", w.layer_idx, w.num_layers,
+                             init_std=0.5, seed=3)
+        dd = wd.make()
+        dq_, dk_, dv_ = (to_dev(dd[n])[:, 0].contiguous() for n in ("q", "k", "v"))
+        state = torch.from_numpy(dd["initial_state"]).to(dev)
+        o_dec = torch.empty((Bd, H, dv), device=dev, dtype=torch.float32)
+        dprob = lattn.LattnProblem(Bd, 1, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
+
+        def dstep():
+            rc = lattn.lattn_decode(dprob, dq_, dk_, dv_, g, w.scale, state, state, o_dec,
+                                    stream=stream.cuda_stream)
+            if rc != lattn.LATTN_OK:
+                raise lattn.LattnError(rc)
+
+        log("decode")
+        d_wall, d_ms = time_calls(torch, dstep, stream, args.warmup, args.steps, settle)
+        st = ms_stats(d_ms)
+        d_alg = 2 * Bd * H * dk * dv * 4 + Bd * (H * dk + Hkv * dk + Hkv * dv) * 2 + Bd * H * dv * 4
+        d_ach = d_alg / (st["mean"] * 1e-3) / 1e9
+        log(f"decode {args.steps} steps: {d_wall:.4f} ms/step wall, mean {st['mean']:.4f} ms")
+        dec = {"batch": Bd, "ms_per_step": d_wall, "tokens_per_s": Bd / (d_wall * 1e-3), "kernel_ms": st,
+               "roofline": {"bound": "hbm", "achieved": d_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                            "frac": d_ach / HBM_PEAK_GBS, "algorithmic_bytes": d_alg, "call_ms": st["mean"]},
+               "inputs": f"{Bd} sequences x H{H} d{dk}: q, k, v bf16, fp32 state updated in place"}
+        del o_dec
 
     configs = None
     if not args.no_configs:
         # The other workloads of the parity suite, forward only, same timing: ms per call
-        # (HIP events), tokens/s and the HBM fraction on each one's algorithmic bytes.
-        print("[bench] other workloads", file=sys.stderr, flush=True)
+        # (HIP events over every kernel of the call), tokens/s and the HBM fraction on each
+        # one's algorithmic bytes.
+        log("other workloads")
         configs = []
         for cw in (inputs.tiny_fp32(), inputs.bf16_d64(), inputs.d192(), inputs.varlen_gqa(False),
                    inputs.varlen_gqa(True)):
@@ -415,162 +561,61 @@ def main():
                 if rc != lattn.LATTN_OK:
                     raise lattn.LattnError(rc)
 
-            c_wall, c_ms = time_calls(torch, cstep, stream, args.warmup, args.steps)
-            c_mean = sum(c_ms) / len(c_ms)
+            c_wall, c_ms = time_calls(torch, cstep, stream, args.warmup, args.steps, settle)
+            st = ms_stats(c_ms)
             ntok = cw.batch * cw.seqlen
             c_alg = (ntok * (cw.num_heads * cw.dk + cw.num_kv_heads * (cw.dk + cw.dv)) * (4 if f32in else 2)
                      + ntok * cw.num_heads * cw.dv * 4
                      + nseq * cw.num_heads * cw.dk * cw.dv * 4 * (2 if cinit is not None else 1))
-            c_gbs = c_alg / (c_mean * 1e-3) / 1e9
+            c_gbs = c_alg / (st["mean"] * 1e-3) / 1e9
             configs.append({"workload": cw.name, "batch": cw.batch, "tokens": ntok, "num_seqs": nseq,
                             "num_heads": cw.num_heads, "num_kv_heads": cw.num_kv_heads, "head_dim_qk": cw.dk,
                             "head_dim_v": cw.dv, "dtype": cw.dtype, "reverse": bool(cw.reverse),
-                            "initial_state": cinit is not None, "ms_per_step": c_wall, "kernel_ms": c_mean,
+                            "initial_state": cinit is not None, "ms_per_step": c_wall, "kernel_ms": st,
                             "tokens_per_s": ntok / (c_wall * 1e-3), "algorithmic_bytes": c_alg,
                             "hbm_gbs": c_gbs, "hbm_frac": c_gbs / HBM_PEAK_GBS})
-            print(f"[bench] {cw.name}: {c_wall:.4f} ms/step wall, kernel mean {c_mean:.4f} ms, "
-                  f"{c_gbs:.0f} GB/s", file=sys.stderr, flush=True)
+            log(f"{cw.name}: {c_wall:.4f} ms/step wall, mean {st['mean']:.4f} ms, median {st['median']:.4f} ms, "
+                f"{c_gbs:.0f} GB/s")
             del cq, ck, cv, co, cfs, cws
 
-    bwd = None
-    if not args.no_bwd:
-        grads = w.make_grads(final_std=None)
-        d_o = to_dev(grads["d_o"])
-        dq = torch.empty((B, T, H, dk), device=dev, dtype=torch.float32)
-        dkk = torch.empty((B, T, Hkv, dk), device=dev, dtype=torch.float32)
-        dvv = torch.empty((B, T, Hkv, dv), device=dev, dtype=torch.float32)
-        dinit = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
-        ws_bytes = lattn.lattn_bwd_workspace_size(prob)
-        ws = torch.empty(ws_bytes, device=dev, dtype=torch.uint8) if ws_bytes else None
+    sweep = None
+    if not args.no_sweep:
+        # The forward at smaller N on device-drawn inputs of the same shape.  Below 1 GB per
+        # call, calls rotate over enough buffer sets (about 1 GB in all) that the working
+        # set cannot stay in the 256 MB Infinity Cache.
+        log("sweep over N")
+        sweep = []
+        for n in SWEEP_N:
+            nbytes = algorithmic_bytes(B, n, H, Hkv, dk, dv, 2)
+            nsets = max(1, min(16, -(-(1 << 30) // nbytes)))
+            sets = []
+            for _ in range(nsets):
+                qs = torch.randn((B, n, H, dk), device=dev, dtype=torch.bfloat16)
+                ks = torch.randn((B, n, Hkv, dk), device=dev, dtype=torch.bfloat16)
+                vs = torch.randn((B, n, Hkv, dv), device=dev, dtype=torch.bfloat16)
+                os_ = torch.empty((B, n, H, dv), device=dev, dtype=torch.float32)
+                fss = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+                sets.append((qs, ks, vs, os_, fss))
+            sprob = lattn.LattnProblem(B, n, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
+            it = [0]
 
-        def bstep():
-            rc = lattn.lattn_bwd(prob, q, k, v, g, w.scale, None, False, None, d_o, None, dq, dkk, dvv,
-                                 dinit, ws, stream=stream.cuda_stream)
-            if rc != lattn.LATTN_OK:
-                raise lattn.LattnError(rc)
-
-        print("[bench] backward", file=sys.stderr, flush=True)
-        b_wall, b_ms = time_calls(torch, bstep, stream, args.warmup, args.steps)
-        b_mean = sum(b_ms) / len(b_ms)
-        b_alg = bwd_algorithmic_bytes(B, T, H, Hkv, dk, dv, 2)
-        b_ach = b_alg / (b_mean * 1e-3) / 1e9
-        print(f"[bench] backward {args.steps} steps: {b_wall:.4f} ms/step wall, mean {b_mean:.4f} ms",
-              file=sys.stderr, flush=True)
-        bwd = {"ms_per_step": b_wall, "tokens_per_s": B * T / (b_wall * 1e-3),
-               "roofline": {"bound": "hbm", "achieved": b_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": b_ach / HBM_PEAK_GBS, "algorithmic_bytes": b_alg, "call_ms": b_mean},
-               "inputs": "q, k, v, d_o bf16; no initial state, no final-state gradient; "
-                         "d_initial_state computed",
-               "page_lightning2_bwd_ms": PAGE_LIGHTNING2_BWD_MS if T == 32768 else None}
-        del dq, dkk, dvv, d_o
-
-    gated = None
-    if not args.no_gated:
-        gates = w.make_gates(("g",), 0.1)
-        gdev = to_dev(gates["g"])
-        go = torch.empty((B, T, H, dv), device=dev, dtype=torch.float32)
-        gfs = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
-
-        def gstep():
-            rc = lattn.lattn_fwd_gated(prob, q, k, v, gdev, None, None, None, w.scale, None, False, None, go,
-                                       gfs, stream=stream.cuda_stream)
-            if rc != lattn.LATTN_OK:
-                raise lattn.LattnError(rc)
-
-        print("[bench] gated forward", file=sys.stderr, flush=True)
-        g_wall, g_ms = time_calls(torch, gstep, stream, args.warmup, args.steps)
-        g_mean = sum(g_ms) / len(g_ms)
-        g_bytes = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2) + B * T * H * dk * 2
-        # the recurrence: decay (1), rank-1 update (2) and readout (2) flops per state element per token
-        g_flops = 5 * B * T * H * dk * dv
-        g_tf = g_flops / (g_mean * 1e-3) / 1e12
-        print(f"[bench] gated {args.steps} steps: {g_wall:.4f} ms/step wall, mean {g_mean:.4f} ms",
-              file=sys.stderr, flush=True)
-        # bf16 inputs run on bf16 MFMA (hi/lo operand splits): at bf16 rates the
-        # algorithm's bytes bind (6.45 GB at 8 TB/s vs 0.34 TFLOP at 2.5 PFLOP/s)
-        g_gbs = g_bytes / (g_mean * 1e-3) / 1e9
-        gated = {"workload": f"GLA gate g ~ U[-0.1, 0) per key channel, B{B} H{H} d{dk} N{T} bf16, "
-                             "bf16 MFMA with hi/lo splits, fp32 accumulation",
-                 "ms_per_step": g_wall, "tokens_per_s": B * T / (g_wall * 1e-3),
-                 "roofline": {"bound": "hbm", "achieved": g_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": g_gbs / HBM_PEAK_GBS, "algorithmic_bytes": g_bytes, "call_ms": g_mean},
-                 "mfma": {"achieved": g_tf, "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                          "frac": g_tf / BF16_MFMA_PEAK_TFS, "algorithmic_flops": g_flops}}
-        del gdev, go, gfs
-
-    split = None
-    if not args.no_split:
-        # One batch row and 8 heads: 32 workgroups unsplit, so the forward cuts each row
-        # into segments chained through their states.
-        Hs = 8
-        ws_ = inputs.Workload("split", 1, T, Hs, Hs, dk, dv, "bf16", w.layer_idx, w.num_layers, seed=5)
-        sd = ws_.make()
-        sq, sk, sv = (to_dev(sd[n]) for n in ("q", "k", "v"))
-        gs = torch.from_numpy(lattn.lattn_lightning_g_gamma(Hs, w.layer_idx, w.num_layers)).to(dev)
-        so = torch.empty((1, T, Hs, dv), device=dev, dtype=torch.float32)
-        sfs = torch.empty((1, Hs, dk, dv), device=dev, dtype=torch.float32)
-        sprob = lattn.LattnProblem(1, T, Hs, Hs, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
-        res = {}
-        for mode in ("split", "unsplit"):
-            if mode == "unsplit":
-                os.environ["LATTN_SPLIT"] = "0"
-            nbytes = lattn.lattn_fwd_workspace_size(sprob)
-            sws = torch.empty(nbytes, device=dev, dtype=torch.uint8) if nbytes else None
-
-            def sstep():
-                rc = lattn.lattn_fwd(sprob, sq, sk, sv, gs, ws_.scale, None, False, None, so, sfs, sws,
+            def sweep_step():
+                qs, ks, vs, os_, fss = sets[it[0] % nsets]
+                it[0] += 1
+                rc = lattn.lattn_fwd(sprob, qs, ks, vs, g, w.scale, None, False, None, os_, fss,
                                      stream=stream.cuda_stream)
                 if rc != lattn.LATTN_OK:
                     raise lattn.LattnError(rc)
 
-            wall_ms, ev_ms = time_calls(torch, sstep, stream, args.warmup, args.steps)
-            res[mode] = (wall_ms, sum(ev_ms) / len(ev_ms), nbytes)
-            os.environ.pop("LATTN_SPLIT", None)
-        s_alg = algorithmic_bytes(1, T, Hs, Hs, dk, dv, 2)
-        s_ach = s_alg / (res["split"][1] * 1e-3) / 1e9
-        print(f"[bench] split B1 H{Hs}: {res['split'][1]:.4f} ms split, {res['unsplit'][1]:.4f} ms unsplit",
-              file=sys.stderr, flush=True)
-        split = {"workload": f"B1 H{Hs} d{dk} N{T} bf16, no initial state",
-                 "ms_per_step": res["split"][0], "tokens_per_s": T / (res["split"][0] * 1e-3),
-                 "unsplit_ms_per_step": res["unsplit"][0],
-                 "speedup": res["unsplit"][1] / res["split"][1],
-                 "workspace_bytes": res["split"][2],
-                 "roofline": {"bound": "hbm", "achieved": s_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": s_ach / HBM_PEAK_GBS, "algorithmic_bytes": s_alg,
-                              "call_ms": res["split"][1]}}
-        del sq, sk, sv, so
-
-    dec = None
-    if args.decode_batch > 0:
-        Bd = args.decode_batch
-        wd = inputs.Workload("decode", Bd, 1, H, Hkv, dk, dv, "bf16", w.layer_idx, w.num_layers,
-                             init_std=0.5, seed=3)
-        dd = wd.make()
-        dq_, dk_, dv_ = (to_dev(dd[n])[:, 0].contiguous() for n in ("q", "k", "v"))
-        state = torch.from_numpy(dd["initial_state"]).to(dev)
-        o_dec = torch.empty((Bd, H, dv), device=dev, dtype=torch.float32)
-        dprob = lattn.LattnProblem(Bd, 1, H, Hkv, dk, dv, 0, lattn.LATTN_BF16, lattn.LATTN_F32)
-
-        def dstep():
-            rc = lattn.lattn_decode(dprob, dq_, dk_, dv_, g, w.scale, state, state, o_dec,
-                                    stream=stream.cuda_stream)
-            if rc != lattn.LATTN_OK:
-                raise lattn.LattnError(rc)
-
-        print("[bench] decode", file=sys.stderr, flush=True)
-        d_wall, d_ms = time_calls(torch, dstep, stream, args.warmup, args.steps)
-        d_mean = sum(d_ms) / len(d_ms)
-        d_alg = 2 * Bd * H * dk * dv * 4 + Bd * (H * dk + Hkv * dk + Hkv * dv) * 2 + Bd * H * dv * 4
-        d_ach = d_alg / (d_mean * 1e-3) / 1e9
-        print(f"[bench] decode {args.steps} steps: {d_wall:.4f} ms/step wall, mean {d_mean:.4f} ms",
-              file=sys.stderr, flush=True)
-        dec = {"batch": Bd, "ms_per_step": d_wall, "tokens_per_s": Bd / (d_wall * 1e-3),
-               "roofline": {"bound": "hbm", "achieved": d_ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": d_ach / HBM_PEAK_GBS, "algorithmic_bytes": d_alg, "call_ms": d_mean},
-               "inputs": f"{Bd} sequences x H{H} d{dk}: q, k, v bf16, fp32 state updated in place"}
-        if not args.no_cpu_baseline:
-            dec["cpu_baseline"] = cpu_baseline_decode(wd, dd)
-        del state, o_dec
+            n_wall, n_ms = time_calls(torch, sweep_step, stream, args.warmup, args.steps, settle)
+            st = ms_stats(n_ms)
+            gbs = nbytes / (st["mean"] * 1e-3) / 1e9
+            sweep.append({"seq_len": n, "ms_per_step": n_wall, "kernel_ms": st,
+                          "tokens_per_s": B * n / (n_wall * 1e-3), "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+                          "buffer_sets": nsets, "page_lightning2_ms": PAGE_LIGHTNING2_SWEEP_MS[n]})
+            log(f"sweep N={n}: {n_wall:.4f} ms/step wall, kernel mean {st['mean']:.4f} ms, median "
+                f"{st['median']:.4f} ms, {gbs:.0f} GB/s ({nsets} buffer sets)")
+            del sets
 
     if args.copy_probe:
         src = torch.empty(1 << 28, device=dev, dtype=torch.float32)  # 1 GiB
@@ -582,10 +627,23 @@ def main():
         del src, dst
 
     if args.bandwidth:
-        print("[bench] " + device_bandwidth(torch, dev), file=sys.stderr, flush=True)
+        log(device_bandwidth(torch, dev))
+
+    # -- the headline: exactly --warmup untimed and --steps timed forward calls ---------------
+    log("forward (headline)")
+    ms_per_step, kernel_ms = time_calls(torch, step, stream, args.warmup, args.steps)
+    kst = ms_stats(kernel_ms)
+    log(f"{args.steps} steps: {ms_per_step:.4f} ms/step wall, kernel mean {kst['mean']:.4f} ms median "
+        f"{kst['median']:.4f} ms min {kst['min']:.4f} max {kst['max']:.4f}")
+    if sweep is not None:
+        full_gbs = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2) / (kst["mean"] * 1e-3) / 1e9
+        sweep.append({"seq_len": T, "ms_per_step": ms_per_step, "kernel_ms": kst,
+                      "tokens_per_s": B * T / (ms_per_step * 1e-3), "hbm_gbs": full_gbs,
+                      "hbm_frac": full_gbs / HBM_PEAK_GBS, "buffer_sets": 1,
+                      "page_lightning2_ms": PAGE_LIGHTNING2_SWEEP_MS.get(T)})
 
     alg = algorithmic_bytes(B, T, H, Hkv, dk, dv, 2)
-    achieved = alg / (mean_kernel_ms * 1e-3) / 1e9
+    bound, hbm, mfma = roofline_pair(alg, fwd_algorithmic_flops(B * T, H, dk, dv), kst["mean"])
     value = B * T / (ms_per_step * 1e-3)
     page_tok_s = 4 * 32768 / (PAGE_LIGHTNING2_MS * 1e-3)
     line = {
@@ -605,16 +663,41 @@ def main():
                    "seq_len": T, "num_heads": H, "num_kv_heads": Hkv, "head_dim_qk": dk,
                    "head_dim_v": dv, "layer_idx": w.layer_idx, "num_layers": w.num_layers,
                    "out_dtype": "f32", "reverse": False, "initial_state": False},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(),
-                     "algorithmic_bytes": alg, "kernel_ms": mean_kernel_ms},
+        "roofline": {"bound": bound, "achieved": hbm["achieved"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": hbm["frac"], "traffic": measured_traffic(), "algorithmic_bytes": alg,
+                     "kernel_ms": kst["mean"], "kernel_ms_median": kst["median"], "kernel_ms_min": kst["min"],
+                     "kernel_ms_max": kst["max"], "mfma": mfma},
     }
+
+    # -- CPU baselines last (the oracle on the host cores) ------------------------------------
     if not args.no_cpu_baseline:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, data)
+        import oracle
+
+        log("cpu baseline (oracle)")
+        cb = cpu_baseline(w, data)
+        cb["cpu_model"] = cpu_model()
+        cb["threads"] = oracle.load().set_threads(0)
+        line["cpu_baseline"] = cb
+        if sweep is not None:
+            # One oracle run per sweep N over the whole workload (all rows and heads) on the
+            # first N tokens of the headline inputs, timed on the wall clock.
+            orc = oracle.load()
+            g_np = orc.lightning_g_gamma(H, w.layer_idx, w.num_layers)
+            for ent in sweep:
+                n = ent["seq_len"]
+                cut = [np.ascontiguousarray(data[x][:, :n]) for x in ("q", "k", "v")]
+                t0 = time.perf_counter()
+                orc.recurrent_fwd(*cut, g_np, w.scale)
+                dt = time.perf_counter() - t0
+                ent["cpu_oracle_s"] = dt
+                ent["cpu_tokens_per_s"] = B * n / dt
+                del cut
+            log("sweep cpu: " + ", ".join(f"N={e['seq_len']} {e['cpu_oracle_s']:.2f} s" for e in sweep))
         if bwd is not None:
-            print("[bench] cpu baseline of the backward (oracle)", file=sys.stderr, flush=True)
+            log("cpu baseline of the backward (oracle)")
             bwd["cpu_baseline"] = cpu_baseline_bwd(w, data, grads)
+        if dec is not None:
+            dec["cpu_baseline"] = cpu_baseline_decode(wd, dd)
     if bwd is not None:
         line["backward"] = bwd
     if dec is not None:
