@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblattn.so")
-SOURCES = [os.path.join(CSRC, n) for n in ("lattn_kernels.hip", "lattn_gated.hip", "lattn_api.cpp")]
+SOURCES = [os.path.join(CSRC, n) for n in ("lattn_kernels.hip", "lattn_gated.hip", "lattn_noalloc.hip", "lattn_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

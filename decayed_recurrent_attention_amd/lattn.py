@@ -34,7 +34,7 @@ LATTN_ERR_LAUNCH = -6
 LATTN_ERR_DEVICE = -7
 
 # Every function declared in include/lattn.h.
-EXPORTS = ("lattn_fwd", "lattn_fwd_workspace_size", "lattn_fwd_gated", "lattn_fwd_gated_workspace_size",
+EXPORTS = ("lattn_fwd", "lattn_fwd_noalloc", "lattn_fwd_workspace_size", "lattn_fwd_gated", "lattn_fwd_gated_workspace_size",
            "lattn_bwd", "lattn_bwd_workspace_size", "lattn_decode", "lattn_lightning_g_gamma",
            "lattn_status_string", "lattn_set_knob", "lattn_abi_version")
 
@@ -75,6 +75,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             lib.lattn_fwd.restype = ctypes.c_int
             lib.lattn_fwd.argtypes = [P, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int, vp, vp,
                                       vp, vp, ctypes.c_size_t, vp]
+            lib.lattn_fwd_noalloc.restype = ctypes.c_int
+            lib.lattn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, ctypes.c_float, vp, ctypes.c_int, vp, vp, vp, vp]
             lib.lattn_fwd_workspace_size.restype = ctypes.c_size_t
             lib.lattn_fwd_workspace_size.argtypes = [P]
             lib.lattn_bwd.restype = ctypes.c_int
@@ -164,6 +166,22 @@ def lattn_fwd(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_sta
         ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g_gamma), float(scale),
         _ptr(initial_state), int(bool(reverse)), _ptr(cu_seqlens), _ptr(o), _ptr(final_state),
         _ptr(workspace), ws_bytes, stream))
+
+
+LATTN_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def lattn_fwd_noalloc(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_state, reverse: bool,
+                      cu_seqlens, o, final_state, stream=None) -> int:
+    """Raw call of the forward that takes its workspace from the library's own device
+    array (nothing is allocated); returns the status code."""
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    return int(load_library().lattn_fwd_noalloc(
+        ctypes.byref(problem), _ptr(q), _ptr(k), _ptr(v), _ptr(g_gamma), float(scale),
+        _ptr(initial_state), int(bool(reverse)), _ptr(cu_seqlens), _ptr(o), _ptr(final_state), stream))
 
 
 def lattn_bwd(problem: LattnProblem, q, k, v, g_gamma, scale: float, initial_state, reverse: bool,

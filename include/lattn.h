@@ -109,6 +109,27 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
               size_t workspace_bytes, void* stream);
 
 /*
+ * lattn_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, and harnesses that forbid hipMalloc.  The arguments
+ * and results are those of lattn_fwd; the workspace comes from a device array that
+ * the library owns, LATTN_NOALLOC_SCRATCH_BYTES (32 MiB) on each device it runs on,
+ * held from the first call on that device until the process ends.  The call itself
+ * allocates nothing.
+ *   Limit: problems with lattn_fwd_workspace_size(p) > LATTN_NOALLOC_SCRATCH_BYTES are
+ *          refused with LATTN_ERR_WORKSPACE before any device call (use lattn_fwd with
+ *          a caller-owned workspace for them).
+ *   Races: every call on one device uses the same array, so calls that may overlap in
+ *          time on one device (other streams, other threads) must be serialized by the
+ *          caller; calls on different devices are independent.
+ * Returns LATTN_OK or a negative status as lattn_fwd does; LATTN_ERR_DEVICE if the
+ * array's device address cannot be obtained.
+ */
+#define LATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int lattn_fwd_noalloc(const lattn_problem* p, const void* q, const void* k, const void* v,
+                      const float* g_gamma, float scale, const float* initial_state, int reverse,
+                      const int32_t* cu_seqlens, void* o, float* final_state, void* stream);
+
+/*
  * Device workspace (bytes) that lattn_bwd needs for problem *p: room for the
  * per-query-head gradients before their sum into kv heads (num_heads >
  * num_kv_heads) and for the sequence order of packed input; 0 when neither

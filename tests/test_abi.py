@@ -350,3 +350,22 @@ def test_graft_entry_build_calls_both_builds(monkeypatch):
     monkeypatch.setattr(oracle_build, "build", lambda *a, **k: calls.append("oracle"))
     entry.build()
     assert calls == ["hip", "oracle"]
+
+
+def test_noalloc_refuses_oversized_workspace():
+    """lattn_fwd_noalloc refuses, before any device call, a problem whose workspace
+    exceeds the library's array, and reports argument errors like lattn_fwd."""
+    L = lattn.load_library()
+    prob = P(batch=1, seqlen=64 * 64, num_heads=8, num_kv_heads=8, head_dim_qk=256, head_dim_v=256)
+    with lattn.knob(lattn.LATTN_KNOB_SPLIT, 64):  # 2 * 64 segments * 8 heads * 256 KiB = 256 MiB
+        assert lattn.lattn_fwd_workspace_size(prob) > lattn.LATTN_NOALLOC_SCRATCH_BYTES
+        assert L.lattn_fwd_noalloc(ctypes.byref(prob), FAKE, FAKE, FAKE, FAKE, 1.0, None, 0, None, FAKE, FAKE,
+                                   None) == lattn.LATTN_ERR_WORKSPACE
+    assert L.lattn_fwd_noalloc(None, FAKE, FAKE, FAKE, FAKE, 1.0, None, 0, None, FAKE, FAKE,
+                               None) == lattn.LATTN_ERR_INVALID_ARG
+    assert L.lattn_fwd_noalloc(ctypes.byref(P(num_kv_heads=3)), FAKE, FAKE, FAKE, FAKE, 1.0, None, 0, None, FAKE,
+                               FAKE, None) == lattn.LATTN_ERR_HEADS
+    assert L.lattn_fwd_noalloc(ctypes.byref(P()), None, FAKE, FAKE, FAKE, 1.0, None, 0, None, FAKE, FAKE,
+                               None) == lattn.LATTN_ERR_INVALID_ARG
+    assert lattn.LATTN_NOALLOC_SCRATCH_BYTES == 32 << 20
+    assert "((size_t)32 << 20)" in open(HEADER).read()
