@@ -30,7 +30,10 @@ Prints one JSON line:  value = B*N / (seconds per step)  [tokens/s], plus
                 matrix figure beside it,
   bf16_out      the same forward with o in bf16 (skipped with --no-bf16-out),
   configs       the other parity workloads (tiny fp32, B2 H8 d64, B2 H12 d192, packed GQA
-                in both directions), forward only (skipped with --no-configs),
+                in both directions), forward only (skipped with --no-configs); the packed
+                ones also without the split planner,
+  packed_split  a skewed packed batch (one long sequence among short ones) with the
+                device-planned split against the same call unsplit,
   sweep         the forward at N = 512 .. 16384 (same B, H, head dims), each N rotating
                 over enough input sets that about 1 GB is touched between repeats, with
                 the Lightning-2 forward time the pages print for that N beside it
@@ -563,6 +566,20 @@ def main():
 
             c_wall, c_ms = time_calls(torch, cstep, stream, args.warmup, args.steps, settle)
             st = ms_stats(c_ms)
+            unplanned = None
+            if cu is not None:
+                # the same call without the split planner (the longest-first order only)
+                with lattn.knob(lattn.LATTN_KNOB_SPLIT, 0):
+                    n0 = lattn.lattn_fwd_workspace_size(cprob)
+                    cws0 = torch.empty(n0, device=dev, dtype=torch.uint8) if n0 else None
+
+                    def cstep0():
+                        rc = lattn.lattn_fwd(cprob, cq, ck, cv, cg, cw.scale, cinit, cw.reverse, cu, co, cfs, cws0,
+                                             stream=stream.cuda_stream)
+                        if rc != lattn.LATTN_OK:
+                            raise lattn.LattnError(rc)
+
+                    unplanned = ms_stats(time_calls(torch, cstep0, stream, args.warmup, args.steps, settle)[1])
             ntok = cw.batch * cw.seqlen
             c_alg = (ntok * (cw.num_heads * cw.dk + cw.num_kv_heads * (cw.dk + cw.dv)) * (4 if f32in else 2)
                      + ntok * cw.num_heads * cw.dv * 4
@@ -574,9 +591,56 @@ def main():
                             "initial_state": cinit is not None, "ms_per_step": c_wall, "kernel_ms": st,
                             "tokens_per_s": ntok / (c_wall * 1e-3), "algorithmic_bytes": c_alg,
                             "hbm_gbs": c_gbs, "hbm_frac": c_gbs / HBM_PEAK_GBS})
+            if unplanned is not None:
+                configs[-1]["kernel_ms_without_planner"] = unplanned
             log(f"{cw.name}: {c_wall:.4f} ms/step wall, mean {st['mean']:.4f} ms, median {st['median']:.4f} ms, "
                 f"{c_gbs:.0f} GB/s")
             del cq, ck, cv, co, cfs, cws
+
+    packed_split = None
+    if not args.no_configs:
+        # A skewed packed batch: one sequence of 49152 tokens among 31 of 64 .. 1024 tokens
+        # (H16 / kv 4, d128, initial states).  Unsplit, the long sequence sets the call's
+        # length; the planner cuts it into segments.
+        lens = [49152] + [int(x) for x in inputs.lengths(31, 64, 1024, 9)]
+        pw = inputs.Workload("packed_skewed", 1, sum(lens), 16, 4, dk, dv, "bf16", 6, 12, seq_lens=lens,
+                             init_std=0.1, seed=9)
+        log(f"skewed packed batch ({sum(lens)} tokens)")
+        pd = pw.make()
+        pq, pk, pv = (to_dev(pd[n]) for n in ("q", "k", "v"))
+        pinit = torch.from_numpy(pd["initial_state"]).to(dev)
+        pcu = torch.from_numpy(pd["cu_seqlens"]).to(dev, torch.int32)
+        pg = torch.from_numpy(lattn.lattn_lightning_g_gamma(16, 6, 12)).to(dev)
+        po = torch.empty((1, pw.seqlen, 16, dv), device=dev, dtype=torch.float32)
+        pfs = torch.empty((len(lens), 16, dk, dv), device=dev, dtype=torch.float32)
+        pprob = lattn.LattnProblem(1, pw.seqlen, 16, 4, dk, dv, len(lens), lattn.LATTN_BF16, lattn.LATTN_F32)
+        res = {}
+        for mode, kv in (("planned", lattn.LATTN_KNOB_AUTO), ("unsplit", 0)):
+            with lattn.knob(lattn.LATTN_KNOB_SPLIT, kv):
+                nb = lattn.lattn_fwd_workspace_size(pprob)
+                pws = torch.empty(nb, device=dev, dtype=torch.uint8) if nb else None
+
+                def pstep():
+                    rc = lattn.lattn_fwd(pprob, pq, pk, pv, pg, pw.scale, pinit, False, pcu, po, pfs, pws,
+                                         stream=stream.cuda_stream)
+                    if rc != lattn.LATTN_OK:
+                        raise lattn.LattnError(rc)
+
+                wall_ms, ev_ms = time_calls(torch, pstep, stream, args.warmup, args.steps, settle)
+            res[mode] = (wall_ms, ms_stats(ev_ms), nb)
+        p_alg = (pw.seqlen * (16 * dk + 4 * (dk + dv)) * 2 + pw.seqlen * 16 * dv * 4 + 2 * len(lens) * 16 * dk * dv * 4)
+        p_mean = res["planned"][1]["mean"]
+        p_gbs = p_alg / (p_mean * 1e-3) / 1e9
+        packed_split = {"workload": f"packed: 1 x 49152 + 31 x U[64, 1024] tokens ({pw.seqlen}), H16 kv4 d{dk} bf16, "
+                                    "initial states, forward",
+                        "ms_per_step": res["planned"][0], "kernel_ms": res["planned"][1],
+                        "unsplit_kernel_ms": res["unsplit"][1],
+                        "speedup": res["unsplit"][1]["mean"] / p_mean, "workspace_bytes": res["planned"][2],
+                        "tokens_per_s": pw.seqlen / (res["planned"][0] * 1e-3),
+                        "roofline": {"bound": "hbm", "achieved": p_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                     "frac": p_gbs / HBM_PEAK_GBS, "algorithmic_bytes": p_alg, "call_ms": p_mean}}
+        log(f"skewed packed: {p_mean:.4f} ms planned, {res['unsplit'][1]['mean']:.4f} ms unsplit")
+        del pq, pk, pv, po
 
     sweep = None
     if not args.no_sweep:
@@ -712,6 +776,8 @@ def main():
         line["sweep"] = sweep
     if configs is not None:
         line["configs"] = configs
+    if packed_split is not None:
+        line["packed_split"] = packed_split
     print(json.dumps(line), flush=True)
 
 

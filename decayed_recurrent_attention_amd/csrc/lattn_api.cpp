@@ -148,15 +148,30 @@ bool make_params(const lattn_problem& p, int dk, int dv, int nw, const float* g_
 
 int64_t heads_of(const lattn_problem& p) { return (int64_t)num_seqs_of(p) * p.num_heads; }
 
-// Intra-sequence split of a fixed-length bf16 forward: each batch row is cut into P
-// segments of seg_len tokens (a multiple of the chunk) that run as independent
-// sequences, so that few (row, head) pairs still fill the GPU.  A state-only pass
-// gives every segment's own state contribution, a scan chains them into the state
+// Intra-sequence split of a bf16 forward: sequences are cut into segments (a multiple
+// of the chunk) that run in parallel.  A state-only pass gives every segment but a
+// sequence's last its own state contribution, a scan chains them into the state
 // entering each segment, and the main pass runs every segment from that state.
+//  - Fixed length: every batch row is cut into P segments of seg_len tokens when the
+//    (row, head) pairs are too few to fill the GPU.
+//  - Packed input: a planner kernel reads cu_seqlens on the device and cuts only the
+//    sequences longer than the balanced load per compute unit (skewed lengths).
 struct Split {
-    int P = 0;
-    int seg_len = 0;
+    int P = 0;            // fixed length: segments per row (0: no split)
+    int seg_len = 0;      // fixed length: tokens per segment
+    bool packed = false;  // packed input: the device-planned split runs
+    int forced = 0;       // packed: segments per sequence forced by the knob (0: balance)
+    int wgs = 0;          // packed: workgroups per segment (heads x value blocks)
+    int min_seg = 0;      // packed: shortest segment in chunks
+    int max_slots = 0;    // packed: capacity of the state slots and the state-only list
+    int max_main = 0;     // packed: capacity of the main-pass list
 };
+
+// Shortest segment worth a state-only pass and a scan: 4 chunks up to dk 128, 16 above
+// (those cost more at dk 192 and 256).  Measured (one box): B2 H8 d64 N2048 ran 23 us
+// in 8 segments against 41 us in 2 and 57 us unsplit; B2 H12 d192 N2048 ran 75 us in 2
+// segments and 84 us in 4.
+int min_seg_chunks(int dk) { return dk <= 128 ? 4 : 16; }
 
 Split choose_split(const lattn_problem& p, int nw) {
     Split sp;
@@ -170,13 +185,7 @@ Split choose_split(const lattn_problem& p, int nw) {
     } else {
         if (wgs >= 128) return sp;  // at least half the compute units busy already
         want = (int)((256 + wgs - 1) / wgs);
-        // Segments of at least 4 chunks up to dk 128 and at least 16 chunks above: a
-        // segment pays for a state-only pass and a scan, which cost more at dk 192 and
-        // 256.  Measured (one box): B2 H8 d64 N2048 runs 23 us in 8 segments against
-        // 41 us in 2 and 57 us unsplit; B2 H12 d192 N2048 runs 75 us in 2 segments and
-        // 84 us in 4.
-        const int min_chunks = p.head_dim_qk <= 128 ? 4 : 16;
-        const int cap = p.seqlen / (min_chunks * lattn::kChunk);
+        const int cap = p.seqlen / (min_seg_chunks(p.head_dim_qk) * lattn::kChunk);
         if (want > cap) want = cap;
         if (want < 2) return sp;
     }
@@ -185,6 +194,29 @@ Split choose_split(const lattn_problem& p, int nw) {
     sp.seg_len = ((chunks + want - 1) / want) * lattn::kChunk;
     sp.P = (p.seqlen + sp.seg_len - 1) / sp.seg_len;
     if (sp.P < 2) sp = Split{};
+    return sp;
+}
+
+// Packed input: the planner's bounds.  Balanced mode cuts sequences longer than 5/4 of
+// Lb = J * sum(chunks) / kNumCu into segments of at least Lb / 2 chunks, so at most
+// 2 kNumCu / J + 1 state slots are used (J = workgroups per segment); forced mode
+// cuts every sequence into at most `forced` segments.
+Split choose_packed_split(const lattn_problem& p, int nw) {
+    Split sp;
+    if (!is_varlen(p) || p.in_dtype != LATTN_BF16 || p.num_seqs > lattn::kMaxPlanSeqs) return sp;
+    const int wgs = p.num_heads * (p.head_dim_v / (16 * nw));
+    const int forced = knob(LATTN_KNOB_SPLIT);
+    if (forced != LATTN_KNOB_AUTO && forced < 2) return sp;
+    if (forced == LATTN_KNOB_AUTO && wgs >= lattn::kNumCu) return sp;  // Lb >= every sequence: nothing to cut
+    sp.packed = true;
+    sp.forced = forced == LATTN_KNOB_AUTO ? 0 : forced;
+    sp.wgs = wgs;
+    sp.min_seg = min_seg_chunks(p.head_dim_qk);
+    const int64_t slots = sp.forced ? (int64_t)p.num_seqs * (sp.forced - 1)
+                                    : 2 * ((lattn::kNumCu + wgs - 1) / wgs) + 2;
+    if (slots < 1 || slots * p.num_heads > 65535 || slots + p.num_seqs > INT_MAX / 64) return Split{};
+    sp.max_slots = (int)slots;
+    sp.max_main = p.num_seqs + sp.max_slots;
     return sp;
 }
 
@@ -198,13 +230,27 @@ int widest_nw(int in_dtype, int dk, int dv) {
 
 Split plan_forward(const lattn_problem& p, int& nw) {
     const int wide = widest_nw(p.in_dtype, p.head_dim_qk, p.head_dim_v);
-    const Split sp = is_varlen(p) ? Split{} : choose_split(p, wide);
-    nw = sp.P > 0 ? wide : choose_nw(p.in_dtype, p.head_dim_qk, p.head_dim_v, heads_of(p));
+    const Split sp = is_varlen(p) ? choose_packed_split(p, wide) : choose_split(p, wide);
+    nw = (sp.P > 0 || sp.packed) ? wide : choose_nw(p.in_dtype, p.head_dim_qk, p.head_dim_v, heads_of(p));
     return sp;
 }
 
-size_t split_state_bytes(const lattn_problem& p, const Split& sp) {
-    return round_up((size_t)p.batch * sp.P * p.num_heads * p.head_dim_qk * p.head_dim_v * sizeof(float), 256);
+size_t state_block_bytes(const lattn_problem& p) {
+    return (size_t)p.num_heads * p.head_dim_qk * p.head_dim_v * sizeof(float);
+}
+
+// Workspace of a split forward: [plan (packed only)][state slots], each 256-byte aligned.
+size_t split_plan_bytes(const Split& sp) {
+    if (!sp.packed) return 0;
+    const size_t words = lattn::kPlanHeader + (size_t)lattn::kPlanEntry * (sp.max_main + sp.max_slots) +
+                         (size_t)lattn::kPlanScan * sp.max_slots;
+    return round_up(words * sizeof(int32_t), 256);
+}
+size_t split_slot_count(const lattn_problem& p, const Split& sp) {
+    return sp.packed ? (size_t)sp.max_slots : (size_t)p.batch * (sp.P - 1);
+}
+size_t split_workspace_bytes(const lattn_problem& p, const Split& sp) {
+    return split_plan_bytes(sp) + round_up(split_slot_count(p, sp) * state_block_bytes(p), 256);
 }
 
 // Byte offsets of the backward workspace regions (each 256-byte aligned).
@@ -258,12 +304,10 @@ const char* lattn_status_string(int status) {
 
 size_t lattn_fwd_workspace_size(const lattn_problem* p) {
     if (p == nullptr || check_problem(*p, true) != LATTN_OK) return 0;
-    if (!is_varlen(*p)) {
-        int nw = 0;
-        const Split sp = plan_forward(*p, nw);
-        return sp.P > 0 ? 2 * split_state_bytes(*p, sp) : 0;
-    }
-    if (p->num_seqs > lattn::kMaxOrderedSeqs) return 0;
+    int nw = 0;
+    const Split sp = plan_forward(*p, nw);
+    if (sp.P > 0 || sp.packed) return split_workspace_bytes(*p, sp);
+    if (!is_varlen(*p) || p->num_seqs > lattn::kMaxOrderedSeqs) return 0;
     return round_up((size_t)p->num_seqs * sizeof(int32_t), 256);
 }
 
@@ -303,33 +347,48 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
 
     int nw = 0;
     const Split sp = plan_forward(*p, nw);
-    if (sp.P > 0) {
-        // state-only pass over the segments -> dS; scan -> state entering each segment
-        // and final_state; main pass over the segments from those states.
-        float* dS = static_cast<float*>(workspace);
-        float* s_in = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + split_state_bytes(*p, sp));
-        const int nseg = p->batch * sp.P;
+    if (sp.P > 0 || sp.packed) {
+        // state-only pass over every segment but each sequence's last -> slots; scan ->
+        // the state entering each segment, in place; main pass over every segment.
+        uint8_t* ws = static_cast<uint8_t*>(workspace);
+        int32_t* plan = sp.packed ? reinterpret_cast<int32_t*>(ws) : nullptr;
+        float* slots = reinterpret_cast<float*>(ws + split_plan_bytes(sp));
+        const int n_sonly = sp.packed ? sp.max_slots : p->batch * (sp.P - 1);
+        const int n_main = sp.packed ? sp.max_main : p->batch * sp.P;
         lattn::FwdParams f1, f3;
-        if (!make_params(*p, p->head_dim_qk, p->head_dim_v, nw, g_gamma, scale, nullptr, nullptr, f1, nseg))
+        if (!make_params(*p, p->head_dim_qk, p->head_dim_v, nw, g_gamma, scale, nullptr, nullptr, f1, n_sonly) ||
+            !make_params(*p, p->head_dim_qk, p->head_dim_v, nw, g_gamma, scale, nullptr, nullptr, f3, n_main))
             return LATTN_ERR_INVALID_ARG;
-        f1.seg_count = sp.P;
-        f1.seg_len = sp.seg_len;
-        f1.k = k;
-        f1.v = v;
-        f1.q = q;
-        f1.final_state = dS;
-        f3 = f1;
-        f3.init = s_in;
+        for (lattn::FwdParams* f : {&f1, &f3}) {
+            f->q = q;
+            f->k = k;
+            f->v = v;
+            f->reverse = reverse != 0;
+            f->slots = slots;
+            f->plan = plan;
+            f->plan_main = sp.max_main;
+            f->plan_slots = sp.max_slots;
+            f->seg_count = sp.P;
+            f->seg_len = sp.seg_len;
+        }
+        f1.seg_phase = 1;
+        f3.seg_phase = 2;
+        f3.init = initial_state;
         f3.o = static_cast<float*>(o);
         f3.o_bf16 = o_bf16;
-        f3.final_state = nullptr;
+        f3.final_state = final_state;
         const int dc = device_check();
         if (dc != LATTN_OK) return dc;
         hipStream_t s = static_cast<hipStream_t>(stream);
-        if (lattn::launch_fwd(f1, p->in_dtype, nw, reverse != 0, s, true) != hipSuccess) return LATTN_ERR_LAUNCH;
-        if (lattn::launch_seg_scan(dS, initial_state, s_in, final_state, g_gamma, p->batch, p->num_heads, sp.P,
-                                   sp.seg_len, p->seqlen, (int64_t)p->head_dim_qk * p->head_dim_v, reverse != 0,
-                                   s) != hipSuccess)
+        if (sp.packed &&
+            lattn::launch_split_plan(cu_seqlens, p->num_seqs, p->seqlen, sp.wgs, sp.min_seg, sp.forced, reverse != 0,
+                                     sp.max_main, sp.max_slots, plan, s) != hipSuccess)
+            return LATTN_ERR_LAUNCH;
+        if (n_sonly > 0 && lattn::launch_fwd(f1, p->in_dtype, nw, reverse != 0, s, true) != hipSuccess)
+            return LATTN_ERR_LAUNCH;
+        if (lattn::launch_seg_scan(plan, sp.max_main, sp.max_slots, sp.max_slots, slots, initial_state, g_gamma,
+                                   p->batch, p->num_heads, sp.P, sp.seg_len,
+                                   (int64_t)p->head_dim_qk * p->head_dim_v, s) != hipSuccess)
             return LATTN_ERR_LAUNCH;
         if (lattn::launch_fwd(f3, p->in_dtype, nw, reverse != 0, s) != hipSuccess) return LATTN_ERR_LAUNCH;
         return LATTN_OK;
@@ -550,7 +609,7 @@ int lattn_fwd_gated(const lattn_problem* p, const void* q, const void* k, const 
     fp.init = initial_state;
     fp.o = static_cast<float*>(o);
     fp.final_state = final_state;
-    fp.reverse_gated = reverse != 0;
+    fp.reverse = reverse != 0;
     const int dc = device_check();
     if (dc != LATTN_OK) return dc;
     hipStream_t s = static_cast<hipStream_t>(stream);

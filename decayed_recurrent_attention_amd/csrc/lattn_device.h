@@ -20,12 +20,14 @@ constexpr int kLdsBudget = 160 * 1024;
 
 // One unit of work, decoded from the workgroup id.
 struct Work {
-    int n;          // sequence (batch row, or packed sequence)
+    int n;          // sequence (batch row, packed sequence, or fixed-length segment)
     int h;          // query head
     int kvh;        // kv head read by h
     int vb;         // value block
-    int64_t start;  // first token row of the sequence in the flattened [B*T] axis
-    int64_t len;    // tokens in the sequence
+    int64_t start;  // first token row of the work in the flattened [B*T] axis
+    int64_t len;    // tokens in the work
+    const float* init_blk;  // this head's initial state block [dk][dv], or null (zeros)
+    float* fin_blk;         // where this head's final state block goes, or null (nowhere)
 };
 
 // Work id (normally the workgroup id) -> work.  Groups are (sequence rank, kv head); the workgroups of one
@@ -41,16 +43,51 @@ __device__ inline bool decode_work(const FwdParams& p, int id, Work& w) {
     const int j = slot % p.group_size;
     const int rank = g / p.num_kv_heads;
     w.kvh = g % p.num_kv_heads;
-    w.n = p.order ? p.order[rank] : rank;
     w.h = w.kvh * (p.num_heads / p.num_kv_heads) + j / p.nvb;
     w.vb = j % p.nvb;
-    if (p.seg_count > 0) {  // sequence n = segment n % seg_count of batch row n / seg_count
-        const int b = w.n / p.seg_count, sg = w.n % p.seg_count;
-        const int64_t a = (int64_t)sg * p.seg_len;
+    const int H = p.num_heads;
+    const int64_t blk = (int64_t)p.dk * p.dv;  // elements of one head's state block
+    if (p.plan) {  // packed split: the plan's entry of this rank
+        const int count = p.plan[p.seg_phase == 1 ? 1 : 0];
+        if (rank >= count) return false;
+        const int32_t* e = p.plan + kPlanHeader + kPlanEntry * (p.seg_phase == 1 ? p.plan_main + rank : rank);
+        w.n = e[2];
+        w.start = e[0];
+        w.len = e[1];
+        if (p.seg_phase == 1) {
+            w.init_blk = nullptr;
+            w.fin_blk = p.slots + ((int64_t)e[5] * H + w.h) * blk;
+        } else {
+            w.init_blk = e[3] >= 0 ? p.slots + ((int64_t)e[3] * H + w.h) * blk
+                                   : (p.init ? p.init + ((int64_t)w.n * H + w.h) * blk : nullptr);
+            w.fin_blk = (e[4] && p.final_state) ? p.final_state + ((int64_t)w.n * H + w.h) * blk : nullptr;
+        }
+        return true;
+    }
+    if (p.seg_count > 0) {  // fixed length: segments of seg_len tokens, in processing order
+        const int P = p.seg_count;
+        const int per = p.seg_phase == 1 ? P - 1 : P;  // the state-only pass skips the last
+        const int b = rank / per, k = rank % per;
+        const int64_t a = (int64_t)k * p.seg_len;
         const int64_t e = min(a + p.seg_len, (int64_t)p.seqlen);
-        w.start = (int64_t)b * p.seqlen + a;
-        w.len = e > a ? e - a : 0;
-    } else if (p.cu) {
+        const int64_t seg_len = e > a ? e - a : 0;
+        // reverse: segment k ends k * seg_len before the row's end
+        w.start = (int64_t)b * p.seqlen + (p.reverse ? (int64_t)p.seqlen - a - seg_len : a);
+        w.len = seg_len;
+        w.n = b;
+        const int64_t slot0 = (int64_t)b * (P - 1);
+        if (p.seg_phase == 1) {
+            w.init_blk = nullptr;
+            w.fin_blk = p.slots + ((slot0 + k) * H + w.h) * blk;
+        } else {
+            w.init_blk = k > 0 ? p.slots + ((slot0 + k - 1) * H + w.h) * blk
+                               : (p.init ? p.init + ((int64_t)b * H + w.h) * blk : nullptr);
+            w.fin_blk = (k == P - 1 && p.final_state) ? p.final_state + ((int64_t)b * H + w.h) * blk : nullptr;
+        }
+        return true;
+    }
+    w.n = p.order ? p.order[rank] : rank;
+    if (p.cu) {
         int64_t a = p.cu[w.n];
         int64_t e = p.cu[w.n + 1];
         a = min(max(a, (int64_t)0), (int64_t)p.seqlen);
@@ -61,6 +98,8 @@ __device__ inline bool decode_work(const FwdParams& p, int id, Work& w) {
         w.start = (int64_t)w.n * p.seqlen;
         w.len = p.seqlen;
     }
+    w.init_blk = p.init ? p.init + ((int64_t)w.n * H + w.h) * blk : nullptr;
+    w.fin_blk = p.final_state ? p.final_state + ((int64_t)w.n * H + w.h) * blk : nullptr;
     return true;
 }
 

@@ -130,7 +130,7 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_f32_kernel(const FwdParams p
     const int H = p.num_heads, dv = p.dv;
     const int64_t L = wk.len;
     const int nch = (int)((L + kGChunk - 1) / kGChunk);
-    const bool rev = p.reverse_gated != 0;
+    const bool rev = p.reverse != 0;
     const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
     const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
     const int j = 16 * wv + lr;       // this lane's column inside the block
@@ -564,7 +564,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
     const int H = p.num_heads, dv = p.dv;
     const int64_t L = wk.len;
     const int nch = (int)((L + kGChunk - 1) / kGChunk);
-    const bool rev = p.reverse_gated != 0;
+    const bool rev = p.reverse != 0;
     const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
     const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
     const int j = 16 * wv + lr;       // matrix waves: this lane's column inside the block

@@ -256,9 +256,14 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     constexpr int NWD = Cfg::NWD, MTL = MT / DS, KBL = KB / DS;  // waves; state tiles, dk blocks per wave
     constexpr int NST = Cfg::STAGES, DEPTH = Cfg::DEPTH;
     constexpr int QROW = DK * 2, VROW = BV * 2;  // LDS row bytes
-    // LDS: the Q tiles of every stage, then the K tiles, then the V tiles, then P.
-    constexpr int KREG = NST * Cfg::Q_BYTES, VREG = 2 * NST * Cfg::Q_BYTES;
-    __shared__ __attribute__((aligned(1024))) uint8_t smem[NST * Cfg::STAGE_BYTES + Cfg::P_BYTES + Cfg::X_BYTES];
+    // LDS: the Q tiles of every stage, then the K tiles, then the V tiles, then P and the
+    // partial sums.  The state-only pass holds only the K and V tiles, so two of its
+    // workgroups fit in one compute unit.
+    constexpr int KREG = SONLY ? 0 : NST * Cfg::Q_BYTES;
+    constexpr int VREG = KREG + NST * Cfg::Q_BYTES;
+    constexpr int LDS_BYTES = SONLY ? VREG + NST * Cfg::V_BYTES : NST * Cfg::STAGE_BYTES + Cfg::P_BYTES + Cfg::X_BYTES;
+    static_assert(!SONLY || 2 * LDS_BYTES <= kLdsBudget, "two state-only workgroups per compute unit");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
     uint8_t* Pbuf = smem + NST * Cfg::STAGE_BYTES;
     uint8_t* Xbuf = Pbuf + Cfg::P_BYTES;
 
@@ -287,7 +292,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     const uint32_t smem_base = lds_addr(smem);
 
     // Tiles (1, 0) and (3, 2) lie above the diagonal: their halves of P stay zero.
-    if (tid < 64) {
+    if (!SONLY && tid < 64) {
         const u32x2 z2 = {0u, 0u};
 #pragma unroll
         for (int hl = 0; hl < 2; ++hl) {
@@ -319,11 +324,9 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
 
     // State block: tile mt holds rows dmap(mt, 4*lg + ii) at column `col`.
     f32x4 S[MTL];
-    const int64_t st_blk = ((int64_t)wk.n * H + wk.h) * DK * dv;  // this head's state block
-    const int64_t st_off = st_blk + (int64_t)wk.vb * BV;
     {
         // Without an initial state the descriptor is empty and every load returns 0.
-        const auto ri = make_rsrc(p.init ? p.init + st_blk : p.g_gamma, p.init ? (uint32_t)(DK * dv * 4) : 0u);
+        const auto ri = make_rsrc(wk.init_blk ? wk.init_blk : p.g_gamma, wk.init_blk ? (uint32_t)(DK * dv * 4) : 0u);
         const int rs = (int)p.init_rs, cs = (int)p.init_cs, gcol = wk.vb * BV + col;
 #pragma unroll
         for (int mt = 0; mt < MTL; ++mt)
@@ -623,18 +626,18 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         wait_vmem<0>();  // no copy may still be writing LDS when the workgroup ends
     }
 
-    if (p.final_state) {
+    if (wk.fin_blk) {
         const float fm = (p.final_lam && nch > 0) ? p.final_mul * exp2f(g2) : p.final_mul;
+        float* fb = wk.fin_blk + wk.vb * BV;
 #pragma unroll
         for (int mt = 0; mt < MTL; ++mt)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                p.final_state[st_off + (int64_t)dmap(wd * MTL + mt, 4 * lg + ii) * dv + col] = fm * S[mt][ii];
+            for (int ii = 0; ii < 4; ++ii) fb[(int64_t)dmap(wd * MTL + mt, 4 * lg + ii) * dv + col] = fm * S[mt][ii];
     }
 }
 
 template <int DK, int NW, bool REV, bool SONLY, int DS = 1, bool OB16 = false>
-__global__ __launch_bounds__(64 * NW * DS, 1) void fwd_bf16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(64 * NW * DS, SONLY ? 2 : 1) void fwd_bf16_kernel(const FwdParams p) {
     fwd_bf16_body<DK, NW, REV, SONLY, DS, OB16>(p, blockIdx.x);
 }
 
@@ -705,14 +708,13 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
 
     // State tile mt holds rows 16*mt + 4*lg + ii, column vcol.
     f32x4 S[MT];
-    const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int ii = 0; ii < 4; ++ii)
-            S[mt][ii] = p.init ? p.init_mul * p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * p.init_rs +
-                                                      (int64_t)vcol * p.init_cs]
-                               : 0.f;
+            S[mt][ii] = wk.init_blk ? p.init_mul * wk.init_blk[(int64_t)(16 * mt + 4 * lg + ii) * p.init_rs +
+                                                                (int64_t)vcol * p.init_cs]
+                                    : 0.f;
 
     f32x4 pq[Cfg::QPER];
     f32x4 pk[Cfg::KPER][4];
@@ -889,13 +891,12 @@ __global__ __launch_bounds__(64 * NW, 1) void fwd_f32_kernel(const FwdParams p) 
         compute_chunk(c, st);
     }
 
-    if (p.final_state) {
+    if (wk.fin_blk) {
         const float fm = (p.final_lam && nch > 0) ? p.final_mul * exp2f(g2) : p.final_mul;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = fm * S[mt][ii];
+            for (int ii = 0; ii < 4; ++ii) wk.fin_blk[(int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = fm * S[mt][ii];
     }
 }
 
@@ -983,33 +984,174 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Intra-sequence split: chain the segments' own state contributions dS (from a
-// state-only pass) into the state entering each segment and the final state.
-// Per (row b, head h) and 4 state elements, in processing order:
-//     S_in[seg] = S;   S = lam^len(seg) * S + dS[seg];   final = S.
-// dS and S_in are [B * P, H, dk, dv] with segment index b * P + seg.
+// Intra-sequence split, chaining step.  A split sequence of P segments owns state
+// slots k = 0 .. P-2, which the state-only pass filled with segment k's own
+// contribution dS_k (from a zero state).  In processing order, with S the state
+// entering segment k (S_0 the sequence's initial state or zeros),
+//     S_{k+1} = lam^{len_k} S_k + dS_k,
+// and slot k is overwritten by S_{k+1} (in place: each element is read before it
+// is written).  Every segment but the last has the same length seg_len.  One thread
+// per 4 state elements; blockIdx.y = (split sequence j, head h).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void seg_scan_kernel(const float* __restrict__ dS, const float* __restrict__ init,
-                                                       float* __restrict__ s_in, float* __restrict__ final_state,
-                                                       const float* __restrict__ g_gamma, int H, int P, int seg_len,
-                                                       int seqlen, int elems4, int rev) {
+__global__ __launch_bounds__(256) void seg_scan_kernel(const int32_t* __restrict__ plan, int plan_main, int plan_slots,
+                                                       float* __restrict__ slots, const float* __restrict__ init,
+                                                       const float* __restrict__ g_gamma, int H, int P_fixed,
+                                                       int seg_len_fixed, int elems4) {
     const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
     if (e4 >= elems4) return;
-    const int64_t bh = blockIdx.y;  // b * H + h
-    const int h = (int)(bh % H);
-    const int64_t b = bh / H;
-    const float g2 = g_gamma[h] * kLog2e;
-    const int64_t elems = (int64_t)elems4 * 4;
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-    if (init) S = *reinterpret_cast<const f32x4*>(init + bh * elems + 4 * e4);
-    for (int j = 0; j < P; ++j) {
-        const int sg = rev ? P - 1 - j : j;
-        const int len = min(seg_len, seqlen - sg * seg_len);
-        const int64_t at = ((b * P + sg) * H + h) * elems + 4 * e4;
-        *reinterpret_cast<f32x4*>(s_in + at) = S;
-        S = exp2f(g2 * (float)len) * S + *reinterpret_cast<const f32x4*>(dS + at);
+    const int j = blockIdx.y / H, h = blockIdx.y % H;
+    int n, slot0, P, seg_len;
+    if (plan) {
+        if (j >= plan[2]) return;
+        const int32_t* e = plan + kPlanHeader + kPlanEntry * (plan_main + plan_slots) + kPlanScan * j;
+        n = e[0];
+        slot0 = e[1];
+        P = e[2];
+        seg_len = e[3];
+    } else {
+        n = j;
+        slot0 = j * (P_fixed - 1);
+        P = P_fixed;
+        seg_len = seg_len_fixed;
     }
-    if (final_state) *reinterpret_cast<f32x4*>(final_state + bh * elems + 4 * e4) = S;
+    const int64_t elems = (int64_t)elems4 * 4;
+    const float lam_seg = exp2f(g_gamma[h] * kLog2e * (float)seg_len);
+    f32x4 S = {0.f, 0.f, 0.f, 0.f};
+    if (init) S = *reinterpret_cast<const f32x4*>(init + ((int64_t)n * H + h) * elems + 4 * e4);
+    for (int k = 0; k + 1 < P; ++k) {
+        f32x4* at = reinterpret_cast<f32x4*>(slots + ((int64_t)(slot0 + k) * H + h) * elems + 4 * e4);
+        S = lam_seg * S + *at;
+        *at = S;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Packed-split planner (one workgroup): cut the packed sequences into segments so
+// that the longest ones no longer set the length of the call.  With c_n the chunks
+// of sequence n, J workgroups per segment and kNumCu compute units, the balanced
+// load per compute unit is Lb = J * sum(c_n) / kNumCu chunks.  A sequence longer
+// than 5/4 Lb (the state-only pass and scan cost about a quarter of a segment) is
+// cut into segments of S = max(min_seg, ceil(Lb / 2)) chunks; with `forced` > 1
+// every sequence of at least two chunks is cut into min(forced, c_n) segments.
+// Sequences whose slots would pass max_slots stay whole.  Writes the main pass's
+// segments longest first (ties by sequence, then segment), the state-only pass's
+// segments, and the scan list (layout in lattn_launch.h).  Segments are numbered
+// in processing order (mirrored positions in reverse), so only a sequence's last
+// segment can be short.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restrict__ cu, int num_seqs, int seqlen,
+                                                          int wgs, int min_seg, int forced, int rev, int max_main,
+                                                          int max_slots, int32_t* __restrict__ plan) {
+    __shared__ int32_t s_start[kMaxPlanSeqs], s_len[kMaxPlanSeqs], s_P[kMaxPlanSeqs], s_S[kMaxPlanSeqs];
+    __shared__ int32_t s_slot0[kMaxPlanSeqs], s_seg0[kMaxPlanSeqs];
+    __shared__ int64_t s_total;
+    __shared__ int32_t s_nsplit;
+    const int tid = threadIdx.x, nt = blockDim.x;
+    if (tid == 0) {
+        s_total = 0;
+        s_nsplit = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < num_seqs; i += nt) {
+        int64_t a = cu[i], e = cu[i + 1];
+        a = min(max(a, (int64_t)0), (int64_t)seqlen);  // clamped as the work decode clamps
+        e = min(max(e, a), (int64_t)seqlen);
+        s_start[i] = (int32_t)a;
+        s_len[i] = (int32_t)(e - a);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&s_total), (unsigned long long)((e - a + kChunk - 1) / kChunk));
+    }
+    __syncthreads();
+    const int64_t lb = (s_total * wgs + kNumCu - 1) / kNumCu;  // balanced chunks per compute unit
+    const int64_t seg_auto = max((int64_t)min_seg, (lb + 1) / 2);
+    for (int i = tid; i < num_seqs; i += nt) {
+        const int c = (s_len[i] + kChunk - 1) / kChunk;
+        int P = 1, S = c;
+        if (forced > 1) {
+            if (c >= 2) {
+                S = (c + min(forced, c) - 1) / min(forced, c);
+                P = (c + S - 1) / S;
+            }
+        } else if (4 * (int64_t)c > 5 * lb) {
+            S = (int)seg_auto;
+            P = (c + S - 1) / S;
+        }
+        s_P[i] = P;
+        s_S[i] = S;
+    }
+    __syncthreads();
+    if (tid == 0) {  // slots in sequence order; sequences past the capacity stay whole
+        int slots = 0, segs = 0, nsplit = 0;
+        for (int i = 0; i < num_seqs; ++i) {
+            if (s_P[i] > 1 && slots + s_P[i] - 1 > max_slots) s_P[i] = 1;
+            s_slot0[i] = slots;
+            s_seg0[i] = segs;
+            if (s_P[i] > 1) {
+                slots += s_P[i] - 1;
+                ++nsplit;
+            }
+            segs += s_P[i];
+        }
+        plan[0] = segs;
+        plan[1] = slots;
+        plan[2] = nsplit;
+        s_nsplit = nsplit;
+    }
+    __syncthreads();
+    // One entry per segment; rank = longest first.
+    int32_t* mainl = plan + kPlanHeader;
+    int32_t* sonly = mainl + kPlanEntry * max_main;
+    int32_t* scan = sonly + kPlanEntry * max_slots;
+    for (int i = tid; i < num_seqs; i += nt) {
+        const int P = s_P[i];
+        const int64_t S64 = (int64_t)s_S[i] * kChunk;
+        const int len = s_len[i];
+        int jrank = 0;  // index of this split sequence in the scan list
+        if (P > 1) {
+            for (int m = 0; m < i; ++m) jrank += s_P[m] > 1;
+            int32_t* e = scan + kPlanScan * jrank;
+            e[0] = i;
+            e[1] = s_slot0[i];
+            e[2] = P;
+            e[3] = (int32_t)S64;
+        }
+        for (int k = 0; k < P; ++k) {
+            const int64_t a = (int64_t)k * S64;
+            const int sl = (int)(P > 1 ? min(S64, (int64_t)len - a) : len);
+            const int st = s_start[i] + (int)(rev ? (int64_t)len - a - sl : a);
+            // rank among all segments: longer first, then by (sequence, segment)
+            int rank = 0;
+            for (int m = 0; m < num_seqs; ++m) {
+                const int Pm = s_P[m];
+                const int64_t Sm = (int64_t)s_S[m] * kChunk;
+                const int lm = s_len[m];
+                // segments of m: Pm - 1 of length Sm and one of the rest (or all of lm)
+                const int full = Pm > 1 ? Pm - 1 : 0;
+                const int last = Pm > 1 ? (int)(lm - (int64_t)(Pm - 1) * Sm) : lm;
+                auto before = [&](int l2, int k2) { return l2 > sl || (l2 == sl && (m < i || (m == i && k2 < k))); };
+                if (full > 0) {
+                    if (Sm > sl) rank += full;
+                    else if (Sm == sl) rank += m < i ? full : (m == i ? min(k, full) : 0);
+                }
+                rank += before(last, Pm - 1) ? 1 : 0;
+            }
+            int32_t* e = mainl + kPlanEntry * rank;
+            e[0] = st;
+            e[1] = sl;
+            e[2] = i;
+            e[3] = (P > 1 && k > 0) ? s_slot0[i] + k - 1 : -1;
+            e[4] = k == P - 1 ? 1 : 0;
+            e[5] = -1;
+            if (P > 1 && k < P - 1) {
+                int32_t* so = sonly + kPlanEntry * (s_slot0[i] + k);
+                so[0] = st;
+                so[1] = sl;
+                so[2] = i;
+                so[3] = -1;
+                so[4] = 0;
+                so[5] = s_slot0[i] + k;
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1211,12 +1353,23 @@ hipError_t launch_decode(const DecodeParams& p, int in_dtype, hipStream_t s) {
     }
 }
 
-hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, float* final_state, const float* g_gamma,
-                           int B, int H, int P, int seg_len, int seqlen, int64_t elems, bool rev, hipStream_t s) {
+hipError_t launch_seg_scan(const int32_t* plan, int plan_main, int plan_slots, int max_seqs, float* slots,
+                           const float* init, const float* g_gamma, int B, int H, int P, int seg_len, int64_t elems,
+                           hipStream_t s) {
     const int elems4 = (int)(elems / 4);
-    const dim3 grid((elems4 + 255) / 256, (unsigned)(B * H));
-    hipLaunchKernelGGL(seg_scan_kernel, grid, dim3(256), 0, s, dS, init, s_in, final_state, g_gamma, H, P, seg_len,
-                       seqlen, elems4, rev ? 1 : 0);
+    const int rows = plan ? max_seqs : B;
+    if (rows <= 0 || elems4 == 0) return hipSuccess;
+    const dim3 grid((elems4 + 255) / 256, (unsigned)(rows * H));
+    hipLaunchKernelGGL(seg_scan_kernel, grid, dim3(256), 0, s, plan, plan_main, plan_slots, slots, init, g_gamma, H, P,
+                       seg_len, elems4);
+    return hipGetLastError();
+}
+
+hipError_t launch_split_plan(const int32_t* cu, int num_seqs, int seqlen, int wgs_per_seq, int min_seg_chunks,
+                             int forced, bool reverse, int max_main, int max_slots, int32_t* plan, hipStream_t s) {
+    if (num_seqs < 1 || num_seqs > kMaxPlanSeqs) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(1024), 0, s, cu, num_seqs, seqlen, wgs_per_seq, min_seg_chunks,
+                       forced, reverse ? 1 : 0, max_main, max_slots, plan);
     return hipGetLastError();
 }
 

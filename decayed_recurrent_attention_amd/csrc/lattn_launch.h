@@ -15,6 +15,21 @@ constexpr int kNumXcd = 8;
 // Largest packed sequence count that the longest-first ordering kernel handles
 // (its lengths live in LDS); above it sequences run in their given order.
 constexpr int kMaxOrderedSeqs = 16384;
+// Compute units of MI355X: the intra-sequence split balances its work over them.
+constexpr int kNumCu = 256;
+// Largest packed sequence count that the split planner handles (one workgroup, its
+// tables in LDS); above it packed input is not split.
+constexpr int kMaxPlanSeqs = 1024;
+// Packed-split plan in the workspace (int32 words): a header, then the main pass's
+// segments (longest first), the state-only pass's segments, and the split sequences
+// that the scan chains.  Segment entries are kPlanEntry words: first row, length,
+// sequence, state slot read as the segment's initial state (-1: the sequence's own),
+// 1 if the segment writes the sequence's final state, state slot written by the
+// state-only pass.  Scan entries are kPlanScan words: sequence, first slot,
+// segments, segment length in tokens.
+constexpr int kPlanHeader = 8;  // main count, state-only count, scan count
+constexpr int kPlanEntry = 8;
+constexpr int kPlanScan = 4;
 
 // Everything one forward launch needs.  Sizes are element counts.
 struct FwdParams {
@@ -49,17 +64,30 @@ struct FwdParams {
     float final_mul;  // final_state = final_mul * S (default 1) ...
     int final_lam;    // ... times exp(g_gamma[h]) when set and the sequence is not empty
                       //    (default 0); final_state may be null
-    int seg_count;    // > 0: sequence n is segment n % seg_count of batch row n / seg_count,
-    int seg_len;      //    positions [s * seg_len, min((s + 1) * seg_len, seqlen)) (default 0)
+    // Intra-sequence split (default 0 / null: off).  Segments are numbered in
+    // processing order: segment k of a sequence of length L covers positions
+    // [k * seg_len, min((k + 1) * seg_len, L)) forward, the mirror image in reverse,
+    // so only the last processed segment can be short.  The state-only pass writes
+    // segment k's own contribution to state slot k of its sequence (k < P - 1); the
+    // scan turns slot k into the state entering segment k + 1, in place; the main
+    // pass starts segment 0 from the sequence's initial state, segment k > 0 from
+    // slot k - 1, and the last segment writes the final state.
+    int seg_phase;    // 1: the state-only pass; 2: the main pass (with seg_count or plan)
+    int seg_count;    // fixed length: P segments per batch row (every row alike)
+    int seg_len;      // fixed length: segment length in tokens (a multiple of the chunk)
+    const int32_t* plan;  // packed input: the plan (kPlanHeader ... above)
+    int plan_main;        // capacity of the plan's main-pass list (entries)
+    int plan_slots;       // capacity of its state-only list and of the state slots
+    float* slots;         // state slots [slots][H][dk][dv]
     int o_bf16;       // 1: o holds bf16, each the round-to-nearest-even of the fp32 result
                       //    (bf16-input chunked kernel only; default 0: fp32)
     // Gated recurrence only (gated kernels): the key log-decay gate g [B, T, H, dk] and
     // the value gate gv [B, T, H, dv], in the input dtype (g in fp32 when gk_is_f32:
-    // the sum of two key gates), or null; the direction.
+    // the sum of two key gates), or null.
     const void* g;
     const void* gv;
     int gk_is_f32;
-    int reverse_gated;
+    int reverse;  // 1: positions descending (the gated kernels and the fixed-length split read it)
 };
 
 // Kernel arguments of the forward kernels: one problem, or two of the same shape
@@ -77,11 +105,16 @@ inline void set_forward_defaults(FwdParams& p) {
     p.init_at_end = 0;
     p.final_mul = 1.f;
     p.final_lam = 0;
+    p.seg_phase = 0;
     p.seg_count = 0;
     p.seg_len = 0;
+    p.plan = nullptr;
+    p.plan_main = 0;
+    p.plan_slots = 0;
+    p.slots = nullptr;
     p.g = p.gv = nullptr;
     p.gk_is_f32 = 0;
-    p.reverse_gated = 0;
+    p.reverse = 0;
 }
 
 // Workgroups of 64 * nw threads own BV = 16 * nw value columns each.
@@ -101,10 +134,19 @@ bool have_gated_kernel(int dk, int nw);
 // out = g + gk in fp32 (n elements, a multiple of 4; inputs in in_dtype).
 hipError_t launch_gate_sum(const void* g, const void* gk, float* out, int64_t n, int in_dtype, hipStream_t stream);
 hipError_t launch_gated(const FwdParams& p, int in_dtype, int nw, hipStream_t stream);
-// Chain per-segment state contributions (intra-sequence split); see seg_scan_kernel.
-hipError_t launch_seg_scan(const float* dS, const float* init, float* s_in, float* final_state,
-                           const float* g_gamma, int B, int H, int P, int seg_len, int seqlen,
-                           int64_t elems, bool rev, hipStream_t stream);
+// Intra-sequence split, chaining step: turn each split sequence's state slots (its
+// segments' own contributions) into the states entering its segments, in place; see
+// seg_scan_kernel.  Fixed length (plan == nullptr): B rows of P segments of seg_len
+// tokens, slots b * (P - 1) + k.  Packed: the plan's scan list (at most max_seqs entries;
+// plan_main and plan_slots are the capacities of the plan's two segment lists).
+hipError_t launch_seg_scan(const int32_t* plan, int plan_main, int plan_slots, int max_seqs, float* slots,
+                           const float* init, const float* g_gamma, int B, int H, int P, int seg_len, int64_t elems,
+                           hipStream_t stream);
+// Packed split plan: cut the sequences of cu_seqlens into segments (see
+// split_plan_kernel) and write the plan.  wgs_per_seq: workgroups per segment;
+// forced > 1: cut every sequence into that many segments (tests); else balance.
+hipError_t launch_split_plan(const int32_t* cu, int num_seqs, int seqlen, int wgs_per_seq, int min_seg_chunks,
+                             int forced, bool reverse, int max_main, int max_slots, int32_t* plan, hipStream_t stream);
 // out[r, j, :] = sum over g < G of part[r, j * G + g, :] for rows r < rows, j < Hkv,
 // with G = H / Hkv and d a multiple of 4.
 hipError_t launch_group_sum(const float* part, float* out, int64_t rows, int H, int Hkv, int d,

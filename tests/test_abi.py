@@ -211,17 +211,18 @@ def test_decode_pointer_errors():
 
 
 def test_split_workspace():
-    """Few (row, head) pairs of a long fixed-length bf16 input: split along the sequence."""
+    """Few (row, head) pairs of a long fixed-length bf16 input: split along the sequence.
+    The workspace holds one float32 state per segment but each row's last."""
     prob = P(batch=1, seqlen=32768, num_heads=8, num_kv_heads=8, head_dim_qk=128, head_dim_v=128)
     # widest workgroups: 8 heads x 2 value blocks = 16 -> 16 segments of 2048 tokens
-    assert lattn.lattn_fwd_workspace_size(prob) == 2 * 16 * 8 * 128 * 128 * 4
+    assert lattn.lattn_fwd_workspace_size(prob) == 15 * 8 * 128 * 128 * 4
     assert call(prob) == lattn.LATTN_ERR_WORKSPACE
     # a bf16 o splits the same way (the split states are float32)
     prob_b = P(batch=1, seqlen=32768, num_heads=8, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
                out_dtype=lattn.LATTN_BF16)
-    assert lattn.lattn_fwd_workspace_size(prob_b) == 2 * 16 * 8 * 128 * 128 * 4
+    assert lattn.lattn_fwd_workspace_size(prob_b) == 15 * 8 * 128 * 128 * 4
     assert call(prob_b) == lattn.LATTN_ERR_WORKSPACE
-    # enough pairs, short sequences, fp32 and packed input never split
+    # enough pairs, short sequences and fp32 never split
     assert lattn.lattn_fwd_workspace_size(P(batch=4, seqlen=32768, num_heads=32, head_dim_qk=128,
                                             head_dim_v=128)) == 0
     # too short for two segments: fewer than 8 chunks at dk <= 128, 32 above
@@ -230,16 +231,47 @@ def test_split_workspace():
                                             head_dim_qk=192, head_dim_v=64)) == 0
     # short segments (4 chunks) at dk 64: B1 H2 N1500 -> 5 segments of 320 tokens
     assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=1500, num_heads=2, num_kv_heads=2)) == \
-        2 * 5 * 2 * 64 * 64 * 4
+        4 * 2 * 64 * 64 * 4
     assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=32768, num_heads=2, num_kv_heads=2,
                                             in_dtype=lattn.LATTN_F32)) == 0
     small = P(batch=2, seqlen=1000, num_heads=4, num_kv_heads=4)
     with lattn.knob(lattn.LATTN_KNOB_SPLIT, 3):
-        # 16 chunks in 3 segments of 6 chunks (384 tokens)
-        assert lattn.lattn_fwd_workspace_size(small) == 2 * 2 * 3 * 4 * 64 * 64 * 4
+        # 16 chunks in 3 segments of 6 chunks (384 tokens): 2 rows x 2 slots
+        assert lattn.lattn_fwd_workspace_size(small) == 2 * 2 * 4 * 64 * 64 * 4
     with lattn.knob(lattn.LATTN_KNOB_SPLIT, 0):
         assert lattn.lattn_fwd_workspace_size(prob) == 0
-    assert lattn.lattn_fwd_workspace_size(prob) == 2 * 16 * 8 * 128 * 128 * 4  # restored
+    assert lattn.lattn_fwd_workspace_size(prob) == 15 * 8 * 128 * 128 * 4  # restored
+
+
+def _packed_split_bytes(num_seqs, H, dk, dv, slots):
+    """Plan (header, main and state-only lists of 8 words, scan list of 4) + state slots."""
+    words = 8 + 8 * (num_seqs + slots + slots) + 4 * slots
+    plan = -(-words * 4 // 256) * 256
+    return plan + -(-slots * H * dk * dv * 4 // 256) * 256
+
+
+def test_packed_split_workspace():
+    """Packed bf16 input with fewer than 256 workgroups per segment gets the planner's
+    workspace: at most 2 * ceil(256 / J) + 2 state slots for J workgroups per segment."""
+    # the packed GQA workload: 16 heads x 2 value blocks = 32 workgroups -> 18 slots
+    prob = P(batch=1, seqlen=70477, num_seqs=16, num_heads=16, num_kv_heads=4, head_dim_qk=128, head_dim_v=128)
+    assert lattn.lattn_fwd_workspace_size(prob) == _packed_split_bytes(16, 16, 128, 128, 18)
+    assert lattn.lattn_fwd_workspace_size(prob) <= lattn.LATTN_NOALLOC_SCRATCH_BYTES
+    # forced: every sequence in at most 3 segments -> 2 slots per sequence
+    with lattn.knob(lattn.LATTN_KNOB_SPLIT, 3):
+        assert lattn.lattn_fwd_workspace_size(prob) == _packed_split_bytes(16, 16, 128, 128, 32)
+    # the knob at 0 turns the planner off: the longest-first order only
+    with lattn.knob(lattn.LATTN_KNOB_SPLIT, 0):
+        assert lattn.lattn_fwd_workspace_size(prob) == 256
+    # 256 workgroups per segment or more: nothing can exceed the balanced load
+    wide = P(batch=1, seqlen=5000, num_seqs=7, num_heads=128, num_kv_heads=128, head_dim_qk=128, head_dim_v=128)
+    assert lattn.lattn_fwd_workspace_size(wide) == 256
+    # more sequences than the planner holds, or fp32 input: the order only
+    many = P(batch=1, seqlen=5000, num_seqs=1025, num_heads=4, num_kv_heads=4)
+    assert lattn.lattn_fwd_workspace_size(many) == -(-1025 * 4 // 256) * 256
+    f32 = P(batch=1, seqlen=5000, num_seqs=7, num_heads=4, num_kv_heads=4, head_dim_qk=32, head_dim_v=32,
+            in_dtype=lattn.LATTN_F32)
+    assert lattn.lattn_fwd_workspace_size(f32) == 256
 
 
 def test_knobs():

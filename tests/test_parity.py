@@ -261,3 +261,44 @@ def test_library_is_the_one_loaded():
     """The HIP library in the package directory is what runs (no fallback)."""
     lib = lattn.load_library()
     assert os.path.samefile(lib._name, lattn.LIB_PATH)
+
+
+# -- packed input split along its sequences (device-planned segments) -----------------------
+@pytest.mark.parametrize("reverse", [False, True])
+def test_packed_split_forced(reverse, knobs):
+    """Every sequence of at least two chunks cut into up to 3 segments: empty, short and
+    ragged sequences, GQA, dk != dv, an initial state, both directions."""
+    knobs(lattn.LATTN_KNOB_SPLIT, 3)
+    lens = [0, 1, 63, 64, 65, 127, 200, 2, 0, 129, 700, 1000]
+    w = inputs.Workload("packed_split3", 1, sum(lens), 8, 2, 128, 64, "bf16", 3, 12, reverse=reverse,
+                        seq_lens=lens, init_std=0.3, seed=81)
+    _compare(w, w.make(), tag=" rev" if reverse else "")
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_packed_split_skewed_automatic(reverse):
+    """One long sequence among short ones: the planner cuts the long one (its chunks exceed
+    the balanced load per compute unit) and leaves the rest whole."""
+    lens = [9000, 70, 130, 64, 1, 300, 0, 250, 90, 128]
+    w = inputs.Workload("packed_skewed", 1, sum(lens), 4, 2, 128, 128, "bf16", 2, 12, reverse=reverse,
+                        seq_lens=lens, init_std=0.2, seed=82)
+    prob = lattn.LattnProblem(1, w.seqlen, 4, 2, 128, 128, len(lens), lattn.LATTN_BF16, lattn.LATTN_F32)
+    assert lattn.lattn_fwd_workspace_size(prob) > 4096, "expected the planner's workspace"
+    _compare(w, w.make(), tag=" rev" if reverse else "")
+
+
+def test_packed_split_matches_unsplit(knobs):
+    """The split and unsplit packed runs agree to rounding (different summation order)."""
+    lens = [5000, 40, 700, 3, 1200]
+    w = inputs.Workload("packed_split_vs", 1, sum(lens), 4, 4, 64, 64, "bf16", 5, 12, seq_lens=lens,
+                        init_std=0.5, seed=83)
+    data = w.make()
+    knobs(lattn.LATTN_KNOB_SPLIT, 0)
+    o0, f0 = gpu_run(w, data)
+    knobs(lattn.LATTN_KNOB_SPLIT, lattn.LATTN_KNOB_AUTO)
+    o1, f1 = gpu_run(w, data)
+    knobs(lattn.LATTN_KNOB_SPLIT, 6)
+    o2, f2 = gpu_run(w, data)
+    for o, f in ((o1, f1), (o2, f2)):
+        assert float((o0 - o).abs().max()) <= 1e-4 * float(o0.abs().max())
+        assert float((f0 - f).abs().max()) <= 1e-4 * float(f0.abs().max())
