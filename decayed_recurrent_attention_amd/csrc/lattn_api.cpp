@@ -167,16 +167,14 @@ struct Split {
     int max_main = 0;     // packed: capacity of the main-pass list
 };
 
-// Shortest segment worth a state-only pass and a scan: 4 chunks up to dk 128, 16 above
-// (those cost more at dk 192 and 256).  Measured (one box): B2 H8 d64 N2048 ran 23 us
-// in 8 segments against 41 us in 2 and 57 us unsplit; B2 H12 d192 N2048 ran 75 us in 2
-// segments and 84 us in 4.
-int min_seg_chunks(int dk) { return dk <= 128 ? 4 : 16; }
+// Shortest segment worth a state-only pass and a scan: 4 chunks up to dk 128, 8 above
+// (those cost more at dk 192 and 256).
+int min_seg_chunks(int dk) { return dk <= 128 ? 4 : 8; }
 
 Split choose_split(const lattn_problem& p, int nw) {
     Split sp;
     if (is_varlen(p) || p.in_dtype != LATTN_BF16 || p.seqlen < 2 * lattn::kChunk) return sp;
-    if ((int64_t)p.batch * p.num_heads > 65535) return sp;  // the scan's grid rows
+    if ((int64_t)p.batch * p.num_heads * 64 > INT_MAX) return sp;  // the scan's grid
     const int64_t wgs = (int64_t)p.batch * p.num_heads * (p.head_dim_v / (16 * nw));
     int want;
     if (const int forced = knob(LATTN_KNOB_SPLIT); forced != LATTN_KNOB_AUTO) {  // forced segment count
@@ -184,7 +182,12 @@ Split choose_split(const lattn_problem& p, int nw) {
         if (want < 2) return sp;
     } else {
         if (wgs >= 128) return sp;  // at least half the compute units busy already
-        want = (int)((256 + wgs - 1) / wgs);
+        // As many segments as keep the main pass to one workgroup per compute unit: a
+        // second round costs more than the parallelism gains.  Measured (one box, us,
+        // by segment count): B2 H12 d192 N2048 (72 workgroups) 93 / 75 / 60 / 75 for
+        // 1 / 2 / 3 / 4; B2 H8 d256 N4096 (64) 206 / 153 / 114 / 94 / 100 for 1 / 2 / 3 /
+        // 4 / 8; B2 H8 d64 N2048 (16) 58 / 42 / 25 / 26 for 1 / 2 / 8 / 16.
+        want = (int)std::max<int64_t>(2, lattn::kNumCu / wgs);
         const int cap = p.seqlen / (min_seg_chunks(p.head_dim_qk) * lattn::kChunk);
         if (want > cap) want = cap;
         if (want < 2) return sp;
@@ -214,7 +217,7 @@ Split choose_packed_split(const lattn_problem& p, int nw) {
     sp.min_seg = min_seg_chunks(p.head_dim_qk);
     const int64_t slots = sp.forced ? (int64_t)p.num_seqs * (sp.forced - 1)
                                     : 2 * ((lattn::kNumCu + wgs - 1) / wgs) + 2;
-    if (slots < 1 || slots * p.num_heads > 65535 || slots + p.num_seqs > INT_MAX / 64) return Split{};
+    if (slots < 1 || slots * p.num_heads * 4 > INT_MAX || slots + p.num_seqs > INT_MAX / 64) return Split{};
     sp.max_slots = (int)slots;
     sp.max_main = p.num_seqs + sp.max_slots;
     return sp;

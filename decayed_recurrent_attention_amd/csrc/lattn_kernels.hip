@@ -33,6 +33,8 @@
 // The state is kept in fp32 and fed to the Q S product as bf16 hi + lo (two MFMAs),
 // and so is the masked intra-chunk matrix P in P V, so that neither rounding reaches
 // the output; o and the states are fp32.
+#include <algorithm>
+
 #include "lattn_device.h"
 
 namespace lattn {
@@ -991,15 +993,16 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 //     S_{k+1} = lam^{len_k} S_k + dS_k,
 // and slot k is overwritten by S_{k+1} (in place: each element is read before it
 // is written).  Every segment but the last has the same length seg_len.  One thread
-// per 4 state elements; blockIdx.y = (split sequence j, head h).
+// per 4 state elements; blockIdx.x = ((split sequence j) * H + head h) * eblocks + eb,
+// each block looping over every eblocks-th group of 256 float4 of the head's block
+// (few blocks per row keep a plan without split sequences cheap).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void seg_scan_kernel(const int32_t* __restrict__ plan, int plan_main, int plan_slots,
                                                        float* __restrict__ slots, const float* __restrict__ init,
                                                        const float* __restrict__ g_gamma, int H, int P_fixed,
-                                                       int seg_len_fixed, int elems4) {
-    const int e4 = blockIdx.x * blockDim.x + threadIdx.x;
-    if (e4 >= elems4) return;
-    const int j = blockIdx.y / H, h = blockIdx.y % H;
+                                                       int seg_len_fixed, int elems4, int eblocks) {
+    const int eb = blockIdx.x % eblocks, row = blockIdx.x / eblocks;
+    const int j = row / H, h = row % H;
     int n, slot0, P, seg_len;
     if (plan) {
         if (j >= plan[2]) return;
@@ -1016,12 +1019,15 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const int32_t* __restrict
     }
     const int64_t elems = (int64_t)elems4 * 4;
     const float lam_seg = exp2f(g_gamma[h] * kLog2e * (float)seg_len);
-    f32x4 S = {0.f, 0.f, 0.f, 0.f};
-    if (init) S = *reinterpret_cast<const f32x4*>(init + ((int64_t)n * H + h) * elems + 4 * e4);
-    for (int k = 0; k + 1 < P; ++k) {
-        f32x4* at = reinterpret_cast<f32x4*>(slots + ((int64_t)(slot0 + k) * H + h) * elems + 4 * e4);
-        S = lam_seg * S + *at;
-        *at = S;
+    const float* ib = init ? init + ((int64_t)n * H + h) * elems : nullptr;
+    for (int e4 = eb * blockDim.x + threadIdx.x; e4 < elems4; e4 += eblocks * blockDim.x) {
+        f32x4 S = {0.f, 0.f, 0.f, 0.f};
+        if (ib) S = *reinterpret_cast<const f32x4*>(ib + 4 * e4);
+        for (int k = 0; k + 1 < P; ++k) {
+            f32x4* at = reinterpret_cast<f32x4*>(slots + ((int64_t)(slot0 + k) * H + h) * elems + 4 * e4);
+            S = lam_seg * S + *at;
+            *at = S;
+        }
     }
 }
 
@@ -1359,9 +1365,12 @@ hipError_t launch_seg_scan(const int32_t* plan, int plan_main, int plan_slots, i
     const int elems4 = (int)(elems / 4);
     const int rows = plan ? max_seqs : B;
     if (rows <= 0 || elems4 == 0) return hipSuccess;
-    const dim3 grid((elems4 + 255) / 256, (unsigned)(rows * H));
+    // fixed length: every row is split, one block per 256 float4; packed: few blocks per
+    // row, most of which find no split sequence and exit
+    const int eblocks = plan ? 4 : std::max(1, std::min(64, (elems4 + 255) / 256));
+    const dim3 grid((unsigned)rows * (unsigned)H * (unsigned)eblocks);
     hipLaunchKernelGGL(seg_scan_kernel, grid, dim3(256), 0, s, plan, plan_main, plan_slots, slots, init, g_gamma, H, P,
-                       seg_len, elems4);
+                       seg_len, elems4, eblocks);
     return hipGetLastError();
 }
 

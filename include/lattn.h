@@ -69,13 +69,20 @@ typedef struct {
 } lattn_problem;
 
 /*
- * Device workspace (bytes) that lattn_fwd needs for problem *p.  Packed input needs
- * room for the longest-first sequence order.  Fixed-length bf16 input with too few
- * (batch row, head) pairs to fill the GPU is split along the sequence (each row cut
- * into segments that run in parallel, chained through their states) and needs two
- * float32 states per segment: 2 * B * P * H * dk * dv * 4 bytes for P segments.
- * Otherwise 0.  The knob LATTN_KNOB_SPLIT (lattn_set_knob) changes the segment count.
- * Returns 0 also for an invalid problem (lattn_fwd then reports it).
+ * Device workspace (bytes) that lattn_fwd needs for problem *p.  Sequences may be cut
+ * into segments that run in parallel, chained through their states (a state-only
+ * pass, a scan, then the main pass), when that fills the GPU better:
+ *  - fixed-length bf16 input with too few (batch row, head) pairs to fill the GPU:
+ *    every row in P segments, one float32 state per segment but the last:
+ *    B * (P - 1) * H * dk * dv * 4 bytes;
+ *  - packed bf16 input (at most 1024 sequences, fewer than 256 workgroups per
+ *    sequence): a plan made on the device from cu_seqlens cuts the sequences longer
+ *    than the balanced load per compute unit; the workspace holds the plan and at
+ *    most 2 * ceil(256 / J) + 2 float32 states per head (J = workgroups per segment).
+ * Other packed input needs room for the longest-first sequence order; other
+ * fixed-length input needs none.  The knob LATTN_KNOB_SPLIT (lattn_set_knob)
+ * changes the segment count.  Returns 0 also for an invalid problem (lattn_fwd then
+ * reports it).
  */
 size_t lattn_fwd_workspace_size(const lattn_problem* p);
 

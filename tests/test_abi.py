@@ -225,10 +225,13 @@ def test_split_workspace():
     # enough pairs, short sequences and fp32 never split
     assert lattn.lattn_fwd_workspace_size(P(batch=4, seqlen=32768, num_heads=32, head_dim_qk=128,
                                             head_dim_v=128)) == 0
-    # too short for two segments: fewer than 8 chunks at dk <= 128, 32 above
+    # too short for two segments: fewer than 8 chunks at dk <= 128, 16 above
     assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=500, num_heads=2, num_kv_heads=2)) == 0
-    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=2000, num_heads=2, num_kv_heads=2,
+    assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=1000, num_heads=2, num_kv_heads=2,
                                             head_dim_qk=192, head_dim_v=64)) == 0
+    # the d192 workload (72 workgroups): 3 segments fill one round of 256, 4 would not
+    d192 = P(batch=2, seqlen=2048, num_heads=12, num_kv_heads=12, head_dim_qk=192, head_dim_v=192)
+    assert lattn.lattn_fwd_workspace_size(d192) == 2 * 2 * 12 * 192 * 192 * 4
     # short segments (4 chunks) at dk 64: B1 H2 N1500 -> 5 segments of 320 tokens
     assert lattn.lattn_fwd_workspace_size(P(batch=1, seqlen=1500, num_heads=2, num_kv_heads=2)) == \
         4 * 2 * 64 * 64 * 4
