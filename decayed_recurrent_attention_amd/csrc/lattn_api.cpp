@@ -203,7 +203,8 @@ Split choose_split(const lattn_problem& p, int nw) {
 // Packed input: the planner's bounds.  Balanced mode cuts sequences longer than 5/4 of
 // Lb = J * sum(chunks) / kNumCu into segments of at least Lb / 2 chunks, so at most
 // 2 kNumCu / J + 1 state slots are used (J = workgroups per segment); forced mode
-// cuts every sequence into at most `forced` segments.
+// cuts every sequence into at most `forced` segments.  The planner lists at most
+// kMaxPlanSegs segments.
 Split choose_packed_split(const lattn_problem& p, int nw) {
     Split sp;
     if (!is_varlen(p) || p.in_dtype != LATTN_BF16 || p.num_seqs > lattn::kMaxPlanSeqs) return sp;
@@ -217,7 +218,7 @@ Split choose_packed_split(const lattn_problem& p, int nw) {
     sp.min_seg = min_seg_chunks(p.head_dim_qk);
     const int64_t slots = sp.forced ? (int64_t)p.num_seqs * (sp.forced - 1)
                                     : 2 * ((lattn::kNumCu + wgs - 1) / wgs) + 2;
-    if (slots < 1 || slots * p.num_heads * 4 > INT_MAX || slots + p.num_seqs > INT_MAX / 64) return Split{};
+    if (slots < 1 || slots + p.num_seqs > lattn::kMaxPlanSegs) return Split{};  // the planner's segment table
     sp.max_slots = (int)slots;
     sp.max_main = p.num_seqs + sp.max_slots;
     return sp;
@@ -245,8 +246,7 @@ size_t state_block_bytes(const lattn_problem& p) {
 // Workspace of a split forward: [plan (packed only)][state slots], each 256-byte aligned.
 size_t split_plan_bytes(const Split& sp) {
     if (!sp.packed) return 0;
-    const size_t words = lattn::kPlanHeader + (size_t)lattn::kPlanEntry * (sp.max_main + sp.max_slots) +
-                         (size_t)lattn::kPlanScan * sp.max_slots;
+    const size_t words = lattn::kPlanHeader + (size_t)lattn::kPlanEntry * (sp.max_main + sp.max_slots);
     return round_up(words * sizeof(int32_t), 256);
 }
 size_t split_slot_count(const lattn_problem& p, const Split& sp) {
@@ -389,9 +389,8 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
             return LATTN_ERR_LAUNCH;
         if (n_sonly > 0 && lattn::launch_fwd(f1, p->in_dtype, nw, reverse != 0, s, true) != hipSuccess)
             return LATTN_ERR_LAUNCH;
-        if (lattn::launch_seg_scan(plan, sp.max_main, sp.max_slots, sp.max_slots, slots, initial_state, g_gamma,
-                                   p->batch, p->num_heads, sp.P, sp.seg_len,
-                                   (int64_t)p->head_dim_qk * p->head_dim_v, s) != hipSuccess)
+        if (!sp.packed && lattn::launch_seg_scan(slots, initial_state, g_gamma, p->batch, p->num_heads, sp.P,
+                                                 sp.seg_len, (int64_t)p->head_dim_qk * p->head_dim_v, s) != hipSuccess)
             return LATTN_ERR_LAUNCH;
         if (lattn::launch_fwd(f3, p->in_dtype, nw, reverse != 0, s) != hipSuccess) return LATTN_ERR_LAUNCH;
         return LATTN_OK;

@@ -28,6 +28,11 @@ struct Work {
     int64_t len;    // tokens in the work
     const float* init_blk;  // this head's initial state block [dk][dv], or null (zeros)
     float* fin_blk;         // where this head's final state block goes, or null (nowhere)
+    // Packed split: the initial state is lam^chain_len applied to the state above plus
+    // the `chain` state blocks at chain_blk, chain_blk + H dk dv, ... in turn.
+    const float* chain_blk;
+    int chain;
+    int chain_len;
 };
 
 // Work id (normally the workgroup id) -> work.  Groups are (sequence rank, kv head); the workgroups of one
@@ -47,6 +52,9 @@ __device__ inline bool decode_work(const FwdParams& p, int id, Work& w) {
     w.vb = j % p.nvb;
     const int H = p.num_heads;
     const int64_t blk = (int64_t)p.dk * p.dv;  // elements of one head's state block
+    w.chain_blk = nullptr;
+    w.chain = 0;
+    w.chain_len = 0;
     if (p.plan) {  // packed split: the plan's entry of this rank
         const int count = p.plan[p.seg_phase == 1 ? 1 : 0];
         if (rank >= count) return false;
@@ -56,11 +64,15 @@ __device__ inline bool decode_work(const FwdParams& p, int id, Work& w) {
         w.len = e[1];
         if (p.seg_phase == 1) {
             w.init_blk = nullptr;
-            w.fin_blk = p.slots + ((int64_t)e[5] * H + w.h) * blk;
+            w.fin_blk = p.slots + ((int64_t)e[7] * H + w.h) * blk;
         } else {
-            w.init_blk = e[3] >= 0 ? p.slots + ((int64_t)e[3] * H + w.h) * blk
-                                   : (p.init ? p.init + ((int64_t)w.n * H + w.h) * blk : nullptr);
-            w.fin_blk = (e[4] && p.final_state) ? p.final_state + ((int64_t)w.n * H + w.h) * blk : nullptr;
+            w.init_blk = p.init ? p.init + ((int64_t)w.n * H + w.h) * blk : nullptr;
+            w.fin_blk = (e[5] && p.final_state) ? p.final_state + ((int64_t)w.n * H + w.h) * blk : nullptr;
+            if (e[3] >= 0 && e[4] > 0) {
+                w.chain_blk = p.slots + ((int64_t)e[3] * H + w.h) * blk;
+                w.chain = e[4];
+                w.chain_len = e[6];
+            }
         }
         return true;
     }

@@ -335,6 +335,32 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 S[mt][ii] = p.init_mul * buf_load_f32(ri, (dmap(wd * MTL + mt, 4 * lg + ii) * rs + gcol * cs) * 4);
+        // Packed split: chain the earlier segments' own contributions into the state
+        // entering this one (their slots hold [dk][dv] blocks, H heads apart).
+        // Four slots' loads go out together before they are added in order.
+        if (wk.chain > 0) {
+            const float lam_seg = exp2f(g2 * (float)wk.chain_len);
+            for (int j0 = 0; j0 < wk.chain; j0 += 4) {
+                f32x4 blk4[4][MTL];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool real = j0 + u < wk.chain;
+                    const auto rj = make_rsrc(real ? wk.chain_blk + (int64_t)(j0 + u) * H * DK * dv : wk.chain_blk,
+                                              real ? (uint32_t)(DK * dv * 4) : 0u);
+#pragma unroll
+                    for (int mt = 0; mt < MTL; ++mt)
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii)
+                            blk4[u][mt][ii] = buf_load_f32(rj, (dmap(wd * MTL + mt, 4 * lg + ii) * dv + gcol) * 4);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (j0 + u < wk.chain) {
+#pragma unroll
+                        for (int mt = 0; mt < MTL; ++mt) S[mt] = lam_seg * S[mt] + blk4[u][mt];
+                    }
+            }
+        }
     }
     bf16x8 Shi[KBL], Slo[KBL];
     split_state<KBL>(S, Shi, Slo);
@@ -986,45 +1012,30 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Intra-sequence split, chaining step.  A split sequence of P segments owns state
-// slots k = 0 .. P-2, which the state-only pass filled with segment k's own
-// contribution dS_k (from a zero state).  In processing order, with S the state
-// entering segment k (S_0 the sequence's initial state or zeros),
-//     S_{k+1} = lam^{len_k} S_k + dS_k,
-// and slot k is overwritten by S_{k+1} (in place: each element is read before it
-// is written).  Every segment but the last has the same length seg_len.  One thread
-// per 4 state elements; blockIdx.x = ((split sequence j) * H + head h) * eblocks + eb,
-// each block looping over every eblocks-th group of 256 float4 of the head's block
-// (few blocks per row keep a plan without split sequences cheap).
+// Intra-sequence split of fixed-length input, chaining step.  Row b (P segments of
+// seg_len tokens, the last possibly shorter) owns state slots b (P - 1) + k, k < P - 1,
+// which the state-only pass filled with segment k's own contribution dS_k (from a zero
+// state).  In processing order, with S the state entering segment k (S_0 the row's
+// initial state or zeros),
+//     S_{k+1} = lam^{seg_len} S_k + dS_k,
+// and slot k is overwritten by S_{k+1} (in place: each element is read before it is
+// written).  One thread per 4 state elements; blockIdx.x = (row b * H + head h) *
+// eblocks + eb, each block looping over every eblocks-th group of 256 float4.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void seg_scan_kernel(const int32_t* __restrict__ plan, int plan_main, int plan_slots,
-                                                       float* __restrict__ slots, const float* __restrict__ init,
-                                                       const float* __restrict__ g_gamma, int H, int P_fixed,
-                                                       int seg_len_fixed, int elems4, int eblocks) {
+__global__ __launch_bounds__(256) void seg_scan_kernel(float* __restrict__ slots, const float* __restrict__ init,
+                                                       const float* __restrict__ g_gamma, int H, int P, int seg_len,
+                                                       int elems4, int eblocks) {
     const int eb = blockIdx.x % eblocks, row = blockIdx.x / eblocks;
-    const int j = row / H, h = row % H;
-    int n, slot0, P, seg_len;
-    if (plan) {
-        if (j >= plan[2]) return;
-        const int32_t* e = plan + kPlanHeader + kPlanEntry * (plan_main + plan_slots) + kPlanScan * j;
-        n = e[0];
-        slot0 = e[1];
-        P = e[2];
-        seg_len = e[3];
-    } else {
-        n = j;
-        slot0 = j * (P_fixed - 1);
-        P = P_fixed;
-        seg_len = seg_len_fixed;
-    }
+    const int b = row / H, h = row % H;
     const int64_t elems = (int64_t)elems4 * 4;
     const float lam_seg = exp2f(g_gamma[h] * kLog2e * (float)seg_len);
-    const float* ib = init ? init + ((int64_t)n * H + h) * elems : nullptr;
+    const float* ib = init ? init + ((int64_t)b * H + h) * elems : nullptr;
+    const int64_t slot0 = (int64_t)b * (P - 1);
     for (int e4 = eb * blockDim.x + threadIdx.x; e4 < elems4; e4 += eblocks * blockDim.x) {
         f32x4 S = {0.f, 0.f, 0.f, 0.f};
         if (ib) S = *reinterpret_cast<const f32x4*>(ib + 4 * e4);
         for (int k = 0; k + 1 < P; ++k) {
-            f32x4* at = reinterpret_cast<f32x4*>(slots + ((int64_t)(slot0 + k) * H + h) * elems + 4 * e4);
+            f32x4* at = reinterpret_cast<f32x4*>(slots + ((slot0 + k) * H + h) * elems + 4 * e4);
             S = lam_seg * S + *at;
             *at = S;
         }
@@ -1032,131 +1043,134 @@ __global__ __launch_bounds__(256) void seg_scan_kernel(const int32_t* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// Packed-split planner (one workgroup): cut the packed sequences into segments so
-// that the longest ones no longer set the length of the call.  With c_n the chunks
-// of sequence n, J workgroups per segment and kNumCu compute units, the balanced
-// load per compute unit is Lb = J * sum(c_n) / kNumCu chunks.  A sequence longer
-// than 5/4 Lb (the state-only pass and scan cost about a quarter of a segment) is
-// cut into segments of S = max(min_seg, ceil(Lb / 2)) chunks; with `forced` > 1
-// every sequence of at least two chunks is cut into min(forced, c_n) segments.
-// Sequences whose slots would pass max_slots stay whole.  Writes the main pass's
-// segments longest first (ties by sequence, then segment), the state-only pass's
-// segments, and the scan list (layout in lattn_launch.h).  Segments are numbered
-// in processing order (mirrored positions in reverse), so only a sequence's last
-// segment can be short.
+// Packed-split planner (one workgroup, a thread per sequence): cut the packed
+// sequences into segments so that the longest ones no longer set the length of the
+// call.  With c_n the chunks of sequence n, J workgroups per segment and kNumCu
+// compute units, the balanced load per compute unit is Lb = J * sum(c_n) / kNumCu
+// chunks.  A sequence longer than 5/4 Lb (the state-only pass costs about a quarter
+// of a segment) is cut into segments of S = max(min_seg, ceil(Lb / 2)) chunks; with
+// `forced` > 1 every sequence of at least two chunks is cut into min(forced, c_n)
+// segments.  Sequences whose slots would pass max_slots stay whole.  Writes the main
+// pass's segments longest first (ties by sequence, then segment) and the state-only
+// pass's segments (layout in lattn_launch.h).  Segments are numbered in processing
+// order (mirrored positions in reverse), so only a sequence's last segment can be
+// short.
 // ---------------------------------------------------------------------------
+// Exclusive prefix sum over the workgroup (one value per thread, buf of blockDim.x);
+// total = the sum.
+__device__ inline int block_exclusive_scan(int v, int32_t* buf, int& total) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    buf[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < nt; off <<= 1) {
+        const int t = tid >= off ? buf[tid - off] : 0;
+        __syncthreads();
+        buf[tid] += t;
+        __syncthreads();
+    }
+    total = buf[nt - 1];
+    const int incl = buf[tid];
+    __syncthreads();
+    return incl - v;
+}
+
 __global__ __launch_bounds__(1024) void split_plan_kernel(const int32_t* __restrict__ cu, int num_seqs, int seqlen,
                                                           int wgs, int min_seg, int forced, int rev, int max_main,
                                                           int max_slots, int32_t* __restrict__ plan) {
     __shared__ int32_t s_start[kMaxPlanSeqs], s_len[kMaxPlanSeqs], s_P[kMaxPlanSeqs], s_S[kMaxPlanSeqs];
-    __shared__ int32_t s_slot0[kMaxPlanSeqs], s_seg0[kMaxPlanSeqs];
-    __shared__ int64_t s_total;
-    __shared__ int32_t s_nsplit;
-    const int tid = threadIdx.x, nt = blockDim.x;
-    if (tid == 0) {
-        s_total = 0;
-        s_nsplit = 0;
-    }
+    __shared__ int32_t s_slot0[kMaxPlanSeqs], s_seg0[kMaxPlanSeqs], s_buf[1024];
+    __shared__ int32_t g_len[kMaxPlanSegs], g_seq[kMaxPlanSegs], g_k[kMaxPlanSegs];
+    __shared__ unsigned long long s_total;
+    const int i = threadIdx.x;  // this thread's sequence (blockDim.x >= num_seqs, a power of two <= 1024)
+    const bool mine = i < num_seqs;
+    if (i == 0) s_total = 0;
     __syncthreads();
-    for (int i = tid; i < num_seqs; i += nt) {
+    int len = 0, start = 0;
+    if (mine) {
         int64_t a = cu[i], e = cu[i + 1];
         a = min(max(a, (int64_t)0), (int64_t)seqlen);  // clamped as the work decode clamps
         e = min(max(e, a), (int64_t)seqlen);
-        s_start[i] = (int32_t)a;
-        s_len[i] = (int32_t)(e - a);
-        atomicAdd(reinterpret_cast<unsigned long long*>(&s_total), (unsigned long long)((e - a + kChunk - 1) / kChunk));
+        start = (int)a;
+        len = (int)(e - a);
+        atomicAdd(&s_total, (unsigned long long)((len + kChunk - 1) / kChunk));
     }
     __syncthreads();
-    const int64_t lb = (s_total * wgs + kNumCu - 1) / kNumCu;  // balanced chunks per compute unit
-    const int64_t seg_auto = max((int64_t)min_seg, (lb + 1) / 2);
-    for (int i = tid; i < num_seqs; i += nt) {
-        const int c = (s_len[i] + kChunk - 1) / kChunk;
-        int P = 1, S = c;
+    const int64_t lb = ((int64_t)s_total * wgs + kNumCu - 1) / kNumCu;  // balanced chunks per compute unit
+    const int c = (len + kChunk - 1) / kChunk;
+    int P = 1, S = c;
+    if (mine) {
         if (forced > 1) {
             if (c >= 2) {
-                S = (c + min(forced, c) - 1) / min(forced, c);
+                const int f = min(forced, c);
+                S = (c + f - 1) / f;
                 P = (c + S - 1) / S;
             }
         } else if (4 * (int64_t)c > 5 * lb) {
-            S = (int)seg_auto;
+            S = (int)max((int64_t)min_seg, (lb + 1) / 2);
             P = (c + S - 1) / S;
         }
-        s_P[i] = P;
-        s_S[i] = S;
     }
-    __syncthreads();
-    if (tid == 0) {  // slots in sequence order; sequences past the capacity stay whole
-        int slots = 0, segs = 0, nsplit = 0;
-        for (int i = 0; i < num_seqs; ++i) {
-            if (s_P[i] > 1 && slots + s_P[i] - 1 > max_slots) s_P[i] = 1;
-            s_slot0[i] = slots;
-            s_seg0[i] = segs;
-            if (s_P[i] > 1) {
-                slots += s_P[i] - 1;
-                ++nsplit;
-            }
-            segs += s_P[i];
-        }
-        plan[0] = segs;
-        plan[1] = slots;
-        plan[2] = nsplit;
-        s_nsplit = nsplit;
+    // slots in sequence order; a sequence whose slots would pass the capacity stays whole
+    int total;
+    const int tent = P > 1 ? P - 1 : 0;
+    if (block_exclusive_scan(tent, s_buf, total) + tent > max_slots) P = 1;
+    const int slots = P > 1 ? P - 1 : 0;
+    int n_slots, n_segs;
+    const int slot0 = block_exclusive_scan(slots, s_buf, n_slots);
+    const int seg0 = block_exclusive_scan(mine ? P : 0, s_buf, n_segs);
+    if (i == 0) {
+        plan[0] = n_segs;
+        plan[1] = n_slots;
     }
-    __syncthreads();
-    // One entry per segment; rank = longest first.
     int32_t* mainl = plan + kPlanHeader;
     int32_t* sonly = mainl + kPlanEntry * max_main;
-    int32_t* scan = sonly + kPlanEntry * max_slots;
-    for (int i = tid; i < num_seqs; i += nt) {
-        const int P = s_P[i];
-        const int64_t S64 = (int64_t)s_S[i] * kChunk;
-        const int len = s_len[i];
-        int jrank = 0;  // index of this split sequence in the scan list
-        if (P > 1) {
-            for (int m = 0; m < i; ++m) jrank += s_P[m] > 1;
-            int32_t* e = scan + kPlanScan * jrank;
-            e[0] = i;
-            e[1] = s_slot0[i];
-            e[2] = P;
-            e[3] = (int32_t)S64;
-        }
+    if (mine) {
+        s_start[i] = start;
+        s_len[i] = len;
+        s_P[i] = P;
+        s_S[i] = S;
+        s_slot0[i] = slot0;
+        s_seg0[i] = seg0;
+        const int64_t S64 = (int64_t)S * kChunk;
         for (int k = 0; k < P; ++k) {
             const int64_t a = (int64_t)k * S64;
             const int sl = (int)(P > 1 ? min(S64, (int64_t)len - a) : len);
-            const int st = s_start[i] + (int)(rev ? (int64_t)len - a - sl : a);
-            // rank among all segments: longer first, then by (sequence, segment)
-            int rank = 0;
-            for (int m = 0; m < num_seqs; ++m) {
-                const int Pm = s_P[m];
-                const int64_t Sm = (int64_t)s_S[m] * kChunk;
-                const int lm = s_len[m];
-                // segments of m: Pm - 1 of length Sm and one of the rest (or all of lm)
-                const int full = Pm > 1 ? Pm - 1 : 0;
-                const int last = Pm > 1 ? (int)(lm - (int64_t)(Pm - 1) * Sm) : lm;
-                auto before = [&](int l2, int k2) { return l2 > sl || (l2 == sl && (m < i || (m == i && k2 < k))); };
-                if (full > 0) {
-                    if (Sm > sl) rank += full;
-                    else if (Sm == sl) rank += m < i ? full : (m == i ? min(k, full) : 0);
-                }
-                rank += before(last, Pm - 1) ? 1 : 0;
-            }
-            int32_t* e = mainl + kPlanEntry * rank;
-            e[0] = st;
-            e[1] = sl;
-            e[2] = i;
-            e[3] = (P > 1 && k > 0) ? s_slot0[i] + k - 1 : -1;
-            e[4] = k == P - 1 ? 1 : 0;
-            e[5] = -1;
-            if (P > 1 && k < P - 1) {
-                int32_t* so = sonly + kPlanEntry * (s_slot0[i] + k);
-                so[0] = st;
+            g_len[seg0 + k] = sl;
+            g_seq[seg0 + k] = i;
+            g_k[seg0 + k] = k;
+            if (k < P - 1) {  // the state-only pass's segment (P > 1 here)
+                int32_t* so = sonly + kPlanEntry * (slot0 + k);
+                so[0] = start + (int)(rev ? (int64_t)len - a - sl : a);
                 so[1] = sl;
                 so[2] = i;
                 so[3] = -1;
                 so[4] = 0;
-                so[5] = s_slot0[i] + k;
+                so[5] = 0;
+                so[6] = (int)S64;
+                so[7] = slot0 + k;
             }
         }
+    }
+    __syncthreads();
+    // Main pass: rank = longest first, then by (sequence, segment) = list order.
+    for (int g = threadIdx.x; g < n_segs; g += blockDim.x) {
+        const int sl = g_len[g];
+        int rank = 0;
+        for (int h = 0; h < n_segs; ++h) {
+            const int lh = g_len[h];
+            rank += (lh > sl) || (lh == sl && h < g);
+        }
+        const int n = g_seq[g], k = g_k[g], Pn = s_P[n];
+        const int64_t S64 = (int64_t)s_S[n] * kChunk, a = (int64_t)k * S64;
+        int32_t* e = mainl + kPlanEntry * rank;
+        e[0] = s_start[n] + (int)(rev ? (int64_t)s_len[n] - a - sl : a);
+        e[1] = sl;
+        e[2] = n;
+        e[3] = (Pn > 1 && k > 0) ? s_slot0[n] : -1;
+        e[4] = Pn > 1 ? k : 0;
+        e[5] = k == Pn - 1 ? 1 : 0;
+        e[6] = (int)S64;
+        e[7] = 0;
     }
 }
 
@@ -1359,26 +1373,24 @@ hipError_t launch_decode(const DecodeParams& p, int in_dtype, hipStream_t s) {
     }
 }
 
-hipError_t launch_seg_scan(const int32_t* plan, int plan_main, int plan_slots, int max_seqs, float* slots,
-                           const float* init, const float* g_gamma, int B, int H, int P, int seg_len, int64_t elems,
-                           hipStream_t s) {
+hipError_t launch_seg_scan(float* slots, const float* init, const float* g_gamma, int B, int H, int P, int seg_len,
+                           int64_t elems, hipStream_t s) {
     const int elems4 = (int)(elems / 4);
-    const int rows = plan ? max_seqs : B;
-    if (rows <= 0 || elems4 == 0) return hipSuccess;
-    // fixed length: every row is split, one block per 256 float4; packed: few blocks per
-    // row, most of which find no split sequence and exit
-    const int eblocks = plan ? 4 : std::max(1, std::min(64, (elems4 + 255) / 256));
-    const dim3 grid((unsigned)rows * (unsigned)H * (unsigned)eblocks);
-    hipLaunchKernelGGL(seg_scan_kernel, grid, dim3(256), 0, s, plan, plan_main, plan_slots, slots, init, g_gamma, H, P,
-                       seg_len, elems4, eblocks);
+    if (B <= 0 || P < 2 || elems4 == 0) return hipSuccess;
+    const int eblocks = std::max(1, std::min(64, (elems4 + 255) / 256));  // one block per 256 float4
+    const dim3 grid((unsigned)B * (unsigned)H * (unsigned)eblocks);
+    hipLaunchKernelGGL(seg_scan_kernel, grid, dim3(256), 0, s, slots, init, g_gamma, H, P, seg_len, elems4, eblocks);
     return hipGetLastError();
 }
 
 hipError_t launch_split_plan(const int32_t* cu, int num_seqs, int seqlen, int wgs_per_seq, int min_seg_chunks,
                              int forced, bool reverse, int max_main, int max_slots, int32_t* plan, hipStream_t s) {
-    if (num_seqs < 1 || num_seqs > kMaxPlanSeqs) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(1024), 0, s, cu, num_seqs, seqlen, wgs_per_seq, min_seg_chunks,
-                       forced, reverse ? 1 : 0, max_main, max_slots, plan);
+    if (num_seqs < 1 || num_seqs > kMaxPlanSeqs || max_main > kMaxPlanSegs) return hipErrorInvalidValue;
+    // a thread per sequence: the smallest power of two >= num_seqs, at least one wave
+    int threads = 64;
+    while (threads < num_seqs) threads *= 2;
+    hipLaunchKernelGGL(split_plan_kernel, dim3(1), dim3(threads), 0, s, cu, num_seqs, seqlen, wgs_per_seq,
+                       min_seg_chunks, forced, reverse ? 1 : 0, max_main, max_slots, plan);
     return hipGetLastError();
 }
 

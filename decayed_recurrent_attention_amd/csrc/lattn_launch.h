@@ -17,19 +17,22 @@ constexpr int kNumXcd = 8;
 constexpr int kMaxOrderedSeqs = 16384;
 // Compute units of MI355X: the intra-sequence split balances its work over them.
 constexpr int kNumCu = 256;
-// Largest packed sequence count that the split planner handles (one workgroup, its
-// tables in LDS); above it packed input is not split.
+// Largest packed sequence count that the split planner handles (one workgroup, a
+// thread per sequence, its tables in LDS), and the most segments it can list; above
+// either, packed input is not split.
 constexpr int kMaxPlanSeqs = 1024;
-// Packed-split plan in the workspace (int32 words): a header, then the main pass's
-// segments (longest first), the state-only pass's segments, and the split sequences
-// that the scan chains.  Segment entries are kPlanEntry words: first row, length,
-// sequence, state slot read as the segment's initial state (-1: the sequence's own),
-// 1 if the segment writes the sequence's final state, state slot written by the
-// state-only pass.  Scan entries are kPlanScan words: sequence, first slot,
-// segments, segment length in tokens.
-constexpr int kPlanHeader = 8;  // main count, state-only count, scan count
+constexpr int kMaxPlanSegs = 2048;
+// Packed-split plan in the workspace (int32 words): a header (main-pass count,
+// state-only count), then the main pass's segments (longest first), then the
+// state-only pass's segments.  An entry is kPlanEntry words:
+//   [0] first row  [1] length  [2] sequence
+//   [3] first state slot to chain into the initial state, or -1
+//   [4] slots to chain (the segment's index k in its sequence)
+//   [5] 1 if the segment writes the sequence's final state
+//   [6] length of the sequence's full segments (tokens)
+//   [7] state slot written by the state-only pass (state-only list)
+constexpr int kPlanHeader = 8;
 constexpr int kPlanEntry = 8;
-constexpr int kPlanScan = 4;
 
 // Everything one forward launch needs.  Sizes are element counts.
 struct FwdParams {
@@ -68,10 +71,13 @@ struct FwdParams {
     // processing order: segment k of a sequence of length L covers positions
     // [k * seg_len, min((k + 1) * seg_len, L)) forward, the mirror image in reverse,
     // so only the last processed segment can be short.  The state-only pass writes
-    // segment k's own contribution to state slot k of its sequence (k < P - 1); the
-    // scan turns slot k into the state entering segment k + 1, in place; the main
-    // pass starts segment 0 from the sequence's initial state, segment k > 0 from
-    // slot k - 1, and the last segment writes the final state.
+    // segment k's own contribution dS_k (from a zero state) to state slot k of its
+    // sequence (k < P - 1).  Fixed length: a scan then turns slot k into the state
+    // entering segment k + 1, in place, and the main pass starts segment k > 0 from
+    // slot k - 1.  Packed: the main pass chains the slots itself: segment k starts
+    // from lam^seg_len ... applied k times to the sequence's initial state plus dS_0 ..
+    // dS_{k-1}.  Segment 0 starts from the sequence's initial state, and the last
+    // segment writes the final state.
     int seg_phase;    // 1: the state-only pass; 2: the main pass (with seg_count or plan)
     int seg_count;    // fixed length: P segments per batch row (every row alike)
     int seg_len;      // fixed length: segment length in tokens (a multiple of the chunk)
@@ -134,14 +140,12 @@ bool have_gated_kernel(int dk, int nw);
 // out = g + gk in fp32 (n elements, a multiple of 4; inputs in in_dtype).
 hipError_t launch_gate_sum(const void* g, const void* gk, float* out, int64_t n, int in_dtype, hipStream_t stream);
 hipError_t launch_gated(const FwdParams& p, int in_dtype, int nw, hipStream_t stream);
-// Intra-sequence split, chaining step: turn each split sequence's state slots (its
-// segments' own contributions) into the states entering its segments, in place; see
-// seg_scan_kernel.  Fixed length (plan == nullptr): B rows of P segments of seg_len
-// tokens, slots b * (P - 1) + k.  Packed: the plan's scan list (at most max_seqs entries;
-// plan_main and plan_slots are the capacities of the plan's two segment lists).
-hipError_t launch_seg_scan(const int32_t* plan, int plan_main, int plan_slots, int max_seqs, float* slots,
-                           const float* init, const float* g_gamma, int B, int H, int P, int seg_len, int64_t elems,
-                           hipStream_t stream);
+// Intra-sequence split of fixed-length input, chaining step: turn the state slots of
+// B rows of P segments of seg_len tokens (row b's slots b * (P - 1) + k, each
+// segment's own contribution) into the states entering the segments, in place; see
+// seg_scan_kernel.
+hipError_t launch_seg_scan(float* slots, const float* init, const float* g_gamma, int B, int H, int P, int seg_len,
+                           int64_t elems, hipStream_t stream);
 // Packed split plan: cut the sequences of cu_seqlens into segments (see
 // split_plan_kernel) and write the plan.  wgs_per_seq: workgroups per segment;
 // forced > 1: cut every sequence into that many segments (tests); else balance.

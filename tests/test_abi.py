@@ -247,8 +247,8 @@ def test_split_workspace():
 
 
 def _packed_split_bytes(num_seqs, H, dk, dv, slots):
-    """Plan (header, main and state-only lists of 8 words, scan list of 4) + state slots."""
-    words = 8 + 8 * (num_seqs + slots + slots) + 4 * slots
+    """Plan (header, main and state-only lists of 8 words) + state slots."""
+    words = 8 + 8 * (num_seqs + slots + slots)
     plan = -(-words * 4 // 256) * 256
     return plan + -(-slots * H * dk * dv * 4 // 256) * 256
 
@@ -269,6 +269,9 @@ def test_packed_split_workspace():
     # 256 workgroups per segment or more: nothing can exceed the balanced load
     wide = P(batch=1, seqlen=5000, num_seqs=7, num_heads=128, num_kv_heads=128, head_dim_qk=128, head_dim_v=128)
     assert lattn.lattn_fwd_workspace_size(wide) == 256
+    # forced splits that would list more than 2048 segments fall back to the order
+    with lattn.knob(lattn.LATTN_KNOB_SPLIT, 200):
+        assert lattn.lattn_fwd_workspace_size(prob) == 256
     # more sequences than the planner holds, or fp32 input: the order only
     many = P(batch=1, seqlen=5000, num_seqs=1025, num_heads=4, num_kv_heads=4)
     assert lattn.lattn_fwd_workspace_size(many) == -(-1025 * 4 // 256) * 256
