@@ -159,6 +159,7 @@ int64_t heads_of(const lattn_problem& p) { return (int64_t)num_seqs_of(p) * p.nu
 struct Split {
     int P = 0;            // fixed length: segments per row (0: no split)
     int seg_len = 0;      // fixed length: tokens per segment
+    bool chain = false;   // fixed length: the main pass chains the slots (no scan)
     bool packed = false;  // packed input: the device-planned split runs
     int forced = 0;       // packed: segments per sequence forced by the knob (0: balance)
     int wgs = 0;          // packed: workgroups per segment (heads x value blocks)
@@ -170,6 +171,8 @@ struct Split {
 // Shortest segment worth a state-only pass and a scan: 4 chunks up to dk 128, 8 above
 // (those cost more at dk 192 and 256).
 int min_seg_chunks(int dk) { return dk <= 128 ? 4 : 8; }
+
+constexpr int kMaxMainChain = 4;
 
 Split choose_split(const lattn_problem& p, int nw) {
     Split sp;
@@ -196,7 +199,11 @@ Split choose_split(const lattn_problem& p, int nw) {
     if (want > chunks) want = chunks;
     sp.seg_len = ((chunks + want - 1) / want) * lattn::kChunk;
     sp.P = (p.seqlen + sp.seg_len - 1) / sp.seg_len;
-    if (sp.P < 2) sp = Split{};
+    if (sp.P < 2) return Split{};
+    // Up to four earlier segments, the main pass chains the slots itself (their loads
+    // go out together), which saves the scan launch; more would lengthen every
+    // workgroup's start, so the scan chains them in parallel instead.
+    sp.chain = sp.P - 1 <= kMaxMainChain;
     return sp;
 }
 
@@ -351,8 +358,9 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
     int nw = 0;
     const Split sp = plan_forward(*p, nw);
     if (sp.P > 0 || sp.packed) {
-        // state-only pass over every segment but each sequence's last -> slots; scan ->
-        // the state entering each segment, in place; main pass over every segment.
+        // state-only pass over every segment but each sequence's last -> slots; with
+        // many segments of fixed length a scan -> the state entering each segment, in
+        // place; main pass over every segment (chaining the slots itself otherwise).
         uint8_t* ws = static_cast<uint8_t*>(workspace);
         int32_t* plan = sp.packed ? reinterpret_cast<int32_t*>(ws) : nullptr;
         float* slots = reinterpret_cast<float*>(ws + split_plan_bytes(sp));
@@ -373,6 +381,7 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
             f->plan_slots = sp.max_slots;
             f->seg_count = sp.P;
             f->seg_len = sp.seg_len;
+            f->seg_chain = sp.chain ? 1 : 0;
         }
         f1.seg_phase = 1;
         f3.seg_phase = 2;
@@ -389,7 +398,7 @@ int lattn_fwd(const lattn_problem* p, const void* q, const void* k, const void* 
             return LATTN_ERR_LAUNCH;
         if (n_sonly > 0 && lattn::launch_fwd(f1, p->in_dtype, nw, reverse != 0, s, true) != hipSuccess)
             return LATTN_ERR_LAUNCH;
-        if (!sp.packed && lattn::launch_seg_scan(slots, initial_state, g_gamma, p->batch, p->num_heads, sp.P,
+        if (!sp.packed && !sp.chain && lattn::launch_seg_scan(slots, initial_state, g_gamma, p->batch, p->num_heads, sp.P,
                                                  sp.seg_len, (int64_t)p->head_dim_qk * p->head_dim_v, s) != hipSuccess)
             return LATTN_ERR_LAUNCH;
         if (lattn::launch_fwd(f3, p->in_dtype, nw, reverse != 0, s) != hipSuccess) return LATTN_ERR_LAUNCH;

@@ -28,8 +28,9 @@ struct Work {
     int64_t len;    // tokens in the work
     const float* init_blk;  // this head's initial state block [dk][dv], or null (zeros)
     float* fin_blk;         // where this head's final state block goes, or null (nowhere)
-    // Packed split: the initial state is lam^chain_len applied to the state above plus
-    // the `chain` state blocks at chain_blk, chain_blk + H dk dv, ... in turn.
+    // Split with the chain in the main pass: the initial state is lam^chain_len applied
+    // to the state above plus the `chain` state blocks at chain_blk, chain_blk + H dk dv,
+    // ... in turn.
     const float* chain_blk;
     int chain;
     int chain_len;
@@ -92,8 +93,17 @@ __device__ inline bool decode_work(const FwdParams& p, int id, Work& w) {
             w.init_blk = nullptr;
             w.fin_blk = p.slots + ((slot0 + k) * H + w.h) * blk;
         } else {
-            w.init_blk = k > 0 ? p.slots + ((slot0 + k - 1) * H + w.h) * blk
-                               : (p.init ? p.init + ((int64_t)b * H + w.h) * blk : nullptr);
+            const float* row_init = p.init ? p.init + ((int64_t)b * H + w.h) * blk : nullptr;
+            if (p.seg_chain) {  // the slots hold dS_0 .. dS_{P-2}: chain the earlier ones
+                w.init_blk = row_init;
+                if (k > 0) {
+                    w.chain_blk = p.slots + (slot0 * H + w.h) * blk;
+                    w.chain = k;
+                    w.chain_len = p.seg_len;
+                }
+            } else {  // the scan left the state entering segment k in slot k - 1
+                w.init_blk = k > 0 ? p.slots + ((slot0 + k - 1) * H + w.h) * blk : row_init;
+            }
             w.fin_blk = (k == P - 1 && p.final_state) ? p.final_state + ((int64_t)b * H + w.h) * blk : nullptr;
         }
         return true;

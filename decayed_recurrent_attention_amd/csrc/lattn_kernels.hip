@@ -335,8 +335,8 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 S[mt][ii] = p.init_mul * buf_load_f32(ri, (dmap(wd * MTL + mt, 4 * lg + ii) * rs + gcol * cs) * 4);
-        // Packed split: chain the earlier segments' own contributions into the state
-        // entering this one (their slots hold [dk][dv] blocks, H heads apart).
+        // Split without a scan: chain the earlier segments' own contributions into the
+        // state entering this one (their slots hold [dk][dv] blocks, H heads apart).
         // Four slots' loads go out together before they are added in order.
         if (wk.chain > 0) {
             const float lam_seg = exp2f(g2 * (float)wk.chain_len);
@@ -467,6 +467,7 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
             }
 #pragma unroll
             for (int mt = 0; mt < MTL; ++mt) S[mt] = mfma_bf16(kop[mt], vop, S[mt]);
+            if constexpr (DK >= 192 && DS == 2) __builtin_amdgcn_sched_barrier(0);
         }
         issue_chunk(cn, kCopyV);
         if constexpr (SONLY) return;
@@ -507,6 +508,9 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
                     const int a = tile_a(t), b = tile_b(t);
                     const bf16x8 ka = lds_load<bf16x8>(Ks + qk_off(16 * a + lr, 4 * kb + lg));
                     At[s] = mfma_bf16(ka, qa[b], At[s]);
+                }
+                if constexpr (DK >= 192 && DS == 2) {
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
 #pragma unroll
@@ -1204,7 +1208,7 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* cu, int n
 // leaves no LDS for the partial sums.  The state-only pass keeps one wave per block.
 template <int DK, int NW>
 constexpr int bf16_dk_split() {
-    return (NW == 4 && (DK == 64 || DK == 128)) ? 2 : 1;
+    return (NW == 4 && (DK == 64 || DK == 128 || DK == 192)) ? 2 : 1;
 }
 
 template <int DK, int NW>

@@ -72,15 +72,17 @@ struct FwdParams {
     // [k * seg_len, min((k + 1) * seg_len, L)) forward, the mirror image in reverse,
     // so only the last processed segment can be short.  The state-only pass writes
     // segment k's own contribution dS_k (from a zero state) to state slot k of its
-    // sequence (k < P - 1).  Fixed length: a scan then turns slot k into the state
-    // entering segment k + 1, in place, and the main pass starts segment k > 0 from
-    // slot k - 1.  Packed: the main pass chains the slots itself: segment k starts
-    // from lam^seg_len ... applied k times to the sequence's initial state plus dS_0 ..
-    // dS_{k-1}.  Segment 0 starts from the sequence's initial state, and the last
-    // segment writes the final state.
+    // sequence (k < P - 1).  Fixed length with many segments: a scan then turns slot
+    // k into the state entering segment k + 1, in place, and the main pass starts
+    // segment k > 0 from slot k - 1.  Packed input, and fixed length with seg_chain
+    // set: the main pass chains the slots itself: segment k starts from lam^seg_len
+    // ... applied k times to the sequence's initial state plus dS_0 .. dS_{k-1}.
+    // Segment 0 starts from the sequence's initial state, and the last segment writes
+    // the final state.
     int seg_phase;    // 1: the state-only pass; 2: the main pass (with seg_count or plan)
     int seg_count;    // fixed length: P segments per batch row (every row alike)
     int seg_len;      // fixed length: segment length in tokens (a multiple of the chunk)
+    int seg_chain;    // fixed length: 1 = the main pass chains the slots (no scan)
     const int32_t* plan;  // packed input: the plan (kPlanHeader ... above)
     int plan_main;        // capacity of the plan's main-pass list (entries)
     int plan_slots;       // capacity of its state-only list and of the state slots
@@ -114,6 +116,7 @@ inline void set_forward_defaults(FwdParams& p) {
     p.seg_phase = 0;
     p.seg_count = 0;
     p.seg_len = 0;
+    p.seg_chain = 0;
     p.plan = nullptr;
     p.plan_main = 0;
     p.plan_slots = 0;
