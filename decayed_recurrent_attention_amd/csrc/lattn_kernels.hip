@@ -1204,8 +1204,8 @@ __global__ __launch_bounds__(256) void seq_order_kernel(const int32_t* cu, int n
 }
 
 // The dk split (two waves per 16-column block, eight waves per workgroup) for four
-// column blocks at dk 64 and 128; at dk 192 its registers would spill, and dk 256
-// leaves no LDS for the partial sums.  The state-only pass keeps one wave per block.
+// column blocks at dk 64, 128 and 192; dk 256 leaves no LDS for the partial sums.
+// The state-only pass keeps one wave per block (with the split it ran no faster).
 template <int DK, int NW>
 constexpr int bf16_dk_split() {
     return (NW == 4 && (DK == 64 || DK == 128 || DK == 192)) ? 2 : 1;

@@ -229,6 +229,17 @@ def test_split_forced_segments(reverse, knobs):
     _compare(w, w.make(), tag=" rev" if reverse else "")
 
 
+@pytest.mark.parametrize("segments", [5, 6])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_split_chain_in_main_pass_or_scan(segments, reverse, knobs):
+    """Five segments (24 chunks of d192): the main pass chains up to four slots itself;
+    six: the scan chains them first.  Both against the oracle, in both directions."""
+    knobs(lattn.LATTN_KNOB_SPLIT, segments)
+    w = inputs.Workload(f"split{segments}_d192", 1, 1500, 2, 2, 192, 192, "bf16", 3, 24, reverse=reverse,
+                        init_std=0.3, seed=45 + segments)
+    _compare(w, w.make(), tag=" rev" if reverse else "")
+
+
 def test_split_forced_gqa_unequal_dims(knobs):
     knobs(lattn.LATTN_KNOB_SPLIT, 5)
     w = inputs.Workload("split5_gqa", 1, 777, 8, 2, 128, 64, "bf16", 6, 12, init_std=0.3, seed=43)
