@@ -206,6 +206,11 @@ struct Bf16Cfg {
     static constexpr int FIT = (kLdsBudget - P_BYTES - X_BYTES) / STAGE_BYTES;
     static constexpr int STAGES = FIT >= 3 ? 3 : FIT;  // ring of chunk stages
     static constexpr int DEPTH = STAGES - 1;           // chunks copied ahead of the one computed
+    // The state-only pass stages K and V only: three stages wherever they fit, and two
+    // of its workgroups share a compute unit where their LDS allows.
+    static constexpr int SO_STAGE_BYTES = Q_BYTES + V_BYTES;
+    static constexpr int SO_STAGES = 3 * SO_STAGE_BYTES <= kLdsBudget ? 3 : 2;
+    static constexpr int SO_PER_CU = 2 * SO_STAGES * SO_STAGE_BYTES <= kLdsBudget ? 2 : 1;
     static constexpr int QCOPIES = PP / NWD;           // copy instructions per wave per Q (or K) tile
     static constexpr int VCOPIES = PVB / NWD;          // ... per V tile
     static constexpr int NCOPY = 2 * QCOPIES + VCOPIES;
@@ -256,15 +261,15 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     using Cfg = Bf16Cfg<DK, NW, DS>;
     constexpr int BV = Cfg::BV, PP = Cfg::PP, PVB = Cfg::PVB, KB = Cfg::KB, MT = Cfg::MT;
     constexpr int NWD = Cfg::NWD, MTL = MT / DS, KBL = KB / DS;  // waves; state tiles, dk blocks per wave
-    constexpr int NST = Cfg::STAGES, DEPTH = Cfg::DEPTH;
+    constexpr int NST = SONLY ? Cfg::SO_STAGES : Cfg::STAGES, DEPTH = NST - 1;
     constexpr int QROW = DK * 2, VROW = BV * 2;  // LDS row bytes
     // LDS: the Q tiles of every stage, then the K tiles, then the V tiles, then P and the
-    // partial sums.  The state-only pass holds only the K and V tiles, so two of its
-    // workgroups fit in one compute unit.
+    // partial sums.  The state-only pass holds only the K and V tiles.
     constexpr int KREG = SONLY ? 0 : NST * Cfg::Q_BYTES;
     constexpr int VREG = KREG + NST * Cfg::Q_BYTES;
     constexpr int LDS_BYTES = SONLY ? VREG + NST * Cfg::V_BYTES : NST * Cfg::STAGE_BYTES + Cfg::P_BYTES + Cfg::X_BYTES;
-    static_assert(!SONLY || 2 * LDS_BYTES <= kLdsBudget, "two state-only workgroups per compute unit");
+    static_assert(LDS_BYTES <= kLdsBudget, "LDS budget");
+    static_assert(!SONLY || Cfg::SO_PER_CU * LDS_BYTES <= kLdsBudget, "state-only workgroups per compute unit");
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
     uint8_t* Pbuf = smem + NST * Cfg::STAGE_BYTES;
     uint8_t* Xbuf = Pbuf + Cfg::P_BYTES;
@@ -668,8 +673,14 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
     }
 }
 
+// Workgroups per compute unit that the kernel is built for.
+template <int DK, int NW, int DS, bool SONLY>
+constexpr int bf16_wgs_per_cu() {
+    return SONLY ? Bf16Cfg<DK, NW, DS>::SO_PER_CU : 1;
+}
+
 template <int DK, int NW, bool REV, bool SONLY, int DS = 1, bool OB16 = false>
-__global__ __launch_bounds__(64 * NW * DS, SONLY ? 2 : 1) void fwd_bf16_kernel(const FwdParams p) {
+__global__ __launch_bounds__(64 * NW * DS, (bf16_wgs_per_cu<DK, NW, DS, SONLY>())) void fwd_bf16_kernel(const FwdParams p) {
     fwd_bf16_body<DK, NW, REV, SONLY, DS, OB16>(p, blockIdx.x);
 }
 
