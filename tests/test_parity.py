@@ -240,6 +240,17 @@ def test_split_chain_in_main_pass_or_scan(segments, reverse, knobs):
     _compare(w, w.make(), tag=" rev" if reverse else "")
 
 
+@pytest.mark.parametrize("dk,dv", [(256, 256), (192, 256)])
+@pytest.mark.parametrize("reverse", [False, True])
+def test_split_widest_heads(dk, dv, reverse, knobs):
+    """The state-only pass with three K/V stages and one workgroup per compute unit (dk 192
+    and 256), with GQA and an initial state."""
+    knobs(lattn.LATTN_KNOB_SPLIT, 3)
+    w = inputs.Workload(f"split3_dk{dk}_dv{dv}", 1, 1400, 4, 2, dk, dv, "bf16", 5, 12, reverse=reverse,
+                        init_std=0.2, seed=47)
+    _compare(w, w.make(), tag=" rev" if reverse else "")
+
+
 def test_split_forced_gqa_unequal_dims(knobs):
     knobs(lattn.LATTN_KNOB_SPLIT, 5)
     w = inputs.Workload("split5_gqa", 1, 777, 8, 2, 128, 64, "bf16", 6, 12, init_std=0.3, seed=43)
