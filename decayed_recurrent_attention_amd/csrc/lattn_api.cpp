@@ -172,7 +172,7 @@ struct Split {
 // (those cost more at dk 192 and 256).
 int min_seg_chunks(int dk) { return dk <= 128 ? 4 : 8; }
 
-constexpr int kMaxMainChain = 4;
+constexpr int kMaxMainChain = 15;
 
 Split choose_split(const lattn_problem& p, int nw) {
     Split sp;
@@ -200,9 +200,10 @@ Split choose_split(const lattn_problem& p, int nw) {
     sp.seg_len = ((chunks + want - 1) / want) * lattn::kChunk;
     sp.P = (p.seqlen + sp.seg_len - 1) / sp.seg_len;
     if (sp.P < 2) return Split{};
-    // Up to four earlier segments, the main pass chains the slots itself (their loads
-    // go out together), which saves the scan launch; more would lengthen every
-    // workgroup's start, so the scan chains them in parallel instead.
+    // Up to 15 earlier segments, the main pass chains the slots itself (four loads at a
+    // time), which saves the scan launch: measured B2 H8 d64 N2048 (P 8) 24.5 -> 20.2 us,
+    // B1 H8 d128 N32768 (P 16) 98.5 -> 96.0 us.  With more, every workgroup's start grows
+    // and the slot reads grow with P^2, so the scan chains them in parallel instead.
     sp.chain = sp.P - 1 <= kMaxMainChain;
     return sp;
 }

@@ -229,13 +229,13 @@ def test_split_forced_segments(reverse, knobs):
     _compare(w, w.make(), tag=" rev" if reverse else "")
 
 
-@pytest.mark.parametrize("segments", [5, 6])
+@pytest.mark.parametrize("segments", [16, 17])
 @pytest.mark.parametrize("reverse", [False, True])
 def test_split_chain_in_main_pass_or_scan(segments, reverse, knobs):
-    """Five segments (24 chunks of d192): the main pass chains up to four slots itself;
-    six: the scan chains them first.  Both against the oracle, in both directions."""
+    """Sixteen one-chunk segments: the main pass chains up to fifteen slots itself;
+    seventeen: the scan chains them first.  Both against the oracle, in both directions."""
     knobs(lattn.LATTN_KNOB_SPLIT, segments)
-    w = inputs.Workload(f"split{segments}_d192", 1, 1500, 2, 2, 192, 192, "bf16", 3, 24, reverse=reverse,
+    w = inputs.Workload(f"split{segments}_d64", 1, 64 * segments, 2, 2, 64, 64, "bf16", 3, 24, reverse=reverse,
                         init_std=0.3, seed=45 + segments)
     _compare(w, w.make(), tag=" rev" if reverse else "")
 
