@@ -200,14 +200,22 @@ def ms_stats(ms):
 
 
 def cpu_model() -> str:
-    """The host CPU's model name from /proc/cpuinfo (or platform's guess)."""
+    """The host CPU's model name from /proc/cpuinfo, with its family, model and stepping
+    numbers (a virtual machine may shorten the name), or platform's guess."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break  # the first processor's block is enough
+                key, _, val = line.partition(":")
+                fields[key.strip()] = val.strip()
     except OSError:
         pass
+    name = fields.get("model name")
+    if name:
+        ids = [f"{k} {fields[k]}" for k in ("cpu family", "model", "stepping") if fields.get(k)]
+        return f"{name} ({', '.join(ids)})" if ids else name
     import platform
 
     return platform.processor() or "unknown"
