@@ -71,7 +71,8 @@ typedef struct {
 /*
  * Device workspace (bytes) that lattn_fwd needs for problem *p.  Sequences may be cut
  * into segments that run in parallel, chained through their states (a state-only
- * pass, a scan, then the main pass), when that fills the GPU better:
+ * pass gives each segment's own contribution; the main pass, or a scan before it when
+ * a row has more than sixteen segments, chains them), when that fills the GPU better:
  *  - fixed-length bf16 input with too few (batch row, head) pairs to fill the GPU:
  *    every row in P segments, one float32 state per segment but the last:
  *    B * (P - 1) * H * dk * dv * 4 bytes;
