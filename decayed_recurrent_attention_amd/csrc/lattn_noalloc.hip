@@ -1,7 +1,7 @@
 // lattn_fwd_noalloc: the forward pass for callers that cannot allocate device memory.
 //
-// The forward's workspace (the longest-first order of packed sequences, or the two
-// float32 states per segment of the intra-sequence split) comes from a device array
+// The forward's workspace (the longest-first order of packed sequences, or the plan
+// and the float32 segment states of the intra-sequence split) comes from a device array
 // that the library owns: one per device, of kNoallocScratchBytes, held from the
 // library's first use on that device until the process ends.  Nothing here allocates;
 // the array's device address is looked up once per device and every later call passes
