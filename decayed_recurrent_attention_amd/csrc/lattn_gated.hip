@@ -414,23 +414,41 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_f32_kernel(const FwdParams p
 // quarters of a pair in one lane quad; each quarter sums its four decays and the quad
 // exchanges the partial sums (DPP), so every lane has its tokens' A_t and A_15.
 // ---------------------------------------------------------------------------
-template <int DK, int NW>
+template <int DK, int NW, bool GF32>
 struct GatedBCfg {
     static constexpr int BV = 16 * NW;
     // Matrix waves first, then two producer waves per matrix wave: the producers'
-    // staging and prep are latency-bound, and twice the waves hide more of it.
+    // prep is latency-bound, and twice the waves hide more of it.
     static constexpr int MTH = 64 * NW;      // matrix threads
     static constexpr int PW = 2;             // producer waves per matrix wave
-    static constexpr int PT = 64 * NW * PW;  // producer threads
+    static constexpr int PWAVES = NW * PW;   // producer waves
+    static constexpr int PT = 64 * PWAVES;   // producer threads
     static constexpr int NT = MTH + PT;      // all threads
     static constexpr int MT = DK / 16;
     static constexpr int KB = DK / 32;  // 32-deep blocks of the dk contraction
-    // Dwords per row.  Staged raw chunk (token-major): q, k and a bf16 key gate;
-    // an fp32 key gate; v and the value gate.  Padded so that the prep reads of a
-    // half-wave (8 pairs x 4 quarters) hit distinct banks.
-    static constexpr int SQ = DK / 2 + 2;
-    static constexpr int SG32 = DK + 4;
-    static constexpr int SV = BV / 2 + 2;
+    // One staged raw chunk, filled by direct global-to-LDS copies of a kilobyte each:
+    // rows of q, k and the key gate (bf16, or fp32 when two gates were summed) over DK
+    // channels, then rows of v and the value gate over BV columns, each region rounded
+    // up to whole kilobytes (dwords below).  Rows are unpadded; the 16-byte blocks of
+    // token row t are XOR-swizzled (stage_dw, stage_fl) so that the prep's reads of a
+    // half-wave (8 channel pairs x 4 quarters) hit distinct banks.
+    static constexpr int QNB = DK / 8, GNB = GF32 ? DK / 4 : DK / 8, VNB = BV / 8;  // 16-byte blocks per row
+    static constexpr int kib(int bytes) { return (bytes + 1023) / 1024; }
+    static constexpr int NCQ = kib(kGChunk * DK * 2), NCG = kib(kGChunk * DK * (GF32 ? 4 : 2)),
+                         NCV = kib(kGChunk * BV * 2);
+    static constexpr int NCOPY = 2 * NCQ + NCG + 2 * NCV;  // copies per chunk
+    // Copies per producer wave and chunk: copy i goes to wave i mod PWAVES; the slots
+    // past NCOPY copy nothing into a sink kilobyte at the end of the stage, so every
+    // wave issues the same count.
+    static constexpr int CPW = (NCOPY + PWAVES - 1) / PWAVES;
+    static constexpr bool SINK = CPW * PWAVES > NCOPY;
+    static constexpr int ST_Q = 0;
+    static constexpr int ST_K = ST_Q + 256 * NCQ;
+    static constexpr int ST_G = ST_K + 256 * NCQ;
+    static constexpr int ST_V = ST_G + 256 * NCG;
+    static constexpr int ST_GV = ST_V + 256 * NCV;
+    static constexpr int ST_SINK = ST_GV + 256 * NCV;
+    static constexpr int ST_SIZE = ST_SINK + (SINK ? 256 : 0);
     // Decayed operands read along dk (token-major): bf16 hi half, lo half, 8 dwords
     // of pad (16-byte blocks per row = 2 mod 32: conflict-free operand reads).
     static constexpr int OPR = DK + 8;
@@ -441,13 +459,6 @@ struct GatedBCfg {
     static constexpr int VMR = 16;
     // fp32 summed decays for the exact path (token-major).
     static constexpr int AR = DK + 4, BR = BV + 4;
-    // One staged raw chunk.
-    static constexpr int ST_Q = 0;
-    static constexpr int ST_K = ST_Q + kGChunk * SQ;
-    static constexpr int ST_G = ST_K + kGChunk * SQ;  // bf16 or fp32 key gate
-    static constexpr int ST_V = ST_G + kGChunk * SG32;
-    static constexpr int ST_GV = ST_V + kGChunk * SV;
-    static constexpr int ST_SIZE = ST_GV + kGChunk * SV;
     // One set of decayed operands.
     static constexpr int D_QH = 0;
     static constexpr int D_KP = D_QH + kGChunk * OPR;
@@ -459,29 +470,47 @@ struct GatedBCfg {
     static constexpr int D_POST = D_PRE + DK;
     static constexpr int D_EB = D_POST + DK;
     static constexpr int D_SIZE = D_EB + BV;
+    // The exact path's summed decays A and B and its W live in the set of decayed
+    // operands that no wave uses at that point.
+    static constexpr int X_A = 0, X_B = X_A + kGChunk * AR, X_W = X_B + kGChunk * BR, X_END = X_W + kGChunk * 17;
+    // LDS: the staged ring (four chunks where they fit, else three), two sets of
+    // decayed operands and the exact path's intra term OI.
+    static constexpr int FIXED = 2 * D_SIZE + kGChunk * BR;
+    static constexpr int NST = (4 * ST_SIZE + FIXED) * 4 <= kLdsBudget ? 4 : 3;
     static constexpr int OFF_ST = 0;
-    static constexpr int OFF_D = OFF_ST + 2 * ST_SIZE;
-    static constexpr int OFF_A = OFF_D + 2 * D_SIZE;
-    static constexpr int OFF_B = OFF_A + kGChunk * AR;
-    static constexpr int OFF_OI = OFF_B + kGChunk * BR;
-    static constexpr int OFF_W = OFF_OI + kGChunk * BR;
-    static constexpr int DWORDS = OFF_W + kGChunk * 17;
-    // Staging: 4-element pieces of a chunk, spread over the producer threads.
-    static constexpr int KITEMS = kGChunk * DK / 4, VITEMS = kGChunk * BV / 4;
-    static constexpr int KPER = (KITEMS + PT - 1) / PT, VPER = (VITEMS + PT - 1) / PT;
+    static constexpr int OFF_D = OFF_ST + NST * ST_SIZE;
+    static constexpr int OFF_OI = OFF_D + 2 * D_SIZE;
+    static constexpr int DWORDS = OFF_OI + kGChunk * BR;
     // Prep items: channel pairs x quarters.
     static constexpr int KPREP = 2 * DK, VPREP = 2 * BV;
     static_assert(DK % 32 == 0 && DK <= 128, "dk must be 32, 64 or 128");
-    static_assert(ST_SIZE % 4 == 0 && D_SIZE % 4 == 0 && OFF_A % 4 == 0 && OFF_OI % 4 == 0 && D_PRE % 4 == 0,
-                  "16-byte alignment");
+    static_assert(X_END <= D_SIZE, "exact-path buffers fit a set of decayed operands");
+    static_assert(CPW * 3 <= 63, "vmcnt range");
+    static_assert(D_SIZE % 4 == 0 && OFF_D % 4 == 0 && OFF_OI % 4 == 0 && D_PRE % 4 == 0, "16-byte alignment");
     static_assert(DWORDS * 4 <= kLdsBudget, "LDS budget");
 };
 
-// A vector of raw words at a byte offset from a workgroup-uniform base (the offset
-// fits 32 bits, so the load takes the scalar-base form).
-template <typename T>
-__device__ inline T load_at(const void* base, uint32_t byte_off) {
-    return *reinterpret_cast<const T*>(static_cast<const char*>(base) + byte_off);
+// A raw buffer descriptor whose words are read from the first lane: the values are
+// workgroup-uniform, and the copy's inline assembly takes the descriptor in scalar
+// registers even where the compiler kept a word in a vector register.
+__device__ inline RawBuf uniform_buf(const void* base, uint32_t bytes) {
+    RawBuf r = raw_buf(base, bytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.d[i] = __builtin_amdgcn_readfirstlane(r.d[i]);
+    return r;
+}
+
+// Swizzle of the 16-byte blocks of staged token row t in a region of nb blocks per
+// row (step 2 for bf16 rows, 4 for fp32 rows): the four quarters of the chunk land
+// on different bank groups.
+__host__ __device__ constexpr int stage_swz(int t, int nb, int step) { return (step * (t >> 2)) & (nb - 1); }
+// Dword index of dword w of token row t in a staged bf16 region of nb blocks per row.
+__host__ __device__ constexpr int stage_dw(int t, int w, int nb) {
+    return t * 4 * nb + (((w >> 2) ^ stage_swz(t, nb, 2)) << 2) + (w & 3);
+}
+// Index of float i of token row t in a staged fp32 region of nb blocks per row.
+__host__ __device__ constexpr int stage_fl(int t, int i, int nb) {
+    return t * 4 * nb + (((i >> 2) ^ stage_swz(t, nb, 4)) << 2) + (i & 3);
 }
 
 __device__ inline f32x4 mfma_bf16_w(u32x4 a, u32x4 b, f32x4 c) {
@@ -498,9 +527,24 @@ __device__ inline f32x4 mfma_bf16_half(uint32_t a0, uint32_t a1, uint32_t b0, ui
 __device__ inline uint32_t hi_pack(float a, float b) {
     return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
 }
-__device__ inline float lo_part(float x) { return x - __uint_as_float(__float_as_uint(x) & 0xffff0000u); }
-// bf16 roundings of what the truncations of a and b leave (exact in fp32).
-__device__ inline uint32_t lo_pack(float a, float b) { return pack_bf16x2(lo_part(a), lo_part(b)); }
+// s minus the bf16 value held in the low (high) half of w, as one v_dot2_f32_bf16 of w
+// against the pair (-1, -0) (against (-0, -1)) accumulated onto s.  When w holds s
+// truncated to bf16 the difference is exact in fp32, so this equals the mask and
+// subtract it replaces, in one instruction instead of two.  The -0 keeps the pair a
+// 32-bit literal: the compiler encodes the pair (-1, 0) as the inline constant -1.0,
+// which the hardware reads as another value (checked on the GPU: wrong results).
+__device__ inline float sub_bf16_lo(uint32_t w, float s) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x8000bf80u), s,
+                                           false);
+}
+__device__ inline float sub_bf16_hi(uint32_t w, float s) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0xbf808000u), s,
+                                           false);
+}
+// bf16 roundings of what the truncations h = hi_pack(a, b) leave (exact in fp32).
+__device__ inline uint32_t lo_pack(uint32_t h, float a, float b) {
+    return pack_bf16x2(sub_bf16_lo(h, a), sub_bf16_hi(h, b));
+}
 // Lane k of this lane's quad.
 template <int K>
 __device__ inline float quad_get(float x) {
@@ -541,18 +585,15 @@ __device__ inline void quarter_sums(const float (&la)[4][2], int tq, float (&a)[
 }
 
 template <int DK, int NW, bool GF32>
-__global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(const FwdParams p) {
-    using Cfg = GatedBCfg<DK, NW>;
+__global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_kernel(const FwdParams p) {
+    using Cfg = GatedBCfg<DK, NW, GF32>;
     constexpr int BV = Cfg::BV, NT = Cfg::NT, PT = Cfg::PT, MT = Cfg::MT, KB = Cfg::KB;
-    constexpr int SQ = Cfg::SQ, SV = Cfg::SV, OPR = Cfg::OPR, TMR = Cfg::TMR, AR = Cfg::AR, BR = Cfg::BR;
-    constexpr int SGR = GF32 ? Cfg::SG32 : SQ;  // row stride of the staged key gate
+    constexpr int OPR = Cfg::OPR, TMR = Cfg::TMR, AR = Cfg::AR, BR = Cfg::BR;
+    constexpr int QNB = Cfg::QNB, GNB = Cfg::GNB, VNB = Cfg::VNB, NST = Cfg::NST, DEPTH = NST - 1, CPW = Cfg::CPW;
     __shared__ __attribute__((aligned(16))) uint32_t sm[Cfg::DWORDS];
     __shared__ int wide_flag[3];  // per chunk mod 3: take the exact VALU path
-    float* Af = reinterpret_cast<float*>(sm + Cfg::OFF_A);
-    float* Bf = reinterpret_cast<float*>(sm + Cfg::OFF_B);
     float* OIf = reinterpret_cast<float*>(sm + Cfg::OFF_OI);
-    float* Wf = reinterpret_cast<float*>(sm + Cfg::OFF_W);
-    auto staged = [&](int c) __attribute__((always_inline)) -> uint32_t* { return sm + Cfg::OFF_ST + (c & 1) * Cfg::ST_SIZE; };
+    auto staged = [&](int c) __attribute__((always_inline)) -> uint32_t* { return sm + Cfg::OFF_ST + (c % NST) * Cfg::ST_SIZE; };
     auto derived = [&](int c) __attribute__((always_inline)) -> uint32_t* { return sm + Cfg::OFF_D + (c & 1) * Cfg::D_SIZE; };
 
     Work wk;
@@ -593,94 +634,95 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
                 S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
     }
 
-    // Producer staging registers: raw words of this thread's pieces (bf16: words 0
-    // and 1).  Two sets: chunk m goes through set m & 1, loaded two chunks ahead of
-    // its store to LDS.  Absent gates are staged as zeros.
-    using GateW = typename std::conditional<GF32, u32x4, u32x2>::type;  // four gate values
-    struct StageRegs {
-        u32x2 q[Cfg::KPER], k[Cfg::KPER], v[Cfg::VPER], b[Cfg::VPER];
-        GateW a[Cfg::KPER];
-        uint32_t kok, vok;  // bit s: piece s lies inside the sequence
+    // Copies of chunk m into its stage (m mod NST), issued by the producer waves: copy
+    // i of a chunk goes to producer wave i mod PWAVES, and the copies past NCOPY copy
+    // nothing into the sink.  A descriptor covers exactly the chunk's valid token rows
+    // of its tensor, so rows past the end of a sequence, and absent gates (empty
+    // descriptors), arrive as zeros; past the last chunk every descriptor is empty,
+    // so each step issues the same number of copies.
+    //
+    // Each producer wave's plan is fixed for the whole sequence: copy j has a region,
+    // an LDS slot inside the stage, and a source offset per lane for full chunks.  A
+    // full chunk then costs a pointer step of 16 rows and one descriptor per copy;
+    // the last chunk, when partial, takes the general path (copy_general).
+    const uint32_t sm_base = lds_addr(sm);
+    const int pw = wv - NW;  // producer wave index (producer waves only)
+    struct CopyRegion {
+        const char* base;  // the tensor at the work's head and columns, token row 0
+        uint32_t stride, rowb;  // row stride; valid bytes per row (0: absent, an empty descriptor)
+        uint32_t dst;           // LDS byte offset of this copy's kilobyte inside a stage
+        int first, lnb, sstep;  // the region's first copy; log2 blocks per row; swizzle step
     };
-    StageRegs R0, R1;
-    auto load_chunk = [&](int c, StageRegs& r) __attribute__((always_inline)) {
-        u32x2(&rq)[Cfg::KPER] = r.q;
-        u32x2(&rk)[Cfg::KPER] = r.k;
-        GateW(&ra)[Cfg::KPER] = r.a;
-        u32x2(&rv)[Cfg::VPER] = r.v;
-        u32x2(&rb)[Cfg::VPER] = r.b;
-        uint32_t& kok = r.kok;
-        uint32_t& vok = r.vok;
-        const int nv = chunk_nv(c);
-        const int64_t low = chunk_low(c, nv);
-        const uint16_t* qb = static_cast<const uint16_t*>(p.q) + (low * qrow + qoff);
-        const uint16_t* kb = static_cast<const uint16_t*>(p.k) + (low * krow + koff);
-        const uint16_t* vb = static_cast<const uint16_t*>(p.v) + (low * vrow + voff);
-        // An absent gate re-reads q (v) at the same offsets: the same number of loads
-        // every chunk keeps the waits on the earlier register set exact.
-        constexpr uint32_t gsz = GF32 ? 4 : 2;
-        const char* gb = has_g ? static_cast<const char*>(p.g) + (low * qrow + qoff) * gsz
-                               : reinterpret_cast<const char*>(qb);
-        const char* gvb = has_gv ? reinterpret_cast<const char*>(static_cast<const uint16_t*>(p.gv) + (low * gvrow + gvoff))
-                                 : reinterpret_cast<const char*>(vb);
-        const uint32_t gvstride = (uint32_t)(has_gv ? gvrow : vrow);
-        kok = vok = 0;
-#pragma unroll
-        for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = ptid + s * PT;
-            const int t = item / (DK / 4), c4 = item % (DK / 4);
-            const bool ok = item < Cfg::KITEMS && t < nv;
-            kok |= (ok ? 1u : 0u) << s;
-            const uint32_t rr = ok ? lrow(t, nv) : 0u;  // rows past the end read row 0
-            rq[s] = load_at<u32x2>(qb, 2 * (rr * (uint32_t)qrow + 4 * c4));
-            rk[s] = load_at<u32x2>(kb, 2 * (rr * (uint32_t)krow + 4 * c4));
-            ra[s] = load_at<GateW>(gb, gsz * (rr * (uint32_t)qrow + 4 * c4));
+    auto copy_region = [&](int ci) __attribute__((always_inline)) -> CopyRegion {
+        constexpr int gsz = GF32 ? 4 : 2;
+        constexpr int LQ = __builtin_ctz(QNB), LG = __builtin_ctz(GNB), LV = __builtin_ctz(VNB);
+        CopyRegion r{static_cast<const char*>(p.q), 0u, 0u, 4u * Cfg::ST_SINK, ci, 0, 2};
+        if (ci < Cfg::NCQ) {
+            r = {static_cast<const char*>(p.q) + qoff * 2, (uint32_t)qrow * 2, DK * 2, 4u * Cfg::ST_Q, 0, LQ, 2};
+        } else if (ci < 2 * Cfg::NCQ) {
+            r = {static_cast<const char*>(p.k) + koff * 2, (uint32_t)krow * 2, DK * 2, 4u * Cfg::ST_K, Cfg::NCQ, LQ, 2};
+        } else if (ci < 2 * Cfg::NCQ + Cfg::NCG) {
+            r = {has_g ? static_cast<const char*>(p.g) + qoff * gsz : static_cast<const char*>(p.q), (uint32_t)qrow * gsz,
+                 has_g ? DK * gsz : 0u, 4u * Cfg::ST_G, 2 * Cfg::NCQ, LG, GF32 ? 4 : 2};
+        } else if (ci < 2 * Cfg::NCQ + Cfg::NCG + Cfg::NCV) {
+            r = {static_cast<const char*>(p.v) + voff * 2, (uint32_t)vrow * 2, BV * 2, 4u * Cfg::ST_V,
+                 2 * Cfg::NCQ + Cfg::NCG, LV, 2};
+        } else if (ci < Cfg::NCOPY) {
+            r = {has_gv ? reinterpret_cast<const char*>(p.gv) + gvoff * 2 : static_cast<const char*>(p.q),
+                 (uint32_t)gvrow * 2, has_gv ? BV * 2 : 0u, 4u * Cfg::ST_GV, 2 * Cfg::NCQ + Cfg::NCG + Cfg::NCV, LV, 2};
         }
-#pragma unroll
-        for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = ptid + s * PT;
-            const int t = item / (BV / 4), c4 = item % (BV / 4);
-            const bool ok = item < Cfg::VITEMS && t < nv;
-            vok |= (ok ? 1u : 0u) << s;
-            const uint32_t rr = ok ? lrow(t, nv) : 0u;
-            rv[s] = load_at<u32x2>(vb, 2 * (rr * (uint32_t)vrow + 4 * c4));
-            rb[s] = load_at<u32x2>(gvb, 2 * (rr * gvstride + 4 * c4));
-        }
+        r.dst += 1024u * (uint32_t)(ci - r.first);
+        return r;
     };
-    // Raw words to LDS (zero past the end); nothing is converted here.
-    auto store_chunk = [&](int c, const StageRegs& r) __attribute__((always_inline)) {
-        const u32x2(&rq)[Cfg::KPER] = r.q;
-        const u32x2(&rk)[Cfg::KPER] = r.k;
-        const GateW(&ra)[Cfg::KPER] = r.a;
-        const u32x2(&rv)[Cfg::VPER] = r.v;
-        const u32x2(&rb)[Cfg::VPER] = r.b;
-        const uint32_t kok = r.kok, vok = r.vok;
-        uint32_t* st = staged(c);
-        const u32x2 z2 = {0u, 0u};
-        const u32x4 z4 = {0u, 0u, 0u, 0u};
+    // Source offset of this lane's 16-byte slot (token row, swizzled block) of copy ci
+    // for a chunk of nv valid rows; past the chunk's rows it is out of range.
+    auto lane_offset = [&](const CopyRegion& r, int ci, int nv) __attribute__((always_inline)) -> int {
+        const int B = (ci - r.first) * 64 + lane, row = B >> r.lnb;
+        const int blk = (B & ((1 << r.lnb) - 1)) ^ stage_swz(row, 1 << r.lnb, r.sstep);
+        const int rs = rev ? nv - 1 - row : row;  // negative (out of range) past the end
+        return row < kGChunk ? rs * (int)r.stride + blk * 16 : 0x7ffffff0;
+    };
+    // First token row of chunk m were it full (reverse: may lie before the sequence).
+    auto full_low = [&](int m) __attribute__((always_inline)) -> int64_t {
+        return rev ? wk.start + L - (int64_t)kGChunk * (m + 1) : wk.start + (int64_t)kGChunk * m;
+    };
+    const char* cur[CPW];  // copy j's source at the next chunk's first row, as if full
+    uint32_t nrec_full[CPW], dst[CPW];
+    int off_full[CPW], cpstep[CPW];
+    if (producer) {
 #pragma unroll
-        for (int s = 0; s < Cfg::KPER; ++s) {
-            const int item = ptid + s * PT;
-            if (item < Cfg::KITEMS) {
-                const int t = item / (DK / 4), c4 = item % (DK / 4);
-                const bool ok = (kok >> s) & 1u;
-                lds_store<u32x2>(st + Cfg::ST_Q + t * SQ + 2 * c4, ok ? rq[s] : z2);
-                lds_store<u32x2>(st + Cfg::ST_K + t * SQ + 2 * c4, ok ? rk[s] : z2);
-                const bool gok = ok && has_g;
-                if constexpr (GF32) lds_store<u32x4>(st + Cfg::ST_G + t * SGR + 4 * c4, gok ? ra[s] : z4);
-                else lds_store<u32x2>(st + Cfg::ST_G + t * SGR + 2 * c4, gok ? ra[s] : z2);
-            }
+        for (int j = 0; j < CPW; ++j) {
+            const int ci = j * Cfg::PWAVES + pw;
+            const CopyRegion r = copy_region(ci);
+            cur[j] = r.base + full_low(0) * (int64_t)r.stride;
+            nrec_full[j] = r.rowb != 0 ? (uint32_t)(kGChunk - 1) * r.stride + r.rowb : 0u;
+            dst[j] = r.dst;
+            off_full[j] = lane_offset(r, ci, kGChunk);
+            cpstep[j] = (rev ? -kGChunk : kGChunk) * (int)r.stride;
+        }
+    }
+    auto copy_general = [&](int m, int j, uint32_t stage) __attribute__((always_inline)) {
+        const int ci = j * Cfg::PWAVES + pw;
+        const CopyRegion r = copy_region(ci);
+        const int nv = chunk_nv(m);
+        const char* src = r.base + chunk_low(m, nv) * (int64_t)r.stride;
+        const uint32_t nrec = r.rowb != 0 ? (uint32_t)(nv - 1) * r.stride + r.rowb : 0u;
+        copy16_to_lds(stage + r.dst, uniform_buf(src, nrec), lane_offset(r, ci, nv));
+    };
+    auto issue_chunk = [&](int m) __attribute__((always_inline)) {
+        const uint32_t stage = sm_base + 4u * (uint32_t)(Cfg::OFF_ST + (m % NST) * Cfg::ST_SIZE);
+        if (m == nch - 1 && chunk_nv(m) != kGChunk) {
+#pragma unroll
+            for (int j = 0; j < CPW; ++j) copy_general(m, j, stage);
+        } else {
+            const bool real = m < nch;
+#pragma unroll
+            for (int j = 0; j < CPW; ++j)
+                copy16_to_lds(stage + __builtin_amdgcn_readfirstlane(dst[j]), uniform_buf(cur[j], real ? nrec_full[j] : 0u),
+                              off_full[j]);
         }
 #pragma unroll
-        for (int s = 0; s < Cfg::VPER; ++s) {
-            const int item = ptid + s * PT;
-            if (item < Cfg::VITEMS) {
-                const int t = item / (BV / 4), c4 = item % (BV / 4);
-                const bool ok = (vok >> s) & 1u;
-                lds_store<u32x2>(st + Cfg::ST_V + t * SV + 2 * c4, ok ? rv[s] : z2);
-                if (has_gv) lds_store<u32x2>(st + Cfg::ST_GV + t * SV + 2 * c4, ok ? rb[s] : z2);
-            }
-        }
+        for (int j = 0; j < CPW; ++j) cur[j] += cpstep[j];
     };
 
     // Prep of chunk c (producer waves): staged(c) -> derived(c) and the chunk's flag.
@@ -701,11 +743,11 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
                 const int t = 4 * tq + tau;
                 float g0, g1;
                 if constexpr (GF32) {
-                    const f32x2 g = lds_load<f32x2>(st + Cfg::ST_G + t * SGR + 2 * pp);
+                    const f32x2 g = lds_load<f32x2>(st + Cfg::ST_G + stage_fl(t, 2 * pp, GNB));
                     g0 = g[0];
                     g1 = g[1];
                 } else {
-                    const uint32_t w = st[Cfg::ST_G + t * SGR + pp];
+                    const uint32_t w = st[Cfg::ST_G + stage_dw(t, pp, QNB)];
                     g0 = bf16_lo(w);
                     g1 = bf16_hi(w);
                 }
@@ -725,26 +767,30 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
             // kp = k ./ e (narrow pair) or k .* 2^{A_15 - A} (wide pair)
             const float off[2] = {wl ? tot[0] : 0.f, wl ? tot[1] : 0.f};
             float qh[4][2], kp[4][2], kl[4][2];
+            uint32_t kh[4];
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
                 const int t = 4 * tq + tau;
-                const uint32_t qw = st[Cfg::ST_Q + t * SQ + pp], kw = st[Cfg::ST_K + t * SQ + pp];
+                const uint32_t qw = st[Cfg::ST_Q + stage_dw(t, pp, QNB)], kw = st[Cfg::ST_K + stage_dw(t, pp, QNB)];
                 const float qv[2] = {bf16_lo(qw), bf16_hi(qw)}, kv[2] = {bf16_lo(kw), bf16_hi(kw)};
 #pragma unroll
                 for (int x = 0; x < 2; ++x) {
                     qh[tau][x] = qv[x] * hw_exp2(a[tau][x]);
                     kp[tau][x] = kv[x] * hw_exp2(off[x] - a[tau][x]);
-                    kl[tau][x] = lo_part(kp[tau][x]);
                 }
+                kh[tau] = hi_pack(kp[tau][0], kp[tau][1]);
+                kl[tau][0] = sub_bf16_lo(kh[tau], kp[tau][0]);
+                kl[tau][1] = sub_bf16_hi(kh[tau], kp[tau][1]);
             }
             const int pd = gpos_dword(pp);
 #pragma unroll
             for (int tau = 0; tau < 4; ++tau) {
                 uint32_t* qr = d + Cfg::D_QH + (4 * tq + tau) * OPR + pd;
                 uint32_t* kr = d + Cfg::D_KP + (4 * tq + tau) * OPR + pd;
-                qr[0] = hi_pack(qh[tau][0], qh[tau][1]);
-                qr[DK / 2] = lo_pack(qh[tau][0], qh[tau][1]);
-                kr[0] = hi_pack(kp[tau][0], kp[tau][1]);
+                const uint32_t qhw = hi_pack(qh[tau][0], qh[tau][1]);
+                qr[0] = qhw;
+                qr[DK / 2] = lo_pack(qhw, qh[tau][0], qh[tau][1]);
+                kr[0] = kh[tau];
                 kr[DK / 2] = pack_bf16x2(kl[tau][0], kl[tau][1]);
             }
 #pragma unroll
@@ -766,7 +812,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
 #pragma unroll
                 for (int tau = 0; tau < 4; ++tau) {
                     const int t = 4 * tq + tau;
-                    const uint32_t w = st[Cfg::ST_GV + t * SV + qq];
+                    const uint32_t w = st[Cfg::ST_GV + stage_dw(t, qq, VNB)];
                     const bool tv = t < nv;
                     la[tau][0] = tv ? kLog2e * bf16_lo(w) : 0.f;
                     la[tau][1] = tv ? kLog2e * bf16_hi(w) : 0.f;
@@ -781,7 +827,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
 #pragma unroll
                 for (int tau = 0; tau < 4; ++tau) {
                     const int t = 4 * tq + tau;
-                    const uint32_t vw = st[Cfg::ST_V + t * SV + qq];
+                    const uint32_t vw = st[Cfg::ST_V + stage_dw(t, qq, VNB)];
                     const float vv[2] = {bf16_lo(vw), bf16_hi(vw)};
 #pragma unroll
                     for (int x = 0; x < 2; ++x) {
@@ -797,15 +843,17 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
                     const int row = vblk(2 * qq + x, tq);
                     lds_store<f32x4>(reinterpret_cast<float*>(d + Cfg::D_BT) + row,
                                      f32x4{bt[0][x], bt[1][x], bt[2][x], bt[3][x]});
-                    lds_store<u32x4>(d + Cfg::D_VP + row, u32x4{hi_pack(vp[0][x], vp[1][x]), hi_pack(vp[2][x], vp[3][x]),
-                                                               lo_pack(vp[0][x], vp[1][x]), lo_pack(vp[2][x], vp[3][x])});
-                    lds_store<u32x4>(d + Cfg::D_VT + row, u32x4{hi_pack(vt[0][x], vt[1][x]), hi_pack(vt[2][x], vt[3][x]),
-                                                               lo_pack(vt[0][x], vt[1][x]), lo_pack(vt[2][x], vt[3][x])});
+                    const uint32_t p0 = hi_pack(vp[0][x], vp[1][x]), p1 = hi_pack(vp[2][x], vp[3][x]);
+                    const uint32_t t0 = hi_pack(vt[0][x], vt[1][x]), t1 = hi_pack(vt[2][x], vt[3][x]);
+                    lds_store<u32x4>(d + Cfg::D_VP + row, u32x4{p0, p1, lo_pack(p0, vp[0][x], vp[1][x]),
+                                                               lo_pack(p1, vp[2][x], vp[3][x])});
+                    lds_store<u32x4>(d + Cfg::D_VT + row, u32x4{t0, t1, lo_pack(t0, vt[0][x], vt[1][x]),
+                                                               lo_pack(t1, vt[2][x], vt[3][x])});
                 }
             } else {  // v is exact in bf16: copy it token-minor, hi only
                 uint32_t w[4];
 #pragma unroll
-                for (int tau = 0; tau < 4; ++tau) w[tau] = st[Cfg::ST_V + (4 * tq + tau) * SV + qq];
+                for (int tau = 0; tau < 4; ++tau) w[tau] = st[Cfg::ST_V + stage_dw(4 * tq + tau, qq, VNB)];
                 lds_store<u32x2>(d + Cfg::D_VT + vblk(2 * qq, tq), u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
                                                                        __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)});
                 lds_store<u32x2>(d + Cfg::D_VT + vblk(2 * qq + 1, tq),
@@ -815,43 +863,52 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
         }
     };
 
-    // Exact intra term of a wide chunk (all threads, between barriers): the summed
+    // Exact intra term of a wide chunk (producer waves; the matrix waves, which hold
+    // the state in registers, only meet its three barriers in exact_wait): the summed
     // decays A and B of every channel from the staged gates (the prep keeps its own
     // only in registers, since few chunks come this way), then W, then
-    // OI = W (v .* 2^{B_t - B_u}).
+    // OI = W (v .* 2^{B_t - B_u}).  A, B and W live in derived(c + 1), which no wave
+    // touches until the prep of chunk c + 1 starts after the last barrier here.
+    auto exact_wait = [&]() __attribute__((always_inline)) {
+        lds_barrier();
+        lds_barrier();
+        lds_barrier();
+    };
     auto exact_chunk = [&](int c) __attribute__((always_inline)) {
         const uint32_t* st = staged(c);
         const int nv = chunk_nv(c);
-        for (int i = tid; i < DK + (has_gv ? BV : 0); i += NT) {
+        float* Af = reinterpret_cast<float*>(derived(c + 1) + Cfg::X_A);
+        float* Bf = reinterpret_cast<float*>(derived(c + 1) + Cfg::X_B);
+        float* Wf = reinterpret_cast<float*>(derived(c + 1) + Cfg::X_W);
+        for (int i = ptid; i < DK + (has_gv ? BV : 0); i += PT) {
             float acc = 0.f;
             if (i < DK) {
                 for (int t = 0; t < kGChunk; ++t) {
                     float gi;
-                    if constexpr (GF32) gi = reinterpret_cast<const float*>(st + Cfg::ST_G + t * SGR)[i];
-                    else gi = bf16_half(st[Cfg::ST_G + t * SGR + (i >> 1)], i & 1);
+                    if constexpr (GF32) gi = reinterpret_cast<const float*>(st + Cfg::ST_G)[stage_fl(t, i, GNB)];
+                    else gi = bf16_half(st[Cfg::ST_G + stage_dw(t, i >> 1, QNB)], i & 1);
                     acc += t < nv ? kLog2e * gi + gg2 : 0.f;
                     Af[t * AR + i] = acc;
                 }
             } else {
                 const int j = i - DK;
                 for (int t = 0; t < kGChunk; ++t) {
-                    acc += t < nv ? kLog2e * bf16_half(st[Cfg::ST_GV + t * SV + (j >> 1)], j & 1) : 0.f;
+                    acc += t < nv ? kLog2e * bf16_half(st[Cfg::ST_GV + stage_dw(t, j >> 1, VNB)], j & 1) : 0.f;
                     Bf[t * BR + j] = acc;
                 }
             }
         }
         lds_barrier();
-        for (int e = tid; e < kGChunk * kGChunk; e += NT) {
+        for (int e = ptid; e < kGChunk * kGChunk; e += PT) {
             const int t = e >> 4, u = e & 15;
             float w = 0.f;
             if (u <= t) {
-                const uint32_t* qt = st + Cfg::ST_Q + t * SQ;
-                const uint32_t* ku = st + Cfg::ST_K + u * SQ;
                 const float* at = Af + t * AR;
                 const float* au = Af + u * AR;
-#pragma unroll 4
-                for (int i = 0; i < DK; i += 4) {
-                    const u32x2 q2 = lds_load<u32x2>(qt + i / 2), k2 = lds_load<u32x2>(ku + i / 2);
+#pragma unroll 2
+                for (int i = 0; i < DK; i += 4) {  // dwords i/2, i/2 + 1 share a staged block
+                    const u32x2 q2 = lds_load<u32x2>(st + Cfg::ST_Q + stage_dw(t, i / 2, QNB));
+                    const u32x2 k2 = lds_load<u32x2>(st + Cfg::ST_K + stage_dw(u, i / 2, QNB));
                     const f32x4 a4 = lds_load<f32x4>(at + i), b4 = lds_load<f32x4>(au + i);
                     const float q4[4] = {bf16_lo(q2[0]), bf16_hi(q2[0]), bf16_lo(q2[1]), bf16_hi(q2[1])};
                     const float k4[4] = {bf16_lo(k2[0]), bf16_hi(k2[0]), bf16_lo(k2[1]), bf16_hi(k2[1])};
@@ -862,12 +919,12 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
             Wf[t * 17 + u] = w;
         }
         lds_barrier();
-        for (int e = tid; e < kGChunk * BV; e += NT) {
+        for (int e = ptid; e < kGChunk * BV; e += PT) {
             const int t = e / BV, jj = e % BV;
             const float bt = has_gv ? Bf[t * BR + jj] : 0.f;
             float acc = 0.f;
             for (int u = 0; u <= t; ++u) {
-                const float vu = bf16_half(st[Cfg::ST_V + u * SV + (jj >> 1)], jj & 1);
+                const float vu = bf16_half(st[Cfg::ST_V + stage_dw(u, jj >> 1, VNB)], jj & 1);
                 const float dd = has_gv ? hw_exp2(bt - Bf[u * BR + jj]) : 1.f;
                 acc += Wf[t * 17 + u] * vu * dd;
             }
@@ -901,8 +958,8 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
                 const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
                 const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
                                   hi_pack(s1[2], s1[3])};
-                const u32x4 sl = {lo_pack(s0[0], s0[1]), lo_pack(s0[2], s0[3]), lo_pack(s1[0], s1[1]),
-                                  lo_pack(s1[2], s1[3])};
+                const u32x4 sl = {lo_pack(sh[0], s0[0], s0[1]), lo_pack(sh[1], s0[2], s0[3]),
+                                  lo_pack(sh[2], s1[0], s1[1]), lo_pack(sh[3], s1[2], s1[3])};
                 Oa = mfma_bf16_w(qh, sh, Oa);
                 Wa = mfma_bf16_w(kh, qh, Wa);
                 Ob = mfma_bf16_w(qh, sl, Ob);
@@ -918,7 +975,8 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
             // Intra term W (v .* 2^{-B}): k = 8lg + e covers the tokens 4lg + (e & 3)
             // with W's hi (e < 4) and lo (e >= 4) parts, against v's hi part twice.
             const u32x4 vpx = lds_load<u32x4>(d + (has_gv ? Cfg::D_VP : Cfg::D_VT) + vrow_j);
-            const u32x4 wa = {hi_pack(W[0], W[1]), hi_pack(W[2], W[3]), lo_pack(W[0], W[1]), lo_pack(W[2], W[3])};
+            const uint32_t w0 = hi_pack(W[0], W[1]), w1 = hi_pack(W[2], W[3]);
+            const u32x4 wa = {w0, w1, lo_pack(w0, W[0], W[1]), lo_pack(w1, W[2], W[3])};
             f32x4 Oi = mfma_bf16_w(wa, u32x4{vpx[0], vpx[1], vpx[0], vpx[1]}, z);
             if (has_gv) Oi = mfma_bf16_half(wa[0], wa[1], vpx[2], vpx[3], Oi);
             O += Oi;
@@ -932,8 +990,8 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
                 const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
                 const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
                                   hi_pack(s1[2], s1[3])};
-                const u32x4 sl = {lo_pack(s0[0], s0[1]), lo_pack(s0[2], s0[3]), lo_pack(s1[0], s1[1]),
-                                  lo_pack(s1[2], s1[3])};
+                const u32x4 sl = {lo_pack(sh[0], s0[0], s0[1]), lo_pack(sh[1], s0[2], s0[3]),
+                                  lo_pack(sh[2], s1[0], s1[1]), lo_pack(sh[3], s1[2], s1[3])};
                 Oa = mfma_bf16_w(qh, sh, Oa);
                 Ob = mfma_bf16_w(qh, sl, Ob);
                 Oc = mfma_bf16_w(ql, sh, Oc);
@@ -986,56 +1044,39 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW>::NT), 1) void gated_bf16_kernel(
         }
     };
 
-    // Pipeline: before the barrier that opens step c, the producers have staged
-    // chunk c+1 and derived chunk c.  During step c the matrix waves compute chunk c
-    // while the producers derive chunk c+1, stage chunk c+2 (into the buffer chunk c
-    // used) and load chunk c+4 (chunks c+3 and c+4 are in flight).  A wide chunk
-    // first takes the exact path with all waves, before its staged buffer is
-    // reused.  Chunk flags cycle through three slots: slot (c+2) mod 3 is cleared
-    // during step c, after every read of chunk c-1's flag and before chunk c+2's
-    // prep.  The two roles run separate loops with the same barriers in the same
-    // order; the producers' steps run in pairs so that each register set has a
-    // fixed name.
+    // Pipeline: before the barrier that opens step c, the producers have derived chunk
+    // c and the copies of chunk c+1 have landed.  During step c the matrix waves
+    // compute chunk c while the producers derive chunk c+1 and then issue the copies
+    // of chunk c+NST into the stage chunk c used (chunks c+2 .. c+NST-1 are in
+    // flight meanwhile).  A wide chunk first takes the exact path with all waves,
+    // before its stage is reused.  Chunk flags cycle through three slots: slot
+    // (c+2) mod 3 is cleared during step c, after every read of chunk c-1's flag and
+    // before chunk c+2's prep.  The two roles run separate loops with the same
+    // barriers in the same order.
     if (producer) {
         if (ptid == 0) wide_flag[0] = wide_flag[1] = wide_flag[2] = 0;
-        // Every step stores and loads one chunk (past the end: the last chunk again,
-        // into a buffer no prep reads), so the loads in flight are always the two
-        // register sets in order and the waits before each store are exact.
-        auto clampc = [&](int m) __attribute__((always_inline)) -> int { return min(m, nch - 1); };
-        if (nch > 0) {
-            load_chunk(0, R0);
-            load_chunk(clampc(1), R1);
-            store_chunk(0, R0);
-            load_chunk(clampc(2), R0);
-        }
+#pragma unroll
+        for (int m = 0; m < NST; ++m) issue_chunk(m);
+        wait_vmem<DEPTH * CPW>();  // this wave's copies of chunk 0 have landed
         lds_barrier();
-        if (nch > 0) {
-            prep_chunk(0);
-            store_chunk(1, R1);
-            load_chunk(clampc(3), R1);
-            auto step = [&](int c, StageRegs& r) __attribute__((always_inline)) {  // r: chunks c+2, c+4
-                if (c < nch) {
-                    lds_barrier();  // chunk c derived, chunk c+1 staged, chunk c's flag final
-                    if (wide_flag[c % 3] != 0) exact_chunk(c);
-                }
-                if (c + 1 < nch) {
-                    if (ptid == 0) wide_flag[(c + 2) % 3] = 0;
-                    prep_chunk(c + 1);
-                }
-                store_chunk(c + 2, r);
-                load_chunk(clampc(c + 4), r);
-            };
-            for (int c = 0; c < nch; c += 2) {
-                step(c, R0);
-                step(c + 1, R1);
+        if (nch > 0) prep_chunk(0);
+        for (int c = 0; c < nch; ++c) {
+            wait_vmem<(DEPTH - 1) * CPW>();  // ... of chunk c+1
+            lds_barrier();  // chunk c derived, chunk c+1 staged, chunk c's flag final
+            if (wide_flag[c % 3] != 0) exact_chunk(c);
+            if (c + 1 < nch) {
+                if (ptid == 0) wide_flag[(c + 2) % 3] = 0;
+                prep_chunk(c + 1);
             }
+            issue_chunk(c + NST);
         }
+        wait_vmem<0>();  // no copy lands after the workgroup ends
     } else {
         lds_barrier();
         for (int c = 0; c < nch; ++c) {
             lds_barrier();
             const bool fast = wide_flag[c % 3] == 0;
-            if (!fast) exact_chunk(c);
+            if (!fast) exact_wait();
             matrix_chunk(c, fast);
         }
     }
@@ -1071,7 +1112,7 @@ template <int DK, int NW>
 hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
     const dim3 grid(fwd_grid_size(p));
     // bf16: NW matrix waves plus 2 NW producer waves; fp32: NW waves
-    const dim3 block_bf16(GatedBCfg<DK, NW>::NT), block_f32(64 * NW);
+    const dim3 block_bf16(GatedBCfg<DK, NW, false>::NT), block_f32(64 * NW);
     if (bf16 && p.gk_is_f32)
         hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true>), grid, block_bf16, 0, s, p);
     else if (bf16)

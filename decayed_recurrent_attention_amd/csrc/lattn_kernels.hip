@@ -81,7 +81,6 @@ __device__ inline void make_lane_decay(float g2, int lr, int lg, LaneDecay& d) {
 // neighbouring packed sequences need no branches.  Offsets stay 32-bit because
 // every descriptor is rebased at its chunk.
 // ---------------------------------------------------------------------------
-constexpr int kRawBufferDword3 = 0x00020000;  // raw (untyped) buffer, gfx9 family
 
 __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRawBufferDword3);
@@ -125,42 +124,6 @@ __device__ inline u32x2 lds_tr16(const uint16_t* p) {
 __device__ inline bf16x8 cat_bf16(u32x2 a, u32x2 b) {
     const u32x4 w = {a[0], a[1], b[0], b[1]};
     return __builtin_bit_cast(bf16x8, w);
-}
-
-// ---------------------------------------------------------------------------
-// Direct global -> LDS copies (buffer_load_dwordx4 ... lds).  One instruction moves
-// 16 bytes per lane to LDS address M0 + 16 * lane, so a wave fills one contiguous
-// kilobyte while each lane picks its own source.  The copies are issued from
-// inline assembly: the compiler would otherwise make every later LDS access wait
-// for all of them.  Their completion is awaited explicitly (vmcnt) before the
-// barrier that publishes a stage, and every barrier in the chunk loop waits for
-// LDS operations only.
-// ---------------------------------------------------------------------------
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-struct RawBuf {
-    i32x4 d;  // raw buffer descriptor (base, stride 0, size in bytes, gfx9 raw format)
-};
-__device__ inline RawBuf raw_buf(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    RawBuf r;
-    r.d = i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xffffu), (int)bytes, kRawBufferDword3};
-    return r;
-}
-__device__ inline uint32_t lds_addr(const void* p) {
-    typedef __attribute__((address_space(3))) const void* lds_ptr;
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)p);
-}
-__device__ inline void copy16_to_lds(uint32_t lds_base, const RawBuf& r, int voffset) {
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-                 :
-                 : "s"(lds_base), "v"(voffset), "s"(r.d)
-                 : "memory", "m0");
-}
-template <int N>
-__device__ inline void wait_vmem() {  // at most N vector-memory operations outstanding
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 // ---------------------------------------------------------------------------
