@@ -171,6 +171,17 @@ __device__ inline void wait_vmem() {  // at most N vector-memory operations outs
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane s
+// supplies the address of four consecutive 16-bit elements; lane i receives
+// element (i & 3) of the piece addressed by lane 4e + (i >> 2), as its element e.
+// With lane s pointing at row (r0 + (s >> 2)), columns c(s & 3) .. c(s & 3) + 3 of
+// a row-major tile, lane i therefore receives column c(i >> 2) + (i & 3) of rows
+// r0 .. r0 + 3: one column per lane, four consecutive rows.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ inline u32x2 lds_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p));
+}
 __device__ inline f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -417,15 +417,20 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_f32_kernel(const FwdParams p
 template <int DK, int NW, bool GF32>
 struct GatedBCfg {
     static constexpr int BV = 16 * NW;
-    // Matrix waves first, then two producer waves per matrix wave: the producers'
-    // prep is latency-bound, and twice the waves hide more of it.
-    static constexpr int MTH = 64 * NW;      // matrix threads
-    static constexpr int PW = 2;             // producer waves per matrix wave
+    static constexpr int MT = DK / 16;
+    static constexpr int KB = DK / 32;  // 32-deep blocks of the dk contraction
+    // dk split: each 16-column block's state is held by DS matrix waves, one per half
+    // of the dk rows (DS = 2 where the dk blocks split evenly), so two matrix waves
+    // share each SIMD and hide each other's latencies.
+    static constexpr int DS = KB % 2 == 0 ? 2 : 1;
+    static constexpr int MTW = MT / DS, KBW = KB / DS;  // state tiles and dk blocks per matrix wave
+    // Matrix waves first, then two producer waves per 16-column block.
+    static constexpr int MW = NW * DS;       // matrix waves
+    static constexpr int MTH = 64 * MW;      // matrix threads
+    static constexpr int PW = 2;             // producer waves per column block
     static constexpr int PWAVES = NW * PW;   // producer waves
     static constexpr int PT = 64 * PWAVES;   // producer threads
     static constexpr int NT = MTH + PT;      // all threads
-    static constexpr int MT = DK / 16;
-    static constexpr int KB = DK / 32;  // 32-deep blocks of the dk contraction
     // One staged raw chunk, filled by direct global-to-LDS copies of a kilobyte each:
     // rows of q, k and the key gate (bf16, or fp32 when two gates were summed) over DK
     // channels, then rows of v and the value gate over BV columns, each region rounded
@@ -450,20 +455,18 @@ struct GatedBCfg {
     static constexpr int ST_SINK = ST_GV + 256 * NCV;
     static constexpr int ST_SIZE = ST_SINK + (SINK ? 256 : 0);
     // Decayed operands read along dk (token-major): bf16 hi half, lo half, 8 dwords
-    // of pad (16-byte blocks per row = 2 mod 32: conflict-free operand reads).
+    // of pad (16-byte blocks per row = 2 mod 32: conflict-free operand reads).  The
+    // state update reads the key rows transposed (lds_tr16).
     static constexpr int OPR = DK + 8;
-    // Token-minor rows (a row per channel): four 16-byte blocks of four tokens,
-    // [hi x4 | lo x4] in bf16 or four fp32.  Key rows carry two blocks of pad; value
-    // rows swizzle their blocks instead (vblk).
-    static constexpr int TMR = 24;
+    // Token-minor value rows (a row per column): four 16-byte blocks of four tokens,
+    // [hi x4 | lo x4] in bf16 or four fp32, blocks swizzled (vblk).
     static constexpr int VMR = 16;
     // fp32 summed decays for the exact path (token-major).
     static constexpr int AR = DK + 4, BR = BV + 4;
     // One set of decayed operands.
     static constexpr int D_QH = 0;
     static constexpr int D_KP = D_QH + kGChunk * OPR;
-    static constexpr int D_KT = D_KP + kGChunk * OPR;
-    static constexpr int D_VP = D_KT + DK * TMR;
+    static constexpr int D_VP = D_KP + kGChunk * OPR;
     static constexpr int D_VT = D_VP + BV * VMR;
     static constexpr int D_BT = D_VT + BV * VMR;
     static constexpr int D_PRE = D_BT + BV * VMR;
@@ -473,20 +476,25 @@ struct GatedBCfg {
     // The exact path's summed decays A and B and its W live in the set of decayed
     // operands that no wave uses at that point.
     static constexpr int X_A = 0, X_B = X_A + kGChunk * AR, X_W = X_B + kGChunk * BR, X_END = X_W + kGChunk * 17;
+    // The partial outputs one wave of each pair hands to the other (DS = 2), per
+    // chunk parity: a 16x16 fp32 tile per column block.
+    static constexpr int XO_SIZE = DS == 2 ? 2 * NW * 256 : 0;
     // LDS: the staged ring (four chunks where they fit, else three), two sets of
-    // decayed operands and the exact path's intra term OI.
-    static constexpr int FIXED = 2 * D_SIZE + kGChunk * BR;
+    // decayed operands, the exact path's intra term OI and the partial outputs.
+    static constexpr int FIXED = 2 * D_SIZE + kGChunk * BR + XO_SIZE;
     static constexpr int NST = (4 * ST_SIZE + FIXED) * 4 <= kLdsBudget ? 4 : 3;
     static constexpr int OFF_ST = 0;
     static constexpr int OFF_D = OFF_ST + NST * ST_SIZE;
     static constexpr int OFF_OI = OFF_D + 2 * D_SIZE;
-    static constexpr int DWORDS = OFF_OI + kGChunk * BR;
+    static constexpr int OFF_XO = OFF_OI + kGChunk * BR;
+    static constexpr int DWORDS = OFF_XO + XO_SIZE;
     // Prep items: channel pairs x quarters.
     static constexpr int KPREP = 2 * DK, VPREP = 2 * BV;
     static_assert(DK % 32 == 0 && DK <= 128, "dk must be 32, 64 or 128");
     static_assert(X_END <= D_SIZE, "exact-path buffers fit a set of decayed operands");
     static_assert(CPW * 3 <= 63, "vmcnt range");
-    static_assert(D_SIZE % 4 == 0 && OFF_D % 4 == 0 && OFF_OI % 4 == 0 && D_PRE % 4 == 0, "16-byte alignment");
+    static_assert(D_SIZE % 4 == 0 && OFF_D % 4 == 0 && OFF_OI % 4 == 0 && OFF_XO % 4 == 0 && D_PRE % 4 == 0,
+                  "16-byte alignment");
     static_assert(DWORDS * 4 <= kLdsBudget, "LDS budget");
 };
 
@@ -587,8 +595,9 @@ __device__ inline void quarter_sums(const float (&la)[4][2], int tq, float (&a)[
 template <int DK, int NW, bool GF32>
 __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_kernel(const FwdParams p) {
     using Cfg = GatedBCfg<DK, NW, GF32>;
-    constexpr int BV = Cfg::BV, NT = Cfg::NT, PT = Cfg::PT, MT = Cfg::MT, KB = Cfg::KB;
-    constexpr int OPR = Cfg::OPR, TMR = Cfg::TMR, AR = Cfg::AR, BR = Cfg::BR;
+    constexpr int BV = Cfg::BV, PT = Cfg::PT;
+    constexpr int DS = Cfg::DS, MW = Cfg::MW, MTW = Cfg::MTW, KBW = Cfg::KBW;
+    constexpr int OPR = Cfg::OPR, AR = Cfg::AR, BR = Cfg::BR;
     constexpr int QNB = Cfg::QNB, GNB = Cfg::GNB, VNB = Cfg::VNB, NST = Cfg::NST, DEPTH = NST - 1, CPW = Cfg::CPW;
     __shared__ __attribute__((aligned(16))) uint32_t sm[Cfg::DWORDS];
     __shared__ int wide_flag[3];  // per chunk mod 3: take the exact VALU path
@@ -600,7 +609,9 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
     if (!decode_work(p, blockIdx.x, wk)) return;
     const int tid = threadIdx.x, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const bool producer = wv >= NW;
+    const bool producer = wv >= MW;
+    // Matrix waves: column block w, dk half h (rows 16 MTW h .. 16 MTW (h + 1) - 1).
+    const int w = wv % NW, h = wv / NW;
     const int ptid = tid - Cfg::MTH;  // producer thread index
     const int H = p.num_heads, dv = p.dv;
     const int64_t L = wk.len;
@@ -608,7 +619,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
     const bool rev = p.reverse != 0;
     const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
     const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
-    const int j = 16 * wv + lr;       // matrix waves: this lane's column inside the block
+    const int j = 16 * w + lr;        // matrix waves: this lane's column inside the block
     const int vcol = wk.vb * BV + j;  // ... of v and o
     const int64_t qrow = (int64_t)H * DK, krow = (int64_t)p.num_kv_heads * DK;
     const int64_t vrow = (int64_t)p.num_kv_heads * dv, gvrow = (int64_t)H * dv;
@@ -624,14 +635,14 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
     };
     auto lrow = [&](int t, int nv) __attribute__((always_inline)) -> uint32_t { return (uint32_t)(rev ? nv - 1 - t : t); };
 
-    f32x4 S[MT];
+    f32x4 S[MTW];  // this wave's state tiles: global tile h MTW + m
     const int64_t st_off = ((int64_t)wk.n * H + wk.h) * DK * dv;
     if (!producer) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int m = 0; m < MTW; ++m)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
-                S[mt][ii] = p.init ? p.init[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] : 0.f;
+                S[m][ii] = p.init ? p.init[st_off + (int64_t)(16 * (h * MTW + m) + 4 * lg + ii) * dv + vcol] : 0.f;
     }
 
     // Copies of chunk m into its stage (m mod NST), issued by the producer waves: copy
@@ -646,7 +657,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
     // full chunk then costs a pointer step of 16 rows and one descriptor per copy;
     // the last chunk, when partial, takes the general path (copy_general).
     const uint32_t sm_base = lds_addr(sm);
-    const int pw = wv - NW;  // producer wave index (producer waves only)
+    const int pw = wv - MW;  // producer wave index (producer waves only)
     struct CopyRegion {
         const char* base;  // the tensor at the work's head and columns, token row 0
         uint32_t stride, rowb;  // row stride; valid bytes per row (0: absent, an empty descriptor)
@@ -793,11 +804,6 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
                 kr[0] = kh[tau];
                 kr[DK / 2] = pack_bf16x2(kl[tau][0], kl[tau][1]);
             }
-#pragma unroll
-            for (int x = 0; x < 2; ++x)
-                lds_store<u32x4>(d + Cfg::D_KT + (2 * pp + x) * TMR + 4 * tq,
-                                 u32x4{hi_pack(kp[0][x], kp[1][x]), hi_pack(kp[2][x], kp[3][x]),
-                                       pack_bf16x2(kl[0][x], kl[1][x]), pack_bf16x2(kl[2][x], kl[3][x])});
         }
         // Value columns 2qq, 2qq+1 of the block, tokens 4tq .. 4tq+3; the last
         // producer threads take these items (the key prep fills the first ones when
@@ -933,13 +939,15 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
         lds_barrier();
     };
 
-    // Matrix phase of chunk c (matrix waves).
-    auto matrix_chunk = [&](int c, bool fast) __attribute__((always_inline)) {
+    // Matrix phase of chunk c (matrix waves) over this wave's half of dk: returns its
+    // share of the chunk's output tile (with DS = 2 the pair's shares add up to it;
+    // the products are linear in the dk contraction, W's causal mask and bf16 split
+    // included) and advances its state rows.
+    auto matrix_chunk = [&](int c, bool fast) __attribute__((always_inline)) -> f32x4 {
         const uint32_t* d = derived(c);
-        const uint32_t* QHw = d + Cfg::D_QH;
-        const uint32_t* KPw = d + Cfg::D_KP;
+        const uint32_t* QHw = d + Cfg::D_QH + lr * OPR + 4 * lg + 16 * KBW * h;
+        const uint32_t* KPw = d + Cfg::D_KP + lr * OPR + 4 * lg + 16 * KBW * h;
         const float* BTf = reinterpret_cast<const float*>(d + Cfg::D_BT);
-        const int nv = chunk_nv(c);
         // Inter-chunk part (q .* 2^A) S: the state tile pair (2s, 2s+1), split into
         // bf16 hi + lo, is the B operand of dk block s.  Fast path: W^T = (k ./ e)
         // (q .* e)^T in the same loop (q .* e is its B operand too); lane holds
@@ -950,9 +958,9 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
         if (fast) {
             f32x4 Oa = z, Ob = z, Oc = z, Wa = z, Wb = z, Wc = z;
 #pragma unroll
-            for (int s = 0; s < KB; ++s) {
-                const uint32_t* qr = QHw + lr * OPR + 16 * s + 4 * lg;
-                const uint32_t* kr = KPw + lr * OPR + 16 * s + 4 * lg;
+            for (int s = 0; s < KBW; ++s) {
+                const uint32_t* qr = QHw + 16 * s;
+                const uint32_t* kr = KPw + 16 * s;
                 const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
                 const u32x4 kh = lds_load<u32x4>(kr), kl = lds_load<u32x4>(kr + DK / 2);
                 const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
@@ -984,8 +992,8 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
         } else {
             f32x4 Oa = z, Ob = z, Oc = z;
 #pragma unroll
-            for (int s = 0; s < KB; ++s) {
-                const uint32_t* qr = QHw + lr * OPR + 16 * s + 4 * lg;
+            for (int s = 0; s < KBW; ++s) {
+                const uint32_t* qr = QHw + 16 * s;
                 const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
                 const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
                 const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
@@ -998,50 +1006,79 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
             }
             O = (Oa + Ob) + Oc;
             if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
+            if (h == 0) {  // the exact intra term, once per pair
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) O[ii] += OIf[(4 * lg + ii) * BR + j];
+                for (int ii = 0; ii < 4; ++ii) O[ii] += OIf[(4 * lg + ii) * BR + j];
+            }
         }
-        {
-            const int64_t orow = (int64_t)H * dv;
-            char* ob = reinterpret_cast<char*>(p.o + (chunk_low(c, nv) * orow + (int64_t)wk.h * dv + wk.vb * BV));
+
+        // State update of this wave's rows: S <- post .* (pre .* 2^{B_15}^T .* S +
+        // kp^T vt), contracting over the 16 tokens with kp's hi and lo parts in one k
+        // range.  kp^T comes from transposing reads of the token-major key rows: lane
+        // group lg takes tokens 4lg .. 4lg+3; lane s of the group addresses token row
+        // 4lg + (s >> 2) at the four positions of channels 16mt + 4(s & 3) .. +3, so
+        // lane lr receives channel 16mt + lr (the position map of gpos_dword).
+        const float* PREf = reinterpret_cast<const float*>(d + Cfg::D_PRE);
+        const float* POSTf = reinterpret_cast<const float*>(d + Cfg::D_POST);
+        const float eb = has_gv ? reinterpret_cast<const float*>(d + Cfg::D_EB)[j] : 1.f;
+        if (!fast) {
+#pragma unroll
+            for (int m = 0; m < MTW; ++m) {
+                const f32x4 pre = lds_load<f32x4>(PREf + 16 * (h * MTW + m) + 4 * lg);
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) S[m][ii] *= pre[ii] * eb;
+            }
+        } else if (has_gv) {
+#pragma unroll
+            for (int m = 0; m < MTW; ++m) S[m] *= eb;
+        }
+        // Every operand is read first (the gated branch below would otherwise split
+        // the reads into one wait per tile).
+        const u32x4 vtx = lds_load<u32x4>(d + Cfg::D_VT + vrow_j);
+        const u32x4 vt2 = {vtx[0], vtx[1], vtx[0], vtx[1]};
+        const uint16_t* ktr = reinterpret_cast<const uint16_t*>(d + Cfg::D_KP) + (4 * lg + (lr >> 2)) * (2 * OPR) +
+                              8 * (lr & 3) + 32 * KBW * h;
+        u32x4 ktx[MTW];
+        f32x4 post[MTW];
+#pragma unroll
+        for (int m = 0; m < MTW; ++m) {
+            const uint16_t* kt = ktr + 32 * (m >> 1) + 4 * (m & 1);  // tile h MTW + m (MTW is even)
+            const u32x2 khi = lds_tr16(kt), klo = lds_tr16(kt + DK);
+            ktx[m] = u32x4{khi[0], khi[1], klo[0], klo[1]};
+            post[m] = lds_load<f32x4>(POSTf + 16 * (h * MTW + m) + 4 * lg);
+        }
+#pragma unroll
+        for (int m = 0; m < MTW; ++m) S[m] = mfma_bf16_w(ktx[m], vt2, S[m]);
+        if (has_gv) {
+#pragma unroll
+            for (int m = 0; m < MTW; ++m) S[m] = mfma_bf16_half(ktx[m][0], ktx[m][1], vtx[2], vtx[3], S[m]);
+        }
+#pragma unroll
+        for (int m = 0; m < MTW; ++m)
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) S[m][ii] *= post[m][ii];
+        return O;
+    };
+    // Output rows of chunk c from its finished tile.
+    auto store_out = [&](int c, const f32x4& O) __attribute__((always_inline)) {
+        const int nv = chunk_nv(c);
+        const int64_t orow = (int64_t)H * dv;
+        char* ob = reinterpret_cast<char*>(p.o + (chunk_low(c, nv) * orow + (int64_t)wk.h * dv + wk.vb * BV));
+        if (nv == kGChunk) {  // (uniform) no row to skip
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                *reinterpret_cast<float*>(ob + 4 * (lrow(4 * lg + ii, kGChunk) * (uint32_t)orow + j)) = p.scale * O[ii];
+        } else {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii) {
                 const int t = 4 * lg + ii;
                 if (t < nv) *reinterpret_cast<float*>(ob + 4 * (lrow(t, nv) * (uint32_t)orow + j)) = p.scale * O[ii];
             }
         }
-
-        // State update: S <- post .* (pre .* 2^{B_15}^T .* S + kp^T vt), contracting
-        // over the 16 tokens with kp's hi and lo parts in one k range (token-minor
-        // operands: lane group lg reads tokens 4lg .. 4lg+3).
-        const float* PREf = reinterpret_cast<const float*>(d + Cfg::D_PRE);
-        const float* POSTf = reinterpret_cast<const float*>(d + Cfg::D_POST);
-        const float eb = has_gv ? reinterpret_cast<const float*>(d + Cfg::D_EB)[j] : 1.f;
-        if (!fast) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const f32x4 pre = lds_load<f32x4>(PREf + 16 * mt + 4 * lg);
-#pragma unroll
-                for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= pre[ii] * eb;
-            }
-        } else if (has_gv) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) S[mt] *= eb;
-        }
-        const u32x4 vtx = lds_load<u32x4>(d + Cfg::D_VT + vrow_j);
-        const u32x4 vt2 = {vtx[0], vtx[1], vtx[0], vtx[1]};
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const u32x4 ktx = lds_load<u32x4>(d + Cfg::D_KT + (16 * mt + lr) * TMR + 4 * lg);
-            S[mt] = mfma_bf16_w(ktx, vt2, S[mt]);
-            if (has_gv) S[mt] = mfma_bf16_half(ktx[0], ktx[1], vtx[2], vtx[3], S[mt]);
-        }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-            const f32x4 post = lds_load<f32x4>(POSTf + 16 * mt + 4 * lg);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) S[mt][ii] *= post[ii];
-        }
+    };
+    // The partial output tile that wave h = 1 of column block w hands over for chunk c.
+    auto xo = [&](int c) __attribute__((always_inline)) -> float* {
+        return reinterpret_cast<float*>(sm + Cfg::OFF_XO + (((c & 1) * NW + w) * 64 + lane) * 4);
     };
 
     // Pipeline: before the barrier that opens step c, the producers have derived chunk
@@ -1070,23 +1107,46 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
             }
             issue_chunk(c + NST);
         }
+        if constexpr (DS == 2) lds_barrier();  // the matrix waves' last hand-over
         wait_vmem<0>();  // no copy lands after the workgroup ends
     } else {
+        // With DS = 2, wave h = 1 leaves its share of chunk c in LDS; after the next
+        // barrier wave h = 0 adds it to its own and stores the chunk, one step later
+        // (a last barrier after the loop hands over the final chunk).
         lds_barrier();
+        f32x4 Oh = {0.f, 0.f, 0.f, 0.f};
         for (int c = 0; c < nch; ++c) {
             lds_barrier();
             const bool fast = wide_flag[c % 3] == 0;
             if (!fast) exact_wait();
-            matrix_chunk(c, fast);
+            f32x4 prev = {0.f, 0.f, 0.f, 0.f};  // (DS = 2, h = 0) the partner's share of chunk c - 1
+            if constexpr (DS == 2) {
+                if (h == 0 && c > 0) prev = lds_load<f32x4>(xo(c - 1));
+            }
+            const f32x4 O = matrix_chunk(c, fast);
+            if constexpr (DS == 2) {
+                if (h == 1) {
+                    lds_store<f32x4>(xo(c), O);
+                } else {
+                    if (c > 0) store_out(c - 1, Oh + prev);
+                    Oh = O;
+                }
+            } else {
+                store_out(c, O);
+            }
+        }
+        if constexpr (DS == 2) {
+            lds_barrier();
+            if (h == 0 && nch > 0) store_out(nch - 1, Oh + lds_load<f32x4>(xo(nch - 1)));
         }
     }
 
     if (!producer && p.final_state) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int m = 0; m < MTW; ++m)
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
-                p.final_state[st_off + (int64_t)(16 * mt + 4 * lg + ii) * dv + vcol] = S[mt][ii];
+                p.final_state[st_off + (int64_t)(16 * (h * MTW + m) + 4 * lg + ii) * dv + vcol] = S[m][ii];
     }
 }
 
