@@ -956,7 +956,9 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
         f32x4 O;
         const int vrow_j = vblk(j, lg);
         if (fast) {
-            f32x4 Oa = z, Ob = z, Oc = z, Wa = z, Wb = z, Wc = z;
+            // One accumulator per product: consecutive MFMAs accumulate in place.
+            f32x4 W = z;
+            O = z;
 #pragma unroll
             for (int s = 0; s < KBW; ++s) {
                 const uint32_t* qr = QHw + 16 * s;
@@ -968,15 +970,13 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
                                   hi_pack(s1[2], s1[3])};
                 const u32x4 sl = {lo_pack(sh[0], s0[0], s0[1]), lo_pack(sh[1], s0[2], s0[3]),
                                   lo_pack(sh[2], s1[0], s1[1]), lo_pack(sh[3], s1[2], s1[3])};
-                Oa = mfma_bf16_w(qh, sh, Oa);
-                Wa = mfma_bf16_w(kh, qh, Wa);
-                Ob = mfma_bf16_w(qh, sl, Ob);
-                Wb = mfma_bf16_w(kh, ql, Wb);
-                Oc = mfma_bf16_w(ql, sh, Oc);
-                Wc = mfma_bf16_w(kl, qh, Wc);
+                O = mfma_bf16_w(qh, sh, O);
+                W = mfma_bf16_w(kh, qh, W);
+                O = mfma_bf16_w(qh, sl, O);
+                W = mfma_bf16_w(kh, ql, W);
+                O = mfma_bf16_w(ql, sh, O);
+                W = mfma_bf16_w(kl, qh, W);
             }
-            O = (Oa + Ob) + Oc;
-            f32x4 W = (Wa + Wb) + Wc;
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 if (4 * lg + ii > lr) W[ii] = 0.f;  // causal: u <= t
@@ -990,7 +990,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
             O += Oi;
             if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
         } else {
-            f32x4 Oa = z, Ob = z, Oc = z;
+            O = z;
 #pragma unroll
             for (int s = 0; s < KBW; ++s) {
                 const uint32_t* qr = QHw + 16 * s;
@@ -1000,11 +1000,10 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
                                   hi_pack(s1[2], s1[3])};
                 const u32x4 sl = {lo_pack(sh[0], s0[0], s0[1]), lo_pack(sh[1], s0[2], s0[3]),
                                   lo_pack(sh[2], s1[0], s1[1]), lo_pack(sh[3], s1[2], s1[3])};
-                Oa = mfma_bf16_w(qh, sh, Oa);
-                Ob = mfma_bf16_w(qh, sl, Ob);
-                Oc = mfma_bf16_w(ql, sh, Oc);
+                O = mfma_bf16_w(qh, sh, O);
+                O = mfma_bf16_w(qh, sl, O);
+                O = mfma_bf16_w(ql, sh, O);
             }
-            O = (Oa + Ob) + Oc;
             if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
             if (h == 0) {  // the exact intra term, once per pair
 #pragma unroll
