@@ -404,12 +404,14 @@ __global__ __launch_bounds__(64 * NW, 1) void gated_f32_kernel(const FwdParams p
 // (per-row factors pre and post); a chunk holding one takes the exact VALU path of
 // gated_f32_kernel for W and the intra term.
 //
-// Roles: a workgroup of 3 NW waves.  Waves 0 .. NW-1 (matrix waves) own 16 value
-// columns each and the state in accumulator registers; waves NW .. 3NW-1 (producer
-// waves, two per matrix wave) stage the chunks from global memory and derive the
-// decayed operands.  With one matrix wave and two producer waves per SIMD, the prep
-// of chunk c+1 runs while the matrix waves compute chunk c.  LDS holds two staged raw
-// chunks and two sets of decayed operands; one barrier per chunk hands both over.
+// Roles: a workgroup of NW blocks of 16 value columns.  Matrix waves come first: DS
+// per block (GatedBCfg::DS), each holding the state of the block's columns over one
+// half of the dk rows in accumulator registers; then two producer waves per block,
+// which copy the raw chunks from global memory into a ring of LDS stages and derive
+// the decayed operands.  The prep of chunk c+1 runs while the matrix waves compute
+// chunk c; LDS holds the ring and two sets of decayed operands, and one barrier per
+// chunk hands a set over.  With DS = 2 the two waves of a block each compute their
+// half of the chunk's output tile; one hands its half to the other through LDS.
 // Prep: one item (channel pair, quarter of the chunk) per producer lane, the four
 // quarters of a pair in one lane quad; each quarter sums its four decays and the quad
 // exchanges the partial sums (DPP), so every lane has its tokens' A_t and A_15.
