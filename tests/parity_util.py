@@ -82,6 +82,31 @@ def oracle_run_bwd(w: inputs.Workload, data: dict, grads: dict, reverse: bool | 
                              cu_seqlens=data["cu_seqlens"])
 
 
+def gpu_run_gated(w: inputs.Workload, data: dict, gates: dict, use_gg: bool = True, reverse: bool | None = None):
+    """Run the HIP gated forward with the gates given (None: absent) and, when use_gg,
+    the Lightning g_gamma of the workload's layer; returns device tensors (o, final_state)."""
+    import torch
+
+    rev = w.reverse if reverse is None else reverse
+    gg = lattn.lattn_lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers) if use_gg else None
+    dev = {n: to_device(data[n], w.dtype) for n in ("q", "k", "v")}
+    gd = {n: to_device(x, w.dtype) for n, x in gates.items() if x is not None}
+    return lattn.recurrent_gated(dev["q"], dev["k"], dev["v"], **gd,
+                                 g_gamma=None if gg is None else torch.from_numpy(gg).cuda(),
+                                 softmax_scale=w.scale, initial_state=to_device(data["initial_state"], "f32"),
+                                 reverse=rev, cu_seqlens=data["cu_seqlens"])
+
+
+def oracle_run_gated(w: inputs.Workload, data: dict, gates: dict, use_gg: bool = True,
+                     reverse: bool | None = None):
+    rev = w.reverse if reverse is None else reverse
+    orc = oracle.load()
+    gg = orc.lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers) if use_gg else None
+    return orc.recurrent_gated_fwd(data["q"], data["k"], data["v"], **gates, g_gamma=gg, scale=w.scale,
+                                   initial_state=data["initial_state"], reverse=rev,
+                                   cu_seqlens=data["cu_seqlens"])
+
+
 class Accum:
     """Streaming parity statistics of one output tensor: the whole-tensor maximum error
     and sum of squares, and the same per (sequence, head) slice.  Feed it pieces of the

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 from decayed_recurrent_attention_amd import inputs, lattn
-from tests.parity_util import TOL, Accum, check, check_fwd, to_device
+from tests.parity_util import TOL, Accum, check, check_fwd, gpu_run_gated, oracle_run_gated, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -21,21 +21,8 @@ def _gpu():
 
 
 def _run(w, data, gates, use_gg=True, reverse=None):
-    import torch
-
-    rev = w.reverse if reverse is None else reverse
-    gg = lattn.lattn_lightning_g_gamma(w.num_heads, w.layer_idx, w.num_layers) if use_gg else None
-    dev = {n: to_device(data[n], w.dtype) for n in ("q", "k", "v")}
-    gd = {n: to_device(x, w.dtype) for n, x in gates.items() if x is not None}
-    o, fs = lattn.recurrent_gated(dev["q"], dev["k"], dev["v"], **gd,
-                                  g_gamma=None if gg is None else torch.from_numpy(gg).cuda(),
-                                  softmax_scale=w.scale, initial_state=to_device(data["initial_state"], "f32"),
-                                  reverse=rev, cu_seqlens=data["cu_seqlens"])
-    import oracle
-
-    o_ref, fs_ref = oracle.load().recurrent_gated_fwd(
-        data["q"], data["k"], data["v"], **gates, g_gamma=gg, scale=w.scale,
-        initial_state=data["initial_state"], reverse=rev, cu_seqlens=data["cu_seqlens"])
+    o, fs = gpu_run_gated(w, data, gates, use_gg, reverse)
+    o_ref, fs_ref = oracle_run_gated(w, data, gates, use_gg, reverse)
     return o, fs, o_ref, fs_ref
 
 
