@@ -945,40 +945,41 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
     // share of the chunk's output tile (with DS = 2 the pair's shares add up to it;
     // the products are linear in the dk contraction, W's causal mask and bf16 split
     // included) and advances its state rows.
-    auto matrix_chunk = [&](int c, bool fast) __attribute__((always_inline)) -> f32x4 {
+    auto matrix_chunk = [&](int c) __attribute__((always_inline)) -> f32x4 {
         const uint32_t* d = derived(c);
         const uint32_t* QHw = d + Cfg::D_QH + lr * OPR + 4 * lg + 16 * KBW * h;
         const uint32_t* KPw = d + Cfg::D_KP + lr * OPR + 4 * lg + 16 * KBW * h;
         const float* BTf = reinterpret_cast<const float*>(d + Cfg::D_BT);
         // Inter-chunk part (q .* 2^A) S: the state tile pair (2s, 2s+1), split into
-        // bf16 hi + lo, is the B operand of dk block s.  Fast path: W^T = (k ./ e)
-        // (q .* e)^T in the same loop (q .* e is its B operand too); lane holds
-        // W[t = lr][u = 4lg + ii].
+        // bf16 hi + lo, is the B operand of dk block s.  W^T = (k ./ e) (q .* e)^T in
+        // the same loop (q .* e is its B operand too); lane holds W[t = lr][u = 4lg + ii].
+        // One accumulator per product: consecutive MFMAs accumulate in place.
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 O;
+        f32x4 O = z, W = z;
         const int vrow_j = vblk(j, lg);
-        if (fast) {
-            // One accumulator per product: consecutive MFMAs accumulate in place.
-            f32x4 W = z;
-            O = z;
 #pragma unroll
-            for (int s = 0; s < KBW; ++s) {
-                const uint32_t* qr = QHw + 16 * s;
-                const uint32_t* kr = KPw + 16 * s;
-                const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
-                const u32x4 kh = lds_load<u32x4>(kr), kl = lds_load<u32x4>(kr + DK / 2);
-                const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
-                const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
-                                  hi_pack(s1[2], s1[3])};
-                const u32x4 sl = {lo_pack(sh[0], s0[0], s0[1]), lo_pack(sh[1], s0[2], s0[3]),
-                                  lo_pack(sh[2], s1[0], s1[1]), lo_pack(sh[3], s1[2], s1[3])};
-                O = mfma_bf16_w(qh, sh, O);
-                W = mfma_bf16_w(kh, qh, W);
-                O = mfma_bf16_w(qh, sl, O);
-                W = mfma_bf16_w(kh, ql, W);
-                O = mfma_bf16_w(ql, sh, O);
-                W = mfma_bf16_w(kl, qh, W);
-            }
+        for (int s = 0; s < KBW; ++s) {
+            const uint32_t* qr = QHw + 16 * s;
+            const uint32_t* kr = KPw + 16 * s;
+            const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
+            const u32x4 kh = lds_load<u32x4>(kr), kl = lds_load<u32x4>(kr + DK / 2);
+            const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
+            const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
+                              hi_pack(s1[2], s1[3])};
+            const u32x4 sl = {lo_pack(sh[0], s0[0], s0[1]), lo_pack(sh[1], s0[2], s0[3]),
+                              lo_pack(sh[2], s1[0], s1[1]), lo_pack(sh[3], s1[2], s1[3])};
+            O = mfma_bf16_w(qh, sh, O);
+            W = mfma_bf16_w(kh, qh, W);
+            O = mfma_bf16_w(qh, sl, O);
+            W = mfma_bf16_w(kh, ql, W);
+            O = mfma_bf16_w(ql, sh, O);
+            W = mfma_bf16_w(kl, qh, W);
+        }
+        // The chunk's path, read only now so that the products above do not wait for
+        // it (W is wasted on a wide chunk; those are rare).  A wide chunk's exact intra
+        // term comes from the producers, whose three barriers this wave meets here.
+        const bool fast = wide_flag[c % 3] == 0;
+        if (fast) {
 #pragma unroll
             for (int ii = 0; ii < 4; ++ii)
                 if (4 * lg + ii > lr) W[ii] = 0.f;  // causal: u <= t
@@ -992,20 +993,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
             O += Oi;
             if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
         } else {
-            O = z;
-#pragma unroll
-            for (int s = 0; s < KBW; ++s) {
-                const uint32_t* qr = QHw + 16 * s;
-                const u32x4 qh = lds_load<u32x4>(qr), ql = lds_load<u32x4>(qr + DK / 2);
-                const f32x4 s0 = S[2 * s], s1 = S[2 * s + 1];
-                const u32x4 sh = {hi_pack(s0[0], s0[1]), hi_pack(s0[2], s0[3]), hi_pack(s1[0], s1[1]),
-                                  hi_pack(s1[2], s1[3])};
-                const u32x4 sl = {lo_pack(sh[0], s0[0], s0[1]), lo_pack(sh[1], s0[2], s0[3]),
-                                  lo_pack(sh[2], s1[0], s1[1]), lo_pack(sh[3], s1[2], s1[3])};
-                O = mfma_bf16_w(qh, sh, O);
-                O = mfma_bf16_w(qh, sl, O);
-                O = mfma_bf16_w(ql, sh, O);
-            }
+            exact_wait();
             if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
             if (h == 0) {  // the exact intra term, once per pair
 #pragma unroll
@@ -1118,13 +1106,11 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
         f32x4 Oh = {0.f, 0.f, 0.f, 0.f};
         for (int c = 0; c < nch; ++c) {
             lds_barrier();
-            const bool fast = wide_flag[c % 3] == 0;
-            if (!fast) exact_wait();
             f32x4 prev = {0.f, 0.f, 0.f, 0.f};  // (DS = 2, h = 0) the partner's share of chunk c - 1
             if constexpr (DS == 2) {
                 if (h == 0 && c > 0) prev = lds_load<f32x4>(xo(c - 1));
             }
-            const f32x4 O = matrix_chunk(c, fast);
+            const f32x4 O = matrix_chunk(c);
             if constexpr (DS == 2) {
                 if (h == 1) {
                     lds_store<f32x4>(xo(c), O);
