@@ -461,7 +461,8 @@ struct GatedBCfg {
     // state update reads the key rows transposed (lds_tr16).
     static constexpr int OPR = DK + 8;
     // Token-minor value rows (a row per column): four 16-byte blocks of four tokens,
-    // [hi x4 | lo x4] in bf16 or four fp32, blocks swizzled (vblk).
+    // [hi x4 | lo x4] in bf16 (raw v without a value gate: [v x4 | v x4]) or four
+    // fp32, blocks swizzled (vblk).
     static constexpr int VMR = 16;
     // fp32 summed decays for the exact path (token-major).
     static constexpr int AR = DK + 4, BR = BV + 4;
@@ -594,7 +595,7 @@ __device__ inline void quarter_sums(const float (&la)[4][2], int tq, float (&a)[
     }
 }
 
-template <int DK, int NW, bool GF32>
+template <int DK, int NW, bool GF32, bool GV>
 __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_kernel(const FwdParams p) {
     using Cfg = GatedBCfg<DK, NW, GF32>;
     constexpr int BV = Cfg::BV, PT = Cfg::PT;
@@ -619,7 +620,8 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
     const int64_t L = wk.len;
     const int nch = (int)((L + kGChunk - 1) / kGChunk);
     const bool rev = p.reverse != 0;
-    const bool has_g = p.g != nullptr, has_gv = p.gv != nullptr;
+    const bool has_g = p.g != nullptr;
+    constexpr bool has_gv = GV;  // the launch picks the instance from p.gv
     const float gg2 = p.g_gamma ? p.g_gamma[wk.h] * kLog2e : 0.f;
     const int j = 16 * w + lr;        // matrix waves: this lane's column inside the block
     const int vcol = wk.vb * BV + j;  // ... of v and o
@@ -858,15 +860,18 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
                     lds_store<u32x4>(d + Cfg::D_VT + row, u32x4{t0, t1, lo_pack(t0, vt[0][x], vt[1][x]),
                                                                lo_pack(t1, vt[2][x], vt[3][x])});
                 }
-            } else {  // v is exact in bf16: copy it token-minor, hi only
+            } else {  // v is exact in bf16: copy it token-minor, the four tokens twice
+                // (the hi | lo k range of the intra term and of the state update meets
+                // v's hi part twice, so the block is the MFMA operand as it stands)
                 uint32_t w[4];
 #pragma unroll
                 for (int tau = 0; tau < 4; ++tau) w[tau] = st[Cfg::ST_V + stage_dw(4 * tq + tau, qq, VNB)];
-                lds_store<u32x2>(d + Cfg::D_VT + vblk(2 * qq, tq), u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
-                                                                       __builtin_amdgcn_perm(w[3], w[2], 0x05040100u)});
-                lds_store<u32x2>(d + Cfg::D_VT + vblk(2 * qq + 1, tq),
-                                 u32x2{__builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
-                                       __builtin_amdgcn_perm(w[3], w[2], 0x07060302u)});
+                const uint32_t a0 = __builtin_amdgcn_perm(w[1], w[0], 0x05040100u),
+                               a1 = __builtin_amdgcn_perm(w[3], w[2], 0x05040100u);
+                const uint32_t b0 = __builtin_amdgcn_perm(w[1], w[0], 0x07060302u),
+                               b1 = __builtin_amdgcn_perm(w[3], w[2], 0x07060302u);
+                lds_store<u32x4>(d + Cfg::D_VT + vblk(2 * qq, tq), u32x4{a0, a1, a0, a1});
+                lds_store<u32x4>(d + Cfg::D_VT + vblk(2 * qq + 1, tq), u32x4{b0, b1, b0, b1});
             }
         }
     };
@@ -988,7 +993,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
             const u32x4 vpx = lds_load<u32x4>(d + (has_gv ? Cfg::D_VP : Cfg::D_VT) + vrow_j);
             const uint32_t w0 = hi_pack(W[0], W[1]), w1 = hi_pack(W[2], W[3]);
             const u32x4 wa = {w0, w1, lo_pack(w0, W[0], W[1]), lo_pack(w1, W[2], W[3])};
-            f32x4 Oi = mfma_bf16_w(wa, u32x4{vpx[0], vpx[1], vpx[0], vpx[1]}, z);
+            f32x4 Oi = mfma_bf16_w(wa, has_gv ? u32x4{vpx[0], vpx[1], vpx[0], vpx[1]} : vpx, z);
             if (has_gv) Oi = mfma_bf16_half(wa[0], wa[1], vpx[2], vpx[3], Oi);
             O += Oi;
             if (has_gv) O *= lds_load<f32x4>(BTf + vrow_j);
@@ -1024,7 +1029,7 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
         // Every operand is read first (the gated branch below would otherwise split
         // the reads into one wait per tile).
         const u32x4 vtx = lds_load<u32x4>(d + Cfg::D_VT + vrow_j);
-        const u32x4 vt2 = {vtx[0], vtx[1], vtx[0], vtx[1]};
+        const u32x4 vt2 = has_gv ? u32x4{vtx[0], vtx[1], vtx[0], vtx[1]} : vtx;
         const uint16_t* ktr = reinterpret_cast<const uint16_t*>(d + Cfg::D_KP) + (4 * lg + (lr >> 2)) * (2 * OPR) +
                               8 * (lr & 3) + 32 * KBW * h;
         u32x4 ktx[MTW];
@@ -1160,10 +1165,15 @@ hipError_t launch_gated_t(const FwdParams& p, bool bf16, hipStream_t s) {
     const dim3 grid(fwd_grid_size(p));
     // bf16: NW matrix waves plus 2 NW producer waves; fp32: NW waves
     const dim3 block_bf16(GatedBCfg<DK, NW, false>::NT), block_f32(64 * NW);
-    if (bf16 && p.gk_is_f32)
-        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true>), grid, block_bf16, 0, s, p);
+    const bool gv = p.gv != nullptr;
+    if (bf16 && p.gk_is_f32 && gv)
+        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true, true>), grid, block_bf16, 0, s, p);
+    else if (bf16 && p.gk_is_f32)
+        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, true, false>), grid, block_bf16, 0, s, p);
+    else if (bf16 && gv)
+        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, false, true>), grid, block_bf16, 0, s, p);
     else if (bf16)
-        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, false>), grid, block_bf16, 0, s, p);
+        hipLaunchKernelGGL((gated_bf16_kernel<DK, NW, false, false>), grid, block_bf16, 0, s, p);
     else
         hipLaunchKernelGGL((gated_f32_kernel<DK, NW>), grid, block_f32, 0, s, p);
     return hipGetLastError();
