@@ -579,16 +579,17 @@ __device__ inline void quarter_sums(const float (&la)[4][2], int tq, float (&a)[
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
         float cs[4];
-        float acc = 0.f;
+        float acc = la[0][x];
+        cs[0] = acc;
 #pragma unroll
-        for (int tau = 0; tau < 4; ++tau) {
+        for (int tau = 1; tau < 4; ++tau) {
             acc += la[tau][x];
             cs[tau] = acc;
         }
         const float s0 = quad_get<0>(acc), s1 = quad_get<1>(acc), s2 = quad_get<2>(acc), s3 = quad_get<3>(acc);
         const float s01 = s0 + s1, s012 = s01 + s2;
-        // sum of the earlier quarters, in the order that gives s012 for tq = 3
-        const float pre = ((tq > 0 ? s0 : 0.f) + (tq > 1 ? s1 : 0.f)) + (tq > 2 ? s2 : 0.f);
+        // sum of the earlier quarters (s012 for tq = 3, so that a = tot at the last token)
+        const float pre = tq > 2 ? s012 : tq > 1 ? s01 : tq > 0 ? s0 : 0.f;
 #pragma unroll
         for (int tau = 0; tau < 4; ++tau) a[tau][x] = pre + cs[tau];
         tot[x] = s012 + s3;
@@ -766,9 +767,13 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
                     g0 = bf16_lo(w);
                     g1 = bf16_hi(w);
                 }
-                const bool tv = t < nv;
-                la[tau][0] = tv ? kLog2e * g0 + gg2 : 0.f;
-                la[tau][1] = tv ? kLog2e * g1 + gg2 : 0.f;
+                la[tau][0] = kLog2e * g0 + gg2;
+                la[tau][1] = kLog2e * g1 + gg2;
+            }
+            if (nv < kGChunk) {  // a partial last chunk: tokens past its end add no decay
+#pragma unroll
+                for (int tau = 0; tau < 4; ++tau)
+                    if (4 * tq + tau >= nv) la[tau][0] = la[tau][1] = 0.f;
             }
             float a[4][2], tot[2];
             quarter_sums(la, tq, a, tot);
@@ -1111,9 +1116,11 @@ __global__ __launch_bounds__((GatedBCfg<DK, NW, GF32>::NT), 1) void gated_bf16_k
         f32x4 Oh = {0.f, 0.f, 0.f, 0.f};
         for (int c = 0; c < nch; ++c) {
             lds_barrier();
-            f32x4 prev = {0.f, 0.f, 0.f, 0.f};  // (DS = 2, h = 0) the partner's share of chunk c - 1
+            // (DS = 2, h = 0) the partner's share of chunk c - 1 (at c = 0 the other
+            // parity's slot, read but not used)
+            f32x4 prev;
             if constexpr (DS == 2) {
-                if (h == 0 && c > 0) prev = lds_load<f32x4>(xo(c - 1));
+                if (h == 0) prev = lds_load<f32x4>(xo(c - 1));
             }
             const f32x4 O = matrix_chunk(c);
             if constexpr (DS == 2) {
