@@ -164,3 +164,21 @@ def test_gated_bf16_mixed_exact_and_fast_chunks(reverse):
     o, fs, o_ref, fs_ref = _run(w, data, gates, use_gg=False, reverse=reverse)
     tag = " rev" if reverse else ""
     check_fwd(o.cpu().numpy(), fs.cpu().numpy(), o_ref, fs_ref, TOL["bf16"], f"gated_mixed{tag}")
+
+
+@pytest.mark.parametrize("reverse", [False, True])
+def test_gated_bf16_per_channel_rates(reverse):
+    """Key channels with very different decay rates (about 0, 0.25 and 1.25 per token on
+    average, the last close to the fast path's span per chunk): the rows' log-scales
+    drift apart, some rows go back to scale one at almost every chunk, others only with
+    the rest; initial state, GQA and g_gamma on."""
+    w = inputs.Workload("gated_rates", 2, 1500, 4, 2, 128, 128, "bf16", 5, 12, reverse=reverse, init_std=0.5,
+                        seed=71)
+    data = w.make()
+    rng = np.random.default_rng(w.seed + 2000)
+    rate = np.array([0.01, 0.5, 2.5, 0.01])[np.arange(w.dk) % 4].astype(np.float32)
+    g = (-rate * rng.random((w.batch, w.seqlen, w.num_heads, w.dk))).astype(np.float32)
+    gates = {"g": inputs.bf16_words(g), "gk": None, "gv": None}
+    o, fs, o_ref, fs_ref = _run(w, data, gates, use_gg=True, reverse=reverse)
+    check_fwd(o.cpu().numpy(), fs.cpu().numpy(), o_ref, fs_ref, TOL["bf16"],
+              f"gated_rates{' rev' if reverse else ''}")
