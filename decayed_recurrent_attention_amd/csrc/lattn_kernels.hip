@@ -528,68 +528,75 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         // With the dk split, the two waves of a column block each hold Q S over half of
         // dk for all 64 rows; each finishes row tiles {0, 3} (wd 0) or {1, 2} (wd 1) and
         // hands the partner its partial sums for the other two.
-        auto own_rows = [&](int b) __attribute__((always_inline)) { return DS == 1 || ((b == 0 || b == 3) ? 0 : 1) == wd; };
-        auto xslot = [&](int w, int b) __attribute__((always_inline)) {
-            return Xbuf + ((w * 2 + (b < 2 ? 0 : 1)) * 64 + lane) * 16;
-        };
-        if constexpr (DS > 1) {
+        // The rest of the chunk is compiled once per dk half (WDC), so that the row tiles
+        // a wave finishes, its hand-over slots and its store offsets are fixed in the code.
+        auto finish = [&](auto wdconst) __attribute__((always_inline)) {
+            constexpr int WDC = decltype(wdconst)::value;
+            auto own_rows = [&](int b) __attribute__((always_inline)) { return DS == 1 || ((b == 0 || b == 3) ? 0 : 1) == WDC; };
+            auto xslot = [&](int w, int b) __attribute__((always_inline)) {
+                return Xbuf + ((w * 2 + (b < 2 ? 0 : 1)) * 64 + lane) * 16;
+            };
+            if constexpr (DS > 1) {
 #pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (!own_rows(b)) lds_store<f32x4>(xslot(wv, b), O[b]);
-        }
-        lds_barrier();  // P complete (and the partial sums handed over)
-        if constexpr (DS > 1) {
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                if (own_rows(b)) O[b] += lds_load<f32x4>(xslot(wv ^ 1, b));
-        }
-
-        // O += P V.  For row tile b and token block kb, P elements 0..3 are tokens
-        // 32kb + 4lg + 0..3 and 4..7 are 32kb + 16 + 4lg + 0..3; V is read in the
-        // same token order.
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int jr = 32 * kb + 4 * lg + (lr >> 2);
-            const bf16x8 vop = cat_bf16(lds_tr16((const uint16_t*)(Vs + v_off(jr, vblk) + vhalf)),
-                                        lds_tr16((const uint16_t*)(Vs + v_off(jr + 16, vblk) + vhalf)));
-#pragma unroll
-            for (int b = 2 * kb; b < 4; ++b) {
-                if (!own_rows(b)) continue;
-                const uint8_t* pp = Pbuf + (pidx(b, kb) * 2 * 64 + lane) * 16;
-                O[b] = mfma_bf16(lds_load<bf16x8>(pp), vop, O[b]);
-                O[b] = mfma_bf16(lds_load<bf16x8>(pp + 64 * 16), vop, O[b]);
+                for (int b = 0; b < 4; ++b)
+                    if (!own_rows(b)) lds_store<f32x4>(xslot(wv, b), O[b]);
             }
-        }
+            lds_barrier();  // P complete (and the partial sums handed over)
+            if constexpr (DS > 1) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    if (own_rows(b)) O[b] += lds_load<f32x4>(xslot(wv ^ 1, b));
+            }
 
-        // Store the chunk's outputs; rows past the end fall outside the descriptor.
-        const int64_t r0 = first_row(p0, Lc);
-        const auto ro = make_rsrc(reinterpret_cast<char*>(p.o) + ((r0 * H + wk.h) * dv + wk.vb * BV) * ob,
-                                  (uint32_t)(Lc - 1) * orow_b + BV * ob);
+            // O += P V.  For row tile b and token block kb, P elements 0..3 are tokens
+            // 32kb + 4lg + 0..3 and 4..7 are 32kb + 16 + 4lg + 0..3; V is read in the
+            // same token order.
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if (!own_rows(b)) continue;
-            if constexpr (OB16) {
-                // Lanes lr and lr ^ 1 hold neighbouring columns: the even lane writes
-                // both columns of rows ii = 0, 1, the odd lane those of rows 2, 3.
-                const bool odd = (lr & 1) != 0;
-                const float t0 = lane_pair_swap(O[b][0]), t1 = lane_pair_swap(O[b][1]);
-                const float t2 = lane_pair_swap(O[b][2]), t3 = lane_pair_swap(O[b][3]);
-                const float a0 = odd ? t2 : O[b][0], a1 = odd ? O[b][2] : t0;
-                const float b0 = odd ? t3 : O[b][1], b1 = odd ? O[b][3] : t1;
-                const int i0 = 16 * b + 4 * lg + (odd ? 2 : 0), cpair = (col & ~1) * 2;
-                const int r0s = REV ? Lc - 1 - i0 : i0, r1s = REV ? Lc - 2 - i0 : i0 + 1;
-                buf_store_bf16x2(a0, a1, ro, r0s * (int)orow_b + cpair);
-                buf_store_bf16x2(b0, b1, ro, r1s * (int)orow_b + cpair);
-            } else {
+            for (int kb = 0; kb < 2; ++kb) {
+                const int jr = 32 * kb + 4 * lg + (lr >> 2);
+                const bf16x8 vop = cat_bf16(lds_tr16((const uint16_t*)(Vs + v_off(jr, vblk) + vhalf)),
+                                            lds_tr16((const uint16_t*)(Vs + v_off(jr + 16, vblk) + vhalf)));
 #pragma unroll
-                for (int ii = 0; ii < 4; ++ii) {
-                    const int i = 16 * b + 4 * lg + ii;
-                    const int rs = REV ? Lc - 1 - i : i;
-                    buf_store_f32(O[b][ii], ro, rs * (int)orow_b + col * 4);
+                for (int b = 2 * kb; b < 4; ++b) {
+                    if (!own_rows(b)) continue;
+                    const uint8_t* pp = Pbuf + (pidx(b, kb) * 2 * 64 + lane) * 16;
+                    O[b] = mfma_bf16(lds_load<bf16x8>(pp), vop, O[b]);
+                    O[b] = mfma_bf16(lds_load<bf16x8>(pp + 64 * 16), vop, O[b]);
                 }
             }
-        }
 
+            // Store the chunk's outputs; rows past the end fall outside the descriptor.
+            const int64_t r0 = first_row(p0, Lc);
+            const auto ro = make_rsrc(reinterpret_cast<char*>(p.o) + ((r0 * H + wk.h) * dv + wk.vb * BV) * ob,
+                                      (uint32_t)(Lc - 1) * orow_b + BV * ob);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                if (!own_rows(b)) continue;
+                if constexpr (OB16) {
+                    // Lanes lr and lr ^ 1 hold neighbouring columns: the even lane writes
+                    // both columns of rows ii = 0, 1, the odd lane those of rows 2, 3.
+                    const bool odd = (lr & 1) != 0;
+                    const float t0 = lane_pair_swap(O[b][0]), t1 = lane_pair_swap(O[b][1]);
+                    const float t2 = lane_pair_swap(O[b][2]), t3 = lane_pair_swap(O[b][3]);
+                    const float a0 = odd ? t2 : O[b][0], a1 = odd ? O[b][2] : t0;
+                    const float b0 = odd ? t3 : O[b][1], b1 = odd ? O[b][3] : t1;
+                    const int i0 = 16 * b + 4 * lg + (odd ? 2 : 0), cpair = (col & ~1) * 2;
+                    const int r0s = REV ? Lc - 1 - i0 : i0, r1s = REV ? Lc - 2 - i0 : i0 + 1;
+                    buf_store_bf16x2(a0, a1, ro, r0s * (int)orow_b + cpair);
+                    buf_store_bf16x2(b0, b1, ro, r1s * (int)orow_b + cpair);
+                } else {
+#pragma unroll
+                    for (int ii = 0; ii < 4; ++ii) {
+                        const int i = 16 * b + 4 * lg + ii;
+                        const int rs = REV ? Lc - 1 - i : i;
+                        buf_store_f32(O[b][ii], ro, rs * (int)orow_b + col * 4);
+                    }
+                }
+            }
+        };
+        if constexpr (DS == 1) finish(IntC<0>{});
+        else if (wd == 0) finish(IntC<0>{});
+        else finish(IntC<1>{});
         split_state<KBL>(S, Shi, Slo);
     };
 
