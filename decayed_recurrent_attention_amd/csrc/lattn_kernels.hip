@@ -392,16 +392,18 @@ __device__ __attribute__((always_inline)) inline void fwd_bf16_body(const FwdPar
         // A state handed in at the first processed position (gradient sweeps) reaches
         // the first chunk one decay step less far.
         const bool at_end = p.init_at_end && c == 0;
-        float lamL = at_end ? exp2f(g2 * (float)(Lc - 1)) : lamC;
-        if (Lc != kChunk) {  // the last chunk of a sequence: decays to its own end
+        float lamL = lamC;
+        if (at_end || Lc != kChunk) {  // (uniform; a full chunk past the first keeps lamC)
             lamL = exp2f(g2 * (float)(at_end ? Lc - 1 : Lc));
+            if (Lc != kChunk) {  // the last chunk of a sequence: decays to its own end
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int j = 32 * kb + 8 * lg + e;
-                    vw[kb][e] = j < Lc ? exp2f(g2 * (float)(Lc - 1 - j)) : 0.f;
-                }
+                    for (int e = 0; e < 8; ++e) {
+                        const int j = 32 * kb + 8 * lg + e;
+                        vw[kb][e] = j < Lc ? exp2f(g2 * (float)(Lc - 1 - j)) : 0.f;
+                    }
+            }
         }
 #pragma unroll
         for (int mt = 0; mt < MTL; ++mt) S[mt] *= lamL;
