@@ -33,8 +33,8 @@ BWD_DIMS = {
 # (dk, dv) pairs of the gated kernels: dk 32, 64, 128 with value blocks of 64 or 16 columns
 GATED_DIMS = [(32, 16), (32, 64), (64, 48), (64, 64), (64, 128), (128, 32), (128, 80), (128, 128)]
 GATE_SETS = [("g",), ("gk",), ("gv",), ("g", "gk"), ("g", "gv"), ("gk", "gv"), ("g", "gk", "gv")]
-CASES = 24
-GATED_CASES = 16
+CASES = 40
+GATED_CASES = 24
 
 
 @pytest.fixture(scope="module", autouse=True)
