@@ -182,3 +182,12 @@ def test_gated_bf16_per_channel_rates(reverse):
     o, fs, o_ref, fs_ref = _run(w, data, gates, use_gg=True, reverse=reverse)
     check_fwd(o.cpu().numpy(), fs.cpu().numpy(), o_ref, fs_ref, TOL["bf16"],
               f"gated_rates{' rev' if reverse else ''}")
+
+
+@pytest.mark.parametrize("dk", [32, 64, 128])
+@pytest.mark.parametrize("which", [("g",), ("g", "gk"), ("gv",), ("g", "gk", "gv")])
+def test_gated_bf16_instances(dk, which):
+    """Every bf16 kernel instance (summed fp32 key gate or not, value gate or not) at each
+    dk: the launch picks the instance from the gates given."""
+    w = inputs.Workload(f"gated_inst_dk{dk}", 2, 90, 4, 2, dk, 64, "bf16", 7, 12, init_std=0.3, seed=80 + dk)
+    _compare(w, which, gmax=0.6, tag=f" dk{dk} {'+'.join(which)}")
